@@ -1,0 +1,211 @@
+/*
+ * w4a8.h -- C ABI of libw4a8.so: the MXFP4 W4A8 linear layer on MI355X (gfx950).
+ *
+ * Two halves, as on the pages:
+ *   load time  NVFP4 -> MXFP4 requantization of a (possibly merged) linear
+ *              ("radiance_nvfp4.py", dequant_nvfp4 / quant_mxfp4 / requant_rows /
+ *              RadianceNvfp4ToMxfp4.process_weights_after_loading), and the
+ *              int4 group-128 load-time check and transpose
+ *              ("radiance_autoround.py", process_weights_after_loading);
+ *   run time   per-token fp8 (e4m3) activation quantization and the block-scaled
+ *              GEMM of fp8 activations against e2m1 weights with e8m0 scales
+ *              ("vllm-radiance (MXFP4)", How the MXFP4 path works: The W4A8
+ *              fp8-WMMA kernel), and the int4 g128 symmetric variant
+ *              ("radiance_autoround.py", autoround_linear, _exact_ref).
+ *
+ * Conventions (all entry points):
+ *   - Pointers named d_* / documented "device" are device (HBM) pointers owned by
+ *     the caller; the library never allocates or frees device memory.  Host
+ *     arrays are named h_*.  Every compute call is asynchronous on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns after enqueueing,
+ *     except w4a8_int4g128_prepare, which synchronizes `stream` (load time).
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     non-OK status nothing has been enqueued (W4A8_ERR_HIP aside: a launch
+ *     or runtime call failed, and earlier work of the same call may have run).
+ *   - Nothing is printed, nothing throws, no environment variable is read.
+ *   - Numbers: e2m1 codes are 4 bits, bit 3 = sign, bits 0-2 index
+ *     {0, .5, 1, 1.5, 2, 3, 4, 6}; two per byte, even k in the low nibble.
+ *     e8m0 byte b means 2^(b-127).  e4m3 is OCP E4M3FN (max 448, 0x7F/0xFF
+ *     NaN).  bf16 and fp16 travel as their raw 16-bit patterns (uint16_t).
+ *   - Row-major throughout; leading dimensions are the logical widths unless a
+ *     stride argument says otherwise.
+ *   - Inputs must be finite (no NaN/Inf e4m3 scale bytes or activations); the
+ *     result for non-finite inputs is unspecified.
+ *   - Calls that share a workspace must not overlap in time (same stream or
+ *     explicitly ordered).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_ERR_INVALID_ARG = 1,       /* null pointer, size < 0 or == 0 where >= 1 is needed,
+                                       unknown enum value, non-positive or non-finite divisor */
+    W4A8_ERR_UNSUPPORTED_SHAPE = 2, /* K % 32 != 0; int4: K % 128 != 0 or N % 8 != 0;
+                                       partition rows that do not add up; ldx < K */
+    W4A8_ERR_WORKSPACE = 3,         /* workspace missing, too small or not 256-byte aligned */
+    W4A8_ERR_ASYMMETRIC = 4,        /* int4: a qzeros word differs from 0x77777777 */
+    W4A8_ERR_HIP = 5                /* a HIP runtime call or kernel launch failed */
+} w4a8_status;
+
+/* Block-exponent rule of the requant ("radiance_nvfp4.py", _block_exponent,
+ * quant_mxfp4 and the module docstring):
+ *   OCP     e = floor(log2 amax) - 2: amax/2^e in [4, 8), the top of the block clips;
+ *   NOCLIP  e = ceil(log2(amax/6)):    amax/2^e in (3, 6], nothing clips;
+ *   MSE     of NOCLIP and NOCLIP-1, the one with the strictly smaller squared
+ *           error of the block (ties keep NOCLIP) -- the pages' default.
+ * Exponents are exact integer functions of amax (not a float log2), amax == 0
+ * gives e = 0, e is clamped to [-127, 127]; under MSE a NOCLIP exponent of -127
+ * is kept (NOCLIP-1 has no e8m0 byte). */
+typedef enum { W4A8_EXP_OCP = 0, W4A8_EXP_NOCLIP = 1, W4A8_EXP_MSE = 2 } w4a8_exp_mode;
+
+/* Weight formats accepted by the GEMMs (for workspace sizing). */
+typedef enum { W4A8_WEIGHT_MXFP4 = 0, W4A8_WEIGHT_INT4G128 = 1 } w4a8_weight_kind;
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 -> MXFP4 requantization of one linear layer.
+ * Source: "radiance_nvfp4.py": dequant_nvfp4, e2m1_index, _block_exponent,
+ * _encode_blocks, quant_mxfp4, requant_rows, and
+ * RadianceNvfp4ToMxfp4.process_weights_after_loading (one global divisor per
+ * partition of a merged linear, outputs concatenated in row order).
+ *
+ * Per element: w = RN32(e2m1(code) * RN32(e4m3(scale) / divisor_p)) (IEEE fp32
+ * division, then the product); per 32-block along K: exponent by `mode`, codes
+ * rounded to nearest e2m1 after dividing by 2^e (clamped to 6, ties to the even
+ * code), sign bit only on nonzero codes, e8m0 byte = e + 127.  The mse squared
+ * error of a block is summed in fp32 in element order, each square rounded
+ * first.  Codes and e8m0 bytes are bit-exact functions of the inputs.
+ *
+ *   d_nv_packed   device uint8 [rows, K/2]   NVFP4 codes, even k in the low nibble
+ *   d_nv_scale    device uint8 [rows, K/16]  e4m3 scale per 16 elements
+ *   h_part_rows   host int64 [n_parts]       rows of each partition, in order;
+ *                                            rows = sum(h_part_rows)
+ *   h_part_divisor host float [n_parts]      each partition's global scale as
+ *                                            stored (6*448/amax): a divisor, > 0
+ *   n_parts       >= 1
+ *   K             elements per row, K % 32 == 0, K >= 32
+ *   mode          w4a8_exp_mode
+ *   row_chunk     rows per pass (one kernel launch per pass and partition);
+ *                 0 = one pass per partition.  4096 reproduces the page's
+ *                 ROW_CHUNK.  Results do not depend on it.
+ *   d_mx_packed   device uint8 [rows, K/2]   out: e2m1 codes, even k low nibble
+ *   d_mx_e8m0     device uint8 [rows, K/32]  out: block exponents + 127
+ *   d_err_stats   device double [2*n_parts] or NULL: out, per partition
+ *                 {sum of chosen block squared errors, sum of w^2}, from which
+ *                 relRMS = sqrt(sum err / sum w^2) as the page logs it.  Filled
+ *                 with atomics: the low bits depend on summation order.
+ * Inputs and outputs must not overlap.  Errors: INVALID_ARG (null pointers,
+ * n_parts < 1, a divisor <= 0 or not finite, bad mode, row_chunk < 0, a
+ * negative partition), UNSUPPORTED_SHAPE (K % 32), HIP. */
+w4a8_status w4a8_requant_nvfp4_to_mxfp4(
+    const uint8_t *d_nv_packed, const uint8_t *d_nv_scale,
+    const int64_t *h_part_rows, const float *h_part_divisor, int n_parts,
+    int64_t K, w4a8_exp_mode mode, int64_t row_chunk,
+    uint8_t *d_mx_packed, uint8_t *d_mx_e8m0, double *d_err_stats, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Dynamic per-token fp8 activation quantization.
+ * Source: "radiance_autoround.py", autoround_linear (per-token dynamic e4m3
+ * with one fp32 scale per row, consumed by the W4A8 GEMM).  The pages leave the
+ * arithmetic to a library op; this is the plain reading:
+ *   s_m = RN32(amax_k |x[m,k]| / 448)   (s_m = 1 for an all-zero row)
+ *   x8[m,k] = e4m3 RNE of RN32(x[m,k] / s_m), saturating at +-448, sign kept.
+ * Codes and scales are bit-exact functions of the inputs.
+ *   d_x_bf16   device uint16 [M, ldx]  bf16 bits; only columns < K are read
+ *   M >= 1, K >= 1, ldx >= K
+ *   d_x_fp8    device uint8 [M, K]     out: e4m3 codes
+ *   d_x_scale  device float [M]        out: per-token scales
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (ldx < K), HIP. */
+w4a8_status w4a8_quant_act_fp8_per_token(
+    const uint16_t *d_x_bf16, int64_t M, int64_t K, int64_t ldx,
+    uint8_t *d_x_fp8, float *d_x_scale, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * GEMM workspace.  The decode band splits K across workgroups; the partial sums
+ * and one counter per output tile live in a caller-owned workspace.  The
+ * counters must be zero before first use (w4a8_workspace_init) and are left at
+ * zero by every GEMM call ("radiance_autoround.py": the split-K scratch is
+ * registered once, before any launch, because allocating inside a captured
+ * graph is illegal).
+ *
+ * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
+ * N, K and kind and any M <= M_max (0 if no split is used).  Pure host
+ * function, never fails (returns 0 for invalid sizes).
+ * w4a8_workspace_init: zero a workspace of `bytes` bytes (device, 256-byte
+ * aligned) on `stream`.  Errors: INVALID_ARG, WORKSPACE, HIP. */
+size_t      w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weight_kind kind);
+w4a8_status w4a8_workspace_init(void *d_ws, size_t bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 W4A8 GEMM:  out[m,n] = bf16_RNE( s_m * sum_k e4m3(x8[m,k]) * e2m1(w[n,k])
+ *                                              * 2^(E[n, k/32] - 127) )
+ * Source: "vllm-radiance (MXFP4)", How the MXFP4 path works: The W4A8 fp8-WMMA
+ * kernel (fp8 activations, e8m0 folded into the product, separate decode and
+ * prefill tilings, split-K decode whose last-arriving workgroup reduces in
+ * place); layouts from "radiance_nvfp4.py" module docstring.  Accumulation is
+ * fp32 (MFMA), then one scaling by s_m and one rounding to bf16.  No bias (the
+ * caller adds it, as "radiance_autoround.py" apply does).  Results are
+ * deterministic: identical bits on every call with the same inputs.
+ *   d_x_fp8    device uint8 [M, K]      e4m3 activations (w4a8_quant_act_fp8_per_token)
+ *   d_x_scale  device float [M]         per-token scales
+ *   d_w_packed device uint8 [N, K/2]    e2m1 codes, even k in the low nibble
+ *   d_w_e8m0   device uint8 [N, K/32]   block exponents + 127
+ *   d_out      device uint16 [M, N]     out: bf16 bits
+ *   M >= 1, N >= 1, K >= 32, K % 32 == 0
+ *   d_ws, ws_bytes   workspace of at least w4a8_gemm_workspace_bytes(M, N, K,
+ *                    W4A8_WEIGHT_MXFP4) bytes, initialized once; may be NULL/0
+ *                    when that is 0.
+ * Band: M <= 64 runs the decode kernels (weights streamed from HBM, split K),
+ * larger M the LDS-tiled prefill kernel.  Errors: INVALID_ARG,
+ * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_mxfp4_gemm(
+    const uint8_t *d_x_fp8, const float *d_x_scale,
+    const uint8_t *d_w_packed, const uint8_t *d_w_e8m0, uint16_t *d_out,
+    int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * int4 group-128 symmetric (AutoGPTQ layout), load-time preparation.
+ * Source: "radiance_autoround.py", module docstring and
+ * AutoRoundLinearMethod.process_weights_after_loading: every qzeros word must
+ * be 0x77777777 (zero point 8, so code c means c - 8); the weight is transposed
+ * from the checkpoint's [K/8, N] to [N, K/8] so one row of N is contiguous.
+ *   d_qweight_kn  device int32 [K/8, N]     nibble j of word i is k = 8i + j
+ *   d_qzeros      device int32 [K/128, N/8]
+ *   d_qweight_nk  device int32 [N, K/8]     out (unspecified on ASYMMETRIC)
+ *   N % 8 == 0, K % 128 == 0, N >= 8, K >= 128
+ * Synchronizes `stream` (the check result is read back).  Errors:
+ * INVALID_ARG, UNSUPPORTED_SHAPE, ASYMMETRIC, HIP. */
+w4a8_status w4a8_int4g128_prepare(
+    const int32_t *d_qweight_kn, const int32_t *d_qzeros, int64_t N, int64_t K,
+    int32_t *d_qweight_nk, void *stream);
+
+/* int4 g128 W4A8 GEMM:
+ *   out[m,n] = bf16_RNE( s_m * sum_k e4m3(x8[m,k]) * (c[n,k] - 8) * fp16(scales[k/128, n]) )
+ * Source: "radiance_autoround.py", _exact_ref and autoround_linear (the same
+ * launch convention as the MXFP4 GEMM; c - 8 is exact in e4m3, so the product
+ * runs on the fp8 matrix cores with the group scale applied per 128-K group in
+ * fp32).  Deterministic.
+ *   d_qweight_nk  device int32 [N, K/8]  (from w4a8_int4g128_prepare)
+ *   d_scales_f16  device uint16 [K/128, N]  fp16 bits
+ *   others as w4a8_mxfp4_gemm; N % 8 == 0, K % 128 == 0; workspace sized with
+ *   W4A8_WEIGHT_INT4G128.  Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_int4g128_gemm(
+    const uint8_t *d_x_fp8, const float *d_x_scale,
+    const int32_t *d_qweight_nk, const uint16_t *d_scales_f16, uint16_t *d_out,
+    int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
+
+/* Static strings; never NULL. */
+const char *w4a8_status_string(w4a8_status s);
+const char *w4a8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A8_H */

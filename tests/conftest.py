@@ -17,3 +17,22 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def gate_tiny(orc):
+    """Oracle MXFP4 (mse) of the tiny NVFP4 weight: (packed, e8m0)."""
+    from w4a8_gemm_amd import synth
+    t = synth.tiny()
+    mp, me, _ = orc.requant_nvfp4_to_mxfp4(t["nv_packed"], t["nv_scale"], t["part_rows"],
+                                          t["part_divisor"], mode="mse")
+    return mp, me
+
+
+@pytest.fixture(scope="session")
+def gate_up_mx(orc):
+    """Oracle MXFP4 (mse) of the merged gate_up NVFP4 weight: (packed, e8m0, stats)."""
+    from w4a8_gemm_amd import synth
+    g = synth.gate_up()
+    return orc.requant_nvfp4_to_mxfp4(g["nv_packed"], g["nv_scale"], g["part_rows"],
+                                      g["part_divisor"], mode="mse")

@@ -1,0 +1,118 @@
+"""C ABI of libw4a8.so on the CPU (no GPU needed).
+
+The library must load, export every function include/w4a8.h declares, and
+reject bad arguments on the host before any device work: each call here fails
+validation, so the (fake, aligned, never dereferenced) device pointers are
+never touched.  Also pins the workspace-size function's contract.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+OK, INVALID, SHAPE, WORKSPACE, ASYM, HIP = range(6)
+FAKE = 0x100000          # aligned stand-in for a device pointer (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from w4a8_gemm_amd import binding
+    return binding.lib()
+
+
+def _p(v=FAKE):
+    return ctypes.c_void_p(v)
+
+
+def test_exports_every_declared_function(L):
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", text)))
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    from w4a8_gemm_amd import binding
+    assert binding.version().startswith("w4a8")
+    for s in range(6):
+        assert binding.status_string(s)
+
+
+def _requant(L, packed=FAKE, scale=FAKE, rows=(64,), divs=(1.0,), n_parts=None, K=128, mode=2,
+             row_chunk=0, out=FAKE, e8=FAKE, stats=None):
+    pr = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    pd = (ctypes.c_float * max(len(divs), 1))(*divs)
+    return L.w4a8_requant_nvfp4_to_mxfp4(_p(packed) if packed else None, _p(scale) if scale else None,
+                                         pr, pd, len(rows) if n_parts is None else n_parts, K, mode,
+                                         row_chunk, _p(out) if out else None, _p(e8) if e8 else None,
+                                         _p(stats) if stats else None, None)
+
+
+def test_requant_validation(L):
+    assert _requant(L, packed=0) == INVALID
+    assert _requant(L, out=0) == INVALID
+    assert _requant(L, K=96 + 16) == SHAPE                       # K % 32
+    assert _requant(L, mode=3) == INVALID
+    assert _requant(L, n_parts=0) == INVALID
+    assert _requant(L, row_chunk=-1) == INVALID
+    assert _requant(L, divs=(0.0,)) == INVALID
+    assert _requant(L, divs=(-1.0,)) == INVALID
+    assert _requant(L, divs=(float("nan"),)) == INVALID
+    assert _requant(L, divs=(float("inf"),)) == INVALID
+    assert _requant(L, rows=(-5,)) == INVALID
+    assert _requant(L, packed=FAKE + 8) == INVALID               # 16-byte alignment
+    assert _requant(L, scale=FAKE + 1) == INVALID
+    assert _requant(L, stats=FAKE + 4) == INVALID
+
+
+def test_act_quant_validation(L):
+    f = L.w4a8_quant_act_fp8_per_token
+    assert f(None, 1, 8, 8, _p(), _p(), None) == INVALID
+    assert f(_p(), 0, 8, 8, _p(), _p(), None) == INVALID
+    assert f(_p(), 1, 0, 8, _p(), _p(), None) == INVALID
+    assert f(_p(), 1, 8, 7, _p(), _p(), None) == SHAPE            # ldx < K
+    assert f(_p(FAKE + 1), 1, 8, 8, _p(), _p(), None) == INVALID
+
+
+def test_gemm_validation(L):
+    g = L.w4a8_mxfp4_gemm
+    args = lambda **k: [_p(k.get("x", FAKE)) if k.get("x", FAKE) else None, _p(), _p(), _p(),
+                        _p(k.get("out", FAKE)), k.get("M", 4), k.get("N", 64), k.get("K", 128),
+                        None, 0, None]
+    assert g(*args(x=0)) == INVALID
+    assert g(*args(M=0)) == INVALID
+    assert g(*args(K=100)) == SHAPE
+    assert g(*args(out=FAKE + 2)) == INVALID
+    # a decode shape that splits K needs a workspace
+    need = L.w4a8_gemm_workspace_bytes(16, 5120, 17408, 0)
+    assert need > 0
+    a = args(M=16, N=5120, K=17408)
+    assert g(*a) == WORKSPACE
+    a[8], a[9] = _p(), need - 256
+    assert g(*a) == WORKSPACE
+    a[8], a[9] = _p(FAKE + 16), need
+    assert g(*a) == WORKSPACE                                    # 256-byte alignment
+    i = L.w4a8_int4g128_gemm
+    assert i(_p(), _p(), _p(), _p(), _p(), 4, 60, 256, None, 0, None) == SHAPE   # N % 8
+    assert i(_p(), _p(), _p(), _p(), _p(), 4, 64, 192, None, 0, None) == SHAPE   # K % 128
+    p = L.w4a8_int4g128_prepare
+    assert p(None, _p(), 64, 256, _p(), None) == INVALID
+    assert p(_p(), _p(), 60, 256, _p(), None) == SHAPE
+    assert p(_p(), _p(), 64, 200, _p(), None) == SHAPE
+
+
+def test_workspace_bytes_contract(L):
+    wb = L.w4a8_gemm_workspace_bytes
+    assert wb(0, 64, 128, 0) == 0
+    assert wb(4, 64, 100, 0) == 0                                # K % 32
+    assert wb(4, 60, 256, 1) == 0                                # int4 N % 8
+    assert wb(4, 64, 128, 7) == 0                                # unknown kind
+    # covers every smaller M, and prefill-only sizes need none
+    prev = 0
+    for m in (1, 2, 8, 16, 17, 32, 64, 65, 4096):
+        cur = wb(m, 5120, 17408, 0)
+        assert cur >= prev
+        prev = cur
+    assert wb(4096, 5120, 17408, 0) == wb(64, 5120, 17408, 0)

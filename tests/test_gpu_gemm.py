@@ -1,0 +1,190 @@
+"""GPU parity: MXFP4 and int4-g128 W4A8 GEMMs against the CPU oracle.
+
+Tolerance contract: relative Frobenius error ||out - ref||_F / ||ref||_F <= 2e-3
+against the oracle's fp64-accumulated dequantized product (bf16 output rounding
+alone contributes ~1.66e-3).  The GEMM inputs (e4m3 activations and their
+scales, MXFP4 weights) come from the generators and the oracle, never from the
+HIP path.  Small shapes are compared in full; the pages' full-size layers on
+sampled outputs computed one by one.  The split-K decode must be bitwise
+deterministic.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a8_gemm_amd as w4
+from gpu_util import GEMM_REL_F, dev_f16, dev_f32, dev_i32, dev_u8, host_bf16_as_f64, rel_frobenius, say
+from w4a8_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    w4.lib()
+
+
+def _acts(M, K, seed, spread=1.0):
+    x8, s = oracle.quant_act_fp8(synth.acts(M, K, seed=seed, spread=spread))
+    return x8, s
+
+
+def _mx_full(name, x8, s, wp, we):
+    M, N = x8.shape[0], wp.shape[0]
+    say("mxfp4_gemm full", name, (M, N, x8.shape[1]))
+    out = w4.mxfp4_gemm(dev_u8(x8), dev_f32(s), dev_u8(wp), dev_u8(we))
+    got = host_bf16_as_f64(out)
+    ref = oracle.mxfp4_gemm(x8, s, wp, we)
+    err = rel_frobenius(got, ref)
+    assert err <= GEMM_REL_F, (name, err)
+    # elementwise: one bf16 rounding of the reference plus fp32 accumulation slack
+    slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
+    assert (np.abs(got - ref) <= slack).all(), name
+    return err
+
+
+def _mx_sampled(name, x8, s, wp, we, n_samples=4096, seed=0, ws=None, reps=2):
+    M, N = x8.shape[0], wp.shape[0]
+    say("mxfp4_gemm sampled", name, (M, N, x8.shape[1]))
+    dx, ds, dw, de = dev_u8(x8), dev_f32(s), dev_u8(wp), dev_u8(we)
+    outs = [host_bf16_as_f64(w4.mxfp4_gemm(dx, ds, dw, de, workspace=ws)) for _ in range(reps)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), (name, "not deterministic")
+    g = np.random.default_rng(seed)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, n_samples)])
+    ni = np.concatenate([g.integers(0, N, M), g.integers(0, N, n_samples)])
+    ref = oracle.mxfp4_gemm(x8, s, wp, we, mi=mi, ni=ni)
+    err = rel_frobenius(outs[0][mi, ni], ref)
+    assert err <= GEMM_REL_F, (name, err)
+    return outs[0]
+
+
+def test_mxfp4_tiny(gate_tiny):
+    t = synth.tiny()
+    x8, s = oracle.quant_act_fp8(t["x"])
+    _mx_full("tiny", x8, s, *gate_tiny)
+
+
+# decode band (M <= 64, split K) and prefill band (M > 64) on ragged shapes:
+# N not a multiple of the tiles, K a multiple of 32 but not of 128, M = 1, 17, 65
+RAGGED = [(1, 64, 128), (1, 300, 96), (4, 256, 512), (5, 100, 544), (16, 257, 1024),
+          (17, 300, 224), (33, 129, 640), (64, 512, 2048), (64, 1000, 4096), (1, 6000, 2560),
+          (65, 200, 384), (130, 260, 640), (256, 256, 256), (300, 77, 160)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_mxfp4_ragged_shapes(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K))
+    x8, s = _acts(M, K, (M, K), spread=10.0)
+    _mx_full(f"ragged {M}x{N}x{K}", x8, s, w["w_packed"], w["w_e8m0"])
+
+
+def test_mxfp4_extreme_scales():
+    # e8m0 bytes across the whole range used by real weights (incl. 2^-127)
+    N, K = 96, 256
+    w = synth.mxfp4_random(N, K, seed=3, e_lo=0, e_hi=140)
+    x8, s = _acts(8, K, 5)
+    _mx_full("extreme e8m0", x8, s, w["w_packed"], w["w_e8m0"])
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 64])
+def test_mxfp4_gate_up_decode(gate_up_mx, M):
+    x8, s = _acts(M, synth.HIDDEN, (1, M), spread=10.0)
+    _mx_sampled(f"gate_up M={M}", x8, s, *gate_up_mx[:2])
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_mxfp4_down_proj_decode(M):
+    d = synth.down_proj()
+    x8, s = _acts(M, synth.INTERMEDIATE, (2, M))
+    _mx_sampled(f"down_proj M={M}", x8, s, d["w_packed"], d["w_e8m0"])
+
+
+def test_mxfp4_prefill_full_size(gate_up_mx):
+    x8, s = _acts(4096, synth.HIDDEN, 3)
+    _mx_sampled("prefill 4096", x8, s, *gate_up_mx[:2], n_samples=8192, reps=1)
+
+
+def test_mxfp4_split_k_deterministic_and_workspace_reuse():
+    d = synth.down_proj()
+    dw, de = dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"])
+    ws = w4.Workspace(64, d["N"], d["K"], "mxfp4")
+    assert ws.nbytes > 0
+    first = {}
+    for rep in range(3):
+        for M in (64, 1, 16, 3):
+            x8, s = _acts(M, d["K"], (9, M))
+            say("split-K repeat", rep, M)
+            o = host_bf16_as_f64(w4.mxfp4_gemm(dev_u8(x8), dev_f32(s), dw, de, workspace=ws))
+            if rep == 0:
+                first[M] = o
+            else:
+                assert np.array_equal(o, first[M]), M
+
+
+def test_mxfp4_rejects_small_workspace():
+    d = synth.down_proj()
+    x8, s = _acts(16, d["K"], 1)
+    need = w4.gemm_workspace_bytes(16, d["N"], d["K"])
+    assert need > 0
+    small = torch.zeros(need // 2 // 256 * 256, dtype=torch.uint8, device="cuda")
+    lib = w4.lib()
+    import ctypes
+    dx, ds = dev_u8(x8), dev_f32(s)
+    dw, de = dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"])
+    out = torch.empty((16, d["N"]), dtype=torch.bfloat16, device="cuda")
+    st = lib.w4a8_mxfp4_gemm(ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(ds.data_ptr()),
+                             ctypes.c_void_p(dw.data_ptr()), ctypes.c_void_p(de.data_ptr()),
+                             ctypes.c_void_p(out.data_ptr()), 16, d["N"], d["K"],
+                             ctypes.c_void_p(small.data_ptr()), small.numel(), None)
+    assert st == w4.binding.ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# int4 group-128 symmetric
+# ---------------------------------------------------------------------------
+
+def _int4_case(name, q, M, seed, full=False, n_samples=4096):
+    N, K = q["N"], q["K"]
+    say("int4 prepare", name, (N, K))
+    nk = w4.int4g128_prepare(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]))
+    ref_nk, bad = oracle.int4_prepare(q["qweight_kn"], q["qzeros"], N, K)
+    assert bad == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(nk.cpu().numpy(), ref_nk), name
+    x8, s = _acts(M, K, seed)
+    say("int4 gemm", name, (M, N, K))
+    out = host_bf16_as_f64(w4.int4g128_gemm(dev_u8(x8), dev_f32(s), nk, dev_f16(q["scales"])))
+    if full:
+        ref = oracle.int4_gemm(x8, s, ref_nk, q["scales"])
+        err = rel_frobenius(out, ref)
+    else:
+        g = np.random.default_rng(seed if isinstance(seed, int) else sum(seed))
+        mi = np.concatenate([np.arange(M), g.integers(0, M, n_samples)])
+        ni = np.concatenate([g.integers(0, N, M), g.integers(0, N, n_samples)])
+        ref = oracle.int4_gemm(x8, s, ref_nk, q["scales"], mi=mi, ni=ni)
+        err = rel_frobenius(out[mi, ni], ref)
+    assert err <= GEMM_REL_F, (name, err)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (4, 256, 512), (17, 136, 384), (64, 520, 1024),
+                                   (65, 64, 256), (130, 200, 640)])
+def test_int4_ragged(M, N, K):
+    _int4_case(f"int4 {M}x{N}x{K}", synth.int4_random(N, K, seed=(N, K)), M, (M, K), full=True)
+
+
+@pytest.mark.parametrize("M", [1, 64, 2048])
+def test_int4_full_size(M):
+    _int4_case(f"int4 I M={M}", synth.int4(), M, (4, M))
+
+
+def test_int4_prepare_rejects_asymmetric_zeros():
+    q = synth.int4_random(64, 256, seed=1)
+    qz = q["qzeros"].copy()
+    qz.view(np.uint32)[1, 3] = 0x77777778
+    say("int4 prepare asymmetric")
+    with pytest.raises(ValueError):
+        w4.int4g128_prepare(dev_i32(q["qweight_kn"]), dev_i32(qz))

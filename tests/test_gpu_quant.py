@@ -1,0 +1,176 @@
+"""GPU parity: per-token fp8 activation quantization and NVFP4 -> MXFP4 requant.
+
+Both are bit-exact contracts: every e4m3 code, fp32 token scale, e2m1 code and
+e8m0 byte from the HIP kernels (called through the C ABI via the binding) must
+equal the CPU oracle's.  Inputs are seeded synthetic data of the pages' shapes
+(w4a8_gemm_amd.synth) plus hand-made edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a8_gemm_amd as w4
+from gpu_util import dev_bf16, dev_u8, host, say
+from w4a8_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    w4.lib()
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _act_case(bits, K=None, ldx=None, name=""):
+    bits = np.ascontiguousarray(bits, np.uint16)
+    M, L = bits.shape
+    K = L if K is None else K
+    say("act_quant", name, (M, K, L))
+    xt = dev_bf16(bits)
+    x8, s = w4.quant_act_fp8_per_token(xt[:, :K])
+    r8, rs = oracle.quant_act_fp8(bits, K=K, ldx=L)
+    g8, gs = host(x8), host(s)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), name
+    bad = np.argwhere(g8 != r8)
+    assert bad.size == 0, (name, bad[:5], g8[tuple(bad[0])], r8[tuple(bad[0])])
+
+
+def test_act_quant_tiny():
+    t = synth.tiny()
+    _act_case(t["x"], name="tiny")
+
+
+def test_act_quant_every_bf16_value():
+    # a row whose amax is 448 has scale exactly 1, so every bf16 value in
+    # [-448, 448] reaches the e4m3 rounding unchanged
+    pos = np.arange(0, 0x43E1, dtype=np.uint16)            # +0 .. 448
+    vals = np.concatenate([pos, pos | 0x8000])
+    K = (vals.size + 7) // 8 * 8
+    row = np.zeros(K, np.uint16)
+    row[: vals.size] = vals
+    # a second row: same values divided by 2^20 (scale 448 / 2^20, non-trivial y)
+    f = torch.from_numpy(row.view(np.int16)).view(torch.bfloat16).float() / 2.0 ** 20
+    row2 = _bf16_bits(f.numpy())
+    _act_case(np.stack([row, row2]), name="all-bf16")
+
+
+def test_act_quant_edge_rows():
+    g = np.random.default_rng(7)
+    K = 4096
+    rows = [np.zeros(K, np.float32),                              # all zero: scale 1
+            -np.zeros(K, np.float32),                             # negative zeros
+            g.standard_normal(K).astype(np.float32) * 1e-38,      # subnormal bf16
+            g.standard_normal(K).astype(np.float32) * 1e30,
+            g.standard_normal(K).astype(np.float32) * 3e-5,
+            np.where(g.random(K) < 0.99, 0.0, g.standard_normal(K)).astype(np.float32)]
+    one = np.zeros(K, np.float32)
+    one[123] = -7.0                                                # single nonzero
+    rows.append(one)
+    _act_case(np.stack([_bf16_bits(r) for r in rows]), name="edge-rows")
+
+
+def test_act_quant_ragged_and_strided():
+    x = synth.acts(37, 1104, seed=11, spread=100.0)
+    _act_case(x, K=1001, name="ragged K=1001 ldx=1104")          # scalar path
+    _act_case(x, K=1096, name="K=1096 ldx=1104")                 # vector path, strided rows
+    _act_case(x[:1, :8], name="1x8")
+    _act_case(x[:1, :1], name="1x1")
+
+
+def test_act_quant_decode_and_prefill_shapes():
+    for M, K, seed in ((1, 5120, (1, 1)), (64, 5120, (1, 64)), (16, 17408, (2, 16))):
+        _act_case(synth.acts(M, K, seed=seed, spread=10.0), name=f"M={M} K={K}")
+    _act_case(synth.acts(4096, 5120, seed=3), name="prefill 4096x5120")
+
+
+# ---------------------------------------------------------------------------
+# requant
+# ---------------------------------------------------------------------------
+
+def _requant_case(d, mode, row_chunk=0, name="", stats=True):
+    say("requant", name, mode, d["nv_packed"].shape, "row_chunk", row_chunk)
+    mp, me, st = w4.requant_nvfp4_to_mxfp4(dev_u8(d["nv_packed"]), dev_u8(d["nv_scale"]),
+                                           d["part_rows"], d["part_divisor"], mode=mode,
+                                           row_chunk=row_chunk, stats=True)
+    rp, re_, rst = oracle.requant_nvfp4_to_mxfp4(d["nv_packed"], d["nv_scale"], d["part_rows"],
+                                                 d["part_divisor"], mode=mode)
+    gp, ge = host(mp), host(me)
+    bad = np.argwhere(ge != re_)
+    assert bad.size == 0, (name, mode, "e8m0", bad[:5], ge[tuple(bad[0])], re_[tuple(bad[0])])
+    bad = np.argwhere(gp != rp)
+    assert bad.size == 0, (name, mode, "codes", bad[:5], gp[tuple(bad[0])], rp[tuple(bad[0])])
+    if stats:
+        np.testing.assert_allclose(host(st), rst, rtol=1e-6, atol=0)
+    return gp, ge
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_requant_tiny(mode):
+    _requant_case(synth.tiny(), mode, name="tiny")
+
+
+def _random_nvfp4(rows, K, seed, divisors):
+    g = np.random.default_rng(seed)
+    packed = g.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scale = g.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    scale[(scale & 0x7F) == 0x7F] = 0x38        # no NaN scale bytes
+    parts = np.full(len(divisors), rows // len(divisors), np.int64)
+    parts[-1] += rows - parts.sum()
+    return dict(nv_packed=packed, nv_scale=scale, part_rows=parts,
+                part_divisor=np.asarray(divisors, np.float32))
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_requant_random_bytes_many_partitions(mode):
+    # every code and scale byte, signed scales, subnormal scales, divisors from
+    # 3e38 (subnormal weights, exponent clamp at -127) to 1e-30 (exponent ~100)
+    d = _random_nvfp4(997, 96, 5, [2688.0, 1.0, 3e38, 1e-30, 0.37, 6.5e4, 1e-3])
+    _requant_case(d, mode, name="random-bytes")
+    _requant_case(d, mode, row_chunk=100, name="random-bytes chunked")
+
+
+def test_requant_partition_edge_cases():
+    d = _random_nvfp4(64, 32, 9, [5.0, 7.0, 11.0])
+    d["part_rows"] = np.array([0, 64, 0], np.int64)                 # empty partitions
+    _requant_case(d, "mse", name="empty partitions")
+    z = dict(d)
+    z["nv_packed"] = np.zeros_like(d["nv_packed"])                  # all-zero blocks: byte 127
+    _, ge = _requant_case(z, "mse", name="zero blocks")
+    assert (ge == 127).all()
+
+
+def test_requant_gate_up_full_mse(gate_up_mx):
+    g = synth.gate_up()
+    gp, ge = _requant_case(g, "mse", row_chunk=4096, name="gate_up ROW_CHUNK=4096")
+    assert np.array_equal(gp, gate_up_mx[0]) and np.array_equal(ge, gate_up_mx[1])
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip"])
+def test_requant_gate_up_other_modes(mode):
+    g = synth.gate_up()
+    # both partitions, 2048 rows each (one from each divisor)
+    rows = 2048
+    sel = np.r_[0:rows, 17408:17408 + rows]
+    d = dict(nv_packed=g["nv_packed"][sel], nv_scale=g["nv_scale"][sel],
+             part_rows=np.array([rows, rows], np.int64), part_divisor=g["part_divisor"])
+    _requant_case(d, mode, name="gate_up subset")
+
+
+def test_requant_rejects_bad_arguments():
+    d = synth.tiny()
+    p, s = dev_u8(d["nv_packed"]), dev_u8(d["nv_scale"])
+    with pytest.raises(ValueError):
+        w4.requant_nvfp4_to_mxfp4(p, s, [128, 100], [1.0, 1.0])     # rows do not add up
+    with pytest.raises(ValueError):
+        w4.requant_nvfp4_to_mxfp4(p, s, [256], [0.0])               # divisor <= 0
+    with pytest.raises(ValueError):
+        w4.requant_nvfp4_to_mxfp4(p, s, [256], [float("inf")])
+    with pytest.raises(ValueError):
+        w4.requant_nvfp4_to_mxfp4(p[:, :8], s[:, :1], [256], [1.0])  # K = 16: K % 32 != 0

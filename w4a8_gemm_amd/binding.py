@@ -1,2 +1,282 @@
-"""Placeholder, replaced by the ctypes binding."""
-__all__ = []
+"""ctypes binding of libw4a8.so (C ABI in include/w4a8.h).
+
+Argument marshalling only: torch tensors become device pointers and sizes, the
+current torch stream becomes the HIP stream, and status codes become
+exceptions (ValueError for argument, shape and format errors, RuntimeError for
+HIP errors).  Every computation runs in the library's HIP kernels; if the
+library cannot be loaded, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "version", "status_string", "EXP_MODES", "W4A8Error",
+    "requant_nvfp4_to_mxfp4", "quant_act_fp8_per_token", "gemm_workspace_bytes",
+    "Workspace", "mxfp4_gemm", "int4g128_prepare", "int4g128_gemm", "w4a8_linear",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_SHAPE, ERR_WORKSPACE, ERR_ASYMMETRIC, ERR_HIP = range(6)
+EXP_MODES = {"ocp": 0, "noclip": 1, "mse": 2}
+WEIGHT_MXFP4, WEIGHT_INT4G128 = 0, 1
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a8.so (built by ``python -m w4a8_gemm_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libw4a8.so is not built ({LIB_PATH}); run "
+                               "`python -m w4a8_gemm_amd.build` (there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.w4a8_requant_nvfp4_to_mxfp4.argtypes = [_vp, _vp, _vp, _vp, _int, _i64, _int, _i64,
+                                                  _vp, _vp, _vp, _vp]
+        L.w4a8_quant_act_fp8_per_token.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+        L.w4a8_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
+        L.w4a8_gemm_workspace_bytes.restype = _size
+        L.w4a8_workspace_init.argtypes = [_vp, _size, _vp]
+        L.w4a8_mxfp4_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_int4g128_prepare.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+        L.w4a8_int4g128_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_status_string.argtypes = [_int]
+        L.w4a8_status_string.restype = ctypes.c_char_p
+        L.w4a8_version.argtypes = []
+        L.w4a8_version.restype = ctypes.c_char_p
+        for name in ("w4a8_requant_nvfp4_to_mxfp4", "w4a8_quant_act_fp8_per_token",
+                     "w4a8_workspace_init", "w4a8_mxfp4_gemm", "w4a8_int4g128_prepare",
+                     "w4a8_int4g128_gemm"):
+            getattr(L, name).restype = _int
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().w4a8_version().decode()
+
+
+def status_string(status: int) -> str:
+    return lib().w4a8_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status == OK:
+        return
+    if status == ERR_HIP:
+        raise W4A8Error(status, what)
+    raise ValueError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# ---------------------------------------------------------------------------
+# load time: NVFP4 -> MXFP4
+# ---------------------------------------------------------------------------
+
+def requant_nvfp4_to_mxfp4(nv_packed: torch.Tensor, nv_scale: torch.Tensor, part_rows,
+                           part_divisor, mode: str = "mse", row_chunk: int = 0,
+                           out_packed: torch.Tensor | None = None,
+                           out_e8m0: torch.Tensor | None = None, stats: bool = False):
+    """NVFP4 [rows, K/2] u8 codes + [rows, K/16] u8 e4m3 scales -> MXFP4 codes
+    [rows, K/2] u8 and e8m0 [rows, K/32] u8.  part_rows / part_divisor: row count
+    and stored global divisor (6*448/amax) of each partition of a merged linear.
+    With stats=True also returns a float64 [n_parts, 2] tensor of
+    (sum of squared block errors, sum of w^2) per partition."""
+    _need(nv_packed, "nv_packed", torch.uint8)
+    _need(nv_scale, "nv_scale", torch.uint8, nv_packed.device)
+    if nv_packed.dim() != 2 or nv_scale.dim() != 2:
+        raise ValueError("nv_packed and nv_scale must be 2-D")
+    rows, half = nv_packed.shape
+    K = 2 * half
+    if tuple(nv_scale.shape) != (rows, K // 16) or K % 16:
+        raise ValueError("nv_scale must be [rows, K/16]")
+    if not (nv_packed.is_contiguous() and nv_scale.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    pr = (ctypes.c_int64 * len(part_rows))(*[int(r) for r in part_rows])
+    pd = (ctypes.c_float * len(part_divisor))(*[float(d) for d in part_divisor])
+    if len(part_rows) != len(part_divisor):
+        raise ValueError("part_rows and part_divisor differ in length")
+    if sum(int(r) for r in part_rows) != rows:
+        raise ValueError(f"partition rows {list(part_rows)} do not add up to {rows}")
+    dev = nv_packed.device
+    if out_packed is None:
+        out_packed = torch.empty((rows, half), dtype=torch.uint8, device=dev)
+    if out_e8m0 is None:
+        out_e8m0 = torch.empty((rows, max(K // 32, 0)), dtype=torch.uint8, device=dev)
+    _need(out_packed, "out_packed", torch.uint8, dev)
+    _need(out_e8m0, "out_e8m0", torch.uint8, dev)
+    st = torch.empty((len(part_rows), 2), dtype=torch.float64, device=dev) if stats else None
+    if mode not in EXP_MODES:
+        raise ValueError(f"mode must be one of {sorted(EXP_MODES)}")
+    status = lib().w4a8_requant_nvfp4_to_mxfp4(
+        _ptr(nv_packed), _ptr(nv_scale), pr, pd, len(part_rows), K, EXP_MODES[mode],
+        int(row_chunk), _ptr(out_packed), _ptr(out_e8m0), _ptr(st), _stream(nv_packed))
+    _check(status, "w4a8_requant_nvfp4_to_mxfp4")
+    return (out_packed, out_e8m0, st) if stats else (out_packed, out_e8m0)
+
+
+# ---------------------------------------------------------------------------
+# run time
+# ---------------------------------------------------------------------------
+
+def quant_act_fp8_per_token(x: torch.Tensor, out: torch.Tensor | None = None,
+                            scale: torch.Tensor | None = None):
+    """bf16 [M, K] (rows may be strided) -> (e4m3 codes u8 [M, K], fp32 scales [M])."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.uint8, dev)
+    _need(scale, "scale", torch.float32, dev)
+    status = lib().w4a8_quant_act_fp8_per_token(_ptr(x), M, K, x.stride(0), _ptr(out),
+                                                _ptr(scale), _stream(x))
+    _check(status, "w4a8_quant_act_fp8_per_token")
+    return out, scale
+
+
+def gemm_workspace_bytes(M_max: int, N: int, K: int, kind: str = "mxfp4") -> int:
+    k = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128}[kind]
+    return int(lib().w4a8_gemm_workspace_bytes(int(M_max), int(N), int(K), k))
+
+
+class Workspace:
+    """Caller-owned split-K workspace for GEMMs with M <= M_max on one (N, K).
+    Allocated by torch and zeroed once; every GEMM leaves its counters at zero."""
+
+    def __init__(self, M_max: int, N: int, K: int, kind: str = "mxfp4", device="cuda"):
+        self.nbytes = gemm_workspace_bytes(M_max, N, K, kind)
+        self.buf = None
+        if self.nbytes:
+            self.buf = torch.empty((self.nbytes + 255) // 256 * 256, dtype=torch.uint8,
+                                   device=device)
+            status = lib().w4a8_workspace_init(_ptr(self.buf), self.buf.numel(),
+                                               _stream(self.buf))
+            _check(status, "w4a8_workspace_init")
+
+    def args(self):
+        if self.buf is None:
+            return None, 0
+        return _ptr(self.buf), self.buf.numel()
+
+
+def _ws_args(workspace, M, N, K, kind, device):
+    if workspace is None:
+        need = gemm_workspace_bytes(M, N, K, kind)
+        if need == 0:
+            return None, 0, None
+        workspace = Workspace(M, N, K, kind, device)
+    p, n = workspace.args()
+    return p, n, workspace
+
+
+def mxfp4_gemm(x_fp8: torch.Tensor, x_scale: torch.Tensor, w_packed: torch.Tensor,
+               w_e8m0: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: Workspace | None = None) -> torch.Tensor:
+    """out[M, N] bf16 = s_m * (e4m3 x) @ (e2m1 w * 2^(e8m0 - 127))^T."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    _need(w_packed, "w_packed", torch.uint8, dev)
+    _need(w_e8m0, "w_e8m0", torch.uint8, dev)
+    M, K = x_fp8.shape
+    N = w_packed.shape[0]
+    if tuple(w_packed.shape) != (N, K // 2) or tuple(w_e8m0.shape) != (N, K // 32):
+        raise ValueError("weight shapes must be [N, K/2] and [N, K/32]")
+    if x_scale.numel() != M:
+        raise ValueError("x_scale must hold M values")
+    for t, n in ((x_fp8, "x_fp8"), (w_packed, "w_packed"), (w_e8m0, "w_e8m0"), (x_scale, "x_scale")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, N, K, "mxfp4", dev)
+    status = lib().w4a8_mxfp4_gemm(_ptr(x_fp8), _ptr(x_scale), _ptr(w_packed), _ptr(w_e8m0),
+                                   _ptr(out), M, N, K, wp, wn, _stream(x_fp8))
+    _check(status, "w4a8_mxfp4_gemm")
+    return out
+
+
+def int4g128_prepare(qweight_kn: torch.Tensor, qzeros: torch.Tensor) -> torch.Tensor:
+    """AutoGPTQ qweight [K/8, N] int32 -> [N, K/8] int32 after checking that every
+    qzeros word is 0x77777777 (synchronizes the stream; load time)."""
+    _need(qweight_kn, "qweight", torch.int32)
+    dev = qweight_kn.device
+    _need(qzeros, "qzeros", torch.int32, dev)
+    K8, N = qweight_kn.shape
+    K = 8 * K8
+    out = torch.empty((N, K8), dtype=torch.int32, device=dev)
+    status = lib().w4a8_int4g128_prepare(_ptr(qweight_kn), _ptr(qzeros), N, K, _ptr(out),
+                                         _stream(qweight_kn))
+    _check(status, "w4a8_int4g128_prepare")
+    return out
+
+
+def int4g128_gemm(x_fp8: torch.Tensor, x_scale: torch.Tensor, qweight_nk: torch.Tensor,
+                  scales: torch.Tensor, out: torch.Tensor | None = None,
+                  workspace: Workspace | None = None) -> torch.Tensor:
+    """out[M, N] bf16 = s_m * (e4m3 x) @ ((c - 8) * scale[k/128, n])^T."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    _need(qweight_nk, "qweight_nk", torch.int32, dev)
+    _need(scales, "scales", torch.float16, dev)
+    M, K = x_fp8.shape
+    N = qweight_nk.shape[0]
+    if tuple(qweight_nk.shape) != (N, K // 8) or tuple(scales.shape) != (K // 128, N):
+        raise ValueError("shapes must be qweight [N, K/8] and scales [K/128, N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, N, K, "int4", dev)
+    status = lib().w4a8_int4g128_gemm(_ptr(x_fp8), _ptr(x_scale), _ptr(qweight_nk), _ptr(scales),
+                                      _ptr(out), M, N, K, wp, wn, _stream(x_fp8))
+    _check(status, "w4a8_int4g128_gemm")
+    return out
+
+
+def w4a8_linear(x: torch.Tensor, w_packed: torch.Tensor, w_e8m0: torch.Tensor,
+                workspace: Workspace | None = None) -> torch.Tensor:
+    """The layer's run-time path: per-token fp8 quantization, then the MXFP4 GEMM."""
+    x2 = x.reshape(-1, x.shape[-1])
+    x8, s = quant_act_fp8_per_token(x2)
+    out = mxfp4_gemm(x8, s, w_packed, w_e8m0, workspace=workspace)
+    return out.reshape(*x.shape[:-1], w_packed.shape[0])

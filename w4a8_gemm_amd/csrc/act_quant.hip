@@ -1,0 +1,97 @@
+// act_quant.hip -- dynamic per-token fp8 (E4M3FN) activation quantization.
+//
+// "radiance_autoround.py", autoround_linear: activations become e4m3 codes with
+// one fp32 scale per token (row) before the W4A8 GEMM.  The pages leave the
+// arithmetic to a library op; the plain reading used here:
+//   s = amax_k |x[m,k]| / 448   (1 for an all-zero row)
+//   code = e4m3 round-to-nearest-even of x / s, saturating at 448, sign kept.
+// One workgroup per row: a grid-stride max over the row (wavefront butterfly,
+// then LDS across the four waves), then the divide-and-encode pass, which
+// re-reads the row from L2.  Rows are read 16 bytes per lane when the layout
+// allows it.
+#include "w4a8_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace w4a8 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    __shared__ float red[kThreads / 64];
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t K, int64_t ldx,
+                                                             uint8_t* __restrict__ x8,
+                                                             float* __restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = x + m * ldx;
+    uint8_t* orow = x8 + m * K;
+    float amax = 0.0f;
+    if (VEC) {
+        const uint4* r4 = reinterpret_cast<const uint4*>(row);
+        for (int64_t c = threadIdx.x; c < K / 8; c += kThreads) {
+            const uint4 v = r4[c];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                amax = fmaxf(amax, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
+                amax = fmaxf(amax, fabsf(bf16_to_f32(d[q] >> 16)));
+            }
+        }
+    } else {
+        for (int64_t k = threadIdx.x; k < K; k += kThreads)
+            amax = fmaxf(amax, fabsf(bf16_to_f32(row[k])));
+    }
+    amax = block_max(amax);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division
+    if (threadIdx.x == 0) xs[m] = s;
+    if (VEC) {
+        const uint4* r4 = reinterpret_cast<const uint4*>(row);
+        uint2* o2 = reinterpret_cast<uint2*>(orow);
+        for (int64_t c = threadIdx.x; c < K / 8; c += kThreads) {
+            const uint4 v = r4[c];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[2] = {0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] & 0xFFFFu) / s);
+                const uint32_t hi = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] >> 16) / s);
+                o[q >> 1] |= (lo | (hi << 8)) << (16 * (q & 1));
+            }
+            o2[c] = make_uint2(o[0], o[1]);
+        }
+    } else {
+        for (int64_t k = threadIdx.x; k < K; k += kThreads)
+            orow[k] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(row[k]) / s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8,
+                            float* xs, hipStream_t stream) {
+    const bool vec = (K % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) &&
+                     ((uintptr_t)x8 % 8 == 0);
+    if (vec)
+        hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(kThreads), 0, stream, x,
+                           K, ldx, x8, xs);
+    else
+        hipLaunchKernelGGL(act_quant_kernel<false>, dim3((unsigned)M), dim3(kThreads), 0, stream,
+                           x, K, ldx, x8, xs);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,0 +1,180 @@
+// api.hip -- the C ABI of libw4a8 (declared in include/w4a8.h).
+//
+// Every entry point validates its arguments on the host before it enqueues
+// anything, then launches the kernels on the caller's stream.  No device memory
+// is allocated or freed here; nothing is printed; no environment is read.
+#include <math.h>
+
+#include "w4a8_internal.h"
+
+using namespace w4a8;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kDecodeMaxM = 64;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline w4a8_status hip_status(hipError_t e) { return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP; }
+
+w4a8_status check_gemm_common(const void* x8, const void* xs, const void* w, void* out,
+                              int64_t M, int64_t N, int64_t K) {
+    if (!x8 || !xs || !w || !out) return W4A8_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return W4A8_ERR_INVALID_ARG;
+    if (!aligned(x8, 16) || !aligned(xs, 4) || !aligned(w, 16) || !aligned(out, 8))
+        return W4A8_ERR_INVALID_ARG;
+    return W4A8_OK;
+}
+
+w4a8_status check_workspace(size_t need, void* ws, size_t ws_bytes) {
+    if (need == 0) return W4A8_OK;
+    if (!ws || ws_bytes < need || !aligned(ws, 256)) return W4A8_ERR_WORKSPACE;
+    return W4A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a8_status w4a8_requant_nvfp4_to_mxfp4(const uint8_t* d_nv_packed, const uint8_t* d_nv_scale,
+                                        const int64_t* h_part_rows, const float* h_part_divisor,
+                                        int n_parts, int64_t K, w4a8_exp_mode mode,
+                                        int64_t row_chunk, uint8_t* d_mx_packed,
+                                        uint8_t* d_mx_e8m0, double* d_err_stats, void* stream) {
+    if (!d_nv_packed || !d_nv_scale || !h_part_rows || !h_part_divisor || !d_mx_packed || !d_mx_e8m0)
+        return W4A8_ERR_INVALID_ARG;
+    if (n_parts < 1 || row_chunk < 0 || K < 1 || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (mode != W4A8_EXP_OCP && mode != W4A8_EXP_NOCLIP && mode != W4A8_EXP_MSE)
+        return W4A8_ERR_INVALID_ARG;
+    if (K % 32 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_nv_packed, 16) || !aligned(d_mx_packed, 16) || !aligned(d_nv_scale, 2) ||
+        (d_err_stats && !aligned(d_err_stats, 8)))
+        return W4A8_ERR_INVALID_ARG;
+    for (int p = 0; p < n_parts; ++p) {
+        const float gd = h_part_divisor[p];
+        if (h_part_rows[p] < 0 || h_part_rows[p] > kMaxDim) return W4A8_ERR_INVALID_ARG;
+        if (!(gd > 0.0f) || !isfinite(gd)) return W4A8_ERR_INVALID_ARG;
+    }
+    hipStream_t s = as_stream(stream);
+    if (d_err_stats) {
+        const hipError_t e = launch_fill_zero_f64(d_err_stats, 2 * (int64_t)n_parts, s);
+        if (e != hipSuccess) return W4A8_ERR_HIP;
+    }
+    int64_t r0 = 0;
+    for (int p = 0; p < n_parts; ++p) {
+        const int64_t width = h_part_rows[p];
+        const int64_t chunk = row_chunk > 0 ? row_chunk : (width > 0 ? width : 1);
+        for (int64_t a = 0; a < width; a += chunk) {
+            const int64_t n = (width - a) < chunk ? (width - a) : chunk;
+            const int64_t r = r0 + a;
+            const hipError_t e = launch_requant(
+                d_nv_packed + r * (K / 2), d_nv_scale + r * (K / 16), h_part_divisor[p],
+                n * (K / 32), (int)mode, d_mx_packed + r * (K / 2), d_mx_e8m0 + r * (K / 32),
+                d_err_stats ? d_err_stats + 2 * p : nullptr, s);
+            if (e != hipSuccess) return W4A8_ERR_HIP;
+        }
+        r0 += width;
+    }
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_quant_act_fp8_per_token(const uint16_t* d_x_bf16, int64_t M, int64_t K,
+                                         int64_t ldx, uint8_t* d_x_fp8, float* d_x_scale,
+                                         void* stream) {
+    if (!d_x_bf16 || !d_x_fp8 || !d_x_scale) return W4A8_ERR_INVALID_ARG;
+    if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim || ldx > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (ldx < K) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_x_bf16, 2) || !aligned(d_x_scale, 4)) return W4A8_ERR_INVALID_ARG;
+    return hip_status(launch_act_quant(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, as_stream(stream)));
+}
+
+size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weight_kind kind) {
+    if (M_max < 1 || N < 1 || K < 32 || M_max > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    if (kind == W4A8_WEIGHT_MXFP4 && K % 32 != 0) return 0;
+    if (kind == W4A8_WEIGHT_INT4G128 && (K % 128 != 0 || N % 8 != 0)) return 0;
+    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128) return 0;
+    size_t need = 0;
+    const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
+    for (int64_t m = 1; m <= top; ++m) {
+        const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K) : plan_int4(m, N, K);
+        const size_t b = plan_workspace_bytes(p, m, N);
+        if (b > need) need = b;
+    }
+    return need;
+}
+
+w4a8_status w4a8_workspace_init(void* d_ws, size_t bytes, void* stream) {
+    if (!d_ws) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(d_ws, 256)) return W4A8_ERR_WORKSPACE;
+    return hip_status(launch_fill_zero_u32(reinterpret_cast<uint32_t*>(d_ws), (int64_t)(bytes / 4),
+                                           as_stream(stream)));
+}
+
+w4a8_status w4a8_mxfp4_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
+                            const uint8_t* d_w_packed, const uint8_t* d_w_e8m0, uint16_t* d_out,
+                            int64_t M, int64_t N, int64_t K, void* d_ws, size_t ws_bytes,
+                            void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w_packed, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_w_e8m0 || !aligned(d_w_e8m0, 4)) return W4A8_ERR_INVALID_ARG;
+    if (K % 32 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    const GemmPlan p = plan_mxfp4(M, N, K);
+    st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_mxfp4_gemm(p, d_x_fp8, d_x_scale, d_w_packed, d_w_e8m0, d_out, M, N, K,
+                                        d_ws, as_stream(stream)));
+}
+
+w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,
+                                  int64_t K, int32_t* d_qweight_nk, void* stream) {
+    if (!d_qweight_kn || !d_qzeros || !d_qweight_nk) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_qweight_kn, 4) || !aligned(d_qzeros, 4) || !aligned(d_qweight_nk, 4))
+        return W4A8_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    // the first output word serves as the mismatch counter before the transpose
+    uint32_t* counter = reinterpret_cast<uint32_t*>(d_qweight_nk);
+    if (launch_fill_zero_u32(counter, 1, s) != hipSuccess) return W4A8_ERR_HIP;
+    if (launch_int4_check_transpose(nullptr, d_qzeros, N, K, nullptr, counter, s) != hipSuccess)
+        return W4A8_ERR_HIP;
+    uint32_t bad = 0;
+    if (hipMemcpyAsync(&bad, counter, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return W4A8_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return W4A8_ERR_HIP;
+    if (bad) return W4A8_ERR_ASYMMETRIC;
+    return hip_status(launch_int4_check_transpose(d_qweight_kn, nullptr, N, K, d_qweight_nk, nullptr, s));
+}
+
+w4a8_status w4a8_int4g128_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
+                               const int32_t* d_qweight_nk, const uint16_t* d_scales_f16,
+                               uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
+                               size_t ws_bytes, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_qweight_nk, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_scales_f16 || !aligned(d_scales_f16, 8)) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    const GemmPlan p = plan_int4(M, N, K);
+    st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_int4_gemm(p, d_x_fp8, d_x_scale, d_qweight_nk, d_scales_f16, d_out, M,
+                                       N, K, d_ws, as_stream(stream)));
+}
+
+const char* w4a8_status_string(w4a8_status s) {
+    switch (s) {
+        case W4A8_OK: return "ok";
+        case W4A8_ERR_INVALID_ARG: return "invalid argument";
+        case W4A8_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case W4A8_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case W4A8_ERR_ASYMMETRIC: return "int4 zero points are not all 8 (asymmetric)";
+        case W4A8_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* w4a8_version(void) { return "w4a8 0.1.0 gfx950"; }
+
+}  // extern "C"

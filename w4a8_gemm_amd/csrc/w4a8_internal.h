@@ -1,0 +1,103 @@
+// w4a8_internal.h -- shared declarations of libw4a8's kernels and launchers.
+//
+// Device helpers here are the library's own number-format code (bit-level, exact);
+// nothing in this tree is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "w4a8.h"
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------------------
+// exact format conversions
+// ---------------------------------------------------------------------------
+
+// OCP E4M3FN byte -> fp32 (exact; the NaN codes never reach these kernels).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t E = (b >> 3) & 15u, m = b & 7u;
+    const float mag = E ? __uint_as_float(((E + 120u) << 23) | (m << 20))
+                        : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// e2m1 magnitude index 0..7 -> {0, .5, 1, 1.5, 2, 3, 4, 6}: the index placed in
+// the top of the fp32 exponent/mantissa field is that value times 2^-126 (a
+// subnormal for indices 0 and 1), so one exact multiply rebiases it.  Needs fp32
+// denormals preserved (the library is built without flush-to-zero).
+__device__ __forceinline__ float e2m1_mag(uint32_t idx) {
+    return __uint_as_float(idx << 22) * 0x1p126f;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> E4M3FN, round to nearest even, magnitudes at or above 448 saturate to
+// 448 (0x7E), sign bit kept (so -0 and negative values that round to zero give
+// 0x80).  Integer rounding on the fp32 bits for the normal range, an exact
+// scaling plus rint for the subnormal range.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fminf(fabsf(y), 448.0f);
+    uint32_t code;
+    if (a < 0x1p-6f) {
+        code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 is the smallest normal
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        code = (b - (120u << 23) + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+    }
+    return sign | code;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (host side; each returns a hipError_t from the launch)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, float divisor,
+                          int64_t nblocks, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0,
+                          double* stats, hipStream_t stream);
+hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream);
+hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8,
+                            float* xs, hipStream_t stream);
+
+// GEMM plans: the host picks the band, the tile and the K split.
+struct GemmPlan {
+    int band;       // 0 decode (weights streamed, split K), 1 prefill (LDS tiles)
+    int mt;         // decode: 16-wide activation tiles (1..4)
+    int rt;         // decode: 16-row weight tiles per wave
+    int ks;         // decode: K splits (1 = no workspace traffic)
+    int s_per;      // decode: 128-wide K steps per split
+    int64_t tiles;  // decode: row blocks of the weight (one counter each)
+};
+GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K);
+GemmPlan plan_int4(int64_t M, int64_t N, int64_t K);
+size_t plan_workspace_bytes(const GemmPlan& p, int64_t M, int64_t N);
+
+hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* xs,
+                             const uint8_t* wq, const uint8_t* we, uint16_t* out, int64_t M,
+                             int64_t N, int64_t K, void* ws, hipStream_t stream);
+
+hipError_t launch_int4_check_transpose(const int32_t* qw_kn, const int32_t* qzeros, int64_t N,
+                                       int64_t K, int32_t* qw_nk, uint32_t* bad_count,
+                                       hipStream_t stream);
+hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* xs,
+                            const int32_t* qw_nk, const uint16_t* scales, uint16_t* out,
+                            int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
+
+// Split-K workspace layout: counters first (one uint32 per row block, padded to
+// 256 bytes), then fp32 partials [ks][M][N].
+inline size_t ws_counter_bytes(int64_t tiles) {
+    return (size_t)((tiles * 4 + 255) / 256 * 256);
+}
+
+}  // namespace w4a8

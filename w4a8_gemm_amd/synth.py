@@ -178,3 +178,17 @@ def int4(seed: int = 4, N: int = HIDDEN, K: int = INTERMEDIATE) -> dict:
     scales = sc.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
     qzeros = np.full((K // 128, N // 8), 0x77777777, dtype=np.uint32).view(np.int32)
     return dict(qweight_kn=qweight, scales=scales, qzeros=qzeros, N=N, K=K)
+
+
+def mxfp4_random(N: int, K: int, seed, e_lo: int = 120, e_hi: int = 130) -> dict:
+    """MXFP4 weight drawn directly in the encoded domain (for ragged-shape parity
+    cases): uniform 4-bit codes, e8m0 bytes uniform in [e_lo, e_hi]."""
+    g = _gen(seed)
+    codes = torch.randint(0, 16, (N, K), generator=g)
+    e8m0 = torch.randint(e_lo, e_hi + 1, (N, K // 32), generator=g).to(torch.uint8).numpy()
+    return dict(w_packed=pack_nibbles(codes), w_e8m0=e8m0, N=N, K=K)
+
+
+def int4_random(N: int, K: int, seed) -> dict:
+    """int4 g128 weight of any (N % 8 == 0, K % 128 == 0) shape, same recipe as int4()."""
+    return int4.__wrapped__(seed=seed, N=N, K=K)
