@@ -1,0 +1,310 @@
+"""Benchmark of the MXFP4 W4A8 linear layer on one MI355X.
+
+Step (the headline, timed K times after W warm-up steps): one decode pass of
+the merged gate_up projection (N = 2 x 17408, K = 5120, MXFP4 weights
+requantized on the GPU from NVFP4 with one global divisor per partition), for
+each batch M in {1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K]
+activation, then the block-scaled W4A8 GEMM -> bf16 [M, N].  Steps rotate over
+four copies of the weight (379 MB), so no step is served from the 256 MB
+Infinity Cache.  Each step is one HIP graph replay (captured once per weight
+copy), so host launch latency is not in the timed region.
+
+value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
+weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
+read back, token scales, and the bf16 output.
+
+Also reported, each from its own short timed loop (HIP events on the stream the
+kernels run on): per-kernel decode GEMM durations (the roofline figure), the
+prefill GEMM (M = 4096) in TFLOP/s, the full-layer requant in GB/s for the
+three exponent rules, the down_proj decode and the int4 g128 variant.
+cpu_baseline: the CPU oracle timed on a bounded sample of the same step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+METRIC = "W4A8 MXFP4 GEMM: decode HBM GB/s (M≤64), prefill TFLOPS (M=4096); requant GB/s"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+DECODE_MS = (1, 8, 16, 64)
+COPIES = 4
+
+
+def decode_bytes(M, N, K):
+    """Algorithmic bytes of act quant + GEMM at one M."""
+    w = N * K // 2 + N * K // 32
+    act = M * K * 2 + M * K + M * 4          # bf16 read, e4m3 written, scale written
+    gemm_in = M * K + M * 4                  # e4m3 and scales read by the GEMM
+    out = M * N * 2
+    return w + act + gemm_in + out
+
+
+def gemm_bytes(M, N, K):
+    return N * K // 2 + N * K // 32 + M * K + M * 4 + M * N * 2
+
+
+def requant_bytes(rows, K):
+    return rows * (K // 2 + K // 16 + K // 2 + K // 32)
+
+
+class Timer:
+    """Average duration of `fn` (which enqueues work on the current stream),
+    measured with HIP events on that stream around `reps` back-to-back calls."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, reps):
+        t = self.torch
+        s = t.cuda.current_stream()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(s)
+        for i in range(reps):
+            fn(i)
+        b.record(s)
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3   # seconds per call
+
+
+def graph_of(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                   # warm (lazy module loading) outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill/requant/int4 loops")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="weight rows in the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a8_gemm_amd as w4
+    from w4a8_gemm_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    w4.lib()
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+    log = lambda *m: print("[bench]", *m, file=sys.stderr, flush=True)
+
+    # ---------------- inputs (resident in HBM before any timing) ----------------
+    log("generating gate_up NVFP4 (2 x 17408 x 5120)")
+    g = synth.gate_up()
+    N, K = g["N"], g["K"]
+    nv_p = torch.from_numpy(g["nv_packed"]).to(dev)
+    nv_s = torch.from_numpy(g["nv_scale"]).to(dev)
+    wp, we = w4.requant_nvfp4_to_mxfp4(nv_p, nv_s, g["part_rows"], g["part_divisor"],
+                                       mode="mse", row_chunk=4096)
+    copies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(COPIES - 1)]
+    xs_bf16 = {M: torch.from_numpy(synth.acts(M, K, seed=(1, M), spread=10.0).view(np.int16))
+               .view(torch.bfloat16).to(dev) for M in DECODE_MS}
+    x8 = {M: torch.empty((M, K), dtype=torch.uint8, device=dev) for M in DECODE_MS}
+    xsc = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in DECODE_MS}
+    out = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
+    ws = w4.Workspace(max(DECODE_MS), N, K, "mxfp4", dev)
+    torch.cuda.synchronize()
+
+    def step(c):
+        w_p, w_e = copies[c]
+        for M in DECODE_MS:
+            w4.quant_act_fp8_per_token(xs_bf16[M], out=x8[M], scale=xsc[M])
+            w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+
+    graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(COPIES)]
+    step_bytes = sum(decode_bytes(M, N, K) for M in DECODE_MS)
+
+    # ---------------- headline: K steps ----------------
+    for i in range(args.warmup):
+        graphs[i % COPIES].replay()
+    torch.cuda.synchronize()
+    t_step = timer(lambda i: graphs[i % COPIES].replay(), args.steps)
+    value = step_bytes / t_step / 1e9
+    log(f"step {t_step * 1e3:.4f} ms, {value:.1f} GB/s")
+
+    # ---------------- decode GEMM kernel durations (roofline) ----------------
+    per_m = {}
+    R = 4 * COPIES
+    for M in DECODE_MS:
+        def gemms(M=M):
+            for r in range(R):
+                w_p, w_e = copies[r % COPIES]
+                w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+        gg = graph_of(torch, gemms)
+        gg.replay()
+        dt = timer(lambda i: gg.replay(), max(2, args.steps // 4)) / R
+        per_m[M] = dt
+        log(f"decode GEMM M={M}: {dt * 1e6:.2f} us, {gemm_bytes(M, N, K) / dt / 1e9:.1f} GB/s")
+    gemm_total_bytes = sum(gemm_bytes(M, N, K) for M in DECODE_MS)
+    gemm_total_t = sum(per_m.values())
+    achieved = gemm_total_bytes / gemm_total_t / 1e9
+    roofline = {"bound": "hbm", "kernel": "mx_decode_kernel (gate_up, M in {1,8,16,64})",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "per_launch_us": {str(M): round(per_m[M] * 1e6, 3) for M in DECODE_MS},
+                "bytes_per_launch": {str(M): gemm_bytes(M, N, K) for M in DECODE_MS}}
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, copies, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, g, args.cpu_rows, log)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 x e2m1 (e8m0 block scale), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "decode gate_up: merged MXFP4 linear N=2x17408 K=5120 "
+                               "(requantized from NVFP4, per-partition divisors), "
+                               "M in {1,8,16,64}, fp8 per-token act quant + GEMM per M",
+                   "N": N, "K": K, "M": list(DECODE_MS), "weight_copies_rotated": COPIES,
+                   "step_bytes": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, copies, dev):
+    N, K = g["N"], g["K"]
+    res = {}
+    # prefill: M = 4096 against the gate_up weight
+    M = 4096
+    xb = torch.from_numpy(synth.acts(M, K, seed=3).view(np.int16)).view(torch.bfloat16).to(dev)
+    x8, xs = w4.quant_act_fp8_per_token(xb)
+    o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gg = graph_of(torch, lambda: [w4.mxfp4_gemm(x8, xs, copies[r][0], copies[r][1], out=o)
+                                  for r in range(2)])
+    gg.replay()
+    dt = timer(lambda i: gg.replay(), 5) / 2
+    flops = 2.0 * M * N * K
+    res["prefill_gemm"] = {"M": M, "N": N, "K": K, "us": round(dt * 1e6, 2),
+                           "tflops": round(flops / dt / 1e12, 1),
+                           "frac_of_fp8_peak": round(flops / dt / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    log("prefill", res["prefill_gemm"])
+    aq = timer(lambda i: w4.quant_act_fp8_per_token(xb, out=x8, scale=xs), 5)
+    res["act_quant_prefill"] = {"M": M, "K": K, "us": round(aq * 1e6, 2),
+                                "gbps": round((M * K * 3 + M * 4) / aq / 1e9, 1)}
+    del o, xb
+    # full-layer requant, three rules, ROW_CHUNK passes and one pass per partition
+    src = [(nv_p, nv_s), (nv_p.clone(), nv_s.clone())]
+    outs = [(torch.empty_like(copies[0][0]), torch.empty_like(copies[0][1])) for _ in range(2)]
+    rq = {}
+    for mode in ("ocp", "noclip", "mse"):
+        for chunk in (4096, 0):
+            def run(i, mode=mode, chunk=chunk):
+                p, s = src[i % 2]
+                op, oe = outs[i % 2]
+                w4.requant_nvfp4_to_mxfp4(p, s, g["part_rows"], g["part_divisor"], mode=mode,
+                                          row_chunk=chunk, out_packed=op, out_e8m0=oe)
+            rg = [graph_of(torch, lambda i=i: run(i)) for i in range(2)]
+            dt = timer(lambda i: rg[i % 2].replay(), 6)
+            rq[f"{mode}_chunk{chunk}"] = {"us": round(dt * 1e6, 1),
+                                          "gbps": round(requant_bytes(N, K) / dt / 1e9, 1)}
+    res["requant_full_layer"] = rq
+    log("requant", rq)
+    del src, outs
+    # down_proj decode
+    d = synth.down_proj()
+    dcopies = [(torch.from_numpy(d["w_packed"]).to(dev), torch.from_numpy(d["w_e8m0"]).to(dev))
+               for _ in range(8)]
+    dws = w4.Workspace(64, d["N"], d["K"], "mxfp4", dev)
+    dp = {}
+    for M in (1, 16, 64):
+        xb = torch.from_numpy(synth.acts(M, d["K"], seed=(2, M)).view(np.int16)).view(torch.bfloat16).to(dev)
+        a8, asc = w4.quant_act_fp8_per_token(xb)
+        oo = torch.empty((M, d["N"]), dtype=torch.bfloat16, device=dev)
+        gg = graph_of(torch, lambda: [w4.mxfp4_gemm(a8, asc, dcopies[r][0], dcopies[r][1], out=oo,
+                                                    workspace=dws) for r in range(8)])
+        gg.replay()
+        dt = timer(lambda i: gg.replay(), 10) / 8
+        b = gemm_bytes(M, d["N"], d["K"])
+        dp[str(M)] = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+                      "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    res["down_proj_decode"] = dp
+    log("down_proj", dp)
+    del dcopies
+    # int4 g128
+    q = synth.int4()
+    qnk = w4.int4g128_prepare(torch.from_numpy(q["qweight_kn"]).to(dev),
+                              torch.from_numpy(q["qzeros"]).to(dev))
+    sc = torch.from_numpy(q["scales"].view(np.int16)).view(torch.float16).to(dev)
+    qcopies = [(qnk, sc)] + [(qnk.clone(), sc.clone()) for _ in range(7)]
+    iws = w4.Workspace(64, q["N"], q["K"], "int4", dev)
+    i4 = {}
+    for M in (1, 64, 2048):
+        xb = torch.from_numpy(synth.acts(M, q["K"], seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)
+        a8, asc = w4.quant_act_fp8_per_token(xb)
+        oo = torch.empty((M, q["N"]), dtype=torch.bfloat16, device=dev)
+        reps = 8 if M <= 64 else 2
+        gg = graph_of(torch, lambda: [w4.int4g128_gemm(a8, asc, qcopies[r][0], qcopies[r][1], out=oo,
+                                                       workspace=iws) for r in range(reps)])
+        gg.replay()
+        dt = timer(lambda i: gg.replay(), 10) / reps
+        b = q["N"] * q["K"] // 2 + q["N"] * q["K"] // 64 + M * q["K"] + M * 4 + M * q["N"] * 2
+        ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1)}
+        if M > 64:
+            ent["tflops"] = round(2.0 * M * q["N"] * q["K"] / dt / 1e12, 1)
+        i4[str(M)] = ent
+    res["int4_g128"] = i4
+    log("int4", i4)
+    return res
+
+
+def cpu_baseline(synth, g, rows, log):
+    """The CPU oracle (as it stands) on a sample of the headline step: the same
+    activations for M in {1, 8, 16, 64}, against the first `rows` weight rows."""
+    import oracle
+    N, K = g["N"], g["K"]
+    rows = min(rows, N)
+    half = rows // 2
+    sel = np.r_[0:half, N // 2:N // 2 + rows - half]
+    mp, me, _ = oracle.requant_nvfp4_to_mxfp4(g["nv_packed"][sel], g["nv_scale"][sel],
+                                              [half, rows - half], g["part_divisor"], mode="mse")
+    xs = {M: synth.acts(M, K, seed=(1, M), spread=10.0) for M in DECODE_MS}
+    t0 = time.perf_counter()
+    for M in DECODE_MS:
+        a8, s = oracle.quant_act_fp8(xs[M])
+        oracle.mxfp4_gemm(a8, s, mp, me)
+    dt = time.perf_counter() - t0
+    b = sum(decode_bytes(M, rows, K) for M in DECODE_MS)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    res = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 2),
+           "sample": f"headline step on {rows} of {N} weight rows (both partitions), "
+                     "M in {1,8,16,64}: oracle fp8 act quant + fp64 GEMM reference"}
+    log("cpu baseline", res)
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -67,7 +67,11 @@ typedef enum {
 typedef enum { W4A8_EXP_OCP = 0, W4A8_EXP_NOCLIP = 1, W4A8_EXP_MSE = 2 } w4a8_exp_mode;
 
 /* Weight formats accepted by the GEMMs (for workspace sizing). */
-typedef enum { W4A8_WEIGHT_MXFP4 = 0, W4A8_WEIGHT_INT4G128 = 1 } w4a8_weight_kind;
+typedef enum {
+    W4A8_WEIGHT_MXFP4 = 0,           /* [N, K/2] codes + [N, K/32] e8m0 */
+    W4A8_WEIGHT_INT4G128 = 1,        /* [N, K/8] int32 (w4a8_int4g128_prepare) + fp16 scales */
+    W4A8_WEIGHT_MXFP4_PREPARED = 2   /* fragment order (w4a8_mxfp4_prepare) */
+} w4a8_weight_kind;
 
 /* ---------------------------------------------------------------------------
  * NVFP4 -> MXFP4 requantization of one linear layer.
@@ -128,12 +132,12 @@ w4a8_status w4a8_quant_act_fp8_per_token(
     uint8_t *d_x_fp8, float *d_x_scale, void *stream);
 
 /* ---------------------------------------------------------------------------
- * GEMM workspace.  The decode band splits K across workgroups; the partial sums
- * and one counter per output tile live in a caller-owned workspace.  The
- * counters must be zero before first use (w4a8_workspace_init) and are left at
- * zero by every GEMM call ("radiance_autoround.py": the split-K scratch is
- * registered once, before any launch, because allocating inside a captured
- * graph is illegal).
+ * GEMM workspace.  The decode band may split K across workgroups; the fp32
+ * partial sums live in a caller-owned workspace, reduced in split order by a
+ * second kernel on the same stream ("radiance_autoround.py": the split-K
+ * scratch is registered once, before any launch, because allocating inside a
+ * captured graph is illegal).  The library keeps no state in it between calls;
+ * w4a8_workspace_init (zero fill) is optional.
  *
  * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
  * N, K and kind and any M <= M_max (0 if no split is used).  Pure host
@@ -171,6 +175,34 @@ w4a8_status w4a8_mxfp4_gemm(
     int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * MXFP4 weights in matrix-core fragment order (load time) and the GEMM on them.
+ * Source: "vllm-radiance (MXFP4)", How the MXFP4 path works: the W4A8 kernel
+ * consumes weights repacked at load time into the order of its matrix
+ * instructions.  Here the order is that of the gfx950 16x16x128 block-scaled
+ * MFMA with the weight as its e2m1 operand: per 16-row tile and 128-wide K step
+ * one 1 KiB block (lane L = n + 16g holds row 16t+n, packed bytes 64s+16g..+16),
+ * tiles major; e8m0 as one 256-byte block per tile and 4-step chunk (lane L's
+ * dword byte u = e8m0 of row 16t+n, K-block 4(4c+u)+g).  Rows are padded to a
+ * multiple of 16 and steps to a multiple of 4 (zero codes, e8m0 127).  The GEMM
+ * result is identical in value to w4a8_mxfp4_gemm on the plain layout (same
+ * products, fp32 accumulation; summation order may differ).
+ *   w4a8_mxfp4_prepared_bytes: sizes of the two prepared buffers (host).
+ *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
+ *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
+ *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, for
+ *     1 <= M <= 32 (the decode band; larger M: UNSUPPORTED_SHAPE); workspace
+ *     sized with W4A8_WEIGHT_MXFP4_PREPARED.
+ * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
+ * WORKSPACE, HIP. */
+w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
+w4a8_status w4a8_mxfp4_prepare(const uint8_t *d_w_packed, const uint8_t *d_w_e8m0, int64_t N,
+                               int64_t K, uint8_t *d_w_prepared, uint8_t *d_s_prepared, void *stream);
+w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x_scale,
+                                     const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
+                                     uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
+                                     size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * int4 group-128 symmetric (AutoGPTQ layout), load-time preparation.
  * Source: "radiance_autoround.py", module docstring and
  * AutoRoundLinearMethod.process_weights_after_loading: every qzeros word must
@@ -200,6 +232,26 @@ w4a8_status w4a8_int4g128_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const int32_t *d_qweight_nk, const uint16_t *d_scales_f16, uint16_t *d_out,
     int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode band with an explicit plan, for tile-size sweeps (the two GEMM entry
+ * points above pick these parameters themselves).  Computes exactly what
+ * w4a8_mxfp4_gemm (kind MXFP4: d_w = packed codes, d_w_scale = e8m0) or
+ * w4a8_int4g128_gemm (kind INT4G128: d_w = qweight [N, K/8], d_w_scale = fp16
+ * scales) computes, for 1 <= M <= 64, with
+ *   rt  16-row weight tiles per wavefront (1, 2 or 4; 4 waves per workgroup),
+ *   u   128-wide K steps per prefetched chunk (1, 2 or 4; 1 if K % 128 != 0),
+ *   ks  requested K splits (>= 1; rounded so each split holds whole chunks).
+ * Kind MXFP4_PREPARED (prepared weights, M <= 32): rt must be 0, u is the
+ * prefetch depth in 512-wide chunks (3 or 4), ks an upper bound on the K splits.
+ * w4a8_decode_plan_workspace_bytes: workspace for that plan (0 = none needed, or
+ * invalid arguments; rt = 0 selects the prepared-weight plan).  Errors as the
+ * GEMMs, INVALID_ARG for a bad plan. */
+size_t      w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt, int u, int ks);
+w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t *d_x_fp8,
+                                  const float *d_x_scale, const void *d_w, const void *d_w_scale,
+                                  uint16_t *d_out, int64_t M, int64_t N, int64_t K, int rt, int u,
+                                  int ks, void *d_ws, size_t ws_bytes, void *stream);
 
 /* Static strings; never NULL. */
 const char *w4a8_status_string(w4a8_status s);

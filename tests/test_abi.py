@@ -116,3 +116,35 @@ def test_workspace_bytes_contract(L):
         assert cur >= prev
         prev = cur
     assert wb(4096, 5120, 17408, 0) == wb(64, 5120, 17408, 0)
+
+
+def test_binding_rejects_mismatched_weight_sizes(L):
+    """The ABI takes raw pointers, so the binding checks tensor sizes against
+    N and K before a call (a flat prepared buffer must not be read as rows)."""
+    from w4a8_gemm_amd import binding
+
+    class Shape:
+        def __init__(self, *shape):
+            self.shape = shape
+
+        def numel(self):
+            n = 1
+            for d in self.shape:
+                n *= d
+            return n
+
+        def element_size(self):
+            return 1
+
+    N, K = 34816, 5120
+    wb, sb = binding._size(), binding._size()
+    assert binding.lib().w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)) == OK
+    w, s = Shape(wb.value), Shape(sb.value)
+    binding._check_weight_sizes("prepared", w, s, N, K)
+    with pytest.raises(ValueError):
+        binding._check_weight_sizes("prepared", w, s, wb.value, K)
+    binding._check_weight_sizes("mxfp4", Shape(N, K // 2), Shape(N, K // 32), N, K)
+    with pytest.raises(ValueError):
+        binding._check_weight_sizes("mxfp4", Shape(N, K // 2), Shape(N, K // 16), N, K)
+    with pytest.raises(ValueError):
+        binding._check_weight_sizes("int4", Shape(N, K // 8), Shape(N, K // 128), N, K)

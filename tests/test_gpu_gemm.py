@@ -188,3 +188,82 @@ def test_int4_prepare_rejects_asymmetric_zeros():
     say("int4 prepare asymmetric")
     with pytest.raises(ValueError):
         w4.int4g128_prepare(dev_i32(q["qweight_kn"]), dev_i32(qz))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 weights in fragment order (prepared) -- decode band
+# ---------------------------------------------------------------------------
+
+def _unprepare(wt, st, N, K):
+    """Invert the documented fragment order on the host (layout check)."""
+    tiles, steps = (N + 15) // 16, K // 128
+    c_pad = (steps + 3) // 4
+    w = wt.reshape(tiles, 4 * c_pad, 4, 16, 16)          # t, s, g, n, 16 bytes
+    w = w.transpose(0, 3, 1, 2, 4).reshape(tiles * 16, 4 * c_pad * 64)[:N, : K // 2]
+    sc = st.reshape(tiles, c_pad, 4, 16, 4)              # t, c, g, n, u
+    sc = sc.transpose(0, 3, 1, 4, 2).reshape(tiles * 16, c_pad * 16)[:N, : K // 32]
+    return w, sc
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (100, 640), (5120, 17408), (34816, 5120)])
+def test_prepare_layout_round_trip(N, K):
+    w = synth.mxfp4_random(N, K, seed=(N, K))
+    say("prepare", (N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    torch.cuda.synchronize()
+    wt, st = pw.w.cpu().numpy(), pw.s.cpu().numpy()
+    back_w, back_s = _unprepare(wt, st, N, K)
+    assert np.array_equal(back_w, w["w_packed"]) and np.array_equal(back_s, w["w_e8m0"])
+    # padding rows / steps: zero codes, e8m0 127
+    tiles, c_pad = (N + 15) // 16, (K // 128 + 3) // 4
+    full_w = wt.reshape(tiles, 4 * c_pad, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(tiles * 16, -1)
+    assert (full_w[N:] == 0).all() and (full_w[:, K // 2:] == 0).all()
+    full_s = st.reshape(tiles, c_pad, 4, 16, 4).transpose(0, 3, 1, 4, 2).reshape(tiles * 16, -1)
+    assert (full_s[N:] == 127).all() and (full_s[:, K // 32:] == 127).all()
+
+
+PREPARED = [(1, 64, 128), (1, 300, 640), (3, 100, 1152), (8, 257, 1024), (16, 1000, 4096),
+            (17, 130, 512), (32, 512, 2048), (1, 6000, 2560)]
+
+
+@pytest.mark.parametrize("M,N,K", PREPARED)
+def test_mxfp4_prepared_ragged(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 1))
+    x8, s = _acts(M, K, (M, K, 1), spread=10.0)
+    say("prepared gemm", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"])
+    err = rel_frobenius(got, ref)
+    assert err <= GEMM_REL_F, err
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_mxfp4_prepared_gate_up(gate_up_mx, M):
+    x8, s = _acts(M, synth.HIDDEN, (1, M), spread=10.0)
+    wp, we = gate_up_mx[:2]
+    pw = w4.mxfp4_prepare(dev_u8(wp), dev_u8(we))
+    say("prepared gate_up", M)
+    dx, ds = dev_u8(x8), dev_f32(s)
+    o1 = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    o2 = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(o1, o2)
+    g = np.random.default_rng(M)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
+    ni = np.concatenate([g.integers(0, wp.shape[0], M), g.integers(0, wp.shape[0], 4096)])
+    ref = oracle.mxfp4_gemm(x8, s, wp, we, mi=mi, ni=ni)
+    assert rel_frobenius(o1[mi, ni], ref) <= GEMM_REL_F
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_mxfp4_prepared_down_proj(M):
+    d = synth.down_proj()
+    x8, s = _acts(M, synth.INTERMEDIATE, (2, M))
+    pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
+    say("prepared down_proj", M)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(M + 7)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
+    ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
+    ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
+    assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F

@@ -17,13 +17,15 @@ __all__ = [
     "LIB_PATH", "lib", "version", "status_string", "EXP_MODES", "W4A8Error",
     "requant_nvfp4_to_mxfp4", "quant_act_fp8_per_token", "gemm_workspace_bytes",
     "Workspace", "mxfp4_gemm", "int4g128_prepare", "int4g128_gemm", "w4a8_linear",
+    "decode_with_plan", "PreparedMXFP4", "mxfp4_prepare", "mxfp4_gemm_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_SHAPE, ERR_WORKSPACE, ERR_ASYMMETRIC, ERR_HIP = range(6)
 EXP_MODES = {"ocp": 0, "noclip": 1, "mse": 2}
-WEIGHT_MXFP4, WEIGHT_INT4G128 = 0, 1
+WEIGHT_MXFP4, WEIGHT_INT4G128, WEIGHT_MXFP4_PREPARED = 0, 1, 2
+_KINDS = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128, "prepared": WEIGHT_MXFP4_PREPARED}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -55,6 +57,17 @@ def lib() -> ctypes.CDLL:
         L.w4a8_mxfp4_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_int4g128_prepare.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
         L.w4a8_int4g128_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_decode_plan_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int]
+        L.w4a8_decode_plan_workspace_bytes.restype = _size
+        L.w4a8_decode_with_plan.argtypes = [_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
+                                            _int, _int, _vp, _size, _vp]
+        L.w4a8_decode_with_plan.restype = _int
+        L.w4a8_mxfp4_prepared_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_size), ctypes.POINTER(_size)]
+        L.w4a8_mxfp4_prepared_bytes.restype = _int
+        L.w4a8_mxfp4_prepare.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
+        L.w4a8_mxfp4_prepare.restype = _int
+        L.w4a8_mxfp4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_mxfp4_gemm_prepared.restype = _int
         L.w4a8_status_string.argtypes = [_int]
         L.w4a8_status_string.restype = ctypes.c_char_p
         L.w4a8_version.argtypes = []
@@ -173,8 +186,7 @@ def quant_act_fp8_per_token(x: torch.Tensor, out: torch.Tensor | None = None,
 
 
 def gemm_workspace_bytes(M_max: int, N: int, K: int, kind: str = "mxfp4") -> int:
-    k = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128}[kind]
-    return int(lib().w4a8_gemm_workspace_bytes(int(M_max), int(N), int(K), k))
+    return int(lib().w4a8_gemm_workspace_bytes(int(M_max), int(N), int(K), _KINDS[kind]))
 
 
 class Workspace:
@@ -270,6 +282,94 @@ def int4g128_gemm(x_fp8: torch.Tensor, x_scale: torch.Tensor, qweight_nk: torch.
     status = lib().w4a8_int4g128_gemm(_ptr(x_fp8), _ptr(x_scale), _ptr(qweight_nk), _ptr(scales),
                                       _ptr(out), M, N, K, wp, wn, _stream(x_fp8))
     _check(status, "w4a8_int4g128_gemm")
+    return out
+
+
+def _check_weight_sizes(kind, w, w_scale, N, K):
+    """The C ABI takes raw pointers: make sure the tensors really hold [N, K] weights."""
+    if kind == "mxfp4":
+        ok = tuple(w.shape) == (N, K // 2) and tuple(w_scale.shape) == (N, K // 32)
+    elif kind == "int4":
+        ok = tuple(w.shape) == (N, K // 8) and tuple(w_scale.shape) == (K // 128, N)
+    else:
+        wb, sb = _size(), _size()
+        _check(lib().w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)),
+               "w4a8_mxfp4_prepared_bytes")
+        ok = (w.numel() * w.element_size() == wb.value and
+              w_scale.numel() * w_scale.element_size() == sb.value)
+    if not ok:
+        raise ValueError(f"{kind} weight tensors do not match N={N}, K={K}")
+
+
+def decode_with_plan(x_fp8, x_scale, w, w_scale, rt: int, u: int, ks: int, kind: str = "mxfp4",
+                     out=None, workspace=None, N: int | None = None):
+    """Decode-band GEMM (M <= 64) with an explicit plan (for tile sweeps): rt 16-row
+    weight tiles per wave, u 128-wide K steps per chunk, ks requested K splits
+    (kind "prepared": rt 0, u the prefetch depth, N required).  `workspace` is a
+    uint8 cuda tensor of at least the plan's workspace bytes."""
+    M, K = x_fp8.shape
+    if N is None:
+        if kind == "prepared":
+            raise ValueError("prepared weights need N")
+        N = w.shape[0]
+    _check_weight_sizes(kind, w, w_scale, int(N), int(K))
+    dev = x_fp8.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    need = int(lib().w4a8_decode_plan_workspace_bytes(M, N, K, rt, u, ks))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=dev)
+    status = lib().w4a8_decode_with_plan(_KINDS[kind], _ptr(x_fp8), _ptr(x_scale), _ptr(w), _ptr(w_scale),
+                                         _ptr(out), M, N, K, rt, u, ks, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(),
+                                         _stream(x_fp8))
+    _check(status, "w4a8_decode_with_plan")
+    return out
+
+
+class PreparedMXFP4:
+    """MXFP4 weight of one linear in matrix-core fragment order (w4a8_mxfp4_prepare)."""
+
+    def __init__(self, w: torch.Tensor, s: torch.Tensor, N: int, K: int):
+        self.w, self.s, self.N, self.K = w, s, int(N), int(K)
+
+
+def mxfp4_prepare(w_packed: torch.Tensor, w_e8m0: torch.Tensor) -> PreparedMXFP4:
+    """[N, K/2] codes + [N, K/32] e8m0 -> PreparedMXFP4 (K % 128 == 0)."""
+    _need(w_packed, "w_packed", torch.uint8)
+    dev = w_packed.device
+    _need(w_e8m0, "w_e8m0", torch.uint8, dev)
+    N, K = w_packed.shape[0], 2 * w_packed.shape[1]
+    if tuple(w_e8m0.shape) != (N, K // 32):
+        raise ValueError("w_e8m0 must be [N, K/32]")
+    wb, sb = _size(), _size()
+    _check(lib().w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)),
+           "w4a8_mxfp4_prepared_bytes")
+    wt = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+    st = torch.empty(sb.value, dtype=torch.uint8, device=dev)
+    _check(lib().w4a8_mxfp4_prepare(_ptr(w_packed), _ptr(w_e8m0), N, K, _ptr(wt), _ptr(st),
+                                    _stream(w_packed)), "w4a8_mxfp4_prepare")
+    return PreparedMXFP4(wt, st, N, K)
+
+
+def mxfp4_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedMXFP4,
+                        out: torch.Tensor | None = None,
+                        workspace: Workspace | None = None) -> torch.Tensor:
+    """As mxfp4_gemm, on prepared weights (decode band, M <= 32)."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    M, K = x_fp8.shape
+    if K != w.K:
+        raise ValueError(f"activation K {K} != weight K {w.K}")
+    _check_weight_sizes("prepared", w.w, w.s, w.N, w.K)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, w.N, K, "prepared", dev)
+    status = lib().w4a8_mxfp4_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
+                                            _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
+    _check(status, "w4a8_mxfp4_gemm_prepared")
     return out
 
 

@@ -94,11 +94,15 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     if (M_max < 1 || N < 1 || K < 32 || M_max > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
     if (kind == W4A8_WEIGHT_MXFP4 && K % 32 != 0) return 0;
     if (kind == W4A8_WEIGHT_INT4G128 && (K % 128 != 0 || N % 8 != 0)) return 0;
-    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128) return 0;
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED && K % 128 != 0) return 0;
+    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED)
+        return 0;
     size_t need = 0;
     const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
     for (int64_t m = 1; m <= top; ++m) {
-        const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K) : plan_int4(m, N, K);
+        const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K)
+                           : kind == W4A8_WEIGHT_INT4G128 ? plan_int4(m, N, K)
+                           : (m <= kPreparedDecodeMaxM ? plan_prepared(m, N, K, 0, 4) : plan_mxfp4(m, N, K));
         const size_t b = plan_workspace_bytes(p, m, N);
         if (b > need) need = b;
     }
@@ -125,6 +129,42 @@ w4a8_status w4a8_mxfp4_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (st != W4A8_OK) return st;
     return hip_status(launch_mxfp4_gemm(p, d_x_fp8, d_x_scale, d_w_packed, d_w_e8m0, d_out, M, N, K,
                                         d_ws, as_stream(stream)));
+}
+
+w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t* h_w_bytes, size_t* h_s_bytes) {
+    if (!h_w_bytes || !h_s_bytes) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    prepared_sizes(N, K, h_w_bytes, h_s_bytes);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_mxfp4_prepare(const uint8_t* d_w_packed, const uint8_t* d_w_e8m0, int64_t N,
+                               int64_t K, uint8_t* d_w_prepared, uint8_t* d_s_prepared,
+                               void* stream) {
+    if (!d_w_packed || !d_w_e8m0 || !d_w_prepared || !d_s_prepared) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_w_packed, 16) || !aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 4))
+        return W4A8_ERR_INVALID_ARG;
+    return hip_status(launch_prepare(d_w_packed, d_w_e8m0, N, K, d_w_prepared, d_s_prepared,
+                                     as_stream(stream)));
+}
+
+w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                     const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
+                                     uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
+                                     size_t ws_bytes, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w_prepared, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_s_prepared || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (M > kPreparedDecodeMaxM) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    const GemmPlan p = plan_prepared(M, N, K, 0, 4);
+    st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared,
+                                             d_out, M, N, K, d_ws, as_stream(stream)));
 }
 
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,
@@ -161,6 +201,58 @@ w4a8_status w4a8_int4g128_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (st != W4A8_OK) return st;
     return hip_status(launch_int4_gemm(p, d_x_fp8, d_x_scale, d_qweight_nk, d_scales_f16, d_out, M,
                                        N, K, d_ws, as_stream(stream)));
+}
+
+// ---- decode band with an explicit plan (tile-size sweeps) ----
+
+size_t w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt, int u, int ks) {
+    if (M < 1 || M > kDecodeMaxM || N < 1 || K < 32 || N > kMaxDim || K > kMaxDim) return 0;
+    if (rt == 0) {   // prepared weights: u = ring depth
+        if (M > kPreparedDecodeMaxM || K % 128 != 0 || (u != 3 && u != 4) || ks < 1) return 0;
+        return plan_workspace_bytes(plan_prepared(M, N, K, ks, u), M, N);
+    }
+    if ((rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1) return 0;
+    return plan_workspace_bytes(make_decode_plan(M, N, K, rt, u, ks), M, N);
+}
+
+w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
+                                  const float* d_x_scale, const void* d_w, const void* d_w_scale,
+                                  uint16_t* d_out, int64_t M, int64_t N, int64_t K, int rt, int u,
+                                  int ks, void* d_ws, size_t ws_bytes, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
+        if (!d_w_scale || !aligned(d_w_scale, 4) || M > kPreparedDecodeMaxM || (u != 3 && u != 4) || ks < 1)
+            return W4A8_ERR_INVALID_ARG;
+        if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+        const GemmPlan p = plan_prepared(M, N, K, ks, u);
+        st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,
+                                                 (const uint8_t*)d_w_scale, d_out, M, N, K, d_ws,
+                                                 as_stream(stream)));
+    }
+    if (M > kDecodeMaxM || (rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1)
+        return W4A8_ERR_INVALID_ARG;
+    if (kind == W4A8_WEIGHT_MXFP4) {
+        if (!d_w_scale || !aligned(d_w_scale, 4)) return W4A8_ERR_INVALID_ARG;
+        if (K % 32 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    } else if (kind == W4A8_WEIGHT_INT4G128) {
+        if (!d_w_scale || !aligned(d_w_scale, 8)) return W4A8_ERR_INVALID_ARG;
+        if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    } else {
+        return W4A8_ERR_INVALID_ARG;
+    }
+    const GemmPlan p = make_decode_plan(M, N, K, rt, u, ks);
+    st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    if (kind == W4A8_WEIGHT_MXFP4)
+        return hip_status(launch_mxfp4_gemm(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,
+                                            (const uint8_t*)d_w_scale, d_out, M, N, K, d_ws,
+                                            as_stream(stream)));
+    return hip_status(launch_int4_gemm(p, d_x_fp8, d_x_scale, (const int32_t*)d_w,
+                                       (const uint16_t*)d_w_scale, d_out, M, N, K, d_ws,
+                                       as_stream(stream)));
 }
 
 const char* w4a8_status_string(w4a8_status s) {

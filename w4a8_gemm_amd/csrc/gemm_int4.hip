@@ -98,11 +98,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// decode band (M <= 64): as the MXFP4 decode kernel, one 128-group per MFMA.
-// Weight lane (n, g) holds k = 32g .. 32g+31 of the group (16 bytes of codes,
-// expanded to 32 e4m3 bytes), and the activation lane (m, g) the same 32
-// activation bytes: the fp8 operand's byte j < 16 sits at MFMA slot 16g + j and
-// byte 16 + j at slot 64 + 16g + j, identically for both operands.
+// decode band (M <= 64): as the MXFP4 decode kernel, one 128-group per MFMA
+// and U groups per prefetched chunk.  Weight lane (n, g) holds k = 32g .. 32g+31
+// of the group (16 bytes of codes at 64G + 16g, so a load instruction reads 64
+// contiguous bytes of 16 rows), expanded to 32 e4m3 bytes; the activation lane
+// (m, g) holds the same 32 activation bytes (the fp8 operand's byte j < 16 sits
+// at MFMA slot 16g + j and byte 16 + j at slot 64 + 16g + j, identically for
+// both operands).  The lane's four output rows n0..n0+3 take their group scales
+// from one 8-byte load.  Split K goes through fp32 partials and the shared
+// reduction kernel.
 // ---------------------------------------------------------------------------
 
 constexpr int kDecThreads = 256;
@@ -113,62 +117,71 @@ struct I4DecArgs {
     const int32_t* qw;
     const uint16_t* sc;
     uint16_t* out;
-    uint32_t* counters;
     float* partials;
     int M, N, K;
     int ks, s_per, tiles;
 };
 
-template <int MT, int RT>
-__device__ __forceinline__ void i4_group(const I4DecArgs& a, int lane, const int* rows, int row0,
-                                         int grp, const uint4* wq, v4f (&acc)[RT][MT]) {
+template <int MT, int RT, int U>
+struct I4Chunk {
+    uint4 w[RT][U];
+    uint2 s[RT][U];
+    uint4 x[MT][U][2];
+};
+
+template <int MT, int RT, int U>
+__device__ __forceinline__ void i4_load(const I4DecArgs& a, int lane, const int* rows, int row0,
+                                        int grp, I4Chunk<MT, RT, U>& c) {
     const int g = lane >> 4;
-    v8i bx[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-        if (m < a.M) {
-            const uint8_t* p = a.x8 + (int64_t)m * a.K + 128 * (int64_t)grp + 32 * g;
-            lo = *reinterpret_cast<const uint4*>(p);
-            hi = *reinterpret_cast<const uint4*>(p + 16);
-        }
-        v8i f = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bx[mt] = f;
-    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const v8i aw = int4x32_frag(wq[rt]);
-        // group scales of this lane's four output rows n0..n0+3
-        const int n0 = row0 + rt * 16 + 4 * g;
-        float s[4];
-        if (n0 + 3 < a.N && (a.N & 3) == 0) {
-            const uint2 h = *reinterpret_cast<const uint2*>(a.sc + (int64_t)grp * a.N + n0);
-            s[0] = f16_to_f32(h.x & 0xFFFFu);
-            s[1] = f16_to_f32(h.x >> 16);
-            s[2] = f16_to_f32(h.y & 0xFFFFu);
-            s[3] = f16_to_f32(h.y >> 16);
-        } else {
+        const int32_t* wr = a.qw + (int64_t)rows[rt] * (a.K >> 3) + 16 * (int64_t)grp + 4 * g;
+        const int n0 = min(row0 + rt * 16 + 4 * g, a.N - 4);   // N % 8 == 0, so n0..n0+3 in range
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s[r] = f16_to_f32(a.sc[(int64_t)grp * a.N + min(n0 + r, a.N - 1)]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const v4f t = mfma16_f8(aw, bx[mt], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rt][mt][r] = __builtin_fmaf(s[r], t[r], acc[rt][mt][r]);
+        for (int u = 0; u < U; ++u) {
+            c.w[rt][u] = *reinterpret_cast<const uint4*>(wr + 16 * u);
+            c.s[rt][u] = *reinterpret_cast<const uint2*>(a.sc + (int64_t)(grp + u) * a.N + n0);
         }
     }
-    (void)rows;
+    // columns m >= M load row M-1 (never stored): unconditional loads
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = min(mt * 16 + (lane & 15), a.M - 1);
+        const uint8_t* xr = a.x8 + (int64_t)m * a.K + 128 * (int64_t)grp + 32 * g;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c.x[mt][u][0] = *reinterpret_cast<const uint4*>(xr + 128 * u);
+            c.x[mt][u][1] = *reinterpret_cast<const uint4*>(xr + 128 * u + 16);
+        }
+    }
 }
 
-template <int MT, int RT>
+template <int MT, int RT, int U>
+__device__ __forceinline__ void i4_compute(const I4Chunk<MT, RT, U>& c, v4f (&acc)[RT][MT]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const v8i aw = int4x32_frag(c.w[rt][u]);
+            const float s[4] = {f16_to_f32(c.s[rt][u].x & 0xFFFFu), f16_to_f32(c.s[rt][u].x >> 16),
+                                f16_to_f32(c.s[rt][u].y & 0xFFFFu), f16_to_f32(c.s[rt][u].y >> 16)};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const v8i bx = {(int)c.x[mt][u][0].x, (int)c.x[mt][u][0].y, (int)c.x[mt][u][0].z,
+                                (int)c.x[mt][u][0].w, (int)c.x[mt][u][1].x, (int)c.x[mt][u][1].y,
+                                (int)c.x[mt][u][1].z, (int)c.x[mt][u][1].w};
+                const v4f t = mfma16_f8(aw, bx, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[rt][mt][r] = __builtin_fmaf(s[r], t[r], acc[rt][mt][r]);
+            }
+        }
+    }
+}
+
+template <int MT, int RT, int U>
 __global__ __launch_bounds__(kDecThreads) void i4_decode_kernel(I4DecArgs a) {
-    const int b = blockIdx.x;
-    const int xcd = b & 7, li = b >> 3;
-    const int split = li % a.ks;
-    const int tile = (li / a.ks) * 8 + xcd;
-    if (tile >= a.tiles) return;
+    const int tile = blockIdx.x % a.tiles;
+    const int split = blockIdx.x / a.tiles;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int row0 = tile * (4 * RT * 16) + wave * (RT * 16);
@@ -185,109 +198,60 @@ __global__ __launch_bounds__(kDecThreads) void i4_decode_kernel(I4DecArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t rowwords = a.K >> 3;
-    uint4 cur[RT];
-    if (s0 < s1) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            cur[rt] = *reinterpret_cast<const uint4*>(a.qw + (int64_t)rows[rt] * rowwords + 16 * (int64_t)s0 + 4 * g);
+    int grp = s0;
+    const int nchunks = s1 > s0 ? (s1 - s0) / U : 0;
+    if (nchunks > 0) {   // two register sets in turn, loads fenced from the MFMAs
+        I4Chunk<MT, RT, U> ca, cb;
+        i4_load<MT, RT, U>(a, lane, rows, row0, s0, ca);
+        int c = 1;
+        for (; c + 1 < nchunks; c += 2) {
+            i4_load<MT, RT, U>(a, lane, rows, row0, s0 + c * U, cb);
+            __builtin_amdgcn_sched_barrier(0);
+            i4_compute<MT, RT, U>(ca, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            i4_load<MT, RT, U>(a, lane, rows, row0, s0 + (c + 1) * U, ca);
+            __builtin_amdgcn_sched_barrier(0);
+            i4_compute<MT, RT, U>(cb, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c < nchunks) {
+            i4_load<MT, RT, U>(a, lane, rows, row0, s0 + c * U, cb);
+            __builtin_amdgcn_sched_barrier(0);
+            i4_compute<MT, RT, U>(ca, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            i4_compute<MT, RT, U>(cb, acc);
+        } else {
+            i4_compute<MT, RT, U>(ca, acc);
+        }
+        grp = s0 + nchunks * U;
     }
-    for (int grp = s0; grp < s1; ++grp) {
-        uint4 nxt[RT];
-        const bool more = grp + 1 < s1;
-        if (more) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                nxt[rt] = *reinterpret_cast<const uint4*>(a.qw + (int64_t)rows[rt] * rowwords + 16 * (int64_t)(grp + 1) + 4 * g);
-        }
-        i4_group<MT, RT>(a, lane, rows, row0, grp, cur, acc);
-        if (more) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) cur[rt] = nxt[rt];
-        }
+    for (; grp < s1; ++grp) {
+        I4Chunk<MT, RT, 1> one;
+        i4_load<MT, RT, 1>(a, lane, rows, row0, grp, one);
+        i4_compute<MT, RT, 1>(one, acc);
     }
 
-    if (a.ks == 1) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int n0 = row0 + rt * 16 + 4 * g;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n0 = row0 + rt * 16 + 4 * g;
+        if (n0 >= a.N) continue;   // N % 8 == 0: n0 < N means n0..n0+3 < N
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int m = mt * 16 + (lane & 15);
-                if (m >= a.M) continue;
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m >= a.M) continue;
+            if (a.ks == 1) {
                 const float sm = a.xs[m];
-                uint16_t* o = a.out + (int64_t)m * a.N + n0;
-                if (n0 + 3 < a.N && (a.N & 3) == 0) {
-                    const uint32_t h0 = f32_to_bf16_rne(sm * acc[rt][mt][0]) | (f32_to_bf16_rne(sm * acc[rt][mt][1]) << 16);
-                    const uint32_t h1 = f32_to_bf16_rne(sm * acc[rt][mt][2]) | (f32_to_bf16_rne(sm * acc[rt][mt][3]) << 16);
-                    *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[rt][mt][r]);
-                }
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n0 = row0 + rt * 16 + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            if (m >= a.M) continue;
-            float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-            if (n0 + 3 < a.N && (a.N & 3) == 0) {
-                *reinterpret_cast<float4*>(p) = make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[rt][mt][0]) | (f32_to_bf16_rne(sm * acc[rt][mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[rt][mt][2]) | (f32_to_bf16_rne(sm * acc[rt][mt][3]) << 16);
+                *reinterpret_cast<uint2*>(a.out + (int64_t)m * a.N + n0) = make_uint2(h0, h1);
             } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) p[r] = acc[rt][mt][r];
+                *reinterpret_cast<float4*>(a.partials + ((int64_t)split * a.M + m) * a.N + n0) =
+                    make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
             }
         }
     }
-    __threadfence();
-    __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[tile], 1u);
-        last = (prev == (uint32_t)(a.ks - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n0 = row0 + rt * 16 + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            if (m >= a.M) continue;
-            const float sm = a.xs[m];
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
-            if (n0 + 3 < a.N && (a.N & 3) == 0) {
-                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int j = 0; j < a.ks; ++j) {
-                    const float4 v = *reinterpret_cast<const float4*>(a.partials + ((int64_t)j * a.M + m) * a.N + n0);
-                    t.x = t.x + v.x;
-                    t.y = t.y + v.y;
-                    t.z = t.z + v.z;
-                    t.w = t.w + v.w;
-                }
-                const uint32_t h0 = f32_to_bf16_rne(sm * t.x) | (f32_to_bf16_rne(sm * t.y) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * t.z) | (f32_to_bf16_rne(sm * t.w) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-            } else {
-                for (int r = 0; r < 4; ++r) {
-                    if (n0 + r >= a.N) continue;
-                    float t = 0.f;
-                    for (int j = 0; j < a.ks; ++j) t = t + a.partials[((int64_t)j * a.M + m) * a.N + n0 + r];
-                    o[r] = (uint16_t)f32_to_bf16_rne(sm * t);
-                }
-            }
-        }
-    }
-    if (threadIdx.x == 0) a.counters[tile] = 0u;
 }
+
 
 // ---------------------------------------------------------------------------
 // prefill band: 128x128 tiles, one 128-group per K step, weights expanded to
@@ -470,44 +434,44 @@ __global__ __launch_bounds__(kPreThreads) void i4_prefill_kernel(I4PreArgs a) {
     }
 }
 
-template <int MT, int RT>
+template <int MT, int RT, int U>
 hipError_t launch_i4dec(const I4DecArgs& a, hipStream_t stream) {
-    const int grid = ((a.tiles + 7) / 8) * 8 * a.ks;
-    hipLaunchKernelGGL((i4_decode_kernel<MT, RT>), dim3(grid), dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((i4_decode_kernel<MT, RT, U>), dim3(a.tiles * a.ks), dim3(kDecThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int RT>
-hipError_t launch_i4dec_rt(const I4DecArgs& a, int mt, hipStream_t stream) {
-    switch (mt) {
-        case 1: return launch_i4dec<1, RT>(a, stream);
-        case 2: return launch_i4dec<2, RT>(a, stream);
-        case 3: return launch_i4dec<3, RT>(a, stream);
-        default: return launch_i4dec<4, RT>(a, stream);
+template <int MT, int RT>
+hipError_t launch_i4dec_u(const I4DecArgs& a, int u, hipStream_t stream) {
+    switch (u) {
+        case 1: return launch_i4dec<MT, RT, 1>(a, stream);
+        case 2: return launch_i4dec<MT, RT, 2>(a, stream);
+        default: return launch_i4dec<MT, RT, 4>(a, stream);
+    }
+}
+
+template <int MT>
+hipError_t launch_i4dec_rt(const I4DecArgs& a, int rt, int u, hipStream_t stream) {
+    switch (rt) {
+        case 1: return launch_i4dec_u<MT, 1>(a, u, stream);
+        case 2: return launch_i4dec_u<MT, 2>(a, u, stream);
+        default: return launch_i4dec_u<MT, 4>(a, u, stream);
     }
 }
 
 }  // namespace
 
 GemmPlan plan_int4(int64_t M, int64_t N, int64_t K) {
-    GemmPlan p{};
     if (M > 64) {
+        GemmPlan p{};
         p.band = 1;
         return p;
     }
-    p.band = 0;
-    p.mt = (int)((M + 15) / 16);
-    p.rt = 4;
-    const int64_t rows_per_tile = 4 * p.rt * 16;
-    p.tiles = (N + rows_per_tile - 1) / rows_per_tile;
-    const int64_t groups = K / 128;
-    const int64_t target = 1024;
-    int64_t sp = (groups * p.tiles + target - 1) / target;
-    if (sp < 2) sp = 2;
-    if (sp > groups) sp = groups;
-    p.s_per = (int)sp;
-    p.ks = (int)((groups + sp - 1) / sp);
-    return p;
+    const int mt = (int)((M + 15) / 16);
+    const int rt = mt >= 3 ? 1 : 2;
+    const int u = mt >= 2 ? 2 : 4;
+    const int64_t tiles = (N + 4 * rt * 16 - 1) / (4 * rt * 16);
+    const int64_t ks = (512 + tiles - 1) / tiles;
+    return make_decode_plan(M, N, K, rt, u, (int)ks);
 }
 
 hipError_t launch_int4_check_transpose(const int32_t* qw_kn, const int32_t* qzeros, int64_t N,
@@ -542,15 +506,17 @@ hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* x
     a.x8 = x8; a.xs = xs; a.qw = qw_nk; a.sc = scales; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.ks = p.ks; a.s_per = p.s_per; a.tiles = (int)p.tiles;
-    if (p.ks > 1) {
-        a.counters = reinterpret_cast<uint32_t*>(ws);
+    if (p.ks > 1)
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+    hipError_t e;
+    switch (p.mt) {
+        case 1: e = launch_i4dec_rt<1>(a, p.rt, p.u, stream); break;
+        case 2: e = launch_i4dec_rt<2>(a, p.rt, p.u, stream); break;
+        case 3: e = launch_i4dec_rt<3>(a, p.rt, p.u, stream); break;
+        default: e = launch_i4dec_rt<4>(a, p.rt, p.u, stream); break;
     }
-    switch (p.rt) {
-        case 1: return launch_i4dec_rt<1>(a, p.mt, stream);
-        case 2: return launch_i4dec_rt<2>(a, p.mt, stream);
-        default: return launch_i4dec_rt<4>(a, p.mt, stream);
-    }
+    if (e != hipSuccess || p.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 
 }  // namespace w4a8

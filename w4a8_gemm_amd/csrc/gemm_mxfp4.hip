@@ -62,13 +62,20 @@ __device__ __forceinline__ v16f mfma32(v8i a_fp4, v8i b_fp8, v16f c, int scale_a
 // Decode band (M <= 64): weights streamed from HBM straight into registers.
 //
 // Workgroup = 4 waves; wave w owns RT*16 consecutive weight rows and all M
-// columns (MT tiles of 16), and the workgroup one K split.  A 512-wide K chunk
-// is 4 MFMAs; in MFMA u, weight lane (row, g) holds 32-block 4g+u of the chunk,
-// so the lane's four weight fragments are one contiguous 64-byte run and its
-// four e8m0 bytes one aligned dword (opsel u picks the byte).  The activation
-// lane (m, g) then needs 16-byte halves of blocks 4(g/2)+u and 8+4(g/2)+u,
-// half g%2, which it reads from L2 (activations are small and shared).
-// A K remainder of fewer than 4 steps runs 128 wide with the hardware order.
+// columns (MT tiles of 16); the grid covers row blocks x K splits.  The K range
+// of a split is walked in chunks of U 128-wide steps, one MFMA per step and
+// 16-row tile, in the instruction's own K order: weight lane (n, g) of step t
+// holds bytes 64t + 16g .. +16 of row n, so each load instruction reads 64
+// contiguous bytes of 16 rows; its e8m0 byte is byte g of the row's dword for
+// the step (shifted down, opsel 0); activation lane (m, g) holds bytes
+// 128t + 16g and 128t + 64 + 16g of row m (L2 resident, shared by all waves).
+// The whole next chunk (weights, scales, activations) is issued before the
+// current chunk's MFMAs, so one chunk of loads is always in flight per wave.
+// With more than one K split each split writes fp32 partial sums; a separate
+// reduction kernel adds them in split order (bitwise deterministic) -- a kernel
+// boundary is the only coherence point shared by all eight per-XCD L2 caches
+// that costs nothing inside the streaming kernel.
+// K % 128 != 0 runs one masked step at a time (U = 1).
 // ===========================================================================
 
 constexpr int kDecThreads = 256;
@@ -79,7 +86,6 @@ struct DecArgs {
     const uint8_t* wq;
     const uint8_t* we;
     uint16_t* out;
-    uint32_t* counters;
     float* partials;
     int M, N, K;
     int ks;        // K splits
@@ -87,28 +93,62 @@ struct DecArgs {
     int tiles;     // row blocks (4 * RT * 16 rows each)
 };
 
-template <int MT>
-__device__ __forceinline__ void load_act_chunk(const DecArgs& a, int lane, int64_t kbyte, int u,
-                                               v8i* bx) {
+template <int MT, int RT, int U>
+struct DecChunk {
+    uint4 w[RT][U];
+    uint32_t s[RT][U];
+    uint4 x[MT][U][2];
+};
+
+template <int MT, int RT, int U>
+__device__ __forceinline__ void dec_load(const DecArgs& a, int lane, const int* rows, int s,
+                                         DecChunk<MT, RT, U>& c) {
     const int g = lane >> 4;
-    const int aoff = 128 * (g >> 1) + 16 * (g & 1) + 32 * u;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint8_t* wr = a.wq + (int64_t)rows[rt] * (a.K >> 1) + 64 * (int64_t)s + 16 * g;
+        const uint8_t* er = a.we + (int64_t)rows[rt] * (a.K >> 5) + 4 * (int64_t)s;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c.w[rt][u] = *reinterpret_cast<const uint4*>(wr + 64 * u);
+            c.s[rt][u] = *reinterpret_cast<const uint32_t*>(er + 4 * u);
+        }
+    }
+    // columns m >= M load row M-1 (their outputs are never stored): every load
+    // is unconditional, so the wait before the MFMAs covers only this chunk
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-        if (m < a.M) {
-            const uint8_t* p = a.x8 + (int64_t)m * a.K + kbyte + aoff;
-            lo = *reinterpret_cast<const uint4*>(p);
-            hi = *reinterpret_cast<const uint4*>(p + 256);
+        const int m = min(mt * 16 + (lane & 15), a.M - 1);
+        const uint8_t* xr = a.x8 + (int64_t)m * a.K + 128 * (int64_t)s + 16 * g;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c.x[mt][u][0] = *reinterpret_cast<const uint4*>(xr + 128 * u);
+            c.x[mt][u][1] = *reinterpret_cast<const uint4*>(xr + 128 * u + 64);
         }
-        bx[mt] = frag_fp8(lo, hi);
     }
 }
 
-// one 128-wide step in the hardware order, with K-tail masking (K % 32 == 0)
-template <int MT, int RT, bool ALIGNED_SCALE>
-__device__ __forceinline__ void dec_step(const DecArgs& a, int lane, const int* rows, int s,
-                                         v4f (&acc)[RT][MT]) {
+template <int MT, int RT, int U>
+__device__ __forceinline__ void dec_compute(int lane, const DecChunk<MT, RT, U>& c,
+                                            v4f (&acc)[RT][MT]) {
+    const int sh = 8 * (lane >> 4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const v8i aw = frag_fp4(c.w[rt][u]);
+            const int sc = (int)(c.s[rt][u] >> sh);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[rt][mt] = mfma16<0>(aw, frag_fp8(c.x[mt][u][0], c.x[mt][u][1]), acc[rt][mt], sc);
+        }
+    }
+}
+
+// one 128-wide step with K-tail masking (any K % 32 == 0)
+template <int MT, int RT>
+__device__ __forceinline__ void dec_step_masked(const DecArgs& a, int lane, const int* rows, int s,
+                                                v4f (&acc)[RT][MT]) {
     const int g = lane >> 4;
     const int kb = 4 * s;                 // first 32-block of the step
     const int kblocks = a.K >> 5;
@@ -139,63 +179,12 @@ __device__ __forceinline__ void dec_step(const DecArgs& a, int lane, const int* 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = mfma16<0>(aw, bx[mt], acc[rt][mt], sc);
     }
-    (void)ALIGNED_SCALE;
 }
 
-template <int RT>
-struct WChunk {
-    uint4 q[RT][4];
-    uint32_t sc[RT];
-};
-
-template <int RT>
-__device__ __forceinline__ void load_w_chunk(const DecArgs& a, int lane, const int* rows, int s,
-                                             WChunk<RT>& c) {
-    const int g = lane >> 4;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const uint4* p = reinterpret_cast<const uint4*>(a.wq + (int64_t)rows[rt] * (a.K >> 1) +
-                                                        64 * (int64_t)s + 64 * g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) c.q[rt][u] = p[u];
-        c.sc[rt] = *reinterpret_cast<const uint32_t*>(a.we + (int64_t)rows[rt] * (a.K >> 5) + 4 * s + 4 * g);
-    }
-}
-
-template <int MT, int RT>
-__device__ __forceinline__ void dec_chunk(const DecArgs& a, int lane, int s, const WChunk<RT>& c,
-                                          v4f (&acc)[RT][MT]) {
-    const int64_t kbyte = 128 * (int64_t)s;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        v8i bx[MT];
-        load_act_chunk<MT>(a, lane, kbyte, u, bx);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const v8i aw = frag_fp4(c.q[rt][u]);
-            const int sc = (int)c.sc[rt];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (u == 0) acc[rt][mt] = mfma16<0>(aw, bx[mt], acc[rt][mt], sc);
-                if (u == 1) acc[rt][mt] = mfma16<1>(aw, bx[mt], acc[rt][mt], sc);
-                if (u == 2) acc[rt][mt] = mfma16<2>(aw, bx[mt], acc[rt][mt], sc);
-                if (u == 3) acc[rt][mt] = mfma16<3>(aw, bx[mt], acc[rt][mt], sc);
-            }
-        }
-    }
-}
-
-template <int MT, int RT, bool K128>
+template <int MT, int RT, int U, bool K128>
 __global__ __launch_bounds__(kDecThreads) void mx_decode_kernel(DecArgs a) {
-    // XCD-aware order: all K splits of a row block land on the same XCD
-    // (workgroups are dealt round-robin over the 8 XCDs), so the partial sums
-    // a last-arriving workgroup reads were written through its own L2.
-    const int b = blockIdx.x;
-    const int xcd = b & 7, li = b >> 3;
-    const int split = li % a.ks;
-    const int tile = (li / a.ks) * 8 + xcd;
-    if (tile >= a.tiles) return;
-
+    const int tile = blockIdx.x % a.tiles;
+    const int split = blockIdx.x / a.tiles;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row0 = tile * (4 * RT * 16) + wave * (RT * 16);
     int rows[RT];
@@ -213,32 +202,62 @@ __global__ __launch_bounds__(kDecThreads) void mx_decode_kernel(DecArgs a) {
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
     int s = s0;
-    if (K128 && s + 4 <= s1) {
-        WChunk<RT> cur;
-        load_w_chunk<RT>(a, lane, rows, s, cur);
-        for (; s + 4 <= s1; s += 4) {
-            WChunk<RT> nxt;
-            const bool more = s + 8 <= s1;
-            if (more) load_w_chunk<RT>(a, lane, rows, s + 4, nxt);
-            dec_chunk<MT, RT>(a, lane, s, cur, acc);
-            if (more) cur = nxt;
+    if (K128) {
+        // software pipeline: the loop body always issues the next chunk's loads
+        // before the current chunk's MFMAs (straight-line, so the wait before
+        // the MFMAs only covers the current chunk)
+        // Two register sets used in turn (no copies); scheduling barriers keep
+        // the compiler from sinking a prefetch next to its use.
+        const int nchunks = s1 > s0 ? (s1 - s0) / U : 0;
+        if (nchunks > 0) {
+            DecChunk<MT, RT, U> ca, cb;
+            dec_load<MT, RT, U>(a, lane, rows, s0, ca);
+            int c = 1;
+            for (; c + 1 < nchunks; c += 2) {
+                dec_load<MT, RT, U>(a, lane, rows, s0 + c * U, cb);
+                __builtin_amdgcn_sched_barrier(0);
+                dec_compute<MT, RT, U>(lane, ca, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                dec_load<MT, RT, U>(a, lane, rows, s0 + (c + 1) * U, ca);
+                __builtin_amdgcn_sched_barrier(0);
+                dec_compute<MT, RT, U>(lane, cb, acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (c < nchunks) {
+                dec_load<MT, RT, U>(a, lane, rows, s0 + c * U, cb);
+                __builtin_amdgcn_sched_barrier(0);
+                dec_compute<MT, RT, U>(lane, ca, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                dec_compute<MT, RT, U>(lane, cb, acc);
+            } else {
+                dec_compute<MT, RT, U>(lane, ca, acc);
+            }
+            s = s0 + nchunks * U;
         }
+        for (; s < s1; ++s) {
+            DecChunk<MT, RT, 1> one;
+            dec_load<MT, RT, 1>(a, lane, rows, s, one);
+            dec_compute<MT, RT, 1>(lane, one, acc);
+        }
+    } else {
+        for (; s < s1; ++s) dec_step_masked<MT, RT>(a, lane, rows, s, acc);
     }
-    for (; s < s1; ++s) dec_step<MT, RT, K128>(a, lane, rows, s, acc);
 
-    // ---------------- epilogue ----------------
+    // epilogue: lane holds rows n0..n0+3 (n0 = tile row + 4g) of column m
     const int g = lane >> 4;
-    if (a.ks == 1) {
+    const bool vec = (a.N & 3) == 0;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int n0 = row0 + rt * 16 + 4 * g;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n0 = row0 + rt * 16 + 4 * g;
+        if (n0 >= a.N) continue;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int m = mt * 16 + (lane & 15);
-                if (m >= a.M) continue;
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m >= a.M) continue;
+            if (a.ks == 1) {
                 const float sm = a.xs[m];
                 uint16_t* o = a.out + (int64_t)m * a.N + n0;
-                if (n0 + 3 < a.N && (a.N & 3) == 0) {
+                if (vec) {
                     const uint32_t h0 = f32_to_bf16_rne(sm * acc[rt][mt][0]) | (f32_to_bf16_rne(sm * acc[rt][mt][1]) << 16);
                     const uint32_t h1 = f32_to_bf16_rne(sm * acc[rt][mt][2]) | (f32_to_bf16_rne(sm * acc[rt][mt][3]) << 16);
                     *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
@@ -246,73 +265,50 @@ __global__ __launch_bounds__(kDecThreads) void mx_decode_kernel(DecArgs a) {
                     for (int r = 0; r < 4; ++r)
                         if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[rt][mt][r]);
                 }
-            }
-        }
-        return;
-    }
-
-    // split K: publish this split's partial sums, then the last arrival reduces
-    // all splits in fixed order 0..ks-1 (bitwise deterministic) and resets the
-    // counter for the next call.
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n0 = row0 + rt * 16 + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            if (m >= a.M) continue;
-            float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-            if (n0 + 3 < a.N && (a.N & 3) == 0) {
-                *reinterpret_cast<float4*>(p) = make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
             } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) p[r] = acc[rt][mt][r];
-            }
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[tile], 1u);
-        last = (prev == (uint32_t)(a.ks - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n0 = row0 + rt * 16 + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            if (m >= a.M) continue;
-            const float sm = a.xs[m];
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
-            if (n0 + 3 < a.N && (a.N & 3) == 0) {
-                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int j = 0; j < a.ks; ++j) {
-                    const float4 v = *reinterpret_cast<const float4*>(a.partials + ((int64_t)j * a.M + m) * a.N + n0);
-                    t.x = t.x + v.x;
-                    t.y = t.y + v.y;
-                    t.z = t.z + v.z;
-                    t.w = t.w + v.w;
-                }
-                const uint32_t h0 = f32_to_bf16_rne(sm * t.x) | (f32_to_bf16_rne(sm * t.y) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * t.z) | (f32_to_bf16_rne(sm * t.w) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-            } else {
-                for (int r = 0; r < 4; ++r) {
-                    if (n0 + r >= a.N) continue;
-                    float t = 0.f;
-                    for (int j = 0; j < a.ks; ++j) t = t + a.partials[((int64_t)j * a.M + m) * a.N + n0 + r];
-                    o[r] = (uint16_t)f32_to_bf16_rne(sm * t);
+                float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
+                if (vec) {
+                    *reinterpret_cast<float4*>(p) = make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < a.N) p[r] = acc[rt][mt][r];
                 }
             }
         }
     }
-    if (threadIdx.x == 0) a.counters[tile] = 0u;
 }
+
+// out[m, n] = bf16(s_m * sum_{j < ks} partials[j, m, n]), j in increasing order
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partials,
+                                                            const float* __restrict__ xs, int M,
+                                                            int N, int ks, uint16_t* __restrict__ out) {
+    const int64_t total = (int64_t)M * N;
+    const int64_t plane = total;
+    if ((N & 3) == 0) {
+        const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+        if (i4 >= total) return;
+        const int m = (int)(i4 / N);
+        float4 t = *reinterpret_cast<const float4*>(partials + i4);
+        for (int j = 1; j < ks; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(partials + (int64_t)j * plane + i4);
+            t.x = t.x + v.x;
+            t.y = t.y + v.y;
+            t.z = t.z + v.z;
+            t.w = t.w + v.w;
+        }
+        const float sm = xs[m];
+        const uint32_t h0 = f32_to_bf16_rne(sm * t.x) | (f32_to_bf16_rne(sm * t.y) << 16);
+        const uint32_t h1 = f32_to_bf16_rne(sm * t.z) | (f32_to_bf16_rne(sm * t.w) << 16);
+        *reinterpret_cast<uint2*>(out + i4) = make_uint2(h0, h1);
+    } else {
+        const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (i >= total) return;
+        float t = partials[i];
+        for (int j = 1; j < ks; ++j) t = t + partials[(int64_t)j * plane + i];
+        out[i] = (uint16_t)f32_to_bf16_rne(xs[i / N] * t);
+    }
+}
+
 
 // ===========================================================================
 // Prefill band (M > 64): 128x128 output tile per workgroup, K in steps of 128
@@ -503,23 +499,31 @@ __global__ __launch_bounds__(kPreThreads) void mx_prefill_kernel(PreArgs a) {
     }
 }
 
-template <int MT, int RT>
+template <int MT, int RT, int U>
 hipError_t launch_dec(const DecArgs& a, bool k128, hipStream_t stream) {
-    const int grid = ((a.tiles + 7) / 8) * 8 * a.ks;
+    const int grid = a.tiles * a.ks;
     if (k128)
-        hipLaunchKernelGGL((mx_decode_kernel<MT, RT, true>), dim3(grid), dim3(kDecThreads), 0, stream, a);
+        hipLaunchKernelGGL((mx_decode_kernel<MT, RT, U, true>), dim3(grid), dim3(kDecThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((mx_decode_kernel<MT, RT, false>), dim3(grid), dim3(kDecThreads), 0, stream, a);
+        hipLaunchKernelGGL((mx_decode_kernel<MT, RT, 1, false>), dim3(grid), dim3(kDecThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int RT>
-hipError_t launch_dec_rt(const DecArgs& a, int mt, bool k128, hipStream_t stream) {
-    switch (mt) {
-        case 1: return launch_dec<1, RT>(a, k128, stream);
-        case 2: return launch_dec<2, RT>(a, k128, stream);
-        case 3: return launch_dec<3, RT>(a, k128, stream);
-        default: return launch_dec<4, RT>(a, k128, stream);
+template <int MT, int RT>
+hipError_t launch_dec_u(const DecArgs& a, int u, bool k128, hipStream_t stream) {
+    switch (u) {
+        case 1: return launch_dec<MT, RT, 1>(a, k128, stream);
+        case 2: return launch_dec<MT, RT, 2>(a, k128, stream);
+        default: return launch_dec<MT, RT, 4>(a, k128, stream);
+    }
+}
+
+template <int MT>
+hipError_t launch_dec_rt(const DecArgs& a, int rt, int u, bool k128, hipStream_t stream) {
+    switch (rt) {
+        case 1: return launch_dec_u<MT, 1>(a, u, k128, stream);
+        case 2: return launch_dec_u<MT, 2>(a, u, k128, stream);
+        default: return launch_dec_u<MT, 4>(a, u, k128, stream);
     }
 }
 
@@ -529,35 +533,45 @@ hipError_t launch_dec_rt(const DecArgs& a, int mt, bool k128, hipStream_t stream
 // plans
 // ---------------------------------------------------------------------------
 
-static int steps_per_split(int64_t steps, int64_t tiles, bool k128) {
-    // aim for about 4 workgroups (16 waves) per CU over 256 CUs
-    const int64_t target = 1024;
-    int64_t sp = (steps * tiles + target - 1) / target;
-    if (sp < 1) sp = 1;
-    if (k128) sp = (sp + 3) / 4 * 4;
-    if (sp > steps) sp = steps;
-    return (int)sp;
-}
-
-GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K) {
+// Decode plan: weight rows per wave (16*rt), steps per chunk (u) and K splits
+// (ks).  Splits are sized so the grid holds about `target` workgroups; each
+// split covers a whole number of chunks.
+GemmPlan make_decode_plan(int64_t M, int64_t N, int64_t K, int rt, int u, int ks_hint) {
     GemmPlan p{};
-    if (M > 64) {
-        p.band = 1;
-        return p;
-    }
     p.band = 0;
     p.mt = (int)((M + 15) / 16);
-    p.rt = 4;
-    const int64_t rows_per_tile = 4 * p.rt * 16;
+    p.rt = rt;
+    p.u = (K % 128 == 0) ? u : 1;
+    const int64_t rows_per_tile = 4 * (int64_t)p.rt * 16;
     p.tiles = (N + rows_per_tile - 1) / rows_per_tile;
     const int64_t steps = (K + 127) / 128;
-    p.s_per = steps_per_split(steps, p.tiles, K % 128 == 0);
-    p.ks = (int)((steps + p.s_per - 1) / p.s_per);
+    int64_t ks = ks_hint;
+    if (ks < 1) ks = 1;
+    if (ks > steps) ks = steps;
+    int64_t sp = (steps + ks - 1) / ks;
+    sp = (sp + p.u - 1) / p.u * p.u;
+    p.s_per = (int)sp;
+    p.ks = (int)((steps + sp - 1) / sp);
     return p;
 }
 
+GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K) {
+    if (M > 64) {
+        GemmPlan p{};
+        p.band = 1;
+        return p;
+    }
+    const int mt = (int)((M + 15) / 16);
+    const int rt = mt >= 3 ? 1 : 2;
+    const int u = mt >= 2 ? 2 : 4;
+    // K splits: enough workgroups for ~8 waves per CU on 256 CUs
+    const int64_t tiles = (N + 4 * rt * 16 - 1) / (4 * rt * 16);
+    int64_t ks = (512 + tiles - 1) / tiles;
+    return make_decode_plan(M, N, K, rt, u, (int)ks);
+}
+
 size_t plan_workspace_bytes(const GemmPlan& p, int64_t M, int64_t N) {
-    if (p.band != 0 || p.ks <= 1) return 0;
+    if (p.band == 1 || p.ks <= 1) return 0;
     return ws_counter_bytes(p.tiles) + (size_t)p.ks * (size_t)M * (size_t)N * sizeof(float);
 }
 
@@ -575,19 +589,27 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
     DecArgs a{};
     a.x8 = x8; a.xs = xs; a.wq = wq; a.we = we; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
-    a.ks = p.ks;
-    a.s_per = p.s_per;
-    a.tiles = (int)p.tiles;
-    if (p.ks > 1) {
-        a.counters = reinterpret_cast<uint32_t*>(ws);
+    a.ks = p.ks; a.s_per = p.s_per; a.tiles = (int)p.tiles;
+    if (p.ks > 1)
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
-    }
     const bool k128 = (K % 128) == 0;
-    switch (p.rt) {
-        case 1: return launch_dec_rt<1>(a, p.mt, k128, stream);
-        case 2: return launch_dec_rt<2>(a, p.mt, k128, stream);
-        default: return launch_dec_rt<4>(a, p.mt, k128, stream);
+    hipError_t e;
+    switch (p.mt) {
+        case 1: e = launch_dec_rt<1>(a, p.rt, p.u, k128, stream); break;
+        case 2: e = launch_dec_rt<2>(a, p.rt, p.u, k128, stream); break;
+        case 3: e = launch_dec_rt<3>(a, p.rt, p.u, k128, stream); break;
+        default: e = launch_dec_rt<4>(a, p.rt, p.u, k128, stream); break;
     }
+    if (e != hipSuccess || p.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+}
+
+hipError_t launch_splitk_reduce(const float* partials, const float* xs, int64_t M, int64_t N,
+                                int ks, uint16_t* out, hipStream_t stream) {
+    const int64_t items = (N % 4 == 0) ? M * N / 4 : M * N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       stream, partials, xs, (int)M, (int)N, ks, out);
+    return hipGetLastError();
 }
 
 }  // namespace w4a8

@@ -75,10 +75,12 @@ struct GemmPlan {
     int band;       // 0 decode (weights streamed, split K), 1 prefill (LDS tiles)
     int mt;         // decode: 16-wide activation tiles (1..4)
     int rt;         // decode: 16-row weight tiles per wave
+    int u;          // decode: 128-wide K steps per prefetched chunk
     int ks;         // decode: K splits (1 = no workspace traffic)
     int s_per;      // decode: 128-wide K steps per split
-    int64_t tiles;  // decode: row blocks of the weight (one counter each)
+    int64_t tiles;  // decode: row blocks of the weight
 };
+GemmPlan make_decode_plan(int64_t M, int64_t N, int64_t K, int rt, int u, int ks_hint);
 GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K);
 GemmPlan plan_int4(int64_t M, int64_t N, int64_t K);
 size_t plan_workspace_bytes(const GemmPlan& p, int64_t M, int64_t N);
@@ -87,6 +89,17 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
                              const uint8_t* wq, const uint8_t* we, uint16_t* out, int64_t M,
                              int64_t N, int64_t K, void* ws, hipStream_t stream);
 
+// MXFP4 weights in fragment order (gemm_prepared.hip)
+void prepared_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64_t K, uint8_t* wt,
+                          uint8_t* st, hipStream_t stream);
+GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth);
+size_t prepared_lds_bytes(const GemmPlan& p, int64_t M);
+hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
+                                  const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream);
+constexpr int64_t kPreparedDecodeMaxM = 32;
+
 hipError_t launch_int4_check_transpose(const int32_t* qw_kn, const int32_t* qzeros, int64_t N,
                                        int64_t K, int32_t* qw_nk, uint32_t* bad_count,
                                        hipStream_t stream);
@@ -94,8 +107,12 @@ hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* x
                             const int32_t* qw_nk, const uint16_t* scales, uint16_t* out,
                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
 
-// Split-K workspace layout: counters first (one uint32 per row block, padded to
-// 256 bytes), then fp32 partials [ks][M][N].
+// out[m, n] = bf16(s_m * sum_j partials[j, m, n]) in split order (decode split K)
+hipError_t launch_splitk_reduce(const float* partials, const float* xs, int64_t M, int64_t N,
+                                int ks, uint16_t* out, hipStream_t stream);
+
+// Split-K workspace layout: a 256-byte-aligned header region (one word per row
+// block, reserved), then fp32 partials [ks][M][N].
 inline size_t ws_counter_bytes(int64_t tiles) {
     return (size_t)((tiles * 4 + 255) / 256 * 256);
 }
