@@ -2,12 +2,15 @@
 
 Step (the headline, timed K times after W warm-up steps): one decode pass of
 the merged gate_up projection (N = 2 x 17408, K = 5120, MXFP4 weights
-requantized on the GPU from NVFP4 with one global divisor per partition), for
-each batch M in {1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K]
-activation, then the block-scaled W4A8 GEMM -> bf16 [M, N].  Steps rotate over
-four copies of the weight (379 MB), so no step is served from the 256 MB
-Infinity Cache.  Each step is one HIP graph replay (captured once per weight
-copy), so host launch latency is not in the timed region.
+requantized on the GPU from NVFP4 with one global divisor per partition, then
+repacked once into matrix-core fragment order), for each batch M in
+{1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K] activation, then the
+block-scaled W4A8 GEMM -> bf16 [M, N] (fragment-order weights for M <= 32, the
+row-major weight for M = 64, which the fragment-order decode kernel does not
+cover).  Steps rotate over four copies of each weight layout (379 MB each), so no
+step is served from the 256 MB Infinity Cache.  Each step is one HIP graph
+replay (captured once per weight copy), so host launch latency is not in the
+timed region.
 
 value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
 weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
@@ -35,6 +38,7 @@ METRIC = "W4A8 MXFP4 GEMM: decode HBM GB/s (M≤64), prefill TFLOPS (M=4096); re
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 DECODE_MS = (1, 8, 16, 64)
+PREPARED_MAX_M = 32
 COPIES = 4
 
 
@@ -121,19 +125,27 @@ def main():
     wp, we = w4.requant_nvfp4_to_mxfp4(nv_p, nv_s, g["part_rows"], g["part_divisor"],
                                        mode="mse", row_chunk=4096)
     copies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(COPIES - 1)]
+    pcopies = [w4.mxfp4_prepare(wp, we) for _ in range(COPIES)]
     xs_bf16 = {M: torch.from_numpy(synth.acts(M, K, seed=(1, M), spread=10.0).view(np.int16))
                .view(torch.bfloat16).to(dev) for M in DECODE_MS}
     x8 = {M: torch.empty((M, K), dtype=torch.uint8, device=dev) for M in DECODE_MS}
     xsc = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in DECODE_MS}
     out = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
     ws = w4.Workspace(max(DECODE_MS), N, K, "mxfp4", dev)
+    pws = w4.Workspace(PREPARED_MAX_M, N, K, "prepared", dev)
     torch.cuda.synchronize()
 
+    def gemm(M, c):
+        if M <= PREPARED_MAX_M:
+            w4.mxfp4_gemm_prepared(x8[M], xsc[M], pcopies[c], out=out[M], workspace=pws)
+        else:
+            w_p, w_e = copies[c]
+            w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+
     def step(c):
-        w_p, w_e = copies[c]
         for M in DECODE_MS:
             w4.quant_act_fp8_per_token(xs_bf16[M], out=x8[M], scale=xsc[M])
-            w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+            gemm(M, c)
 
     graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(COPIES)]
     step_bytes = sum(decode_bytes(M, N, K) for M in DECODE_MS)
@@ -152,8 +164,7 @@ def main():
     for M in DECODE_MS:
         def gemms(M=M):
             for r in range(R):
-                w_p, w_e = copies[r % COPIES]
-                w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+                gemm(M, r % COPIES)
         gg = graph_of(torch, gemms)
         gg.replay()
         dt = timer(lambda i: gg.replay(), max(2, args.steps // 4)) / R
@@ -162,7 +173,9 @@ def main():
     gemm_total_bytes = sum(gemm_bytes(M, N, K) for M in DECODE_MS)
     gemm_total_t = sum(per_m.values())
     achieved = gemm_total_bytes / gemm_total_t / 1e9
-    roofline = {"bound": "hbm", "kernel": "mx_decode_kernel (gate_up, M in {1,8,16,64})",
+    roofline = {"bound": "hbm",
+                "kernel": "decode GEMM, gate_up, M in {1,8,16,64} (pdec_kernel for M<=32, "
+                          "mx_decode_kernel + splitk_reduce for M=64); graph-timed incl. launch gaps",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "per_launch_us": {str(M): round(per_m[M] * 1e6, 3) for M in DECODE_MS},
@@ -252,6 +265,23 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, co
                       "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
     res["down_proj_decode"] = dp
     log("down_proj", dp)
+    pdc = [w4.mxfp4_prepare(dcopies[r][0], dcopies[r][1]) for r in range(8)]
+    pdws = w4.Workspace(PREPARED_MAX_M, d["N"], d["K"], "prepared", dev)
+    pdp = {}
+    for M in (1, 16):
+        xb = torch.from_numpy(synth.acts(M, d["K"], seed=(2, M)).view(np.int16)).view(torch.bfloat16).to(dev)
+        a8, asc = w4.quant_act_fp8_per_token(xb)
+        oo = torch.empty((M, d["N"]), dtype=torch.bfloat16, device=dev)
+        gg = graph_of(torch, lambda: [w4.mxfp4_gemm_prepared(a8, asc, pdc[r], out=oo, workspace=pdws)
+                                      for r in range(8)])
+        gg.replay()
+        dt = timer(lambda i: gg.replay(), 10) / 8
+        b = gemm_bytes(M, d["N"], d["K"])
+        pdp[str(M)] = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+                       "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    res["down_proj_decode_prepared"] = pdp
+    log("down_proj prepared", pdp)
+    del pdc
     del dcopies
     # int4 g128
     q = synth.int4()

@@ -84,14 +84,19 @@ __global__ __launch_bounds__(256) void prep_s_kernel(const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 // decode band on prepared weights (M <= 32)
 //
-// Workgroup = 4 waves = 64 weight rows (one 16-row tile per wave) x one K split
-// of whole 512-wide chunks.  The workgroup first copies the split's activations
-// (all M rows) into LDS (rows padded by 16 bytes: the 16 column lanes of an
-// MFMA fragment read then fall in distinct banks); each wave then streams its
-// tile's weight blocks and scale dwords through a D-deep register ring, loads
-// issued D-1 chunks ahead of the MFMAs (straight-line code between scheduling
-// barriers, so each wait covers exactly the chunk about to be used; chunk
-// indices past the end re-read the last chunk instead of branching).
+// Workgroup = TW x KW waves: TW 16-row weight tiles, each tile's K range cut into
+// KW parts, one wave per (tile, part) -- many short contiguous weight streams
+// (per wave a few KiB in 1 KiB load instructions) keep HBM busier than one long
+// stream per tile.  The workgroup first copies the activations of its K range
+// (all M rows) into LDS (rows padded by 16 bytes, so the 16 column lanes of an
+// MFMA fragment hit distinct banks), then each wave streams its weight blocks
+// and scale dwords through a D-deep register ring, loads issued D-1 chunks
+// ahead of the MFMAs (straight-line code between scheduling barriers; chunk
+// indices past the end re-read the last chunk rather than branching).  The KW
+// partial accumulators of a tile are added through LDS in part order 0..KW-1
+// (deterministic) by the part-0 wave, which writes the bf16 output -- or, when
+// the grid also splits K across workgroups (ks > 1, for activations too large
+// for LDS), fp32 partials for the reduction kernel.
 // ---------------------------------------------------------------------------
 
 struct PDecArgs {
@@ -104,17 +109,17 @@ struct PDecArgs {
     int M, N, K;
     int s_pad, c_pad;   // padded 128-steps and 4-step chunks per row tile
     int tiles;          // 16-row tiles (ceil(N / 16))
-    int groups;         // workgroups per split (ceil(tiles / 4))
-    int ks, c_per;      // K splits, chunks per split
+    int tw, kw;         // tiles and K parts per workgroup
+    int groups;         // workgroups per split (ceil(tiles / tw))
+    int ks, c_per;      // K splits across workgroups, chunks per split
 };
 
-template <int MT>
 struct PChunk {
     uint4 w[4];
     uint32_t s;
 };
 
-__device__ __forceinline__ void pdec_load(const uint4* wp, const uint32_t* sp, int j, PChunk<1>& c) {
+__device__ __forceinline__ void pdec_load(const uint4* wp, const uint32_t* sp, int j, PChunk& c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
     c.s = sp[j * 64];
@@ -122,7 +127,7 @@ __device__ __forceinline__ void pdec_load(const uint4* wp, const uint32_t* sp, i
 
 template <int MT>
 __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int lane, int M, int j,
-                                             const PChunk<1>& c, v4f (&acc)[MT]) {
+                                             const PChunk& c, v4f (&acc)[MT]) {
     const int g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -141,19 +146,43 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int 
 }
 
 template <int MT, int D>
-__global__ __launch_bounds__(256) void pdec_kernel(PDecArgs a) {
+__global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = tg * 4 + wave;
+    const int nthreads = a.tw * a.kw * 64;
+    const int t = tg * a.tw + wave % a.tw;
+    const int part = wave / a.tw;
     const int c0 = split * a.c_per;
     const int c1 = min(a.c_pad, c0 + a.c_per);
-    const int nch = c1 > c0 ? c1 - c0 : 0;
-    const int kbase = c0 * 512, kr = nch * 512, stride = kr + 16;
+    const int nch_wg = c1 > c0 ? c1 - c0 : 0;
+    const int kbase = c0 * 512, kr = nch_wg * 512, stride = kr + 16;
+    // this wave's chunks within the workgroup's range: an even share, the
+    // first (nch_wg % kw) parts one chunk longer
+    const int base_n = nch_wg / a.kw, extra = nch_wg % a.kw;
+    const int j0 = part * base_n + min(part, extra);
+    const int nch = base_n + (part < extra ? 1 : 0);
+    const bool active = t < a.tiles && nch > 0;
 
-    // activations of this split -> LDS (columns at or past K read as zero)
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // idle waves (past the last tile, or a part with no chunks) still run the
+    // prologue loads: point them at a valid chunk of a valid tile
+    const int tc = min(t, a.tiles - 1);
+    const int jb = nch > 0 ? j0 : 0;
+    const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
+    const uint32_t* sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
+    const int last = nch > 0 ? nch - 1 : 0;
+
+    // weight ring prologue first (HBM latency overlaps the activation copy)
+    PChunk ring[D];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) pdec_load(wp, sp, min(d, last), ring[d]);
+
+    // activations of this workgroup's K range -> LDS (columns >= K read as zero)
     const int per_row = kr / 16;
-    for (int q = threadIdx.x; q < a.M * per_row; q += 256) {
+    for (int q = threadIdx.x; q < a.M * per_row; q += nthreads) {
         const int m = q / per_row, col = q - m * per_row;
         const int k = kbase + 16 * col;
         const uint4 v = k < a.K ? *reinterpret_cast<const uint4*>(a.x8 + (int64_t)m * a.K + k)
@@ -161,26 +190,44 @@ __global__ __launch_bounds__(256) void pdec_kernel(PDecArgs a) {
         *reinterpret_cast<uint4*>(xl + m * stride + 16 * col) = v;
     }
     __syncthreads();
-    if (t >= a.tiles || nch == 0) return;   // no barrier follows
 
-    v4f acc[MT];
+    const uint8_t* xw = xl + 512 * j0;   // this part's first activation column
+    if (active) {
+        for (int j = 0; j < nch; j += D) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint4* wp = a.wt + ((int64_t)t * a.s_pad + 4 * (int64_t)c0) * 64 + lane;
-    const uint32_t* sp = a.st + ((int64_t)t * a.c_pad + c0) * 64 + lane;
-
-    PChunk<1> ring[D];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) pdec_load(wp, sp, min(d, nch - 1), ring[d]);
-    for (int j = 0; j < nch; j += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            pdec_load(wp, sp, min(j + d + D - 1, nch - 1), ring[(d + D - 1) % D]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (j + d < nch) pdec_compute<MT>(xl, stride, lane, a.M, j + d, ring[d], acc);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int d = 0; d < D; ++d) {
+                pdec_load(wp, sp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + d < nch) pdec_compute<MT>(xw, stride, lane, a.M, j + d, ring[d], acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
+
+    // add the K parts of each tile through LDS, in part order
+    if (a.kw > 1) {
+        __syncthreads();   // all waves are done reading activations
+        float4* red = reinterpret_cast<float4*>(xl);   // [kw][tw][MT][64 lanes]
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            red[((part * a.tw + wave % a.tw) * MT + mt) * 64 + lane] =
+                make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float4 tsum = red[((0 * a.tw + wave) * MT + mt) * 64 + lane];
+            for (int q = 1; q < a.kw; ++q) {
+                const float4 v = red[((q * a.tw + wave) * MT + mt) * 64 + lane];
+                tsum.x = tsum.x + v.x;
+                tsum.y = tsum.y + v.y;
+                tsum.z = tsum.z + v.z;
+                tsum.w = tsum.w + v.w;
+            }
+            acc[mt] = v4f{tsum.x, tsum.y, tsum.z, tsum.w};
+        }
+    }
+    if (t >= a.tiles) return;
 
     const int g = lane >> 4;
     const int n0 = 16 * t + 4 * g;
@@ -222,7 +269,8 @@ hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((pdec_kernel<MT, D>), dim3(a.groups * a.ks), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((pdec_kernel<MT, D>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -253,36 +301,60 @@ hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64
     return hipGetLastError();
 }
 
-// Decode plan on prepared weights: K splits so the split's activations fit the
-// LDS budget and the grid has enough waves; D-deep ring.
+// Decode plan on prepared weights: plan fields rt = tiles per workgroup, kw =
+// K parts per tile, ks = K splits across workgroups, s_per = chunks per split,
+// u = ring depth.
+static void prepared_shape(int64_t M, int64_t N, int64_t K, int* tw, int* kw, int* ks, int* c_per) {
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    const int64_t act_budget = 80 * 1024;          // activations resident in LDS per workgroup
+    // K splits across workgroups only when the activations do not fit
+    int64_t c_max = (act_budget / M - 16) / 512;
+    if (c_max < 1) c_max = 1;
+    int64_t s = (c_pad + c_max - 1) / c_max;
+    int64_t cp = (c_pad + s - 1) / s;
+    s = (c_pad + cp - 1) / cp;
+    // tiles per workgroup: enough activation reuse (the L2 -> LDS copies,
+    // M*K per workgroup, at most about a quarter of the weight bytes), at most 4
+    int64_t t_w = (M + 3) / 4;
+    if (t_w < 1) t_w = 1;
+    if (t_w > 4) t_w = 4;
+    // K parts per tile (measured on gfx950: two for wide layers, four for
+    // narrow ones), at most 16 waves per group
+    int64_t k_w = tiles * s >= 1024 ? 2 : 4;
+    if (k_w > cp) k_w = cp;
+    if (k_w > 16 / t_w) k_w = 16 / t_w;
+    if (k_w < 1) k_w = 1;
+    *tw = (int)t_w;
+    *kw = (int)k_w;
+    *ks = (int)s;
+    *c_per = (int)cp;
+}
+
 GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth) {
     GemmPlan p{};
     p.band = 2;
     p.mt = (int)((M + 15) / 16);
-    p.rt = 1;
+    int tw, kw, ks, cp;
+    prepared_shape(M, N, K, &tw, &kw, &ks, &cp);
+    if (ks_hint > 0) {   // tuning: ks_hint encodes kw (K parts per tile)
+        kw = ks_hint;
+        if (kw * tw > 16) kw = 16 / tw;
+        if (kw > cp) kw = cp;
+    }
+    p.rt = tw;
+    p.kw = kw;
     p.u = depth;
-    const int64_t tiles = (N + 15) / 16;
-    const int64_t groups = (tiles + 3) / 4;
-    const int64_t c_pad = (K / 128 + 3) / 4;
-    const int64_t lds_budget = 64 * 1024;
-    int64_t c_max = (lds_budget / M - 16) / 512;
-    if (c_max < 1) c_max = 1;
-    int64_t ks = (c_pad + c_max - 1) / c_max;
-    const int64_t want_waves = 2048;
-    const int64_t ks_par = (want_waves + 4 * groups - 1) / (4 * groups);
-    if (ks < ks_par) ks = ks_par;
-    if (ks_hint > 0) ks = ks_hint < ks ? ks : ks_hint;   // a hint may only lower the split
-    if (ks < (c_pad + c_max - 1) / c_max) ks = (c_pad + c_max - 1) / c_max;
-    if (ks > c_pad) ks = c_pad;
-    const int64_t c_per = (c_pad + ks - 1) / ks;
-    p.s_per = (int)c_per;
-    p.ks = (int)((c_pad + c_per - 1) / c_per);
-    p.tiles = tiles;
+    p.ks = ks;
+    p.s_per = cp;
+    p.tiles = (N + 15) / 16;
     return p;
 }
 
 size_t prepared_lds_bytes(const GemmPlan& p, int64_t M) {
-    return (size_t)(M * ((int64_t)p.s_per * 512 + 16));
+    const size_t act = (size_t)(M * ((int64_t)p.s_per * 512 + 16));
+    const size_t red = (size_t)p.kw * p.rt * p.mt * 64 * 16;
+    return act > red ? act : red;
 }
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
@@ -297,7 +369,9 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     a.c_pad = (int)((K / 128 + 3) / 4);
     a.s_pad = 4 * a.c_pad;
     a.tiles = (int)p.tiles;
-    a.groups = (int)((p.tiles + 3) / 4);
+    a.tw = p.rt;
+    a.kw = p.kw;
+    a.groups = (int)((p.tiles + p.rt - 1) / p.rt);
     a.ks = p.ks;
     a.c_per = p.s_per;
     if (p.ks > 1)

@@ -79,6 +79,7 @@ struct GemmPlan {
     int ks;         // decode: K splits (1 = no workspace traffic)
     int s_per;      // decode: 128-wide K steps per split
     int64_t tiles;  // decode: row blocks of the weight
+    int kw;         // prepared decode: K parts per tile inside a workgroup
 };
 GemmPlan make_decode_plan(int64_t M, int64_t N, int64_t K, int rt, int u, int ks_hint);
 GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K);
