@@ -191,7 +191,8 @@ def test_int4_prepare_rejects_asymmetric_zeros():
 
 
 # ---------------------------------------------------------------------------
-# MXFP4 weights in fragment order (prepared) -- decode band
+# MXFP4 weights in fragment order (prepared): split-K decode kernel for
+# M <= 32, tiled kernel (64/128/256-row tiles) above
 # ---------------------------------------------------------------------------
 
 def _unprepare(wt, st, N, K):
@@ -263,6 +264,57 @@ def test_mxfp4_prepared_down_proj(M):
     say("prepared down_proj", M)
     got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
     g = np.random.default_rng(M + 7)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
+    ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
+    ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
+    assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
+
+
+# tiled band: every tile height, ragged M and N, K of one, two and three steps
+# (the three-stage copy ring), an N that is not a multiple of 4 (scalar stores)
+PREPARED_TILED = [(33, 64, 128), (64, 300, 256), (65, 257, 384), (100, 1000, 1152),
+                  (128, 130, 4096), (129, 512, 640), (256, 1026, 2048), (300, 100, 1280),
+                  (513, 600, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", PREPARED_TILED)
+def test_mxfp4_prepared_tiled_ragged(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 2))
+    x8, s = _acts(M, K, (M, K, 2), spread=10.0)
+    say("prepared tiled gemm", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"])
+    assert rel_frobenius(got, ref) <= GEMM_REL_F
+    slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
+    assert (np.abs(got - ref) <= slack).all()
+
+
+@pytest.mark.parametrize("M", [64, 4096])
+def test_mxfp4_prepared_tiled_gate_up(gate_up_mx, M):
+    x8, s = _acts(M, synth.HIDDEN, (3, M), spread=10.0)
+    wp, we = gate_up_mx[:2]
+    pw = w4.mxfp4_prepare(dev_u8(wp), dev_u8(we))
+    say("prepared tiled gate_up", M)
+    dx, ds = dev_u8(x8), dev_f32(s)
+    o1 = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    o2 = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(o1, o2)
+    g = np.random.default_rng(M + 11)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
+    ni = np.concatenate([g.integers(0, wp.shape[0], M), g.integers(0, wp.shape[0], 4096)])
+    ref = oracle.mxfp4_gemm(x8, s, wp, we, mi=mi, ni=ni)
+    assert rel_frobenius(o1[mi, ni], ref) <= GEMM_REL_F
+
+
+def test_mxfp4_prepared_tiled_down_proj():
+    d = synth.down_proj()
+    M = 4096
+    x8, s = _acts(M, synth.INTERMEDIATE, (4, M))
+    pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
+    say("prepared tiled down_proj", M)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(5)
     mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
     ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
     ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)

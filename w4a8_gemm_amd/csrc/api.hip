@@ -102,7 +102,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     for (int64_t m = 1; m <= top; ++m) {
         const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K)
                            : kind == W4A8_WEIGHT_INT4G128 ? plan_int4(m, N, K)
-                           : (m <= kPreparedDecodeMaxM ? plan_prepared(m, N, K, 0, 3) : plan_mxfp4(m, N, K));
+                           : (m <= kPreparedDecodeMaxM ? plan_prepared(m, N, K, 0, 3) : GemmPlan{1, 0, 0, 0, 0, 0, 0, 0});
         const size_t b = plan_workspace_bytes(p, m, N);
         if (b > need) need = b;
     }
@@ -159,7 +159,9 @@ w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_sc
     if (st != W4A8_OK) return st;
     if (!d_s_prepared || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-    if (M > kPreparedDecodeMaxM) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (M > kPreparedDecodeMaxM)
+        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
+                                                M, N, K, as_stream(stream)));
     const GemmPlan p = plan_prepared(M, N, K, 0, 3);
     st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
     if (st != W4A8_OK) return st;

@@ -274,6 +274,222 @@ hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// tiled band on prepared weights (M > 32): 256 weight rows x BM activation rows
+// per workgroup, K in 128-wide steps through a 3-stage LDS ring.
+//
+// Eight waves in an NWN x NWM grid; wave tile = 16*FN weight rows x 16*FM
+// activation rows of 16x16x128 MFMAs.  Every stage is filled with direct
+// global -> LDS copies (global_load_lds, 1 KiB or 256 B per wave instruction, no
+// registers): the 16 weight fragment blocks of the panel (lane order = MFMA
+// order, read back with one conflict-free ds_read_b128 per fragment), the BM x
+// 128 activation slice, whose 16-byte chunk c of row r sits at chunk position
+// c ^ ((r >> 1) & 7) (so the 16 rows of a fragment read land in 16 distinct
+// bank groups), and the panel's e8m0 dwords for the step's 4-step chunk.  One
+// barrier per step: the wait + barrier at the top of step s makes stage s
+// visible and frees stage s-1, whose slot then receives step s+2.  LDS offsets
+// start at 256: a direct-to-LDS destination of address 0 would be taken for a
+// null pointer by the address-space cast.
+// ---------------------------------------------------------------------------
+
+struct PfArgs {
+    const uint8_t* x8;
+    const float* xs;
+    const uint8_t* wt;
+    const uint8_t* st;
+    uint16_t* out;
+    int M, N, K;
+    int s_pad, c_pad, tiles16;
+    int tiles_m, tiles_n;
+};
+
+constexpr int kPfThreads = 512;
+constexpr int kPfBN = 256;
+constexpr int kPfBase = 256;
+
+// Direct global -> LDS copies, lane L's bytes landing at lds + L * size.  Issued
+// through inline asm (M0 = the wave-uniform LDS destination, set in the same
+// statement) so that the compiler's wait insertion does not treat them as LDS
+// stores of unknown address -- it would otherwise drain every copy in flight
+// before each LDS read.  Their completion is awaited explicitly (wait_vmcnt,
+// then a barrier) before the stage they fill is read; loads complete in issue
+// order, so the compiler's own vmcnt waits for other loads stay correct.
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint8_t* lds) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+}
+
+template <int BM>
+struct PfShape {
+    static constexpr int NWM = BM >= 256 ? 4 : (BM >= 128 ? 2 : 1);
+    static constexpr int NWN = 8 / NWM;
+    static constexpr int FN = kPfBN / (16 * NWN);
+    static constexpr int FM = BM / (16 * NWM);
+    static constexpr int WBYTES = kPfBN / 16 * 1024;      // weight blocks per stage
+    static constexpr int ABYTES = BM * 128;                // activation slice
+    static constexpr int SBYTES = kPfBN / 16 * 256;        // e8m0 dwords
+    static constexpr int STAGE = WBYTES + ABYTES + SBYTES;
+    static constexpr int LDS = kPfBase + 3 * STAGE;
+    static constexpr int DMA_PER_STAGE = (kPfBN / 16) / 8 + (BM / 8) / 8 + (kPfBN / 16) / 8;
+};
+
+template <int BM>
+__device__ __forceinline__ void pf_issue(const PfArgs& a, uint8_t* stage, int tm, int tn, int s,
+                                         int wave, int lane) {
+    using S = PfShape<BM>;
+    // weight fragment blocks: 16 per stage, 2 per wave
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = wave + 8 * i;
+        const int t = min(tn * 16 + b, a.tiles16 - 1);
+        lds_dma16(a.wt + ((int64_t)t * a.s_pad + s) * 1024 + 16 * lane, stage + 1024 * b);
+    }
+    // activations: BM rows x 128 B, 8 rows per wave instruction, swizzled chunks
+#pragma unroll
+    for (int i = 0; i < (BM / 8) / 8; ++i) {
+        const int ins = wave + 8 * i;
+        const int r = 8 * ins + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int m = min(tm * BM + r, a.M - 1);
+        lds_dma16(a.x8 + (int64_t)m * a.K + 128 * (int64_t)s + 16 * c, stage + S::WBYTES + 1024 * ins);
+    }
+    // e8m0 dwords of the step's 4-step chunk: 16 blocks of 256 B, 2 per wave
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = wave + 8 * i;
+        const int t = min(tn * 16 + b, a.tiles16 - 1);
+        lds_dma4(a.st + ((int64_t)t * a.c_pad + (s >> 2)) * 256 + 4 * lane,
+                 stage + S::WBYTES + S::ABYTES + 256 * b);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM>
+__device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int wm, int lane,
+                                           v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM]) {
+    using S = PfShape<BM>;
+    const int g = lane >> 4;
+    const uint8_t* ws = st;
+    const uint8_t* as = st + S::WBYTES;
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(st + S::WBYTES + S::ABYTES);
+    // activation fragments of the wave's FM column tiles, then the weight
+    // fragments one at a time against all of them, the next one's LDS read
+    // issued before the current one's products
+    v8i bx[S::FM];
+#pragma unroll
+    for (int h = 0; h < S::FM; ++h) {
+        const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
+        const int sw = (r >> 1) & 7;
+        const uint8_t* rowp = as + 128 * r;
+        bx[h] = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
+                         *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
+    }
+    const uint8_t* wp = ws + 1024 * (wn * S::FN) + 16 * lane;
+    const uint32_t* sp = ss + 64 * (wn * S::FN) + lane;
+    const int sh = 8 * (s & 3);
+    uint32_t sc = sp[0];
+    uint4 wa = *reinterpret_cast<const uint4*>(wp);
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f) {
+        const v8i af = frag_fp4(wa);
+        const int scf = (int)(sc >> sh);
+        if (f + 1 < S::FN) {
+            sc = sp[64 * (f + 1)];
+            wa = *reinterpret_cast<const uint4*>(wp + 1024 * (f + 1));
+        }
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[f][h] = mfma16<0>(af, bx[h], acc[f][h], scf);
+    }
+}
+
+// One K step: wait for this step's copies (the next step's may stay in
+// flight), barrier (stage visible to all waves; the stage used two steps ago is
+// free), start the copies two steps ahead into that free stage, compute.
+template <int BM>
+__global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
+    using S = PfShape<BM>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
+    const int total = a.tiles_m * a.tiles_n;
+    const int per_xcd = (total + 7) >> 3;
+    const int T = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (T >= total) return;
+    const int group = T / (8 * a.tiles_n);
+    const int first_m = group * 8;
+    const int gsize = min(a.tiles_m - first_m, 8);
+    const int rem = T % (8 * a.tiles_n);
+    const int tm = first_m + rem % gsize, tn = rem / gsize;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % S::NWN, wm = wave / S::NWN;
+
+    v4f acc[S::FN][S::FM];
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int steps = a.K >> 7;
+    uint8_t* const base = lds + kPfBase;
+    pf_issue<BM>(a, base, tm, tn, 0, wave, lane);
+    if (steps > 1) pf_issue<BM>(a, base + S::STAGE, tm, tn, 1, wave, lane);
+    int cur = 0, nxt = 2 * S::STAGE;       // stage offsets of steps s and s + 2
+    for (int s = 0; s < steps; ++s) {
+        // opaque to the optimiser: stage addresses are formed per step from a
+        // few lane bases and immediate offsets instead of being unrolled and
+        // hoisted into dozens of live registers
+        asm volatile("" : "+s"(cur), "+s"(nxt));
+        if (s + 1 < steps) wait_vmcnt<S::DMA_PER_STAGE>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");     // no LDS access moves across the barrier
+        if (s + 2 < steps) pf_issue<BM>(a, base + nxt, tm, tn, s + 2, wave, lane);
+        pf_compute<BM>(base + cur, s, wn, wm, lane, acc);
+        cur = cur == 2 * S::STAGE ? 0 : cur + S::STAGE;
+        nxt = nxt == 2 * S::STAGE ? 0 : nxt + S::STAGE;
+    }
+    const int g = lane >> 4;
+
+    // epilogue: lane holds rows n0..n0+3 of column m in every 16x16 tile
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int h = 0; h < S::FM; ++h) {
+        const int m = tm * BM + wm * 16 * S::FM + 16 * h + (lane & 15);
+        if (m >= a.M) continue;
+        const float sm = a.xs[m];
+#pragma unroll
+        for (int f = 0; f < S::FN; ++f) {
+            const int n0 = tn * kPfBN + (wn * S::FN + f) * 16 + 4 * g;
+            if (n0 >= a.N) continue;
+            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            if (vec) {
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[f][h][0]) | (f32_to_bf16_rne(sm * acc[f][h][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[f][h][2]) | (f32_to_bf16_rne(sm * acc[f][h][3]) << 16);
+                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[f][h][r]);
+            }
+        }
+    }
+}
+
+template <int BM>
+hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
+    const int total = a.tiles_m * a.tiles_n;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL((pf_kernel<BM>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -355,6 +571,29 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M) {
     const size_t act = (size_t)(M * ((int64_t)p.s_per * 512 + 16));
     const size_t red = (size_t)p.kw * p.rt * p.mt * 64 * 16;
     return act > red ? act : red;
+}
+
+hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
+                                 const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t stream) {
+    PfArgs a{};
+    a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.tiles16 = (int)((N + 15) / 16);
+    a.tiles_n = (int)((N + kPfBN - 1) / kPfBN);
+    if ((M + 63) / 64 * (int64_t)a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    if (M <= 64) {
+        a.tiles_m = (int)((M + 63) / 64);
+        return launch_pf<64>(a, stream);
+    }
+    if (M <= 128) {
+        a.tiles_m = (int)((M + 127) / 128);
+        return launch_pf<128>(a, stream);
+    }
+    a.tiles_m = (int)((M + 255) / 256);
+    return launch_pf<256>(a, stream);
 }
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,

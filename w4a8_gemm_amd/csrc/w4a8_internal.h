@@ -99,6 +99,9 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M);
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
                                   int64_t N, int64_t K, void* ws, hipStream_t stream);
+hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
+                                 const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 
 hipError_t launch_int4_check_transpose(const int32_t* qw_kn, const int32_t* qzeros, int64_t N,
