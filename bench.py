@@ -5,21 +5,22 @@ the merged gate_up projection (N = 2 x 17408, K = 5120, MXFP4 weights
 requantized on the GPU from NVFP4 with one global divisor per partition, then
 repacked once into matrix-core fragment order), for each batch M in
 {1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K] activation, then the
-block-scaled W4A8 GEMM -> bf16 [M, N] (fragment-order weights for M <= 32, the
-row-major weight for M = 64, which the fragment-order decode kernel does not
-cover).  Steps rotate over four copies of each weight layout (379 MB each), so no
-step is served from the 256 MB Infinity Cache.  Each step is one HIP graph
-replay (captured once per weight copy), so host launch latency is not in the
-timed region.
+block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights (split-K
+decode kernel for M <= 32, the tiled kernel for M = 64).  Steps rotate over four
+copies of the weight (95 MB each, 379 MB in all), so no step is served from the
+256 MB Infinity Cache.  Each step is one HIP graph replay (captured once per
+weight copy), so host launch latency is not in the timed region.
 
 value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
 weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
 read back, token scales, and the bf16 output.
 
 Also reported, each from its own short timed loop (HIP events on the stream the
-kernels run on): per-kernel decode GEMM durations (the roofline figure), the
-prefill GEMM (M = 4096) in TFLOP/s, the full-layer requant in GB/s for the
-three exponent rules, the down_proj decode and the int4 g128 variant.
+kernels run on): the decode GEMM per M, with the roofline taken on the decode
+kernel at M = 1 (one kernel per call there); the prefill GEMM (M = 4096) in
+TFLOP/s; the full-layer requant in GB/s for the three exponent rules; the
+down_proj decode and prefill; the int4 g128 variant; and the row-major weight
+layout's GEMM for comparison.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same step.
 """
 import argparse
@@ -38,7 +39,6 @@ METRIC = "W4A8 MXFP4 GEMM: decode HBM GB/s (M≤64), prefill TFLOPS (M=4096); re
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 DECODE_MS = (1, 8, 16, 64)
-PREPARED_MAX_M = 32
 COPIES = 4
 
 
@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill/requant/int4 loops")
-    ap.add_argument("--cpu-rows", type=int, default=8192, help="weight rows in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=34816, help="weight rows in the oracle sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -124,23 +124,17 @@ def main():
     nv_s = torch.from_numpy(g["nv_scale"]).to(dev)
     wp, we = w4.requant_nvfp4_to_mxfp4(nv_p, nv_s, g["part_rows"], g["part_divisor"],
                                        mode="mse", row_chunk=4096)
-    copies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(COPIES - 1)]
     pcopies = [w4.mxfp4_prepare(wp, we) for _ in range(COPIES)]
     xs_bf16 = {M: torch.from_numpy(synth.acts(M, K, seed=(1, M), spread=10.0).view(np.int16))
                .view(torch.bfloat16).to(dev) for M in DECODE_MS}
     x8 = {M: torch.empty((M, K), dtype=torch.uint8, device=dev) for M in DECODE_MS}
     xsc = {M: torch.empty((M,), dtype=torch.float32, device=dev) for M in DECODE_MS}
     out = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in DECODE_MS}
-    ws = w4.Workspace(max(DECODE_MS), N, K, "mxfp4", dev)
-    pws = w4.Workspace(PREPARED_MAX_M, N, K, "prepared", dev)
+    pws = w4.Workspace(max(DECODE_MS), N, K, "prepared", dev)
     torch.cuda.synchronize()
 
     def gemm(M, c):
-        if M <= PREPARED_MAX_M:
-            w4.mxfp4_gemm_prepared(x8[M], xsc[M], pcopies[c], out=out[M], workspace=pws)
-        else:
-            w_p, w_e = copies[c]
-            w4.mxfp4_gemm(x8[M], xsc[M], w_p, w_e, out=out[M], workspace=ws)
+        w4.mxfp4_gemm_prepared(x8[M], xsc[M], pcopies[c], out=out[M], workspace=pws)
 
     def step(c):
         for M in DECODE_MS:
@@ -170,20 +164,24 @@ def main():
         dt = timer(lambda i: gg.replay(), max(2, args.steps // 4)) / R
         per_m[M] = dt
         log(f"decode GEMM M={M}: {dt * 1e6:.2f} us, {gemm_bytes(M, N, K) / dt / 1e9:.1f} GB/s")
-    gemm_total_bytes = sum(gemm_bytes(M, N, K) for M in DECODE_MS)
-    gemm_total_t = sum(per_m.values())
-    achieved = gemm_total_bytes / gemm_total_t / 1e9
+    # roofline: the split-K decode kernel at M = 1, the largest share of the
+    # step and a single kernel per GEMM call (no reduction pass)
+    b1 = gemm_bytes(1, N, K)
+    achieved = b1 / per_m[1] / 1e9
     roofline = {"bound": "hbm",
-                "kernel": "decode GEMM, gate_up, M in {1,8,16,64} (pdec_kernel for M<=32, "
-                          "mx_decode_kernel + splitk_reduce for M=64); graph-timed incl. launch gaps",
+                "kernel": "pdec_kernel<1,3> (fragment-order split-K decode), gate_up M=1; "
+                          "average over graph-replayed launches rotating 4 weight copies",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "per_launch_us": {str(M): round(per_m[M] * 1e6, 3) for M in DECODE_MS},
-                "bytes_per_launch": {str(M): gemm_bytes(M, N, K) for M in DECODE_MS}}
+                "bytes_per_launch": b1, "avg_launch_us": round(per_m[1] * 1e6, 3),
+                "gemm_call_us_by_M": {str(M): round(per_m[M] * 1e6, 3) for M in DECODE_MS},
+                "gemm_call_gbps_by_M": {str(M): round(gemm_bytes(M, N, K) / per_m[M] / 1e9, 1)
+                                        for M in DECODE_MS}}
 
     extra = {}
     if not args.no_extra:
-        extra = extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, copies, dev)
+        extra = extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp, we,
+                                   pcopies, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -197,7 +195,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode gate_up: merged MXFP4 linear N=2x17408 K=5120 "
                                "(requantized from NVFP4, per-partition divisors), "
-                               "M in {1,8,16,64}, fp8 per-token act quant + GEMM per M",
+                               "M in {1,8,16,64}, fp8 per-token act quant + GEMM per M "
+                               "(fragment-order weights)",
                    "N": N, "K": K, "M": list(DECODE_MS), "weight_copies_rotated": COPIES,
                    "step_bytes": step_bytes},
         "roofline": roofline,
@@ -207,30 +206,51 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, copies, dev):
+def _timed_graph(torch, timer, graph_of, calls, reps):
+    """Average duration of one call: `calls` is a list of closures replayed as
+    one graph; the graph is replayed `reps` times after one untimed replay."""
+    gg = graph_of(torch, lambda: [c() for c in calls])
+    gg.replay()
+    return timer(lambda i: gg.replay(), reps) / len(calls)
+
+
+def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp, we, pcopies, dev):
     N, K = g["N"], g["K"]
     res = {}
-    # prefill: M = 4096 against the gate_up weight
+    # prefill: M = 4096 against the gate_up weight (fragment order, tiled kernel)
     M = 4096
     xb = torch.from_numpy(synth.acts(M, K, seed=3).view(np.int16)).view(torch.bfloat16).to(dev)
     x8, xs = w4.quant_act_fp8_per_token(xb)
     o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    gg = graph_of(torch, lambda: [w4.mxfp4_gemm(x8, xs, copies[r][0], copies[r][1], out=o)
-                                  for r in range(2)])
-    gg.replay()
-    dt = timer(lambda i: gg.replay(), 5) / 2
     flops = 2.0 * M * N * K
-    res["prefill_gemm"] = {"M": M, "N": N, "K": K, "us": round(dt * 1e6, 2),
+    dt = _timed_graph(torch, timer, graph_of,
+                      [lambda r=r: w4.mxfp4_gemm_prepared(x8, xs, pcopies[r], out=o) for r in range(4)], 5)
+    res["prefill_gemm"] = {"M": M, "N": N, "K": K, "kernel": "pf_kernel<256>", "us": round(dt * 1e6, 2),
                            "tflops": round(flops / dt / 1e12, 1),
                            "frac_of_fp8_peak": round(flops / dt / 1e12 / FP8_PEAK_TFLOPS, 4)}
     log("prefill", res["prefill_gemm"])
     aq = timer(lambda i: w4.quant_act_fp8_per_token(xb, out=x8, scale=xs), 5)
     res["act_quant_prefill"] = {"M": M, "K": K, "us": round(aq * 1e6, 2),
                                 "gbps": round((M * K * 3 + M * 4) / aq / 1e9, 1)}
-    del o, xb
+    # the row-major weight layout (no repack), for comparison: M = 1 and 4096
+    rm = {}
+    rcopies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(3)]
+    rws = w4.Workspace(1, N, K, "mxfp4", dev)
+    x1, s1 = w4.quant_act_fp8_per_token(xb[:1].contiguous())
+    o1 = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    dt1 = _timed_graph(torch, timer, graph_of,
+                       [lambda r=r: w4.mxfp4_gemm(x1, s1, rcopies[r][0], rcopies[r][1], out=o1, workspace=rws)
+                        for r in range(4)], 10)
+    rm["decode_M1"] = {"us": round(dt1 * 1e6, 2), "gbps": round(gemm_bytes(1, N, K) / dt1 / 1e9, 1)}
+    dtp = _timed_graph(torch, timer, graph_of,
+                       [lambda r=r: w4.mxfp4_gemm(x8, xs, rcopies[r][0], rcopies[r][1], out=o) for r in range(2)], 3)
+    rm["prefill_M4096"] = {"us": round(dtp * 1e6, 2), "tflops": round(flops / dtp / 1e12, 1)}
+    res["rowmajor_layout_gemm"] = rm
+    log("row-major layout", rm)
+    del o, xb, rcopies
     # full-layer requant, three rules, ROW_CHUNK passes and one pass per partition
     src = [(nv_p, nv_s), (nv_p.clone(), nv_s.clone())]
-    outs = [(torch.empty_like(copies[0][0]), torch.empty_like(copies[0][1])) for _ in range(2)]
+    outs = [(torch.empty_like(wp), torch.empty_like(we)) for _ in range(2)]
     rq = {}
     for mode in ("ocp", "noclip", "mse"):
         for chunk in (4096, 0):
@@ -246,43 +266,32 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, co
     res["requant_full_layer"] = rq
     log("requant", rq)
     del src, outs
-    # down_proj decode
+    # down_proj (K = 17408), fragment-order weights, eight copies
     d = synth.down_proj()
-    dcopies = [(torch.from_numpy(d["w_packed"]).to(dev), torch.from_numpy(d["w_e8m0"]).to(dev))
-               for _ in range(8)]
-    dws = w4.Workspace(64, d["N"], d["K"], "mxfp4", dev)
-    dp = {}
-    for M in (1, 16, 64):
-        xb = torch.from_numpy(synth.acts(M, d["K"], seed=(2, M)).view(np.int16)).view(torch.bfloat16).to(dev)
-        a8, asc = w4.quant_act_fp8_per_token(xb)
-        oo = torch.empty((M, d["N"]), dtype=torch.bfloat16, device=dev)
-        gg = graph_of(torch, lambda: [w4.mxfp4_gemm(a8, asc, dcopies[r][0], dcopies[r][1], out=oo,
-                                                    workspace=dws) for r in range(8)])
-        gg.replay()
-        dt = timer(lambda i: gg.replay(), 10) / 8
-        b = gemm_bytes(M, d["N"], d["K"])
-        dp[str(M)] = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
-                      "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
-    res["down_proj_decode"] = dp
-    log("down_proj", dp)
-    pdc = [w4.mxfp4_prepare(dcopies[r][0], dcopies[r][1]) for r in range(8)]
-    pdws = w4.Workspace(PREPARED_MAX_M, d["N"], d["K"], "prepared", dev)
+    dw = torch.from_numpy(d["w_packed"]).to(dev)
+    de = torch.from_numpy(d["w_e8m0"]).to(dev)
+    pdc = [w4.mxfp4_prepare(dw, de) for _ in range(8)]
+    pdws = w4.Workspace(64, d["N"], d["K"], "prepared", dev)
     pdp = {}
-    for M in (1, 16):
+    for M in (1, 16, 64, 4096):
         xb = torch.from_numpy(synth.acts(M, d["K"], seed=(2, M)).view(np.int16)).view(torch.bfloat16).to(dev)
         a8, asc = w4.quant_act_fp8_per_token(xb)
         oo = torch.empty((M, d["N"]), dtype=torch.bfloat16, device=dev)
-        gg = graph_of(torch, lambda: [w4.mxfp4_gemm_prepared(a8, asc, pdc[r], out=oo, workspace=pdws)
-                                      for r in range(8)])
-        gg.replay()
-        dt = timer(lambda i: gg.replay(), 10) / 8
+        reps = 8 if M <= 64 else 2
+        dt = _timed_graph(torch, timer, graph_of,
+                          [lambda r=r: w4.mxfp4_gemm_prepared(a8, asc, pdc[r], out=oo, workspace=pdws)
+                           for r in range(reps)], 10 if M <= 64 else 3)
         b = gemm_bytes(M, d["N"], d["K"])
-        pdp[str(M)] = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
-                       "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
-    res["down_proj_decode_prepared"] = pdp
+        ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+               "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
+        if M > 64:
+            fl = 2.0 * M * d["N"] * d["K"]
+            ent["tflops"] = round(fl / dt / 1e12, 1)
+            ent["frac_of_fp8_peak"] = round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4)
+        pdp[str(M)] = ent
+    res["down_proj_prepared"] = pdp
     log("down_proj prepared", pdp)
-    del pdc
-    del dcopies
+    del pdc, dw, de
     # int4 g128
     q = synth.int4()
     qnk = w4.int4g128_prepare(torch.from_numpy(q["qweight_kn"]).to(dev),
@@ -296,10 +305,9 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, co
         a8, asc = w4.quant_act_fp8_per_token(xb)
         oo = torch.empty((M, q["N"]), dtype=torch.bfloat16, device=dev)
         reps = 8 if M <= 64 else 2
-        gg = graph_of(torch, lambda: [w4.int4g128_gemm(a8, asc, qcopies[r][0], qcopies[r][1], out=oo,
-                                                       workspace=iws) for r in range(reps)])
-        gg.replay()
-        dt = timer(lambda i: gg.replay(), 10) / reps
+        dt = _timed_graph(torch, timer, graph_of,
+                          [lambda r=r: w4.int4g128_gemm(a8, asc, qcopies[r][0], qcopies[r][1], out=oo,
+                                                        workspace=iws) for r in range(reps)], 10)
         b = q["N"] * q["K"] // 2 + q["N"] * q["K"] // 64 + M * q["K"] + M * 4 + M * q["N"] * 2
         ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1)}
         if M > 64:

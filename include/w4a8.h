@@ -189,9 +189,11 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepared_bytes: sizes of the two prepared buffers (host).
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
- *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, for
- *     1 <= M <= 32 (the decode band; larger M: UNSUPPORTED_SHAPE); workspace
- *     sized with W4A8_WEIGHT_MXFP4_PREPARED.
+ *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
+ *     M >= 1.  M <= 32 runs the split-K decode kernel (workspace sized with
+ *     W4A8_WEIGHT_MXFP4_PREPARED, needed only when the activations of a K range
+ *     do not fit in LDS); larger M the tiled kernel (64/128/256 x 256 output
+ *     tiles), which needs no workspace.
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
  * WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
