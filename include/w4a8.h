@@ -193,7 +193,8 @@ w4a8_status w4a8_mxfp4_gemm(
  *     M >= 1.  M <= 32 runs the split-K decode kernel (workspace sized with
  *     W4A8_WEIGHT_MXFP4_PREPARED, needed only when the activations of a K range
  *     do not fit in LDS); larger M the tiled kernel (64/128/256 x 256 output
- *     tiles), which needs no workspace.
+ *     tiles), which needs no workspace and takes K < 2^24 (UNSUPPORTED_SHAPE
+ *     above).
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
  * WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);

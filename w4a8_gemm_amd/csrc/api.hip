@@ -159,9 +159,12 @@ w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_sc
     if (st != W4A8_OK) return st;
     if (!d_s_prepared || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-    if (M > kPreparedDecodeMaxM)
+    if (M > kPreparedDecodeMaxM) {
+        // the tiled kernel addresses a 256-row activation block with 32-bit buffer offsets
+        if (K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
         return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
                                                 M, N, K, as_stream(stream)));
+    }
     const GemmPlan p = plan_prepared(M, N, K, 0, 3);
     st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
     if (st != W4A8_OK) return st;

@@ -301,26 +301,47 @@ struct PfArgs {
     int M, N, K;
     int s_pad, c_pad, tiles16;
     int tiles_m, tiles_n;
+    int group_m;                // M tiles per group of the tile order
 };
 
 constexpr int kPfThreads = 512;
 constexpr int kPfBN = 256;
 constexpr int kPfBase = 256;
 
-// Direct global -> LDS copies, lane L's bytes landing at lds + L * size.  Issued
-// through inline asm (M0 = the wave-uniform LDS destination, set in the same
-// statement) so that the compiler's wait insertion does not treat them as LDS
-// stores of unknown address -- it would otherwise drain every copy in flight
-// before each LDS read.  Their completion is awaited explicitly (wait_vmcnt,
-// then a barrier) before the stage they fill is read; loads complete in issue
-// order, so the compiler's own vmcnt waits for other loads stay correct.
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+// Direct global -> LDS copies through buffer loads with the LDS bit: lane L's
+// 16 (4) bytes land at M0 + 16 L (4 L).  The buffer form moves L2-resident
+// data into LDS at about twice the rate of the global form on gfx950
+// (measured: ~32 vs ~14.5 TB/s aggregate for 1 KiB copies).  Issued through
+// inline asm (M0 set in the same statement) so that the compiler's wait
+// insertion does not treat them as LDS stores of unknown address -- it would
+// otherwise drain every copy in flight before each LDS read.  Their
+// completion is awaited explicitly (wait_vmcnt, then a barrier) before the
+// stage they fill is read; loads complete in issue order, so the compiler's
+// own vmcnt waits for other loads stay correct.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// raw buffer descriptor: 48-bit base, stride 0, `bytes` records (reads past
+// them return zero), dword 3 = 32-bit data format as for every gfx9 buffer
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = 0x00020000;
+    return r;
 }
-__device__ __forceinline__ void lds_dma4(const void* g, uint8_t* lds) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
 template <int BM>
@@ -329,42 +350,82 @@ struct PfShape {
     static constexpr int NWN = 8 / NWM;
     static constexpr int FN = kPfBN / (16 * NWN);
     static constexpr int FM = BM / (16 * NWM);
+    static constexpr int NS = 3;                           // ring stages
     static constexpr int WBYTES = kPfBN / 16 * 1024;      // weight blocks per stage
     static constexpr int ABYTES = BM * 128;                // activation slice
-    static constexpr int SBYTES = kPfBN / 16 * 256;        // e8m0 dwords
-    static constexpr int STAGE = WBYTES + ABYTES + SBYTES;
-    static constexpr int LDS = kPfBase + 3 * STAGE;
-    static constexpr int DMA_PER_STAGE = (kPfBN / 16) / 8 + (BM / 8) / 8 + (kPfBN / 16) / 8;
+    static constexpr int STAGE = WBYTES + ABYTES;
+    static constexpr int SBYTES = kPfBN / 16 * 256;        // e8m0 dwords of one 4-step chunk
+    static constexpr int LDS = kPfBase + NS * STAGE + 2 * SBYTES;
+    static constexpr int DMA_PER_STAGE = (kPfBN / 16) / 8 + (BM / 8) / 8;   // per wave
+    static constexpr int DMA_SCALES = (kPfBN / 16) / 8;                     // per wave, per chunk
+};
+
+// Per-workgroup copy sources: one buffer descriptor per operand based at the
+// workgroup's tile, per-lane offsets that stay fixed over the K steps (the
+// step advance goes into the scalar offset).
+template <int BM>
+struct PfSrc {
+    i32x4 w, x, sc;
+    uint32_t w_off[2], x_off[BM / 64], s_off[2];
 };
 
 template <int BM>
-__device__ __forceinline__ void pf_issue(const PfArgs& a, uint8_t* stage, int tm, int tn, int s,
-                                         int wave, int lane) {
-    using S = PfShape<BM>;
-    // weight fragment blocks: 16 per stage, 2 per wave
+__device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int wave, int lane, PfSrc<BM>& src) {
+    const int t0 = tn * 16;
+    const int64_t wblk = (int64_t)a.s_pad * 1024, sblk = (int64_t)a.c_pad * 256;
+    src.w = make_rsrc(a.wt + t0 * wblk, (uint64_t)(a.tiles16 - t0) * wblk);
+    src.sc = make_rsrc(a.st + t0 * sblk, (uint64_t)(a.tiles16 - t0) * sblk);
+    src.x = make_rsrc(a.x8 + (int64_t)tm * BM * a.K, (uint64_t)(a.M - tm * BM) * a.K);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int b = wave + 8 * i;
-        const int t = min(tn * 16 + b, a.tiles16 - 1);
-        lds_dma16(a.wt + ((int64_t)t * a.s_pad + s) * 1024 + 16 * lane, stage + 1024 * b);
+        // weight and e8m0 blocks b = wave, wave + 8 of the 16 tiles (clamped to the last tile)
+        const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
+        src.w_off[i] = (uint32_t)(t * wblk) + 16u * lane;
+        src.s_off[i] = (uint32_t)(t * sblk) + 4u * lane;
     }
-    // activations: BM rows x 128 B, 8 rows per wave instruction, swizzled chunks
 #pragma unroll
-    for (int i = 0; i < (BM / 8) / 8; ++i) {
-        const int ins = wave + 8 * i;
-        const int r = 8 * ins + (lane >> 3);
+    for (int i = 0; i < BM / 64; ++i) {
+        // activation rows: 8 per copy, 16-byte chunks XOR-swizzled by row
+        const int r = 8 * (wave + 8 * i) + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
-        const int m = min(tm * BM + r, a.M - 1);
-        lds_dma16(a.x8 + (int64_t)m * a.K + 128 * (int64_t)s + 16 * c, stage + S::WBYTES + 1024 * ins);
+        const int m = min(tm * BM + r, a.M - 1) - tm * BM;
+        src.x_off[i] = (uint32_t)m * (uint32_t)a.K + 16u * c;
     }
-    // e8m0 dwords of the step's 4-step chunk: 16 blocks of 256 B, 2 per wave
+}
+
+// Copy j (0 <= j < DMA_PER_STAGE) of this wave for K step s into `stage`:
+// two weight blocks, then BM/64 activation row groups.
+template <int BM, int J>
+__device__ __forceinline__ void pf_issue_one(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
+    using S = PfShape<BM>;
+    if constexpr (J < 2) {
+        lds_dma16(src.w, src.w_off[J], 1024u * s, lds_addr(stage + 1024 * (wave + 8 * J)));
+    } else {
+        constexpr int i = J - 2;
+        lds_dma16(src.x, src.x_off[i], 128u * s, lds_addr(stage + S::WBYTES + 1024 * (wave + 8 * i)));
+    }
+}
+
+// e8m0 dwords of 4-step chunk c (two 256-byte blocks per wave) into `sbuf`
+template <int BM>
+__device__ __forceinline__ void pf_issue_scales(const PfSrc<BM>& src, uint8_t* sbuf, int c, int wave) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int b = wave + 8 * i;
-        const int t = min(tn * 16 + b, a.tiles16 - 1);
-        lds_dma4(a.st + ((int64_t)t * a.c_pad + (s >> 2)) * 256 + 4 * lane,
-                 stage + S::WBYTES + S::ABYTES + 256 * b);
+    for (int i = 0; i < PfShape<BM>::DMA_SCALES; ++i)
+        lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
+}
+
+// copies [J0, J1) of the stage
+template <int BM, int J0, int J1>
+__device__ __forceinline__ void pf_issue_range(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
+    if constexpr (J0 < J1) {
+        pf_issue_one<BM, J0>(src, stage, s, wave);
+        pf_issue_range<BM, J0 + 1, J1>(src, stage, s, wave);
     }
+}
+
+template <int BM>
+__device__ __forceinline__ void pf_issue(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
+    pf_issue_range<BM, 0, PfShape<BM>::DMA_PER_STAGE>(src, stage, s, wave);
 }
 
 template <int N>
@@ -373,14 +434,47 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Products of one K step from `st`, with the copies of a later step into
+// `nxt` spread between the MFMA groups: a wave whose copy issue stalls on a
+// full memory queue then still has products in flight.  The order is pinned
+// with scheduling barriers (the scheduler would otherwise sink the products
+// below every copy).
+template <int BM, int F>
+__device__ __forceinline__ void pf_copies_at(const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
+    constexpr int D = PfShape<BM>::DMA_PER_STAGE, FN = PfShape<BM>::FN;
+    pf_issue_range<BM, F * D / FN, (F + 1) * D / FN>(src, nxt, s_nxt, wave);
+}
+
+template <int BM, int F>
+__device__ __forceinline__ void pf_group(const uint8_t* wp, const uint32_t* sp, int sh, const v8i (&bx)[PfShape<BM>::FM],
+                                         uint4& wa, uint32_t& sc, v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM],
+                                         const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
+    using S = PfShape<BM>;
+    if constexpr (F < S::FN) {
+        const v8i af = frag_fp4(wa);
+        const int scf = (int)(sc >> sh);
+        if constexpr (F + 1 < S::FN) {
+            sc = sp[64 * (F + 1)];
+            wa = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 1));
+        }
+        pf_copies_at<BM, F>(src, nxt, s_nxt, wave);
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[F][h] = mfma16<0>(af, bx[h], acc[F][h], scf);
+        __builtin_amdgcn_sched_barrier(0);
+        pf_group<BM, F + 1>(wp, sp, sh, bx, wa, sc, acc, src, nxt, s_nxt, wave);
+    }
+}
+
 template <int BM>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int wm, int lane,
-                                           v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM]) {
+                                           v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM],
+                                           const uint8_t* sbuf,
+                                           const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
     using S = PfShape<BM>;
     const int g = lane >> 4;
     const uint8_t* ws = st;
     const uint8_t* as = st + S::WBYTES;
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(st + S::WBYTES + S::ABYTES);
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(sbuf);
     // activation fragments of the wave's FM column tiles, then the weight
     // fragments one at a time against all of them, the next one's LDS read
     // issued before the current one's products
@@ -395,37 +489,33 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
     }
     const uint8_t* wp = ws + 1024 * (wn * S::FN) + 16 * lane;
     const uint32_t* sp = ss + 64 * (wn * S::FN) + lane;
-    const int sh = 8 * (s & 3);
     uint32_t sc = sp[0];
     uint4 wa = *reinterpret_cast<const uint4*>(wp);
-#pragma unroll
-    for (int f = 0; f < S::FN; ++f) {
-        const v8i af = frag_fp4(wa);
-        const int scf = (int)(sc >> sh);
-        if (f + 1 < S::FN) {
-            sc = sp[64 * (f + 1)];
-            wa = *reinterpret_cast<const uint4*>(wp + 1024 * (f + 1));
-        }
-#pragma unroll
-        for (int h = 0; h < S::FM; ++h) acc[f][h] = mfma16<0>(af, bx[h], acc[f][h], scf);
-    }
+    pf_group<BM, 0>(wp, sp, 8 * (s & 3), bx, wa, sc, acc, src, nxt, s_nxt, wave);
 }
 
-// One K step: wait for this step's copies (the next step's may stay in
-// flight), barrier (stage visible to all waves; the stage used two steps ago is
-// free), start the copies two steps ahead into that free stage, compute.
+
+// Three-stage ring, copies issued two steps ahead; e8m0 chunks (one per four
+// steps) in two buffers of their own.  Per step s: wait for the copies of
+// step s (those of step s + 1 may stay in flight), barrier (stage visible to
+// all waves; the stage read in step s - 1 is free), issue the e8m0 chunk that
+// starts at step s + 2 (if any), then compute, with the copies for step s + 2
+// into the free stage issued between the products.  In issue order the
+// copies of step u are: [e8m0 chunk u/4 if u % 4 == 0] [weights, activations].
 template <int BM>
 __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     using S = PfShape<BM>;
+    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
     __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
     const int total = a.tiles_m * a.tiles_n;
     const int per_xcd = (total + 7) >> 3;
     const int T = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (T >= total) return;
-    const int group = T / (8 * a.tiles_n);
-    const int first_m = group * 8;
-    const int gsize = min(a.tiles_m - first_m, 8);
-    const int rem = T % (8 * a.tiles_n);
+    const int gm = a.group_m;
+    const int group = T / (gm * a.tiles_n);
+    const int first_m = group * gm;
+    const int gsize = min(a.tiles_m - first_m, gm);
+    const int rem = T % (gm * a.tiles_n);
     const int tm = first_m + rem % gsize, tn = rem / gsize;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -439,23 +529,36 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
 
     const int steps = a.K >> 7;
     uint8_t* const base = lds + kPfBase;
-    pf_issue<BM>(a, base, tm, tn, 0, wave, lane);
-    if (steps > 1) pf_issue<BM>(a, base + S::STAGE, tm, tn, 1, wave, lane);
+    uint8_t* const sbase = base + S::NS * S::STAGE;
+    PfSrc<BM> src;
+    pf_sources<BM>(a, tm, tn, wave, lane, src);
+    // prologue: step 0 (with e8m0 chunk 0) and step 1 (repeating step 0 when K has one step)
+    pf_issue_scales<BM>(src, sbase, 0, wave);
+    pf_issue<BM>(src, base, 0, wave);
+    pf_issue<BM>(src, base + S::STAGE, min(1, steps - 1), wave);
     int cur = 0, nxt = 2 * S::STAGE;       // stage offsets of steps s and s + 2
     for (int s = 0; s < steps; ++s) {
         // opaque to the optimiser: stage addresses are formed per step from a
         // few lane bases and immediate offsets instead of being unrolled and
         // hoisted into dozens of live registers
         asm volatile("" : "+s"(cur), "+s"(nxt));
-        if (s + 1 < steps) wait_vmcnt<S::DMA_PER_STAGE>();
-        else wait_vmcnt<0>();
+        if (((s + 1) & 3) == 0 && s + 1 < steps) wait_vmcnt<D + DS>();
+        else wait_vmcnt<D>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");     // no LDS access moves across the barrier
-        if (s + 2 < steps) pf_issue<BM>(a, base + nxt, tm, tn, s + 2, wave, lane);
-        pf_compute<BM>(base + cur, s, wn, wm, lane, acc);
+        const int u = s + 2;
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        // copies for step s + 2; in the last two steps they repeat the last
+        // step into the free stage, which is never read again (no branch in
+        // the product sequence)
+        pf_compute<BM>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * S::SBYTES, src, base + nxt,
+                       min(u, steps - 1), wave);
         cur = cur == 2 * S::STAGE ? 0 : cur + S::STAGE;
         nxt = nxt == 2 * S::STAGE ? 0 : nxt + S::STAGE;
     }
+    // the repeated copies of the last steps may still be landing: drain them
+    // before the workgroup's LDS is released
+    wait_vmcnt<0>();
     const int g = lane >> 4;
 
     // epilogue: lane holds rows n0..n0+3 of column m in every 16x16 tile
@@ -584,6 +687,7 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     a.tiles16 = (int)((N + 15) / 16);
     a.tiles_n = (int)((N + kPfBN - 1) / kPfBN);
     if ((M + 63) / 64 * (int64_t)a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    a.group_m = 8;
     if (M <= 64) {
         a.tiles_m = (int)((M + 63) / 64);
         return launch_pf<64>(a, stream);

@@ -103,6 +103,9 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
                                  hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
+// largest K of the tiled kernel on prepared weights (32-bit buffer offsets
+// into a 256-row activation block: 256 * K < 2^32)
+constexpr int64_t kPreparedTiledMaxK = (1 << 24) - 128;
 
 hipError_t launch_int4_check_transpose(const int32_t* qw_kn, const int32_t* qzeros, int64_t N,
                                        int64_t K, int32_t* qw_nk, uint32_t* bad_count,
