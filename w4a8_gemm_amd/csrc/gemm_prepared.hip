@@ -145,6 +145,31 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int 
     }
 }
 
+constexpr int kActBatch = 8;
+
+// activation elements q0 + u * nthreads (u < kActBatch) of the workgroup's
+// [M, kr] slice, 16 bytes each
+__device__ __forceinline__ void pdec_act_load(const PDecArgs& a, int kbase, int per_row, int total, int q0,
+                                              int nthreads, uint4 (&v)[kActBatch]) {
+#pragma unroll
+    for (int u = 0; u < kActBatch; ++u) {
+        const int q = q0 + u * nthreads;
+        const int m = q / per_row, col = q - m * per_row;
+        const int k = kbase + 16 * col;
+        v[u] = (q < total && k < a.K) ? *reinterpret_cast<const uint4*>(a.x8 + (int64_t)m * a.K + k)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_row, int total, int q0,
+                                               int nthreads, const uint4 (&v)[kActBatch]) {
+#pragma unroll
+    for (int u = 0; u < kActBatch; ++u) {
+        const int q = q0 + u * nthreads;
+        const int m = q / per_row, col = q - m * per_row;
+        if (q < total) *reinterpret_cast<uint4*>(xl + m * stride + 16 * col) = v[u];
+    }
+}
+
 template <int MT, int D>
 __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
@@ -175,19 +200,23 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const uint32_t* sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
     const int last = nch > 0 ? nch - 1 : 0;
 
-    // weight ring prologue first (HBM latency overlaps the activation copy)
+    // Activations of this workgroup's K range -> LDS (columns >= K read as
+    // zero), 16 bytes per thread and load, in batches of kActBatch loads per
+    // thread so that their latencies overlap.  The first batch is issued
+    // before the weight ring prologue: its LDS writes then wait only for these
+    // (L2-resident) loads while the weight loads stay in flight.
+    const int per_row = kr / 16, act_total = a.M * per_row;
+    uint4 av[kActBatch];
+    pdec_act_load(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
+    __builtin_amdgcn_sched_barrier(0);
     PChunk ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) pdec_load(wp, sp, min(d, last), ring[d]);
-
-    // activations of this workgroup's K range -> LDS (columns >= K read as zero)
-    const int per_row = kr / 16;
-    for (int q = threadIdx.x; q < a.M * per_row; q += nthreads) {
-        const int m = q / per_row, col = q - m * per_row;
-        const int k = kbase + 16 * col;
-        const uint4 v = k < a.K ? *reinterpret_cast<const uint4*>(a.x8 + (int64_t)m * a.K + k)
-                                : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(xl + m * stride + 16 * col) = v;
+    __builtin_amdgcn_sched_barrier(0);
+    pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
+    for (int q0 = threadIdx.x + kActBatch * nthreads; q0 < act_total; q0 += kActBatch * nthreads) {
+        pdec_act_load(a, kbase, per_row, act_total, q0, nthreads, av);
+        pdec_act_store(xl, stride, per_row, act_total, q0, nthreads, av);
     }
     __syncthreads();
 
