@@ -190,11 +190,14 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
- *     M >= 1.  M <= 32 runs the split-K decode kernel (workspace sized with
- *     W4A8_WEIGHT_MXFP4_PREPARED, needed only when the activations of a K range
- *     do not fit in LDS); larger M the tiled kernel (64/128/256 x 256 output
- *     tiles), which needs no workspace and takes K < 2^24 (UNSUPPORTED_SHAPE
- *     above).
+ *     M >= 1.  Small M runs the split-K decode kernel (M <= 12; M <= 32 on
+ *     narrow layers: fewer than 64 column tiles of 256); M <= 64 on narrow
+ *     layers a register-streamed kernel with K split across workgroups;
+ *     otherwise the tiled kernel (64/128/256 x 256 output tiles).  A workspace
+ *     sized with W4A8_WEIGHT_MXFP4_PREPARED for the largest M covers every
+ *     case (the tiled kernel needs none).  Above the split-K decode kernel's
+ *     range K must be < 2^24 (UNSUPPORTED_SHAPE): those kernels address a
+ *     256-row activation block with 32-bit offsets.
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
  * WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);

@@ -319,3 +319,54 @@ def test_mxfp4_prepared_tiled_down_proj():
     ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
     ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
     assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
+
+
+# 256-wide tiles at every tile height (chosen when 256-wide tiles give at least
+# one workgroup per CU): sampled outputs against the oracle
+@pytest.mark.parametrize("M,N,K", [(40, 65600, 256), (100, 65600, 384), (300, 33000, 384)])
+def test_mxfp4_prepared_tiled_wide(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 3))
+    x8, s = _acts(M, K, (M, K, 3), spread=10.0)
+    say("prepared tiled wide", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(M + N)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 8192), np.full(64, M - 1)])
+    ni = np.concatenate([g.integers(0, N, M), g.integers(0, N, 8192), N - 1 - np.arange(64)])
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni)
+    assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
+    slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
+    assert (np.abs(got[mi, ni] - ref) <= slack).all()
+
+
+# register-streamed band: 33 <= M <= 64 on layers too narrow for the tiled
+# kernel, K split across workgroups (fp32 partials + reduction) when long
+@pytest.mark.parametrize("M,N,K", [(33, 16, 1152), (64, 200, 1024), (40, 2000, 2048), (48, 1000, 4096),
+                                   (57, 301, 3200)])
+def test_mxfp4_prepared_regstream(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 4))
+    x8, s = _acts(M, K, (M, K, 4), spread=10.0)
+    say("prepared regstream", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    again = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(got, again)
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"])
+    assert rel_frobenius(got, ref) <= GEMM_REL_F
+    slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
+    assert (np.abs(got - ref) <= slack).all()
+
+
+def test_mxfp4_prepared_regstream_down_proj():
+    d = synth.down_proj()
+    M = 64
+    x8, s = _acts(M, synth.INTERMEDIATE, (5, M))
+    pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
+    say("prepared regstream down_proj", M)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(6)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
+    ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
+    ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
+    assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F

@@ -100,10 +100,15 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     size_t need = 0;
     const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
     for (int64_t m = 1; m <= top; ++m) {
-        const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K)
-                           : kind == W4A8_WEIGHT_INT4G128 ? plan_int4(m, N, K)
-                           : (m <= kPreparedDecodeMaxM ? plan_prepared(m, N, K, 0, 3) : GemmPlan{1, 0, 0, 0, 0, 0, 0, 0});
-        const size_t b = plan_workspace_bytes(p, m, N);
+        size_t b = 0;
+        if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
+            const PreparedRoute r = prepared_route(m, N, K);
+            if (r == PreparedRoute::Decode) b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 3), m, N);
+            else if (r == PreparedRoute::RegStream) b = pdr_workspace_bytes(m, N, K);
+        } else {
+            const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K) : plan_int4(m, N, K);
+            b = plan_workspace_bytes(p, m, N);
+        }
         if (b > need) need = b;
     }
     return need;
@@ -159,17 +164,26 @@ w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_sc
     if (st != W4A8_OK) return st;
     if (!d_s_prepared || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-    if (M > kPreparedDecodeMaxM) {
-        // the tiled kernel addresses a 256-row activation block with 32-bit buffer offsets
-        if (K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    // the tiled and register-streamed kernels address activations with 32-bit offsets
+    const PreparedRoute route = prepared_route(M, N, K);
+    if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    switch (route) {
+    case PreparedRoute::Tiled:
         return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
                                                 M, N, K, as_stream(stream)));
+    case PreparedRoute::RegStream:
+        st = check_workspace(pdr_workspace_bytes(M, N, K), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_regstream(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
+                                                    M, N, K, d_ws, as_stream(stream)));
+    default: {
+        const GemmPlan p = plan_prepared(M, N, K, 0, 3);
+        st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared,
+                                                 d_out, M, N, K, d_ws, as_stream(stream)));
     }
-    const GemmPlan p = plan_prepared(M, N, K, 0, 3);
-    st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
-    if (st != W4A8_OK) return st;
-    return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared,
-                                             d_out, M, N, K, d_ws, as_stream(stream)));
+    }
 }
 
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,

@@ -304,6 +304,176 @@ hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode band with register-streamed weights (16 < M <= 64 and narrow layers)
+//
+// A workgroup of WW waves owns WW 16-row weight tiles, one per wave, and a
+// range of K steps (the whole K, or one of ks splits).  Each wave streams its
+// tile's 1 KiB fragment blocks straight from HBM into a P-deep register ring
+// (P steps ahead), so the weight bytes in flight grow with the number of
+// waves, not with LDS.  Only the activation slice of a step (MT x 16 rows x
+// 128 B) goes through LDS, double-buffered: every wave loads its share into
+// registers together with its weight block, P steps ahead, and writes it one
+// step before use (rows XOR-swizzled in 16-byte chunks, as in the tiled
+// kernels).  Per step j: write the activation slice of step j + 1, read the
+// fragments of step j and multiply, issue the loads of step j + P into the
+// freed ring slot, then lgkmcnt(0) and a barrier (slice j + 1 visible, slice
+// j free).  All loads are ordinary compiler-visible loads, so the compiler's
+// in-order vmcnt bookkeeping is exact.
+// ---------------------------------------------------------------------------
+
+struct PDrArgs {
+    const uint8_t* x8;
+    const float* xs;
+    const uint4* wt;
+    const uint32_t* st;
+    uint16_t* out;
+    float* partials;
+    int M, N, K;
+    int s_pad, c_pad;   // padded 128-steps and 4-step chunks per row tile
+    int tiles;          // 16-row tiles
+    int groups;         // workgroups per K split (ceil(tiles / WW))
+    int ks, sp;         // K splits, steps per split
+};
+
+template <int MT, int WW>
+struct PDrSlot {
+    uint4 w;                                  // weight fragment block of one step
+    uint32_t sc;                              // its e8m0 dword (byte = step % 4)
+    uint32_t x[(MT * 8 + WW - 1) / WW];       // this wave's share of the activation slice
+};
+
+template <int MT, int WW>
+__device__ __forceinline__ void pdr_load(const PDrArgs& a, const uint4* wp, const uint32_t* sp, int s, int wave,
+                                         const uint32_t (&xoff)[(MT * 8 + WW - 1) / WW], PDrSlot<MT, WW>& r) {
+    constexpr int U = (MT * 8 + WW - 1) / WW;
+    // activations first: their LDS write, one step before use, then waits only for them
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+        if (wave + WW * i < MT * 8)
+            r.x[i] = *reinterpret_cast<const uint32_t*>(a.x8 + xoff[i] + 128 * (int64_t)s);
+    r.w = wp[(int64_t)s * 64];
+    r.sc = sp[(int64_t)(s >> 2) * 64];
+}
+
+template <int MT, int WW>
+__device__ __forceinline__ void pdr_write(uint8_t* slice, int wave, int lane, const PDrSlot<MT, WW>& r) {
+    constexpr int U = (MT * 8 + WW - 1) / WW;
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+        if (wave + WW * i < MT * 8)
+            *reinterpret_cast<uint32_t*>(slice + 256 * (wave + WW * i) + 4 * lane) = r.x[i];
+}
+
+template <int MT>
+__device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const uint4& w, uint32_t sc, int s,
+                                        v4f (&acc)[MT]) {
+    const int g = lane >> 4;
+    const v8i aw = frag_fp4(w);
+    const int scf = (int)(sc >> (8 * (s & 3)));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * mt + (lane & 15);
+        const int sw = (r >> 1) & 7;
+        const uint8_t* rowp = slice + 128 * r;
+        const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
+                                *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
+        acc[mt] = mfma16<0>(aw, bx, acc[mt], scf);
+    }
+}
+
+template <int MT, int WW, int P>
+__global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
+    constexpr int U = (MT * 8 + WW - 1) / WW;
+    constexpr int SLICE = MT * 2048;
+    __shared__ __attribute__((aligned(16))) uint8_t xl[2 * SLICE];
+    const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t_raw = tg * WW + wave;
+    const int t = min(t_raw, a.tiles - 1);           // idle waves stream a valid tile, write nothing
+    const int steps = a.K >> 7;
+    const int s0 = split * a.sp;
+    const int n = min(steps - s0, a.sp);             // >= 1 (host)
+    const uint4* wp = a.wt + (int64_t)t * a.s_pad * 64 + lane;
+    const uint32_t* scp = a.st + (int64_t)t * a.c_pad * 64 + lane;
+    // this wave's activation copy units: unit q covers slice rows 2q, 2q + 1
+    // (256 bytes, 4 per lane); lane -> row 2q + lane / 32, swizzled chunk
+    // position (lane % 32) / 4, byte 4 (lane % 4) of it
+    uint32_t xoff[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int q = wave + WW * i;
+        const int r = 2 * q + (lane >> 5);
+        const int c = ((lane & 31) >> 2) ^ ((r >> 1) & 7);
+        const int m = min(min(r, MT * 16 - 1), a.M - 1);
+        xoff[i] = (uint32_t)m * (uint32_t)a.K + 16u * c + 4u * (lane & 3);
+    }
+
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    PDrSlot<MT, WW> ring[P];
+#pragma unroll
+    for (int d = 0; d < P; ++d) pdr_load<MT, WW>(a, wp, scp, s0 + min(d, n - 1), wave, xoff, ring[d]);
+    pdr_write<MT, WW>(xl, wave, lane, ring[0]);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+
+    for (int j0 = 0; j0 < n; j0 += P) {
+#pragma unroll
+        for (int d = 0; d < P; ++d) {
+            const int j = j0 + d;
+            // slice j + 1 (its registers are in slot d + 1) into the free buffer
+            if (j + 1 < n) pdr_write<MT, WW>(xl + ((j + 1) & 1) * SLICE, wave, lane, ring[(d + 1) % P]);
+            if (j < n) pdr_mma<MT>(xl + (j & 1) * SLICE, lane, ring[d].w, ring[d].sc, s0 + j, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            // step j + P into the slot just consumed (past the end: the last step again)
+            pdr_load<MT, WW>(a, wp, scp, s0 + min(j + P, n - 1), wave, xoff, ring[d]);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+        }
+    }
+
+    if (t_raw >= a.tiles) return;
+    const int g = lane >> 4;
+    const int n0 = 16 * t + 4 * g;
+    if (n0 >= a.N) return;
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + (lane & 15);
+        if (m >= a.M) continue;
+        if (a.ks == 1) {
+            const float sm = a.xs[m];
+            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            if (vec) {
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[mt][2]) | (f32_to_bf16_rne(sm * acc[mt][3]) << 16);
+                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[mt][r]);
+            }
+        } else {
+            float* pp = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
+            if (vec) {
+                *reinterpret_cast<float4*>(pp) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < a.N) pp[r] = acc[mt][r];
+            }
+        }
+    }
+}
+
+template <int MT, int WW, int P>
+hipError_t launch_pdr(const PDrArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((pdr_kernel<MT, WW, P>), dim3(a.groups * a.ks), dim3(WW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // tiled band on prepared weights (M > 32): 256 weight rows x BM activation rows
 // per workgroup, K in 128-wide steps through a 3-stage LDS ring.
 //
@@ -334,7 +504,6 @@ struct PfArgs {
 };
 
 constexpr int kPfThreads = 512;
-constexpr int kPfBN = 256;
 constexpr int kPfBase = 256;
 
 // Direct global -> LDS copies through buffer loads with the LDS bit: lane L's
@@ -373,41 +542,39 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t voff, uint32_
                  ::"v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
-template <int BM>
+template <int BM, int BN>
 struct PfShape {
     static constexpr int NWM = BM >= 256 ? 4 : (BM >= 128 ? 2 : 1);
     static constexpr int NWN = 8 / NWM;
-    static constexpr int FN = kPfBN / (16 * NWN);
+    static constexpr int FN = BN / (16 * NWN);
     static constexpr int FM = BM / (16 * NWM);
-    static constexpr int NS = 3;                           // ring stages
-    static constexpr int WBYTES = kPfBN / 16 * 1024;      // weight blocks per stage
+    static constexpr int WBYTES = BN / 16 * 1024;      // weight blocks per stage
     static constexpr int ABYTES = BM * 128;                // activation slice
     static constexpr int STAGE = WBYTES + ABYTES;
-    static constexpr int SBYTES = kPfBN / 16 * 256;        // e8m0 dwords of one 4-step chunk
-    static constexpr int LDS = kPfBase + NS * STAGE + 2 * SBYTES;
-    static constexpr int DMA_PER_STAGE = (kPfBN / 16) / 8 + (BM / 8) / 8;   // per wave
-    static constexpr int DMA_SCALES = (kPfBN / 16) / 8;                     // per wave, per chunk
+    static constexpr int SBYTES = BN / 16 * 256;        // e8m0 dwords of one 4-step chunk
+    static constexpr int DMA_PER_STAGE = (BN / 16) / 8 + (BM / 8) / 8;   // per wave
+    static constexpr int DMA_SCALES = (BN / 16) / 8;                     // per wave, per chunk
 };
 
 // Per-workgroup copy sources: one buffer descriptor per operand based at the
 // workgroup's tile, per-lane offsets that stay fixed over the K steps (the
 // step advance goes into the scalar offset).
-template <int BM>
+template <int BM, int BN>
 struct PfSrc {
     i32x4 w, x, sc;
-    uint32_t w_off[2], x_off[BM / 64], s_off[2];
+    uint32_t w_off[BN / 128], x_off[BM / 64], s_off[BN / 128];
 };
 
-template <int BM>
-__device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int wave, int lane, PfSrc<BM>& src) {
-    const int t0 = tn * 16;
+template <int BM, int BN>
+__device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int wave, int lane, PfSrc<BM, BN>& src) {
+    const int t0 = tn * (BN / 16);
     const int64_t wblk = (int64_t)a.s_pad * 1024, sblk = (int64_t)a.c_pad * 256;
     src.w = make_rsrc(a.wt + t0 * wblk, (uint64_t)(a.tiles16 - t0) * wblk);
     src.sc = make_rsrc(a.st + t0 * sblk, (uint64_t)(a.tiles16 - t0) * sblk);
     src.x = make_rsrc(a.x8 + (int64_t)tm * BM * a.K, (uint64_t)(a.M - tm * BM) * a.K);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        // weight and e8m0 blocks b = wave, wave + 8 of the 16 tiles (clamped to the last tile)
+    for (int i = 0; i < BN / 128; ++i) {
+        // weight and e8m0 blocks b = wave + 8 i of the BN/16 tiles (clamped to the last tile)
         const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
         src.w_off[i] = (uint32_t)(t * wblk) + 16u * lane;
         src.s_off[i] = (uint32_t)(t * sblk) + 4u * lane;
@@ -423,38 +590,38 @@ __device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int 
 }
 
 // Copy j (0 <= j < DMA_PER_STAGE) of this wave for K step s into `stage`:
-// two weight blocks, then BM/64 activation row groups.
-template <int BM, int J>
-__device__ __forceinline__ void pf_issue_one(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
-    using S = PfShape<BM>;
-    if constexpr (J < 2) {
+// BN/128 weight blocks, then BM/64 activation row groups.
+template <int BM, int BN, int J>
+__device__ __forceinline__ void pf_issue_one(const PfSrc<BM, BN>& src, uint8_t* stage, int s, int wave) {
+    using S = PfShape<BM, BN>;
+    if constexpr (J < BN / 128) {
         lds_dma16(src.w, src.w_off[J], 1024u * s, lds_addr(stage + 1024 * (wave + 8 * J)));
     } else {
-        constexpr int i = J - 2;
+        constexpr int i = J - BN / 128;
         lds_dma16(src.x, src.x_off[i], 128u * s, lds_addr(stage + S::WBYTES + 1024 * (wave + 8 * i)));
     }
 }
 
 // e8m0 dwords of 4-step chunk c (two 256-byte blocks per wave) into `sbuf`
-template <int BM>
-__device__ __forceinline__ void pf_issue_scales(const PfSrc<BM>& src, uint8_t* sbuf, int c, int wave) {
+template <int BM, int BN>
+__device__ __forceinline__ void pf_issue_scales(const PfSrc<BM, BN>& src, uint8_t* sbuf, int c, int wave) {
 #pragma unroll
-    for (int i = 0; i < PfShape<BM>::DMA_SCALES; ++i)
+    for (int i = 0; i < PfShape<BM, BN>::DMA_SCALES; ++i)
         lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
 }
 
 // copies [J0, J1) of the stage
-template <int BM, int J0, int J1>
-__device__ __forceinline__ void pf_issue_range(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
+template <int BM, int BN, int J0, int J1>
+__device__ __forceinline__ void pf_issue_range(const PfSrc<BM, BN>& src, uint8_t* stage, int s, int wave) {
     if constexpr (J0 < J1) {
-        pf_issue_one<BM, J0>(src, stage, s, wave);
-        pf_issue_range<BM, J0 + 1, J1>(src, stage, s, wave);
+        pf_issue_one<BM, BN, J0>(src, stage, s, wave);
+        pf_issue_range<BM, BN, J0 + 1, J1>(src, stage, s, wave);
     }
 }
 
-template <int BM>
-__device__ __forceinline__ void pf_issue(const PfSrc<BM>& src, uint8_t* stage, int s, int wave) {
-    pf_issue_range<BM, 0, PfShape<BM>::DMA_PER_STAGE>(src, stage, s, wave);
+template <int BM, int BN>
+__device__ __forceinline__ void pf_issue(const PfSrc<BM, BN>& src, uint8_t* stage, int s, int wave) {
+    pf_issue_range<BM, BN, 0, PfShape<BM, BN>::DMA_PER_STAGE>(src, stage, s, wave);
 }
 
 template <int N>
@@ -468,17 +635,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // full memory queue then still has products in flight.  The order is pinned
 // with scheduling barriers (the scheduler would otherwise sink the products
 // below every copy).
-template <int BM, int F>
-__device__ __forceinline__ void pf_copies_at(const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
-    constexpr int D = PfShape<BM>::DMA_PER_STAGE, FN = PfShape<BM>::FN;
-    pf_issue_range<BM, F * D / FN, (F + 1) * D / FN>(src, nxt, s_nxt, wave);
+template <int BM, int BN, int F>
+__device__ __forceinline__ void pf_copies_at(const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
+    constexpr int D = PfShape<BM, BN>::DMA_PER_STAGE, FN = PfShape<BM, BN>::FN;
+    pf_issue_range<BM, BN, F * D / FN, (F + 1) * D / FN>(src, nxt, s_nxt, wave);
 }
 
-template <int BM, int F>
-__device__ __forceinline__ void pf_group(const uint8_t* wp, const uint32_t* sp, int sh, const v8i (&bx)[PfShape<BM>::FM],
-                                         uint4& wa, uint32_t& sc, v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM],
-                                         const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
-    using S = PfShape<BM>;
+template <int BM, int BN, int F>
+__device__ __forceinline__ void pf_group(const uint8_t* wp, const uint32_t* sp, int sh, const v8i (&bx)[PfShape<BM, BN>::FM],
+                                         uint4& wa, uint32_t& sc, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+                                         const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
+    using S = PfShape<BM, BN>;
     if constexpr (F < S::FN) {
         const v8i af = frag_fp4(wa);
         const int scf = (int)(sc >> sh);
@@ -486,20 +653,20 @@ __device__ __forceinline__ void pf_group(const uint8_t* wp, const uint32_t* sp, 
             sc = sp[64 * (F + 1)];
             wa = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 1));
         }
-        pf_copies_at<BM, F>(src, nxt, s_nxt, wave);
+        pf_copies_at<BM, BN, F>(src, nxt, s_nxt, wave);
 #pragma unroll
         for (int h = 0; h < S::FM; ++h) acc[F][h] = mfma16<0>(af, bx[h], acc[F][h], scf);
         __builtin_amdgcn_sched_barrier(0);
-        pf_group<BM, F + 1>(wp, sp, sh, bx, wa, sc, acc, src, nxt, s_nxt, wave);
+        pf_group<BM, BN, F + 1>(wp, sp, sh, bx, wa, sc, acc, src, nxt, s_nxt, wave);
     }
 }
 
-template <int BM>
+template <int BM, int BN>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int wm, int lane,
-                                           v4f (&acc)[PfShape<BM>::FN][PfShape<BM>::FM],
+                                           v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                            const uint8_t* sbuf,
-                                           const PfSrc<BM>& src, uint8_t* nxt, int s_nxt, int wave) {
-    using S = PfShape<BM>;
+                                           const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
+    using S = PfShape<BM, BN>;
     const int g = lane >> 4;
     const uint8_t* ws = st;
     const uint8_t* as = st + S::WBYTES;
@@ -520,77 +687,35 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
     const uint32_t* sp = ss + 64 * (wn * S::FN) + lane;
     uint32_t sc = sp[0];
     uint4 wa = *reinterpret_cast<const uint4*>(wp);
-    pf_group<BM, 0>(wp, sp, 8 * (s & 3), bx, wa, sc, acc, src, nxt, s_nxt, wave);
+    pf_group<BM, BN, 0>(wp, sp, 8 * (s & 3), bx, wa, sc, acc, src, nxt, s_nxt, wave);
 }
 
 
-// Three-stage ring, copies issued two steps ahead; e8m0 chunks (one per four
-// steps) in two buffers of their own.  Per step s: wait for the copies of
-// step s (those of step s + 1 may stay in flight), barrier (stage visible to
-// all waves; the stage read in step s - 1 is free), issue the e8m0 chunk that
-// starts at step s + 2 (if any), then compute, with the copies for step s + 2
-// into the free stage issued between the products.  In issue order the
-// copies of step u are: [e8m0 chunk u/4 if u % 4 == 0] [weights, activations].
-template <int BM>
-__global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
-    using S = PfShape<BM>;
-    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
+// Output tile of this workgroup: workgroup ids are dealt round-robin over
+// the 8 XCDs, so consecutive tiles go to consecutive ids on one XCD; tiles
+// are numbered in groups of group_m M-tiles so that the workgroups resident
+// on an XCD share weight and activation panels in its L2.
+__device__ __forceinline__ bool pf_tile(const PfArgs& a, int& tm, int& tn) {
     const int total = a.tiles_m * a.tiles_n;
     const int per_xcd = (total + 7) >> 3;
     const int T = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (T >= total) return;
+    if (T >= total) return false;
     const int gm = a.group_m;
     const int group = T / (gm * a.tiles_n);
     const int first_m = group * gm;
     const int gsize = min(a.tiles_m - first_m, gm);
     const int rem = T % (gm * a.tiles_n);
-    const int tm = first_m + rem % gsize, tn = rem / gsize;
+    tm = first_m + rem % gsize;
+    tn = rem / gsize;
+    return true;
+}
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wn = wave % S::NWN, wm = wave / S::NWN;
-
-    v4f acc[S::FN][S::FM];
-#pragma unroll
-    for (int f = 0; f < S::FN; ++f)
-#pragma unroll
-        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int steps = a.K >> 7;
-    uint8_t* const base = lds + kPfBase;
-    uint8_t* const sbase = base + S::NS * S::STAGE;
-    PfSrc<BM> src;
-    pf_sources<BM>(a, tm, tn, wave, lane, src);
-    // prologue: step 0 (with e8m0 chunk 0) and step 1 (repeating step 0 when K has one step)
-    pf_issue_scales<BM>(src, sbase, 0, wave);
-    pf_issue<BM>(src, base, 0, wave);
-    pf_issue<BM>(src, base + S::STAGE, min(1, steps - 1), wave);
-    int cur = 0, nxt = 2 * S::STAGE;       // stage offsets of steps s and s + 2
-    for (int s = 0; s < steps; ++s) {
-        // opaque to the optimiser: stage addresses are formed per step from a
-        // few lane bases and immediate offsets instead of being unrolled and
-        // hoisted into dozens of live registers
-        asm volatile("" : "+s"(cur), "+s"(nxt));
-        if (((s + 1) & 3) == 0 && s + 1 < steps) wait_vmcnt<D + DS>();
-        else wait_vmcnt<D>();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");     // no LDS access moves across the barrier
-        const int u = s + 2;
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
-        // copies for step s + 2; in the last two steps they repeat the last
-        // step into the free stage, which is never read again (no branch in
-        // the product sequence)
-        pf_compute<BM>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * S::SBYTES, src, base + nxt,
-                       min(u, steps - 1), wave);
-        cur = cur == 2 * S::STAGE ? 0 : cur + S::STAGE;
-        nxt = nxt == 2 * S::STAGE ? 0 : nxt + S::STAGE;
-    }
-    // the repeated copies of the last steps may still be landing: drain them
-    // before the workgroup's LDS is released
-    wait_vmcnt<0>();
+// lane holds rows n0..n0+3 of column m in every 16x16 tile: out = bf16(s_m * acc)
+template <int BM, int BN>
+__device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int wn, int wm, int lane,
+                                            const v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM]) {
+    using S = PfShape<BM, BN>;
     const int g = lane >> 4;
-
-    // epilogue: lane holds rows n0..n0+3 of column m in every 16x16 tile
     const bool vec = (a.N & 3) == 0;
 #pragma unroll
     for (int h = 0; h < S::FM; ++h) {
@@ -599,7 +724,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         const float sm = a.xs[m];
 #pragma unroll
         for (int f = 0; f < S::FN; ++f) {
-            const int n0 = tn * kPfBN + (wn * S::FN + f) * 16 + 4 * g;
+            const int n0 = tn * BN + (wn * S::FN + f) * 16 + 4 * g;
             if (n0 >= a.N) continue;
             uint16_t* o = a.out + (int64_t)m * a.N + n0;
             if (vec) {
@@ -614,11 +739,253 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     }
 }
 
-template <int BM>
+// NS-stage ring, copies issued NS - 1 steps ahead; e8m0 chunks (one per four
+// steps) in two buffers of their own (chunk c in buffer c & 1: with NS <= 5,
+// chunk c is copied from step 4c - NS + 1 >= 4c - 4 on, after the last use of
+// chunk c - 2 at step 4c - 5).  Per step s: wait for the copies of step s
+// (those of steps s + 1 .. s + NS - 2 may stay in flight), barrier (stage
+// visible to all waves; the stage read in step s - 1 is free), issue the e8m0
+// chunk that starts at step u = s + NS - 1 (if any), then compute, with the
+// copies for step u into the free stage issued between the products.  In
+// issue order the copies of step u are: [e8m0 chunk u/4 if u % 4 == 0 and
+// u < steps] [weights, activations (of step min(u, steps - 1))].
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
+    using S = PfShape<BM, BN>;
+    static_assert(NS >= 3 && NS <= 5, "ring depth");
+    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
+    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * S::SBYTES;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+    int tm, tn;
+    if (!pf_tile(a, tm, tn)) return;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % S::NWN, wm = wave / S::NWN;
+
+    v4f acc[S::FN][S::FM];
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int steps = a.K >> 7;
+    uint8_t* const base = lds + kPfBase;
+    uint8_t* const sbase = base + NS * S::STAGE;
+    PfSrc<BM, BN> src;
+    pf_sources<BM, BN>(a, tm, tn, wave, lane, src);
+    // prologue: steps 0 .. NS - 2 (repeating the last step when K is shorter)
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
+    }
+    int cur = 0, nxt = (NS - 1) * S::STAGE;   // stage offsets of steps s and s + NS - 1
+    for (int s = 0; s < steps; ++s) {
+        // opaque to the optimiser: stage addresses are formed per step from a
+        // few lane bases and immediate offsets instead of being unrolled and
+        // hoisted into dozens of live registers
+        asm volatile("" : "+s"(cur), "+s"(nxt));
+        // copies allowed in flight: those of steps s + 1 .. s + NS - 2, which
+        // include at most one e8m0 chunk (NS - 2 <= 3 consecutive steps)
+        bool chunk_ahead = false;
+#pragma unroll
+        for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < steps;
+        if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
+        else wait_vmcnt<(NS - 2) * D>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");     // no LDS access moves across the barrier
+        const int u = s + NS - 1;
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        // copies for step u; in the last NS - 1 steps they repeat the last step
+        // into the free stage, which is never read again (no branch in the
+        // product sequence)
+        pf_compute<BM, BN>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * S::SBYTES, src, base + nxt,
+                           min(u, steps - 1), wave);
+        cur = cur == (NS - 1) * S::STAGE ? 0 : cur + S::STAGE;
+        nxt = nxt == (NS - 1) * S::STAGE ? 0 : nxt + S::STAGE;
+    }
+    // the repeated copies of the last steps may still be landing: drain them
+    // before the workgroup's LDS is released
+    wait_vmcnt<0>();
+    pf_epilogue<BM, BN>(a, tm, tn, wn, wm, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled band, short tiles (BM <= 128, decode-sized M): the same stages and
+// copies, software-pipelined across steps.  A wave holds two register sets
+// of fragments (activations, weights, e8m0 dwords of one step); in iteration
+// s it multiplies set s while the barrier for stage s + 1 and the LDS reads of
+// set s + 1 happen between its MFMA groups, so neither the barrier nor the
+// LDS latency stalls the matrix pipe (with one workgroup per CU at these M,
+// nothing else would hide them).
+//
+// Iteration s: [e8m0 chunk for step u = s + NS - 1] [first half of the MFMA
+// groups of step s, the copies for step u into stage (s - 1) % NS between
+// them] [wait for the copies of step s + 1; lgkmcnt(0); barrier; LDS reads of
+// step s + 1 into the other set] [second half of the MFMA groups].
+// Stage (s - 1) % NS is free in iteration s: its reads were issued in
+// iteration s - 2 and completed (lgkmcnt(0)) before the barrier of iteration
+// s - 1, which every wave has passed.  The waits, barrier and reads run in
+// the last iteration too (on a stage holding a repeated step), so the MFMA
+// sequence has no branch.
+// ---------------------------------------------------------------------------
+
+template <int BM, int BN>
+struct PfFrag {
+    v8i bx[PfShape<BM, BN>::FM];
+    uint4 af[PfShape<BM, BN>::FN];
+    uint32_t sc[PfShape<BM, BN>::FN];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void pf_read(const uint8_t* st, const uint8_t* sbuf, int wn, int wm, int lane,
+                                        PfFrag<BM, BN>& F) {
+    using S = PfShape<BM, BN>;
+    const int g = lane >> 4;
+    const uint8_t* as = st + S::WBYTES;
+#pragma unroll
+    for (int h = 0; h < S::FM; ++h) {
+        const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
+        const int sw = (r >> 1) & 7;
+        const uint8_t* rowp = as + 128 * r;
+        F.bx[h] = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
+                           *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
+    }
+    const uint8_t* wp = st + 1024 * (wn * S::FN) + 16 * lane;
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(sbuf) + 64 * (wn * S::FN) + lane;
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f) {
+        F.af[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
+        F.sc[f] = sp[64 * f];
+    }
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+    // s_waitcnt lgkmcnt(0), vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int BM, int BN, int F0, int F1>
+__device__ __forceinline__ void pfp_groups(const PfFrag<BM, BN>& F, int sh, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+                                           const PfSrc<BM, BN>& src, uint8_t* tgt, int s_cp, int wave) {
+    using S = PfShape<BM, BN>;
+    if constexpr (F0 < F1) {
+        constexpr int H = S::FN > 1 ? S::FN / 2 : 1, D = S::DMA_PER_STAGE;
+        if constexpr (F0 < H) pf_issue_range<BM, BN, F0 * D / H, (F0 + 1) * D / H>(src, tgt, s_cp, wave);
+        const v8i af = frag_fp4(F.af[F0]);
+        const int scf = (int)(F.sc[F0] >> sh);
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[F0][h] = mfma16<0>(af, F.bx[h], acc[F0][h], scf);
+        __builtin_amdgcn_sched_barrier(0);
+        pfp_groups<BM, BN, F0 + 1, F1>(F, sh, acc, src, tgt, s_cp, wave);
+    }
+}
+
+template <int BM, int BN, int NS>
+__device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN>& Fc, PfFrag<BM, BN>& Fn,
+                                         v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+                                         const PfSrc<BM, BN>& src, uint8_t* base, uint8_t* sbase, int& cur,
+                                         int wn, int wm, int lane, int wave) {
+    using S = PfShape<BM, BN>;
+    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
+    constexpr int H = S::FN > 1 ? S::FN / 2 : 1;
+    constexpr int LAST = (NS - 1) * S::STAGE;
+    // opaque to the optimiser (addresses from a few bases plus immediates)
+    asm volatile("" : "+s"(cur));
+    const int nx = cur == LAST ? 0 : cur + S::STAGE;       // stage of step s + 1
+    const int tg = cur == 0 ? LAST : cur - S::STAGE;       // stage (s - 1) % NS: copies for step u
+    const int u = s + NS - 1;
+    if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+    const int sh = 8 * (s & 3);
+    pfp_groups<BM, BN, 0, H>(Fc, sh, acc, src, base + tg, min(u, steps - 1), wave);
+    // pin the first half's products before the barrier (they touch no memory,
+    // so nothing else keeps them there): the matrix pipe works through them
+    // while the wave waits
+#pragma unroll
+    for (int f = 0; f < H; ++f)
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) asm volatile("" : "+v"(acc[f][h]));
+    // copies allowed in flight: those of steps s + 2 .. s + NS - 1, with at
+    // most one e8m0 chunk among them (NS - 2 <= 3 consecutive steps)
+    bool chunk_ahead = false;
+#pragma unroll
+    for (int v = 2; v <= NS - 1; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < steps;
+    if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
+    else wait_vmcnt<(NS - 2) * D>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");     // no LDS access moves across the barrier
+    pf_read<BM, BN>(base + nx, sbase + (((s + 1) >> 2) & 1) * S::SBYTES, wn, wm, lane, Fn);
+    __builtin_amdgcn_sched_barrier(0);
+    pfp_groups<BM, BN, H, S::FN>(Fc, sh, acc, src, base + tg, min(u, steps - 1), wave);
+    cur = nx;
+}
+
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
+    using S = PfShape<BM, BN>;
+    static_assert(NS >= 3 && NS <= 5, "ring depth");
+    static_assert(BM <= 128, "two fragment sets fit in registers for short tiles only");
+    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
+    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * S::SBYTES;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+    int tm, tn;
+    if (!pf_tile(a, tm, tn)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % S::NWN, wm = wave / S::NWN;
+
+    v4f acc[S::FN][S::FM];
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int steps = a.K >> 7;
+    uint8_t* const base = lds + kPfBase;
+    uint8_t* const sbase = base + NS * S::STAGE;
+    PfSrc<BM, BN> src;
+    pf_sources<BM, BN>(a, tm, tn, wave, lane, src);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
+    }
+    // step 0's copies (steps 1 .. NS - 2 may stay in flight), then its fragments
+    bool chunk_ahead = false;
+#pragma unroll
+    for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= (v & 3) == 0 && v < steps;
+    if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
+    else wait_vmcnt<(NS - 2) * D>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    PfFrag<BM, BN> F0, F1;
+    pf_read<BM, BN>(base, sbase, wn, wm, lane, F0);
+    int cur = 0;
+    for (int s = 0; s < steps; s += 2) {
+        pfp_iter<BM, BN, NS>(s, steps, F0, F1, acc, src, base, sbase, cur, wn, wm, lane, wave);
+        if (s + 1 < steps) pfp_iter<BM, BN, NS>(s + 1, steps, F1, F0, acc, src, base, sbase, cur, wn, wm, lane, wave);
+    }
+    // the repeated copies of the last steps may still be landing: drain them
+    // before the workgroup's LDS is released
+    wait_vmcnt<0>();
+    pf_epilogue<BM, BN>(a, tm, tn, wn, wm, lane, acc);
+}
+
+template <int BM, int BN, int NS>
+hipError_t launch_pfp(const PfArgs& a, hipStream_t stream) {
+    const int total = a.tiles_m * a.tiles_n;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL((pfp_kernel<BM, BN, NS>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int NS>
 hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((pf_kernel<BM>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((pf_kernel<BM, BN, NS>), dim3(grid), dim3(kPfThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -714,19 +1081,85 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     a.c_pad = (int)((K / 128 + 3) / 4);
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
-    a.tiles_n = (int)((N + kPfBN - 1) / kPfBN);
-    if ((M + 63) / 64 * (int64_t)a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
     a.group_m = 8;
-    if (M <= 64) {
-        a.tiles_m = (int)((M + 63) / 64);
-        return launch_pf<64>(a, stream);
+    // tile height by M, the ring as deep as LDS allows for it (5 / 4 / 3
+    // stages); tile width 256, or 128 when 256-wide tiles would leave most
+    // CUs idle (decode-sized M on narrow layers)
+    const int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
+    a.tiles_m = (int)((M + bm - 1) / bm);
+    const int64_t wide = (int64_t)a.tiles_m * ((N + 255) / 256);
+    const int bn = wide < 64 ? 128 : 256;
+    a.tiles_n = (int)((N + bn - 1) / bn);
+    if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    if (bm == 64) return bn == 128 ? launch_pfp<64, 128, 5>(a, stream) : launch_pfp<64, 256, 5>(a, stream);
+    if (bm == 128) return bn == 128 ? launch_pfp<128, 128, 4>(a, stream) : launch_pfp<128, 256, 4>(a, stream);
+    return bn == 128 ? launch_pf<256, 128, 3>(a, stream) : launch_pf<256, 256, 3>(a, stream);
+}
+
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
+    // workgroups (three quarters of the CUs idle in the tiled kernel)
+    const bool narrow = (N + 255) / 256 < 64;
+    // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
+    // narrow): on wide layers the split-K decode kernel wins up to M = 12
+    // (M = 12: 23.8 us; at four weight tiles per workgroup, M = 15: 26.5 us,
+    // against about 25 us tiled for any M <= 32); on narrow ones up to M = 32,
+    // then the register-streamed kernel with K split across workgroups
+    // (down_proj M = 64: 27 us vs 52 us tiled)
+    if (M <= (narrow ? kPreparedDecodeMaxM : 12)) return PreparedRoute::Decode;
+    if (M <= 64 && narrow) return PreparedRoute::RegStream;
+    return PreparedRoute::Tiled;
+}
+
+// Register-streamed decode: MT = ceil(M / 16) in {1, 2, 4}, eight waves per
+// workgroup, weights prefetched eight steps ahead; K split across
+// workgroups (fp32 partials + reduction) when the tile groups alone would
+// leave CUs idle.  Returns the split count through *ks_out (workspace:
+// ks * M * N floats after the counter header when ks > 1).
+static void pdr_shape(int64_t M, int64_t N, int64_t K, int* groups, int* ks, int* sp) {
+    const int64_t tiles = (N + 15) / 16, steps = K / 128;
+    const int64_t g = (tiles + 7) / 8;
+    int64_t k = (256 + g - 1) / g;                 // at least one workgroup per CU
+    if (k > steps / 8) k = steps / 8;              // at least 8 steps per split
+    if (k < 1) k = 1;
+    int64_t per = (steps + k - 1) / k;
+    k = (steps + per - 1) / per;                   // no empty split
+    *groups = (int)g;
+    *ks = (int)k;
+    *sp = (int)per;
+}
+
+size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    int g, k, per;
+    pdr_shape(M, N, K, &g, &k, &per);
+    if (k <= 1) return 0;
+    return ws_counter_bytes((N + 15) / 16) + (size_t)k * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream) {
+    PDrArgs a{};
+    a.x8 = x8; a.xs = xs;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.out = out;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.tiles = (int)((N + 15) / 16);
+    pdr_shape(M, N, K, &a.groups, &a.ks, &a.sp);
+    if (a.ks > 1) {
+        if (!ws) return hipErrorInvalidValue;
+        a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles));
     }
-    if (M <= 128) {
-        a.tiles_m = (int)((M + 127) / 128);
-        return launch_pf<128>(a, stream);
-    }
-    a.tiles_m = (int)((M + 255) / 256);
-    return launch_pf<256>(a, stream);
+    hipError_t e;
+    if (M <= 16) e = launch_pdr<1, 8, 8>(a, stream);
+    else if (M <= 32) e = launch_pdr<2, 8, 8>(a, stream);
+    else e = launch_pdr<4, 8, 8>(a, stream);
+    if (e != hipSuccess || a.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,

@@ -99,6 +99,16 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M);
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
                                   int64_t N, int64_t K, void* ws, hipStream_t stream);
+// Which kernel serves a GEMM on prepared weights: the split-K decode kernel
+// (M <= 12; M <= 32 on narrow layers), the register-streamed kernel (up to
+// M = 64 on layers too narrow for the tiled kernel to fill the CUs: K split
+// across workgroups), or the tiled kernel.
+enum class PreparedRoute { Decode, RegStream, Tiled };
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K);
+size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
                                  hipStream_t stream);
