@@ -474,21 +474,21 @@ hipError_t launch_pdr(const PDrArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// tiled band on prepared weights (M > 32): 256 weight rows x BM activation rows
-// per workgroup, K in 128-wide steps through a 3-stage LDS ring.
+// tiled band on prepared weights: BN (256 or 128) weight rows x BM (64, 128
+// or 256) activation rows per workgroup, K in 128-wide steps through an
+// NS-stage LDS ring (5 / 4 / 3 stages for BM = 64 / 128 / 256).
 //
 // Eight waves in an NWN x NWM grid; wave tile = 16*FN weight rows x 16*FM
 // activation rows of 16x16x128 MFMAs.  Every stage is filled with direct
-// global -> LDS copies (global_load_lds, 1 KiB or 256 B per wave instruction, no
-// registers): the 16 weight fragment blocks of the panel (lane order = MFMA
-// order, read back with one conflict-free ds_read_b128 per fragment), the BM x
-// 128 activation slice, whose 16-byte chunk c of row r sits at chunk position
-// c ^ ((r >> 1) & 7) (so the 16 rows of a fragment read land in 16 distinct
-// bank groups), and the panel's e8m0 dwords for the step's 4-step chunk.  One
-// barrier per step: the wait + barrier at the top of step s makes stage s
-// visible and frees stage s-1, whose slot then receives step s+2.  LDS offsets
-// start at 256: a direct-to-LDS destination of address 0 would be taken for a
-// null pointer by the address-space cast.
+// global -> LDS copies (buffer loads with the LDS bit, 1 KiB per wave
+// instruction, no registers): the BN/16 weight fragment blocks of the panel
+// (lane order = MFMA order, read back with one conflict-free ds_read_b128 per
+// fragment) and the BM x 128 activation slice, whose 16-byte chunk c of row r
+// sits at chunk position c ^ ((r >> 1) & 7) (so the 16 rows of a fragment
+// read land in 16 distinct bank groups).  The e8m0 dwords of a 4-step chunk
+// (256 B per weight tile) go to one of two buffers of their own.  LDS offsets
+// start at 256: a direct-to-LDS destination of address 0 would be taken for
+// a null pointer by the address-space cast.
 // ---------------------------------------------------------------------------
 
 struct PfArgs {
