@@ -84,6 +84,13 @@ def test_act_quant_ragged_and_strided():
     _act_case(x[:1, :1], name="1x1")
 
 
+def test_act_quant_register_and_two_pass_boundaries():
+    # rows held in registers take 1/2/4/8/16 uint4 per thread (K <= 32768);
+    # K = 32776 falls back to the two-pass form
+    for K in (8, 2048, 2056, 4104, 8200, 12288, 32768, 32776):
+        _act_case(synth.acts(3, K, seed=(5, K), spread=50.0), name=f"K={K}")
+
+
 def test_act_quant_decode_and_prefill_shapes():
     for M, K, seed in ((1, 5120, (1, 1)), (64, 5120, (1, 64)), (16, 17408, (2, 16))):
         _act_case(synth.acts(M, K, seed=seed, spread=10.0), name=f"M={M} K={K}")

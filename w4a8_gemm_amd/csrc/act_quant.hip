@@ -5,10 +5,12 @@
 // arithmetic to a library op; the plain reading used here:
 //   s = amax_k |x[m,k]| / 448   (1 for an all-zero row)
 //   code = e4m3 round-to-nearest-even of x / s, saturating at 448, sign kept.
-// One workgroup per row: a grid-stride max over the row (wavefront butterfly,
-// then LDS across the four waves), then the divide-and-encode pass, which
-// re-reads the row from L2.  Rows are read 16 bytes per lane when the layout
-// allows it.
+// One workgroup per row.  Rows of up to 256 * 8 * 16 elements (and 16-byte
+// aligned) are read once into registers -- every load issued before the first
+// use, so the row costs one memory latency -- then the block max (wavefront
+// butterfly, then LDS across the four waves) and the divide-and-encode from
+// registers.  Longer or unaligned rows take a two-pass form that re-reads the
+// row from L2.
 #include "w4a8_internal.h"
 
 #pragma clang fp contract(off)
@@ -79,13 +81,65 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
     }
 }
 
+// single pass: the row in registers, R uint4 (8 bf16 each) per thread
+template <int R>
+__global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                                 int64_t ldx, uint8_t* __restrict__ x8,
+                                                                 float* __restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const uint4* r4 = reinterpret_cast<const uint4*>(x + m * ldx);
+    uint2* o2 = reinterpret_cast<uint2*>(x8 + m * K);
+    const int n8 = (int)(K / 8);
+    uint4 v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int c = threadIdx.x + kThreads * i;
+        v[i] = c < n8 ? r4[c] : make_uint4(0, 0, 0, 0);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
+            amax = fmaxf(amax, fabsf(bf16_to_f32(d[q] >> 16)));
+        }
+    }
+    amax = block_max(amax);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division
+    if (threadIdx.x == 0) xs[m] = s;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int c = threadIdx.x + kThreads * i;
+        if (c >= n8) continue;
+        const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] & 0xFFFFu) / s);
+            const uint32_t hi = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] >> 16) / s);
+            o[q >> 1] |= (lo | (hi << 8)) << (16 * (q & 1));
+        }
+        o2[c] = make_uint2(o[0], o[1]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8,
                             float* xs, hipStream_t stream) {
     const bool vec = (K % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) &&
                      ((uintptr_t)x8 % 8 == 0);
-    if (vec)
+    const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;   // uint4 per thread
+    if (vec && per_thread <= 16) {
+        const dim3 g((unsigned)M), b(kThreads);
+        if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs);
+        else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs);
+        else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs);
+        else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs);
+        else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs);
+    } else if (vec)
         hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(kThreads), 0, stream, x,
                            K, ldx, x8, xs);
     else
