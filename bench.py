@@ -42,6 +42,32 @@ DECODE_MS = (1, 8, 16, 64)
 COPIES = 4
 
 
+TRAFFIC_RECORD = os.path.join(HERE, "profiles", "pdec_gate_up_m1_traffic.md")
+ROOFLINE_SOURCE = os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip")
+ROOFLINE_GRID = 278528          # pdec_kernel launch at gate_up M = 1: 2176 workgroups x 128 threads
+CALIB_BYTES = 1 << 30           # plain device-to-device copy used to scale the HBM counters
+
+
+def _source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic_record():
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    record, or None when the kernel's source has changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = dict(line.split(": ", 1) for line in f.read().splitlines()
+                       if line.startswith(("traffic_bytes: ", "kernel_source_sha256: ")))
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256", "").strip() != _source_hash(ROOFLINE_SOURCE):
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def decode_bytes(M, N, K):
     """Algorithmic bytes of act quant + GEMM at one M."""
     w = N * K // 2 + N * K // 32
@@ -100,7 +126,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill/requant/int4 loops")
     ap.add_argument("--cpu-rows", type=int, default=34816, help="weight rows in the oracle sample")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only the launches the HBM counters are read on: a 1 GiB device copy "
+                         "(calibration) and the roofline kernel (run under rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
+                         "into the traffic record under profiles/")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
@@ -135,6 +170,10 @@ def main():
 
     def gemm(M, c):
         w4.mxfp4_gemm_prepared(x8[M], xsc[M], pcopies[c], out=out[M], workspace=pws)
+
+    if args.pmc_probe:
+        pmc_probe(torch, w4, timer, graph_of, gemm, x8, xsc, xs_bf16, dev, log)
+        return
 
     def step(c):
         for M in DECODE_MS:
@@ -172,7 +211,7 @@ def main():
                 "kernel": "pdec_kernel<1,3> (fragment-order split-K decode), gate_up M=1; "
                           "average over graph-replayed launches rotating 4 weight copies",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic_record(),
                 "bytes_per_launch": b1, "avg_launch_us": round(per_m[1] * 1e6, 3),
                 "gemm_call_us_by_M": {str(M): round(per_m[M] * 1e6, 3) for M in DECODE_MS},
                 "gemm_call_gbps_by_M": {str(M): round(gemm_bytes(M, N, K) / per_m[M] / 1e9, 1)
@@ -204,6 +243,85 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def pmc_probe(torch, w4, timer, graph_of, gemm, x8, xsc, xs_bf16, dev, log):
+    """Launches for the HBM byte counters: a plain device-to-device copy of
+    CALIB_BYTES (read and written once: the counters' scale), then 16
+    launches of the roofline kernel (gate_up, M = 1, rotating the four weight
+    copies), each stream-ordered and separate."""
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w4.quant_act_fp8_per_token(xs_bf16[1], out=x8[1], scale=xsc[1])
+    for r in range(16):
+        gemm(1, r % COPIES)
+    torch.cuda.synchronize()
+    log("pmc probe done")
+
+
+def pmc_summarize(fetch_dir, write_dir):
+    """Traffic record of the roofline kernel from two rocprofv3 --pmc runs of
+    `bench.py --pmc-probe`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of
+    the roofline kernel's launches, each scaled by the factor the same counter
+    reads on the calibration copy (CALIB_BYTES read and written)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = list(csv.DictReader(open(files[0])))
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = r["Dispatch_Id"]
+            name, grid = r["Kernel_Name"], int(r["Grid_Size"])
+            v = acc.setdefault(key, [name, grid, 0.0])
+            v[2] += float(r["Counter_Value"])
+        return list(acc.values())
+
+    def pick(recs):
+        copies = [v for n, g, v in recs if "copy" in n.lower() and v > 0]
+        kern = [v for n, g, v in recs if "pdec_kernel" in n and g == ROOFLINE_GRID]
+        if not copies or not kern:
+            raise SystemExit("calibration copy or roofline kernel dispatches not found")
+        return max(copies), kern
+
+    fc, fk = pick(per_dispatch(fetch_dir, "FETCH_SIZE"))
+    wc, wk = pick(per_dispatch(write_dir, "WRITE_SIZE"))
+    f_scale = fc * 1024 / CALIB_BYTES          # counter bytes per true byte read
+    w_scale = wc * 1024 / CALIB_BYTES          # counter bytes per true byte written
+    fetch = sum(fk) / len(fk) * 1024 / f_scale
+    write = sum(wk) / len(wk) * 1024 / w_scale
+    algo = gemm_bytes(1, 34816, 5120)
+    lines = [
+        "# HBM traffic of pdec_kernel, gate_up M = 1 (roofline kernel of bench.py)",
+        "",
+        "Commands (repository root, one MI355X):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python -u bench.py --pmc-probe",
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python -u bench.py --pmc-probe",
+        "    python bench.py --pmc-summarize gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "",
+        f"Calibration: a {CALIB_BYTES} B device-to-device copy reads FETCH_SIZE {fc:.0f} KiB "
+        f"(scale {f_scale:.4f}) and WRITE_SIZE {wc:.0f} KiB (scale {w_scale:.4f}).",
+        f"Roofline kernel: {len(fk)} / {len(wk)} dispatches, mean FETCH_SIZE {sum(fk) / len(fk):.0f} KiB, "
+        f"mean WRITE_SIZE {sum(wk) / len(wk):.0f} KiB.",
+        f"Scaled HBM bytes per launch: read {fetch:.0f}, written {write:.0f}; "
+        f"algorithmic bytes {algo} (ratio {(fetch + write) / algo:.4f}).",
+        "",
+        f"traffic_bytes: {int(round(fetch + write))}",
+        f"kernel_source_sha256: {_source_hash(ROOFLINE_SOURCE)}",
+    ]
+    with open(TRAFFIC_RECORD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _timed_graph(torch, timer, graph_of, calls, reps):
