@@ -193,7 +193,7 @@ def main():
 
     # ---------------- decode GEMM kernel durations (roofline) ----------------
     per_m = {}
-    R = 4 * COPIES
+    R = 16 * COPIES        # launches per graph: the gap between graph replays (~8 us) spreads thin
     for M in DECODE_MS:
         def gemms(M=M):
             for r in range(R):
@@ -209,7 +209,7 @@ def main():
     achieved = b1 / per_m[1] / 1e9
     roofline = {"bound": "hbm",
                 "kernel": "pdec_kernel<1,3> (fragment-order split-K decode), gate_up M=1; "
-                          "average over graph-replayed launches rotating 4 weight copies",
+                          "average over graph replays of 64 launches rotating 4 weight copies",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic_record(),
                 "bytes_per_launch": b1, "avg_launch_us": round(per_m[1] * 1e6, 3),

@@ -370,3 +370,21 @@ def test_mxfp4_prepared_regstream_down_proj():
     ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096)])
     ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
     assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
+
+
+def test_mxfp4_prepared_tiled_tall():
+    # 256-row tiles (at least two 256 x 256 tiles per CU): ragged M and N,
+    # sampled outputs including the last row and column
+    M, N, K = 600, 45060, 256
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 5))
+    x8, s = _acts(M, K, (M, K, 5), spread=10.0)
+    say("prepared tiled tall", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(9)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 8192), np.full(64, M - 1)])
+    ni = np.concatenate([g.integers(0, N, M), g.integers(0, N, 8192), N - 1 - np.arange(64)])
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni)
+    assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
+    slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
+    assert (np.abs(got[mi, ni] - ref) <= slack).all()

@@ -1084,16 +1084,22 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     a.group_m = 8;
     // tile height by M, the ring as deep as LDS allows for it (5 / 4 / 3
     // stages); tile width 256, or 128 when 256-wide tiles would leave most
-    // CUs idle (decode-sized M on narrow layers)
-    const int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
+    // CUs idle (decode-sized M on narrow layers).  Large M keeps 128-row
+    // (pipelined) tiles while 256-row tiles would give fewer than two per CU
+    // (measured, down_proj M = 4096: 359 us vs 391 us with 256-row tiles;
+    // gate_up M = 4096, 8.5 tiles per CU: 663 us vs 716 us the other way)
+    int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
+    if (bm == 256 && ((M + 255) / 256) * ((N + 255) / 256) < 512) bm = 128;
     a.tiles_m = (int)((M + bm - 1) / bm);
     const int64_t wide = (int64_t)a.tiles_m * ((N + 255) / 256);
     const int bn = wide < 64 ? 128 : 256;
     a.tiles_n = (int)((N + bn - 1) / bn);
     if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
-    if (bm == 64) return bn == 128 ? launch_pfp<64, 128, 5>(a, stream) : launch_pfp<64, 256, 5>(a, stream);
+    // (64-row tiles are wide: narrow layers take the register-streamed kernel
+    // at M <= 64; 256-row tiles come only with at least 512 256-wide tiles)
+    if (bm == 64) return launch_pfp<64, 256, 5>(a, stream);
     if (bm == 128) return bn == 128 ? launch_pfp<128, 128, 4>(a, stream) : launch_pfp<128, 256, 4>(a, stream);
-    return bn == 128 ? launch_pf<256, 128, 3>(a, stream) : launch_pf<256, 256, 3>(a, stream);
+    return launch_pf<256, 256, 3>(a, stream);
 }
 
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K) {
