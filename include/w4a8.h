@@ -70,7 +70,8 @@ typedef enum { W4A8_EXP_OCP = 0, W4A8_EXP_NOCLIP = 1, W4A8_EXP_MSE = 2 } w4a8_ex
 typedef enum {
     W4A8_WEIGHT_MXFP4 = 0,           /* [N, K/2] codes + [N, K/32] e8m0 */
     W4A8_WEIGHT_INT4G128 = 1,        /* [N, K/8] int32 (w4a8_int4g128_prepare) + fp16 scales */
-    W4A8_WEIGHT_MXFP4_PREPARED = 2   /* fragment order (w4a8_mxfp4_prepare) */
+    W4A8_WEIGHT_MXFP4_PREPARED = 2,  /* fragment order (w4a8_mxfp4_prepare) */
+    W4A8_WEIGHT_INT4G128_PREPARED = 3 /* fragment order (w4a8_int4g128_prepare_fragments) */
 } w4a8_weight_kind;
 
 /* ---------------------------------------------------------------------------
@@ -238,6 +239,37 @@ w4a8_status w4a8_int4g128_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const int32_t *d_qweight_nk, const uint16_t *d_scales_f16, uint16_t *d_out,
     int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
+
+/* int4 g128 weights in matrix-core fragment order (load time) and the GEMM on
+ * them.  Source: "radiance_autoround.py", as w4a8_int4g128_gemm above, with the
+ * load-time repack of "vllm-radiance (MXFP4)", How the MXFP4 path works.  The
+ * layout follows the MXFP4 fragment order: one 1 KiB block per 16-row tile t
+ * and 128-wide K step s, tiles major; lane L = n + 16g holds 16 bytes of codes
+ * of row 16t+n: words 16s+2g, 16s+2g+1 (k = 128s+16g .. +15) and 16s+8+2g,
+ * 16s+9+2g (k = 128s+64+16g .. +15) of the checkpoint layout -- the k order of
+ * the fp8 matrix operand, so the codes widen to c - 8 in e4m3 in registers.
+ * Row scales: fp16 [tile][4-step chunk][step][16 rows].  Rows are padded to 16
+ * and steps to a multiple of 4 (code 8, scale 0).  The result equals
+ * w4a8_int4g128_gemm's in value (fp32 accumulation; summation order may
+ * differ).
+ *   w4a8_int4g128_prepared_bytes: sizes of the two buffers (host).
+ *   w4a8_int4g128_prepare_fragments: checkpoint qweight [K/8, N], qzeros
+ *     [K/128, N/8] (all 0x77777777, else ASYMMETRIC), scales [K/128, N] fp16
+ *     -> d_w_prepared (16-byte aligned), d_s_prepared (8-byte aligned).
+ *     Synchronizes `stream` (the check result is read back).
+ *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
+ *     kernel choice and workspace of w4a8_mxfp4_gemm_prepared (size it with
+ *     W4A8_WEIGHT_INT4G128_PREPARED).
+ * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
+ * UNSUPPORTED_SHAPE, WORKSPACE, ASYMMETRIC (prepare), HIP. */
+w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
+w4a8_status w4a8_int4g128_prepare_fragments(const int32_t *d_qweight_kn, const int32_t *d_qzeros,
+                                            const uint16_t *d_scales_f16, int64_t N, int64_t K,
+                                            uint8_t *d_w_prepared, uint8_t *d_s_prepared, void *stream);
+w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x_scale,
+                                        const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
+                                        uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
+                                        size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Decode band with an explicit plan, for tile-size sweeps (the two GEMM entry

@@ -101,6 +101,17 @@ def test_gemm_validation(L):
     assert p(None, _p(), 64, 256, _p(), None) == INVALID
     assert p(_p(), _p(), 60, 256, _p(), None) == SHAPE
     assert p(_p(), _p(), 64, 200, _p(), None) == SHAPE
+    pf = L.w4a8_int4g128_prepare_fragments
+    assert pf(_p(), _p(), None, 64, 256, _p(), _p(), None) == INVALID
+    assert pf(_p(), _p(), _p(), 60, 256, _p(), _p(), None) == SHAPE
+    assert pf(_p(), _p(), _p(), 64, 200, _p(), _p(), None) == SHAPE
+    assert pf(_p(), _p(), _p(), 64, 256, _p(FAKE + 8), _p(), None) == INVALID   # 16-byte aligned
+    assert pf(_p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 4), None) == INVALID   # 8-byte aligned
+    ip = L.w4a8_int4g128_gemm_prepared
+    assert ip(_p(), _p(), _p(), _p(), _p(), 4, 60, 256, None, 0, None) == SHAPE  # N % 8
+    assert ip(_p(), _p(), _p(), _p(), _p(), 4, 64, 192, None, 0, None) == SHAPE  # K % 128
+    assert ip(_p(), _p(), _p(), _p(FAKE + 4), _p(), 4, 64, 256, None, 0, None) == INVALID
+    assert ip(_p(), _p(), _p(), None, _p(), 4, 64, 256, None, 0, None) == INVALID
 
 
 def test_workspace_bytes_contract(L):
@@ -144,6 +155,16 @@ def test_binding_rejects_mismatched_weight_sizes(L):
     with pytest.raises(ValueError):
         binding._check_weight_sizes("prepared", w, s, wb.value, K)
     binding._check_weight_sizes("mxfp4", Shape(N, K // 2), Shape(N, K // 32), N, K)
+    # int4 fragment order: 1 KiB per (16-row tile, 128-wide step), 128 B of fp16
+    # scales per (tile, 4-step chunk); rows padded to 16, steps to 4
+    N4, K4 = 5128, 17408 + 128
+    assert binding.lib().w4a8_int4g128_prepared_bytes(N4, K4, ctypes.byref(wb), ctypes.byref(sb)) == OK
+    tiles, chunks = (N4 + 15) // 16, (K4 // 128 + 3) // 4
+    assert (wb.value, sb.value) == (tiles * chunks * 4096, tiles * chunks * 128)
+    binding._check_weight_sizes("int4_prepared", Shape(wb.value), Shape(sb.value), N4, K4)
+    with pytest.raises(ValueError):
+        binding._check_weight_sizes("int4_prepared", Shape(wb.value), Shape(2 * sb.value), N4, K4)
+    assert binding.lib().w4a8_int4g128_prepared_bytes(60, 256, ctypes.byref(wb), ctypes.byref(sb)) == SHAPE
     with pytest.raises(ValueError):
         binding._check_weight_sizes("mxfp4", Shape(N, K // 2), Shape(N, K // 16), N, K)
     with pytest.raises(ValueError):

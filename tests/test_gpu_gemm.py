@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import w4a8_gemm_amd as w4
-from gpu_util import GEMM_REL_F, dev_f16, dev_f32, dev_i32, dev_u8, host_bf16_as_f64, rel_frobenius, say
+from gpu_util import GEMM_REL_F, assert_gemm_close, dev_f16, dev_f32, dev_i32, dev_u8, host_bf16_as_f64, rel_frobenius, say
 from w4a8_gemm_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -388,3 +388,94 @@ def test_mxfp4_prepared_tiled_tall():
     assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
     slack = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.sqrt(np.mean(ref * ref))
     assert (np.abs(got[mi, ni] - ref) <= slack).all()
+
+
+# ---------------------------------------------------------------------------
+# int4 g128 weights in fragment order: the same four kernels as the prepared
+# MXFP4 weights, the codes widened to e4m3 (c - 8) in registers
+# ---------------------------------------------------------------------------
+
+def _unprepare_int4(wt, st, N, K):
+    """Invert the documented int4 fragment order on the host: -> qweight [N_pad,
+    K_pad/8] words (transposed checkpoint layout) and fp16 scales [N_pad, K_pad/128]."""
+    tiles, steps = (N + 15) // 16, K // 128
+    s4 = 4 * ((steps + 3) // 4)
+    w = wt.view(np.uint32).reshape(tiles, s4, 4, 16, 2, 2)        # t, s, g, n, half, pair
+    w = w.transpose(0, 3, 1, 4, 2, 5).reshape(tiles * 16, s4 * 16)  # word 16s + 8h + 2g + p
+    sc = st.view(np.uint16).reshape(tiles, s4 // 4, 4, 16)        # t, chunk, step, n
+    sc = sc.transpose(0, 3, 1, 2).reshape(tiles * 16, s4)
+    return w, sc
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (104, 640), (5120, 17408)])
+def test_int4_prepare_fragments_layout(N, K):
+    q = synth.int4_random(N, K, seed=(N, K, 7))
+    say("int4 prepare fragments", (N, K))
+    pw = w4.int4g128_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]),
+                                       dev_f16(q["scales"]))
+    torch.cuda.synchronize()
+    w, sc = _unprepare_int4(pw.w.cpu().numpy(), pw.s.cpu().numpy(), N, K)
+    assert np.array_equal(w[:N, :K // 8], q["qweight_kn"].view(np.uint32).T)
+    assert np.array_equal(sc[:N, :K // 128], q["scales"].T)
+    # padding: code 8 (value 0) and scale 0
+    assert (w[N:] == 0x88888888).all() and (w[:, K // 8:] == 0x88888888).all()
+    assert (sc[N:] == 0).all() and (sc[:, K // 128:] == 0).all()
+
+
+def _int4_prepared_case(name, q, M, seed, full=False, n_samples=4096, spread=1.0):
+    N, K = q["N"], q["K"]
+    ref_nk, bad = oracle.int4_prepare(q["qweight_kn"], q["qzeros"], N, K)
+    assert bad == 0
+    say("int4 prepared", name, (M, N, K))
+    pw = w4.int4g128_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]),
+                                       dev_f16(q["scales"]))
+    x8, s = _acts(M, K, seed, spread=spread)
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.int4g128_gemm_prepared(dx, ds, pw))
+    again = host_bf16_as_f64(w4.int4g128_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(got, again), name
+    if full:
+        ref = oracle.int4_gemm(x8, s, ref_nk, q["scales"])
+        sel = got
+    else:
+        g = np.random.default_rng(seed if isinstance(seed, int) else sum(seed))
+        mi = np.concatenate([np.arange(M), g.integers(0, M, n_samples), np.full(64, M - 1)])
+        ni = np.concatenate([g.integers(0, N, M), g.integers(0, N, n_samples), N - 1 - np.arange(64)])
+        ref = oracle.int4_gemm(x8, s, ref_nk, q["scales"], mi=mi, ni=ni)
+        sel = got[mi, ni]
+    assert_gemm_close(sel, ref, name)
+
+
+# every route: split-K decode (M <= 32 narrow, M <= 12 wide), register-streamed
+# (33..64 narrow), tiled 64/128/256-row tiles with 128- and 256-wide columns
+INT4_PREPARED = [(1, 64, 128), (3, 136, 1152), (17, 520, 1024), (32, 1000, 4096),
+                 (33, 16, 1152), (48, 1000, 4096), (64, 200, 1024),
+                 (65, 264, 384), (100, 1000, 1152), (129, 512, 640), (256, 1032, 2048),
+                 (513, 600, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", INT4_PREPARED)
+def test_int4_prepared_ragged(M, N, K):
+    _int4_prepared_case(f"{M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 8)), M, (M, K, 8),
+                        full=True, spread=10.0)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (40, 65600, 256), (300, 33000, 384),
+                                   (600, 45064, 256)])
+def test_int4_prepared_wide(M, N, K):
+    _int4_prepared_case(f"wide {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 9)), M,
+                        (M, K, 9), n_samples=8192)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 2048])
+def test_int4_prepared_full_size(M):
+    _int4_prepared_case(f"I M={M}", synth.int4(), M, (10, M))
+
+
+def test_int4_prepare_fragments_rejects_asymmetric_zeros():
+    q = synth.int4_random(64, 256, seed=2)
+    qz = q["qzeros"].copy()
+    qz.view(np.uint32)[0, 5] = 0x77777770
+    say("int4 prepare fragments asymmetric")
+    with pytest.raises(ValueError):
+        w4.int4g128_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(qz), dev_f16(q["scales"]))

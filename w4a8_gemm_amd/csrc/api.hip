@@ -95,13 +95,15 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     if (kind == W4A8_WEIGHT_MXFP4 && K % 32 != 0) return 0;
     if (kind == W4A8_WEIGHT_INT4G128 && (K % 128 != 0 || N % 8 != 0)) return 0;
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED && K % 128 != 0) return 0;
-    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED)
+    if (kind == W4A8_WEIGHT_INT4G128_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
+    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED &&
+        kind != W4A8_WEIGHT_INT4G128_PREPARED)
         return 0;
     size_t need = 0;
     const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
     for (int64_t m = 1; m <= top; ++m) {
         size_t b = 0;
-        if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
+        if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED) {
             const PreparedRoute r = prepared_route(m, N, K);
             if (r == PreparedRoute::Decode) b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 3), m, N);
             else if (r == PreparedRoute::RegStream) b = pdr_workspace_bytes(m, N, K);
@@ -156,34 +158,82 @@ w4a8_status w4a8_mxfp4_prepare(const uint8_t* d_w_packed, const uint8_t* d_w_e8m
                                      as_stream(stream)));
 }
 
-w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
-                                     const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
-                                     uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
-                                     size_t ws_bytes, void* stream) {
-    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w_prepared, d_out, M, N, K);
+// GEMM on fragment-order weights (MXFP4 or int4): kernel by prepared_route
+static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale, const uint8_t* d_w,
+                                 const uint8_t* d_s, uint16_t* d_out, int64_t M, int64_t N, int64_t K,
+                                 void* d_ws, size_t ws_bytes, void* stream, bool int4) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
-    if (!d_s_prepared || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
-    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     // the tiled and register-streamed kernels address activations with 32-bit offsets
     const PreparedRoute route = prepared_route(M, N, K);
     if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
     case PreparedRoute::Tiled:
-        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
-                                                M, N, K, as_stream(stream)));
+        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
+                                                as_stream(stream), int4));
     case PreparedRoute::RegStream:
         st = check_workspace(pdr_workspace_bytes(M, N, K), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
-        return hip_status(launch_prepared_regstream(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out,
-                                                    M, N, K, d_ws, as_stream(stream)));
+        return hip_status(launch_prepared_regstream(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
+                                                    as_stream(stream), int4));
     default: {
         const GemmPlan p = plan_prepared(M, N, K, 0, 3);
         st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
-        return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared,
-                                                 d_out, M, N, K, d_ws, as_stream(stream)));
+        return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
+                                                 as_stream(stream), int4));
     }
     }
+}
+
+w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                     const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
+                                     uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
+                                     size_t ws_bytes, void* stream) {
+    return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws, ws_bytes,
+                         stream, false);
+}
+
+w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t* h_w_bytes, size_t* h_s_bytes) {
+    if (!h_w_bytes || !h_s_bytes) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    prepared_i4_sizes(N, K, h_w_bytes, h_s_bytes);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_int4g128_prepare_fragments(const int32_t* d_qweight_kn, const int32_t* d_qzeros,
+                                            const uint16_t* d_scales_f16, int64_t N, int64_t K,
+                                            uint8_t* d_w_prepared, uint8_t* d_s_prepared, void* stream) {
+    if (!d_qweight_kn || !d_qzeros || !d_scales_f16 || !d_w_prepared || !d_s_prepared)
+        return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_qweight_kn, 4) || !aligned(d_qzeros, 4) || !aligned(d_scales_f16, 2) ||
+        !aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 8))
+        return W4A8_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    // the first prepared word serves as the mismatch counter before the repack
+    uint32_t* counter = reinterpret_cast<uint32_t*>(d_w_prepared);
+    if (launch_fill_zero_u32(counter, 1, s) != hipSuccess) return W4A8_ERR_HIP;
+    if (launch_int4_check_transpose(nullptr, d_qzeros, N, K, nullptr, counter, s) != hipSuccess)
+        return W4A8_ERR_HIP;
+    uint32_t bad = 0;
+    if (hipMemcpyAsync(&bad, counter, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return W4A8_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return W4A8_ERR_HIP;
+    if (bad) return W4A8_ERR_ASYMMETRIC;
+    return hip_status(launch_prepare_i4(d_qweight_kn, d_scales_f16, N, K, d_w_prepared, d_s_prepared, s));
+}
+
+w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                        const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
+                                        uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
+                                        size_t ws_bytes, void* stream) {
+    return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws, ws_bytes,
+                         stream, true);
 }
 
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,
@@ -249,7 +299,7 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,
                                                  (const uint8_t*)d_w_scale, d_out, M, N, K, d_ws,
-                                                 as_stream(stream)));
+                                                 as_stream(stream), false));
     }
     if (M > kDecodeMaxM || (rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1)
         return W4A8_ERR_INVALID_ARG;

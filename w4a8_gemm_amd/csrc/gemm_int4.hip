@@ -25,30 +25,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kFmtFp8 = 0;
 constexpr int kUnitScale = 127;
 
-__device__ __forceinline__ float f16_to_f32(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// Eight int4 codes (one word, nibble j = k j) -> eight e4m3 bytes of (c - 8) in
-// k order.  Codes 0..7 map to -8..-1 and 8..15 to 0..7; each half is an 8-byte
-// table indexed by c & 7, and bit 3 picks the half.
-__device__ __forceinline__ uint2 int4x8_to_e4m3(uint32_t w) {
-    const uint32_t kNegLo = 0xCACCCED0u, kNegHi = 0xB8C0C4C8u;  // -8 -7 -6 -5 | -4 -3 -2 -1
-    const uint32_t kPosLo = 0x44403800u, kPosHi = 0x4E4C4A48u;  //  0  1  2  3 |  4  5  6  7
-    const uint32_t ev = w & 0x0F0F0F0Fu;          // k = 0, 2, 4, 6
-    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // k = 1, 3, 5, 7
-    const uint32_t se = ev & 0x07070707u, so = od & 0x07070707u;
-    const uint32_t ne = __builtin_amdgcn_perm(kNegHi, kNegLo, se);
-    const uint32_t pe = __builtin_amdgcn_perm(kPosHi, kPosLo, se);
-    const uint32_t no = __builtin_amdgcn_perm(kNegHi, kNegLo, so);
-    const uint32_t po = __builtin_amdgcn_perm(kPosHi, kPosLo, so);
-    const uint32_t me = ((ev >> 1) & 0x04040404u) | 0x03020100u;  // byte i -> i, or i+4 if c >= 8
-    const uint32_t mo = ((od >> 1) & 0x04040404u) | 0x03020100u;
-    const uint32_t e = __builtin_amdgcn_perm(pe, ne, me);
-    const uint32_t o = __builtin_amdgcn_perm(po, no, mo);
-    return make_uint2(__builtin_amdgcn_perm(o, e, 0x05010400u), __builtin_amdgcn_perm(o, e, 0x07030602u));
-}
-
 // 32 codes (4 words, k = 32 consecutive) -> fp8 fragment of the same k order
 __device__ __forceinline__ v8i int4x32_frag(uint4 q) {
     const uint2 a = int4x8_to_e4m3(q.x), b = int4x8_to_e4m3(q.y);

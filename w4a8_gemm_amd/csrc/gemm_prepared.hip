@@ -44,6 +44,50 @@ __device__ __forceinline__ v4f mfma16(v8i a_fp4, v8i b_fp8, v4f c, int scale_a) 
                                                             scale_a, 0, kUnitScale);
 }
 
+// Weight formats of the fragment-order layout (same 1 KiB block per 16-row
+// tile and 128-wide K step, same lane order; the activation operand is the
+// same for both):
+//   kWMx  MXFP4: e2m1 codes (lane bytes = k 32g .. 32g+31), e8m0 scales as a
+//         dword per lane and 4-step chunk, applied by the MFMA's scale operand.
+//   kWI4  symmetric int4 g128: codes c (value c - 8), lane bytes = k 16g ..
+//         16g+15 and 64+16g .. 64+16g+15 (the fp8 operand order), widened to
+//         e4m3 in registers; one fp16 scale per weight row and step, applied
+//         to the step's products in fp32.
+constexpr int kWMx = 0, kWI4 = 1;
+
+template <int WF> struct WStep;                               // per-step scale data of a lane
+template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte = step % 4)
+template <> struct WStep<kWI4> { using T = uint2; };         // fp16 scales of its 4 output rows
+
+// a lane's weight fragment (A operand) from its 16 stored bytes
+template <int WF>
+__device__ __forceinline__ v8i wfrag(uint4 q) {
+    if constexpr (WF == kWMx) {
+        return frag_fp4(q);
+    } else {
+        const uint2 a = int4x8_to_e4m3(q.x), b = int4x8_to_e4m3(q.y);
+        const uint2 c = int4x8_to_e4m3(q.z), d = int4x8_to_e4m3(q.w);
+        v8i r = {(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, (int)d.x, (int)d.y};
+        return r;
+    }
+}
+
+// acc += one K step's products (MXFP4: e8m0 byte OPSEL of the dword)
+template <int WF, int OPSEL>
+__device__ __forceinline__ v4f wmma(v8i a, v8i b, v4f acc, typename WStep<WF>::T sc) {
+    if constexpr (WF == kWMx) {
+        return mfma16<OPSEL>(a, b, acc, (int)sc);
+    } else {
+        const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+                                                                       kFmtFp8, 0, kUnitScale, 0, kUnitScale);
+        acc[0] = acc[0] + f16_to_f32(sc.x & 0xFFFFu) * t[0];
+        acc[1] = acc[1] + f16_to_f32(sc.x >> 16) * t[1];
+        acc[2] = acc[2] + f16_to_f32(sc.y & 0xFFFFu) * t[2];
+        acc[3] = acc[3] + f16_to_f32(sc.y >> 16) * t[3];
+        return acc;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // prepare: plain [N, K/2] codes + [N, K/32] e8m0 -> fragment order
 // ---------------------------------------------------------------------------
@@ -81,6 +125,43 @@ __global__ __launch_bounds__(256) void prep_s_kernel(const uint8_t* __restrict__
     st[i] = d;
 }
 
+// int4 g128 -> fragment order.  Weights from the checkpoint layout qweight
+// [K/8, N] (nibble j of word i is k = 8i + j): block (t, s), lane L = n + 16g
+// takes words 16s + 2g, +1 (k = 128s + 16g .. +15) and 16s + 8 + 2g, +1
+// (k = 128s + 64 + 16g .. +15) of column 16t + n -- the fp8 operand's k order.
+// Padding rows and steps hold code 8 (value 0).  Scales [K/128, N] fp16 ->
+// [tile][chunk][step][16 rows], padding 0.
+__global__ __launch_bounds__(256) void prep_i4w_kernel(const uint32_t* __restrict__ qkn, int N, int K,
+                                                       int tiles, int s_pad, uint4* __restrict__ wt) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)tiles * s_pad * 64) return;
+    const int L = (int)(i & 63);
+    const int64_t blk = i >> 6;
+    const int s = (int)(blk % s_pad), t = (int)(blk / s_pad);
+    const int row = 16 * t + (L & 15), g = L >> 4;
+    uint4 v = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+    if (row < N && s < K / 128) {
+        const int64_t i0 = 16 * (int64_t)s + 2 * g;
+        v.x = qkn[i0 * N + row];
+        v.y = qkn[(i0 + 1) * N + row];
+        v.z = qkn[(i0 + 8) * N + row];
+        v.w = qkn[(i0 + 9) * N + row];
+    }
+    wt[i] = v;
+}
+
+__global__ __launch_bounds__(256) void prep_i4s_kernel(const uint16_t* __restrict__ sc, int N, int K,
+                                                       int tiles, int c_pad, uint16_t* __restrict__ st) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)tiles * c_pad * 64) return;
+    const int r = (int)(i & 15);
+    const int u = (int)((i >> 4) & 3);
+    const int64_t tc = i >> 6;
+    const int c = (int)(tc % c_pad), t = (int)(tc / c_pad);
+    const int s = 4 * c + u, n = 16 * t + r;
+    st[i] = (n < N && s < K / 128) ? sc[(int64_t)s * N + n] : (uint16_t)0;
+}
+
 // ---------------------------------------------------------------------------
 // decode band on prepared weights (M <= 32)
 //
@@ -103,7 +184,7 @@ struct PDecArgs {
     const uint8_t* x8;
     const float* xs;
     const uint4* wt;
-    const uint32_t* st;
+    const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
     uint16_t* out;
     float* partials;
     int M, N, K;
@@ -114,33 +195,49 @@ struct PDecArgs {
     int ks, c_per;      // K splits across workgroups, chunks per split
 };
 
-struct PChunk {
+template <int WF> struct PChunk;
+template <> struct PChunk<kWMx> {
     uint4 w[4];
-    uint32_t s;
+    uint32_t s;          // e8m0 dword of the chunk
+};
+template <> struct PChunk<kWI4> {
+    uint4 w[4];
+    uint2 s[4];          // fp16 row scales of each step
 };
 
-__device__ __forceinline__ void pdec_load(const uint4* wp, const uint32_t* sp, int j, PChunk& c) {
+// chunk j of this wave's range: 4 weight blocks (sp: MXFP4 dwords of the
+// tile's chunks, lane-indexed; int4 8-byte row-scale quads, (chunk, step, g))
+template <int WF>
+__device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, int j, PChunk<WF>& c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
-    c.s = sp[j * 64];
+    if constexpr (WF == kWMx) {
+        c.s = reinterpret_cast<const uint32_t*>(sp)[j * 64];
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c.s[u] = reinterpret_cast<const uint2*>(sp)[j * 16 + u * 4];
+    }
 }
 
-template <int MT>
+template <int MT, int WF>
 __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int lane, int M, int j,
-                                             const PChunk& c, v4f (&acc)[MT]) {
+                                             const PChunk<WF>& c, v4f (&acc)[MT]) {
     const int g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const v8i aw = frag_fp4(c.w[u]);
+        const v8i aw = wfrag<WF>(c.w[u]);
+        typename WStep<WF>::T sc;
+        if constexpr (WF == kWMx) sc = c.s;
+        else sc = c.s[u];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = min(mt * 16 + (lane & 15), M - 1);
             const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
             const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-            if (u == 0) acc[mt] = mfma16<0>(aw, bx, acc[mt], (int)c.s);
-            if (u == 1) acc[mt] = mfma16<1>(aw, bx, acc[mt], (int)c.s);
-            if (u == 2) acc[mt] = mfma16<2>(aw, bx, acc[mt], (int)c.s);
-            if (u == 3) acc[mt] = mfma16<3>(aw, bx, acc[mt], (int)c.s);
+            if (u == 0) acc[mt] = wmma<WF, 0>(aw, bx, acc[mt], sc);
+            if (u == 1) acc[mt] = wmma<WF, 1>(aw, bx, acc[mt], sc);
+            if (u == 2) acc[mt] = wmma<WF, 2>(aw, bx, acc[mt], sc);
+            if (u == 3) acc[mt] = wmma<WF, 3>(aw, bx, acc[mt], sc);
         }
     }
 }
@@ -170,7 +267,7 @@ __device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_
     }
 }
 
-template <int MT, int D>
+template <int MT, int D, int WF>
 __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
@@ -197,7 +294,11 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int tc = min(t, a.tiles - 1);
     const int jb = nch > 0 ? j0 : 0;
     const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
-    const uint32_t* sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
+    const void* sp;
+    if constexpr (WF == kWMx)
+        sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
+    else
+        sp = reinterpret_cast<const uint2*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 16 + (lane >> 4);
     const int last = nch > 0 ? nch - 1 : 0;
 
     // Activations of this workgroup's K range -> LDS (columns >= K read as
@@ -209,9 +310,9 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     uint4 av[kActBatch];
     pdec_act_load(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
     __builtin_amdgcn_sched_barrier(0);
-    PChunk ring[D];
+    PChunk<WF> ring[D];
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) pdec_load(wp, sp, min(d, last), ring[d]);
+    for (int d = 0; d < D - 1; ++d) pdec_load<WF>(wp, sp, min(d, last), ring[d]);
     __builtin_amdgcn_sched_barrier(0);
     pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
     for (int q0 = threadIdx.x + kActBatch * nthreads; q0 < act_total; q0 += kActBatch * nthreads) {
@@ -225,9 +326,9 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
         for (int j = 0; j < nch; j += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                pdec_load(wp, sp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
+                pdec_load<WF>(wp, sp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (j + d < nch) pdec_compute<MT>(xw, stride, lane, a.M, j + d, ring[d], acc);
+                if (j + d < nch) pdec_compute<MT, WF>(xw, stride, lane, a.M, j + d, ring[d], acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -289,16 +390,16 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     }
 }
 
-template <int MT, int D>
+template <int MT, int D, int WF>
 hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D>,
+        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D, WF>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((pdec_kernel<MT, D>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
+    hipLaunchKernelGGL((pdec_kernel<MT, D, WF>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
                        stream, a);
     return hipGetLastError();
 }
@@ -325,7 +426,7 @@ struct PDrArgs {
     const uint8_t* x8;
     const float* xs;
     const uint4* wt;
-    const uint32_t* st;
+    const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
     uint16_t* out;
     float* partials;
     int M, N, K;
@@ -335,16 +436,16 @@ struct PDrArgs {
     int ks, sp;         // K splits, steps per split
 };
 
-template <int MT, int WW>
+template <int MT, int WW, int WF>
 struct PDrSlot {
     uint4 w;                                  // weight fragment block of one step
-    uint32_t sc;                              // its e8m0 dword (byte = step % 4)
+    typename WStep<WF>::T sc;                 // its scale data (MXFP4: chunk dword, byte = step % 4)
     uint32_t x[(MT * 8 + WW - 1) / WW];       // this wave's share of the activation slice
 };
 
-template <int MT, int WW>
-__device__ __forceinline__ void pdr_load(const PDrArgs& a, const uint4* wp, const uint32_t* sp, int s, int wave,
-                                         const uint32_t (&xoff)[(MT * 8 + WW - 1) / WW], PDrSlot<MT, WW>& r) {
+template <int MT, int WW, int WF>
+__device__ __forceinline__ void pdr_load(const PDrArgs& a, const uint4* wp, const void* sp, int s, int wave,
+                                         const uint32_t (&xoff)[(MT * 8 + WW - 1) / WW], PDrSlot<MT, WW, WF>& r) {
     constexpr int U = (MT * 8 + WW - 1) / WW;
     // activations first: their LDS write, one step before use, then waits only for them
 #pragma unroll
@@ -352,11 +453,12 @@ __device__ __forceinline__ void pdr_load(const PDrArgs& a, const uint4* wp, cons
         if (wave + WW * i < MT * 8)
             r.x[i] = *reinterpret_cast<const uint32_t*>(a.x8 + xoff[i] + 128 * (int64_t)s);
     r.w = wp[(int64_t)s * 64];
-    r.sc = sp[(int64_t)(s >> 2) * 64];
+    if constexpr (WF == kWMx) r.sc = reinterpret_cast<const uint32_t*>(sp)[(int64_t)(s >> 2) * 64];
+    else r.sc = reinterpret_cast<const uint2*>(sp)[(int64_t)(s >> 2) * 16 + (s & 3) * 4];
 }
 
-template <int MT, int WW>
-__device__ __forceinline__ void pdr_write(uint8_t* slice, int wave, int lane, const PDrSlot<MT, WW>& r) {
+template <int MT, int WW, int WF>
+__device__ __forceinline__ void pdr_write(uint8_t* slice, int wave, int lane, const PDrSlot<MT, WW, WF>& r) {
     constexpr int U = (MT * 8 + WW - 1) / WW;
 #pragma unroll
     for (int i = 0; i < U; ++i)
@@ -364,12 +466,14 @@ __device__ __forceinline__ void pdr_write(uint8_t* slice, int wave, int lane, co
             *reinterpret_cast<uint32_t*>(slice + 256 * (wave + WW * i) + 4 * lane) = r.x[i];
 }
 
-template <int MT>
-__device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const uint4& w, uint32_t sc, int s,
-                                        v4f (&acc)[MT]) {
+template <int MT, int WF>
+__device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const uint4& w, typename WStep<WF>::T sc,
+                                        int s, v4f (&acc)[MT]) {
     const int g = lane >> 4;
-    const v8i aw = frag_fp4(w);
-    const int scf = (int)(sc >> (8 * (s & 3)));
+    const v8i aw = wfrag<WF>(w);
+    typename WStep<WF>::T scf;
+    if constexpr (WF == kWMx) scf = sc >> (8 * (s & 3));
+    else scf = sc;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int r = 16 * mt + (lane & 15);
@@ -377,11 +481,11 @@ __device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const ui
         const uint8_t* rowp = slice + 128 * r;
         const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
                                 *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
-        acc[mt] = mfma16<0>(aw, bx, acc[mt], scf);
+        acc[mt] = wmma<WF, 0>(aw, bx, acc[mt], scf);
     }
 }
 
-template <int MT, int WW, int P>
+template <int MT, int WW, int P, int WF>
 __global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
     constexpr int U = (MT * 8 + WW - 1) / WW;
     constexpr int SLICE = MT * 2048;
@@ -394,7 +498,9 @@ __global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
     const int s0 = split * a.sp;
     const int n = min(steps - s0, a.sp);             // >= 1 (host)
     const uint4* wp = a.wt + (int64_t)t * a.s_pad * 64 + lane;
-    const uint32_t* scp = a.st + (int64_t)t * a.c_pad * 64 + lane;
+    const void* scp;
+    if constexpr (WF == kWMx) scp = reinterpret_cast<const uint32_t*>(a.st) + (int64_t)t * a.c_pad * 64 + lane;
+    else scp = reinterpret_cast<const uint2*>(a.st) + (int64_t)t * a.c_pad * 16 + (lane >> 4);
     // this wave's activation copy units: unit q covers slice rows 2q, 2q + 1
     // (256 bytes, 4 per lane); lane -> row 2q + lane / 32, swizzled chunk
     // position (lane % 32) / 4, byte 4 (lane % 4) of it
@@ -412,10 +518,10 @@ __global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    PDrSlot<MT, WW> ring[P];
+    PDrSlot<MT, WW, WF> ring[P];
 #pragma unroll
-    for (int d = 0; d < P; ++d) pdr_load<MT, WW>(a, wp, scp, s0 + min(d, n - 1), wave, xoff, ring[d]);
-    pdr_write<MT, WW>(xl, wave, lane, ring[0]);
+    for (int d = 0; d < P; ++d) pdr_load<MT, WW, WF>(a, wp, scp, s0 + min(d, n - 1), wave, xoff, ring[d]);
+    pdr_write<MT, WW, WF>(xl, wave, lane, ring[0]);
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
 
@@ -424,11 +530,11 @@ __global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
         for (int d = 0; d < P; ++d) {
             const int j = j0 + d;
             // slice j + 1 (its registers are in slot d + 1) into the free buffer
-            if (j + 1 < n) pdr_write<MT, WW>(xl + ((j + 1) & 1) * SLICE, wave, lane, ring[(d + 1) % P]);
-            if (j < n) pdr_mma<MT>(xl + (j & 1) * SLICE, lane, ring[d].w, ring[d].sc, s0 + j, acc);
+            if (j + 1 < n) pdr_write<MT, WW, WF>(xl + ((j + 1) & 1) * SLICE, wave, lane, ring[(d + 1) % P]);
+            if (j < n) pdr_mma<MT, WF>(xl + (j & 1) * SLICE, lane, ring[d].w, ring[d].sc, s0 + j, acc);
             __builtin_amdgcn_sched_barrier(0);
             // step j + P into the slot just consumed (past the end: the last step again)
-            pdr_load<MT, WW>(a, wp, scp, s0 + min(j + P, n - 1), wave, xoff, ring[d]);
+            pdr_load<MT, WW, WF>(a, wp, scp, s0 + min(j + P, n - 1), wave, xoff, ring[d]);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
@@ -467,9 +573,9 @@ __global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
     }
 }
 
-template <int MT, int WW, int P>
+template <int MT, int WW, int P, int WF>
 hipError_t launch_pdr(const PDrArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((pdr_kernel<MT, WW, P>), dim3(a.groups * a.ks), dim3(WW * 64), 0, stream, a);
+    hipLaunchKernelGGL((pdr_kernel<MT, WW, P, WF>), dim3(a.groups * a.ks), dim3(WW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -551,10 +657,32 @@ struct PfShape {
     static constexpr int WBYTES = BN / 16 * 1024;      // weight blocks per stage
     static constexpr int ABYTES = BM * 128;                // activation slice
     static constexpr int STAGE = WBYTES + ABYTES;
-    static constexpr int SBYTES = BN / 16 * 256;        // e8m0 dwords of one 4-step chunk
     static constexpr int DMA_PER_STAGE = (BN / 16) / 8 + (BM / 8) / 8;   // per wave
-    static constexpr int DMA_SCALES = (BN / 16) / 8;                     // per wave, per chunk
 };
+
+// Scale buffer of one 4-step chunk: MXFP4 e8m0 dwords (256 B per tile, lane
+// order, BN/128 copies per wave), or int4 row scales (128 B per tile = 4 steps
+// x 16 fp16, one 256-byte copy per wave: wave w's 256 bytes hold the records
+// of tiles (BN/128) w and (BN/128) w + 1 -- for BN = 128 the second half holds
+// the next tile's record and is not read).
+template <int BN, int WF>
+struct PfScales {
+    static constexpr int BYTES = WF == kWMx ? BN / 16 * 256 : 8 * 256;
+    static constexpr int DMA = WF == kWMx ? (BN / 16) / 8 : 1;             // per wave, per chunk
+    static constexpr int TILE_BYTES = WF == kWMx ? 256 : 128;             // per tile and chunk in HBM
+};
+
+// a lane's scale data of step s for weight tile b (0 <= b < BN/16) of the panel
+template <int BN, int WF>
+__device__ __forceinline__ typename WStep<WF>::T pf_scale(const uint8_t* sbuf, int b, int s, int lane) {
+    if constexpr (WF == kWMx) {
+        return reinterpret_cast<const uint32_t*>(sbuf)[64 * b + lane] >> (8 * (s & 3));
+    } else {
+        constexpr int TPW = BN / 128;   // tiles per wave record
+        return *reinterpret_cast<const uint2*>(sbuf + 256 * (b / TPW) + 128 * (b % TPW) + 32 * (s & 3) +
+                                               8 * (lane >> 4));
+    }
+}
 
 // Per-workgroup copy sources: one buffer descriptor per operand based at the
 // workgroup's tile, per-lane offsets that stay fixed over the K steps (the
@@ -565,19 +693,24 @@ struct PfSrc {
     uint32_t w_off[BN / 128], x_off[BM / 64], s_off[BN / 128];
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int WF>
 __device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int wave, int lane, PfSrc<BM, BN>& src) {
     const int t0 = tn * (BN / 16);
-    const int64_t wblk = (int64_t)a.s_pad * 1024, sblk = (int64_t)a.c_pad * 256;
+    const int64_t wblk = (int64_t)a.s_pad * 1024, sblk = (int64_t)a.c_pad * PfScales<BN, WF>::TILE_BYTES;
     src.w = make_rsrc(a.wt + t0 * wblk, (uint64_t)(a.tiles16 - t0) * wblk);
     src.sc = make_rsrc(a.st + t0 * sblk, (uint64_t)(a.tiles16 - t0) * sblk);
     src.x = make_rsrc(a.x8 + (int64_t)tm * BM * a.K, (uint64_t)(a.M - tm * BM) * a.K);
 #pragma unroll
     for (int i = 0; i < BN / 128; ++i) {
-        // weight and e8m0 blocks b = wave + 8 i of the BN/16 tiles (clamped to the last tile)
+        // weight (and MXFP4 e8m0) blocks b = wave + 8 i of the BN/16 tiles (clamped to the last tile)
         const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
         src.w_off[i] = (uint32_t)(t * wblk) + 16u * lane;
         src.s_off[i] = (uint32_t)(t * sblk) + 4u * lane;
+    }
+    if constexpr (WF == kWI4) {
+        // int4 row-scale records: tile (BN/128) wave + lane / 32, 4 bytes per lane
+        const int t = min(t0 + wave * (BN / 128) + (lane >> 5), a.tiles16 - 1) - t0;
+        src.s_off[0] = (uint32_t)(t * sblk) + 4u * (lane & 31);
     }
 #pragma unroll
     for (int i = 0; i < BM / 64; ++i) {
@@ -603,11 +736,15 @@ __device__ __forceinline__ void pf_issue_one(const PfSrc<BM, BN>& src, uint8_t* 
 }
 
 // e8m0 dwords of 4-step chunk c (two 256-byte blocks per wave) into `sbuf`
-template <int BM, int BN>
+template <int BM, int BN, int WF>
 __device__ __forceinline__ void pf_issue_scales(const PfSrc<BM, BN>& src, uint8_t* sbuf, int c, int wave) {
+    if constexpr (WF == kWMx) {
 #pragma unroll
-    for (int i = 0; i < PfShape<BM, BN>::DMA_SCALES; ++i)
-        lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
+        for (int i = 0; i < PfScales<BN, WF>::DMA; ++i)
+            lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
+    } else {
+        lds_dma4(src.sc, src.s_off[0], 128u * c, lds_addr(sbuf + 256 * wave));
+    }
 }
 
 // copies [J0, J1) of the stage
@@ -641,27 +778,28 @@ __device__ __forceinline__ void pf_copies_at(const PfSrc<BM, BN>& src, uint8_t* 
     pf_issue_range<BM, BN, F * D / FN, (F + 1) * D / FN>(src, nxt, s_nxt, wave);
 }
 
-template <int BM, int BN, int F>
-__device__ __forceinline__ void pf_group(const uint8_t* wp, const uint32_t* sp, int sh, const v8i (&bx)[PfShape<BM, BN>::FM],
-                                         uint4& wa, uint32_t& sc, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+template <int BM, int BN, int WF, int F>
+__device__ __forceinline__ void pf_group(const uint8_t* wp, const uint8_t* sbuf, int s, int wn, int lane,
+                                         const v8i (&bx)[PfShape<BM, BN>::FM], uint4& wa,
+                                         typename WStep<WF>::T& sc, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                          const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
     using S = PfShape<BM, BN>;
     if constexpr (F < S::FN) {
-        const v8i af = frag_fp4(wa);
-        const int scf = (int)(sc >> sh);
+        const v8i af = wfrag<WF>(wa);
+        const typename WStep<WF>::T scf = sc;
         if constexpr (F + 1 < S::FN) {
-            sc = sp[64 * (F + 1)];
+            sc = pf_scale<BN, WF>(sbuf, wn * S::FN + F + 1, s, lane);
             wa = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 1));
         }
         pf_copies_at<BM, BN, F>(src, nxt, s_nxt, wave);
 #pragma unroll
-        for (int h = 0; h < S::FM; ++h) acc[F][h] = mfma16<0>(af, bx[h], acc[F][h], scf);
+        for (int h = 0; h < S::FM; ++h) acc[F][h] = wmma<WF, 0>(af, bx[h], acc[F][h], scf);
         __builtin_amdgcn_sched_barrier(0);
-        pf_group<BM, BN, F + 1>(wp, sp, sh, bx, wa, sc, acc, src, nxt, s_nxt, wave);
+        pf_group<BM, BN, WF, F + 1>(wp, sbuf, s, wn, lane, bx, wa, sc, acc, src, nxt, s_nxt, wave);
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WF>
 __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int wm, int lane,
                                            v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                            const uint8_t* sbuf,
@@ -670,7 +808,6 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
     const int g = lane >> 4;
     const uint8_t* ws = st;
     const uint8_t* as = st + S::WBYTES;
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(sbuf);
     // activation fragments of the wave's FM column tiles, then the weight
     // fragments one at a time against all of them, the next one's LDS read
     // issued before the current one's products
@@ -684,10 +821,9 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
                          *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
     }
     const uint8_t* wp = ws + 1024 * (wn * S::FN) + 16 * lane;
-    const uint32_t* sp = ss + 64 * (wn * S::FN) + lane;
-    uint32_t sc = sp[0];
+    typename WStep<WF>::T sc = pf_scale<BN, WF>(sbuf, wn * S::FN, s, lane);
     uint4 wa = *reinterpret_cast<const uint4*>(wp);
-    pf_group<BM, BN, 0>(wp, sp, 8 * (s & 3), bx, wa, sc, acc, src, nxt, s_nxt, wave);
+    pf_group<BM, BN, WF, 0>(wp, sbuf, s, wn, lane, bx, wa, sc, acc, src, nxt, s_nxt, wave);
 }
 
 
@@ -749,12 +885,13 @@ __device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int
 // copies for step u into the free stage issued between the products.  In
 // issue order the copies of step u are: [e8m0 chunk u/4 if u % 4 == 0 and
 // u < steps] [weights, activations (of step min(u, steps - 1))].
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WF>
 __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     using S = PfShape<BM, BN>;
+    using SC = PfScales<BN, WF>;
     static_assert(NS >= 3 && NS <= 5, "ring depth");
-    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
-    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * S::SBYTES;
+    constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
+    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * SC::BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
     int tm, tn;
@@ -773,11 +910,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     uint8_t* const base = lds + kPfBase;
     uint8_t* const sbase = base + NS * S::STAGE;
     PfSrc<BM, BN> src;
-    pf_sources<BM, BN>(a, tm, tn, wave, lane, src);
+    pf_sources<BM, BN, WF>(a, tm, tn, wave, lane, src);
     // prologue: steps 0 .. NS - 2 (repeating the last step when K is shorter)
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) {
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
         pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
     }
     int cur = 0, nxt = (NS - 1) * S::STAGE;   // stage offsets of steps s and s + NS - 1
@@ -796,11 +933,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");     // no LDS access moves across the barrier
         const int u = s + NS - 1;
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
         // copies for step u; in the last NS - 1 steps they repeat the last step
         // into the free stage, which is never read again (no branch in the
         // product sequence)
-        pf_compute<BM, BN>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * S::SBYTES, src, base + nxt,
+        pf_compute<BM, BN, WF>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
                            min(u, steps - 1), wave);
         cur = cur == (NS - 1) * S::STAGE ? 0 : cur + S::STAGE;
         nxt = nxt == (NS - 1) * S::STAGE ? 0 : nxt + S::STAGE;
@@ -831,16 +968,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
 // sequence has no branch.
 // ---------------------------------------------------------------------------
 
-template <int BM, int BN>
+template <int BM, int BN, int WF>
 struct PfFrag {
     v8i bx[PfShape<BM, BN>::FM];
     uint4 af[PfShape<BM, BN>::FN];
-    uint32_t sc[PfShape<BM, BN>::FN];
+    typename WStep<WF>::T sc[PfShape<BM, BN>::FN];     // of the fragments' step
 };
 
-template <int BM, int BN>
-__device__ __forceinline__ void pf_read(const uint8_t* st, const uint8_t* sbuf, int wn, int wm, int lane,
-                                        PfFrag<BM, BN>& F) {
+template <int BM, int BN, int WF>
+__device__ __forceinline__ void pf_read(const uint8_t* st, const uint8_t* sbuf, int s, int wn, int wm, int lane,
+                                        PfFrag<BM, BN, WF>& F) {
     using S = PfShape<BM, BN>;
     const int g = lane >> 4;
     const uint8_t* as = st + S::WBYTES;
@@ -853,11 +990,10 @@ __device__ __forceinline__ void pf_read(const uint8_t* st, const uint8_t* sbuf, 
                            *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
     }
     const uint8_t* wp = st + 1024 * (wn * S::FN) + 16 * lane;
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(sbuf) + 64 * (wn * S::FN) + lane;
 #pragma unroll
     for (int f = 0; f < S::FN; ++f) {
         F.af[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
-        F.sc[f] = sp[64 * f];
+        F.sc[f] = pf_scale<BN, WF>(sbuf, wn * S::FN + f, s, lane);
     }
 }
 
@@ -866,29 +1002,29 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int BM, int BN, int F0, int F1>
-__device__ __forceinline__ void pfp_groups(const PfFrag<BM, BN>& F, int sh, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+template <int BM, int BN, int WF, int F0, int F1>
+__device__ __forceinline__ void pfp_groups(const PfFrag<BM, BN, WF>& F, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                            const PfSrc<BM, BN>& src, uint8_t* tgt, int s_cp, int wave) {
     using S = PfShape<BM, BN>;
     if constexpr (F0 < F1) {
         constexpr int H = S::FN > 1 ? S::FN / 2 : 1, D = S::DMA_PER_STAGE;
         if constexpr (F0 < H) pf_issue_range<BM, BN, F0 * D / H, (F0 + 1) * D / H>(src, tgt, s_cp, wave);
-        const v8i af = frag_fp4(F.af[F0]);
-        const int scf = (int)(F.sc[F0] >> sh);
+        const v8i af = wfrag<WF>(F.af[F0]);
 #pragma unroll
-        for (int h = 0; h < S::FM; ++h) acc[F0][h] = mfma16<0>(af, F.bx[h], acc[F0][h], scf);
+        for (int h = 0; h < S::FM; ++h) acc[F0][h] = wmma<WF, 0>(af, F.bx[h], acc[F0][h], F.sc[F0]);
         __builtin_amdgcn_sched_barrier(0);
-        pfp_groups<BM, BN, F0 + 1, F1>(F, sh, acc, src, tgt, s_cp, wave);
+        pfp_groups<BM, BN, WF, F0 + 1, F1>(F, acc, src, tgt, s_cp, wave);
     }
 }
 
-template <int BM, int BN, int NS>
-__device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN>& Fc, PfFrag<BM, BN>& Fn,
+template <int BM, int BN, int NS, int WF>
+__device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN, WF>& Fc, PfFrag<BM, BN, WF>& Fn,
                                          v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                          const PfSrc<BM, BN>& src, uint8_t* base, uint8_t* sbase, int& cur,
                                          int wn, int wm, int lane, int wave) {
     using S = PfShape<BM, BN>;
-    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
+    using SC = PfScales<BN, WF>;
+    constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
     constexpr int H = S::FN > 1 ? S::FN / 2 : 1;
     constexpr int LAST = (NS - 1) * S::STAGE;
     // opaque to the optimiser (addresses from a few bases plus immediates)
@@ -896,9 +1032,8 @@ __device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN>&
     const int nx = cur == LAST ? 0 : cur + S::STAGE;       // stage of step s + 1
     const int tg = cur == 0 ? LAST : cur - S::STAGE;       // stage (s - 1) % NS: copies for step u
     const int u = s + NS - 1;
-    if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
-    const int sh = 8 * (s & 3);
-    pfp_groups<BM, BN, 0, H>(Fc, sh, acc, src, base + tg, min(u, steps - 1), wave);
+    if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
+    pfp_groups<BM, BN, WF, 0, H>(Fc, acc, src, base + tg, min(u, steps - 1), wave);
     // pin the first half's products before the barrier (they touch no memory,
     // so nothing else keeps them there): the matrix pipe works through them
     // while the wave waits
@@ -916,19 +1051,20 @@ __device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN>&
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");     // no LDS access moves across the barrier
-    pf_read<BM, BN>(base + nx, sbase + (((s + 1) >> 2) & 1) * S::SBYTES, wn, wm, lane, Fn);
+    pf_read<BM, BN, WF>(base + nx, sbase + (((s + 1) >> 2) & 1) * SC::BYTES, s + 1, wn, wm, lane, Fn);
     __builtin_amdgcn_sched_barrier(0);
-    pfp_groups<BM, BN, H, S::FN>(Fc, sh, acc, src, base + tg, min(u, steps - 1), wave);
+    pfp_groups<BM, BN, WF, H, S::FN>(Fc, acc, src, base + tg, min(u, steps - 1), wave);
     cur = nx;
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WF>
 __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     using S = PfShape<BM, BN>;
+    using SC = PfScales<BN, WF>;
     static_assert(NS >= 3 && NS <= 5, "ring depth");
     static_assert(BM <= 128, "two fragment sets fit in registers for short tiles only");
-    constexpr int D = S::DMA_PER_STAGE, DS = S::DMA_SCALES;
-    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * S::SBYTES;
+    constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
+    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * SC::BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
     int tm, tn;
@@ -946,10 +1082,10 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     uint8_t* const base = lds + kPfBase;
     uint8_t* const sbase = base + NS * S::STAGE;
     PfSrc<BM, BN> src;
-    pf_sources<BM, BN>(a, tm, tn, wave, lane, src);
+    pf_sources<BM, BN, WF>(a, tm, tn, wave, lane, src);
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) {
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
         pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
     }
     // step 0's copies (steps 1 .. NS - 2 may stay in flight), then its fragments
@@ -960,12 +1096,12 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     else wait_vmcnt<(NS - 2) * D>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    PfFrag<BM, BN> F0, F1;
-    pf_read<BM, BN>(base, sbase, wn, wm, lane, F0);
+    PfFrag<BM, BN, WF> F0, F1;
+    pf_read<BM, BN, WF>(base, sbase, 0, wn, wm, lane, F0);
     int cur = 0;
     for (int s = 0; s < steps; s += 2) {
-        pfp_iter<BM, BN, NS>(s, steps, F0, F1, acc, src, base, sbase, cur, wn, wm, lane, wave);
-        if (s + 1 < steps) pfp_iter<BM, BN, NS>(s + 1, steps, F1, F0, acc, src, base, sbase, cur, wn, wm, lane, wave);
+        pfp_iter<BM, BN, NS, WF>(s, steps, F0, F1, acc, src, base, sbase, cur, wn, wm, lane, wave);
+        if (s + 1 < steps) pfp_iter<BM, BN, NS, WF>(s + 1, steps, F1, F0, acc, src, base, sbase, cur, wn, wm, lane, wave);
     }
     // the repeated copies of the last steps may still be landing: drain them
     // before the workgroup's LDS is released
@@ -973,19 +1109,19 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     pf_epilogue<BM, BN>(a, tm, tn, wn, wm, lane, acc);
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WF>
 hipError_t launch_pfp(const PfArgs& a, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((pfp_kernel<BM, BN, NS>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((pfp_kernel<BM, BN, NS, WF>), dim3(grid), dim3(kPfThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WF>
 hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n;
     const int grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((pf_kernel<BM, BN, NS>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((pf_kernel<BM, BN, NS, WF>), dim3(grid), dim3(kPfThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1013,6 +1149,28 @@ hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prep_s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, we,
                        (int)N, (int)K, tiles, c_pad, reinterpret_cast<uint32_t*>(st));
+    return hipGetLastError();
+}
+
+void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes) {
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    *w_bytes = (size_t)(tiles * c_pad * 4 * 1024);
+    *s_bytes = (size_t)(tiles * c_pad * 128);
+}
+
+hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
+                             uint8_t* st, hipStream_t stream) {
+    const int tiles = (int)((N + 15) / 16);
+    const int c_pad = (int)((K / 128 + 3) / 4);
+    const int64_t nw = (int64_t)tiles * c_pad * 4 * 64, ns = (int64_t)tiles * c_pad * 64;
+    hipLaunchKernelGGL(prep_i4w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qkn), (int)N, (int)K, tiles, 4 * c_pad,
+                       reinterpret_cast<uint4*>(wt));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_i4s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, sc,
+                       (int)N, (int)K, tiles, c_pad, reinterpret_cast<uint16_t*>(st));
     return hipGetLastError();
 }
 
@@ -1074,7 +1232,7 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M) {
 
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool int4) {
     PfArgs a{};
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -1097,9 +1255,16 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
     // (64-row tiles are wide: narrow layers take the register-streamed kernel
     // at M <= 64; 256-row tiles come only with at least 512 256-wide tiles)
-    if (bm == 64) return launch_pfp<64, 256, 5>(a, stream);
-    if (bm == 128) return bn == 128 ? launch_pfp<128, 128, 4>(a, stream) : launch_pfp<128, 256, 4>(a, stream);
-    return launch_pf<256, 256, 3>(a, stream);
+    if (int4) {
+        if (bm == 64) return launch_pfp<64, 256, 5, kWI4>(a, stream);
+        if (bm == 128)
+            return bn == 128 ? launch_pfp<128, 128, 4, kWI4>(a, stream) : launch_pfp<128, 256, 4, kWI4>(a, stream);
+        return launch_pf<256, 256, 3, kWI4>(a, stream);
+    }
+    if (bm == 64) return launch_pfp<64, 256, 5, kWMx>(a, stream);
+    if (bm == 128)
+        return bn == 128 ? launch_pfp<128, 128, 4, kWMx>(a, stream) : launch_pfp<128, 256, 4, kWMx>(a, stream);
+    return launch_pf<256, 256, 3, kWMx>(a, stream);
 }
 
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K) {
@@ -1145,11 +1310,11 @@ size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                                      uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, bool int4) {
     PDrArgs a{};
     a.x8 = x8; a.xs = xs;
     a.wt = reinterpret_cast<const uint4*>(wt);
-    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.st = st;
     a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.c_pad = (int)((K / 128 + 3) / 4);
@@ -1161,20 +1326,23 @@ hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const u
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles));
     }
     hipError_t e;
-    if (M <= 16) e = launch_pdr<1, 8, 8>(a, stream);
-    else if (M <= 32) e = launch_pdr<2, 8, 8>(a, stream);
-    else e = launch_pdr<4, 8, 8>(a, stream);
+    if (int4)
+        e = M <= 16 ? launch_pdr<1, 8, 8, kWI4>(a, stream)
+            : M <= 32 ? launch_pdr<2, 8, 8, kWI4>(a, stream) : launch_pdr<4, 8, 8, kWI4>(a, stream);
+    else
+        e = M <= 16 ? launch_pdr<1, 8, 8, kWMx>(a, stream)
+            : M <= 32 ? launch_pdr<2, 8, 8, kWMx>(a, stream) : launch_pdr<4, 8, 8, kWMx>(a, stream);
     if (e != hipSuccess || a.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
-                                  int64_t N, int64_t K, void* ws, hipStream_t stream) {
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4) {
     PDecArgs a{};
     a.x8 = x8; a.xs = xs;
     a.wt = reinterpret_cast<const uint4*>(wt);
-    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.st = st;
     a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.c_pad = (int)((K / 128 + 3) / 4);
@@ -1189,10 +1357,14 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
     const size_t lds = prepared_lds_bytes(p, M);
     hipError_t e;
-    if (p.mt == 1)
-        e = p.u == 4 ? launch_pdec<1, 4>(a, lds, stream) : launch_pdec<1, 3>(a, lds, stream);
-    else
-        e = p.u == 4 ? launch_pdec<2, 4>(a, lds, stream) : launch_pdec<2, 3>(a, lds, stream);
+    if (int4) {   // ring depth 3 (the tuning entry point's depth 4 is MXFP4 only)
+        e = p.mt == 1 ? launch_pdec<1, 3, kWI4>(a, lds, stream) : launch_pdec<2, 3, kWI4>(a, lds, stream);
+    } else {
+        if (p.mt == 1)
+            e = p.u == 4 ? launch_pdec<1, 4, kWMx>(a, lds, stream) : launch_pdec<1, 3, kWMx>(a, lds, stream);
+        else
+            e = p.u == 4 ? launch_pdec<2, 4, kWMx>(a, lds, stream) : launch_pdec<2, 3, kWMx>(a, lds, stream);
+    }
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }

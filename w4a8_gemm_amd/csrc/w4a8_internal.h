@@ -44,6 +44,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // 448 (0x7E), sign bit kept (so -0 and negative values that round to zero give
 // 0x80).  Integer rounding on the fp32 bits for the normal range, an exact
 // scaling plus rint for the subnormal range.
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Eight int4 codes (one word, nibble j = k j) -> eight e4m3 bytes of (c - 8) in
+// k order.  Codes 0..7 map to -8..-1 and 8..15 to 0..7; each half is an 8-byte
+// table indexed by c & 7, and bit 3 picks the half.
+__device__ __forceinline__ uint2 int4x8_to_e4m3(uint32_t w) {
+    const uint32_t kNegLo = 0xCACCCED0u, kNegHi = 0xB8C0C4C8u;  // -8 -7 -6 -5 | -4 -3 -2 -1
+    const uint32_t kPosLo = 0x44403800u, kPosHi = 0x4E4C4A48u;  //  0  1  2  3 |  4  5  6  7
+    const uint32_t ev = w & 0x0F0F0F0Fu;          // k = 0, 2, 4, 6
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // k = 1, 3, 5, 7
+    const uint32_t se = ev & 0x07070707u, so = od & 0x07070707u;
+    const uint32_t ne = __builtin_amdgcn_perm(kNegHi, kNegLo, se);
+    const uint32_t pe = __builtin_amdgcn_perm(kPosHi, kPosLo, se);
+    const uint32_t no = __builtin_amdgcn_perm(kNegHi, kNegLo, so);
+    const uint32_t po = __builtin_amdgcn_perm(kPosHi, kPosLo, so);
+    const uint32_t me = ((ev >> 1) & 0x04040404u) | 0x03020100u;  // byte i -> i, or i+4 if c >= 8
+    const uint32_t mo = ((od >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t e = __builtin_amdgcn_perm(pe, ne, me);
+    const uint32_t o = __builtin_amdgcn_perm(po, no, mo);
+    return make_uint2(__builtin_amdgcn_perm(o, e, 0x05010400u), __builtin_amdgcn_perm(o, e, 0x07030602u));
+}
+
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
     const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
     const float a = fminf(fabsf(y), 448.0f);
@@ -98,7 +122,7 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth);
 size_t prepared_lds_bytes(const GemmPlan& p, int64_t M);
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
-                                  int64_t N, int64_t K, void* ws, hipStream_t stream);
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
 // Which kernel serves a GEMM on prepared weights: the split-K decode kernel
 // (M <= 12; M <= 32 on narrow layers), the register-streamed kernel (up to
 // M = 64 on layers too narrow for the tiled kernel to fill the CUs: K split
@@ -108,10 +132,15 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K);
 size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                                      uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
-                                     hipStream_t stream);
+                                     hipStream_t stream, bool int4);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool int4);
+// int4 g128 in fragment order (same weight geometry as MXFP4; row scales
+// [tile][chunk][step][16] fp16)
+void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
+                             uint8_t* st, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
