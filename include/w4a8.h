@@ -243,12 +243,11 @@ w4a8_status w4a8_int4g128_gemm(
 /* int4 g128 weights in matrix-core fragment order (load time) and the GEMM on
  * them.  Source: "radiance_autoround.py", as w4a8_int4g128_gemm above, with the
  * load-time repack of "vllm-radiance (MXFP4)", How the MXFP4 path works.  The
- * layout follows the MXFP4 fragment order: one 1 KiB block per 16-row tile t
- * and 128-wide K step s, tiles major; lane L = n + 16g holds 16 bytes of codes
- * of row 16t+n: words 16s+2g, 16s+2g+1 (k = 128s+16g .. +15) and 16s+8+2g,
- * 16s+9+2g (k = 128s+64+16g .. +15) of the checkpoint layout -- the k order of
- * the fp8 matrix operand, so the codes widen to c - 8 in e4m3 in registers.
- * Row scales: fp16 [tile][4-step chunk][step][16 rows].  Rows are padded to 16
+ * layout is the MXFP4 fragment order: one 1 KiB block per 16-row tile t and
+ * 128-wide K step s, tiles major; lane L = n + 16g holds 16 bytes of codes of
+ * row 16t+n: words 16s+4g .. 16s+4g+3 of the checkpoint layout (k = 128s+32g
+ * .. +31, nibble j of a word is k = 8i + j).  Row scales: fp16 [tile][4-step
+ * chunk][step][16 rows].  Rows are padded to 16
  * and steps to a multiple of 4 (code 8, scale 0).  The result equals
  * w4a8_int4g128_gemm's in value (fp32 accumulation; summation order may
  * differ).

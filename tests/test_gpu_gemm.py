@@ -400,8 +400,8 @@ def _unprepare_int4(wt, st, N, K):
     K_pad/8] words (transposed checkpoint layout) and fp16 scales [N_pad, K_pad/128]."""
     tiles, steps = (N + 15) // 16, K // 128
     s4 = 4 * ((steps + 3) // 4)
-    w = wt.view(np.uint32).reshape(tiles, s4, 4, 16, 2, 2)        # t, s, g, n, half, pair
-    w = w.transpose(0, 3, 1, 4, 2, 5).reshape(tiles * 16, s4 * 16)  # word 16s + 8h + 2g + p
+    w = wt.view(np.uint32).reshape(tiles, s4, 4, 16, 4)           # t, s, g, n, word
+    w = w.transpose(0, 3, 1, 2, 4).reshape(tiles * 16, s4 * 16)     # word 16s + 4g + i
     sc = st.view(np.uint16).reshape(tiles, s4 // 4, 4, 16)        # t, chunk, step, n
     sc = sc.transpose(0, 3, 1, 2).reshape(tiles * 16, s4)
     return w, sc

@@ -49,15 +49,35 @@ __device__ __forceinline__ v4f mfma16(v8i a_fp4, v8i b_fp8, v4f c, int scale_a) 
 // same for both):
 //   kWMx  MXFP4: e2m1 codes (lane bytes = k 32g .. 32g+31), e8m0 scales as a
 //         dword per lane and 4-step chunk, applied by the MFMA's scale operand.
-//   kWI4  symmetric int4 g128: codes c (value c - 8), lane bytes = k 16g ..
-//         16g+15 and 64+16g .. 64+16g+15 (the fp8 operand order), widened to
-//         e4m3 in registers; one fp16 scale per weight row and step, applied
-//         to the step's products in fp32.
+//   kWI4  symmetric int4 g128: codes c (value c - 8) in the same nibble order
+//         (lane bytes = k 32g .. 32g+31, low nibble even k); one fp16 scale
+//         per weight row and step, applied to the step's products in fp32.
+//         The tiled kernels widen the codes to e4m3 in registers and multiply
+//         fp8 x fp8, the activation fragment read in the same k order (the
+//         dot product is indifferent to how k is dealt to the operand bytes,
+//         as long as both operands agree).  The split-K decode kernels, where
+//         each weight fragment meets one or a few activation fragments and
+//         the widening would bound the kernel, split the code instead:
+//         c - 8 = 2 (c & 3)/2 + 8 ((c >> 2) & 3)/2 - 8, two e2m1 fragments
+//         (codes 0..3 are the values 0, 0.5, 1, 1.5) taken with one mask each,
+//         scaled by 2 and 8 through the matrix core's e8m0 operand, and the
+//         -8 sum(x) term from a constant fragment (-1 x 8) fed in as the
+//         accumulator input.
 constexpr int kWMx = 0, kWI4 = 1;
 
 template <int WF> struct WStep;                               // per-step scale data of a lane
 template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte = step % 4)
 template <> struct WStep<kWI4> { using T = uint2; };         // fp16 scales of its 4 output rows
+
+// a lane's activation fragment (B operand) from its LDS row (16-byte chunks
+// XOR-swizzled by sw): MXFP4 pairs with the fp8 operand's own k order, the
+// widened int4 codes with 32 consecutive k
+template <int WF>
+__device__ __forceinline__ v8i act_frag(const uint8_t* rowp, int g, int sw) {
+    const int c0 = WF == kWMx ? g : 2 * g, c1 = WF == kWMx ? 4 + g : 2 * g + 1;
+    return frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (c0 ^ sw)),
+                    *reinterpret_cast<const uint4*>(rowp + 16 * (c1 ^ sw)));
+}
 
 // a lane's weight fragment (A operand) from its 16 stored bytes
 template <int WF>
@@ -86,6 +106,32 @@ __device__ __forceinline__ v4f wmma(v8i a, v8i b, v4f acc, typename WStep<WF>::T
         acc[3] = acc[3] + f16_to_f32(sc.y >> 16) * t[3];
         return acc;
     }
+}
+
+// Decode kernels, int4: the two e2m1 halves of a lane's 16 stored bytes
+struct I4Split {
+    v8i lo, hi;
+};
+__device__ __forceinline__ I4Split i4_split(uint4 q) {
+    constexpr uint32_t m = 0x33333333u;
+    I4Split r;
+    r.lo = frag_fp4(make_uint4(q.x & m, q.y & m, q.z & m, q.w & m));
+    r.hi = frag_fp4(make_uint4((q.x >> 2) & m, (q.y >> 2) & m, (q.z >> 2) & m, (q.w >> 2) & m));
+    return r;
+}
+// acc += scale(row) * (x . (c - 8)) over one K step
+__device__ __forceinline__ v4f i4_split_mma(const I4Split& w, v8i bx, v4f acc, uint2 sc) {
+    constexpr int kX2 = 128, kX8 = 130;                       // e8m0 2^1, 2^3
+    const v8i neg1 = {(int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, 0, 0, 0, 0};
+    v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(neg1, bx, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4,
+                                                             kFmtFp8, 0, kX8, 0, kUnitScale);
+    t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.lo, bx, t, kFmtFp4, kFmtFp8, 0, kX2, 0, kUnitScale);
+    t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0, kUnitScale);
+    acc[0] = acc[0] + f16_to_f32(sc.x & 0xFFFFu) * t[0];
+    acc[1] = acc[1] + f16_to_f32(sc.x >> 16) * t[1];
+    acc[2] = acc[2] + f16_to_f32(sc.y & 0xFFFFu) * t[2];
+    acc[3] = acc[3] + f16_to_f32(sc.y >> 16) * t[3];
+    return acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -127,10 +173,9 @@ __global__ __launch_bounds__(256) void prep_s_kernel(const uint8_t* __restrict__
 
 // int4 g128 -> fragment order.  Weights from the checkpoint layout qweight
 // [K/8, N] (nibble j of word i is k = 8i + j): block (t, s), lane L = n + 16g
-// takes words 16s + 2g, +1 (k = 128s + 16g .. +15) and 16s + 8 + 2g, +1
-// (k = 128s + 64 + 16g .. +15) of column 16t + n -- the fp8 operand's k order.
-// Padding rows and steps hold code 8 (value 0).  Scales [K/128, N] fp16 ->
-// [tile][chunk][step][16 rows], padding 0.
+// takes words 16s + 4g .. 16s + 4g + 3 (k = 128s + 32g .. +31) of column
+// 16t + n -- the MXFP4 layout's k order.  Padding rows and steps hold code 8
+// (value 0).  Scales [K/128, N] fp16 -> [tile][chunk][step][16 rows], padding 0.
 __global__ __launch_bounds__(256) void prep_i4w_kernel(const uint32_t* __restrict__ qkn, int N, int K,
                                                        int tiles, int s_pad, uint4* __restrict__ wt) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -141,11 +186,11 @@ __global__ __launch_bounds__(256) void prep_i4w_kernel(const uint32_t* __restric
     const int row = 16 * t + (L & 15), g = L >> 4;
     uint4 v = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
     if (row < N && s < K / 128) {
-        const int64_t i0 = 16 * (int64_t)s + 2 * g;
+        const int64_t i0 = 16 * (int64_t)s + 4 * g;
         v.x = qkn[i0 * N + row];
         v.y = qkn[(i0 + 1) * N + row];
-        v.z = qkn[(i0 + 8) * N + row];
-        v.w = qkn[(i0 + 9) * N + row];
+        v.z = qkn[(i0 + 2) * N + row];
+        v.w = qkn[(i0 + 3) * N + row];
     }
     wt[i] = v;
 }
@@ -225,19 +270,27 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int 
     const int g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const v8i aw = wfrag<WF>(c.w[u]);
-        typename WStep<WF>::T sc;
-        if constexpr (WF == kWMx) sc = c.s;
-        else sc = c.s[u];
+        if constexpr (WF == kWMx) {
+            const v8i aw = frag_fp4(c.w[u]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = min(mt * 16 + (lane & 15), M - 1);
-            const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
-            const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-            if (u == 0) acc[mt] = wmma<WF, 0>(aw, bx, acc[mt], sc);
-            if (u == 1) acc[mt] = wmma<WF, 1>(aw, bx, acc[mt], sc);
-            if (u == 2) acc[mt] = wmma<WF, 2>(aw, bx, acc[mt], sc);
-            if (u == 3) acc[mt] = wmma<WF, 3>(aw, bx, acc[mt], sc);
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = min(mt * 16 + (lane & 15), M - 1);
+                const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
+                const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+                if (u == 0) acc[mt] = mfma16<0>(aw, bx, acc[mt], (int)c.s);
+                if (u == 1) acc[mt] = mfma16<1>(aw, bx, acc[mt], (int)c.s);
+                if (u == 2) acc[mt] = mfma16<2>(aw, bx, acc[mt], (int)c.s);
+                if (u == 3) acc[mt] = mfma16<3>(aw, bx, acc[mt], (int)c.s);
+            }
+        } else {
+            const I4Split w = i4_split(c.w[u]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = min(mt * 16 + (lane & 15), M - 1);
+                const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
+                const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+                acc[mt] = i4_split_mma(w, bx, acc[mt], c.s[u]);
+            }
         }
     }
 }
@@ -470,18 +523,23 @@ template <int MT, int WF>
 __device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const uint4& w, typename WStep<WF>::T sc,
                                         int s, v4f (&acc)[MT]) {
     const int g = lane >> 4;
-    const v8i aw = wfrag<WF>(w);
-    typename WStep<WF>::T scf;
-    if constexpr (WF == kWMx) scf = sc >> (8 * (s & 3));
-    else scf = sc;
+    if constexpr (WF == kWMx) {
+        const v8i aw = frag_fp4(w);
+        const int scf = (int)(sc >> (8 * (s & 3)));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int r = 16 * mt + (lane & 15);
-        const int sw = (r >> 1) & 7;
-        const uint8_t* rowp = slice + 128 * r;
-        const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
-                                *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
-        acc[mt] = wmma<WF, 0>(aw, bx, acc[mt], scf);
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = 16 * mt + (lane & 15);
+            const v8i bx = act_frag<kWMx>(slice + 128 * r, g, (r >> 1) & 7);
+            acc[mt] = mfma16<0>(aw, bx, acc[mt], scf);
+        }
+    } else {
+        const I4Split ws = i4_split(w);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = 16 * mt + (lane & 15);
+            const v8i bx = act_frag<kWMx>(slice + 128 * r, g, (r >> 1) & 7);
+            acc[mt] = i4_split_mma(ws, bx, acc[mt], sc);
+        }
     }
 }
 
@@ -817,8 +875,7 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
         const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
         const int sw = (r >> 1) & 7;
         const uint8_t* rowp = as + 128 * r;
-        bx[h] = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
-                         *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
+        bx[h] = act_frag<WF>(rowp, g, sw);
     }
     const uint8_t* wp = ws + 1024 * (wn * S::FN) + 16 * lane;
     typename WStep<WF>::T sc = pf_scale<BN, WF>(sbuf, wn * S::FN, s, lane);
@@ -986,8 +1043,7 @@ __device__ __forceinline__ void pf_read(const uint8_t* st, const uint8_t* sbuf, 
         const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
         const int sw = (r >> 1) & 7;
         const uint8_t* rowp = as + 128 * r;
-        F.bx[h] = frag_fp8(*reinterpret_cast<const uint4*>(rowp + 16 * (g ^ sw)),
-                           *reinterpret_cast<const uint4*>(rowp + 16 * ((4 + g) ^ sw)));
+        F.bx[h] = act_frag<WF>(rowp, g, sw);
     }
     const uint8_t* wp = st + 1024 * (wn * S::FN) + 16 * lane;
 #pragma unroll
