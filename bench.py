@@ -410,26 +410,30 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
     res["down_proj_prepared"] = pdp
     log("down_proj prepared", pdp)
     del pdc, dw, de
-    # int4 g128
+    # int4 g128, fragment order (the load-time check of qzeros, then the repack), eight copies
     q = synth.int4()
-    qnk = w4.int4g128_prepare(torch.from_numpy(q["qweight_kn"]).to(dev),
-                              torch.from_numpy(q["qzeros"]).to(dev))
+    qkn = torch.from_numpy(q["qweight_kn"]).to(dev)
+    qz = torch.from_numpy(q["qzeros"]).to(dev)
     sc = torch.from_numpy(q["scales"].view(np.int16)).view(torch.float16).to(dev)
-    qcopies = [(qnk, sc)] + [(qnk.clone(), sc.clone()) for _ in range(7)]
-    iws = w4.Workspace(64, q["N"], q["K"], "int4", dev)
+    qcopies = [w4.int4g128_prepare_fragments(qkn, qz, sc) for _ in range(8)]
+    del qkn, qz, sc
+    iws = w4.Workspace(64, q["N"], q["K"], "int4_prepared", dev)
     i4 = {}
-    for M in (1, 64, 2048):
+    for M in (1, 16, 64, 2048):
         xb = torch.from_numpy(synth.acts(M, q["K"], seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)
         a8, asc = w4.quant_act_fp8_per_token(xb)
         oo = torch.empty((M, q["N"]), dtype=torch.bfloat16, device=dev)
         reps = 8 if M <= 64 else 2
         dt = _timed_graph(torch, timer, graph_of,
-                          [lambda r=r: w4.int4g128_gemm(a8, asc, qcopies[r][0], qcopies[r][1], out=oo,
-                                                        workspace=iws) for r in range(reps)], 10)
+                          [lambda r=r: w4.int4g128_gemm_prepared(a8, asc, qcopies[r], out=oo, workspace=iws)
+                           for r in range(reps)], 10 if M <= 64 else 3)
         b = q["N"] * q["K"] // 2 + q["N"] * q["K"] // 64 + M * q["K"] + M * 4 + M * q["N"] * 2
-        ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1)}
+        ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+               "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
         if M > 64:
-            ent["tflops"] = round(2.0 * M * q["N"] * q["K"] / dt / 1e12, 1)
+            fl = 2.0 * M * q["N"] * q["K"]
+            ent["tflops"] = round(fl / dt / 1e12, 1)
+            ent["frac_of_fp8_peak"] = round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4)
         i4[str(M)] = ent
     res["int4_g128"] = i4
     log("int4", i4)
