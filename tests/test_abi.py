@@ -129,6 +129,27 @@ def test_workspace_bytes_contract(L):
     assert wb(4096, 5120, 17408, 0) == wb(64, 5120, 17408, 0)
 
 
+def test_prepared_tiled_split_workspace(L):
+    """Few tiles on a long K: the tiled kernel splits K (fp32 partials), so a
+    prepared GEMM above the decode band may need a workspace; sizing and the
+    missing-workspace error are host-side."""
+    N, K, M = 5120, 17408, 128
+    # 128-row tiles, 128 wide (40 of them): at most one workgroup per CU ->
+    # 6 splits of 24 steps; header of one counter per 16 rows, then [ks][M][N]
+    header = (((N + 15) // 16) * 4 + 255) // 256 * 256
+    want = header + 6 * M * N * 4
+    for kind in (2, 3):
+        assert L.w4a8_gemm_workspace_bytes(M, N, K, kind) == want
+        assert L.w4a8_gemm_workspace_bytes(M + 64, N, K, kind) >= want
+        # many tiles: no split, the decode band's need is all that remains
+        assert L.w4a8_gemm_workspace_bytes(4096, N, K, kind) == L.w4a8_gemm_workspace_bytes(1024, N, K, kind)
+    g = L.w4a8_mxfp4_gemm_prepared
+    assert g(_p(), _p(), _p(), _p(), _p(), M, N, K, None, 0, None) == WORKSPACE
+    assert g(_p(), _p(), _p(), _p(), _p(), M, N, K, _p(), want - 256, None) == WORKSPACE
+    i = L.w4a8_int4g128_gemm_prepared
+    assert i(_p(), _p(), _p(), _p(), _p(), M, N, K, None, 0, None) == WORKSPACE
+
+
 def test_binding_rejects_mismatched_weight_sizes(L):
     """The ABI takes raw pointers, so the binding checks tensor sizes against
     N and K before a call (a flat prepared buffer must not be read as rows)."""

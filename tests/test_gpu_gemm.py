@@ -372,6 +372,36 @@ def test_mxfp4_prepared_regstream_down_proj():
     assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
 
 
+# K split across workgroups (few tiles on a long K): ragged N (scalar partial
+# stores), and the full-size narrow layer at a few hundred rows
+@pytest.mark.parametrize("M,N,K", [(100, 1002, 4096), (200, 520, 3072)])
+def test_mxfp4_prepared_tiled_split_ragged(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 6))
+    x8, s = _acts(M, K, (M, K, 6), spread=10.0)
+    say("prepared tiled split", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    again = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(got, again)
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"])
+    assert_gemm_close(got, ref, (M, N, K))
+
+
+@pytest.mark.parametrize("M", [128, 512])
+def test_mxfp4_prepared_tiled_split_down_proj(M):
+    d = synth.down_proj()
+    x8, s = _acts(M, synth.INTERMEDIATE, (7, M))
+    pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
+    say("prepared tiled split down_proj", M)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    g = np.random.default_rng(M + 13)
+    mi = np.concatenate([np.arange(M), g.integers(0, M, 4096), np.full(64, M - 1)])
+    ni = np.concatenate([g.integers(0, d["N"], M), g.integers(0, d["N"], 4096), d["N"] - 1 - np.arange(64)])
+    ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
+    assert_gemm_close(got[mi, ni], ref, M)
+
+
 def test_mxfp4_prepared_tiled_tall():
     # 256-row tiles (at least two 256 x 256 tiles per CU): ragged M and N,
     # sampled outputs including the last row and column
@@ -460,14 +490,14 @@ def test_int4_prepared_ragged(M, N, K):
                         full=True, spread=10.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (40, 65600, 256), (300, 33000, 384),
+@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (20, 65600, 384), (40, 65600, 256), (300, 33000, 384),
                                    (600, 45064, 256)])
 def test_int4_prepared_wide(M, N, K):
     _int4_prepared_case(f"wide {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 9)), M,
                         (M, K, 9), n_samples=8192)
 
 
-@pytest.mark.parametrize("M", [1, 16, 64, 2048])
+@pytest.mark.parametrize("M", [1, 16, 64, 128, 512, 2048])
 def test_int4_prepared_full_size(M):
     _int4_prepared_case(f"I M={M}", synth.int4(), M, (10, M))
 

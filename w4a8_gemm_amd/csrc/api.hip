@@ -100,17 +100,28 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         kind != W4A8_WEIGHT_INT4G128_PREPARED)
         return 0;
     size_t need = 0;
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED) {
+        const bool int4 = kind == W4A8_WEIGHT_INT4G128_PREPARED;
+        auto at = [&](int64_t m) -> size_t {
+            const PreparedRoute r = prepared_route(m, N, K, int4);
+            if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 3), m, N);
+            if (r == PreparedRoute::RegStream) return pdr_workspace_bytes(m, N, K);
+            return K <= kPreparedTiledMaxK ? tiled_workspace_bytes(m, N, K, int4) : 0;
+        };
+        auto keep = [&](size_t b) { if (b > need) need = b; };
+        // every M up to 64; above, the tiled kernel's shape is constant on each
+        // interval (64j, 64j + 64] and its split workspace grows with M there,
+        // so the interval ends and M_max cover it; from 32768 rows on there
+        // are at least 128 tiles and K is not split
+        for (int64_t m = 1; m <= M_max && m <= kDecodeMaxM; ++m) keep(at(m));
+        for (int64_t m = 2 * kDecodeMaxM; m < M_max && m <= 32768; m += kDecodeMaxM) keep(at(m));
+        if (M_max > kDecodeMaxM) keep(at(M_max));
+        return need;
+    }
     const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
     for (int64_t m = 1; m <= top; ++m) {
-        size_t b = 0;
-        if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED) {
-            const PreparedRoute r = prepared_route(m, N, K);
-            if (r == PreparedRoute::Decode) b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 3), m, N);
-            else if (r == PreparedRoute::RegStream) b = pdr_workspace_bytes(m, N, K);
-        } else {
-            const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K) : plan_int4(m, N, K);
-            b = plan_workspace_bytes(p, m, N);
-        }
+        const GemmPlan p = kind == W4A8_WEIGHT_MXFP4 ? plan_mxfp4(m, N, K) : plan_int4(m, N, K);
+        const size_t b = plan_workspace_bytes(p, m, N);
         if (b > need) need = b;
     }
     return need;
@@ -167,11 +178,13 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     // the tiled and register-streamed kernels address activations with 32-bit offsets
-    const PreparedRoute route = prepared_route(M, N, K);
+    const PreparedRoute route = prepared_route(M, N, K, int4);
     if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
     case PreparedRoute::Tiled:
-        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
+        st = check_workspace(tiled_workspace_bytes(M, N, K, int4), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
                                                 as_stream(stream), int4));
     case PreparedRoute::RegStream:
         st = check_workspace(pdr_workspace_bytes(M, N, K), d_ws, ws_bytes);

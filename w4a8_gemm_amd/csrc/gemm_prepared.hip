@@ -100,10 +100,10 @@ __device__ __forceinline__ v4f wmma(v8i a, v8i b, v4f acc, typename WStep<WF>::T
     } else {
         const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
                                                                        kFmtFp8, 0, kUnitScale, 0, kUnitScale);
-        acc[0] = acc[0] + f16_to_f32(sc.x & 0xFFFFu) * t[0];
-        acc[1] = acc[1] + f16_to_f32(sc.x >> 16) * t[1];
-        acc[2] = acc[2] + f16_to_f32(sc.y & 0xFFFFu) * t[2];
-        acc[3] = acc[3] + f16_to_f32(sc.y >> 16) * t[3];
+        acc[0] = __builtin_fmaf(f16_to_f32(sc.x & 0xFFFFu), t[0], acc[0]);
+        acc[1] = __builtin_fmaf(f16_to_f32(sc.x >> 16), t[1], acc[1]);
+        acc[2] = __builtin_fmaf(f16_to_f32(sc.y & 0xFFFFu), t[2], acc[2]);
+        acc[3] = __builtin_fmaf(f16_to_f32(sc.y >> 16), t[3], acc[3]);
         return acc;
     }
 }
@@ -127,10 +127,10 @@ __device__ __forceinline__ v4f i4_split_mma(const I4Split& w, v8i bx, v4f acc, u
                                                              kFmtFp8, 0, kX8, 0, kUnitScale);
     t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.lo, bx, t, kFmtFp4, kFmtFp8, 0, kX2, 0, kUnitScale);
     t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0, kUnitScale);
-    acc[0] = acc[0] + f16_to_f32(sc.x & 0xFFFFu) * t[0];
-    acc[1] = acc[1] + f16_to_f32(sc.x >> 16) * t[1];
-    acc[2] = acc[2] + f16_to_f32(sc.y & 0xFFFFu) * t[2];
-    acc[3] = acc[3] + f16_to_f32(sc.y >> 16) * t[3];
+    acc[0] = __builtin_fmaf(f16_to_f32(sc.x & 0xFFFFu), t[0], acc[0]);
+    acc[1] = __builtin_fmaf(f16_to_f32(sc.x >> 16), t[1], acc[1]);
+    acc[2] = __builtin_fmaf(f16_to_f32(sc.y & 0xFFFFu), t[2], acc[2]);
+    acc[3] = __builtin_fmaf(f16_to_f32(sc.y >> 16), t[3], acc[3]);
     return acc;
 }
 
@@ -665,6 +665,8 @@ struct PfArgs {
     int s_pad, c_pad, tiles16;
     int tiles_m, tiles_n;
     int group_m;                // M tiles per group of the tile order
+    int ks, s_per;              // K splits (steps s_per each, a multiple of 4; ks = 1: none)
+    float* partials;            // ks > 1: fp32 [ks][M][N], token scale not applied
 };
 
 constexpr int kPfThreads = 512;
@@ -706,9 +708,15 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t voff, uint32_
                  ::"v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
-template <int BM, int BN>
+// Stage sizes and the waves' share of the output tile.  MXFP4: NWM x NWN waves
+// over (M, N), each with FN weight and FM activation fragments per step.
+// int4: one wave row (NWM = 1), so that each wave widens only its FN = BN/128
+// weight fragments per step and uses each against FM = BM/16 activation
+// fragments (the widening and the per-step scaling are vector-ALU work that
+// the MXFP4 format does inside the matrix instruction).
+template <int BM, int BN, int WF = 0>
 struct PfShape {
-    static constexpr int NWM = BM >= 256 ? 4 : (BM >= 128 ? 2 : 1);
+    static constexpr int NWM = WF == 1 ? 1 : (BM >= 256 ? 4 : (BM >= 128 ? 2 : 1));
     static constexpr int NWN = 8 / NWM;
     static constexpr int FN = BN / (16 * NWN);
     static constexpr int FM = BM / (16 * NWM);
@@ -884,15 +892,19 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
 }
 
 
-// Output tile of this workgroup: workgroup ids are dealt round-robin over
-// the 8 XCDs, so consecutive tiles go to consecutive ids on one XCD; tiles
-// are numbered in groups of group_m M-tiles so that the workgroups resident
-// on an XCD share weight and activation panels in its L2.
-__device__ __forceinline__ bool pf_tile(const PfArgs& a, int& tm, int& tn) {
-    const int total = a.tiles_m * a.tiles_n;
+// Output tile and K split of this workgroup: workgroup ids are dealt
+// round-robin over the 8 XCDs, so consecutive tiles go to consecutive ids on
+// one XCD; tiles are numbered in groups of group_m M-tiles so that the
+// workgroups resident on an XCD share weight and activation panels in its L2;
+// the K split is the outermost index.
+__device__ __forceinline__ bool pf_tile(const PfArgs& a, int& tm, int& tn, int& split) {
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int total = tiles * a.ks;
     const int per_xcd = (total + 7) >> 3;
-    const int T = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    int T = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (T >= total) return false;
+    split = T / tiles;
+    T -= split * tiles;
     const int gm = a.group_m;
     const int group = T / (gm * a.tiles_n);
     const int first_m = group * gm;
@@ -903,13 +915,97 @@ __device__ __forceinline__ bool pf_tile(const PfArgs& a, int& tm, int& tn) {
     return true;
 }
 
-// lane holds rows n0..n0+3 of column m in every 16x16 tile: out = bf16(s_m * acc)
+// int4 products of one K step from `st` (one wave row): the wave's FN weight
+// fragments are widened to e4m3 and their fp16 row scales converted once, then
+// the FM activation fragments are read one at a time (the next one's LDS read
+// issued before the current one's products) with the copies for step s_nxt
+// spread between the groups.
+template <int BM, int BN, int H>
+__device__ __forceinline__ void pfi_groups(const uint8_t* as, int g, int lane, const v8i (&af)[PfShape<BM, BN, kWI4>::FN],
+                                           const float (&sf)[PfShape<BM, BN, kWI4>::FN][4], v8i bx,
+                                           v4f (&acc)[PfShape<BM, BN, kWI4>::FN][PfShape<BM, BN, kWI4>::FM],
+                                           const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
+    using W = PfShape<BM, BN, kWI4>;
+    if constexpr (H < W::FM) {
+        constexpr int D = W::DMA_PER_STAGE;
+        v8i bn = bx;
+        if constexpr (H + 1 < W::FM) {
+            const int r = 16 * (H + 1) + (lane & 15);
+            bn = act_frag<kWI4>(as + 128 * r, g, (r >> 1) & 7);
+        }
+        pf_issue_range<BM, BN, H * D / W::FM, (H + 1) * D / W::FM>(src, nxt, s_nxt, wave);
+#pragma unroll
+        for (int f = 0; f < W::FN; ++f) {
+            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[f], bx, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+                                                                           kFmtFp8, 0, kUnitScale, 0, kUnitScale);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][H][i] = __builtin_fmaf(sf[f][i], t[i], acc[f][H][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pfi_groups<BM, BN, H + 1>(as, g, lane, af, sf, bn, acc, src, nxt, s_nxt, wave);
+    }
+}
+
 template <int BM, int BN>
-__device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int wn, int wm, int lane,
-                                            const v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM]) {
-    using S = PfShape<BM, BN>;
+__device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, int lane,
+                                            v4f (&acc)[PfShape<BM, BN, kWI4>::FN][PfShape<BM, BN, kWI4>::FM],
+                                            const uint8_t* sbuf, const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt,
+                                            int wave) {
+    using W = PfShape<BM, BN, kWI4>;
+    const int g = lane >> 4;
+    const uint8_t* as = st + W::WBYTES;
+    const uint8_t* wp = st + 1024 * (wn * W::FN) + 16 * lane;
+    uint4 q[W::FN];
+    uint2 sc[W::FN];
+#pragma unroll
+    for (int f = 0; f < W::FN; ++f) {
+        q[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
+        sc[f] = pf_scale<BN, kWI4>(sbuf, wn * W::FN + f, s, lane);
+    }
+    const int r0 = lane & 15;
+    const v8i bx = act_frag<kWI4>(as + 128 * r0, g, (r0 >> 1) & 7);
+    v8i af[W::FN];
+    float sf[W::FN][4];
+#pragma unroll
+    for (int f = 0; f < W::FN; ++f) {
+        af[f] = wfrag<kWI4>(q[f]);
+        sf[f][0] = f16_to_f32(sc[f].x & 0xFFFFu);
+        sf[f][1] = f16_to_f32(sc[f].x >> 16);
+        sf[f][2] = f16_to_f32(sc[f].y & 0xFFFFu);
+        sf[f][3] = f16_to_f32(sc[f].y >> 16);
+    }
+    pfi_groups<BM, BN, 0>(as, g, lane, af, sf, bx, acc, src, nxt, s_nxt, wave);
+}
+
+// lane holds rows n0..n0+3 of column m in every 16x16 tile: out = bf16(s_m * acc)
+template <int BM, int BN, int WF>
+__device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int split, int wn, int wm, int lane,
+                                            const v4f (&acc)[PfShape<BM, BN, WF>::FN][PfShape<BM, BN, WF>::FM]) {
+    using S = PfShape<BM, BN, WF>;
     const int g = lane >> 4;
     const bool vec = (a.N & 3) == 0;
+    if (a.ks > 1) {
+        // this split's fp32 sums; the reduction applies the token scale
+        float* part = a.partials + (int64_t)split * a.M * a.N;
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) {
+            const int m = tm * BM + wm * 16 * S::FM + 16 * h + (lane & 15);
+            if (m >= a.M) continue;
+#pragma unroll
+            for (int f = 0; f < S::FN; ++f) {
+                const int n0 = tn * BN + (wn * S::FN + f) * 16 + 4 * g;
+                if (n0 >= a.N) continue;
+                float* o = part + (int64_t)m * a.N + n0;
+                if (vec) {
+                    *reinterpret_cast<float4*>(o) = make_float4(acc[f][h][0], acc[f][h][1], acc[f][h][2], acc[f][h][3]);
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (n0 + r < a.N) o[r] = acc[f][h][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int h = 0; h < S::FM; ++h) {
         const int m = tm * BM + wm * 16 * S::FM + 16 * h + (lane & 15);
@@ -941,41 +1037,46 @@ __device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int
 // chunk that starts at step u = s + NS - 1 (if any), then compute, with the
 // copies for step u into the free stage issued between the products.  In
 // issue order the copies of step u are: [e8m0 chunk u/4 if u % 4 == 0 and
-// u < steps] [weights, activations (of step min(u, steps - 1))].
+// u < s1] [weights, activations (of step min(u, s1 - 1))], where [s0, s1) is
+// the workgroup's range of K steps (all of K, or one split of it: fp32
+// partials, added and scaled by the reduction kernel).
 template <int BM, int BN, int NS, int WF>
 __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     using S = PfShape<BM, BN>;
+    using W = PfShape<BM, BN, WF>;
     using SC = PfScales<BN, WF>;
     static_assert(NS >= 3 && NS <= 5, "ring depth");
     constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
     constexpr int LDS = kPfBase + NS * S::STAGE + 2 * SC::BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
-    int tm, tn;
-    if (!pf_tile(a, tm, tn)) return;
+    int tm, tn, split;
+    if (!pf_tile(a, tm, tn, split)) return;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wn = wave % S::NWN, wm = wave / S::NWN;
+    const int wn = wave % W::NWN, wm = wave / W::NWN;
 
-    v4f acc[S::FN][S::FM];
+    v4f acc[W::FN][W::FM];
 #pragma unroll
-    for (int f = 0; f < S::FN; ++f)
+    for (int f = 0; f < W::FN; ++f)
 #pragma unroll
-        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < W::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int steps = a.K >> 7;
+    // this workgroup's K steps [s0, s1) (s0 a multiple of 4: whole scale chunks)
+    const int s0 = split * a.s_per, s1 = min(a.K >> 7, s0 + a.s_per);
     uint8_t* const base = lds + kPfBase;
     uint8_t* const sbase = base + NS * S::STAGE;
     PfSrc<BM, BN> src;
     pf_sources<BM, BN, WF>(a, tm, tn, wave, lane, src);
-    // prologue: steps 0 .. NS - 2 (repeating the last step when K is shorter)
+    // prologue: steps s0 .. s0 + NS - 2 (repeating the last step when the range is shorter)
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) {
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
-        pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
+    for (int i = 0; i < NS - 1; ++i) {
+        const int u = s0 + i;
+        if ((u & 3) == 0 && u < s1) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
+        pf_issue<BM, BN>(src, base + i * S::STAGE, min(u, s1 - 1), wave);
     }
     int cur = 0, nxt = (NS - 1) * S::STAGE;   // stage offsets of steps s and s + NS - 1
-    for (int s = 0; s < steps; ++s) {
+    for (int s = s0; s < s1; ++s) {
         // opaque to the optimiser: stage addresses are formed per step from a
         // few lane bases and immediate offsets instead of being unrolled and
         // hoisted into dozens of live registers
@@ -984,25 +1085,29 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         // include at most one e8m0 chunk (NS - 2 <= 3 consecutive steps)
         bool chunk_ahead = false;
 #pragma unroll
-        for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < steps;
+        for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < s1;
         if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
         else wait_vmcnt<(NS - 2) * D>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");     // no LDS access moves across the barrier
         const int u = s + NS - 1;
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
+        if ((u & 3) == 0 && u < s1) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
         // copies for step u; in the last NS - 1 steps they repeat the last step
         // into the free stage, which is never read again (no branch in the
         // product sequence)
-        pf_compute<BM, BN, WF>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
-                           min(u, steps - 1), wave);
+        if constexpr (WF == kWI4)
+            pfi_compute<BM, BN>(base + cur, s, wn, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
+                                min(u, s1 - 1), wave);
+        else
+            pf_compute<BM, BN, WF>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src,
+                                   base + nxt, min(u, s1 - 1), wave);
         cur = cur == (NS - 1) * S::STAGE ? 0 : cur + S::STAGE;
         nxt = nxt == (NS - 1) * S::STAGE ? 0 : nxt + S::STAGE;
     }
     // the repeated copies of the last steps may still be landing: drain them
     // before the workgroup's LDS is released
     wait_vmcnt<0>();
-    pf_epilogue<BM, BN>(a, tm, tn, wn, wm, lane, acc);
+    pf_epilogue<BM, BN, WF>(a, tm, tn, split, wn, wm, lane, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1074,7 +1179,7 @@ __device__ __forceinline__ void pfp_groups(const PfFrag<BM, BN, WF>& F, v4f (&ac
 }
 
 template <int BM, int BN, int NS, int WF>
-__device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN, WF>& Fc, PfFrag<BM, BN, WF>& Fn,
+__device__ __forceinline__ void pfp_iter(int s, int s_end, const PfFrag<BM, BN, WF>& Fc, PfFrag<BM, BN, WF>& Fn,
                                          v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                          const PfSrc<BM, BN>& src, uint8_t* base, uint8_t* sbase, int& cur,
                                          int wn, int wm, int lane, int wave) {
@@ -1088,8 +1193,8 @@ __device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN, 
     const int nx = cur == LAST ? 0 : cur + S::STAGE;       // stage of step s + 1
     const int tg = cur == 0 ? LAST : cur - S::STAGE;       // stage (s - 1) % NS: copies for step u
     const int u = s + NS - 1;
-    if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
-    pfp_groups<BM, BN, WF, 0, H>(Fc, acc, src, base + tg, min(u, steps - 1), wave);
+    if ((u & 3) == 0 && u < s_end) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
+    pfp_groups<BM, BN, WF, 0, H>(Fc, acc, src, base + tg, min(u, s_end - 1), wave);
     // pin the first half's products before the barrier (they touch no memory,
     // so nothing else keeps them there): the matrix pipe works through them
     // while the wave waits
@@ -1101,7 +1206,7 @@ __device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN, 
     // most one e8m0 chunk among them (NS - 2 <= 3 consecutive steps)
     bool chunk_ahead = false;
 #pragma unroll
-    for (int v = 2; v <= NS - 1; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < steps;
+    for (int v = 2; v <= NS - 1; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < s_end;
     if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
     else wait_vmcnt<(NS - 2) * D>();
     wait_lgkm0();
@@ -1109,7 +1214,7 @@ __device__ __forceinline__ void pfp_iter(int s, int steps, const PfFrag<BM, BN, 
     asm volatile("" ::: "memory");     // no LDS access moves across the barrier
     pf_read<BM, BN, WF>(base + nx, sbase + (((s + 1) >> 2) & 1) * SC::BYTES, s + 1, wn, wm, lane, Fn);
     __builtin_amdgcn_sched_barrier(0);
-    pfp_groups<BM, BN, WF, H, S::FN>(Fc, acc, src, base + tg, min(u, steps - 1), wave);
+    pfp_groups<BM, BN, WF, H, S::FN>(Fc, acc, src, base + tg, min(u, s_end - 1), wave);
     cur = nx;
 }
 
@@ -1119,12 +1224,13 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     using SC = PfScales<BN, WF>;
     static_assert(NS >= 3 && NS <= 5, "ring depth");
     static_assert(BM <= 128, "two fragment sets fit in registers for short tiles only");
+    static_assert(WF == kWMx, "int4 weights take pf_kernel at every tile height");
     constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
     constexpr int LDS = kPfBase + NS * S::STAGE + 2 * SC::BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
-    int tm, tn;
-    if (!pf_tile(a, tm, tn)) return;
+    int tm, tn, split;
+    if (!pf_tile(a, tm, tn, split)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wn = wave % S::NWN, wm = wave / S::NWN;
 
@@ -1134,40 +1240,42 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
 #pragma unroll
         for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int steps = a.K >> 7;
+    // this workgroup's K steps [s0, s1) (s0 a multiple of 4: whole scale chunks)
+    const int s0 = split * a.s_per, s1 = min(a.K >> 7, s0 + a.s_per);
     uint8_t* const base = lds + kPfBase;
     uint8_t* const sbase = base + NS * S::STAGE;
     PfSrc<BM, BN> src;
     pf_sources<BM, BN, WF>(a, tm, tn, wave, lane, src);
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) {
-        if ((u & 3) == 0 && u < steps) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
-        pf_issue<BM, BN>(src, base + u * S::STAGE, min(u, steps - 1), wave);
+    for (int i = 0; i < NS - 1; ++i) {
+        const int u = s0 + i;
+        if ((u & 3) == 0 && u < s1) pf_issue_scales<BM, BN, WF>(src, sbase + ((u >> 2) & 1) * SC::BYTES, u >> 2, wave);
+        pf_issue<BM, BN>(src, base + i * S::STAGE, min(u, s1 - 1), wave);
     }
-    // step 0's copies (steps 1 .. NS - 2 may stay in flight), then its fragments
+    // step s0's copies (steps s0 + 1 .. s0 + NS - 2 may stay in flight), then its fragments
     bool chunk_ahead = false;
 #pragma unroll
-    for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= (v & 3) == 0 && v < steps;
+    for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= ((s0 + v) & 3) == 0 && s0 + v < s1;
     if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
     else wait_vmcnt<(NS - 2) * D>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     PfFrag<BM, BN, WF> F0, F1;
-    pf_read<BM, BN, WF>(base, sbase, 0, wn, wm, lane, F0);
+    pf_read<BM, BN, WF>(base, sbase + ((s0 >> 2) & 1) * SC::BYTES, s0, wn, wm, lane, F0);
     int cur = 0;
-    for (int s = 0; s < steps; s += 2) {
-        pfp_iter<BM, BN, NS, WF>(s, steps, F0, F1, acc, src, base, sbase, cur, wn, wm, lane, wave);
-        if (s + 1 < steps) pfp_iter<BM, BN, NS, WF>(s + 1, steps, F1, F0, acc, src, base, sbase, cur, wn, wm, lane, wave);
+    for (int s = s0; s < s1; s += 2) {
+        pfp_iter<BM, BN, NS, WF>(s, s1, F0, F1, acc, src, base, sbase, cur, wn, wm, lane, wave);
+        if (s + 1 < s1) pfp_iter<BM, BN, NS, WF>(s + 1, s1, F1, F0, acc, src, base, sbase, cur, wn, wm, lane, wave);
     }
     // the repeated copies of the last steps may still be landing: drain them
     // before the workgroup's LDS is released
     wait_vmcnt<0>();
-    pf_epilogue<BM, BN>(a, tm, tn, wn, wm, lane, acc);
+    pf_epilogue<BM, BN, kWMx>(a, tm, tn, split, wn, wm, lane, acc);
 }
 
 template <int BM, int BN, int NS, int WF>
 hipError_t launch_pfp(const PfArgs& a, hipStream_t stream) {
-    const int total = a.tiles_m * a.tiles_n;
+    const int total = a.tiles_m * a.tiles_n * a.ks;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((pfp_kernel<BM, BN, NS, WF>), dim3(grid), dim3(kPfThreads), 0, stream, a);
     return hipGetLastError();
@@ -1175,7 +1283,7 @@ hipError_t launch_pfp(const PfArgs& a, hipStream_t stream) {
 
 template <int BM, int BN, int NS, int WF>
 hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
-    const int total = a.tiles_m * a.tiles_n;
+    const int total = a.tiles_m * a.tiles_n * a.ks;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL((pf_kernel<BM, BN, NS, WF>), dim3(grid), dim3(kPfThreads), 0, stream, a);
     return hipGetLastError();
@@ -1286,9 +1394,71 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M) {
     return act > red ? act : red;
 }
 
+// Tile shape and K split of the tiled kernels.  Tile height by M (64 / 128 /
+// 256), the ring as deep as LDS allows for it (5 / 4 / 3 stages); tile width
+// 256, or 128 when 256-wide tiles would leave most CUs idle (decode-sized M
+// on narrow layers).  With fewer than 128 tiles K is split across workgroups
+// (at most one per CU, whole 4-step scale chunks, at least 8 steps each):
+// narrow layers at a few hundred rows otherwise run a handful of workgroups
+// through all of K (down_proj M = 128: 67 us unsplit, 28 us split).
+// Above 128 rows, MXFP4 takes 256-row tiles when their rounds of workgroups
+// over the 256 CUs cost no more, a 256-row tile counted as 1.8 128-row ones
+// (measured: gate_up M = 200 / 2048 / 4096 and down_proj M = 2048 favour 256
+// rows, gate_up M = 512 and down_proj M = 4096 favour 128, M = 1024 even).
+// int4 keeps 256-row tiles down to 128 of them: there each wave widens its
+// weight fragments once for 16 activation fragments instead of 8, which
+// outweighs idle CUs (down_proj-shaped M = 2048, 160 tiles: 290 us vs 399 us
+// with 128-row tiles; M = 256, 20 tiles: 278 vs 129 us).
+struct TiledShape {
+    int bm, bn, tiles_m, tiles_n, ks, s_per;
+};
+static void tiled_grid(int64_t M, int64_t N, int bm, TiledShape& t) {
+    t.bm = bm;
+    t.tiles_m = (int)((M + bm - 1) / bm);
+    const int64_t wide = (int64_t)t.tiles_m * ((N + 255) / 256);
+    t.bn = wide < 64 ? 128 : 256;
+    t.tiles_n = (int)((N + t.bn - 1) / t.bn);
+}
+static int64_t tiled_rounds(const TiledShape& t) {
+    const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n;
+    return tiles < 128 ? 1 : (tiles + 255) / 256;      // few tiles: K split fills one round
+}
+static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
+    TiledShape t{};
+    tiled_grid(M, N, M <= 64 ? 64 : 128, t);
+    if (M > 128) {
+        TiledShape t256{};
+        tiled_grid(M, N, 256, t256);
+        const bool take = int4 ? (int64_t)t256.tiles_m * t256.tiles_n >= 128
+                               : 9 * tiled_rounds(t256) <= 5 * tiled_rounds(t);
+        if (take) t = t256;
+    }
+    const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n, steps = K / 128;
+    t.ks = 1;
+    t.s_per = (int)steps;
+    if (tiles < 128 && steps >= 16) {
+        int64_t k = 256 / tiles;                        // at most one round of workgroups
+        int64_t per = (steps + k - 1) / k;
+        per = (per + 3) / 4 * 4;
+        if (per < 8) per = 8;
+        k = (steps + per - 1) / per;
+        if (k > 1) {
+            t.ks = (int)k;
+            t.s_per = (int)per;
+        }
+    }
+    return t;
+}
+
+size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4) {
+    const TiledShape t = tiled_shape(M, N, K, int4);
+    if (t.ks <= 1) return 0;
+    return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
+}
+
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t stream, bool int4) {
+                                 void* ws, hipStream_t stream, bool int4) {
     PfArgs a{};
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -1296,34 +1466,36 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
     a.group_m = 8;
-    // tile height by M, the ring as deep as LDS allows for it (5 / 4 / 3
-    // stages); tile width 256, or 128 when 256-wide tiles would leave most
-    // CUs idle (decode-sized M on narrow layers).  Large M keeps 128-row
-    // (pipelined) tiles while 256-row tiles would give fewer than two per CU
-    // (measured, down_proj M = 4096: 359 us vs 391 us with 256-row tiles;
-    // gate_up M = 4096, 8.5 tiles per CU: 663 us vs 716 us the other way)
-    int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
-    if (bm == 256 && ((M + 255) / 256) * ((N + 255) / 256) < 512) bm = 128;
-    a.tiles_m = (int)((M + bm - 1) / bm);
-    const int64_t wide = (int64_t)a.tiles_m * ((N + 255) / 256);
-    const int bn = wide < 64 ? 128 : 256;
-    a.tiles_n = (int)((N + bn - 1) / bn);
-    if ((int64_t)a.tiles_m * a.tiles_n > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
-    // (64-row tiles are wide: narrow layers take the register-streamed kernel
-    // at M <= 64; 256-row tiles come only with at least 512 256-wide tiles)
-    if (int4) {
-        if (bm == 64) return launch_pfp<64, 256, 5, kWI4>(a, stream);
-        if (bm == 128)
-            return bn == 128 ? launch_pfp<128, 128, 4, kWI4>(a, stream) : launch_pfp<128, 256, 4, kWI4>(a, stream);
-        return launch_pf<256, 256, 3, kWI4>(a, stream);
+    const TiledShape t = tiled_shape(M, N, K, int4);
+    const int bm = t.bm, bn = t.bn;
+    a.tiles_m = t.tiles_m;
+    a.tiles_n = t.tiles_n;
+    a.ks = t.ks;
+    a.s_per = t.s_per;
+    if ((int64_t)a.tiles_m * a.tiles_n * a.ks > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    if (a.ks > 1) {
+        if (!ws) return hipErrorInvalidValue;
+        a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles16));
     }
-    if (bm == 64) return launch_pfp<64, 256, 5, kWMx>(a, stream);
-    if (bm == 128)
-        return bn == 128 ? launch_pfp<128, 128, 4, kWMx>(a, stream) : launch_pfp<128, 256, 4, kWMx>(a, stream);
-    return launch_pf<256, 256, 3, kWMx>(a, stream);
+    hipError_t e;
+    // (64-row tiles are wide: narrow layers take the register-streamed kernel
+    // at M <= 64; 256-row tiles come only with enough of them)
+    if (int4) {
+        if (bm == 64) e = launch_pf<64, 256, 5, kWI4>(a, stream);
+        else if (bm == 128)
+            e = bn == 128 ? launch_pf<128, 128, 4, kWI4>(a, stream) : launch_pf<128, 256, 4, kWI4>(a, stream);
+        else e = launch_pf<256, 256, 3, kWI4>(a, stream);
+    } else {
+        if (bm == 64) e = launch_pfp<64, 256, 5, kWMx>(a, stream);
+        else if (bm == 128)
+            e = bn == 128 ? launch_pfp<128, 128, 4, kWMx>(a, stream) : launch_pfp<128, 256, 4, kWMx>(a, stream);
+        else e = launch_pf<256, 256, 3, kWMx>(a, stream);
+    }
+    if (e != hipSuccess || a.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
-PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K) {
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     (void)K;
     // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
     // workgroups (three quarters of the CUs idle in the tiled kernel)
@@ -1336,6 +1508,10 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K) {
     // (down_proj M = 64: 27 us vs 52 us tiled)
     if (M <= (narrow ? kPreparedDecodeMaxM : 12)) return PreparedRoute::Decode;
     if (M <= 64 && narrow) return PreparedRoute::RegStream;
+    // int4 on wide layers: the tiled kernel's 64-row tiles widen each weight
+    // fragment for only four activation fragments (gate_up M = 16 / 32:
+    // 28.9 / 33.4 us register-streamed, 49 / 50 us tiled; M = 64: 63 vs 52 us)
+    if (int4 && M <= 32) return PreparedRoute::RegStream;
     return PreparedRoute::Tiled;
 }
 

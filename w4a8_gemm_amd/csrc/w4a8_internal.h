@@ -125,17 +125,19 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
                                   int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
 // Which kernel serves a GEMM on prepared weights: the split-K decode kernel
 // (M <= 12; M <= 32 on narrow layers), the register-streamed kernel (up to
-// M = 64 on layers too narrow for the tiled kernel to fill the CUs: K split
-// across workgroups), or the tiled kernel.
+// M = 64 on layers too narrow for the tiled kernel to fill the CUs, K split
+// across workgroups; int4 weights also up to M = 32 on wide layers), or the
+// tiled kernel (K split across workgroups when its tiles are few).
 enum class PreparedRoute { Decode, RegStream, Tiled };
-PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K);
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
+size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
 size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                                      uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
                                      hipStream_t stream, bool int4);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t stream, bool int4);
+                                 void* ws, hipStream_t stream, bool int4);
 // int4 g128 in fragment order (same weight geometry as MXFP4; row scales
 // [tile][chunk][step][16] fp16)
 void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
