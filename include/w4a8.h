@@ -194,11 +194,13 @@ w4a8_status w4a8_mxfp4_gemm(
  *     M >= 1.  Small M runs the split-K decode kernel (M <= 12; M <= 32 on
  *     narrow layers: fewer than 64 column tiles of 256); M <= 64 on narrow
  *     layers a register-streamed kernel with K split across workgroups;
- *     otherwise the tiled kernel (64/128/256 x 256 output tiles).  A workspace
- *     sized with W4A8_WEIGHT_MXFP4_PREPARED for the largest M covers every
- *     case (the tiled kernel needs none).  Above the split-K decode kernel's
- *     range K must be < 2^24 (UNSUPPORTED_SHAPE): those kernels address a
- *     256-row activation block with 32-bit offsets.
+ *     otherwise the tiled kernel (64/128/256 x 128/256 output tiles), which
+ *     also splits K across workgroups when it has fewer than 128 tiles (fp32
+ *     partials in the workspace, then a reduction kernel).  A workspace sized
+ *     with W4A8_WEIGHT_MXFP4_PREPARED for the largest M covers every case
+ *     (many tiles need none).  Above the split-K decode kernel's range K must
+ *     be < 2^24 (UNSUPPORTED_SHAPE): those kernels address a 256-row
+ *     activation block with 32-bit offsets.
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
  * WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
@@ -247,8 +249,8 @@ w4a8_status w4a8_int4g128_gemm(
  * 128-wide K step s, tiles major; lane L = n + 16g holds 16 bytes of codes of
  * row 16t+n: words 16s+4g .. 16s+4g+3 of the checkpoint layout (k = 128s+32g
  * .. +31, nibble j of a word is k = 8i + j).  Row scales: fp16 [tile][4-step
- * chunk][step][16 rows].  Rows are padded to 16
- * and steps to a multiple of 4 (code 8, scale 0).  The result equals
+ * chunk][step][16 rows].  Rows are padded to 16 and steps to a multiple of
+ * 4 (code 8, scale 0).  The result equals
  * w4a8_int4g128_gemm's in value (fp32 accumulation; summation order may
  * differ).
  *   w4a8_int4g128_prepared_bytes: sizes of the two buffers (host).
@@ -257,8 +259,9 @@ w4a8_status w4a8_int4g128_gemm(
  *     -> d_w_prepared (16-byte aligned), d_s_prepared (8-byte aligned).
  *     Synchronizes `stream` (the check result is read back).
  *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
- *     kernel choice and workspace of w4a8_mxfp4_gemm_prepared (size it with
- *     W4A8_WEIGHT_INT4G128_PREPARED).
+ *     kernels of w4a8_mxfp4_gemm_prepared (the register-streamed one also for
+ *     M <= 32 on wide layers, 256-row tiles from 128 of them on) and its
+ *     workspace rules (size it with W4A8_WEIGHT_INT4G128_PREPARED).
  * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, ASYMMETRIC (prepare), HIP. */
 w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
