@@ -374,7 +374,7 @@ def test_mxfp4_prepared_regstream_down_proj():
 
 # K split across workgroups (few tiles on a long K): ragged N (scalar partial
 # stores), and the full-size narrow layer at a few hundred rows
-@pytest.mark.parametrize("M,N,K", [(100, 1002, 4096), (200, 520, 3072)])
+@pytest.mark.parametrize("M,N,K", [(100, 1002, 4096), (200, 520, 3072), (40, 20000, 4096)])
 def test_mxfp4_prepared_tiled_split_ragged(M, N, K):
     w = synth.mxfp4_random(N, K, seed=(M, N, K, 6))
     x8, s = _acts(M, K, (M, K, 6), spread=10.0)
@@ -481,7 +481,7 @@ def _int4_prepared_case(name, q, M, seed, full=False, n_samples=4096, spread=1.0
 INT4_PREPARED = [(1, 64, 128), (3, 136, 1152), (17, 520, 1024), (32, 1000, 4096),
                  (33, 16, 1152), (48, 1000, 4096), (64, 200, 1024),
                  (65, 264, 384), (100, 1000, 1152), (129, 512, 640), (256, 1032, 2048),
-                 (513, 600, 768)]
+                 (513, 600, 768), (48, 20000, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", INT4_PREPARED)

@@ -1416,7 +1416,9 @@ static void tiled_grid(int64_t M, int64_t N, int bm, TiledShape& t) {
     t.bm = bm;
     t.tiles_m = (int)((M + bm - 1) / bm);
     const int64_t wide = (int64_t)t.tiles_m * ((N + 255) / 256);
-    t.bn = wide < 64 ? 128 : 256;
+    // 64-row tiles come only 256 wide (the router sends narrow layers at
+    // M <= 64 to other kernels; few of them are split in K instead)
+    t.bn = bm == 64 || wide >= 64 ? 256 : 128;
     t.tiles_n = (int)((N + t.bn - 1) / t.bn);
 }
 static int64_t tiled_rounds(const TiledShape& t) {
@@ -1477,19 +1479,21 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
         if (!ws) return hipErrorInvalidValue;
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles16));
     }
+    // one kernel per (height, width) that tiled_shape can produce; anything
+    // else is refused rather than run with a grid the kernel does not assume
     hipError_t e;
-    // (64-row tiles are wide: narrow layers take the register-streamed kernel
-    // at M <= 64; 256-row tiles come only with enough of them)
     if (int4) {
-        if (bm == 64) e = launch_pf<64, 256, 5, kWI4>(a, stream);
-        else if (bm == 128)
-            e = bn == 128 ? launch_pf<128, 128, 4, kWI4>(a, stream) : launch_pf<128, 256, 4, kWI4>(a, stream);
-        else e = launch_pf<256, 256, 3, kWI4>(a, stream);
+        if (bm == 64 && bn == 256) e = launch_pf<64, 256, 5, kWI4>(a, stream);
+        else if (bm == 128 && bn == 128) e = launch_pf<128, 128, 4, kWI4>(a, stream);
+        else if (bm == 128 && bn == 256) e = launch_pf<128, 256, 4, kWI4>(a, stream);
+        else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWI4>(a, stream);
+        else return hipErrorInvalidValue;
     } else {
-        if (bm == 64) e = launch_pfp<64, 256, 5, kWMx>(a, stream);
-        else if (bm == 128)
-            e = bn == 128 ? launch_pfp<128, 128, 4, kWMx>(a, stream) : launch_pfp<128, 256, 4, kWMx>(a, stream);
-        else e = launch_pf<256, 256, 3, kWMx>(a, stream);
+        if (bm == 64 && bn == 256) e = launch_pfp<64, 256, 5, kWMx>(a, stream);
+        else if (bm == 128 && bn == 128) e = launch_pfp<128, 128, 4, kWMx>(a, stream);
+        else if (bm == 128 && bn == 256) e = launch_pfp<128, 256, 4, kWMx>(a, stream);
+        else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWMx>(a, stream);
+        else return hipErrorInvalidValue;
     }
     if (e != hipSuccess || a.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
