@@ -192,11 +192,10 @@ w4a8_status w4a8_mxfp4_gemm(
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
  *     M >= 1.  Small M runs the split-K decode kernel (M <= 12; M <= 32 on
- *     narrow layers: fewer than 64 column tiles of 256); M <= 64 on narrow
- *     layers a register-streamed kernel with K split across workgroups;
- *     otherwise the tiled kernel (64/128/256 x 128/256 output tiles), which
- *     also splits K across workgroups when it has fewer than 128 tiles (fp32
- *     partials in the workspace, then a reduction kernel).  A workspace sized
+ *     narrow layers: fewer than 64 column tiles of 256); larger M the tiled
+ *     kernel (64/128/256 x 128/256 output tiles), which splits K across
+ *     workgroups when it has fewer than 128 tiles (fp32 partials in the
+ *     workspace, then a reduction kernel).  A workspace sized
  *     with W4A8_WEIGHT_MXFP4_PREPARED for the largest M covers every case
  *     (many tiles need none).  Above the split-K decode kernel's range K must
  *     be < 2^24 (UNSUPPORTED_SHAPE): those kernels address a 256-row
@@ -259,9 +258,10 @@ w4a8_status w4a8_int4g128_gemm(
  *     -> d_w_prepared (16-byte aligned), d_s_prepared (8-byte aligned).
  *     Synchronizes `stream` (the check result is read back).
  *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
- *     kernels of w4a8_mxfp4_gemm_prepared (the register-streamed one also for
- *     M <= 32 on wide layers, 256-row tiles from 128 of them on) and its
- *     workspace rules (size it with W4A8_WEIGHT_INT4G128_PREPARED).
+ *     kernels of w4a8_mxfp4_gemm_prepared (with a register-streamed kernel,
+ *     K split across workgroups, for 12 < M <= 32 on wide layers, and 256-row
+ *     tiles from 128 of them on) and its workspace rules (size it with
+ *     W4A8_WEIGHT_INT4G128_PREPARED).
  * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, ASYMMETRIC (prepare), HIP. */
 w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);

@@ -339,14 +339,14 @@ def test_mxfp4_prepared_tiled_wide(M, N, K):
     assert (np.abs(got[mi, ni] - ref) <= slack).all()
 
 
-# register-streamed band: 33 <= M <= 64 on layers too narrow for the tiled
-# kernel, K split across workgroups (fp32 partials + reduction) when long
+# narrow layers at 33 <= M <= 64: 64-row tiles, K split across workgroups
+# (fp32 partials + reduction) when long
 @pytest.mark.parametrize("M,N,K", [(33, 16, 1152), (64, 200, 1024), (40, 2000, 2048), (48, 1000, 4096),
                                    (57, 301, 3200)])
-def test_mxfp4_prepared_regstream(M, N, K):
+def test_mxfp4_prepared_narrow_mid(M, N, K):
     w = synth.mxfp4_random(N, K, seed=(M, N, K, 4))
     x8, s = _acts(M, K, (M, K, 4), spread=10.0)
-    say("prepared regstream", (M, N, K))
+    say("prepared narrow mid", (M, N, K))
     pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
     dx, ds = dev_u8(x8), dev_f32(s)
     got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
@@ -358,12 +358,12 @@ def test_mxfp4_prepared_regstream(M, N, K):
     assert (np.abs(got - ref) <= slack).all()
 
 
-def test_mxfp4_prepared_regstream_down_proj():
+def test_mxfp4_prepared_narrow_down_proj_m64():
     d = synth.down_proj()
     M = 64
     x8, s = _acts(M, synth.INTERMEDIATE, (5, M))
     pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
-    say("prepared regstream down_proj", M)
+    say("prepared narrow down_proj", M)
     got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
     g = np.random.default_rng(6)
     mi = np.concatenate([np.arange(M), g.integers(0, M, 4096)])
@@ -490,8 +490,10 @@ def test_int4_prepared_ragged(M, N, K):
                         full=True, spread=10.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (20, 65600, 384), (40, 65600, 256), (300, 33000, 384),
-                                   (600, 45064, 256)])
+# wide layers: split-K decode (M <= 12), register-streamed (12 < M <= 32),
+# tiled (64/128/256-row tiles)
+@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (20, 65600, 384), (32, 34816, 5120), (40, 65600, 256),
+                                   (300, 33000, 384), (600, 45064, 256)])
 def test_int4_prepared_wide(M, N, K):
     _int4_prepared_case(f"wide {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 9)), M,
                         (M, K, 9), n_samples=8192)

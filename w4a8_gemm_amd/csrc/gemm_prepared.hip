@@ -458,7 +458,8 @@ hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode band with register-streamed weights (16 < M <= 64 and narrow layers)
+// Decode band with register-streamed weights (int4 weights, 12 < M <= 32 on
+// wide layers)
 //
 // A workgroup of WW waves owns WW 16-row weight tiles, one per wave, and a
 // range of K steps (the whole K, or one of ks splits).  Each wave streams its
@@ -1507,11 +1508,11 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow): on wide layers the split-K decode kernel wins up to M = 12
     // (M = 12: 23.8 us; at four weight tiles per workgroup, M = 15: 26.5 us,
-    // against about 25 us tiled for any M <= 32); on narrow ones up to M = 32,
-    // then the register-streamed kernel with K split across workgroups
-    // (down_proj M = 64: 27 us vs 52 us tiled)
+    // against about 25 us tiled for any M <= 32); on narrow ones up to M = 32
+    // (even with the tiled kernel split in K: M = 16 / 32 18.4 / 21.1 us vs
+    // 18.8 / 20.9), then the tiled kernel split in K (M = 33 / 64: 21.0 /
+    // 23.8 us vs 25.9 / 28.4 register-streamed; int4 27.1 / 30.4 vs 37.5 / 39.0)
     if (M <= (narrow ? kPreparedDecodeMaxM : 12)) return PreparedRoute::Decode;
-    if (M <= 64 && narrow) return PreparedRoute::RegStream;
     // int4 on wide layers: the tiled kernel's 64-row tiles widen each weight
     // fragment for only four activation fragments (gate_up M = 16 / 32:
     // 28.9 / 33.4 us register-streamed, 49 / 50 us tiled; M = 64: 63 vs 52 us)
@@ -1519,7 +1520,7 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     return PreparedRoute::Tiled;
 }
 
-// Register-streamed decode: MT = ceil(M / 16) in {1, 2, 4}, eight waves per
+// Register-streamed decode: MT = ceil(M / 16) in {1, 2}, eight waves per
 // workgroup, weights prefetched eight steps ahead; K split across
 // workgroups (fp32 partials + reduction) when the tile groups alone would
 // leave CUs idle.  Returns the split count through *ks_out (workspace:
@@ -1561,13 +1562,9 @@ hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const u
         if (!ws) return hipErrorInvalidValue;
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles));
     }
-    hipError_t e;
-    if (int4)
-        e = M <= 16 ? launch_pdr<1, 8, 8, kWI4>(a, stream)
-            : M <= 32 ? launch_pdr<2, 8, 8, kWI4>(a, stream) : launch_pdr<4, 8, 8, kWI4>(a, stream);
-    else
-        e = M <= 16 ? launch_pdr<1, 8, 8, kWMx>(a, stream)
-            : M <= 32 ? launch_pdr<2, 8, 8, kWMx>(a, stream) : launch_pdr<4, 8, 8, kWMx>(a, stream);
+    // served only for int4 weights on wide layers (prepared_route)
+    if (!int4 || M > 32) return hipErrorInvalidValue;
+    const hipError_t e = M <= 16 ? launch_pdr<1, 8, 8, kWI4>(a, stream) : launch_pdr<2, 8, 8, kWI4>(a, stream);
     if (e != hipSuccess || a.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
