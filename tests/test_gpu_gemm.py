@@ -403,9 +403,10 @@ def test_mxfp4_prepared_tiled_split_down_proj(M):
 
 
 def test_mxfp4_prepared_tiled_tall():
-    # 256-row tiles (at least two 256 x 256 tiles per CU): ragged M and N,
+    # 256-row tiles (one round of 137 of them beats two rounds of 128-row
+    # tiles): ragged M, an N that is not a multiple of 4 (scalar stores),
     # sampled outputs including the last row and column
-    M, N, K = 600, 45060, 256
+    M, N, K = 200, 34818, 384
     w = synth.mxfp4_random(N, K, seed=(M, N, K, 5))
     x8, s = _acts(M, K, (M, K, 5), spread=10.0)
     say("prepared tiled tall", (M, N, K))

@@ -751,6 +751,20 @@ __device__ __forceinline__ typename WStep<WF>::T pf_scale(const uint8_t* sbuf, i
     }
 }
 
+// the same, split into the LDS read (MXFP4: the whole chunk dword) and the
+// selection of step s's byte at the point of use, so that a read issued late
+// in a burst does not hold up products that do not need it
+template <int BN, int WF>
+__device__ __forceinline__ typename WStep<WF>::T pf_scale_raw(const uint8_t* sbuf, int b, int s, int lane) {
+    if constexpr (WF == kWMx) return reinterpret_cast<const uint32_t*>(sbuf)[64 * b + lane];
+    else return pf_scale<BN, WF>(sbuf, b, s, lane);
+}
+template <int WF>
+__device__ __forceinline__ typename WStep<WF>::T pf_scale_use(typename WStep<WF>::T raw, int s) {
+    if constexpr (WF == kWMx) return raw >> (8 * (s & 3));
+    else return raw;
+}
+
 // Per-workgroup copy sources: one buffer descriptor per operand based at the
 // workgroup's tile, per-lane offsets that stay fixed over the K steps (the
 // step advance goes into the scalar offset).
@@ -828,6 +842,14 @@ __device__ __forceinline__ void pf_issue(const PfSrc<BM, BN>& src, uint8_t* stag
     pf_issue_range<BM, BN, 0, PfShape<BM, BN>::DMA_PER_STAGE>(src, stage, s, wave);
 }
 
+// The epilogue's kernel arguments, consumed here so that their scalar loads
+// complete before the main loop: an outstanding scalar load makes the LDS
+// counter unordered, and the loop's first LDS wait would then be a full
+// lgkmcnt(0) on every step instead of a wait for the reads it needs.
+__device__ __forceinline__ void pf_args_ready(const PfArgs& a) {
+    asm volatile("" ::"s"(a.xs), "s"(a.out), "s"(a.partials), "s"(a.M), "s"(a.N), "s"(a.ks));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima)
@@ -847,22 +869,26 @@ __device__ __forceinline__ void pf_copies_at(const PfSrc<BM, BN>& src, uint8_t* 
 
 template <int BM, int BN, int WF, int F>
 __device__ __forceinline__ void pf_group(const uint8_t* wp, const uint8_t* sbuf, int s, int wn, int lane,
-                                         const v8i (&bx)[PfShape<BM, BN>::FM], uint4& wa,
-                                         typename WStep<WF>::T& sc, v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
+                                         const v8i (&bx)[PfShape<BM, BN>::FM], uint4 wa0,
+                                         typename WStep<WF>::T sc0, uint4 wa1, typename WStep<WF>::T sc1,
+                                         v4f (&acc)[PfShape<BM, BN>::FN][PfShape<BM, BN>::FM],
                                          const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
     using S = PfShape<BM, BN>;
     if constexpr (F < S::FN) {
-        const v8i af = wfrag<WF>(wa);
-        const typename WStep<WF>::T scf = sc;
-        if constexpr (F + 1 < S::FN) {
-            sc = pf_scale<BN, WF>(sbuf, wn * S::FN + F + 1, s, lane);
-            wa = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 1));
+        const v8i af = wfrag<WF>(wa0);
+        // weight fragment F + 2 (and its scale) read two groups ahead
+        uint4 wa2 = wa1;
+        typename WStep<WF>::T sc2 = sc1;
+        if constexpr (F + 2 < S::FN) {
+            sc2 = pf_scale_raw<BN, WF>(sbuf, wn * S::FN + F + 2, s, lane);
+            wa2 = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 2));
         }
         pf_copies_at<BM, BN, F>(src, nxt, s_nxt, wave);
+        const typename WStep<WF>::T scf = pf_scale_use<WF>(sc0, s);
 #pragma unroll
         for (int h = 0; h < S::FM; ++h) acc[F][h] = wmma<WF, 0>(af, bx[h], acc[F][h], scf);
         __builtin_amdgcn_sched_barrier(0);
-        pf_group<BM, BN, WF, F + 1>(wp, sbuf, s, wn, lane, bx, wa, sc, acc, src, nxt, s_nxt, wave);
+        pf_group<BM, BN, WF, F + 1>(wp, sbuf, s, wn, lane, bx, wa1, sc1, wa2, sc2, acc, src, nxt, s_nxt, wave);
     }
 }
 
@@ -875,21 +901,33 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, int s, int wn, int
     const int g = lane >> 4;
     const uint8_t* ws = st;
     const uint8_t* as = st + S::WBYTES;
-    // activation fragments of the wave's FM column tiles, then the weight
-    // fragments one at a time against all of them, the next one's LDS read
-    // issued before the current one's products
-    v8i bx[S::FM];
-#pragma unroll
-    for (int h = 0; h < S::FM; ++h) {
-        const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
-        const int sw = (r >> 1) & 7;
-        const uint8_t* rowp = as + 128 * r;
-        bx[h] = act_frag<WF>(rowp, g, sw);
-    }
     const uint8_t* wp = ws + 1024 * (wn * S::FN) + 16 * lane;
-    typename WStep<WF>::T sc = pf_scale<BN, WF>(sbuf, wn * S::FN, s, lane);
-    uint4 wa = *reinterpret_cast<const uint4*>(wp);
-    pf_group<BM, BN, WF, 0>(wp, sbuf, s, wn, lane, bx, wa, sc, acc, src, nxt, s_nxt, wave);
+    // LDS reads in the order the products need them: all waves leave the
+    // barrier together and queue their reads on the LDS at once, so the first
+    // product waits only for the first weight fragment, its scale and the first
+    // activation fragment; then the other activation fragments and the second
+    // weight fragment.  Each group then reads the weight fragment two groups on.
+    v8i bx[S::FM];
+    const uint4 wa0 = *reinterpret_cast<const uint4*>(wp);
+    const typename WStep<WF>::T sc0 = pf_scale_raw<BN, WF>(sbuf, wn * S::FN, s, lane);
+    {
+        const int r = wm * 16 * S::FM + (lane & 15);
+        bx[0] = act_frag<WF>(as + 128 * r, g, (r >> 1) & 7);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 1; h < S::FM; ++h) {
+        const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
+        bx[h] = act_frag<WF>(as + 128 * r, g, (r >> 1) & 7);
+    }
+    uint4 wa1 = wa0;
+    typename WStep<WF>::T sc1 = sc0;
+    if constexpr (S::FN > 1) {
+        wa1 = *reinterpret_cast<const uint4*>(wp + 1024);
+        sc1 = pf_scale_raw<BN, WF>(sbuf, wn * S::FN + 1, s, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pf_group<BM, BN, WF, 0>(wp, sbuf, s, wn, lane, bx, wa0, sc0, wa1, sc1, acc, src, nxt, s_nxt, wave);
 }
 
 
@@ -1077,6 +1115,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         pf_issue<BM, BN>(src, base + i * S::STAGE, min(u, s1 - 1), wave);
     }
     int cur = 0, nxt = (NS - 1) * S::STAGE;   // stage offsets of steps s and s + NS - 1
+    pf_args_ready(a);
     for (int s = s0; s < s1; ++s) {
         // opaque to the optimiser: stage addresses are formed per step from a
         // few lane bases and immediate offsets instead of being unrolled and
@@ -1262,6 +1301,7 @@ __global__ __launch_bounds__(kPfThreads) void pfp_kernel(PfArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     PfFrag<BM, BN, WF> F0, F1;
+    pf_args_ready(a);
     pf_read<BM, BN, WF>(base, sbase + ((s0 >> 2) & 1) * SC::BYTES, s0, wn, wm, lane, F0);
     int cur = 0;
     for (int s = s0; s < s1; s += 2) {
