@@ -63,6 +63,10 @@ def lib():
         L.orc_requant_nvfp4_to_mxfp4.argtypes = [_u8p, _u8p, _i64p, _f32p, ctypes.c_int, _i64,
                                                  ctypes.c_int, _i64, _u8p, _u8p, _f64p]
         L.orc_requant_nvfp4_to_mxfp4.restype = ctypes.c_int
+        L.orc_quant_bf16_to_mxfp4.argtypes = [_u16p, _i64, _i64, ctypes.c_int, _u8p, _u8p, _f64p]
+        L.orc_quant_bf16_to_mxfp4.restype = ctypes.c_int
+        L.orc_quant_fp8ch_to_mxfp4.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int, _u8p, _u8p, _f64p]
+        L.orc_quant_fp8ch_to_mxfp4.restype = ctypes.c_int
         L.orc_quant_act_fp8.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _f32p]
         L.orc_quant_act_fp8.restype = ctypes.c_int
         L.orc_mxfp4_gemm.argtypes = [_u8p, _f32p, _u8p, _u8p, _i64, _i64, _i64, _vp, _vp, _i64, _f64p]
@@ -205,6 +209,32 @@ def requant_nvfp4_to_mxfp4(nv_packed, nv_scale, part_rows, part_divisor, mode="m
     if rc != 0:
         raise ValueError("oracle requant rejected its arguments")
     return mp, me, st.reshape(-1, 2)
+
+
+def quant_bf16_to_mxfp4(w_bf16_bits, mode="mse"):
+    """bf16 bits [rows, K] (uint16) -> (packed [rows,K/2], e8m0 [rows,K/32], stats {err, w^2})."""
+    w = _c(w_bf16_bits, np.uint16)
+    rows, K = w.shape
+    mp = np.zeros((rows, K // 2), np.uint8)
+    me = np.zeros((rows, K // 32), np.uint8)
+    st = np.zeros(2, np.float64)
+    if lib().orc_quant_bf16_to_mxfp4(w, rows, K, MODES.get(mode, mode), mp, me, st) != 0:
+        raise ValueError("oracle bf16 quant rejected its arguments")
+    return mp, me, st
+
+
+def quant_fp8ch_to_mxfp4(w_e4m3, row_scale, mode="mse"):
+    """e4m3 codes [rows, K] (uint8) + fp32 scale per row -> (packed, e8m0, stats {err, w^2})."""
+    w = _c(w_e4m3, np.uint8)
+    s = _c(row_scale, np.float32)
+    rows, K = w.shape
+    assert s.shape == (rows,)
+    mp = np.zeros((rows, K // 2), np.uint8)
+    me = np.zeros((rows, K // 32), np.uint8)
+    st = np.zeros(2, np.float64)
+    if lib().orc_quant_fp8ch_to_mxfp4(w, s, rows, K, MODES.get(mode, mode), mp, me, st) != 0:
+        raise ValueError("oracle fp8 quant rejected its arguments")
+    return mp, me, st
 
 
 def quant_act_fp8(x_bf16_bits, K=None, ldx=None):

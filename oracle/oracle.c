@@ -311,6 +311,70 @@ int orc_requant_nvfp4_to_mxfp4(const uint8_t *nv_packed, const uint8_t *nv_scale
 }
 
 /* ------------------------------------------------------------------------ */
+/* bf16 and fp8 per-channel weights -> MXFP4                                 */
+/* ------------------------------------------------------------------------ */
+
+/* [P1] RadianceBf16ToMxfp4.process_weights_after_loading: requant_rows on the
+ * bf16 weight itself -- each element widened to fp32 (exact), then
+ * quant_mxfp4 over rows.  The ROW_CHUNK passes do not change any output.
+ * stats (nullable): {sum of chosen block errors, sum of w^2}, fp64.
+ * Returns 0, or -1 on a bad argument (K % 32) or a non-finite input. */
+int orc_quant_bf16_to_mxfp4(const uint16_t *w_bf16, int64_t rows, int64_t K, int mode,
+                            uint8_t *mx_packed, uint8_t *mx_e8m0, double *stats) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
+    float *w = (float *)malloc((size_t)((rows > 0 ? rows : 1) * K) * sizeof(float));
+    if (!w) return -1;
+    int bad = 0;
+    for (int64_t i = 0; i < rows * K; ++i) {
+        w[i] = orc_bf16_value(w_bf16[i]);
+        if (!isfinite(w[i])) bad = 1;
+    }
+    if (!bad) {
+        double e = 0.0, s = 0.0;
+        orc_quant_mxfp4(w, rows, K, mode, mx_packed, mx_e8m0, NULL, &e, &s);
+        if (stats) {
+            stats[0] = e;
+            stats[1] = s;
+        }
+    }
+    free(w);
+    return bad ? -1 : 0;
+}
+
+/* [P1] RadianceFp8ChannelToMxfp4.process_weights_after_loading: the e4m3
+ * weight widened to fp32 and multiplied by its row's fp32 scale (one
+ * correctly rounded fp32 product), then quant_mxfp4 over rows.  stats as
+ * above.  Returns 0, or -1 on a bad argument or a NaN code / non-finite
+ * scale. */
+int orc_quant_fp8ch_to_mxfp4(const uint8_t *w_e4m3, const float *row_scale, int64_t rows,
+                             int64_t K, int mode, uint8_t *mx_packed, uint8_t *mx_e8m0,
+                             double *stats) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
+    float *w = (float *)malloc((size_t)((rows > 0 ? rows : 1) * K) * sizeof(float));
+    if (!w) return -1;
+    int bad = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float s = row_scale[r];
+        if (!isfinite(s)) bad = 1;
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = orc_e4m3_value(w_e4m3[r * K + k]);
+            if (!isfinite(v)) bad = 1;
+            w[r * K + k] = (float)v * s;
+        }
+    }
+    if (!bad) {
+        double e = 0.0, ss = 0.0;
+        orc_quant_mxfp4(w, rows, K, mode, mx_packed, mx_e8m0, NULL, &e, &ss);
+        if (stats) {
+            stats[0] = e;
+            stats[1] = ss;
+        }
+    }
+    free(w);
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* per-token fp8 activations (reading R5)                                    */
 /* ------------------------------------------------------------------------ */
 

@@ -14,7 +14,9 @@
  * Sources (cited by page title and section, never by line):
  *   [P1] "radiance_nvfp4.py" -- unpack_e2m1, dequant_nvfp4, e2m1_index,
  *        _block_exponent, _encode_blocks, quant_mxfp4, dequant_mxfp4,
- *        requant_rows, RadianceNvfp4ToMxfp4.process_weights_after_loading.
+ *        requant_rows, RadianceNvfp4ToMxfp4.process_weights_after_loading,
+ *        RadianceBf16ToMxfp4 and RadianceFp8ChannelToMxfp4
+ *        .process_weights_after_loading.
  *   [P2] "vllm-radiance (MXFP4)" -- How the MXFP4 path works: The W4A8
  *        fp8-WMMA kernel; NVFP4 checkpoints: online requantization to MXFP4.
  *   [P3] "radiance_autoround.py" -- module docstring (int4 format),
@@ -54,6 +56,14 @@ int     orc_requant_nvfp4_to_mxfp4(const uint8_t *nv_packed, const uint8_t *nv_s
                                    const int64_t *part_rows, const float *part_divisor,
                                    int n_parts, int64_t K, int mode, int64_t row_chunk,
                                    uint8_t *mx_packed, uint8_t *mx_e8m0, double *stats);
+
+/* --- bf16 / fp8 per-channel -> MXFP4 ([P1] RadianceBf16ToMxfp4,
+ *     RadianceFp8ChannelToMxfp4) ------------------------------------------ */
+int     orc_quant_bf16_to_mxfp4(const uint16_t *w_bf16, int64_t rows, int64_t K, int mode,
+                                uint8_t *mx_packed, uint8_t *mx_e8m0, double *stats);
+int     orc_quant_fp8ch_to_mxfp4(const uint8_t *w_e4m3, const float *row_scale, int64_t rows,
+                                 int64_t K, int mode, uint8_t *mx_packed, uint8_t *mx_e8m0,
+                                 double *stats);
 
 /* --- per-token fp8 activations ------------------------------------------- */
 int     orc_quant_act_fp8(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t ldx,
