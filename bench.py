@@ -18,7 +18,8 @@ read back, token scales, and the bf16 output.
 Also reported, each from its own short timed loop (HIP events on the stream the
 kernels run on): the decode GEMM per M, with the roofline taken on the decode
 kernel at M = 1 (one kernel per call there); the prefill GEMM (M = 4096) in
-TFLOP/s; the full-layer requant in GB/s for the three exponent rules; the
+TFLOP/s; the full-layer requant in GB/s for the three exponent rules, and
+the bf16 / fp8-per-channel -> MXFP4 encoders on the same shape; the
 down_proj decode and prefill; the int4 g128 variant; and the row-major weight
 layout's GEMM for comparison.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same step.
@@ -384,6 +385,33 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
     res["requant_full_layer"] = rq
     log("requant", rq)
     del src, outs
+    # bf16 and fp8 per-channel weights of the same shape -> MXFP4 (the requant
+    # encoder with other input stages), two input copies alternating
+    lq = {}
+    wb = torch.from_numpy(synth.bf16_weight(N, K).view(np.int16)).view(torch.bfloat16).to(dev)
+    bsrc = [wb, wb.clone()]
+    del wb
+    f8 = synth.fp8ch_weight(N, K)
+    w8 = torch.from_numpy(f8["w8"]).to(dev)
+    rs = torch.from_numpy(f8["row_scale"]).to(dev)
+    fsrc = [(w8, rs), (w8.clone(), rs.clone())]
+    del w8, f8
+    outs = [(torch.empty_like(wp), torch.empty_like(we)) for _ in range(2)]
+    for mode in ("ocp", "mse"):
+        def run_b(i, mode=mode):
+            w4.quant_bf16_to_mxfp4(bsrc[i % 2], mode=mode, out_packed=outs[i % 2][0], out_e8m0=outs[i % 2][1])
+
+        def run_f(i, mode=mode):
+            w4.quant_fp8ch_to_mxfp4(fsrc[i % 2][0], fsrc[i % 2][1], mode=mode, out_packed=outs[i % 2][0],
+                                    out_e8m0=outs[i % 2][1])
+        for name, run, nbytes in (("bf16", run_b, N * K * 2 + N * K // 2 + N * K // 32),
+                                  ("fp8ch", run_f, N * K + 4 * N + N * K // 2 + N * K // 32)):
+            rg = [graph_of(torch, lambda i=i, run=run: run(i)) for i in range(2)]
+            dt = timer(lambda i: rg[i % 2].replay(), 6)
+            lq[f"{name}_{mode}"] = {"us": round(dt * 1e6, 1), "gbps": round(nbytes / dt / 1e9, 1)}
+    res["load_quant_full_layer"] = lq
+    log("bf16 / fp8 -> mxfp4", lq)
+    del bsrc, fsrc, outs
     # down_proj (K = 17408), fragment-order weights, eight copies
     d = synth.down_proj()
     dw = torch.from_numpy(d["w_packed"]).to(dev)

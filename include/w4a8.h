@@ -116,6 +116,33 @@ w4a8_status w4a8_requant_nvfp4_to_mxfp4(
     uint8_t *d_mx_packed, uint8_t *d_mx_e8m0, double *d_err_stats, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * bf16 and fp8-per-channel weights -> MXFP4 at load time, with the encoder of
+ * w4a8_requant_nvfp4_to_mxfp4 (same exponent rules, code rounding, signs and
+ * statistics).  Source: "radiance_nvfp4.py", RadianceBf16ToMxfp4 (the bf16
+ * weight itself, widened exactly) and RadianceFp8ChannelToMxfp4 (each e4m3
+ * weight times its row's fp32 scale, one rounded fp32 product) with
+ * quant_mxfp4 / requant_rows (the page's row chunks change no output, so one
+ * pass covers the weight).
+ *   d_w_bf16      device uint16 [rows, K] bf16 bits, 16-byte aligned
+ *   d_w_e4m3      device uint8 [rows, K] OCP e4m3 codes, 16-byte aligned
+ *   d_row_scale   device float [rows], 4-byte aligned
+ *   rows          >= 0;  K % 32 == 0 and rows * K/32 < 2^32 (else
+ *                 UNSUPPORTED_SHAPE)
+ *   mode          w4a8_exp_mode; the page's schemes use mse
+ *   d_mx_packed   device uint8 [rows, K/2] out (16-byte aligned), d_mx_e8m0
+ *                 device uint8 [rows, K/32] out
+ *   d_err_stats   device double [2] or NULL: out {sum of chosen block squared
+ *                 errors, sum of w^2} (atomics: low bits depend on order)
+ * Non-finite inputs are excluded (unspecified results).  Inputs and outputs
+ * must not overlap.  Errors: INVALID_ARG, UNSUPPORTED_SHAPE, HIP. */
+w4a8_status w4a8_quant_bf16_to_mxfp4(const uint16_t *d_w_bf16, int64_t rows, int64_t K, w4a8_exp_mode mode,
+                                     uint8_t *d_mx_packed, uint8_t *d_mx_e8m0, double *d_err_stats,
+                                     void *stream);
+w4a8_status w4a8_quant_fp8ch_to_mxfp4(const uint8_t *d_w_e4m3, const float *d_row_scale, int64_t rows,
+                                      int64_t K, w4a8_exp_mode mode, uint8_t *d_mx_packed,
+                                      uint8_t *d_mx_e8m0, double *d_err_stats, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Dynamic per-token fp8 activation quantization.
  * Source: "radiance_autoround.py", autoround_linear (per-token dynamic e4m3
  * with one fp32 scale per row, consumed by the W4A8 GEMM).  The pages leave the

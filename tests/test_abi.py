@@ -76,6 +76,21 @@ def test_act_quant_validation(L):
     assert f(_p(FAKE + 1), 1, 8, 8, _p(), _p(), None) == INVALID
 
 
+def test_load_quant_validation(L):
+    b = L.w4a8_quant_bf16_to_mxfp4
+    f = L.w4a8_quant_fp8ch_to_mxfp4
+    assert b(None, 4, 64, 2, _p(), _p(), None, None) == INVALID
+    assert b(_p(), 4, 64, 3, _p(), _p(), None, None) == INVALID                 # bad mode
+    assert b(_p(), -1, 64, 2, _p(), _p(), None, None) == INVALID
+    assert b(_p(), 4, 48, 2, _p(), _p(), None, None) == SHAPE                   # K % 32
+    assert b(_p(FAKE + 8), 4, 64, 2, _p(), _p(), None, None) == INVALID         # 16-byte aligned in
+    assert b(_p(), 4, 64, 2, _p(FAKE + 8), _p(), None, None) == INVALID         # 16-byte aligned out
+    assert b(_p(), 4, 64, 2, _p(), _p(), _p(FAKE + 4), None) == INVALID         # 8-byte aligned stats
+    assert f(_p(), None, 4, 64, 2, _p(), _p(), None, None) == INVALID           # row scales required
+    assert f(_p(), _p(FAKE + 2), 4, 64, 2, _p(), _p(), None, None) == INVALID
+    assert f(_p(), _p(), 4, 96 + 16, 2, _p(), _p(), None, None) == SHAPE
+
+
 def test_gemm_validation(L):
     g = L.w4a8_mxfp4_gemm
     args = lambda **k: [_p(k.get("x", FAKE)) if k.get("x", FAKE) else None, _p(), _p(), _p(),

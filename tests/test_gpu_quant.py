@@ -181,3 +181,66 @@ def test_requant_rejects_bad_arguments():
         w4.requant_nvfp4_to_mxfp4(p, s, [256], [float("inf")])
     with pytest.raises(ValueError):
         w4.requant_nvfp4_to_mxfp4(p[:, :8], s[:, :1], [256], [1.0])  # K = 16: K % 32 != 0
+
+
+# ---------------------------------------------------------------------------
+# bf16 / fp8 per-channel weights -> MXFP4 at load (the requant encoder)
+# ---------------------------------------------------------------------------
+
+def _load_case(kind, a, mode, name, scale=None):
+    rows, K = a.shape
+    say("load quant", kind, name, mode, (rows, K))
+    if kind == "bf16":
+        mp, me, st = w4.quant_bf16_to_mxfp4(dev_bf16(a), mode=mode, stats=True)
+        rp, re_, rst = oracle.quant_bf16_to_mxfp4(a, mode)
+    else:
+        mp, me, st = w4.quant_fp8ch_to_mxfp4(dev_u8(a), torch.from_numpy(scale).cuda(), mode=mode, stats=True)
+        rp, re_, rst = oracle.quant_fp8ch_to_mxfp4(a, scale, mode)
+    gp, ge = host(mp), host(me)
+    bad = np.argwhere(ge != re_)
+    assert bad.size == 0, (kind, name, mode, "e8m0", bad[:5])
+    bad = np.argwhere(gp != rp)
+    assert bad.size == 0, (kind, name, mode, "codes", bad[:5])
+    np.testing.assert_allclose(host(st), rst, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_quant_bf16_random_bits(mode):
+    # every finite bf16 pattern class: subnormals, zeros of both signs, the
+    # largest finite values (exponent clamp at 127), ragged row counts
+    g = np.random.default_rng(21)
+    for rows, K in [(1, 32), (7, 96), (257, 320)]:
+        a = g.integers(0, 1 << 16, (rows, K)).astype(np.uint16)
+        a[(a & 0x7F80) == 0x7F80] &= 0xFF7F                       # no inf / NaN
+        _load_case("bf16", a, mode, f"random {rows}x{K}")
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_quant_fp8ch_random_codes(mode):
+    g = np.random.default_rng(22)
+    for rows, K in [(1, 32), (9, 160), (300, 256)]:
+        c = g.integers(0, 256, (rows, K)).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x7E                              # no NaN codes
+        s = np.exp2(g.uniform(-30, 20, rows)).astype(np.float32) * g.uniform(1, 2, rows).astype(np.float32)
+        _load_case("fp8", c, mode, f"random {rows}x{K}", s)
+
+
+def test_quant_bf16_gate_up_shape():
+    a = synth.bf16_weight()
+    _load_case("bf16", a, "mse", "gate_up-shaped")
+
+
+def test_quant_fp8ch_gate_up_shape():
+    d = synth.fp8ch_weight()
+    _load_case("fp8", d["w8"], "mse", "gate_up-shaped", d["row_scale"])
+
+
+def test_load_quant_rejects_bad_arguments():
+    z = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        w4.quant_bf16_to_mxfp4(z)                                   # K % 32
+    c = torch.zeros((4, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        w4.quant_fp8ch_to_mxfp4(c, torch.ones(3, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        w4.quant_bf16_to_mxfp4(torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"), mode="nearest")

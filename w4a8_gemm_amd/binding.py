@@ -19,6 +19,7 @@ __all__ = [
     "Workspace", "mxfp4_gemm", "int4g128_prepare", "int4g128_gemm", "w4a8_linear",
     "decode_with_plan", "PreparedMXFP4", "mxfp4_prepare", "mxfp4_gemm_prepared",
     "PreparedInt4", "int4g128_prepare_fragments", "int4g128_gemm_prepared",
+    "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -53,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.w4a8_requant_nvfp4_to_mxfp4.argtypes = [_vp, _vp, _vp, _vp, _int, _i64, _int, _i64,
                                                   _vp, _vp, _vp, _vp]
         L.w4a8_quant_act_fp8_per_token.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+        L.w4a8_quant_bf16_to_mxfp4.argtypes = [_vp, _i64, _i64, _int, _vp, _vp, _vp, _vp]
+        L.w4a8_quant_bf16_to_mxfp4.restype = _int
+        L.w4a8_quant_fp8ch_to_mxfp4.argtypes = [_vp, _vp, _i64, _i64, _int, _vp, _vp, _vp, _vp]
+        L.w4a8_quant_fp8ch_to_mxfp4.restype = _int
         L.w4a8_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
         L.w4a8_gemm_workspace_bytes.restype = _size
         L.w4a8_workspace_init.argtypes = [_vp, _size, _vp]
@@ -168,6 +173,57 @@ def requant_nvfp4_to_mxfp4(nv_packed: torch.Tensor, nv_scale: torch.Tensor, part
         _ptr(nv_packed), _ptr(nv_scale), pr, pd, len(part_rows), K, EXP_MODES[mode],
         int(row_chunk), _ptr(out_packed), _ptr(out_e8m0), _ptr(st), _stream(nv_packed))
     _check(status, "w4a8_requant_nvfp4_to_mxfp4")
+    return (out_packed, out_e8m0, st) if stats else (out_packed, out_e8m0)
+
+
+def _load_outputs(rows, K, dev, out_packed, out_e8m0, stats, mode):
+    if mode not in EXP_MODES:
+        raise ValueError(f"mode must be one of {sorted(EXP_MODES)}")
+    if out_packed is None:
+        out_packed = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    if out_e8m0 is None:
+        out_e8m0 = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
+    _need(out_packed, "out_packed", torch.uint8, dev)
+    _need(out_e8m0, "out_e8m0", torch.uint8, dev)
+    if tuple(out_packed.shape) != (rows, K // 2) or tuple(out_e8m0.shape) != (rows, K // 32):
+        raise ValueError("outputs must be [rows, K/2] and [rows, K/32]")
+    st = torch.empty(2, dtype=torch.float64, device=dev) if stats else None
+    return out_packed, out_e8m0, st
+
+
+def quant_bf16_to_mxfp4(w: torch.Tensor, mode: str = "mse", out_packed: torch.Tensor | None = None,
+                        out_e8m0: torch.Tensor | None = None, stats: bool = False):
+    """bf16 weight [rows, K] -> MXFP4 codes [rows, K/2] u8 and e8m0 [rows, K/32] u8
+    (with stats=True also float64 [2]: sum of squared block errors, sum of w^2)."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    rows, K = w.shape
+    out_packed, out_e8m0, st = _load_outputs(rows, K, w.device, out_packed, out_e8m0, stats, mode)
+    status = lib().w4a8_quant_bf16_to_mxfp4(_ptr(w), rows, K, EXP_MODES[mode], _ptr(out_packed),
+                                            _ptr(out_e8m0), _ptr(st), _stream(w))
+    _check(status, "w4a8_quant_bf16_to_mxfp4")
+    return (out_packed, out_e8m0, st) if stats else (out_packed, out_e8m0)
+
+
+def quant_fp8ch_to_mxfp4(w8: torch.Tensor, row_scale: torch.Tensor, mode: str = "mse",
+                         out_packed: torch.Tensor | None = None, out_e8m0: torch.Tensor | None = None,
+                         stats: bool = False):
+    """fp8 e4m3 weight [rows, K] (float8_e4m3fn or its uint8 codes) with one fp32
+    scale per row ([rows] or [rows, 1]) -> MXFP4 as quant_bf16_to_mxfp4."""
+    if isinstance(w8, torch.Tensor) and w8.dtype == torch.float8_e4m3fn:
+        w8 = w8.view(torch.uint8)
+    _need(w8, "w8", torch.uint8)
+    if w8.dim() != 2 or not w8.is_contiguous():
+        raise ValueError("w8 must be a contiguous 2-D tensor")
+    rows, K = w8.shape
+    _need(row_scale, "row_scale", torch.float32, w8.device)
+    if row_scale.numel() != rows or not row_scale.is_contiguous():
+        raise ValueError("row_scale must hold one contiguous fp32 scale per row")
+    out_packed, out_e8m0, st = _load_outputs(rows, K, w8.device, out_packed, out_e8m0, stats, mode)
+    status = lib().w4a8_quant_fp8ch_to_mxfp4(_ptr(w8), _ptr(row_scale), rows, K, EXP_MODES[mode],
+                                             _ptr(out_packed), _ptr(out_e8m0), _ptr(st), _stream(w8))
+    _check(status, "w4a8_quant_fp8ch_to_mxfp4")
     return (out_packed, out_e8m0, st) if stats else (out_packed, out_e8m0)
 
 

@@ -80,6 +80,40 @@ w4a8_status w4a8_requant_nvfp4_to_mxfp4(const uint8_t* d_nv_packed, const uint8_
     return W4A8_OK;
 }
 
+// bf16 or fp8-per-channel weight [rows, K] -> MXFP4, one launch
+static w4a8_status quant_load(const void* d_w, const float* d_row_scale, bool fp8, int64_t rows, int64_t K,
+                              w4a8_exp_mode mode, uint8_t* d_mx_packed, uint8_t* d_mx_e8m0,
+                              double* d_err_stats, void* stream) {
+    if (!d_w || (fp8 && !d_row_scale) || !d_mx_packed || !d_mx_e8m0) return W4A8_ERR_INVALID_ARG;
+    if (rows < 0 || rows > kMaxDim || K < 1 || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (mode != W4A8_EXP_OCP && mode != W4A8_EXP_NOCLIP && mode != W4A8_EXP_MSE) return W4A8_ERR_INVALID_ARG;
+    if (K % 32 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (rows * (K / 32) >= ((int64_t)1 << 32)) return W4A8_ERR_UNSUPPORTED_SHAPE;   // 32-bit block index
+    if (!aligned(d_w, 16) || !aligned(d_mx_packed, 16) || (fp8 && !aligned(d_row_scale, 4)) ||
+        (d_err_stats && !aligned(d_err_stats, 8)))
+        return W4A8_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (d_err_stats && launch_fill_zero_f64(d_err_stats, 2, s) != hipSuccess) return W4A8_ERR_HIP;
+    if (fp8)
+        return hip_status(launch_quant_fp8ch(static_cast<const uint8_t*>(d_w), d_row_scale, rows, K, (int)mode,
+                                             d_mx_packed, d_mx_e8m0, d_err_stats, s));
+    return hip_status(launch_quant_bf16(static_cast<const uint16_t*>(d_w), rows, K, (int)mode, d_mx_packed,
+                                        d_mx_e8m0, d_err_stats, s));
+}
+
+w4a8_status w4a8_quant_bf16_to_mxfp4(const uint16_t* d_w_bf16, int64_t rows, int64_t K, w4a8_exp_mode mode,
+                                     uint8_t* d_mx_packed, uint8_t* d_mx_e8m0, double* d_err_stats,
+                                     void* stream) {
+    return quant_load(d_w_bf16, nullptr, false, rows, K, mode, d_mx_packed, d_mx_e8m0, d_err_stats, stream);
+}
+
+w4a8_status w4a8_quant_fp8ch_to_mxfp4(const uint8_t* d_w_e4m3, const float* d_row_scale, int64_t rows,
+                                      int64_t K, w4a8_exp_mode mode, uint8_t* d_mx_packed, uint8_t* d_mx_e8m0,
+                                      double* d_err_stats, void* stream) {
+    return quant_load(d_w_e4m3, d_row_scale, true, rows, K, mode, d_mx_packed, d_mx_e8m0, d_err_stats,
+                      stream);
+}
+
 w4a8_status w4a8_quant_act_fp8_per_token(const uint16_t* d_x_bf16, int64_t M, int64_t K,
                                          int64_t ldx, uint8_t* d_x_fp8, float* d_x_scale,
                                          void* stream) {

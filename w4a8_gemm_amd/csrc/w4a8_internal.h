@@ -88,6 +88,11 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
 hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, float divisor,
                           int64_t nblocks, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0,
                           double* stats, hipStream_t stream);
+// bf16 / fp8-per-channel weights -> MXFP4 (the requant encoder, other input stages)
+hipError_t launch_quant_bf16(const uint16_t* w, int64_t rows, int64_t K, int mode, uint8_t* mx_packed,
+                             uint8_t* mx_e8m0, double* stats, hipStream_t stream);
+hipError_t launch_quant_fp8ch(const uint8_t* w, const float* row_scale, int64_t rows, int64_t K, int mode,
+                              uint8_t* mx_packed, uint8_t* mx_e8m0, double* stats, hipStream_t stream);
 hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream);
 hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 

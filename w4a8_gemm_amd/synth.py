@@ -192,3 +192,24 @@ def mxfp4_random(N: int, K: int, seed, e_lo: int = 120, e_hi: int = 130) -> dict
 def int4_random(N: int, K: int, seed) -> dict:
     """int4 g128 weight of any (N % 8 == 0, K % 128 == 0) shape, same recipe as int4()."""
     return int4.__wrapped__(seed=seed, N=N, K=K)
+
+
+def bf16_weight(N: int = 2 * INTERMEDIATE, K: int = HIDDEN, seed=5) -> np.ndarray:
+    """An unquantized bf16 linear [N, K] (bf16 bits, uint16): N(0, 0.02^2) with
+    0.1% of entries multiplied by 20, cast to bf16 (RNE)."""
+    g = _gen(seed)
+    w = torch.randn((N, K), generator=g, dtype=torch.float32) * 0.02
+    w = torch.where(torch.rand((N, K), generator=g) < 0.001, w * 20.0, w)
+    return bf16_bits(w)
+
+
+def fp8ch_weight(N: int = 2 * INTERMEDIATE, K: int = HIDDEN, seed=6) -> dict:
+    """An fp8 per-channel linear as such checkpoints store it: the weight of
+    bf16_weight's recipe, one fp32 scale per row s = amax_row / 448, codes
+    e4m3(w / s) (torch's RNE cast).  -> dict(w8 [N, K] u8, row_scale [N] f32)."""
+    g = _gen(seed)
+    w = torch.randn((N, K), generator=g, dtype=torch.float32) * 0.02
+    w = torch.where(torch.rand((N, K), generator=g) < 0.001, w * 20.0, w)
+    s = (w.abs().amax(1) / 448.0).clamp(min=1e-12)
+    w8 = (w / s[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return dict(w8=w8, row_scale=s.numpy().astype(np.float32), N=N, K=K)
