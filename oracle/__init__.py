@@ -71,6 +71,8 @@ def lib():
         L.orc_quant_act_fp8.restype = ctypes.c_int
         L.orc_mxfp4_gemm.argtypes = [_u8p, _f32p, _u8p, _u8p, _i64, _i64, _i64, _vp, _vp, _i64, _f64p]
         L.orc_mxfp4_gemm.restype = None
+        L.orc_w4a4_gemm.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _vp, _vp, _i64, _f64p]
+        L.orc_w4a4_gemm.restype = None
         L.orc_int4_prepare.argtypes = [_i32p, _i32p, _i64, _i64, _i32p]
         L.orc_int4_prepare.restype = ctypes.c_int
         L.orc_int4_gemm.argtypes = [_u8p, _f32p, _i32p, _u16p, _i64, _i64, _i64, _vp, _vp, _i64, _f64p]
@@ -266,6 +268,33 @@ def mxfp4_gemm(x8, x_scale, w_packed, w_e8m0, mi=None, ni=None):
     ni = _c(ni, np.int64)
     ref = np.zeros(len(mi), np.float64)
     lib().orc_mxfp4_gemm(x8, xs, wp, we, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
+    return ref
+
+
+def quant_act_mxfp4(x_bf16_bits):
+    """MXFP4 activations (W4A4): each token row quantized per 32-block by the
+    OCP rule -- the page's "ocp" exponent, nearest-even codes, saturation at 6.
+    -> (packed [M, K/2], e8m0 [M, K/32])."""
+    p, e, _ = quant_bf16_to_mxfp4(x_bf16_bits, "ocp")
+    return p, e
+
+
+def w4a4_gemm(x_packed, x_e8m0, w_packed, w_e8m0, mi=None, ni=None):
+    """fp64 reference of the MXFP4 x MXFP4 GEMM; full [M,N] or values at (mi[i], ni[i])."""
+    xp = _c(x_packed, np.uint8)
+    xe = _c(x_e8m0, np.uint8)
+    wp = _c(w_packed, np.uint8)
+    we = _c(w_e8m0, np.uint8)
+    M, K = xp.shape[0], 2 * xp.shape[1]
+    N = wp.shape[0]
+    if mi is None:
+        ref = np.zeros((M, N), np.float64)
+        lib().orc_w4a4_gemm(xp, xe, wp, we, M, N, K, None, None, 0, ref)
+        return ref
+    mi = _c(mi, np.int64)
+    ni = _c(ni, np.int64)
+    ref = np.zeros(len(mi), np.float64)
+    lib().orc_w4a4_gemm(xp, xe, wp, we, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
     return ref
 
 

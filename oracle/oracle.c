@@ -437,6 +437,39 @@ void orc_mxfp4_gemm(const uint8_t *x8, const float *x_scale, const uint8_t *w_pa
     }
 }
 
+/* [P2] MXFP4 checkpoints with MXFP4 activations (the declared W4A4 numerics
+ * the page's W4A8 kernel departs from): activations quantized per token and
+ * 32-block to e2m1 + e8m0, weights e2m1 + e8m0;
+ *   out[m,n] = sum_k e2m1(x[m,k]) 2^(Ex[m,k/32]-127) * e2m1(w[n,k]) 2^(Ew[n,k/32]-127),
+ * exact products, fp64 accumulation, not rounded. */
+static double w4a4_dot(const uint8_t *xp, const uint8_t *xe, const uint8_t *wp, const uint8_t *we,
+                       int64_t m, int64_t n, int64_t K) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        uint8_t xb = xp[m * (K / 2) + k / 2], wb = wp[n * (K / 2) + k / 2];
+        int xc = (k & 1) ? (xb >> 4) : (xb & 15), wc = (k & 1) ? (wb >> 4) : (wb & 15);
+        double xv = (double)orc_e2m1_value(xc) * ldexp(1.0, (int)xe[m * (K / 32) + k / 32] - 127);
+        double wv = (double)orc_e2m1_value(wc) * ldexp(1.0, (int)we[n * (K / 32) + k / 32] - 127);
+        acc += xv * wv;
+    }
+    return acc;
+}
+
+void orc_w4a4_gemm(const uint8_t *x_packed, const uint8_t *x_e8m0, const uint8_t *w_packed,
+                   const uint8_t *w_e8m0, int64_t M, int64_t N, int64_t K,
+                   const int64_t *mi, const int64_t *ni, int64_t count, double *ref) {
+    if (!mi) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = 0; m < M; ++m)
+                ref[m * N + n] = w4a4_dot(x_packed, x_e8m0, w_packed, w_e8m0, m, n, K);
+    } else {
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t i = 0; i < count; ++i)
+            ref[i] = w4a4_dot(x_packed, x_e8m0, w_packed, w_e8m0, mi[i], ni[i], K);
+    }
+}
+
 /* [P3] process_weights_after_loading: every qzeros word must be 0x77777777
  * (zero point 8, symmetric); the weight is transposed from [K/8, N] to
  * [N, K/8].  Returns the number of qzeros words that differ (0 = accepted);

@@ -73,6 +73,9 @@ int     orc_quant_act_fp8(const uint16_t *x_bf16, int64_t M, int64_t K, int64_t 
 void    orc_mxfp4_gemm(const uint8_t *x8, const float *x_scale, const uint8_t *w_packed,
                        const uint8_t *w_e8m0, int64_t M, int64_t N, int64_t K,
                        const int64_t *mi, const int64_t *ni, int64_t count, double *ref);
+void    orc_w4a4_gemm(const uint8_t *x_packed, const uint8_t *x_e8m0, const uint8_t *w_packed,
+                      const uint8_t *w_e8m0, int64_t M, int64_t N, int64_t K,
+                      const int64_t *mi, const int64_t *ni, int64_t count, double *ref);
 int     orc_int4_prepare(const int32_t *qweight_kn, const int32_t *qzeros,
                          int64_t N, int64_t K, int32_t *qweight_nk);
 void    orc_int4_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweight_nk,
