@@ -71,7 +71,9 @@ typedef enum {
     W4A8_WEIGHT_MXFP4 = 0,           /* [N, K/2] codes + [N, K/32] e8m0 */
     W4A8_WEIGHT_INT4G128 = 1,        /* [N, K/8] int32 (w4a8_int4g128_prepare) + fp16 scales */
     W4A8_WEIGHT_MXFP4_PREPARED = 2,  /* fragment order (w4a8_mxfp4_prepare) */
-    W4A8_WEIGHT_INT4G128_PREPARED = 3 /* fragment order (w4a8_int4g128_prepare_fragments) */
+    W4A8_WEIGHT_INT4G128_PREPARED = 3, /* fragment order (w4a8_int4g128_prepare_fragments) */
+    W4A8_W4A4_PREPARED = 4            /* MXFP4 fragment order with MXFP4 activations
+                                         (w4a8_w4a4_gemm_prepared) */
 } w4a8_weight_kind;
 
 /* ---------------------------------------------------------------------------
@@ -267,6 +269,30 @@ w4a8_status w4a8_int4g128_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const int32_t *d_qweight_nk, const uint16_t *d_scales_f16, uint16_t *d_out,
     int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * W4A4: MXFP4 activations x MXFP4 weights (prepared by w4a8_mxfp4_prepare) on
+ * the fp4 x fp4 block-scaled matrix instructions.  Source: "vllm-radiance
+ * (MXFP4)", the Quark MXFP4 checkpoints' declared numerics (MXFP4 weights and
+ * activations, group 32, e8m0 scales) that the page's W4A8 kernel departs
+ * from.  Activations are quantized per token and 32-block by the OCP rule:
+ * w4a8_quant_bf16_to_mxfp4 with W4A8_EXP_OCP on the [M, K] bf16 activations
+ * (the pages do not print the activation quantizer; this is the OCP MX
+ * reading).
+ *   out[m, n] = bf16( sum_k e2m1(x[m,k]) 2^(Ex[m,k/32]-127) e2m1(w[n,k]) 2^(Ew[n,k/32]-127) )
+ * with fp32 accumulation (summation order differs from a sequential sum).
+ *   d_x_fp4   device uint8 [M, K/2] e2m1 codes (even k low nibble), 16-byte aligned
+ *   d_x_e8m0  device uint8 [M, K/32], 4-byte aligned
+ *   d_w_prepared, d_s_prepared: from w4a8_mxfp4_prepare
+ *   d_out     device bf16 [M, N], 8-byte aligned
+ * Any M >= 1; K % 128 == 0 and K < 2^24 (else UNSUPPORTED_SHAPE).  One tiled
+ * kernel (128- or 256-row tiles, 256 wide) serves every M; with fewer than 128
+ * tiles K is split across workgroups: fp32 partials in the workspace (size it
+ * with W4A8_W4A4_PREPARED for the largest M), then a reduction.  Errors:
+ * INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t *d_x_fp4, const uint8_t *d_x_e8m0,
+                                    const uint8_t *d_w_prepared, const uint8_t *d_s_prepared, uint16_t *d_out,
+                                    int64_t M, int64_t N, int64_t K, void *d_ws, size_t ws_bytes, void *stream);
 
 /* int4 g128 weights in matrix-core fragment order (load time) and the GEMM on
  * them.  Source: "radiance_autoround.py", as w4a8_int4g128_gemm above, with the

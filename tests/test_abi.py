@@ -91,6 +91,20 @@ def test_load_quant_validation(L):
     assert f(_p(), _p(), 4, 96 + 16, 2, _p(), _p(), None, None) == SHAPE
 
 
+def test_w4a4_validation(L):
+    g = L.w4a8_w4a4_gemm_prepared
+    assert g(None, _p(), _p(), _p(), _p(), 4, 64, 128, None, 0, None) == INVALID
+    assert g(_p(), _p(FAKE + 2), _p(), _p(), _p(), 4, 64, 128, None, 0, None) == INVALID   # e8m0 4-byte aligned
+    assert g(_p(), _p(), _p(), _p(FAKE + 2), _p(), 4, 64, 128, None, 0, None) == INVALID
+    assert g(_p(), _p(), _p(), _p(), _p(), 4, 64, 96, None, 0, None) == SHAPE             # K % 128
+    # a few tiles on a long K are split: the workspace is required and sized by kind 4
+    need = L.w4a8_gemm_workspace_bytes(128, 5120, 17408, 4)
+    assert need > 0
+    assert g(_p(), _p(), _p(), _p(), _p(), 128, 5120, 17408, None, 0, None) == WORKSPACE
+    assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 4) <= need
+    assert L.w4a8_gemm_workspace_bytes(4096, 34816, 5120, 4) == L.w4a8_gemm_workspace_bytes(128, 34816, 5120, 4)
+
+
 def test_gemm_validation(L):
     g = L.w4a8_mxfp4_gemm
     args = lambda **k: [_p(k.get("x", FAKE)) if k.get("x", FAKE) else None, _p(), _p(), _p(),

@@ -19,16 +19,16 @@ __all__ = [
     "Workspace", "mxfp4_gemm", "int4g128_prepare", "int4g128_gemm", "w4a8_linear",
     "decode_with_plan", "PreparedMXFP4", "mxfp4_prepare", "mxfp4_gemm_prepared",
     "PreparedInt4", "int4g128_prepare_fragments", "int4g128_gemm_prepared",
-    "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4",
+    "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4", "quant_act_mxfp4", "w4a4_gemm_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_SHAPE, ERR_WORKSPACE, ERR_ASYMMETRIC, ERR_HIP = range(6)
 EXP_MODES = {"ocp": 0, "noclip": 1, "mse": 2}
-WEIGHT_MXFP4, WEIGHT_INT4G128, WEIGHT_MXFP4_PREPARED, WEIGHT_INT4G128_PREPARED = 0, 1, 2, 3
+WEIGHT_MXFP4, WEIGHT_INT4G128, WEIGHT_MXFP4_PREPARED, WEIGHT_INT4G128_PREPARED, W4A4_PREPARED = 0, 1, 2, 3, 4
 _KINDS = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128, "prepared": WEIGHT_MXFP4_PREPARED,
-          "int4_prepared": WEIGHT_INT4G128_PREPARED}
+          "int4_prepared": WEIGHT_INT4G128_PREPARED, "w4a4": W4A4_PREPARED}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.w4a8_mxfp4_prepare.restype = _int
         L.w4a8_mxfp4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_mxfp4_gemm_prepared.restype = _int
+        L.w4a8_w4a4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_w4a4_gemm_prepared.restype = _int
         L.w4a8_int4g128_prepared_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_size),
                                                    ctypes.POINTER(_size)]
         L.w4a8_int4g128_prepared_bytes.restype = _int
@@ -488,6 +490,34 @@ def int4g128_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: Prepar
     status = lib().w4a8_int4g128_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
                                                _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
     _check(status, "w4a8_int4g128_gemm_prepared")
+    return out
+
+
+def quant_act_mxfp4(x: torch.Tensor):
+    """W4A4 activations: bf16 [M, K] -> (e2m1 codes [M, K/2] u8, e8m0 [M, K/32] u8),
+    per token and 32-block by the OCP rule (quant_bf16_to_mxfp4, mode "ocp")."""
+    return quant_bf16_to_mxfp4(x, mode="ocp")
+
+
+def w4a4_gemm_prepared(x_fp4: torch.Tensor, x_e8m0: torch.Tensor, w: PreparedMXFP4,
+                       out: torch.Tensor | None = None, workspace: Workspace | None = None) -> torch.Tensor:
+    """out[M, N] bf16 = (e2m1 x * 2^(Ex-127)) @ (e2m1 w * 2^(Ew-127))^T on prepared MXFP4 weights."""
+    _need(x_fp4, "x_fp4", torch.uint8)
+    dev = x_fp4.device
+    _need(x_e8m0, "x_e8m0", torch.uint8, dev)
+    M, K = x_fp4.shape[0], 2 * x_fp4.shape[1]
+    if K != w.K or tuple(x_e8m0.shape) != (M, K // 32):
+        raise ValueError(f"activations [M, K/2] + [M, K/32] with K = {w.K} expected")
+    if not (x_fp4.is_contiguous() and x_e8m0.is_contiguous()):
+        raise ValueError("activations must be contiguous")
+    _check_weight_sizes("prepared", w.w, w.s, w.N, w.K)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, w.N, K, "w4a4", dev)
+    status = lib().w4a8_w4a4_gemm_prepared(_ptr(x_fp4), _ptr(x_e8m0), _ptr(w.w), _ptr(w.s), _ptr(out),
+                                           M, w.N, K, wp, wn, _stream(x_fp4))
+    _check(status, "w4a8_w4a4_gemm_prepared")
     return out
 
 

@@ -130,10 +130,22 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     if (kind == W4A8_WEIGHT_INT4G128 && (K % 128 != 0 || N % 8 != 0)) return 0;
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED && K % 128 != 0) return 0;
     if (kind == W4A8_WEIGHT_INT4G128_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
+    if (kind == W4A8_W4A4_PREPARED && K % 128 != 0) return 0;
     if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED &&
-        kind != W4A8_WEIGHT_INT4G128_PREPARED)
+        kind != W4A8_WEIGHT_INT4G128_PREPARED && kind != W4A8_W4A4_PREPARED)
         return 0;
     size_t need = 0;
+    if (kind == W4A8_W4A4_PREPARED) {
+        // one tile kernel for every M: its shape is constant on each interval
+        // (128j, 128j + 128] and its split workspace grows with M there
+        if (K > kPreparedTiledMaxK) return 0;
+        for (int64_t m = 128; m < M_max && m <= 32768; m += 128) {
+            const size_t b = w4a4_workspace_bytes(m, N, K);
+            if (b > need) need = b;
+        }
+        const size_t b = w4a4_workspace_bytes(M_max, N, K);
+        return b > need ? b : need;
+    }
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED) {
         const bool int4 = kind == W4A8_WEIGHT_INT4G128_PREPARED;
         auto at = [&](int64_t m) -> size_t {
@@ -241,6 +253,20 @@ w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_sc
                                      size_t ws_bytes, void* stream) {
     return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws, ws_bytes,
                          stream, false);
+}
+
+w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t* d_x_fp4, const uint8_t* d_x_e8m0,
+                                    const uint8_t* d_w_prepared, const uint8_t* d_s_prepared, uint16_t* d_out,
+                                    int64_t M, int64_t N, int64_t K, void* d_ws, size_t ws_bytes, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp4, d_x_e8m0, d_w_prepared, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_s_prepared || !aligned(d_s_prepared, 4) || !aligned(d_x_fp4, 16) || !aligned(d_x_e8m0, 4))
+        return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0 || K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    st = check_workspace(w4a4_workspace_bytes(M, N, K), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_prepared_w4a4(d_x_fp4, d_x_e8m0, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws,
+                                           as_stream(stream)));
 }
 
 w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t* h_w_bytes, size_t* h_s_bytes) {

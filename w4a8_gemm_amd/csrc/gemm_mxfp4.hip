@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             t.z = t.z + v.z;
             t.w = t.w + v.w;
         }
-        const float sm = xs[m];
+        const float sm = xs ? xs[m] : 1.0f;   // no token scale: the scales were inside the products
         const uint32_t h0 = f32_to_bf16_rne(sm * t.x) | (f32_to_bf16_rne(sm * t.y) << 16);
         const uint32_t h1 = f32_to_bf16_rne(sm * t.z) | (f32_to_bf16_rne(sm * t.w) << 16);
         *reinterpret_cast<uint2*>(out + i4) = make_uint2(h0, h1);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         if (i >= total) return;
         float t = partials[i];
         for (int j = 1; j < ks; ++j) t = t + partials[(int64_t)j * plane + i];
-        out[i] = (uint16_t)f32_to_bf16_rne(xs[i / N] * t);
+        out[i] = (uint16_t)f32_to_bf16_rne((xs ? xs[i / N] : 1.0f) * t);
     }
 }
 

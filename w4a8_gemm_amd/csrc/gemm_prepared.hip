@@ -668,6 +668,7 @@ struct PfArgs {
     int group_m;                // M tiles per group of the tile order
     int ks, s_per;              // K splits (steps s_per each, a multiple of 4; ks = 1: none)
     float* partials;            // ks > 1: fp32 [ks][M][N], token scale not applied
+    const uint8_t* xe;          // W4A4: activation e8m0 [M, K/32] (x8 then holds e2m1 [M, K/2])
 };
 
 constexpr int kPfThreads = 512;
@@ -1049,7 +1050,7 @@ __device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int
     for (int h = 0; h < S::FM; ++h) {
         const int m = tm * BM + wm * 16 * S::FM + 16 * h + (lane & 15);
         if (m >= a.M) continue;
-        const float sm = a.xs[m];
+        const float sm = a.xs ? a.xs[m] : 1.0f;   // W4A4: no token scale
 #pragma unroll
         for (int f = 0; f < S::FN; ++f) {
             const int n0 = tn * BN + (wn * S::FN + f) * 16 + 4 * g;
@@ -1322,6 +1323,223 @@ hipError_t launch_pfp(const PfArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// W4A4: MXFP4 activations x MXFP4 weights on the fp4 x fp4 block-scaled MFMA
+// (twice the fp8 rate).  The tile kernel of the MXFP4 weights with the
+// activation operand in e2m1 + e8m0: per stage BN/16 weight blocks and BM
+// activation rows of 64 bytes (16-byte chunks XOR-swizzled by (row >> 2) & 3,
+// so that the 16 rows of a fragment read fall in distinct bank groups); per
+// 4-step chunk the weights' e8m0 dwords and BM x 16 bytes of activation e8m0
+// (each row's bytes of the chunk, as stored).  Each product takes both
+// scales: the weight's byte (step % 4) of its dword and, for the activation
+// column of the lane, the byte (lane / 16) of that row's dword for the step.
+// No token scale: the epilogue writes bf16(acc).  Same ring, waits and copy
+// interleave as pf_kernel.
+// ---------------------------------------------------------------------------
+
+template <int BM, int BN>
+struct PaShape {
+    static constexpr int NWM = BM >= 256 ? 4 : 2;
+    static constexpr int NWN = 8 / NWM;
+    static constexpr int FN = BN / (16 * NWN);
+    static constexpr int FM = BM / (16 * NWM);
+    static constexpr int WBYTES = BN / 16 * 1024;          // weight blocks per stage
+    static constexpr int ABYTES = BM * 64;                 // activation rows per stage
+    static constexpr int STAGE = WBYTES + ABYTES;
+    static constexpr int WCP = BN / 128, ACP = BM / 128;   // 1 KiB copies per wave and step
+    static constexpr int DMA_PER_STAGE = WCP + ACP;
+    static constexpr int SW = BN / 16 * 256, SA = BM * 16; // scale bytes per chunk
+    static constexpr int SBYTES = SW + SA;
+    static constexpr int SDMA = (BN / 16) / 8 + BM / 128;  // 256-byte copies per wave and chunk
+    static_assert(BM == 128 || BM == 256, "W4A4 tiles are 128 or 256 rows");
+    static_assert(BN == 256, "W4A4 tiles are 256 wide");
+};
+
+template <int BM, int BN>
+struct PaSrc {
+    i32x4 w, x, sw, sx;
+    uint32_t w_off[BN / 128], x_off[BM / 128], sw_off[BN / 128], sx_off[BM / 128];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void pa_sources(const PfArgs& a, int tm, int tn, int wave, int lane, PaSrc<BM, BN>& src) {
+    const int t0 = tn * (BN / 16);
+    const int64_t wblk = (int64_t)a.s_pad * 1024, sblk = (int64_t)a.c_pad * 256;
+    const int64_t rowb = a.K / 2, srow = a.K / 32;
+    src.w = make_rsrc(a.wt + t0 * wblk, (uint64_t)(a.tiles16 - t0) * wblk);
+    src.sw = make_rsrc(a.st + t0 * sblk, (uint64_t)(a.tiles16 - t0) * sblk);
+    src.x = make_rsrc(a.x8 + (int64_t)tm * BM * rowb, (uint64_t)(a.M - tm * BM) * rowb);
+    src.sx = make_rsrc(a.xe + (int64_t)tm * BM * srow, (uint64_t)(a.M - tm * BM) * srow);
+#pragma unroll
+    for (int i = 0; i < BN / 128; ++i) {
+        // weight blocks and e8m0 dwords of tiles wave + 8 i (clamped to the last tile)
+        const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
+        src.w_off[i] = (uint32_t)(t * wblk) + 16u * lane;
+        src.sw_off[i] = (uint32_t)(t * sblk) + 4u * lane;
+    }
+#pragma unroll
+    for (int i = 0; i < BM / 128; ++i) {
+        // activation rows 16 (wave + 8 i) .. + 15 of the tile, lane -> row
+        // lane / 4 and stored chunk position lane % 4 (swizzled); rows past M
+        // read row M - 1
+        const int r = 16 * (wave + 8 * i) + (lane >> 2);
+        const int m = min(tm * BM + r, a.M - 1) - tm * BM;
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        src.x_off[i] = (uint32_t)m * (uint32_t)rowb + 16u * c;
+        src.sx_off[i] = (uint32_t)m * (uint32_t)srow + 4u * (lane & 3);
+    }
+}
+
+template <int BM, int BN, int J>
+__device__ __forceinline__ void pa_issue_one(const PaSrc<BM, BN>& src, uint8_t* stage, int s, int wave) {
+    using S = PaShape<BM, BN>;
+    if constexpr (J < S::WCP) {
+        lds_dma16(src.w, src.w_off[J], 1024u * s, lds_addr(stage + 1024 * (wave + 8 * J)));
+    } else {
+        constexpr int i = J - S::WCP;
+        lds_dma16(src.x, src.x_off[i], 64u * s, lds_addr(stage + S::WBYTES + 1024 * (wave + 8 * i)));
+    }
+}
+template <int BM, int BN, int J0, int J1>
+__device__ __forceinline__ void pa_issue_range(const PaSrc<BM, BN>& src, uint8_t* stage, int s, int wave) {
+    if constexpr (J0 < J1) {
+        pa_issue_one<BM, BN, J0>(src, stage, s, wave);
+        pa_issue_range<BM, BN, J0 + 1, J1>(src, stage, s, wave);
+    }
+}
+// the weight e8m0 dwords and the activation e8m0 rows of 4-step chunk c
+template <int BM, int BN>
+__device__ __forceinline__ void pa_issue_scales(const PaSrc<BM, BN>& src, uint8_t* sbuf, int c, int wave) {
+    using S = PaShape<BM, BN>;
+#pragma unroll
+    for (int i = 0; i < (BN / 16) / 8; ++i)
+        lds_dma4(src.sw, src.sw_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
+#pragma unroll
+    for (int i = 0; i < BM / 128; ++i)
+        lds_dma4(src.sx, src.sx_off[i], 16u * c, lds_addr(sbuf + S::SW + 256 * (wave + 8 * i)));
+}
+
+template <int BM, int BN, int F>
+__device__ __forceinline__ void pa_group(const uint8_t* wp, const uint8_t* sbuf, int s, int wn, int lane,
+                                         const v8i (&bx)[PaShape<BM, BN>::FM],
+                                         const uint32_t (&scx)[PaShape<BM, BN>::FM], uint4 wa0, uint32_t sc0,
+                                         uint4 wa1, uint32_t sc1,
+                                         v4f (&acc)[PaShape<BM, BN>::FN][PaShape<BM, BN>::FM],
+                                         const PaSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
+    using S = PaShape<BM, BN>;
+    if constexpr (F < S::FN) {
+        const v8i af = frag_fp4(wa0);
+        uint4 wa2 = wa1;
+        uint32_t sc2 = sc1;
+        if constexpr (F + 2 < S::FN) {
+            sc2 = reinterpret_cast<const uint32_t*>(sbuf)[64 * (wn * S::FN + F + 2) + lane];
+            wa2 = *reinterpret_cast<const uint4*>(wp + 1024 * (F + 2));
+        }
+        constexpr int D = S::DMA_PER_STAGE;
+        pa_issue_range<BM, BN, F * D / S::FN, (F + 1) * D / S::FN>(src, nxt, s_nxt, wave);
+        const int scw = (int)(sc0 >> (8 * (s & 3)));
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h)
+            acc[F][h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bx[h], acc[F][h], kFmtFp4, kFmtFp4, 0,
+                                                                         scw, 0, (int)scx[h]);
+        __builtin_amdgcn_sched_barrier(0);
+        pa_group<BM, BN, F + 1>(wp, sbuf, s, wn, lane, bx, scx, wa1, sc1, wa2, sc2, acc, src, nxt, s_nxt, wave);
+    }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void pa_act(const uint8_t* as, const uint8_t* sbuf, int s, int wm, int h, int lane,
+                                       v8i& bx, uint32_t& scx) {
+    using S = PaShape<BM, BN>;
+    const int g = lane >> 4;
+    const int r = wm * 16 * S::FM + 16 * h + (lane & 15);
+    bx = frag_fp4(*reinterpret_cast<const uint4*>(as + 64 * r + 16 * (g ^ ((r >> 2) & 3))));
+    scx = reinterpret_cast<const uint32_t*>(sbuf + S::SW + 16 * r)[s & 3] >> (8 * g);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void pa_compute(const uint8_t* st, int s, int wn, int wm, int lane,
+                                           v4f (&acc)[PaShape<BM, BN>::FN][PaShape<BM, BN>::FM],
+                                           const uint8_t* sbuf, const PaSrc<BM, BN>& src, uint8_t* nxt, int s_nxt,
+                                           int wave) {
+    using S = PaShape<BM, BN>;
+    const uint8_t* as = st + S::WBYTES;
+    const uint8_t* wp = st + 1024 * (wn * S::FN) + 16 * lane;
+    // LDS reads in the order the products need them (as in pf_compute)
+    v8i bx[S::FM];
+    uint32_t scx[S::FM];
+    const uint4 wa0 = *reinterpret_cast<const uint4*>(wp);
+    const uint32_t sc0 = reinterpret_cast<const uint32_t*>(sbuf)[64 * (wn * S::FN) + lane];
+    pa_act<BM, BN>(as, sbuf, s, wm, 0, lane, bx[0], scx[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 1; h < S::FM; ++h) pa_act<BM, BN>(as, sbuf, s, wm, h, lane, bx[h], scx[h]);
+    const uint4 wa1 = *reinterpret_cast<const uint4*>(wp + 1024);
+    const uint32_t sc1 = reinterpret_cast<const uint32_t*>(sbuf)[64 * (wn * S::FN + 1) + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    pa_group<BM, BN, 0>(wp, sbuf, s, wn, lane, bx, scx, wa0, sc0, wa1, sc1, acc, src, nxt, s_nxt, wave);
+}
+
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(kPfThreads) void pfa_kernel(PfArgs a) {
+    using S = PaShape<BM, BN>;
+    static_assert(NS >= 3 && NS <= 5, "ring depth");
+    constexpr int D = S::DMA_PER_STAGE, DS = S::SDMA;
+    constexpr int LDS = kPfBase + NS * S::STAGE + 2 * S::SBYTES;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+    int tm, tn, split;
+    if (!pf_tile(a, tm, tn, split)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % S::NWN, wm = wave / S::NWN;
+
+    v4f acc[S::FN][S::FM];
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+        for (int h = 0; h < S::FM; ++h) acc[f][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int s0 = split * a.s_per, s1 = min(a.K >> 7, s0 + a.s_per);
+    uint8_t* const base = lds + kPfBase;
+    uint8_t* const sbase = base + NS * S::STAGE;
+    PaSrc<BM, BN> src;
+    pa_sources<BM, BN>(a, tm, tn, wave, lane, src);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) {
+        const int u = s0 + i;
+        if ((u & 3) == 0 && u < s1) pa_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        pa_issue_range<BM, BN, 0, D>(src, base + i * S::STAGE, min(u, s1 - 1), wave);
+    }
+    int cur = 0, nxt = (NS - 1) * S::STAGE;
+    pf_args_ready(a);
+    for (int s = s0; s < s1; ++s) {
+        asm volatile("" : "+s"(cur), "+s"(nxt));
+        bool chunk_ahead = false;
+#pragma unroll
+        for (int v = 1; v <= NS - 2; ++v) chunk_ahead |= ((s + v) & 3) == 0 && s + v < s1;
+        if (chunk_ahead) wait_vmcnt<(NS - 2) * D + DS>();
+        else wait_vmcnt<(NS - 2) * D>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int u = s + NS - 1;
+        if ((u & 3) == 0 && u < s1) pa_issue_scales<BM, BN>(src, sbase + ((u >> 2) & 1) * S::SBYTES, u >> 2, wave);
+        pa_compute<BM, BN>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * S::SBYTES, src, base + nxt,
+                           min(u, s1 - 1), wave);
+        cur = cur == (NS - 1) * S::STAGE ? 0 : cur + S::STAGE;
+        nxt = nxt == (NS - 1) * S::STAGE ? 0 : nxt + S::STAGE;
+    }
+    wait_vmcnt<0>();
+    pf_epilogue<BM, BN, kWMx>(a, tm, tn, split, wn, wm, lane, acc);
+}
+
+template <int BM, int BN, int NS>
+hipError_t launch_pfa(const PfArgs& a, hipStream_t stream) {
+    const int total = a.tiles_m * a.tiles_n * a.ks;
+    const int grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL((pfa_kernel<BM, BN, NS>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int NS, int WF>
 hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n * a.ks;
@@ -1538,6 +1756,73 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     }
     if (e != hipSuccess || a.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
+}
+
+// W4A4 tiles: 128 rows up to M = 128, above that 256 rows by the same rounds
+// rule as the MXFP4 tiles; always 256 wide; K split as in tiled_shape when the
+// tiles are few (this also serves decode-sized M).
+static TiledShape w4a4_shape(int64_t M, int64_t N, int64_t K) {
+    auto grid = [&](int bm) {
+        TiledShape t{};
+        t.bm = bm;
+        t.bn = 256;
+        t.tiles_m = (int)((M + bm - 1) / bm);
+        t.tiles_n = (int)((N + 255) / 256);
+        return t;
+    };
+    TiledShape t = grid(128);
+    if (M > 128) {
+        const TiledShape t256 = grid(256);
+        if (9 * tiled_rounds(t256) <= 5 * tiled_rounds(t)) t = t256;
+    }
+    const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n, steps = K / 128;
+    t.ks = 1;
+    t.s_per = (int)steps;
+    if (tiles < 128 && steps >= 16) {
+        int64_t k = 256 / tiles;
+        int64_t per = (steps + k - 1) / k;
+        per = (per + 3) / 4 * 4;
+        if (per < 8) per = 8;
+        k = (steps + per - 1) / per;
+        if (k > 1) {
+            t.ks = (int)k;
+            t.s_per = (int)per;
+        }
+    }
+    return t;
+}
+
+size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const TiledShape t = w4a4_shape(M, N, K);
+    if (t.ks <= 1) return 0;
+    return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                                uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream) {
+    PfArgs a{};
+    a.x8 = x4; a.xe = xe; a.xs = nullptr; a.wt = wt; a.st = st; a.out = out;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.tiles16 = (int)((N + 15) / 16);
+    a.group_m = 8;
+    const TiledShape t = w4a4_shape(M, N, K);
+    a.tiles_m = t.tiles_m;
+    a.tiles_n = t.tiles_n;
+    a.ks = t.ks;
+    a.s_per = t.s_per;
+    if ((int64_t)a.tiles_m * a.tiles_n * a.ks > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    if (a.ks > 1) {
+        if (!ws) return hipErrorInvalidValue;
+        a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles16));
+    }
+    hipError_t e;
+    if (t.bm == 128 && t.bn == 256) e = launch_pfa<128, 256, 5>(a, stream);
+    else if (t.bm == 256 && t.bn == 256) e = launch_pfa<256, 256, 4>(a, stream);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess || a.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, nullptr, M, N, a.ks, out, stream);
 }
 
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {

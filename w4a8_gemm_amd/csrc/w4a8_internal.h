@@ -136,6 +136,10 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 enum class PreparedRoute { Decode, RegStream, Tiled };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
+// W4A4 (MXFP4 activations, prepared MXFP4 weights): the fp4 x fp4 tile kernel
+size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                                uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
 size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                                      uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
