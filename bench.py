@@ -19,7 +19,8 @@ Also reported, each from its own short timed loop (HIP events on the stream the
 kernels run on): the decode GEMM per M, with the roofline taken on the decode
 kernel at M = 1 (one kernel per call there); the prefill GEMM (M = 4096) in
 TFLOP/s; the full-layer requant in GB/s for the three exponent rules, and
-the bf16 / fp8-per-channel -> MXFP4 encoders on the same shape; the
+the bf16 / fp8-per-channel -> MXFP4 encoders on the same shape; W4A4 (MXFP4
+activations) on the same weights, prefill and decode; the
 down_proj decode and prefill; the int4 g128 variant; and the row-major weight
 layout's GEMM for comparison.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same step.
@@ -39,6 +40,7 @@ if HERE not in sys.path:
 METRIC = "W4A8 MXFP4 GEMM: decode HBM GB/s (M≤64), prefill TFLOPS (M=4096); requant GB/s"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 (fp4 x fp4 block-scaled MFMA)
 DECODE_MS = (1, 8, 16, 64)
 COPIES = 4
 
@@ -351,6 +353,26 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
     aq = timer(lambda i: w4.quant_act_fp8_per_token(xb, out=x8, scale=xs), 5)
     res["act_quant_prefill"] = {"M": M, "K": K, "us": round(aq * 1e6, 2),
                                 "gbps": round((M * K * 3 + M * 4) / aq / 1e9, 1)}
+    # W4A4 (MXFP4 activations, OCP rule) on the same prepared weights: the
+    # activation quant and the fp4 x fp4 GEMM, prefill M = 4096 and decode M = 1
+    xa4, xe4 = w4.quant_act_mxfp4(xb)
+    aq4 = timer(lambda i: w4.quant_act_mxfp4(xb), 5)
+    dt4 = _timed_graph(torch, timer, graph_of,
+                       [lambda r=r: w4.w4a4_gemm_prepared(xa4, xe4, pcopies[r], out=o) for r in range(4)], 5)
+    x1b = xb[:1].contiguous()
+    xa1, xe1 = w4.quant_act_mxfp4(x1b)
+    o1a = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    ws4 = w4.Workspace(1, N, K, "w4a4", dev)
+    dt41 = _timed_graph(torch, timer, graph_of,
+                        [lambda r=r: w4.w4a4_gemm_prepared(xa1, xe1, pcopies[r], out=o1a, workspace=ws4)
+                         for r in range(4)], 10)
+    b1 = N * K // 2 + N * K // 32 + K // 2 + K // 32 + 2 * N
+    res["w4a4"] = {"prefill_M4096": {"us": round(dt4 * 1e6, 2), "tflops": round(flops / dt4 / 1e12, 1),
+                                     "frac_of_fp4_peak": round(flops / dt4 / 1e12 / FP4_PEAK_TFLOPS, 4)},
+                   "act_quant_mxfp4_M4096_us": round(aq4 * 1e6, 2),
+                   "decode_M1": {"us": round(dt41 * 1e6, 2), "gbps": round(b1 / dt41 / 1e9, 1)}}
+    log("w4a4", res["w4a4"])
+    del xa4, xe4
     # the row-major weight layout (no repack), for comparison: M = 1 and 4096
     rm = {}
     rcopies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(3)]
