@@ -359,18 +359,19 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
     aq4 = timer(lambda i: w4.quant_act_mxfp4(xb), 5)
     dt4 = _timed_graph(torch, timer, graph_of,
                        [lambda r=r: w4.w4a4_gemm_prepared(xa4, xe4, pcopies[r], out=o) for r in range(4)], 5)
-    x1b = xb[:1].contiguous()
-    xa1, xe1 = w4.quant_act_mxfp4(x1b)
-    o1a = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-    ws4 = w4.Workspace(1, N, K, "w4a4", dev)
-    dt41 = _timed_graph(torch, timer, graph_of,
-                        [lambda r=r: w4.w4a4_gemm_prepared(xa1, xe1, pcopies[r], out=o1a, workspace=ws4)
-                         for r in range(4)], 10)
-    b1 = N * K // 2 + N * K // 32 + K // 2 + K // 32 + 2 * N
     res["w4a4"] = {"prefill_M4096": {"us": round(dt4 * 1e6, 2), "tflops": round(flops / dt4 / 1e12, 1),
                                      "frac_of_fp4_peak": round(flops / dt4 / 1e12 / FP4_PEAK_TFLOPS, 4)},
-                   "act_quant_mxfp4_M4096_us": round(aq4 * 1e6, 2),
-                   "decode_M1": {"us": round(dt41 * 1e6, 2), "gbps": round(b1 / dt41 / 1e9, 1)}}
+                   "act_quant_mxfp4_M4096_us": round(aq4 * 1e6, 2)}
+    # decode-sized M: the split-K decode kernel with fp4 activations
+    ws4 = w4.Workspace(32, N, K, "w4a4", dev)
+    for Md in (1, 32):
+        xad, xed = w4.quant_act_mxfp4(xb[:Md].contiguous())
+        od = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+        dtd = _timed_graph(torch, timer, graph_of,
+                           [lambda r=r: w4.w4a4_gemm_prepared(xad, xed, pcopies[r], out=od, workspace=ws4)
+                            for r in range(4)], 10)
+        bd = N * K // 2 + N * K // 32 + Md * (K // 2 + K // 32) + 2 * Md * N
+        res["w4a4"][f"decode_M{Md}"] = {"us": round(dtd * 1e6, 2), "gbps": round(bd / dtd / 1e9, 1)}
     log("w4a4", res["w4a4"])
     del xa4, xe4
     # the row-major weight layout (no repack), for comparison: M = 1 and 4096

@@ -103,6 +103,12 @@ def test_w4a4_validation(L):
     assert g(_p(), _p(), _p(), _p(), _p(), 128, 5120, 17408, None, 0, None) == WORKSPACE
     assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 4) <= need
     assert L.w4a8_gemm_workspace_bytes(4096, 34816, 5120, 4) == L.w4a8_gemm_workspace_bytes(128, 34816, 5120, 4)
+    # decode-sized M on a narrow layer with a long K: the decode kernel splits
+    # K in 4 (9 of the 34 four-step chunks per split), partials after the
+    # 256-byte-rounded counter header of its 320 row tiles
+    assert L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 4) == 1280 + 4 * 32 * 5120 * 4
+    assert g(_p(), _p(), _p(), _p(), _p(), 32, 5120, 17408, None, 0, None) == WORKSPACE
+    assert L.w4a8_gemm_workspace_bytes(1, 34816, 5120, 4) == 0                  # one split, none needed
 
 
 def test_gemm_validation(L):

@@ -54,12 +54,26 @@ def test_w4a4_ragged(M, N, K):
     _case(f"{M}x{N}x{K}", w["w_packed"], w["w_e8m0"], M, (M, K, 7), spread=10.0)
 
 
-@pytest.mark.parametrize("M", [1, 64, 4096])
+# the split-K decode kernel (M <= 12 on wide layers, <= 32 on narrow ones):
+# one and two 16-row activation tiles, ragged N, K ending inside a 4-step
+# chunk (partial e8m0 chunk), a long K split across workgroups, and the first
+# M past the wide-layer bound (tile kernel)
+W4A4_DECODE = [(12, 20000, 640), (13, 20000, 640), (16, 4100, 2560), (17, 36, 4736), (32, 520, 17408),
+               (3, 1001, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", W4A4_DECODE)
+def test_w4a4_decode(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 11))
+    _case(f"decode {M}x{N}x{K}", w["w_packed"], w["w_e8m0"], M, (M, K, 11), spread=10.0)
+
+
+@pytest.mark.parametrize("M", [1, 8, 12, 13, 64, 4096])
 def test_w4a4_gate_up(gate_up_mx, M):
     _case(f"gate_up M={M}", gate_up_mx[0], gate_up_mx[1], M, (8, M), sample=4096)
 
 
-@pytest.mark.parametrize("M", [1, 4096])
+@pytest.mark.parametrize("M", [1, 16, 32, 4096])
 def test_w4a4_down_proj(M):
     d = synth.down_proj()
     _case(f"down_proj M={M}", d["w_packed"], d["w_e8m0"], M, (9, M), sample=4096)

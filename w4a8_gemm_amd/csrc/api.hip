@@ -136,9 +136,14 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         return 0;
     size_t need = 0;
     if (kind == W4A8_W4A4_PREPARED) {
-        // one tile kernel for every M: its shape is constant on each interval
-        // (128j, 128j + 128] and its split workspace grows with M there
+        // the decode kernel's split for every M it serves; above, one tile
+        // kernel, its shape constant on each interval (128j, 128j + 128] and
+        // its split workspace growing with M there
         if (K > kPreparedTiledMaxK) return 0;
+        for (int64_t m = 1; m <= M_max && m <= kPreparedDecodeMaxM; ++m) {
+            const size_t b = w4a4_workspace_bytes(m, N, K);
+            if (b > need) need = b;
+        }
         for (int64_t m = 128; m < M_max && m <= 32768; m += 128) {
             const size_t b = w4a4_workspace_bytes(m, N, K);
             if (b > need) need = b;

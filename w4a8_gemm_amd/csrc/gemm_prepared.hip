@@ -43,6 +43,13 @@ __device__ __forceinline__ v4f mfma16(v8i a_fp4, v8i b_fp8, v4f c, int scale_a) 
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp8, c, kFmtFp4, kFmtFp8, OPSEL,
                                                             scale_a, 0, kUnitScale);
 }
+// fp4 x fp4: weight scale byte OPSEL of scale_a, activation scale in the low
+// byte of scale_b
+template <int OPSEL>
+__device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp4, c, kFmtFp4, kFmtFp4, OPSEL, scale_a,
+                                                            0, scale_b);
+}
 
 // Weight formats of the fragment-order layout (same 1 KiB block per 16-row
 // tile and 128-wide K step, same lane order; the activation operand is the
@@ -63,11 +70,16 @@ __device__ __forceinline__ v4f mfma16(v8i a_fp4, v8i b_fp8, v4f c, int scale_a) 
 //         scaled by 2 and 8 through the matrix core's e8m0 operand, and the
 //         -8 sum(x) term from a constant fragment (-1 x 8) fed in as the
 //         accumulator input.
-constexpr int kWMx = 0, kWI4 = 1;
+//   kWMxA4  MXFP4 weights as kWMx, multiplied with MXFP4 activations (e2m1
+//         codes and an e8m0 scale per 32 k of a token) on the fp4 x fp4
+//         product; only the split-K decode kernel takes it (the tiled W4A4
+//         kernel is its own).
+constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2;
 
 template <int WF> struct WStep;                               // per-step scale data of a lane
 template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte = step % 4)
 template <> struct WStep<kWI4> { using T = uint2; };         // fp16 scales of its 4 output rows
+template <> struct WStep<kWMxA4> { using T = uint32_t; };
 
 // a lane's activation fragment (B operand) from its LDS row (16-byte chunks
 // XOR-swizzled by sw): MXFP4 pairs with the fp8 operand's own k order, the
@@ -226,8 +238,9 @@ __global__ __launch_bounds__(256) void prep_i4s_kernel(const uint16_t* __restric
 // ---------------------------------------------------------------------------
 
 struct PDecArgs {
-    const uint8_t* x8;
-    const float* xs;
+    const uint8_t* x8;      // fp8 [M, K] (W4A4: e2m1 codes [M, K/2])
+    const float* xs;        // token scales (W4A4: none)
+    const uint8_t* xe;      // W4A4: activation e8m0 [M, K/32]
     const uint4* wt;
     const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
     uint16_t* out;
@@ -249,6 +262,7 @@ template <> struct PChunk<kWI4> {
     uint4 w[4];
     uint2 s[4];          // fp16 row scales of each step
 };
+template <> struct PChunk<kWMxA4> : PChunk<kWMx> {};
 
 // chunk j of this wave's range: 4 weight blocks (sp: MXFP4 dwords of the
 // tile's chunks, lane-indexed; int4 8-byte row-scale quads, (chunk, step, g))
@@ -256,7 +270,7 @@ template <int WF>
 __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, int j, PChunk<WF>& c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
-    if constexpr (WF == kWMx) {
+    if constexpr (WF != kWI4) {
         c.s = reinterpret_cast<const uint32_t*>(sp)[j * 64];
     } else {
 #pragma unroll
@@ -264,10 +278,29 @@ __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, int j
     }
 }
 
+// chunk j's products: activation rows from LDS (xl, stride; W4A4 codes 256 B
+// per chunk, their e8m0 at xel, 16 B per chunk and row)
 template <int MT, int WF>
-__device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int lane, int M, int j,
-                                             const PChunk<WF>& c, v4f (&acc)[MT]) {
+__device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, const uint8_t* xel, int estride,
+                                             int lane, int M, int j, const PChunk<WF>& c, v4f (&acc)[MT]) {
     const int g = lane >> 4;
+    if constexpr (WF == kWMxA4) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(mt * 16 + (lane & 15), M - 1);
+            const uint4 e = *reinterpret_cast<const uint4*>(xel + m * estride + 16 * j);
+            const uint8_t* p = xl + m * stride + 256 * j + 16 * g;
+            const v8i b0 = frag_fp4(*reinterpret_cast<const uint4*>(p));
+            const v8i b1 = frag_fp4(*reinterpret_cast<const uint4*>(p + 64));
+            const v8i b2 = frag_fp4(*reinterpret_cast<const uint4*>(p + 128));
+            const v8i b3 = frag_fp4(*reinterpret_cast<const uint4*>(p + 192));
+            acc[mt] = mfma44<0>(frag_fp4(c.w[0]), b0, acc[mt], (int)c.s, (int)(e.x >> (8 * g)));
+            acc[mt] = mfma44<1>(frag_fp4(c.w[1]), b1, acc[mt], (int)c.s, (int)(e.y >> (8 * g)));
+            acc[mt] = mfma44<2>(frag_fp4(c.w[2]), b2, acc[mt], (int)c.s, (int)(e.z >> (8 * g)));
+            acc[mt] = mfma44<3>(frag_fp4(c.w[3]), b3, acc[mt], (int)c.s, (int)(e.w >> (8 * g)));
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         if constexpr (WF == kWMx) {
@@ -282,7 +315,7 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int 
                 if (u == 2) acc[mt] = mfma16<2>(aw, bx, acc[mt], (int)c.s);
                 if (u == 3) acc[mt] = mfma16<3>(aw, bx, acc[mt], (int)c.s);
             }
-        } else {
+        } else if constexpr (WF == kWI4) {
             const I4Split w = i4_split(c.w[u]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -298,16 +331,38 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, int 
 constexpr int kActBatch = 8;
 
 // activation elements q0 + u * nthreads (u < kActBatch) of the workgroup's
-// [M, kr] slice, 16 bytes each
+// [M, kr] slice, 16 bytes each (16 fp8 values, or 32 e2m1 codes for W4A4)
+template <bool A4>
 __device__ __forceinline__ void pdec_act_load(const PDecArgs& a, int kbase, int per_row, int total, int q0,
                                               int nthreads, uint4 (&v)[kActBatch]) {
+    constexpr int kPer = A4 ? 32 : 16;
+    const int64_t row_bytes = A4 ? a.K / 2 : a.K;
 #pragma unroll
     for (int u = 0; u < kActBatch; ++u) {
         const int q = q0 + u * nthreads;
         const int m = q / per_row, col = q - m * per_row;
-        const int k = kbase + 16 * col;
-        v[u] = (q < total && k < a.K) ? *reinterpret_cast<const uint4*>(a.x8 + (int64_t)m * a.K + k)
-                                      : make_uint4(0, 0, 0, 0);
+        const int k = kbase + kPer * col;
+        v[u] = (q < total && k < a.K)
+                   ? *reinterpret_cast<const uint4*>(a.x8 + (int64_t)m * row_bytes + (A4 ? k / 2 : k))
+                   : make_uint4(0, 0, 0, 0);
+    }
+}
+// W4A4: the e8m0 of the workgroup's chunks -> LDS, 16 bytes per chunk and
+// row (dword u = step u's four 32-wide blocks); blocks past K read as zero.
+// Rows of e8m0 are K/32 bytes, a multiple of 4 but not always of 16: dword loads.
+__device__ __forceinline__ void pdec_e8_load(const PDecArgs& a, int kbase, int nch, uint8_t* xel, int estride,
+                                             int nthreads) {
+    const int total = a.M * nch;
+    for (int q = threadIdx.x; q < total; q += nthreads) {
+        const int m = q / nch, c = q - m * nch;
+        const int k0 = kbase + 512 * c;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.xe + (int64_t)m * (a.K / 32)) + k0 / 128;
+        uint4 v;
+        v.x = k0 < a.K ? src[0] : 0u;
+        v.y = k0 + 128 < a.K ? src[1] : 0u;
+        v.z = k0 + 256 < a.K ? src[2] : 0u;
+        v.w = k0 + 384 < a.K ? src[3] : 0u;
+        *reinterpret_cast<uint4*>(xel + m * estride + 16 * c) = v;
     }
 }
 __device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_row, int total, int q0,
@@ -331,7 +386,12 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int c0 = split * a.c_per;
     const int c1 = min(a.c_pad, c0 + a.c_per);
     const int nch_wg = c1 > c0 ? c1 - c0 : 0;
-    const int kbase = c0 * 512, kr = nch_wg * 512, stride = kr + 16;
+    constexpr bool A4 = WF == kWMxA4;
+    // LDS: activation rows of this K range, 16 bytes apart mod 128 (W4A4:
+    // the code rows, then the e8m0 rows)
+    const int kbase = c0 * 512, kr = nch_wg * 512, stride = (A4 ? kr / 2 : kr) + 16;
+    const int estride = kr / 32 + 16;
+    uint8_t* xel = xl + a.M * stride;
     // this wave's chunks within the workgroup's range: an even share, the
     // first (nch_wg % kw) parts one chunk longer
     const int base_n = nch_wg / a.kw, extra = nch_wg % a.kw;
@@ -348,7 +408,7 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int jb = nch > 0 ? j0 : 0;
     const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
     const void* sp;
-    if constexpr (WF == kWMx)
+    if constexpr (WF != kWI4)
         sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
     else
         sp = reinterpret_cast<const uint2*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 16 + (lane >> 4);
@@ -359,9 +419,9 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     // thread so that their latencies overlap.  The first batch is issued
     // before the weight ring prologue: its LDS writes then wait only for these
     // (L2-resident) loads while the weight loads stay in flight.
-    const int per_row = kr / 16, act_total = a.M * per_row;
+    const int per_row = A4 ? kr / 32 : kr / 16, act_total = a.M * per_row;
     uint4 av[kActBatch];
-    pdec_act_load(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
+    pdec_act_load<A4>(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
     __builtin_amdgcn_sched_barrier(0);
     PChunk<WF> ring[D];
 #pragma unroll
@@ -369,19 +429,22 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
     for (int q0 = threadIdx.x + kActBatch * nthreads; q0 < act_total; q0 += kActBatch * nthreads) {
-        pdec_act_load(a, kbase, per_row, act_total, q0, nthreads, av);
+        pdec_act_load<A4>(a, kbase, per_row, act_total, q0, nthreads, av);
         pdec_act_store(xl, stride, per_row, act_total, q0, nthreads, av);
     }
+    if constexpr (A4) pdec_e8_load(a, kbase, nch_wg, xel, estride, nthreads);
     __syncthreads();
 
-    const uint8_t* xw = xl + 512 * j0;   // this part's first activation column
+    // this part's first activation column
+    const uint8_t* xw = xl + (A4 ? 256 : 512) * j0;
+    const uint8_t* xew = xel + 16 * j0;
     if (active) {
         for (int j = 0; j < nch; j += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 pdec_load<WF>(wp, sp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (j + d < nch) pdec_compute<MT, WF>(xw, stride, lane, a.M, j + d, ring[d], acc);
+                if (j + d < nch) pdec_compute<MT, WF>(xw, stride, xew, estride, lane, a.M, j + d, ring[d], acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -421,7 +484,7 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
         const int m = mt * 16 + (lane & 15);
         if (m >= a.M) continue;
         if (a.ks == 1) {
-            const float sm = a.xs[m];
+            const float sm = A4 ? 1.f : a.xs[m];
             uint16_t* o = a.out + (int64_t)m * a.N + n0;
             if (vec) {
                 const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
@@ -1599,13 +1662,17 @@ hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, 
 
 // Decode plan on prepared weights: plan fields rt = tiles per workgroup, kw =
 // K parts per tile, ks = K splits across workgroups, s_per = chunks per split,
-// u = ring depth.
-static void prepared_shape(int64_t M, int64_t N, int64_t K, int* tw, int* kw, int* ks, int* c_per) {
+// u = ring depth.  LDS per activation row: 512 bytes per 4-step chunk and 16
+// of padding (fp8), or 256 + 16 per chunk and 32 (W4A4 codes and e8m0).
+static int64_t lds_row_chunk(bool a4) { return a4 ? 272 : 512; }
+static int64_t lds_row_pad(bool a4) { return a4 ? 32 : 16; }
+
+static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, int* kw, int* ks, int* c_per) {
     const int64_t tiles = (N + 15) / 16;
     const int64_t c_pad = (K / 128 + 3) / 4;
     const int64_t act_budget = 80 * 1024;          // activations resident in LDS per workgroup
     // K splits across workgroups only when the activations do not fit
-    int64_t c_max = (act_budget / M - 16) / 512;
+    int64_t c_max = (act_budget / M - lds_row_pad(a4)) / lds_row_chunk(a4);
     if (c_max < 1) c_max = 1;
     int64_t s = (c_pad + c_max - 1) / c_max;
     int64_t cp = (c_pad + s - 1) / s;
@@ -1627,12 +1694,12 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, int* tw, int* kw, in
     *c_per = (int)cp;
 }
 
-GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth) {
+GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4) {
     GemmPlan p{};
     p.band = 2;
     p.mt = (int)((M + 15) / 16);
     int tw, kw, ks, cp;
-    prepared_shape(M, N, K, &tw, &kw, &ks, &cp);
+    prepared_shape(M, N, K, a4, &tw, &kw, &ks, &cp);
     if (ks_hint > 0) {   // tuning: ks_hint encodes kw (K parts per tile)
         kw = ks_hint;
         if (kw * tw > 16) kw = 16 / tw;
@@ -1647,8 +1714,8 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth) 
     return p;
 }
 
-size_t prepared_lds_bytes(const GemmPlan& p, int64_t M) {
-    const size_t act = (size_t)(M * ((int64_t)p.s_per * 512 + 16));
+size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4) {
+    const size_t act = (size_t)(M * ((int64_t)p.s_per * lds_row_chunk(a4) + lds_row_pad(a4)));
     const size_t red = (size_t)p.kw * p.rt * p.mt * 64 * 16;
     return act > red ? act : red;
 }
@@ -1792,14 +1859,30 @@ static TiledShape w4a4_shape(int64_t M, int64_t N, int64_t K) {
     return t;
 }
 
+bool w4a4_decode_route(int64_t M, int64_t N) {
+    // the split-K decode kernel for every M it takes (two 16-row activation
+    // tiles), on wide layers too: with fp4 activations its LDS reads and
+    // products cost half of W4A8's (measured on gfx950, gate_up 34816 x 5120:
+    // M = 1 / 12 / 13 / 32: 19.8 / 21.4 / 24.2 / 30.0 us, against 32.5 / 35.2 /
+    // 35.2 / 34.3 us in the 128-row tile kernel)
+    (void)N;
+    return M <= kPreparedDecodeMaxM;
+}
+
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (w4a4_decode_route(M, N)) return plan_workspace_bytes(plan_prepared(M, N, K, 0, 3, true), M, N);
     const TiledShape t = w4a4_shape(M, N, K);
     if (t.ks <= 1) return 0;
     return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
 }
 
+static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream);
+
 hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream) {
+    if (w4a4_decode_route(M, N)) return launch_w4a4_decode(x4, xe, wt, st, out, M, N, K, ws, stream);
     PfArgs a{};
     a.x8 = x4; a.xe = xe; a.xs = nullptr; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -1894,11 +1977,9 @@ hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const u
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
-hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
-                                  const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
-                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4) {
+static PDecArgs pdec_args(const GemmPlan& p, const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
+                          int64_t N, int64_t K, void* ws) {
     PDecArgs a{};
-    a.x8 = x8; a.xs = xs;
     a.wt = reinterpret_cast<const uint4*>(wt);
     a.st = st;
     a.out = out;
@@ -1913,7 +1994,16 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     a.c_per = p.s_per;
     if (p.ks > 1)
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
-    const size_t lds = prepared_lds_bytes(p, M);
+    return a;
+}
+
+hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
+                                  const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4) {
+    if (p.ks > 1 && !ws) return hipErrorInvalidValue;
+    PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
+    a.x8 = x8; a.xs = xs;
+    const size_t lds = prepared_lds_bytes(p, M, false);
     hipError_t e;
     if (int4) {   // ring depth 3 (the tuning entry point's depth 4 is MXFP4 only)
         e = p.mt == 1 ? launch_pdec<1, 3, kWI4>(a, lds, stream) : launch_pdec<2, 3, kWI4>(a, lds, stream);
@@ -1925,6 +2015,23 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     }
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+}
+
+// W4A4 decode: the split-K decode kernel on MXFP4 activations (no token
+// scale: the split-K reduction takes none either)
+static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream) {
+    if (M < 1 || M > kPreparedDecodeMaxM) return hipErrorInvalidValue;
+    const GemmPlan p = plan_prepared(M, N, K, 0, 3, true);
+    if (p.ks > 1 && !ws) return hipErrorInvalidValue;
+    PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
+    a.x8 = x4; a.xe = xe; a.xs = nullptr;
+    const size_t lds = prepared_lds_bytes(p, M, true);
+    const hipError_t e = p.mt == 1 ? launch_pdec<1, 3, kWMxA4>(a, lds, stream)
+                                   : launch_pdec<2, 3, kWMxA4>(a, lds, stream);
+    if (e != hipSuccess || p.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, nullptr, M, N, p.ks, out, stream);
 }
 
 }  // namespace w4a8

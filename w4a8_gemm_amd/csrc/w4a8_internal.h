@@ -123,8 +123,8 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
 void prepared_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64_t K, uint8_t* wt,
                           uint8_t* st, hipStream_t stream);
-GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth);
-size_t prepared_lds_bytes(const GemmPlan& p, int64_t M);
+GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4 = false);
+size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4 = false);
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
                                   int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
@@ -136,7 +136,10 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 enum class PreparedRoute { Decode, RegStream, Tiled };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
-// W4A4 (MXFP4 activations, prepared MXFP4 weights): the fp4 x fp4 tile kernel
+// W4A4 (MXFP4 activations, prepared MXFP4 weights): the split-K decode
+// kernel's W4A4 variant where w4a4_decode_route says so, else the fp4 x fp4
+// tile kernel
+bool w4a4_decode_route(int64_t M, int64_t N);
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
