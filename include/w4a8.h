@@ -220,7 +220,7 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
- *     M >= 1.  Small M runs the split-K decode kernel (M <= 12; M <= 32 on
+ *     M >= 1.  Small M runs the split-K decode kernel (M <= 16; M <= 32 on
  *     narrow layers: fewer than 64 column tiles of 256); larger M the tiled
  *     kernel (64/128/256 x 128/256 output tiles), which splits K across
  *     workgroups when it has fewer than 128 tiles (fp32 partials in the
@@ -313,10 +313,9 @@ w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t *d_x_fp4, const uint8_t *d_x_e
  *     -> d_w_prepared (16-byte aligned), d_s_prepared (8-byte aligned).
  *     Synchronizes `stream` (the check result is read back).
  *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
- *     kernels of w4a8_mxfp4_gemm_prepared (with a register-streamed kernel,
- *     K split across workgroups, for 12 < M <= 32 on wide layers, and 256-row
- *     tiles from 128 of them on) and its workspace rules (size it with
- *     W4A8_WEIGHT_INT4G128_PREPARED).
+ *     kernels of w4a8_mxfp4_gemm_prepared (the split-K decode kernel for
+ *     M <= 32 on every layer, and 256-row tiles from 128 of them on) and its
+ *     workspace rules (size it with W4A8_WEIGHT_INT4G128_PREPARED).
  * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, ASYMMETRIC (prepare), HIP. */
 w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
@@ -338,7 +337,10 @@ w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
  *   u   128-wide K steps per prefetched chunk (1, 2 or 4; 1 if K % 128 != 0),
  *   ks  requested K splits (>= 1; rounded so each split holds whole chunks).
  * Kind MXFP4_PREPARED (prepared weights, M <= 32): rt must be 0, u is the
- * prefetch depth in 512-wide chunks (3 or 4), ks an upper bound on the K splits.
+ * register ring depth in 512-wide chunks (2, 3 or 4), ks the K parts each
+ * weight tile is divided into inside a workgroup (clamped to 16 waves per
+ * workgroup and to the chunks of a split); the K splits across workgroups and
+ * the tiles per workgroup are the entry point's own.
  * w4a8_decode_plan_workspace_bytes: workspace for that plan (0 = none needed, or
  * invalid arguments; rt = 0 selects the prepared-weight plan).  Errors as the
  * GEMMs, INVALID_ARG for a bad plan. */

@@ -239,7 +239,7 @@ def test_mxfp4_prepared_ragged(M, N, K):
     assert err <= GEMM_REL_F, err
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 8, 12, 16, 17, 32])
 def test_mxfp4_prepared_gate_up(gate_up_mx, M):
     x8, s = _acts(M, synth.HIDDEN, (1, M), spread=10.0)
     wp, we = gate_up_mx[:2]
@@ -321,9 +321,11 @@ def test_mxfp4_prepared_tiled_down_proj():
     assert rel_frobenius(got[mi, ni], ref) <= GEMM_REL_F
 
 
-# 256-wide tiles at every tile height (chosen when 256-wide tiles give at least
-# one workgroup per CU): sampled outputs against the oracle
-@pytest.mark.parametrize("M,N,K", [(40, 65600, 256), (100, 65600, 384), (300, 33000, 384)])
+# wide layers: the split-K decode kernel up to M = 16 (one 16-row activation
+# tile, two or four K parts by how many workgroups fit LDS), 256-wide tiles at
+# every tile height above: sampled outputs against the oracle
+@pytest.mark.parametrize("M,N,K", [(13, 65600, 384), (16, 33000, 2560), (17, 33000, 384), (40, 65600, 256),
+                                   (100, 65600, 384), (300, 33000, 384)])
 def test_mxfp4_prepared_tiled_wide(M, N, K):
     w = synth.mxfp4_random(N, K, seed=(M, N, K, 3))
     x8, s = _acts(M, K, (M, K, 3), spread=10.0)
@@ -477,8 +479,8 @@ def _int4_prepared_case(name, q, M, seed, full=False, n_samples=4096, spread=1.0
     assert_gemm_close(sel, ref, name)
 
 
-# every route: split-K decode (M <= 32 narrow, M <= 12 wide), register-streamed
-# (33..64 narrow), tiled 64/128/256-row tiles with 128- and 256-wide columns
+# every route: split-K decode (M <= 32), tiled 64/128/256-row tiles with 128-
+# and 256-wide columns
 INT4_PREPARED = [(1, 64, 128), (3, 136, 1152), (17, 520, 1024), (32, 1000, 4096),
                  (33, 16, 1152), (48, 1000, 4096), (64, 200, 1024),
                  (65, 264, 384), (100, 1000, 1152), (129, 512, 640), (256, 1032, 2048),
@@ -491,9 +493,10 @@ def test_int4_prepared_ragged(M, N, K):
                         full=True, spread=10.0)
 
 
-# wide layers: split-K decode (M <= 12), register-streamed (12 < M <= 32),
+# wide layers: split-K decode (M <= 32; one and two 16-row activation tiles),
 # tiled (64/128/256-row tiles)
-@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (20, 65600, 384), (32, 34816, 5120), (40, 65600, 256),
+@pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (13, 34816, 5120), (20, 65600, 384), (32, 34816, 5120),
+                                   (33, 34816, 640), (40, 65600, 256),
                                    (300, 33000, 384), (600, 45064, 256)])
 def test_int4_prepared_wide(M, N, K):
     _int4_prepared_case(f"wide {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 9)), M,

@@ -155,8 +155,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         const bool int4 = kind == W4A8_WEIGHT_INT4G128_PREPARED;
         auto at = [&](int64_t m) -> size_t {
             const PreparedRoute r = prepared_route(m, N, K, int4);
-            if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 3), m, N);
-            if (r == PreparedRoute::RegStream) return pdr_workspace_bytes(m, N, K);
+            if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
             return K <= kPreparedTiledMaxK ? tiled_workspace_bytes(m, N, K, int4) : 0;
         };
         auto keep = [&](size_t b) { if (b > need) need = b; };
@@ -228,7 +227,7 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (st != W4A8_OK) return st;
     if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
-    // the tiled and register-streamed kernels address activations with 32-bit offsets
+    // the tiled kernel addresses activations with 32-bit offsets
     const PreparedRoute route = prepared_route(M, N, K, int4);
     if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
@@ -237,13 +236,8 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
                                                 as_stream(stream), int4));
-    case PreparedRoute::RegStream:
-        st = check_workspace(pdr_workspace_bytes(M, N, K), d_ws, ws_bytes);
-        if (st != W4A8_OK) return st;
-        return hip_status(launch_prepared_regstream(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
-                                                    as_stream(stream), int4));
     default: {
-        const GemmPlan p = plan_prepared(M, N, K, 0, 3);
+        const GemmPlan p = plan_prepared(M, N, K, 0, 0, false, int4);
         st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
@@ -355,8 +349,8 @@ w4a8_status w4a8_int4g128_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
 size_t w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt, int u, int ks) {
     if (M < 1 || M > kDecodeMaxM || N < 1 || K < 32 || N > kMaxDim || K > kMaxDim) return 0;
     if (rt == 0) {   // prepared weights: u = ring depth
-        if (M > kPreparedDecodeMaxM || K % 128 != 0 || (u != 3 && u != 4) || ks < 1) return 0;
-        return plan_workspace_bytes(plan_prepared(M, N, K, ks, u), M, N);
+        if (M > kPreparedDecodeMaxM || K % 128 != 0 || u < 2 || u > 4 || ks < 1) return 0;
+        return plan_workspace_bytes(plan_prepared(M, N, K, ks, u, false, false), M, N);
     }
     if ((rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1) return 0;
     return plan_workspace_bytes(make_decode_plan(M, N, K, rt, u, ks), M, N);
@@ -369,10 +363,10 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
     w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
-        if (!d_w_scale || !aligned(d_w_scale, 4) || M > kPreparedDecodeMaxM || (u != 3 && u != 4) || ks < 1)
+        if (!d_w_scale || !aligned(d_w_scale, 4) || M > kPreparedDecodeMaxM || u < 2 || u > 4 || ks < 1)
             return W4A8_ERR_INVALID_ARG;
         if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-        const GemmPlan p = plan_prepared(M, N, K, ks, u);
+        const GemmPlan p = plan_prepared(M, N, K, ks, u, false, false);
         st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,

@@ -328,17 +328,15 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, cons
     }
 }
 
-constexpr int kActBatch = 8;
-
-// activation elements q0 + u * nthreads (u < kActBatch) of the workgroup's
-// [M, kr] slice, 16 bytes each (16 fp8 values, or 32 e2m1 codes for W4A4)
-template <bool A4>
+// activation elements q0 + u * nthreads (u < AB) of the workgroup's [M, kr]
+// slice, 16 bytes each (16 fp8 values, or 32 e2m1 codes for W4A4)
+template <bool A4, int AB>
 __device__ __forceinline__ void pdec_act_load(const PDecArgs& a, int kbase, int per_row, int total, int q0,
-                                              int nthreads, uint4 (&v)[kActBatch]) {
+                                              int nthreads, uint4 (&v)[AB]) {
     constexpr int kPer = A4 ? 32 : 16;
     const int64_t row_bytes = A4 ? a.K / 2 : a.K;
 #pragma unroll
-    for (int u = 0; u < kActBatch; ++u) {
+    for (int u = 0; u < AB; ++u) {
         const int q = q0 + u * nthreads;
         const int m = q / per_row, col = q - m * per_row;
         const int k = kbase + kPer * col;
@@ -365,17 +363,18 @@ __device__ __forceinline__ void pdec_e8_load(const PDecArgs& a, int kbase, int n
         *reinterpret_cast<uint4*>(xel + m * estride + 16 * c) = v;
     }
 }
+template <int AB>
 __device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_row, int total, int q0,
-                                               int nthreads, const uint4 (&v)[kActBatch]) {
+                                               int nthreads, const uint4 (&v)[AB]) {
 #pragma unroll
-    for (int u = 0; u < kActBatch; ++u) {
+    for (int u = 0; u < AB; ++u) {
         const int q = q0 + u * nthreads;
         const int m = q / per_row, col = q - m * per_row;
         if (q < total) *reinterpret_cast<uint4*>(xl + m * stride + 16 * col) = v[u];
     }
 }
 
-template <int MT, int D, int WF>
+template <int MT, int D, int WF, int AB>
 __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
@@ -415,21 +414,21 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int last = nch > 0 ? nch - 1 : 0;
 
     // Activations of this workgroup's K range -> LDS (columns >= K read as
-    // zero), 16 bytes per thread and load, in batches of kActBatch loads per
+    // zero), 16 bytes per thread and load, in batches of AB loads per
     // thread so that their latencies overlap.  The first batch is issued
     // before the weight ring prologue: its LDS writes then wait only for these
     // (L2-resident) loads while the weight loads stay in flight.
     const int per_row = A4 ? kr / 32 : kr / 16, act_total = a.M * per_row;
-    uint4 av[kActBatch];
-    pdec_act_load<A4>(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
+    uint4 av[AB];
+    pdec_act_load<A4, AB>(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
     __builtin_amdgcn_sched_barrier(0);
     PChunk<WF> ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) pdec_load<WF>(wp, sp, min(d, last), ring[d]);
     __builtin_amdgcn_sched_barrier(0);
     pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
-    for (int q0 = threadIdx.x + kActBatch * nthreads; q0 < act_total; q0 += kActBatch * nthreads) {
-        pdec_act_load<A4>(a, kbase, per_row, act_total, q0, nthreads, av);
+    for (int q0 = threadIdx.x + AB * nthreads; q0 < act_total; q0 += AB * nthreads) {
+        pdec_act_load<A4, AB>(a, kbase, per_row, act_total, q0, nthreads, av);
         pdec_act_store(xl, stride, per_row, act_total, q0, nthreads, av);
     }
     if constexpr (A4) pdec_e8_load(a, kbase, nch_wg, xel, estride, nthreads);
@@ -506,199 +505,31 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     }
 }
 
-template <int MT, int D, int WF>
+template <int MT, int D, int WF, int AB>
 hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D, WF>,
+        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D, WF, AB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((pdec_kernel<MT, D, WF>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
+    hipLaunchKernelGGL((pdec_kernel<MT, D, WF, AB>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
                        stream, a);
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Decode band with register-streamed weights (int4 weights, 12 < M <= 32 on
-// wide layers)
-//
-// A workgroup of WW waves owns WW 16-row weight tiles, one per wave, and a
-// range of K steps (the whole K, or one of ks splits).  Each wave streams its
-// tile's 1 KiB fragment blocks straight from HBM into a P-deep register ring
-// (P steps ahead), so the weight bytes in flight grow with the number of
-// waves, not with LDS.  Only the activation slice of a step (MT x 16 rows x
-// 128 B) goes through LDS, double-buffered: every wave loads its share into
-// registers together with its weight block, P steps ahead, and writes it one
-// step before use (rows XOR-swizzled in 16-byte chunks, as in the tiled
-// kernels).  Per step j: write the activation slice of step j + 1, read the
-// fragments of step j and multiply, issue the loads of step j + P into the
-// freed ring slot, then lgkmcnt(0) and a barrier (slice j + 1 visible, slice
-// j free).  All loads are ordinary compiler-visible loads, so the compiler's
-// in-order vmcnt bookkeeping is exact.
-// ---------------------------------------------------------------------------
-
-struct PDrArgs {
-    const uint8_t* x8;
-    const float* xs;
-    const uint4* wt;
-    const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
-    uint16_t* out;
-    float* partials;
-    int M, N, K;
-    int s_pad, c_pad;   // padded 128-steps and 4-step chunks per row tile
-    int tiles;          // 16-row tiles
-    int groups;         // workgroups per K split (ceil(tiles / WW))
-    int ks, sp;         // K splits, steps per split
-};
-
-template <int MT, int WW, int WF>
-struct PDrSlot {
-    uint4 w;                                  // weight fragment block of one step
-    typename WStep<WF>::T sc;                 // its scale data (MXFP4: chunk dword, byte = step % 4)
-    uint32_t x[(MT * 8 + WW - 1) / WW];       // this wave's share of the activation slice
-};
-
-template <int MT, int WW, int WF>
-__device__ __forceinline__ void pdr_load(const PDrArgs& a, const uint4* wp, const void* sp, int s, int wave,
-                                         const uint32_t (&xoff)[(MT * 8 + WW - 1) / WW], PDrSlot<MT, WW, WF>& r) {
-    constexpr int U = (MT * 8 + WW - 1) / WW;
-    // activations first: their LDS write, one step before use, then waits only for them
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-        if (wave + WW * i < MT * 8)
-            r.x[i] = *reinterpret_cast<const uint32_t*>(a.x8 + xoff[i] + 128 * (int64_t)s);
-    r.w = wp[(int64_t)s * 64];
-    if constexpr (WF == kWMx) r.sc = reinterpret_cast<const uint32_t*>(sp)[(int64_t)(s >> 2) * 64];
-    else r.sc = reinterpret_cast<const uint2*>(sp)[(int64_t)(s >> 2) * 16 + (s & 3) * 4];
-}
-
-template <int MT, int WW, int WF>
-__device__ __forceinline__ void pdr_write(uint8_t* slice, int wave, int lane, const PDrSlot<MT, WW, WF>& r) {
-    constexpr int U = (MT * 8 + WW - 1) / WW;
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-        if (wave + WW * i < MT * 8)
-            *reinterpret_cast<uint32_t*>(slice + 256 * (wave + WW * i) + 4 * lane) = r.x[i];
-}
-
-template <int MT, int WF>
-__device__ __forceinline__ void pdr_mma(const uint8_t* slice, int lane, const uint4& w, typename WStep<WF>::T sc,
-                                        int s, v4f (&acc)[MT]) {
-    const int g = lane >> 4;
-    if constexpr (WF == kWMx) {
-        const v8i aw = frag_fp4(w);
-        const int scf = (int)(sc >> (8 * (s & 3)));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = 16 * mt + (lane & 15);
-            const v8i bx = act_frag<kWMx>(slice + 128 * r, g, (r >> 1) & 7);
-            acc[mt] = mfma16<0>(aw, bx, acc[mt], scf);
-        }
-    } else {
-        const I4Split ws = i4_split(w);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = 16 * mt + (lane & 15);
-            const v8i bx = act_frag<kWMx>(slice + 128 * r, g, (r >> 1) & 7);
-            acc[mt] = i4_split_mma(ws, bx, acc[mt], sc);
-        }
-    }
-}
-
-template <int MT, int WW, int P, int WF>
-__global__ __launch_bounds__(WW * 64) void pdr_kernel(PDrArgs a) {
-    constexpr int U = (MT * 8 + WW - 1) / WW;
-    constexpr int SLICE = MT * 2048;
-    __shared__ __attribute__((aligned(16))) uint8_t xl[2 * SLICE];
-    const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t_raw = tg * WW + wave;
-    const int t = min(t_raw, a.tiles - 1);           // idle waves stream a valid tile, write nothing
-    const int steps = a.K >> 7;
-    const int s0 = split * a.sp;
-    const int n = min(steps - s0, a.sp);             // >= 1 (host)
-    const uint4* wp = a.wt + (int64_t)t * a.s_pad * 64 + lane;
-    const void* scp;
-    if constexpr (WF == kWMx) scp = reinterpret_cast<const uint32_t*>(a.st) + (int64_t)t * a.c_pad * 64 + lane;
-    else scp = reinterpret_cast<const uint2*>(a.st) + (int64_t)t * a.c_pad * 16 + (lane >> 4);
-    // this wave's activation copy units: unit q covers slice rows 2q, 2q + 1
-    // (256 bytes, 4 per lane); lane -> row 2q + lane / 32, swizzled chunk
-    // position (lane % 32) / 4, byte 4 (lane % 4) of it
-    uint32_t xoff[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-        const int q = wave + WW * i;
-        const int r = 2 * q + (lane >> 5);
-        const int c = ((lane & 31) >> 2) ^ ((r >> 1) & 7);
-        const int m = min(min(r, MT * 16 - 1), a.M - 1);
-        xoff[i] = (uint32_t)m * (uint32_t)a.K + 16u * c + 4u * (lane & 3);
-    }
-
-    v4f acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    PDrSlot<MT, WW, WF> ring[P];
-#pragma unroll
-    for (int d = 0; d < P; ++d) pdr_load<MT, WW, WF>(a, wp, scp, s0 + min(d, n - 1), wave, xoff, ring[d]);
-    pdr_write<MT, WW, WF>(xl, wave, lane, ring[0]);
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-
-    for (int j0 = 0; j0 < n; j0 += P) {
-#pragma unroll
-        for (int d = 0; d < P; ++d) {
-            const int j = j0 + d;
-            // slice j + 1 (its registers are in slot d + 1) into the free buffer
-            if (j + 1 < n) pdr_write<MT, WW, WF>(xl + ((j + 1) & 1) * SLICE, wave, lane, ring[(d + 1) % P]);
-            if (j < n) pdr_mma<MT, WF>(xl + (j & 1) * SLICE, lane, ring[d].w, ring[d].sc, s0 + j, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            // step j + P into the slot just consumed (past the end: the last step again)
-            pdr_load<MT, WW, WF>(a, wp, scp, s0 + min(j + P, n - 1), wave, xoff, ring[d]);
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-        }
-    }
-
-    if (t_raw >= a.tiles) return;
-    const int g = lane >> 4;
-    const int n0 = 16 * t + 4 * g;
-    if (n0 >= a.N) return;
-    const bool vec = (a.N & 3) == 0;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        if (m >= a.M) continue;
-        if (a.ks == 1) {
-            const float sm = a.xs[m];
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
-            if (vec) {
-                const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * acc[mt][2]) | (f32_to_bf16_rne(sm * acc[mt][3]) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-            } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[mt][r]);
-            }
-        } else {
-            float* pp = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-            if (vec) {
-                *reinterpret_cast<float4*>(pp) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-            } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) pp[r] = acc[mt][r];
-            }
-        }
-    }
-}
-
-template <int MT, int WW, int P, int WF>
-hipError_t launch_pdr(const PDrArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((pdr_kernel<MT, WW, P, WF>), dim3(a.groups * a.ks), dim3(WW * 64), 0, stream, a);
-    return hipGetLastError();
+// the plan's kernel instance: activation tiles p.mt, ring depth p.u (2..4),
+// activation loads per thread and batch p.ab (4 or 8)
+template <int WF>
+hipError_t launch_pdec_plan(const GemmPlan& p, const PDecArgs& a, size_t lds, hipStream_t stream) {
+#define W4A8_PDEC(MT, D, AB) \
+    if (p.mt == MT && p.u == D && p.ab == AB) return launch_pdec<MT, D, WF, AB>(a, lds, stream);
+    W4A8_PDEC(1, 2, 4) W4A8_PDEC(1, 2, 8) W4A8_PDEC(1, 3, 4) W4A8_PDEC(1, 3, 8) W4A8_PDEC(1, 4, 4)
+    W4A8_PDEC(1, 4, 8) W4A8_PDEC(2, 2, 4) W4A8_PDEC(2, 2, 8) W4A8_PDEC(2, 3, 4) W4A8_PDEC(2, 3, 8)
+    W4A8_PDEC(2, 4, 4) W4A8_PDEC(2, 4, 8)
+#undef W4A8_PDEC
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -1677,14 +1508,21 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, in
     int64_t s = (c_pad + c_max - 1) / c_max;
     int64_t cp = (c_pad + s - 1) / s;
     s = (c_pad + cp - 1) / cp;
-    // tiles per workgroup: enough activation reuse (the L2 -> LDS copies,
-    // M*K per workgroup, at most about a quarter of the weight bytes), at most 4
-    int64_t t_w = (M + 3) / 4;
-    if (t_w < 1) t_w = 1;
-    if (t_w > 4) t_w = 4;
-    // K parts per tile (measured on gfx950: two for wide layers, four for
-    // narrow ones), at most 16 waves per group
-    int64_t k_w = tiles * s >= 1024 ? 2 : 4;
+    const int64_t act = M * (cp * lds_row_chunk(a4) + lds_row_pad(a4));   // LDS bytes of the slice
+    const bool narrow = (N + 255) / 256 < 64;
+    // tiles per workgroup: 3; 4 above M = 16 (more reuse of the activation
+    // slice); 2 on narrow layers whose K is not split (more workgroups on the
+    // CUs: 160 instead of 107 on a 5120-row layer)
+    int64_t t_w = M > 16 ? 4 : (narrow && s == 1 ? 2 : 3);
+    if (t_w > tiles) t_w = tiles;
+    // K parts per tile: the most of 4, 2, 1 that keeps the launch at about ten
+    // waves per CU (tiles x splits x parts <= 2560); twice that on wide layers
+    // whose activation slice leaves LDS room for two workgroups per CU or
+    // fewer (more resident waves)
+    int64_t k_w = 4;
+    while (k_w > 1 && tiles * s * k_w > 2560) k_w /= 2;
+    if (!narrow && (160 * 1024) / act <= 2) k_w *= 2;
+    if (k_w > 4) k_w = 4;
     if (k_w > cp) k_w = cp;
     if (k_w > 16 / t_w) k_w = 16 / t_w;
     if (k_w < 1) k_w = 1;
@@ -1694,7 +1532,19 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, in
     *c_per = (int)cp;
 }
 
-GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4) {
+// Decode plan: the shape above; ring depth 3 on MXFP4 weights at M <= 4 (and
+// M <= 8 on wide layers), else 2 (int4's split products hold more
+// registers); 4 activation loads per thread and batch when one batch covers
+// the workgroup's slice (fewer registers, more resident waves), else 8.
+// Fitted to a sweep of ring depth x batch x tiles x K parts on gfx950 (graph
+// replays over 8 weight copies; gate_up 34816 x 5120 and down_proj 5120 x
+// 17408, MXFP4 / int4 / W4A4, M from 1 to 32): 1.9 % above the per-shape best
+// on average, against the former fixed plan (one or two tiles per workgroup,
+// two or four K parts, depth 3, batches of 8): gate_up M = 1 / 8 / 12: 19.6 /
+// 22.1 / 22.8 -> 18.7 / 19.7 / 23.8 us (MXFP4); down_proj M = 1 / 8 / 16:
+// 13.5 / 15.7 / 18.3 -> 12.2 / 14.4 / 15.9 us; int4 down_proj M = 1 / 16:
+// 14.7 / 19.6 -> 12.8 / 17.0 us.
+GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4, bool int4) {
     GemmPlan p{};
     p.band = 2;
     p.mt = (int)((M + 15) / 16);
@@ -1705,9 +1555,12 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, 
         if (kw * tw > 16) kw = 16 / tw;
         if (kw > cp) kw = cp;
     }
+    const bool narrow = (N + 255) / 256 < 64;
     p.rt = tw;
     p.kw = kw;
-    p.u = depth;
+    p.u = depth > 0 ? depth : (!int4 && (M <= 4 || (!narrow && M <= 8)) ? 3 : 2);
+    const int64_t per_row = (int64_t)cp * 512 / (a4 ? 32 : 16);   // 16-byte activation loads per row
+    p.ab = M * per_row <= 4 * 64 * (int64_t)tw * kw ? 4 : 8;
     p.ks = ks;
     p.s_per = cp;
     p.tiles = (N + 15) / 16;
@@ -1870,7 +1723,7 @@ bool w4a4_decode_route(int64_t M, int64_t N) {
 }
 
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (w4a4_decode_route(M, N)) return plan_workspace_bytes(plan_prepared(M, N, K, 0, 3, true), M, N);
+    if (w4a4_decode_route(M, N)) return plan_workspace_bytes(plan_prepared(M, N, K, 0, 0, true, false), M, N);
     const TiledShape t = w4a4_shape(M, N, K);
     if (t.ks <= 1) return 0;
     return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
@@ -1914,67 +1767,14 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // workgroups (three quarters of the CUs idle in the tiled kernel)
     const bool narrow = (N + 255) / 256 < 64;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
-    // narrow): on wide layers the split-K decode kernel wins up to M = 12
-    // (M = 12: 23.8 us; at four weight tiles per workgroup, M = 15: 26.5 us,
-    // against about 25 us tiled for any M <= 32); on narrow ones up to M = 32
-    // (even with the tiled kernel split in K: M = 16 / 32 18.4 / 21.1 us vs
-    // 18.8 / 20.9), then the tiled kernel split in K (M = 33 / 64: 21.0 /
-    // 23.8 us vs 25.9 / 28.4 register-streamed; int4 27.1 / 30.4 vs 37.5 / 39.0)
-    if (M <= (narrow ? kPreparedDecodeMaxM : 12)) return PreparedRoute::Decode;
-    // int4 on wide layers: the tiled kernel's 64-row tiles widen each weight
-    // fragment for only four activation fragments (gate_up M = 16 / 32:
-    // 28.9 / 33.4 us register-streamed, 49 / 50 us tiled; M = 64: 63 vs 52 us)
-    if (int4 && M <= 32) return PreparedRoute::RegStream;
+    // narrow), split-K decode kernel against the tiled kernel: narrow layers
+    // M = 16 / 32: 15.9 / 20.2 us vs 18.4 / 21.1 us (tiled split in K); wide
+    // layers M = 12 / 13 / 16: 23.8 / 24.0 / 25.3 us vs 25.7 / 26.2 / 25.9 us,
+    // M = 24: 28.1 vs 26.5 us.  int4 on wide layers, where the tiled kernel's
+    // 64-row tiles widen each weight fragment for only four activation
+    // fragments: M = 16 / 24 / 32: 26.6 / 30.9 / 33.5 us vs 49 / 50 / 50 us.
+    if (M <= (narrow || int4 ? kPreparedDecodeMaxM : 16)) return PreparedRoute::Decode;
     return PreparedRoute::Tiled;
-}
-
-// Register-streamed decode: MT = ceil(M / 16) in {1, 2}, eight waves per
-// workgroup, weights prefetched eight steps ahead; K split across
-// workgroups (fp32 partials + reduction) when the tile groups alone would
-// leave CUs idle.  Returns the split count through *ks_out (workspace:
-// ks * M * N floats after the counter header when ks > 1).
-static void pdr_shape(int64_t M, int64_t N, int64_t K, int* groups, int* ks, int* sp) {
-    const int64_t tiles = (N + 15) / 16, steps = K / 128;
-    const int64_t g = (tiles + 7) / 8;
-    int64_t k = (256 + g - 1) / g;                 // at least one workgroup per CU
-    if (k > steps / 8) k = steps / 8;              // at least 8 steps per split
-    if (k < 1) k = 1;
-    int64_t per = (steps + k - 1) / k;
-    k = (steps + per - 1) / per;                   // no empty split
-    *groups = (int)g;
-    *ks = (int)k;
-    *sp = (int)per;
-}
-
-size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    int g, k, per;
-    pdr_shape(M, N, K, &g, &k, &per);
-    if (k <= 1) return 0;
-    return ws_counter_bytes((N + 15) / 16) + (size_t)k * (size_t)M * (size_t)N * sizeof(float);
-}
-
-hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
-                                     hipStream_t stream, bool int4) {
-    PDrArgs a{};
-    a.x8 = x8; a.xs = xs;
-    a.wt = reinterpret_cast<const uint4*>(wt);
-    a.st = st;
-    a.out = out;
-    a.M = (int)M; a.N = (int)N; a.K = (int)K;
-    a.c_pad = (int)((K / 128 + 3) / 4);
-    a.s_pad = 4 * a.c_pad;
-    a.tiles = (int)((N + 15) / 16);
-    pdr_shape(M, N, K, &a.groups, &a.ks, &a.sp);
-    if (a.ks > 1) {
-        if (!ws) return hipErrorInvalidValue;
-        a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(a.tiles));
-    }
-    // served only for int4 weights on wide layers (prepared_route)
-    if (!int4 || M > 32) return hipErrorInvalidValue;
-    const hipError_t e = M <= 16 ? launch_pdr<1, 8, 8, kWI4>(a, stream) : launch_pdr<2, 8, 8, kWI4>(a, stream);
-    if (e != hipSuccess || a.ks == 1) return e;
-    return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
 static PDecArgs pdec_args(const GemmPlan& p, const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
@@ -2004,15 +1804,7 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
     a.x8 = x8; a.xs = xs;
     const size_t lds = prepared_lds_bytes(p, M, false);
-    hipError_t e;
-    if (int4) {   // ring depth 3 (the tuning entry point's depth 4 is MXFP4 only)
-        e = p.mt == 1 ? launch_pdec<1, 3, kWI4>(a, lds, stream) : launch_pdec<2, 3, kWI4>(a, lds, stream);
-    } else {
-        if (p.mt == 1)
-            e = p.u == 4 ? launch_pdec<1, 4, kWMx>(a, lds, stream) : launch_pdec<1, 3, kWMx>(a, lds, stream);
-        else
-            e = p.u == 4 ? launch_pdec<2, 4, kWMx>(a, lds, stream) : launch_pdec<2, 3, kWMx>(a, lds, stream);
-    }
+    const hipError_t e = int4 ? launch_pdec_plan<kWI4>(p, a, lds, stream) : launch_pdec_plan<kWMx>(p, a, lds, stream);
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
@@ -2023,13 +1815,12 @@ static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const
                                      uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
                                      hipStream_t stream) {
     if (M < 1 || M > kPreparedDecodeMaxM) return hipErrorInvalidValue;
-    const GemmPlan p = plan_prepared(M, N, K, 0, 3, true);
+    const GemmPlan p = plan_prepared(M, N, K, 0, 0, true, false);
     if (p.ks > 1 && !ws) return hipErrorInvalidValue;
     PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
     a.x8 = x4; a.xe = xe; a.xs = nullptr;
     const size_t lds = prepared_lds_bytes(p, M, true);
-    const hipError_t e = p.mt == 1 ? launch_pdec<1, 3, kWMxA4>(a, lds, stream)
-                                   : launch_pdec<2, 3, kWMxA4>(a, lds, stream);
+    const hipError_t e = launch_pdec_plan<kWMxA4>(p, a, lds, stream);
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, nullptr, M, N, p.ks, out, stream);
 }

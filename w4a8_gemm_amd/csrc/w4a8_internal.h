@@ -109,6 +109,7 @@ struct GemmPlan {
     int s_per;      // decode: 128-wide K steps per split
     int64_t tiles;  // decode: row blocks of the weight
     int kw;         // prepared decode: K parts per tile inside a workgroup
+    int ab;         // prepared decode: activation loads per thread and batch (4 or 8)
 };
 GemmPlan make_decode_plan(int64_t M, int64_t N, int64_t K, int rt, int u, int ks_hint);
 GemmPlan plan_mxfp4(int64_t M, int64_t N, int64_t K);
@@ -123,17 +124,17 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
 void prepared_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64_t K, uint8_t* wt,
                           uint8_t* st, hipStream_t stream);
-GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4 = false);
+// split-K decode plan on prepared weights; depth 0 = the plan's own ring depth
+GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4, bool int4);
 size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4 = false);
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
                                   int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
 // Which kernel serves a GEMM on prepared weights: the split-K decode kernel
-// (M <= 12; M <= 32 on narrow layers), the register-streamed kernel (up to
-// M = 64 on layers too narrow for the tiled kernel to fill the CUs, K split
-// across workgroups; int4 weights also up to M = 32 on wide layers), or the
-// tiled kernel (K split across workgroups when its tiles are few).
-enum class PreparedRoute { Decode, RegStream, Tiled };
+// (M <= 32 on narrow layers and for int4 weights, M <= 16 on wide MXFP4
+// layers) or the tiled kernel (K split across workgroups when its tiles are
+// few).
+enum class PreparedRoute { Decode, Tiled };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
 // W4A4 (MXFP4 activations, prepared MXFP4 weights): the split-K decode
@@ -143,10 +144,6 @@ bool w4a4_decode_route(int64_t M, int64_t N);
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
-size_t pdr_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_prepared_regstream(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                                     uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
-                                     hipStream_t stream, bool int4);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
                                  void* ws, hipStream_t stream, bool int4);
