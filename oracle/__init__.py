@@ -323,3 +323,14 @@ def int4_gemm(x8, x_scale, qweight_nk, scales_f16_bits, mi=None, ni=None):
     ref = np.zeros(len(mi), np.float64)
     lib().orc_int4_gemm(x8, xs, qw, sc, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
     return ref
+
+
+def linear_bf16(x_bf16_bits, w_packed, w_e8m0, mi=None, ni=None):
+    """The W4A8 linear on bf16 activations as one operation -- the fp8
+    activation stream that the W4A8 kernel plugin serves ("radiance_nvfp4.py",
+    module docstring; "vllm-radiance (MXFP4)", NVFP4 checkpoints: online
+    requantization to MXFP4): per-token e4m3 quantization of the activations,
+    then the block-scaled GEMM.  The two references above composed, nothing
+    else.  -> fp64 [M, N], or the values at (mi[i], ni[i])."""
+    x8, s = quant_act_fp8(x_bf16_bits)
+    return mxfp4_gemm(x8, s, w_packed, w_e8m0, mi, ni)
