@@ -5,11 +5,14 @@ the merged gate_up projection (N = 2 x 17408, K = 5120, MXFP4 weights
 requantized on the GPU from NVFP4 with one global divisor per partition, then
 repacked once into matrix-core fragment order), for each batch M in
 {1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K] activation, then the
-block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights (split-K
-decode kernel for M <= 32, the tiled kernel for M = 64).  Steps rotate over four
-copies of the weight (95 MB each, 379 MB in all), so no step is served from the
-256 MB Infinity Cache.  Each step is one HIP graph replay (captured once per
-weight copy), so host launch latency is not in the timed region.
+block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights, one call
+of the linear entry point per M (at M = 1 one launch: the quantization runs in
+the split-K decode kernel's prologue; M = 8 the quant kernel and the decode
+kernel; M = 16 and 64 the quant kernel and the tiled kernel).  Steps rotate
+over eight copies of the weight (95 MB each, 758 MB in all, three times the
+256 MB Infinity Cache), so every weight byte of a step comes from HBM.  Each
+step is one HIP graph replay (captured once per weight copy), so host launch
+latency is not in the timed region.
 
 value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
 weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
@@ -42,12 +45,12 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0        # MI355X dense MXFP4 (fp4 x fp4 block-scaled MFMA)
 DECODE_MS = (1, 8, 16, 64)
-COPIES = 4
+COPIES = 8
 
 
 TRAFFIC_RECORD = os.path.join(HERE, "profiles", "pdec_gate_up_m1_traffic.md")
 ROOFLINE_SOURCE = os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip")
-ROOFLINE_GRID = 278528          # pdec_kernel launch at gate_up M = 1: 2176 workgroups x 128 threads
+ROOFLINE_GRID = 139392          # pdec_kernel launch at gate_up M = 1: 726 workgroups x 192 threads
 CALIB_BYTES = 1 << 30           # plain device-to-device copy used to scale the HBM counters
 
 
@@ -179,9 +182,11 @@ def main():
         return
 
     def step(c):
+        # the linear on bf16 activations: the per-token quantization runs in
+        # the decode kernel's prologue where it fits (M = 1), else its own
+        # kernel before the GEMM
         for M in DECODE_MS:
-            w4.quant_act_fp8_per_token(xs_bf16[M], out=x8[M], scale=xsc[M])
-            gemm(M, c)
+            w4.mxfp4_linear_prepared(xs_bf16[M], pcopies[c], out=out[M], workspace=pws, x8=x8[M], xs=xsc[M])
 
     graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(COPIES)]
     step_bytes = sum(decode_bytes(M, N, K) for M in DECODE_MS)
@@ -196,7 +201,7 @@ def main():
 
     # ---------------- decode GEMM kernel durations (roofline) ----------------
     per_m = {}
-    R = 16 * COPIES        # launches per graph: the gap between graph replays (~8 us) spreads thin
+    R = 8 * COPIES         # launches per graph: the gap between graph replays (~8 us) spreads thin
     for M in DECODE_MS:
         def gemms(M=M):
             for r in range(R):
@@ -211,8 +216,8 @@ def main():
     b1 = gemm_bytes(1, N, K)
     achieved = b1 / per_m[1] / 1e9
     roofline = {"bound": "hbm",
-                "kernel": "pdec_kernel<1,3> (fragment-order split-K decode), gate_up M=1; "
-                          "average over graph replays of 64 launches rotating 4 weight copies",
+                "kernel": "pdec_kernel<1,3,0,4> (fragment-order split-K decode), gate_up M=1; "
+                          "average over graph replays of 64 launches rotating 8 weight copies",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic_record(),
                 "bytes_per_launch": b1, "avg_launch_us": round(per_m[1] * 1e6, 3),
@@ -251,7 +256,7 @@ def main():
 def pmc_probe(torch, w4, timer, graph_of, gemm, x8, xsc, xs_bf16, dev, log):
     """Launches for the HBM byte counters: a plain device-to-device copy of
     CALIB_BYTES (read and written once: the counters' scale), then 16
-    launches of the roofline kernel (gate_up, M = 1, rotating the four weight
+    launches of the roofline kernel (gate_up, M = 1, rotating the weight
     copies), each stream-ordered and separate."""
     src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(7)
     dst = torch.empty_like(src)
@@ -369,20 +374,20 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
         od = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
         dtd = _timed_graph(torch, timer, graph_of,
                            [lambda r=r: w4.w4a4_gemm_prepared(xad, xed, pcopies[r], out=od, workspace=ws4)
-                            for r in range(4)], 10)
+                            for r in range(len(pcopies))], 10)
         bd = N * K // 2 + N * K // 32 + Md * (K // 2 + K // 32) + 2 * Md * N
         res["w4a4"][f"decode_M{Md}"] = {"us": round(dtd * 1e6, 2), "gbps": round(bd / dtd / 1e9, 1)}
     log("w4a4", res["w4a4"])
     del xa4, xe4
     # the row-major weight layout (no repack), for comparison: M = 1 and 4096
     rm = {}
-    rcopies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(3)]
+    rcopies = [(wp, we)] + [(wp.clone(), we.clone()) for _ in range(7)]
     rws = w4.Workspace(1, N, K, "mxfp4", dev)
     x1, s1 = w4.quant_act_fp8_per_token(xb[:1].contiguous())
     o1 = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
     dt1 = _timed_graph(torch, timer, graph_of,
                        [lambda r=r: w4.mxfp4_gemm(x1, s1, rcopies[r][0], rcopies[r][1], out=o1, workspace=rws)
-                        for r in range(4)], 10)
+                        for r in range(len(rcopies))], 10)
     rm["decode_M1"] = {"us": round(dt1 * 1e6, 2), "gbps": round(gemm_bytes(1, N, K) / dt1 / 1e9, 1)}
     dtp = _timed_graph(torch, timer, graph_of,
                        [lambda r=r: w4.mxfp4_gemm(x8, xs, rcopies[r][0], rcopies[r][1], out=o) for r in range(2)], 3)

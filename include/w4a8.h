@@ -220,8 +220,9 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
- *     M >= 1.  Small M runs the split-K decode kernel (M <= 16; M <= 32 on
- *     narrow layers: fewer than 64 column tiles of 256); larger M the tiled
+ *     M >= 1.  Small M runs the split-K decode kernel (M <= 32 on narrow
+ *     layers: fewer than 64 column tiles of 256; on wider ones up to M = 16
+ *     while M x K fp8 activations fit about 80 KB of LDS); larger M the tiled
  *     kernel (64/128/256 x 128/256 output tiles), which splits K across
  *     workgroups when it has fewer than 128 tiles (fp32 partials in the
  *     workspace, then a reduction kernel).  A workspace sized
@@ -326,6 +327,37 @@ w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
                                         const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
                                         uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
                                         size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The linear on bf16 activations in one call: per-token fp8 quantization of
+ * x (the rule of w4a8_quant_act_fp8_per_token), then the GEMM on prepared
+ * weights.  Source: "radiance_nvfp4.py", module docstring (the W4A8 kernel
+ * plugin serves an fp8 activation stream) and "vllm-radiance (MXFP4)", NVFP4
+ * checkpoints: online requantization to MXFP4 (fp8 residual stream, norm and
+ * quant epilogues feeding the next linear): the quantization leaves its own
+ * kernel and joins the linear.
+ *   d_x_bf16   device bf16 [M, ldx] (ldx >= K elements, 2-byte aligned)
+ *   d_x_fp8    device output e4m3 codes [M, K], 16-byte aligned
+ *   d_x_scale  device output fp32 token scales [M], 4-byte aligned: the same
+ *              bytes as w4a8_quant_act_fp8_per_token writes
+ *   others as w4a8_mxfp4_gemm_prepared / w4a8_int4g128_gemm_prepared, the
+ *   workspace sized with the same kind.
+ * out equals that GEMM on d_x_fp8 / d_x_scale bit for bit (the same kernel
+ * plan, the same products in the same order).  When the split-K decode
+ * kernel serves the GEMM with K unsplit, x is 16-byte aligned with
+ * ldx % 8 == 0, M <= 16 and the bf16 slice fits one batch of the kernel's
+ * registers (M x K/8 <= 8 x its threads), the quantization runs in that
+ * kernel's prologue: one launch (codes and scales written out by one
+ * workgroup).  Otherwise the quant kernel runs first, then the GEMM.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_mxfp4_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx, const uint8_t *d_w_prepared,
+                                       const uint8_t *d_s_prepared, uint16_t *d_out, int64_t M, int64_t N,
+                                       int64_t K, uint8_t *d_x_fp8, float *d_x_scale, void *d_ws,
+                                       size_t ws_bytes, void *stream);
+w4a8_status w4a8_int4g128_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx, const uint8_t *d_w_prepared,
+                                          const uint8_t *d_s_prepared, uint16_t *d_out, int64_t M, int64_t N,
+                                          int64_t K, uint8_t *d_x_fp8, float *d_x_scale, void *d_ws,
+                                          size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Decode band with an explicit plan, for tile-size sweeps (the two GEMM entry

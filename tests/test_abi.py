@@ -225,3 +225,19 @@ def test_binding_rejects_mismatched_weight_sizes(L):
         binding._check_weight_sizes("mxfp4", Shape(N, K // 2), Shape(N, K // 16), N, K)
     with pytest.raises(ValueError):
         binding._check_weight_sizes("int4", Shape(N, K // 8), Shape(N, K // 128), N, K)
+
+
+def test_linear_validation(L):
+    for f in (L.w4a8_mxfp4_linear_prepared, L.w4a8_int4g128_linear_prepared):
+        ok = lambda **k: [k.get("x", _p()), k.get("ldx", 256), _p(), _p(), _p(), 4, 64, k.get("K", 256),
+                          k.get("x8", _p()), k.get("xs", _p()), None, 0, None]
+        assert f(*ok(x=None)) == INVALID
+        assert f(*ok(x=_p(FAKE + 1))) == INVALID                  # bf16 2-byte aligned
+        assert f(*ok(ldx=128)) == SHAPE                           # ldx < K
+        assert f(*ok(K=200, ldx=200)) == SHAPE                    # K % 128
+        assert f(*ok(x8=None)) == INVALID                         # codes are an output
+        assert f(*ok(x8=_p(FAKE + 8))) == INVALID                 # 16-byte aligned codes
+        assert f(*ok(xs=_p(FAKE + 2))) == INVALID
+    # the int4 form keeps N % 8
+    a = [_p(), 256, _p(), _p(), _p(), 4, 60, 256, _p(), _p(), None, 0, None]
+    assert L.w4a8_int4g128_linear_prepared(*a) == SHAPE

@@ -20,6 +20,7 @@ __all__ = [
     "decode_with_plan", "PreparedMXFP4", "mxfp4_prepare", "mxfp4_gemm_prepared",
     "PreparedInt4", "int4g128_prepare_fragments", "int4g128_gemm_prepared",
     "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4", "quant_act_mxfp4", "w4a4_gemm_prepared",
+    "mxfp4_linear_prepared", "int4g128_linear_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.w4a8_mxfp4_prepare.restype = _int
         L.w4a8_mxfp4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_mxfp4_gemm_prepared.restype = _int
+        for f in ("w4a8_mxfp4_linear_prepared", "w4a8_int4g128_linear_prepared"):
+            getattr(L, f).argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _size, _vp]
+            getattr(L, f).restype = _int
         L.w4a8_w4a4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_w4a4_gemm_prepared.restype = _int
         L.w4a8_int4g128_prepared_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_size),
@@ -491,6 +495,49 @@ def int4g128_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: Prepar
                                                _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
     _check(status, "w4a8_int4g128_gemm_prepared")
     return out
+
+
+def _linear_prepared(fn, kind, x, w, out, workspace, x8, xs):
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dev = x.device
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activation K {K} != weight K {w.K}")
+    _check_weight_sizes(kind, w.w, w.s, w.N, w.K)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _need(x8, "x8", torch.uint8, dev)
+    _need(xs, "xs", torch.float32, dev)
+    if tuple(x8.shape) != (M, K) or tuple(xs.shape) != (M,) or tuple(out.shape) != (M, w.N):
+        raise ValueError("out [M, N], x8 [M, K], xs [M] expected")
+    wp, wn, _keep = _ws_args(workspace, M, w.N, K, kind, dev)
+    status = getattr(lib(), fn)(_ptr(x), x.stride(0), _ptr(w.w), _ptr(w.s), _ptr(out), M, w.N, K,
+                                _ptr(x8), _ptr(xs), wp, wn, _stream(x))
+    _check(status, fn)
+    return out, x8, xs
+
+
+def mxfp4_linear_prepared(x: torch.Tensor, w: PreparedMXFP4, out: torch.Tensor | None = None,
+                          workspace: Workspace | None = None, x8: torch.Tensor | None = None,
+                          xs: torch.Tensor | None = None):
+    """The linear on bf16 activations [M, K] (rows may be strided): per-token fp8
+    quantization fused with the GEMM on prepared MXFP4 weights ->
+    (out bf16 [M, N], e4m3 codes [M, K], token scales [M])."""
+    return _linear_prepared("w4a8_mxfp4_linear_prepared", "prepared", x, w, out, workspace, x8, xs)
+
+
+def int4g128_linear_prepared(x: torch.Tensor, w: PreparedInt4, out: torch.Tensor | None = None,
+                             workspace: Workspace | None = None, x8: torch.Tensor | None = None,
+                             xs: torch.Tensor | None = None):
+    """As mxfp4_linear_prepared, on fragment-order int4 g128 weights."""
+    return _linear_prepared("w4a8_int4g128_linear_prepared", "int4_prepared", x, w, out, workspace, x8, xs)
 
 
 def quant_act_mxfp4(x: torch.Tensor):

@@ -246,6 +246,43 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     }
 }
 
+// the linear on bf16 activations: fused per-token quant in the decode kernel
+// where the plan allows it, else the quant kernel then gemm_prepared
+static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const uint8_t* d_w, const uint8_t* d_s,
+                                   uint16_t* d_out, int64_t M, int64_t N, int64_t K, uint8_t* d_x_fp8,
+                                   float* d_x_scale, void* d_ws, size_t ws_bytes, void* stream, bool int4) {
+    if (!d_x_bf16 || !aligned(d_x_bf16, 2)) return W4A8_ERR_INVALID_ARG;
+    if (ldx < K || ldx > kMaxDim) return ldx < K ? W4A8_ERR_UNSUPPORTED_SHAPE : W4A8_ERR_INVALID_ARG;
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    GemmPlan p{};
+    const bool vec = aligned(d_x_bf16, 16) && ldx % 8 == 0;
+    if (vec && prepared_route(M, N, K, int4) == PreparedRoute::Decode && plan_prepared_fused(M, N, K, int4, &p))
+        return hip_status(launch_prepared_linear_fused(p, d_x_bf16, ldx, d_w, d_s, d_out, M, N, K, d_x_fp8,
+                                                       d_x_scale, as_stream(stream), int4));
+    st = hip_status(launch_act_quant(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, as_stream(stream)));
+    if (st != W4A8_OK) return st;
+    return gemm_prepared(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws, ws_bytes, stream, int4);
+}
+
+w4a8_status w4a8_mxfp4_linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const uint8_t* d_w_prepared,
+                                       const uint8_t* d_s_prepared, uint16_t* d_out, int64_t M, int64_t N,
+                                       int64_t K, uint8_t* d_x_fp8, float* d_x_scale, void* d_ws,
+                                       size_t ws_bytes, void* stream) {
+    return linear_prepared(d_x_bf16, ldx, d_w_prepared, d_s_prepared, d_out, M, N, K, d_x_fp8, d_x_scale, d_ws,
+                           ws_bytes, stream, false);
+}
+
+w4a8_status w4a8_int4g128_linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const uint8_t* d_w_prepared,
+                                          const uint8_t* d_s_prepared, uint16_t* d_out, int64_t M, int64_t N,
+                                          int64_t K, uint8_t* d_x_fp8, float* d_x_scale, void* d_ws,
+                                          size_t ws_bytes, void* stream) {
+    return linear_prepared(d_x_bf16, ldx, d_w_prepared, d_s_prepared, d_out, M, N, K, d_x_fp8, d_x_scale, d_ws,
+                           ws_bytes, stream, true);
+}
+
 w4a8_status w4a8_mxfp4_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
                                      const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
                                      uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,

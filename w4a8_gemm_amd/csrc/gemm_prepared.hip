@@ -241,6 +241,10 @@ struct PDecArgs {
     const uint8_t* x8;      // fp8 [M, K] (W4A4: e2m1 codes [M, K/2])
     const float* xs;        // token scales (W4A4: none)
     const uint8_t* xe;      // W4A4: activation e8m0 [M, K/32]
+    const uint16_t* xb;     // fused quant: bf16 activations, row stride ldx elements
+    int64_t ldx;
+    uint8_t* x8_out;        // fused quant: e4m3 codes [M, K] and token scales [M] written
+    float* xs_out;          // by workgroup 0
     const uint4* wt;
     const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
     uint16_t* out;
@@ -348,6 +352,76 @@ __device__ __forceinline__ void pdec_act_load(const PDecArgs& a, int kbase, int 
 // W4A4: the e8m0 of the workgroup's chunks -> LDS, 16 bytes per chunk and
 // row (dword u = step u's four 32-wide blocks); blocks past K read as zero.
 // Rows of e8m0 are K/32 bytes, a multiple of 4 but not always of 16: dword loads.
+// Fused quant: the bf16 activations of the workgroup's (whole) K range,
+// items of 8 values (16 bytes), q0 + u * nthreads for u < AB; items past K
+// read as zero
+// (every load issued, from an in-range address, and the out-of-range items
+// zeroed afterwards: loads under branches leave the compiler's wait counts
+// conservative, and the first use would then wait for the weight loads
+// issued behind them)
+template <int AB>
+__device__ __forceinline__ void pdec_bf16_load(const PDecArgs& a, int per_row, int total, int q0, int nthreads,
+                                               uint4 (&v)[AB]) {
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+        const int q = q0 + u * nthreads;
+        const int qc = min(q, total - 1);
+        const int m = qc / per_row, k = 8 * (qc - m * per_row);
+        const uint4 t = *reinterpret_cast<const uint4*>(a.xb + (int64_t)m * a.ldx + min(k, a.K - 8));
+        const bool ok = q < total && k < a.K;
+        v[u] = make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+    }
+}
+
+// Fused quant: per-token e4m3 quantization of the loaded items into the LDS
+// activation rows, by the rule of the standalone quant kernel (s = amax / 448,
+// 1 for a zero row; code = e4m3 of x / s, nearest even, saturating): the row
+// amax as the largest fp32 bit pattern of the items' non-negative maxima
+// (fmaxf drops NaN as the standalone kernel's reduction does), reduced across
+// the wave -- a row is a multiple of 64 items and a wave's 64 items of one
+// batch are consecutive, so they share a row and are all valid or all past
+// the end -- then one LDS max atomic per wave and batch; then every value
+// divided by its row's scale.  amax_u: M words of LDS.
+template <int AB>
+__device__ __forceinline__ void pdec_fused_quant(const PDecArgs& a, uint8_t* xl, int stride, int per_row, int total,
+                                                 int nthreads, const uint4 (&v)[AB], uint32_t* amax_u) {
+    if ((int)threadIdx.x < a.M) amax_u[threadIdx.x] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+        const int q = threadIdx.x + u * nthreads;
+        if (q - (int)(threadIdx.x & 63) >= total) continue;   // the wave's first item: uniform
+        const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mx = fmaxf(mx, fabsf(bf16_to_f32(d[i] & 0xFFFFu)));
+            mx = fmaxf(mx, fabsf(bf16_to_f32(d[i] >> 16)));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if ((threadIdx.x & 63) == 0) atomicMax(&amax_u[q / per_row], __float_as_uint(mx));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < AB; ++u) {
+        const int q = threadIdx.x + u * nthreads;
+        if (q >= total) continue;
+        const int m = q / per_row, col = q - m * per_row;
+        const float amax = __uint_as_float(amax_u[m]);
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = f32_to_e4m3_rne_sat(bf16_to_f32(d[i] & 0xFFFFu) / sc);
+            const uint32_t hi = f32_to_e4m3_rne_sat(bf16_to_f32(d[i] >> 16) / sc);
+            o[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+        }
+        *reinterpret_cast<uint2*>(xl + m * stride + 8 * col) = make_uint2(o[0], o[1]);
+    }
+}
+
 __device__ __forceinline__ void pdec_e8_load(const PDecArgs& a, int kbase, int nch, uint8_t* xel, int estride,
                                              int nthreads) {
     const int total = a.M * nch;
@@ -374,7 +448,7 @@ __device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_
     }
 }
 
-template <int MT, int D, int WF, int AB>
+template <int MT, int D, int WF, int AB, bool FQ>
 __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
@@ -418,21 +492,53 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     // thread so that their latencies overlap.  The first batch is issued
     // before the weight ring prologue: its LDS writes then wait only for these
     // (L2-resident) loads while the weight loads stay in flight.
-    const int per_row = A4 ? kr / 32 : kr / 16, act_total = a.M * per_row;
+    // (fused quant: the bf16 activations instead, all in one batch, and K
+    // not split across workgroups)
+    const int per_row = FQ ? kr / 8 : (A4 ? kr / 32 : kr / 16), act_total = a.M * per_row;
     uint4 av[AB];
-    pdec_act_load<A4, AB>(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
+    if constexpr (FQ)
+        pdec_bf16_load<AB>(a, per_row, act_total, threadIdx.x, nthreads, av);
+    else
+        pdec_act_load<A4, AB>(a, kbase, per_row, act_total, threadIdx.x, nthreads, av);
     __builtin_amdgcn_sched_barrier(0);
     PChunk<WF> ring[D];
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) pdec_load<WF>(wp, sp, min(d, last), ring[d]);
     __builtin_amdgcn_sched_barrier(0);
-    pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
-    for (int q0 = threadIdx.x + AB * nthreads; q0 < act_total; q0 += AB * nthreads) {
-        pdec_act_load<A4, AB>(a, kbase, per_row, act_total, q0, nthreads, av);
-        pdec_act_store(xl, stride, per_row, act_total, q0, nthreads, av);
+    [[maybe_unused]] uint32_t* amax_u = reinterpret_cast<uint32_t*>(xl + a.M * stride);   // fused quant: row amax
+    if constexpr (FQ) {
+        pdec_fused_quant<AB>(a, xl, stride, per_row, act_total, nthreads, av, amax_u);
+    } else {
+        pdec_act_store(xl, stride, per_row, act_total, threadIdx.x, nthreads, av);
+        for (int q0 = threadIdx.x + AB * nthreads; q0 < act_total; q0 += AB * nthreads) {
+            pdec_act_load<A4, AB>(a, kbase, per_row, act_total, q0, nthreads, av);
+            pdec_act_store(xl, stride, per_row, act_total, q0, nthreads, av);
+        }
     }
     if constexpr (A4) pdec_e8_load(a, kbase, nch_wg, xel, estride, nthreads);
     __syncthreads();
+    // fused quant: this lane's token scales (the reduction below reuses the
+    // LDS), and the codes and scales written out once, by workgroup 0
+    [[maybe_unused]] float sm_fq[MT];
+    if constexpr (FQ) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float amax = __uint_as_float(amax_u[min(mt * 16 + (lane & 15), a.M - 1)]);
+            sm_fq[mt] = amax > 0.0f ? amax / 448.0f : 1.0f;
+        }
+        if (blockIdx.x == 0) {
+            const int row16 = a.K / 16;
+            for (int q = threadIdx.x; q < a.M * row16; q += nthreads) {
+                const int m = q / row16, c = q - m * row16;
+                *reinterpret_cast<uint4*>(a.x8_out + (int64_t)m * a.K + 16 * c) =
+                    *reinterpret_cast<const uint4*>(xl + m * stride + 16 * c);
+            }
+            if ((int)threadIdx.x < a.M) {
+                const float amax = __uint_as_float(amax_u[threadIdx.x]);
+                a.xs_out[threadIdx.x] = amax > 0.0f ? amax / 448.0f : 1.0f;
+            }
+        }
+    }
 
     // this part's first activation column
     const uint8_t* xw = xl + (A4 ? 256 : 512) * j0;
@@ -483,7 +589,10 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
         const int m = mt * 16 + (lane & 15);
         if (m >= a.M) continue;
         if (a.ks == 1) {
-            const float sm = A4 ? 1.f : a.xs[m];
+            float sm;
+            if constexpr (A4) sm = 1.f;
+            else if constexpr (FQ) sm = sm_fq[mt];
+            else sm = a.xs[m];
             uint16_t* o = a.out + (int64_t)m * a.N + n0;
             if (vec) {
                 const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
@@ -505,16 +614,16 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     }
 }
 
-template <int MT, int D, int WF, int AB>
+template <int MT, int D, int WF, int AB, bool FQ = false>
 hipError_t launch_pdec(const PDecArgs& a, size_t lds, hipStream_t stream) {
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D, WF, AB>,
+        hipError_t e = hipFuncSetAttribute((const void*)pdec_kernel<MT, D, WF, AB, FQ>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((pdec_kernel<MT, D, WF, AB>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
+    hipLaunchKernelGGL((pdec_kernel<MT, D, WF, AB, FQ>), dim3(a.groups * a.ks), dim3(64 * a.tw * a.kw), lds,
                        stream, a);
     return hipGetLastError();
 }
@@ -529,6 +638,17 @@ hipError_t launch_pdec_plan(const GemmPlan& p, const PDecArgs& a, size_t lds, hi
     W4A8_PDEC(1, 4, 8) W4A8_PDEC(2, 2, 4) W4A8_PDEC(2, 2, 8) W4A8_PDEC(2, 3, 4) W4A8_PDEC(2, 3, 8)
     W4A8_PDEC(2, 4, 4) W4A8_PDEC(2, 4, 8)
 #undef W4A8_PDEC
+    return hipErrorInvalidValue;
+}
+
+// fused-quant instances: one 16-row activation tile, the bf16 slice in one
+// batch of 4 loads per thread (ring depth 2 or 3) or 8 (depth 2)
+template <int WF>
+hipError_t launch_pdec_fused(const GemmPlan& p, const PDecArgs& a, size_t lds, hipStream_t stream) {
+    if (p.mt != 1 || p.ks != 1) return hipErrorInvalidValue;
+    if (p.u == 2 && p.ab == 4) return launch_pdec<1, 2, WF, 4, true>(a, lds, stream);
+    if (p.u == 2 && p.ab == 8) return launch_pdec<1, 2, WF, 8, true>(a, lds, stream);
+    if (p.u == 3 && p.ab == 4) return launch_pdec<1, 3, WF, 4, true>(a, lds, stream);
     return hipErrorInvalidValue;
 }
 
@@ -1498,7 +1618,8 @@ hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, 
 static int64_t lds_row_chunk(bool a4) { return a4 ? 272 : 512; }
 static int64_t lds_row_pad(bool a4) { return a4 ? 32 : 16; }
 
-static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, int* kw, int* ks, int* c_per) {
+static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, bool int4, int* tw, int* kw, int* ks,
+                           int* c_per, bool* lds_bound) {
     const int64_t tiles = (N + 15) / 16;
     const int64_t c_pad = (K / 128 + 3) / 4;
     const int64_t act_budget = 80 * 1024;          // activations resident in LDS per workgroup
@@ -1516,12 +1637,15 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, in
     int64_t t_w = M > 16 ? 4 : (narrow && s == 1 ? 2 : 3);
     if (t_w > tiles) t_w = tiles;
     // K parts per tile: the most of 4, 2, 1 that keeps the launch at about ten
-    // waves per CU (tiles x splits x parts <= 2560); twice that on wide layers
-    // whose activation slice leaves LDS room for two workgroups per CU or
-    // fewer (more resident waves)
+    // waves per CU (tiles x splits x parts <= 2560).  On wide layers whose
+    // activation slice leaves LDS room for two workgroups per CU or fewer,
+    // more waves per workgroup: four parts for one 16-row activation tile of
+    // fp8 or fp4 (with the small activation batch, so that two such
+    // workgroups also fit the registers), else twice the parts
     int64_t k_w = 4;
     while (k_w > 1 && tiles * s * k_w > 2560) k_w /= 2;
-    if (!narrow && (160 * 1024) / act <= 2) k_w *= 2;
+    *lds_bound = !narrow && (160 * 1024) / act <= 2 && M <= 16 && !int4;
+    if (!narrow && (160 * 1024) / act <= 2) k_w = *lds_bound ? 4 : 2 * k_w;
     if (k_w > 4) k_w = 4;
     if (k_w > cp) k_w = cp;
     if (k_w > 16 / t_w) k_w = 16 / t_w;
@@ -1535,7 +1659,8 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, int* tw, in
 // Decode plan: the shape above; ring depth 3 on MXFP4 weights at M <= 4 (and
 // M <= 8 on wide layers), else 2 (int4's split products hold more
 // registers); 4 activation loads per thread and batch when one batch covers
-// the workgroup's slice (fewer registers, more resident waves), else 8.
+// the workgroup's slice or LDS bounds the workgroups per CU (fewer
+// registers, more resident waves), else 8.
 // Fitted to a sweep of ring depth x batch x tiles x K parts on gfx950 (graph
 // replays over 8 weight copies; gate_up 34816 x 5120 and down_proj 5120 x
 // 17408, MXFP4 / int4 / W4A4, M from 1 to 32): 1.9 % above the per-shape best
@@ -1549,7 +1674,8 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, 
     p.band = 2;
     p.mt = (int)((M + 15) / 16);
     int tw, kw, ks, cp;
-    prepared_shape(M, N, K, a4, &tw, &kw, &ks, &cp);
+    bool lds_bound;
+    prepared_shape(M, N, K, a4, int4, &tw, &kw, &ks, &cp, &lds_bound);
     if (ks_hint > 0) {   // tuning: ks_hint encodes kw (K parts per tile)
         kw = ks_hint;
         if (kw * tw > 16) kw = 16 / tw;
@@ -1560,7 +1686,7 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, 
     p.kw = kw;
     p.u = depth > 0 ? depth : (!int4 && (M <= 4 || (!narrow && M <= 8)) ? 3 : 2);
     const int64_t per_row = (int64_t)cp * 512 / (a4 ? 32 : 16);   // 16-byte activation loads per row
-    p.ab = M * per_row <= 4 * 64 * (int64_t)tw * kw ? 4 : 8;
+    p.ab = lds_bound || M * per_row <= 4 * 64 * (int64_t)tw * kw ? 4 : 8;
     p.ks = ks;
     p.s_per = cp;
     p.tiles = (N + 15) / 16;
@@ -1762,19 +1888,24 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
 }
 
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
-    (void)K;
     // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
     // workgroups (three quarters of the CUs idle in the tiled kernel)
     const bool narrow = (N + 255) / 256 < 64;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
-    // M = 16 / 32: 15.9 / 20.2 us vs 18.4 / 21.1 us (tiled split in K); wide
-    // layers M = 12 / 13 / 16: 23.8 / 24.0 / 25.3 us vs 25.7 / 26.2 / 25.9 us,
-    // M = 24: 28.1 vs 26.5 us.  int4 on wide layers, where the tiled kernel's
-    // 64-row tiles widen each weight fragment for only four activation
-    // fragments: M = 16 / 24 / 32: 26.6 / 30.9 / 33.5 us vs 49 / 50 / 50 us.
-    if (M <= (narrow || int4 ? kPreparedDecodeMaxM : 16)) return PreparedRoute::Decode;
-    return PreparedRoute::Tiled;
+    // M = 16 / 32: 15.9 / 20.2 us vs 18.4 / 21.1 us (tiled split in K); int4
+    // on wide layers, where the tiled kernel's 64-row tiles widen each weight
+    // fragment for only four activation fragments: M = 16 / 24 / 32: 26.6 /
+    // 30.9 / 33.5 us vs 49 / 50 / 50 us
+    if (narrow || int4) return M <= kPreparedDecodeMaxM ? PreparedRoute::Decode : PreparedRoute::Tiled;
+    // wide MXFP4 layers: the decode kernel while the activation slice of all
+    // of K fits one workgroup's LDS (a K split adds a reduction pass): gate_up
+    // M = 12 / 15: 22.4 / 22.7 us vs 24.5 / 24.7 us tiled; M = 16 (split in
+    // two): 25.3 vs 24.5 us
+    int tw, kw, ks, cp;
+    bool lds_bound;
+    prepared_shape(M, N, K, false, false, &tw, &kw, &ks, &cp, &lds_bound);
+    return M <= 16 && ks == 1 ? PreparedRoute::Decode : PreparedRoute::Tiled;
 }
 
 static PDecArgs pdec_args(const GemmPlan& p, const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
@@ -1807,6 +1938,42 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     const hipError_t e = int4 ? launch_pdec_plan<kWI4>(p, a, lds, stream) : launch_pdec_plan<kWMx>(p, a, lds, stream);
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+}
+
+// The fused-quant plan: the decode plan, when K is not split across
+// workgroups and the whole bf16 activation slice (M x K/8 items of 16 bytes)
+// fits one batch of at most 8 loads per thread (4 where that suffices).  The
+// plan itself is kept: more K parts per tile to fit a larger slice add waves
+// beyond what stays resident (gate_up M = 4 fused in three rounds: 37 us
+// against 23 us for the quant kernel and the GEMM).
+bool plan_prepared_fused(int64_t M, int64_t N, int64_t K, bool int4, GemmPlan* out) {
+    if (M > 16) return false;
+    GemmPlan p = plan_prepared(M, N, K, 0, 0, false, int4);
+    if (p.ks != 1) return false;
+    const int64_t items = M * ((int64_t)p.s_per * 512 / 8), threads = 64 * (int64_t)p.rt * p.kw;
+    const int64_t groups = (p.tiles + p.rt - 1) / p.rt;
+    // every workgroup quantizes the whole slice (about 25 VALU instructions
+    // per value, before its weight stream starts): the 8-load batch only with
+    // at most one workgroup per CU (down_proj M = 1: 17.9 us fused vs 19.6 us
+    // for quant kernel + GEMM; gate_up M = 2, 726 workgroups: 24.7 vs 22.7 us)
+    if (items > 8 * threads || (items > 4 * threads && groups > 256)) return false;
+    p.ab = items <= 4 * threads ? 4 : 8;
+    if (p.ab == 8) p.u = 2;   // the 8-load batch and a 3-deep ring exceed the registers
+    *out = p;
+    return true;
+}
+
+hipError_t launch_prepared_linear_fused(const GemmPlan& p, const uint16_t* xb, int64_t ldx, const uint8_t* wt,
+                                        const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                                        uint8_t* x8_out, float* xs_out, hipStream_t stream, bool int4) {
+    if (p.ks != 1 || p.mt != 1) return hipErrorInvalidValue;
+    PDecArgs a = pdec_args(p, wt, st, out, M, N, K, nullptr);
+    a.xb = xb; a.ldx = ldx; a.x8_out = x8_out; a.xs_out = xs_out;
+    // the fp8 rows, then one amax word per row; the K-part reduction reuses the start
+    const size_t act = prepared_lds_bytes(p, M, false) + 4 * (size_t)M;
+    const size_t red = (size_t)p.kw * p.rt * p.mt * 64 * 16;
+    const size_t lds = act > red ? act : red;
+    return int4 ? launch_pdec_fused<kWI4>(p, a, lds, stream) : launch_pdec_fused<kWMx>(p, a, lds, stream);
 }
 
 // W4A4 decode: the split-K decode kernel on MXFP4 activations (no token

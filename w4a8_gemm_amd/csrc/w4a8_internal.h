@@ -131,12 +131,20 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
                                   int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
 // Which kernel serves a GEMM on prepared weights: the split-K decode kernel
-// (M <= 32 on narrow layers and for int4 weights, M <= 16 on wide MXFP4
-// layers) or the tiled kernel (K split across workgroups when its tiles are
-// few).
+// (M <= 32 on narrow layers and for int4 weights; on wide MXFP4 layers up to
+// M = 16 while the activation slice of all of K fits one workgroup's LDS) or
+// the tiled kernel (K split across workgroups when its tiles are few).
 enum class PreparedRoute { Decode, Tiled };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
+// The linear on bf16 activations with the per-token fp8 quantization fused
+// into the split-K decode kernel's prologue (one launch), where the plan
+// allows it (plan_prepared_fused); codes and scales also written to x8_out /
+// xs_out by one workgroup.
+bool plan_prepared_fused(int64_t M, int64_t N, int64_t K, bool int4, GemmPlan* out);
+hipError_t launch_prepared_linear_fused(const GemmPlan& p, const uint16_t* xb, int64_t ldx, const uint8_t* wt,
+                                        const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                                        uint8_t* x8_out, float* xs_out, hipStream_t stream, bool int4);
 // W4A4 (MXFP4 activations, prepared MXFP4 weights): the split-K decode
 // kernel's W4A4 variant where w4a4_decode_route says so, else the fp4 x fp4
 // tile kernel
