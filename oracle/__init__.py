@@ -77,6 +77,9 @@ def lib():
         L.orc_int4_prepare.restype = ctypes.c_int
         L.orc_int4_gemm.argtypes = [_u8p, _f32p, _i32p, _u16p, _i64, _i64, _i64, _vp, _vp, _i64, _f64p]
         L.orc_int4_gemm.restype = None
+        L.orc_int4_zp_gemm.argtypes = [_u8p, _f32p, _i32p, _i32p, _u16p, _i64, _i64, _i64, _vp, _vp, _i64,
+                                       _f64p]
+        L.orc_int4_zp_gemm.restype = None
         L.orc_e2m1_index_array.argtypes = [_f32p, _i64, _u8p]
         L.orc_e2m1_index_array.restype = None
         L.orc_block_exponent_array.argtypes = [_f32p, _i64, ctypes.c_int, _i32p]
@@ -322,6 +325,28 @@ def int4_gemm(x8, x_scale, qweight_nk, scales_f16_bits, mi=None, ni=None):
     ni = _c(ni, np.int64)
     ref = np.zeros(len(mi), np.float64)
     lib().orc_int4_gemm(x8, xs, qw, sc, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
+    return ref
+
+
+def int4_zp_gemm(x8, x_scale, qweight_kn, qzeros, scales_f16_bits, mi=None, ni=None):
+    """int4 g128 with a zero point per group and column, from the checkpoint
+    layout (qweight [K/8, N], qzeros [K/128, N/8] holding z - 1, scales
+    [K/128, N] fp16 bits): fp64 reference, full [M, N] or values at (mi, ni)."""
+    x8 = _c(x8, np.uint8)
+    xs = _c(x_scale, np.float32)
+    qw = _c(qweight_kn, np.int32)
+    qz = _c(qzeros, np.int32)
+    sc = _c(scales_f16_bits, np.uint16)
+    M, K = x8.shape
+    N = qw.shape[1]
+    if mi is None:
+        ref = np.zeros((M, N), np.float64)
+        lib().orc_int4_zp_gemm(x8, xs, qw, qz, sc, M, N, K, None, None, 0, ref)
+        return ref
+    mi = _c(mi, np.int64)
+    ni = _c(ni, np.int64)
+    ref = np.zeros(len(mi), np.float64)
+    lib().orc_int4_zp_gemm(x8, xs, qw, qz, sc, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
     return ref
 
 

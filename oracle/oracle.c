@@ -516,6 +516,43 @@ void orc_int4_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweig
     }
 }
 
+/* int4 g128 with a zero point per group and column (asymmetric): "vllm-radiance
+ * (MXFP4)", ParoQuant (int4 W4A8 and int5 W5A8): int4 group-128 asymmetric
+ * weights on the W4A8 path; the checkpoint layout and zero convention of
+ * "radiance_autoround.py", module docstring: qweight [K/8, N] with eight
+ * codes along K (nibble k % 8 of word [k/8, n]), scales [K/128, N] fp16,
+ * qzeros [K/128, N/8] with eight zero points along N, each stored minus one
+ * (nibble n % 8 of word [k/128, n/8] is z - 1).  Weight (c - z) * scale;
+ * then as the MXFP4 reference. */
+static double i4zp_dot(const uint8_t *x8, const int32_t *qw_kn, const int32_t *qz, const uint16_t *sc,
+                       int64_t m, int64_t n, int64_t N, int64_t K) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        uint32_t word = (uint32_t)qw_kn[(k / 8) * N + n];
+        int c = (int)((word >> (4 * (k % 8))) & 15u);
+        uint32_t zw = (uint32_t)qz[(k / 128) * (N / 8) + n / 8];
+        int z = (int)((zw >> (4 * (n % 8))) & 15u) + 1;
+        double wv = (double)(c - z) * orc_f16_value(sc[(k / 128) * N + n]);
+        acc += orc_e4m3_value(x8[m * K + k]) * wv;
+    }
+    return acc;
+}
+
+void orc_int4_zp_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweight_kn,
+                      const int32_t *qzeros, const uint16_t *scales_f16, int64_t M, int64_t N, int64_t K,
+                      const int64_t *mi, const int64_t *ni, int64_t count, double *ref) {
+    if (!mi) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = 0; m < M; ++m)
+                ref[m * N + n] = (double)x_scale[m] * i4zp_dot(x8, qweight_kn, qzeros, scales_f16, m, n, N, K);
+    } else {
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t i = 0; i < count; ++i)
+            ref[i] = (double)x_scale[mi[i]] * i4zp_dot(x8, qweight_kn, qzeros, scales_f16, mi[i], ni[i], N, K);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* array forms of the scalar functions above (loops only, for sweeps)        */
 /* ------------------------------------------------------------------------ */

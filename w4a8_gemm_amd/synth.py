@@ -194,6 +194,17 @@ def int4_random(N: int, K: int, seed) -> dict:
     return int4.__wrapped__(seed=seed, N=N, K=K)
 
 
+def int4_zp(N: int = HIDDEN, K: int = INTERMEDIATE, seed=11) -> dict:
+    """int4 g128 asymmetric in the same checkpoint layout: codes and fp16 scales
+    as int4(), qzeros [K/128, N/8] with every nibble (the zero point minus one)
+    uniform in 0..15, so zero points 1..16 all occur."""
+    d = dict(int4.__wrapped__(seed=seed, N=N, K=K))
+    g = _gen((seed, 1))
+    qz = torch.randint(-(2 ** 31), 2 ** 31, (K // 128, N // 8), generator=g, dtype=torch.int64)
+    d["qzeros"] = qz.to(torch.int32).numpy()
+    return d
+
+
 def bf16_weight(N: int = 2 * INTERMEDIATE, K: int = HIDDEN, seed=5) -> np.ndarray:
     """An unquantized bf16 linear [N, K] (bf16 bits, uint16): N(0, 0.02^2) with
     0.1% of entries multiplied by 20, cast to bf16 (RNE)."""
