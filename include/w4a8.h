@@ -72,8 +72,10 @@ typedef enum {
     W4A8_WEIGHT_INT4G128 = 1,        /* [N, K/8] int32 (w4a8_int4g128_prepare) + fp16 scales */
     W4A8_WEIGHT_MXFP4_PREPARED = 2,  /* fragment order (w4a8_mxfp4_prepare) */
     W4A8_WEIGHT_INT4G128_PREPARED = 3, /* fragment order (w4a8_int4g128_prepare_fragments) */
-    W4A8_W4A4_PREPARED = 4            /* MXFP4 fragment order with MXFP4 activations
+    W4A8_W4A4_PREPARED = 4,           /* MXFP4 fragment order with MXFP4 activations
                                          (w4a8_w4a4_gemm_prepared) */
+    W4A8_WEIGHT_INT4G128_ZP_PREPARED = 5 /* int4 g128 with zero points, fragment order
+                                            (w4a8_int4g128_zp_prepare_fragments) */
 } w4a8_weight_kind;
 
 /* ---------------------------------------------------------------------------
@@ -327,6 +329,38 @@ w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
                                         const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
                                         uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
                                         size_t ws_bytes, void *stream);
+
+/* int4 g128 with a zero point per group and column (asymmetric), in
+ * matrix-core fragment order.  Source: "vllm-radiance (MXFP4)", ParoQuant
+ * (int4 W4A8 and int5 W5A8): int4 group-128 asymmetric weights on the W4A8
+ * path, the zero point folded into the GEMM as a row-sum correction rather
+ * than dequantized into the matmul; the checkpoint layout and the zero
+ * convention (stored zero - 1) of "radiance_autoround.py", module docstring.
+ *   out[m,n] = bf16_RNE( s_m * sum_k e4m3(x8[m,k]) * (c[n,k] - z[k/128,n]) * fp16(scales[k/128,n]) )
+ * with c = nibble k % 8 of qweight[k/8, n] and z - 1 = nibble n % 8 of
+ * qzeros[k/128, n/8] (fp32 accumulation; summation order may differ).  The
+ * products run against c - 8 as in the symmetric form, and (8 - z) times the
+ * group's activation sum is added per group before its scale.
+ *   w4a8_int4g128_zp_prepared_bytes: sizes of the two buffers (host): the
+ *     codes as w4a8_int4g128_prepare_fragments; per 16-row tile and 4-step
+ *     chunk one 256-byte record of fp16 scales [step][row], bytes 16 - z
+ *     [step][row] and padding.
+ *   w4a8_int4g128_zp_prepare_fragments: qweight [K/8, N], qzeros [K/128, N/8],
+ *     scales [K/128, N] fp16 -> d_w_prepared (16-byte aligned), d_s_prepared
+ *     (16-byte aligned).  Any zero points; asynchronous.
+ *   w4a8_int4g128_zp_gemm_prepared: as w4a8_int4g128_gemm_prepared (routes,
+ *     workspace rules, any M >= 1), the workspace sized with
+ *     W4A8_WEIGHT_INT4G128_ZP_PREPARED.
+ * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
+ * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_int4g128_zp_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);
+w4a8_status w4a8_int4g128_zp_prepare_fragments(const int32_t *d_qweight_kn, const int32_t *d_qzeros,
+                                               const uint16_t *d_scales_f16, int64_t N, int64_t K,
+                                               uint8_t *d_w_prepared, uint8_t *d_s_prepared, void *stream);
+w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x_scale,
+                                           const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
+                                           uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
+                                           size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * The linear on bf16 activations in one call: per-token fp8 quantization of

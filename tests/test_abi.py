@@ -241,3 +241,20 @@ def test_linear_validation(L):
     # the int4 form keeps N % 8
     a = [_p(), 256, _p(), _p(), _p(), 4, 60, 256, _p(), _p(), None, 0, None]
     assert L.w4a8_int4g128_linear_prepared(*a) == SHAPE
+
+
+def test_int4_zp_validation(L):
+    b, pf, g = L.w4a8_int4g128_zp_prepared_bytes, L.w4a8_int4g128_zp_prepare_fragments, L.w4a8_int4g128_zp_gemm_prepared
+    import ctypes
+    wb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert b(60, 256, ctypes.byref(wb), ctypes.byref(sb)) == SHAPE
+    assert b(64, 256, ctypes.byref(wb), ctypes.byref(sb)) == 0
+    assert sb.value == 4 * 1 * 256 and wb.value == 4 * 1 * 4 * 1024     # 4 tiles, 1 chunk
+    assert pf(None, _p(), _p(), 64, 256, _p(), _p(), None) == INVALID
+    assert pf(_p(), _p(), _p(), 64, 200, _p(), _p(), None) == SHAPE
+    assert pf(_p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 8), None) == INVALID   # 16-byte aligned records
+    assert g(_p(), _p(), _p(), _p(), _p(), 4, 60, 256, None, 0, None) == SHAPE
+    assert g(_p(), _p(), _p(), _p(FAKE + 8), _p(), 4, 64, 256, None, 0, None) == INVALID
+    # the same routes and splits as the symmetric int4 kernels
+    for M in (1, 16, 33, 128):
+        assert L.w4a8_gemm_workspace_bytes(M, 5120, 17408, 5) == L.w4a8_gemm_workspace_bytes(M, 5120, 17408, 3)

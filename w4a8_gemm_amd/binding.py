@@ -21,6 +21,7 @@ __all__ = [
     "PreparedInt4", "int4g128_prepare_fragments", "int4g128_gemm_prepared",
     "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4", "quant_act_mxfp4", "w4a4_gemm_prepared",
     "mxfp4_linear_prepared", "int4g128_linear_prepared",
+    "PreparedInt4ZP", "int4g128_zp_prepare_fragments", "int4g128_zp_gemm_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -28,8 +29,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_SHAPE, ERR_WORKSPACE, ERR_ASYMMETRIC, ERR_HIP = range(6)
 EXP_MODES = {"ocp": 0, "noclip": 1, "mse": 2}
 WEIGHT_MXFP4, WEIGHT_INT4G128, WEIGHT_MXFP4_PREPARED, WEIGHT_INT4G128_PREPARED, W4A4_PREPARED = 0, 1, 2, 3, 4
+WEIGHT_INT4G128_ZP_PREPARED = 5
 _KINDS = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128, "prepared": WEIGHT_MXFP4_PREPARED,
-          "int4_prepared": WEIGHT_INT4G128_PREPARED, "w4a4": W4A4_PREPARED}
+          "int4_prepared": WEIGHT_INT4G128_PREPARED, "w4a4": W4A4_PREPARED,
+          "int4_zp_prepared": WEIGHT_INT4G128_ZP_PREPARED}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -86,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.w4a8_int4g128_prepared_bytes.restype = _int
         L.w4a8_int4g128_prepare_fragments.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
         L.w4a8_int4g128_prepare_fragments.restype = _int
+        L.w4a8_int4g128_zp_prepared_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_size), ctypes.POINTER(_size)]
+        L.w4a8_int4g128_zp_prepared_bytes.restype = _int
+        L.w4a8_int4g128_zp_prepare_fragments.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
+        L.w4a8_int4g128_zp_prepare_fragments.restype = _int
+        L.w4a8_int4g128_zp_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
+        L.w4a8_int4g128_zp_gemm_prepared.restype = _int
         L.w4a8_int4g128_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                                   _size, _vp]
         L.w4a8_int4g128_gemm_prepared.restype = _int
@@ -364,7 +373,8 @@ def _check_weight_sizes(kind, w, w_scale, N, K):
     elif kind == "int4":
         ok = tuple(w.shape) == (N, K // 8) and tuple(w_scale.shape) == (K // 128, N)
     else:
-        fn = "w4a8_mxfp4_prepared_bytes" if kind == "prepared" else "w4a8_int4g128_prepared_bytes"
+        fn = {"prepared": "w4a8_mxfp4_prepared_bytes", "int4_prepared": "w4a8_int4g128_prepared_bytes",
+              "int4_zp_prepared": "w4a8_int4g128_zp_prepared_bytes"}[kind]
         wb, sb = _size(), _size()
         _check(getattr(lib(), fn)(N, K, ctypes.byref(wb), ctypes.byref(sb)), fn)
         ok = (w.numel() * w.element_size() == wb.value and
@@ -474,6 +484,55 @@ def int4g128_prepare_fragments(qweight_kn: torch.Tensor, qzeros: torch.Tensor,
                                                  _ptr(wt), _ptr(st), _stream(qweight_kn)),
            "w4a8_int4g128_prepare_fragments")
     return PreparedInt4(wt, st, N, K)
+
+
+class PreparedInt4ZP(PreparedInt4):
+    """int4 g128 weight with zero points, fragment order
+    (w4a8_int4g128_zp_prepare_fragments)."""
+
+
+def int4g128_zp_prepare_fragments(qweight_kn: torch.Tensor, qzeros: torch.Tensor,
+                                  scales: torch.Tensor) -> PreparedInt4ZP:
+    """Checkpoint qweight [K/8, N] int32, qzeros [K/128, N/8] int32 (any zero
+    points, each stored minus one), scales [K/128, N] fp16 -> PreparedInt4ZP."""
+    _need(qweight_kn, "qweight", torch.int32)
+    dev = qweight_kn.device
+    _need(qzeros, "qzeros", torch.int32, dev)
+    _need(scales, "scales", torch.float16, dev)
+    K8, N = qweight_kn.shape
+    K = 8 * K8
+    if tuple(qzeros.shape) != (K // 128, N // 8) or tuple(scales.shape) != (K // 128, N):
+        raise ValueError("shapes must be qweight [K/8, N], qzeros [K/128, N/8], scales [K/128, N]")
+    wb, sb = _size(), _size()
+    _check(lib().w4a8_int4g128_zp_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)),
+           "w4a8_int4g128_zp_prepared_bytes")
+    wt = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+    st = torch.empty(sb.value, dtype=torch.uint8, device=dev)
+    _check(lib().w4a8_int4g128_zp_prepare_fragments(_ptr(qweight_kn), _ptr(qzeros), _ptr(scales), N, K,
+                                                    _ptr(wt), _ptr(st), _stream(qweight_kn)),
+           "w4a8_int4g128_zp_prepare_fragments")
+    return PreparedInt4ZP(wt, st, N, K)
+
+
+def int4g128_zp_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedInt4ZP,
+                              out: torch.Tensor | None = None,
+                              workspace: Workspace | None = None) -> torch.Tensor:
+    """The asymmetric int4 g128 GEMM on prepared weights (any M >= 1)."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    M, K = x_fp8.shape
+    if K != w.K:
+        raise ValueError(f"activation K {K} != weight K {w.K}")
+    _check_weight_sizes("int4_zp_prepared", w.w, w.s, w.N, w.K)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, w.N, K, "int4_zp_prepared", dev)
+    status = lib().w4a8_int4g128_zp_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
+                                                  _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
+    _check(status, "w4a8_int4g128_zp_gemm_prepared")
+    return out
 
 
 def int4g128_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedInt4,

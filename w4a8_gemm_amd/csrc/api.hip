@@ -131,8 +131,10 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED && K % 128 != 0) return 0;
     if (kind == W4A8_WEIGHT_INT4G128_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
     if (kind == W4A8_W4A4_PREPARED && K % 128 != 0) return 0;
+    if (kind == W4A8_WEIGHT_INT4G128_ZP_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
     if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED &&
-        kind != W4A8_WEIGHT_INT4G128_PREPARED && kind != W4A8_W4A4_PREPARED)
+        kind != W4A8_WEIGHT_INT4G128_PREPARED && kind != W4A8_W4A4_PREPARED &&
+        kind != W4A8_WEIGHT_INT4G128_ZP_PREPARED)
         return 0;
     size_t need = 0;
     if (kind == W4A8_W4A4_PREPARED) {
@@ -151,8 +153,10 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         const size_t b = w4a4_workspace_bytes(M_max, N, K);
         return b > need ? b : need;
     }
-    if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED) {
-        const bool int4 = kind == W4A8_WEIGHT_INT4G128_PREPARED;
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED ||
+        kind == W4A8_WEIGHT_INT4G128_ZP_PREPARED) {
+        // the zero-point form takes the int4 kernels' routes and shapes
+        const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
         auto at = [&](int64_t m) -> size_t {
             const PreparedRoute r = prepared_route(m, N, K, int4);
             if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
@@ -219,10 +223,11 @@ w4a8_status w4a8_mxfp4_prepare(const uint8_t* d_w_packed, const uint8_t* d_w_e8m
                                      as_stream(stream)));
 }
 
-// GEMM on fragment-order weights (MXFP4 or int4): kernel by prepared_route
+// GEMM on fragment-order weights (MXFP4, int4, int4 with zero points):
+// kernel by prepared_route
 static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale, const uint8_t* d_w,
                                  const uint8_t* d_s, uint16_t* d_out, int64_t M, int64_t N, int64_t K,
-                                 void* d_ws, size_t ws_bytes, void* stream, bool int4) {
+                                 void* d_ws, size_t ws_bytes, void* stream, bool int4, bool zp = false) {
     w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
     if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
@@ -235,13 +240,13 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
         st = check_workspace(tiled_workspace_bytes(M, N, K, int4), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
-                                                as_stream(stream), int4));
+                                                as_stream(stream), int4, zp));
     default: {
         const GemmPlan p = plan_prepared(M, N, K, 0, 0, false, int4);
         st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws,
-                                                 as_stream(stream), int4));
+                                                 as_stream(stream), int4, zp));
     }
     }
 }
@@ -345,6 +350,37 @@ w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x
                          stream, true);
 }
 
+w4a8_status w4a8_int4g128_zp_prepared_bytes(int64_t N, int64_t K, size_t* h_w_bytes, size_t* h_s_bytes) {
+    if (!h_w_bytes || !h_s_bytes) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    prepared_i4z_sizes(N, K, h_w_bytes, h_s_bytes);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_int4g128_zp_prepare_fragments(const int32_t* d_qweight_kn, const int32_t* d_qzeros,
+                                               const uint16_t* d_scales_f16, int64_t N, int64_t K,
+                                               uint8_t* d_w_prepared, uint8_t* d_s_prepared, void* stream) {
+    if (!d_qweight_kn || !d_qzeros || !d_scales_f16 || !d_w_prepared || !d_s_prepared)
+        return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_qweight_kn, 4) || !aligned(d_qzeros, 4) || !aligned(d_scales_f16, 2) ||
+        !aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 16))
+        return W4A8_ERR_INVALID_ARG;
+    return hip_status(launch_prepare_i4z(d_qweight_kn, d_qzeros, d_scales_f16, N, K, d_w_prepared, d_s_prepared,
+                                         as_stream(stream)));
+}
+
+w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                           const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
+                                           uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* d_ws,
+                                           size_t ws_bytes, void* stream) {
+    if (d_s_prepared && !aligned(d_s_prepared, 16)) return W4A8_ERR_INVALID_ARG;
+    return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws, ws_bytes,
+                         stream, true, true);
+}
+
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,
                                   int64_t K, int32_t* d_qweight_nk, void* stream) {
     if (!d_qweight_kn || !d_qzeros || !d_qweight_nk) return W4A8_ERR_INVALID_ARG;
@@ -408,7 +444,7 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,
                                                  (const uint8_t*)d_w_scale, d_out, M, N, K, d_ws,
-                                                 as_stream(stream), false));
+                                                 as_stream(stream), false, false));
     }
     if (M > kDecodeMaxM || (rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1)
         return W4A8_ERR_INVALID_ARG;

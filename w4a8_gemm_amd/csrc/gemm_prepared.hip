@@ -74,12 +74,23 @@ __device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, 
 //         codes and an e8m0 scale per 32 k of a token) on the fp4 x fp4
 //         product; only the split-K decode kernel takes it (the tiled W4A4
 //         kernel is its own).
-constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2;
+//   kWI4Z int4 g128 with a zero point z per group and row: the codes as kWI4.
+//         The decode kernels take products against c - 8 as there and add
+//         (8 - z) x (the group's activation sum) per group before its row
+//         scale, the sum from the constant fragment's -8 sum(x).  The tiled
+//         kernels widen c - z directly (exact in e4m3: -16..14), each lane
+//         through the 16-byte table of its row's z, read from a 16-table LDS
+//         block.  Scales and zeros share one 256-byte record per 16-row tile
+//         and 4-step chunk: fp16 scales [step][row], then bytes 16 - z
+//         [step][row], then padding.
+constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2, kWI4Z = 3;
+template <int WF> constexpr bool kIsI4 = WF == kWI4 || WF == kWI4Z;
 
 template <int WF> struct WStep;                               // per-step scale data of a lane
 template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte = step % 4)
 template <> struct WStep<kWI4> { using T = uint2; };         // fp16 scales of its 4 output rows
 template <> struct WStep<kWMxA4> { using T = uint32_t; };
+template <> struct WStep<kWI4Z> { using T = uint2; };
 
 // a lane's activation fragment (B operand) from its LDS row (16-byte chunks
 // XOR-swizzled by sw): MXFP4 pairs with the fp8 operand's own k order, the
@@ -143,6 +154,27 @@ __device__ __forceinline__ v4f i4_split_mma(const I4Split& w, v8i bx, v4f acc, u
     acc[1] = __builtin_fmaf(f16_to_f32(sc.x >> 16), t[1], acc[1]);
     acc[2] = __builtin_fmaf(f16_to_f32(sc.y & 0xFFFFu), t[2], acc[2]);
     acc[3] = __builtin_fmaf(f16_to_f32(sc.y >> 16), t[3], acc[3]);
+    return acc;
+}
+
+// the same with a zero point per row: acc += scale(row) * (x . (c - z)), from
+// x . (c - 8) and (8 - z) * sum(x), sum(x) = -t0 / 8 of the constant product;
+// zb: bytes 16 - z of the lane's four rows
+__device__ __forceinline__ v4f i4z_split_mma(const I4Split& w, v8i bx, v4f acc, uint2 sc, uint32_t zb) {
+    constexpr int kX2 = 128, kX8 = 130;
+    const v8i neg1 = {(int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, 0, 0, 0, 0};
+    const v4f t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(neg1, bx, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4,
+                                                                    kFmtFp8, 0, kX8, 0, kUnitScale);
+    v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.lo, bx, t0, kFmtFp4, kFmtFp8, 0, kX2, 0, kUnitScale);
+    t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0, kUnitScale);
+    const float s4[4] = {f16_to_f32(sc.x & 0xFFFFu), f16_to_f32(sc.x >> 16), f16_to_f32(sc.y & 0xFFFFu),
+                         f16_to_f32(sc.y >> 16)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float zo = (float)((int)((zb >> (8 * r)) & 0xFFu) - 8);     // 8 - z
+        const float u = __builtin_fmaf(zo * -0.125f, t0[r], t[r]);
+        acc[r] = __builtin_fmaf(s4[r], u, acc[r]);
+    }
     return acc;
 }
 
@@ -219,6 +251,29 @@ __global__ __launch_bounds__(256) void prep_i4s_kernel(const uint16_t* __restric
     st[i] = (n < N && s < K / 128) ? sc[(int64_t)s * N + n] : (uint16_t)0;
 }
 
+// int4 with zero points: one 256-byte record per (16-row tile, 4-step chunk):
+// fp16 scales [step][row] (bytes 0..127), bytes 16 - z [step][row] (128..191;
+// z - 1 is nibble n % 8 of qzeros[s, n / 8]), zero padding (192..255).  Rows
+// past N and steps past K get scale 0 and z = 8.  One thread per (record, step,
+// row), the first 64 also clearing the padding.
+__global__ __launch_bounds__(256) void prep_i4zs_kernel(const uint16_t* __restrict__ sc,
+                                                        const uint32_t* __restrict__ qz, int N, int K, int tiles,
+                                                        int c_pad, uint8_t* __restrict__ st) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)tiles * c_pad * 64) return;
+    const int r = (int)(i & 15);
+    const int u = (int)((i >> 4) & 3);
+    const int64_t tc = i >> 6;
+    const int c = (int)(tc % c_pad), t = (int)(tc / c_pad);
+    const int s = 4 * c + u, n = 16 * t + r;
+    const bool in = n < N && s < K / 128;
+    uint8_t* rec = st + 256 * tc;
+    const int e = 16 * u + r;
+    reinterpret_cast<uint16_t*>(rec)[e] = in ? sc[(int64_t)s * N + n] : (uint16_t)0;
+    rec[128 + e] = in ? (uint8_t)(15u - ((qz[(int64_t)s * (N / 8) + n / 8] >> (4 * (n % 8))) & 15u)) : (uint8_t)8;
+    rec[192 + e] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // decode band on prepared weights (M <= 32)
 //
@@ -267,6 +322,11 @@ template <> struct PChunk<kWI4> {
     uint2 s[4];          // fp16 row scales of each step
 };
 template <> struct PChunk<kWMxA4> : PChunk<kWMx> {};
+template <> struct PChunk<kWI4Z> {
+    uint4 w[4];
+    uint2 s[4];          // fp16 row scales of each step (the lane's four output rows)
+    uint32_t z[4];       // bytes 16 - z of the same rows
+};
 
 // chunk j of this wave's range: 4 weight blocks (sp: MXFP4 dwords of the
 // tile's chunks, lane-indexed; int4 8-byte row-scale quads, (chunk, step, g))
@@ -274,11 +334,20 @@ template <int WF>
 __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, int j, PChunk<WF>& c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
-    if constexpr (WF != kWI4) {
-        c.s = reinterpret_cast<const uint32_t*>(sp)[j * 64];
-    } else {
+    if constexpr (WF == kWI4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) c.s[u] = reinterpret_cast<const uint2*>(sp)[j * 16 + u * 4];
+    } else if constexpr (WF == kWI4Z) {
+        // sp: the tile's record of the wave's first chunk (256 bytes per chunk)
+        const int g = (threadIdx.x & 63) >> 4;
+        const uint8_t* rec = reinterpret_cast<const uint8_t*>(sp) + 256 * j;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c.s[u] = *reinterpret_cast<const uint2*>(rec + 32 * u + 8 * g);
+            c.z[u] = *reinterpret_cast<const uint32_t*>(rec + 128 + 16 * u + 4 * g);
+        }
+    } else {
+        c.s = reinterpret_cast<const uint32_t*>(sp)[j * 64];
     }
 }
 
@@ -319,14 +388,17 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, cons
                 if (u == 2) acc[mt] = mfma16<2>(aw, bx, acc[mt], (int)c.s);
                 if (u == 3) acc[mt] = mfma16<3>(aw, bx, acc[mt], (int)c.s);
             }
-        } else if constexpr (WF == kWI4) {
+        } else if constexpr (kIsI4<WF>) {
             const I4Split w = i4_split(c.w[u]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = min(mt * 16 + (lane & 15), M - 1);
                 const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
                 const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-                acc[mt] = i4_split_mma(w, bx, acc[mt], c.s[u]);
+                if constexpr (WF == kWI4Z)
+                    acc[mt] = i4z_split_mma(w, bx, acc[mt], c.s[u], c.z[u]);
+                else
+                    acc[mt] = i4_split_mma(w, bx, acc[mt], c.s[u]);
             }
         }
     }
@@ -481,10 +553,12 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int jb = nch > 0 ? j0 : 0;
     const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
     const void* sp;
-    if constexpr (WF != kWI4)
-        sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
-    else
+    if constexpr (WF == kWI4)
         sp = reinterpret_cast<const uint2*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 16 + (lane >> 4);
+    else if constexpr (WF == kWI4Z)
+        sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 256;
+    else
+        sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
     const int last = nch > 0 ? nch - 1 : 0;
 
     // Activations of this workgroup's K range -> LDS (columns >= K read as
@@ -732,7 +806,7 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t voff, uint32_
 // the MXFP4 format does inside the matrix instruction).
 template <int BM, int BN, int WF = 0>
 struct PfShape {
-    static constexpr int NWM = WF == 1 ? 1 : (BM >= 256 ? 4 : (BM >= 128 ? 2 : 1));
+    static constexpr int NWM = kIsI4<WF> ? 1 : (BM >= 256 ? 4 : (BM >= 128 ? 2 : 1));
     static constexpr int NWN = 8 / NWM;
     static constexpr int FN = BN / (16 * NWN);
     static constexpr int FM = BM / (16 * NWM);
@@ -746,12 +820,14 @@ struct PfShape {
 // order, BN/128 copies per wave), or int4 row scales (128 B per tile = 4 steps
 // x 16 fp16, one 256-byte copy per wave: wave w's 256 bytes hold the records
 // of tiles (BN/128) w and (BN/128) w + 1 -- for BN = 128 the second half holds
-// the next tile's record and is not read).
+// the next tile's record and is not read), or the int4 records with zero
+// points (256 B per tile, copied as the MXFP4 ones).
+template <int WF> constexpr bool kRec256 = WF == kWMx || WF == kWI4Z;
 template <int BN, int WF>
 struct PfScales {
-    static constexpr int BYTES = WF == kWMx ? BN / 16 * 256 : 8 * 256;
-    static constexpr int DMA = WF == kWMx ? (BN / 16) / 8 : 1;             // per wave, per chunk
-    static constexpr int TILE_BYTES = WF == kWMx ? 256 : 128;             // per tile and chunk in HBM
+    static constexpr int BYTES = kRec256<WF> ? BN / 16 * 256 : 8 * 256;
+    static constexpr int DMA = kRec256<WF> ? (BN / 16) / 8 : 1;           // per wave, per chunk
+    static constexpr int TILE_BYTES = kRec256<WF> ? 256 : 128;           // per tile and chunk in HBM
 };
 
 // a lane's scale data of step s for weight tile b (0 <= b < BN/16) of the panel
@@ -834,7 +910,7 @@ __device__ __forceinline__ void pf_issue_one(const PfSrc<BM, BN>& src, uint8_t* 
 // e8m0 dwords of 4-step chunk c (two 256-byte blocks per wave) into `sbuf`
 template <int BM, int BN, int WF>
 __device__ __forceinline__ void pf_issue_scales(const PfSrc<BM, BN>& src, uint8_t* sbuf, int c, int wave) {
-    if constexpr (WF == kWMx) {
+    if constexpr (kRec256<WF>) {
 #pragma unroll
         for (int i = 0; i < PfScales<BN, WF>::DMA; ++i)
             lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
@@ -974,61 +1050,105 @@ __device__ __forceinline__ bool pf_tile(const PfArgs& a, int& tm, int& tn, int& 
 // the FM activation fragments are read one at a time (the next one's LDS read
 // issued before the current one's products) with the copies for step s_nxt
 // spread between the groups.
-template <int BM, int BN, int H>
-__device__ __forceinline__ void pfi_groups(const uint8_t* as, int g, int lane, const v8i (&af)[PfShape<BM, BN, kWI4>::FN],
-                                           const float (&sf)[PfShape<BM, BN, kWI4>::FN][4], v8i bx,
-                                           v4f (&acc)[PfShape<BM, BN, kWI4>::FN][PfShape<BM, BN, kWI4>::FM],
+template <int BM, int BN, int WF, int H>
+__device__ __forceinline__ void pfi_groups(const uint8_t* as, int g, int lane, const v8i (&af)[PfShape<BM, BN, WF>::FN],
+                                           const float (&sf)[PfShape<BM, BN, WF>::FN][4], v8i bx,
+                                           v4f (&acc)[PfShape<BM, BN, WF>::FN][PfShape<BM, BN, WF>::FM],
                                            const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt, int wave) {
-    using W = PfShape<BM, BN, kWI4>;
+    using W = PfShape<BM, BN, WF>;
     if constexpr (H < W::FM) {
         constexpr int D = W::DMA_PER_STAGE;
         v8i bn = bx;
         if constexpr (H + 1 < W::FM) {
             const int r = 16 * (H + 1) + (lane & 15);
-            bn = act_frag<kWI4>(as + 128 * r, g, (r >> 1) & 7);
+            bn = act_frag<WF>(as + 128 * r, g, (r >> 1) & 7);
         }
         pf_issue_range<BM, BN, H * D / W::FM, (H + 1) * D / W::FM>(src, nxt, s_nxt, wave);
 #pragma unroll
         for (int f = 0; f < W::FN; ++f) {
-            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[f], bx, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
-                                                                           kFmtFp8, 0, kUnitScale, 0, kUnitScale);
+            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[f], bx, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           kFmtFp8, kFmtFp8, 0, kUnitScale, 0,
+                                                                           kUnitScale);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[f][H][i] = __builtin_fmaf(sf[f][i], t[i], acc[f][H][i]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        pfi_groups<BM, BN, H + 1>(as, g, lane, af, sf, bn, acc, src, nxt, s_nxt, wave);
+        pfi_groups<BM, BN, WF, H + 1>(as, g, lane, af, sf, bn, acc, src, nxt, s_nxt, wave);
     }
 }
 
-template <int BM, int BN>
+// e4m3 of an integer in [-16, 16] (exact: at most four significant bits)
+__device__ __forceinline__ uint32_t e4m3_small_int(int v) {
+    if (v == 0) return 0u;
+    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+    const int e = 31 - __builtin_clz(a);
+    const uint32_t mant = (e >= 3 ? a >> (e - 3) : a << (3 - e)) & 7u;
+    return (v < 0 ? 0x80u : 0u) | ((uint32_t)(e + 7) << 3) | mant;
+}
+
+// kWI4Z's 16 tables of 16 bytes at zt: table z - 1 holds e4m3(c - z) for
+// c = 0..15; one word per thread of the first 64
+__device__ __forceinline__ void pfi_fill_zero_tables(uint8_t* zt) {
+    const int t = threadIdx.x;
+    if (t < 64) {
+        const int z = t / 4 + 1, c0 = 4 * (t % 4);
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= e4m3_small_int(c0 + i - z) << (8 * i);
+        reinterpret_cast<uint32_t*>(zt)[t] = w;
+    }
+}
+
+// (zt: kWI4Z's 16 tables of 16 bytes, table z - 1 = e4m3(c - z) for c = 0..15)
+template <int BM, int BN, int WF>
 __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, int lane,
-                                            v4f (&acc)[PfShape<BM, BN, kWI4>::FN][PfShape<BM, BN, kWI4>::FM],
+                                            v4f (&acc)[PfShape<BM, BN, WF>::FN][PfShape<BM, BN, WF>::FM],
                                             const uint8_t* sbuf, const PfSrc<BM, BN>& src, uint8_t* nxt, int s_nxt,
-                                            int wave) {
-    using W = PfShape<BM, BN, kWI4>;
+                                            int wave, const uint8_t* zt) {
+    using W = PfShape<BM, BN, WF>;
     const int g = lane >> 4;
     const uint8_t* as = st + W::WBYTES;
     const uint8_t* wp = st + 1024 * (wn * W::FN) + 16 * lane;
     uint4 q[W::FN];
     uint2 sc[W::FN];
+    [[maybe_unused]] uint4 tz[W::FN];
 #pragma unroll
     for (int f = 0; f < W::FN; ++f) {
         q[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
-        sc[f] = pf_scale<BN, kWI4>(sbuf, wn * W::FN + f, s, lane);
+        if constexpr (WF == kWI4Z) {
+            // record of tile b: scales of the lane's output rows; the zero
+            // byte 16 - z of its weight-operand row (row lane % 16) picks the
+            // table z - 1
+            const uint8_t* rec = sbuf + 256 * (wn * W::FN + f);
+            sc[f] = *reinterpret_cast<const uint2*>(rec + 32 * (s & 3) + 8 * g);
+            const uint32_t zb = rec[128 + 16 * (s & 3) + (lane & 15)];
+            tz[f] = *reinterpret_cast<const uint4*>(zt + 16 * ((15u - zb) & 15u));
+        } else {
+            sc[f] = pf_scale<BN, kWI4>(sbuf, wn * W::FN + f, s, lane);
+        }
     }
     const int r0 = lane & 15;
-    const v8i bx = act_frag<kWI4>(as + 128 * r0, g, (r0 >> 1) & 7);
+    const v8i bx = act_frag<WF>(as + 128 * r0, g, (r0 >> 1) & 7);
     v8i af[W::FN];
     float sf[W::FN][4];
 #pragma unroll
     for (int f = 0; f < W::FN; ++f) {
-        af[f] = wfrag<kWI4>(q[f]);
+        if constexpr (WF == kWI4Z) {
+            const uint4 qq = q[f], t = tz[f];
+            const uint2 a0 = int4x8_to_e4m3_tab(qq.x, t.x, t.y, t.z, t.w);
+            const uint2 a1 = int4x8_to_e4m3_tab(qq.y, t.x, t.y, t.z, t.w);
+            const uint2 a2 = int4x8_to_e4m3_tab(qq.z, t.x, t.y, t.z, t.w);
+            const uint2 a3 = int4x8_to_e4m3_tab(qq.w, t.x, t.y, t.z, t.w);
+            af[f] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, (int)a3.x, (int)a3.y};
+        } else {
+            af[f] = wfrag<WF>(q[f]);
+        }
         sf[f][0] = f16_to_f32(sc[f].x & 0xFFFFu);
         sf[f][1] = f16_to_f32(sc[f].x >> 16);
         sf[f][2] = f16_to_f32(sc[f].y & 0xFFFFu);
         sf[f][3] = f16_to_f32(sc[f].y >> 16);
     }
-    pfi_groups<BM, BN, 0>(as, g, lane, af, sf, bx, acc, src, nxt, s_nxt, wave);
+    pfi_groups<BM, BN, WF, 0>(as, g, lane, af, sf, bx, acc, src, nxt, s_nxt, wave);
 }
 
 // lane holds rows n0..n0+3 of column m in every 16x16 tile: out = bf16(s_m * acc)
@@ -1120,6 +1240,12 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     const int s0 = split * a.s_per, s1 = min(a.K >> 7, s0 + a.s_per);
     uint8_t* const base = lds + kPfBase;
     uint8_t* const sbase = base + NS * S::STAGE;
+    if constexpr (WF == kWI4Z) {
+        // the zero-point tables in the reserved bytes below the stages, before
+        // any copy is in flight (so the barrier waits for nothing else)
+        pfi_fill_zero_tables(lds);
+        __syncthreads();
+    }
     PfSrc<BM, BN> src;
     pf_sources<BM, BN, WF>(a, tm, tn, wave, lane, src);
     // prologue: steps s0 .. s0 + NS - 2 (repeating the last step when the range is shorter)
@@ -1150,9 +1276,9 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         // copies for step u; in the last NS - 1 steps they repeat the last step
         // into the free stage, which is never read again (no branch in the
         // product sequence)
-        if constexpr (WF == kWI4)
-            pfi_compute<BM, BN>(base + cur, s, wn, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
-                                min(u, s1 - 1), wave);
+        if constexpr (kIsI4<WF>)
+            pfi_compute<BM, BN, WF>(base + cur, s, wn, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
+                                    min(u, s1 - 1), wave, lds);
         else
             pf_compute<BM, BN, WF>(base + cur, s, wn, wm, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src,
                                    base + nxt, min(u, s1 - 1), wave);
@@ -1611,6 +1737,28 @@ hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, 
     return hipGetLastError();
 }
 
+void prepared_i4z_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes) {
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    *w_bytes = (size_t)(tiles * c_pad * 4 * 1024);
+    *s_bytes = (size_t)(tiles * c_pad * 256);
+}
+
+hipError_t launch_prepare_i4z(const int32_t* qkn, const int32_t* qz, const uint16_t* sc, int64_t N, int64_t K,
+                              uint8_t* wt, uint8_t* st, hipStream_t stream) {
+    const int tiles = (int)((N + 15) / 16);
+    const int c_pad = (int)((K / 128 + 3) / 4);
+    const int64_t nw = (int64_t)tiles * c_pad * 4 * 64, ns = (int64_t)tiles * c_pad * 64;
+    hipLaunchKernelGGL(prep_i4w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qkn), (int)N, (int)K, tiles, 4 * c_pad,
+                       reinterpret_cast<uint4*>(wt));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_i4zs_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, sc,
+                       reinterpret_cast<const uint32_t*>(qz), (int)N, (int)K, tiles, c_pad, st);
+    return hipGetLastError();
+}
+
 // Decode plan on prepared weights: plan fields rt = tiles per workgroup, kw =
 // K parts per tile, ks = K splits across workgroups, s_per = chunks per split,
 // u = ring depth.  LDS per activation row: 512 bytes per 4-step chunk and 16
@@ -1765,7 +1913,7 @@ size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4) {
 
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 void* ws, hipStream_t stream, bool int4) {
+                                 void* ws, hipStream_t stream, bool int4, bool zp) {
     PfArgs a{};
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -1787,7 +1935,13 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     // one kernel per (height, width) that tiled_shape can produce; anything
     // else is refused rather than run with a grid the kernel does not assume
     hipError_t e;
-    if (int4) {
+    if (int4 && zp) {
+        if (bm == 64 && bn == 256) e = launch_pf<64, 256, 5, kWI4Z>(a, stream);
+        else if (bm == 128 && bn == 128) e = launch_pf<128, 128, 4, kWI4Z>(a, stream);
+        else if (bm == 128 && bn == 256) e = launch_pf<128, 256, 4, kWI4Z>(a, stream);
+        else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWI4Z>(a, stream);
+        else return hipErrorInvalidValue;
+    } else if (int4) {
         if (bm == 64 && bn == 256) e = launch_pf<64, 256, 5, kWI4>(a, stream);
         else if (bm == 128 && bn == 128) e = launch_pf<128, 128, 4, kWI4>(a, stream);
         else if (bm == 128 && bn == 256) e = launch_pf<128, 256, 4, kWI4>(a, stream);
@@ -1930,12 +2084,13 @@ static PDecArgs pdec_args(const GemmPlan& p, const uint8_t* wt, const uint8_t* s
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
-                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4) {
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4, bool zp) {
     if (p.ks > 1 && !ws) return hipErrorInvalidValue;
     PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
     a.x8 = x8; a.xs = xs;
     const size_t lds = prepared_lds_bytes(p, M, false);
-    const hipError_t e = int4 ? launch_pdec_plan<kWI4>(p, a, lds, stream) : launch_pdec_plan<kWMx>(p, a, lds, stream);
+    const hipError_t e = int4 ? (zp ? launch_pdec_plan<kWI4Z>(p, a, lds, stream) : launch_pdec_plan<kWI4>(p, a, lds, stream))
+                              : launch_pdec_plan<kWMx>(p, a, lds, stream);
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }

@@ -51,6 +51,25 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
 // Eight int4 codes (one word, nibble j = k j) -> eight e4m3 bytes of (c - 8) in
 // k order.  Codes 0..7 map to -8..-1 and 8..15 to 0..7; each half is an 8-byte
 // table indexed by c & 7, and bit 3 picks the half.
+// The same with the two 8-byte halves of the table given: lo = e4m3 of codes
+// 0..7, hi = codes 8..15 (for a zero point z: e4m3(c - z), exact for
+// c - z in [-16, 14]).
+__device__ __forceinline__ uint2 int4x8_to_e4m3_tab(uint32_t w, uint32_t lo0, uint32_t lo1, uint32_t hi0,
+                                                    uint32_t hi1) {
+    const uint32_t ev = w & 0x0F0F0F0Fu;
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t se = ev & 0x07070707u, so = od & 0x07070707u;
+    const uint32_t ne = __builtin_amdgcn_perm(lo1, lo0, se);
+    const uint32_t pe = __builtin_amdgcn_perm(hi1, hi0, se);
+    const uint32_t no = __builtin_amdgcn_perm(lo1, lo0, so);
+    const uint32_t po = __builtin_amdgcn_perm(hi1, hi0, so);
+    const uint32_t me = ((ev >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t mo = ((od >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t e = __builtin_amdgcn_perm(pe, ne, me);
+    const uint32_t o = __builtin_amdgcn_perm(po, no, mo);
+    return make_uint2(__builtin_amdgcn_perm(o, e, 0x05010400u), __builtin_amdgcn_perm(o, e, 0x07030602u));
+}
+
 __device__ __forceinline__ uint2 int4x8_to_e4m3(uint32_t w) {
     const uint32_t kNegLo = 0xCACCCED0u, kNegHi = 0xB8C0C4C8u;  // -8 -7 -6 -5 | -4 -3 -2 -1
     const uint32_t kPosLo = 0x44403800u, kPosHi = 0x4E4C4A48u;  //  0  1  2  3 |  4  5  6  7
@@ -127,9 +146,10 @@ hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64
 // split-K decode plan on prepared weights; depth 0 = the plan's own ring depth
 GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4, bool int4);
 size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4 = false);
+// zp: int4 weights with zero points (prepared by launch_prepare_i4z)
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
-                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4);
+                                  int64_t N, int64_t K, void* ws, hipStream_t stream, bool int4, bool zp);
 // Which kernel serves a GEMM on prepared weights: the split-K decode kernel
 // (M <= 32 on narrow layers and for int4 weights; on wide MXFP4 layers up to
 // M = 16 while the activation slice of all of K fits one workgroup's LDS) or
@@ -154,10 +174,14 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 void* ws, hipStream_t stream, bool int4);
+                                 void* ws, hipStream_t stream, bool int4, bool zp);
 // int4 g128 in fragment order (same weight geometry as MXFP4; row scales
 // [tile][chunk][step][16] fp16)
 void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+// int4 with zero points: codes as launch_prepare_i4, scales and zeros in 256-byte records
+void prepared_i4z_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+hipError_t launch_prepare_i4z(const int32_t* qkn, const int32_t* qz, const uint16_t* sc, int64_t N, int64_t K,
+                              uint8_t* wt, uint8_t* st, hipStream_t stream);
 hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
                              uint8_t* st, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;

@@ -199,7 +199,7 @@ def int4_zp(N: int = HIDDEN, K: int = INTERMEDIATE, seed=11) -> dict:
     as int4(), qzeros [K/128, N/8] with every nibble (the zero point minus one)
     uniform in 0..15, so zero points 1..16 all occur."""
     d = dict(int4.__wrapped__(seed=seed, N=N, K=K))
-    g = _gen((seed, 1))
+    g = _gen((*seed, 1) if isinstance(seed, (tuple, list)) else (seed, 1))
     qz = torch.randint(-(2 ** 31), 2 ** 31, (K // 128, N // 8), generator=g, dtype=torch.int64)
     d["qzeros"] = qz.to(torch.int32).numpy()
     return d
