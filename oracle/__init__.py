@@ -80,6 +80,9 @@ def lib():
         L.orc_int4_zp_gemm.argtypes = [_u8p, _f32p, _i32p, _i32p, _u16p, _i64, _i64, _i64, _vp, _vp, _i64,
                                        _f64p]
         L.orc_int4_zp_gemm.restype = None
+        L.orc_int5_gemm.argtypes = [_u8p, _f32p, _i32p, _i32p, _u8p, _u16p, _i64, _i64, _i64, _vp, _vp, _i64,
+                                    _f64p]
+        L.orc_int5_gemm.restype = None
         L.orc_e2m1_index_array.argtypes = [_f32p, _i64, _u8p]
         L.orc_e2m1_index_array.restype = None
         L.orc_block_exponent_array.argtypes = [_f32p, _i64, ctypes.c_int, _i32p]
@@ -347,6 +350,29 @@ def int4_zp_gemm(x8, x_scale, qweight_kn, qzeros, scales_f16_bits, mi=None, ni=N
     ni = _c(ni, np.int64)
     ref = np.zeros(len(mi), np.float64)
     lib().orc_int4_zp_gemm(x8, xs, qw, qz, sc, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
+    return ref
+
+
+def int5_gemm(x8, x_scale, qweight_kn, qweight_hi, qzeros_u8, scales_f16_bits, mi=None, ni=None):
+    """int5 g128 (W5A8): low four bits [K/8, N] int32, fifth bits [K/32, N]
+    int32, zero points minus one [K/128, N] uint8, scales [K/128, N] fp16 bits:
+    fp64 reference, full [M, N] or values at (mi, ni)."""
+    x8 = _c(x8, np.uint8)
+    xs = _c(x_scale, np.float32)
+    qw = _c(qweight_kn, np.int32)
+    qh = _c(qweight_hi, np.int32)
+    qz = _c(qzeros_u8, np.uint8)
+    sc = _c(scales_f16_bits, np.uint16)
+    M, K = x8.shape
+    N = qw.shape[1]
+    if mi is None:
+        ref = np.zeros((M, N), np.float64)
+        lib().orc_int5_gemm(x8, xs, qw, qh, qz, sc, M, N, K, None, None, 0, ref)
+        return ref
+    mi = _c(mi, np.int64)
+    ni = _c(ni, np.int64)
+    ref = np.zeros(len(mi), np.float64)
+    lib().orc_int5_gemm(x8, xs, qw, qh, qz, sc, M, N, K, mi.ctypes.data, ni.ctypes.data, len(mi), ref)
     return ref
 
 

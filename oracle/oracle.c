@@ -553,6 +553,46 @@ void orc_int4_zp_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qw
     }
 }
 
+/* int5 g128 (W5A8): "vllm-radiance (MXFP4)", int5 (W5A8): 5-bit ParoQuant
+ * codes on the W4A8 path, the zero point folded as for int4.  The pages
+ * describe the kernel's staging (low nibbles in the int4 word layout, the
+ * fifth bit in a plane of its own) but print no checkpoint layout; the
+ * reading here: qweight [K/8, N] holds the low four bits of each code as the
+ * int4 layout, qweight_hi [K/32, N] the fifth bits (bit k % 32 of word
+ * [k/32, n] is bit 4 of code k), qzeros [K/128, N] one byte per group and
+ * column holding z - 1 (the zero stored minus one, as the int4 checkpoints),
+ * scales [K/128, N] fp16.  Weight (c - z) * scale, c = low | fifth << 4. */
+static double i5_dot(const uint8_t *x8, const int32_t *qw_kn, const int32_t *qh_kn, const uint8_t *qz,
+                     const uint16_t *sc, int64_t m, int64_t n, int64_t N, int64_t K) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        uint32_t lo = ((uint32_t)qw_kn[(k / 8) * N + n] >> (4 * (k % 8))) & 15u;
+        uint32_t hi = ((uint32_t)qh_kn[(k / 32) * N + n] >> (k % 32)) & 1u;
+        int c = (int)(lo | (hi << 4));
+        int z = (int)qz[(k / 128) * N + n] + 1;
+        double wv = (double)(c - z) * orc_f16_value(sc[(k / 128) * N + n]);
+        acc += orc_e4m3_value(x8[m * K + k]) * wv;
+    }
+    return acc;
+}
+
+void orc_int5_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweight_kn, const int32_t *qweight_hi,
+                   const uint8_t *qzeros, const uint16_t *scales_f16, int64_t M, int64_t N, int64_t K,
+                   const int64_t *mi, const int64_t *ni, int64_t count, double *ref) {
+    if (!mi) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = 0; m < M; ++m)
+                ref[m * N + n] = (double)x_scale[m] *
+                                 i5_dot(x8, qweight_kn, qweight_hi, qzeros, scales_f16, m, n, N, K);
+    } else {
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t i = 0; i < count; ++i)
+            ref[i] = (double)x_scale[mi[i]] *
+                     i5_dot(x8, qweight_kn, qweight_hi, qzeros, scales_f16, mi[i], ni[i], N, K);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* array forms of the scalar functions above (loops only, for sweeps)        */
 /* ------------------------------------------------------------------------ */

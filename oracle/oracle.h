@@ -84,6 +84,10 @@ void    orc_int4_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qw
 void    orc_int4_zp_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweight_kn,
                          const int32_t *qzeros, const uint16_t *scales_f16, int64_t M, int64_t N, int64_t K,
                          const int64_t *mi, const int64_t *ni, int64_t count, double *ref);
+void    orc_int5_gemm(const uint8_t *x8, const float *x_scale, const int32_t *qweight_kn,
+                      const int32_t *qweight_hi, const uint8_t *qzeros, const uint16_t *scales_f16,
+                      int64_t M, int64_t N, int64_t K, const int64_t *mi, const int64_t *ni, int64_t count,
+                      double *ref);
 double  orc_f16_value(uint16_t h);
 
 /* array forms (loops over the scalar functions) */

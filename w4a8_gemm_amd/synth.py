@@ -205,6 +205,23 @@ def int4_zp(N: int = HIDDEN, K: int = INTERMEDIATE, seed=11) -> dict:
     return d
 
 
+def int5(N: int = HIDDEN, K: int = INTERMEDIATE, seed=12, symmetric: bool = False) -> dict:
+    """int5 g128: uniform 5-bit codes split into the int4 word layout (low four
+    bits, qweight [K/8, N]) and a fifth-bit plane (qweight_hi [K/32, N], bit
+    k % 32 of word [k/32, n]); zero points minus one [K/128, N] uint8 uniform
+    in 0..31 (15, i.e. z = 16, when symmetric); fp16 scales |N(0, 0.005^2)|."""
+    g = _gen((*seed, 2) if isinstance(seed, (tuple, list)) else (seed, 2))
+    lo = torch.randint(-(2 ** 31), 2 ** 31, (K // 8, N), generator=g, dtype=torch.int64)
+    hi = torch.randint(-(2 ** 31), 2 ** 31, (K // 32, N), generator=g, dtype=torch.int64)
+    sc = (torch.randn((K // 128, N), generator=g, dtype=torch.float32) * 0.005).abs()
+    if symmetric:
+        qz = np.full((K // 128, N), 15, np.uint8)
+    else:
+        qz = torch.randint(0, 32, (K // 128, N), generator=g).to(torch.uint8).numpy()
+    return dict(qweight_kn=lo.to(torch.int32).numpy(), qweight_hi=hi.to(torch.int32).numpy(), qzeros=qz,
+                scales=sc.to(torch.float16).view(torch.int16).numpy().view(np.uint16), N=N, K=K)
+
+
 def bf16_weight(N: int = 2 * INTERMEDIATE, K: int = HIDDEN, seed=5) -> np.ndarray:
     """An unquantized bf16 linear [N, K] (bf16 bits, uint16): N(0, 0.02^2) with
     0.1% of entries multiplied by 20, cast to bf16 (RNE)."""
