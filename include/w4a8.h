@@ -74,8 +74,9 @@ typedef enum {
     W4A8_WEIGHT_INT4G128_PREPARED = 3, /* fragment order (w4a8_int4g128_prepare_fragments) */
     W4A8_W4A4_PREPARED = 4,           /* MXFP4 fragment order with MXFP4 activations
                                          (w4a8_w4a4_gemm_prepared) */
-    W4A8_WEIGHT_INT4G128_ZP_PREPARED = 5 /* int4 g128 with zero points, fragment order
+    W4A8_WEIGHT_INT4G128_ZP_PREPARED = 5, /* int4 g128 with zero points, fragment order
                                             (w4a8_int4g128_zp_prepare_fragments) */
+    W4A8_WEIGHT_INT5G128_PREPARED = 6    /* int5 g128, fragment order (w4a8_int5g128_prepare_fragments) */
 } w4a8_weight_kind;
 
 /* ---------------------------------------------------------------------------
@@ -361,6 +362,42 @@ w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t *d_x_fp8, const float *
                                            const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
                                            uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *d_ws,
                                            size_t ws_bytes, void *stream);
+
+/* int5 g128 (W5A8) in matrix-core fragment order.  Source: "vllm-radiance
+ * (MXFP4)", int5 (W5A8): 5-bit codes on the W4A8 path, c - 16 (-16..15) exact
+ * in e4m3, the zero point folded as for int4, the low nibbles in the int4
+ * word layout and the fifth bit in a plane of its own.  The pages print no
+ * checkpoint layout; the one read here:
+ *   qweight [K/8, N] int32   the low four bits of each code, as the int4 layout
+ *   qweight_hi [K/32, N] int32  the fifth bits: bit k % 32 of word [k/32, n]
+ *   qzeros [K/128, N] uint8  z - 1 per group and column (0..31)
+ *   scales [K/128, N] fp16
+ *   out[m,n] = bf16_RNE( s_m * sum_k e4m3(x8[m,k]) * (c[n,k] - z[k/128,n]) * fp16(scales[k/128,n]) )
+ * (fp32 accumulation; summation order may differ).  The split-K decode
+ * kernel takes x . (c - 16) as four block-scaled fp4 x fp8 products per step
+ * (two 2-bit halves of the low nibble, the fifth bit, a constant -16 term)
+ * and adds (16 - z) times the group's activation sum before its scale.
+ *   w4a8_int5g128_prepared_bytes: sizes of the three buffers (host): codes as
+ *     the int4 fragment order, the fifth-bit plane (256 B per 16-row tile and
+ *     step), 256-byte scale and zero records per tile and 4-step chunk.
+ *   w4a8_int5g128_prepare_fragments: the checkpoint tensors -> the three
+ *     buffers (16-byte aligned).  Asynchronous.
+ *   w4a8_int5g128_gemm_prepared: any M >= 1; M <= 32 one pass of the split-K
+ *     decode kernel, larger M that kernel on consecutive 32-row slices (the
+ *     weights read once per slice: there is no tiled int5 kernel).
+ *     Workspace sized with W4A8_WEIGHT_INT5G128_PREPARED.
+ * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
+ * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+w4a8_status w4a8_int5g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_w5_bytes,
+                                         size_t *h_s_bytes);
+w4a8_status w4a8_int5g128_prepare_fragments(const int32_t *d_qweight_kn, const int32_t *d_qweight_hi,
+                                            const uint8_t *d_qzeros, const uint16_t *d_scales_f16, int64_t N,
+                                            int64_t K, uint8_t *d_w_prepared, uint8_t *d_w5_prepared,
+                                            uint8_t *d_s_prepared, void *stream);
+w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x_scale,
+                                        const uint8_t *d_w_prepared, const uint8_t *d_w5_prepared,
+                                        const uint8_t *d_s_prepared, uint16_t *d_out, int64_t M, int64_t N,
+                                        int64_t K, void *d_ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * The linear on bf16 activations in one call: per-token fp8 quantization of

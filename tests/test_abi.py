@@ -258,3 +258,21 @@ def test_int4_zp_validation(L):
     # the same routes and splits as the symmetric int4 kernels
     for M in (1, 16, 33, 128):
         assert L.w4a8_gemm_workspace_bytes(M, 5120, 17408, 5) == L.w4a8_gemm_workspace_bytes(M, 5120, 17408, 3)
+
+
+def test_int5_validation(L):
+    import ctypes
+    b, pf, g = L.w4a8_int5g128_prepared_bytes, L.w4a8_int5g128_prepare_fragments, L.w4a8_int5g128_gemm_prepared
+    wb, w5b, sb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert b(64, 200, ctypes.byref(wb), ctypes.byref(w5b), ctypes.byref(sb)) == SHAPE
+    assert b(20, 640, ctypes.byref(wb), ctypes.byref(w5b), ctypes.byref(sb)) == 0
+    # 2 tiles x 2 chunks: 4 KiB of codes, 1 KiB of fifth bits and one record per tile and chunk
+    assert (wb.value, w5b.value, sb.value) == (2 * 2 * 4096, 2 * 2 * 1024, 2 * 2 * 256)
+    assert pf(None, _p(), _p(), _p(), 64, 256, _p(), _p(), _p(), None) == INVALID
+    assert pf(_p(), _p(), _p(), _p(), 64, 200, _p(), _p(), _p(), None) == SHAPE
+    assert pf(_p(), _p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 4), _p(), None) == INVALID
+    assert g(_p(), _p(), _p(), None, _p(), _p(), 4, 64, 256, None, 0, None) == INVALID
+    assert g(_p(), _p(), _p(), _p(), _p(), _p(), 4, 64, 200, None, 0, None) == SHAPE
+    # M past 32 runs 32-row slices: the workspace is the slices'
+    assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 6) == L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 6)
+    assert L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 6) > 0

@@ -22,6 +22,7 @@ __all__ = [
     "quant_bf16_to_mxfp4", "quant_fp8ch_to_mxfp4", "quant_act_mxfp4", "w4a4_gemm_prepared",
     "mxfp4_linear_prepared", "int4g128_linear_prepared",
     "PreparedInt4ZP", "int4g128_zp_prepare_fragments", "int4g128_zp_gemm_prepared",
+    "PreparedInt5", "int5g128_prepare_fragments", "int5g128_gemm_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -29,10 +30,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_SHAPE, ERR_WORKSPACE, ERR_ASYMMETRIC, ERR_HIP = range(6)
 EXP_MODES = {"ocp": 0, "noclip": 1, "mse": 2}
 WEIGHT_MXFP4, WEIGHT_INT4G128, WEIGHT_MXFP4_PREPARED, WEIGHT_INT4G128_PREPARED, W4A4_PREPARED = 0, 1, 2, 3, 4
-WEIGHT_INT4G128_ZP_PREPARED = 5
+WEIGHT_INT4G128_ZP_PREPARED, WEIGHT_INT5G128_PREPARED = 5, 6
 _KINDS = {"mxfp4": WEIGHT_MXFP4, "int4": WEIGHT_INT4G128, "prepared": WEIGHT_MXFP4_PREPARED,
           "int4_prepared": WEIGHT_INT4G128_PREPARED, "w4a4": W4A4_PREPARED,
-          "int4_zp_prepared": WEIGHT_INT4G128_ZP_PREPARED}
+          "int4_zp_prepared": WEIGHT_INT4G128_ZP_PREPARED, "int5_prepared": WEIGHT_INT5G128_PREPARED}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -95,6 +96,14 @@ def lib() -> ctypes.CDLL:
         L.w4a8_int4g128_zp_prepare_fragments.restype = _int
         L.w4a8_int4g128_zp_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_int4g128_zp_gemm_prepared.restype = _int
+        L.w4a8_int5g128_prepared_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_size), ctypes.POINTER(_size),
+                                                   ctypes.POINTER(_size)]
+        L.w4a8_int5g128_prepared_bytes.restype = _int
+        L.w4a8_int5g128_prepare_fragments.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
+        L.w4a8_int5g128_prepare_fragments.restype = _int
+        L.w4a8_int5g128_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size,
+                                                  _vp]
+        L.w4a8_int5g128_gemm_prepared.restype = _int
         L.w4a8_int4g128_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                                   _size, _vp]
         L.w4a8_int4g128_gemm_prepared.restype = _int
@@ -532,6 +541,70 @@ def int4g128_zp_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: Pre
     status = lib().w4a8_int4g128_zp_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
                                                   _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
     _check(status, "w4a8_int4g128_zp_gemm_prepared")
+    return out
+
+
+class PreparedInt5:
+    """int5 g128 weight in fragment order (w4a8_int5g128_prepare_fragments):
+    codes' low bits, the fifth-bit plane, scale and zero records."""
+
+    def __init__(self, w: torch.Tensor, w5: torch.Tensor, s: torch.Tensor, N: int, K: int):
+        self.w, self.w5, self.s, self.N, self.K = w, w5, s, int(N), int(K)
+
+
+def _int5_sizes(N, K):
+    wb, w5b, sb = _size(), _size(), _size()
+    _check(lib().w4a8_int5g128_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(w5b), ctypes.byref(sb)),
+           "w4a8_int5g128_prepared_bytes")
+    return wb.value, w5b.value, sb.value
+
+
+def int5g128_prepare_fragments(qweight_kn: torch.Tensor, qweight_hi: torch.Tensor, qzeros: torch.Tensor,
+                               scales: torch.Tensor) -> PreparedInt5:
+    """int5 g128: low bits qweight [K/8, N] int32, fifth bits qweight_hi [K/32, N]
+    int32, zero points minus one qzeros [K/128, N] uint8, scales [K/128, N] fp16
+    -> PreparedInt5."""
+    _need(qweight_kn, "qweight", torch.int32)
+    dev = qweight_kn.device
+    _need(qweight_hi, "qweight_hi", torch.int32, dev)
+    _need(qzeros, "qzeros", torch.uint8, dev)
+    _need(scales, "scales", torch.float16, dev)
+    K8, N = qweight_kn.shape
+    K = 8 * K8
+    if (tuple(qweight_hi.shape) != (K // 32, N) or tuple(qzeros.shape) != (K // 128, N)
+            or tuple(scales.shape) != (K // 128, N)):
+        raise ValueError("shapes must be qweight [K/8, N], qweight_hi [K/32, N], qzeros [K/128, N], "
+                         "scales [K/128, N]")
+    wb, w5b, sb = _int5_sizes(N, K)
+    wt = torch.empty(wb, dtype=torch.uint8, device=dev)
+    w5 = torch.empty(w5b, dtype=torch.uint8, device=dev)
+    st = torch.empty(sb, dtype=torch.uint8, device=dev)
+    _check(lib().w4a8_int5g128_prepare_fragments(_ptr(qweight_kn), _ptr(qweight_hi), _ptr(qzeros), _ptr(scales),
+                                                 N, K, _ptr(wt), _ptr(w5), _ptr(st), _stream(qweight_kn)),
+           "w4a8_int5g128_prepare_fragments")
+    return PreparedInt5(wt, w5, st, N, K)
+
+
+def int5g128_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedInt5,
+                           out: torch.Tensor | None = None,
+                           workspace: Workspace | None = None) -> torch.Tensor:
+    """The int5 g128 GEMM on prepared weights (any M >= 1)."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    M, K = x_fp8.shape
+    if K != w.K:
+        raise ValueError(f"activation K {K} != weight K {w.K}")
+    sizes = _int5_sizes(w.N, w.K)
+    if tuple(t.numel() * t.element_size() for t in (w.w, w.w5, w.s)) != sizes:
+        raise ValueError("prepared int5 buffers do not match N, K")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    wp, wn, _keep = _ws_args(workspace, M, w.N, K, "int5_prepared", dev)
+    status = lib().w4a8_int5g128_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.w5), _ptr(w.s),
+                                               _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
+    _check(status, "w4a8_int5g128_gemm_prepared")
     return out
 
 

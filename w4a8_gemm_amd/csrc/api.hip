@@ -132,11 +132,20 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
     if (kind == W4A8_WEIGHT_INT4G128_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
     if (kind == W4A8_W4A4_PREPARED && K % 128 != 0) return 0;
     if (kind == W4A8_WEIGHT_INT4G128_ZP_PREPARED && (K % 128 != 0 || N % 8 != 0)) return 0;
+    if (kind == W4A8_WEIGHT_INT5G128_PREPARED && K % 128 != 0) return 0;
     if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128 && kind != W4A8_WEIGHT_MXFP4_PREPARED &&
         kind != W4A8_WEIGHT_INT4G128_PREPARED && kind != W4A8_W4A4_PREPARED &&
-        kind != W4A8_WEIGHT_INT4G128_ZP_PREPARED)
+        kind != W4A8_WEIGHT_INT4G128_ZP_PREPARED && kind != W4A8_WEIGHT_INT5G128_PREPARED)
         return 0;
     size_t need = 0;
+    if (kind == W4A8_WEIGHT_INT5G128_PREPARED) {
+        // the decode kernel on slices of at most 32 rows, one after another
+        for (int64_t m = 1; m <= M_max && m <= kPreparedDecodeMaxM; ++m) {
+            const size_t b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
+            if (b > need) need = b;
+        }
+        return need;
+    }
     if (kind == W4A8_W4A4_PREPARED) {
         // the decode kernel's split for every M it serves; above, one tile
         // kernel, its shape constant on each interval (128j, 128j + 128] and
@@ -379,6 +388,61 @@ w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t* d_x_fp8, const float* 
     if (d_s_prepared && !aligned(d_s_prepared, 16)) return W4A8_ERR_INVALID_ARG;
     return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, d_ws, ws_bytes,
                          stream, true, true);
+}
+
+w4a8_status w4a8_int5g128_prepared_bytes(int64_t N, int64_t K, size_t* h_w_bytes, size_t* h_w5_bytes,
+                                         size_t* h_s_bytes) {
+    if (!h_w_bytes || !h_w5_bytes || !h_s_bytes) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    prepared_i5_sizes(N, K, h_w_bytes, h_w5_bytes, h_s_bytes);
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_int5g128_prepare_fragments(const int32_t* d_qweight_kn, const int32_t* d_qweight_hi,
+                                            const uint8_t* d_qzeros, const uint16_t* d_scales_f16, int64_t N,
+                                            int64_t K, uint8_t* d_w_prepared, uint8_t* d_w5_prepared,
+                                            uint8_t* d_s_prepared, void* stream) {
+    if (!d_qweight_kn || !d_qweight_hi || !d_qzeros || !d_scales_f16 || !d_w_prepared || !d_w5_prepared ||
+        !d_s_prepared)
+        return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_qweight_kn, 4) || !aligned(d_qweight_hi, 4) || !aligned(d_scales_f16, 2) ||
+        !aligned(d_w_prepared, 16) || !aligned(d_w5_prepared, 16) || !aligned(d_s_prepared, 16))
+        return W4A8_ERR_INVALID_ARG;
+    return hip_status(launch_prepare_i5(d_qweight_kn, d_qweight_hi, d_qzeros, d_scales_f16, N, K, d_w_prepared,
+                                        d_w5_prepared, d_s_prepared, as_stream(stream)));
+}
+
+w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                        const uint8_t* d_w_prepared, const uint8_t* d_w5_prepared,
+                                        const uint8_t* d_s_prepared, uint16_t* d_out, int64_t M, int64_t N,
+                                        int64_t K, void* d_ws, size_t ws_bytes, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w_prepared, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    if (!d_w5_prepared || !d_s_prepared || !aligned(d_w5_prepared, 16) || !aligned(d_s_prepared, 16))
+        return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    // the split-K decode kernel on row slices of at most 32 (one slice at
+    // decode sizes); each slice's split workspace is reused by the next
+    const int64_t first = M < kPreparedDecodeMaxM ? M : kPreparedDecodeMaxM;
+    size_t need = 0;
+    for (int64_t m : {first, M % kPreparedDecodeMaxM}) {
+        if (m < 1) continue;
+        const size_t b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
+        if (b > need) need = b;
+    }
+    st = check_workspace(need, d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    hipStream_t s = as_stream(stream);
+    for (int64_t m0 = 0; m0 < M; m0 += kPreparedDecodeMaxM) {
+        const int64_t m = M - m0 < kPreparedDecodeMaxM ? M - m0 : kPreparedDecodeMaxM;
+        st = hip_status(launch_prepared_decode_i5(d_x_fp8 + m0 * K, d_x_scale + m0, d_w_prepared, d_w5_prepared,
+                                                  d_s_prepared, d_out + m0 * N, m, N, K, d_ws, s));
+        if (st != W4A8_OK) return st;
+    }
+    return W4A8_OK;
 }
 
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,

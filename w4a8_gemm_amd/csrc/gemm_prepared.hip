@@ -83,7 +83,13 @@ __device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, 
 //         block.  Scales and zeros share one 256-byte record per 16-row tile
 //         and 4-step chunk: fp16 scales [step][row], then bytes 16 - z
 //         [step][row], then padding.
-constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2, kWI4Z = 3;
+//   kWI5  int5 g128 (split-K decode kernel only): the low four bits of each
+//         code as kWI4's nibbles, the fifth bits in a plane of one word per
+//         lane and step (bit j = k 32g + j); c - 16 = 2 v(c & 3) + 8 v((c >> 2)
+//         & 3) + 16 b4 - 16 as four fp4 x fp8 products (the fifth bits
+//         spread to e2m1 1.0 nibbles, scale 16), and the zero point folded as
+//         (16 - z) x sum(x).  Records as kWI4Z with the bytes 16 - z (signed).
+constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2, kWI4Z = 3, kWI5 = 4;
 template <int WF> constexpr bool kIsI4 = WF == kWI4 || WF == kWI4Z;
 
 template <int WF> struct WStep;                               // per-step scale data of a lane
@@ -91,6 +97,7 @@ template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte
 template <> struct WStep<kWI4> { using T = uint2; };         // fp16 scales of its 4 output rows
 template <> struct WStep<kWMxA4> { using T = uint32_t; };
 template <> struct WStep<kWI4Z> { using T = uint2; };
+template <> struct WStep<kWI5> { using T = uint2; };
 
 // a lane's activation fragment (B operand) from its LDS row (16-byte chunks
 // XOR-swizzled by sw): MXFP4 pairs with the fp8 operand's own k order, the
@@ -173,6 +180,42 @@ __device__ __forceinline__ v4f i4z_split_mma(const I4Split& w, v8i bx, v4f acc, 
     for (int r = 0; r < 4; ++r) {
         const float zo = (float)((int)((zb >> (8 * r)) & 0xFFu) - 8);     // 8 - z
         const float u = __builtin_fmaf(zo * -0.125f, t0[r], t[r]);
+        acc[r] = __builtin_fmaf(s4[r], u, acc[r]);
+    }
+    return acc;
+}
+
+// int5: the fifth bits of a lane's 32 codes (bit j = k 32g + j) as an e2m1
+// fragment, nibble j = 2 (value 1.0) where the bit is set
+__device__ __forceinline__ v8i i5_bit_frag(uint32_t b) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x = (b >> (8 * i)) & 0xFFu;
+        x = (x | (x << 12)) & 0x000F000Fu;
+        x = (x | (x << 6)) & 0x03030303u;
+        x = (x | (x << 3)) & 0x11111111u;   // bit j -> bit 4j
+        w[i] = x << 1;
+    }
+    return v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+}
+// acc += scale(row) * (x . (c - z)) over one K step for int5 codes: x . (c - 16)
+// from four products, then (16 - z) * sum(x), sum(x) = -t0 / 16; zb: signed
+// bytes 16 - z of the lane's four rows
+__device__ __forceinline__ v4f i5_split_mma(const I4Split& w, v8i b4, v8i bx, v4f acc, uint2 sc, uint32_t zb) {
+    constexpr int kX2 = 128, kX8 = 130, kX16 = 131;
+    const v8i neg1 = {(int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, 0, 0, 0, 0};
+    const v4f t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(neg1, bx, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4,
+                                                                    kFmtFp8, 0, kX16, 0, kUnitScale);
+    v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.lo, bx, t0, kFmtFp4, kFmtFp8, 0, kX2, 0, kUnitScale);
+    t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0, kUnitScale);
+    t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b4, bx, t, kFmtFp4, kFmtFp8, 0, kX16, 0, kUnitScale);
+    const float s4[4] = {f16_to_f32(sc.x & 0xFFFFu), f16_to_f32(sc.x >> 16), f16_to_f32(sc.y & 0xFFFFu),
+                         f16_to_f32(sc.y >> 16)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float zo = (float)(int)(int8_t)((zb >> (8 * r)) & 0xFFu);    // 16 - z
+        const float u = __builtin_fmaf(zo * -0.0625f, t0[r], t[r]);
         acc[r] = __builtin_fmaf(s4[r], u, acc[r]);
     }
     return acc;
@@ -274,6 +317,40 @@ __global__ __launch_bounds__(256) void prep_i4zs_kernel(const uint16_t* __restri
     rec[192 + e] = 0;
 }
 
+// int5: the fifth-bit plane, one word per (tile, step, lane): lane L's 32
+// codes (row 16t + L % 16, k = 128s + 32(L / 16) + j) are bits j of the
+// checkpoint word qweight_hi[4s + L / 16, row]; zero past N or K
+__global__ __launch_bounds__(256) void prep_i5b_kernel(const uint32_t* __restrict__ qhi, int N, int K, int tiles,
+                                                       int s_pad, uint32_t* __restrict__ w5) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)tiles * s_pad * 64) return;
+    const int L = (int)(i & 63);
+    const int64_t blk = i >> 6;
+    const int s = (int)(blk % s_pad), t = (int)(blk / s_pad);
+    const int row = 16 * t + (L & 15), g = L >> 4;
+    w5[i] = (row < N && s < K / 128) ? qhi[(int64_t)(4 * s + g) * N + row] : 0u;
+}
+
+// int5 records as the int4 zero-point ones, the zero byte holding 16 - z as
+// a signed byte (z - 1 = qzeros[s, n], a byte per group and column); rows
+// past N and steps past K: scale 0, byte 0
+__global__ __launch_bounds__(256) void prep_i5s_kernel(const uint16_t* __restrict__ sc, const uint8_t* __restrict__ qz,
+                                                       int N, int K, int tiles, int c_pad, uint8_t* __restrict__ st) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)tiles * c_pad * 64) return;
+    const int r = (int)(i & 15);
+    const int u = (int)((i >> 4) & 3);
+    const int64_t tc = i >> 6;
+    const int c = (int)(tc % c_pad), t = (int)(tc / c_pad);
+    const int s = 4 * c + u, n = 16 * t + r;
+    const bool in = n < N && s < K / 128;
+    uint8_t* rec = st + 256 * tc;
+    const int e = 16 * u + r;
+    reinterpret_cast<uint16_t*>(rec)[e] = in ? sc[(int64_t)s * N + n] : (uint16_t)0;
+    rec[128 + e] = in ? (uint8_t)(int8_t)(15 - (int)qz[(int64_t)s * N + n]) : (uint8_t)0;
+    rec[192 + e] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // decode band on prepared weights (M <= 32)
 //
@@ -296,6 +373,7 @@ struct PDecArgs {
     const uint8_t* x8;      // fp8 [M, K] (W4A4: e2m1 codes [M, K/2])
     const float* xs;        // token scales (W4A4: none)
     const uint8_t* xe;      // W4A4: activation e8m0 [M, K/32]
+    const uint32_t* w5;     // int5: fifth-bit plane, one word per lane and step
     const uint16_t* xb;     // fused quant: bf16 activations, row stride ldx elements
     int64_t ldx;
     uint8_t* x8_out;        // fused quant: e4m3 codes [M, K] and token scales [M] written
@@ -327,17 +405,25 @@ template <> struct PChunk<kWI4Z> {
     uint2 s[4];          // fp16 row scales of each step (the lane's four output rows)
     uint32_t z[4];       // bytes 16 - z of the same rows
 };
+template <> struct PChunk<kWI5> : PChunk<kWI4Z> {
+    uint32_t b[4];       // fifth bits of each step's 32 codes
+};
 
 // chunk j of this wave's range: 4 weight blocks (sp: MXFP4 dwords of the
 // tile's chunks, lane-indexed; int4 8-byte row-scale quads, (chunk, step, g))
 template <int WF>
-__device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, int j, PChunk<WF>& c) {
+__device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, const uint32_t* bp, int j,
+                                          PChunk<WF>& c) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
+    if constexpr (WF == kWI5) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c.b[u] = bp[(4 * j + u) * 64];
+    }
     if constexpr (WF == kWI4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) c.s[u] = reinterpret_cast<const uint2*>(sp)[j * 16 + u * 4];
-    } else if constexpr (WF == kWI4Z) {
+    } else if constexpr (WF == kWI4Z || WF == kWI5) {
         // sp: the tile's record of the wave's first chunk (256 bytes per chunk)
         const int g = (threadIdx.x & 63) >> 4;
         const uint8_t* rec = reinterpret_cast<const uint8_t*>(sp) + 256 * j;
@@ -388,14 +474,16 @@ __device__ __forceinline__ void pdec_compute(const uint8_t* xl, int stride, cons
                 if (u == 2) acc[mt] = mfma16<2>(aw, bx, acc[mt], (int)c.s);
                 if (u == 3) acc[mt] = mfma16<3>(aw, bx, acc[mt], (int)c.s);
             }
-        } else if constexpr (kIsI4<WF>) {
+        } else if constexpr (kIsI4<WF> || WF == kWI5) {
             const I4Split w = i4_split(c.w[u]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = min(mt * 16 + (lane & 15), M - 1);
                 const uint8_t* p = xl + m * stride + 128 * (4 * j + u) + 16 * g;
                 const v8i bx = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-                if constexpr (WF == kWI4Z)
+                if constexpr (WF == kWI5)
+                    acc[mt] = i5_split_mma(w, i5_bit_frag(c.b[u]), bx, acc[mt], c.s[u], c.z[u]);
+                else if constexpr (WF == kWI4Z)
                     acc[mt] = i4z_split_mma(w, bx, acc[mt], c.s[u], c.z[u]);
                 else
                     acc[mt] = i4_split_mma(w, bx, acc[mt], c.s[u]);
@@ -552,10 +640,12 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int tc = min(t, a.tiles - 1);
     const int jb = nch > 0 ? j0 : 0;
     const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
+    // int5: the same lane's fifth-bit words (one per step)
+    const uint32_t* bp = WF == kWI5 ? a.w5 + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane : nullptr;
     const void* sp;
     if constexpr (WF == kWI4)
         sp = reinterpret_cast<const uint2*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 16 + (lane >> 4);
-    else if constexpr (WF == kWI4Z)
+    else if constexpr (WF == kWI4Z || WF == kWI5)
         sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 256;
     else
         sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
@@ -577,7 +667,7 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     PChunk<WF> ring[D];
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) pdec_load<WF>(wp, sp, min(d, last), ring[d]);
+    for (int d = 0; d < D - 1; ++d) pdec_load<WF>(wp, sp, bp, min(d, last), ring[d]);
     __builtin_amdgcn_sched_barrier(0);
     [[maybe_unused]] uint32_t* amax_u = reinterpret_cast<uint32_t*>(xl + a.M * stride);   // fused quant: row amax
     if constexpr (FQ) {
@@ -621,7 +711,7 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
         for (int j = 0; j < nch; j += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                pdec_load<WF>(wp, sp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
+                pdec_load<WF>(wp, sp, bp, min(j + d + D - 1, last), ring[(d + D - 1) % D]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (j + d < nch) pdec_compute<MT, WF>(xw, stride, xew, estride, lane, a.M, j + d, ring[d], acc);
                 __builtin_amdgcn_sched_barrier(0);
@@ -1759,6 +1849,34 @@ hipError_t launch_prepare_i4z(const int32_t* qkn, const int32_t* qz, const uint1
     return hipGetLastError();
 }
 
+void prepared_i5_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* w5_bytes, size_t* s_bytes) {
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    *w_bytes = (size_t)(tiles * c_pad * 4 * 1024);
+    *w5_bytes = (size_t)(tiles * c_pad * 4 * 256);
+    *s_bytes = (size_t)(tiles * c_pad * 256);
+}
+
+hipError_t launch_prepare_i5(const int32_t* qkn, const int32_t* qhi, const uint8_t* qz, const uint16_t* sc,
+                             int64_t N, int64_t K, uint8_t* wt, uint8_t* w5, uint8_t* st, hipStream_t stream) {
+    const int tiles = (int)((N + 15) / 16);
+    const int c_pad = (int)((K / 128 + 3) / 4);
+    const int64_t nw = (int64_t)tiles * c_pad * 4 * 64, ns = (int64_t)tiles * c_pad * 64;
+    hipLaunchKernelGGL(prep_i4w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qkn), (int)N, (int)K, tiles, 4 * c_pad,
+                       reinterpret_cast<uint4*>(wt));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_i5b_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qhi), (int)N, (int)K, tiles, 4 * c_pad,
+                       reinterpret_cast<uint32_t*>(w5));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_i5s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, sc, qz,
+                       (int)N, (int)K, tiles, c_pad, st);
+    return hipGetLastError();
+}
+
 // Decode plan on prepared weights: plan fields rt = tiles per workgroup, kw =
 // K parts per tile, ks = K splits across workgroups, s_per = chunks per split,
 // u = ring depth.  LDS per activation row: 512 bytes per 4-step chunk and 16
@@ -2129,6 +2247,22 @@ hipError_t launch_prepared_linear_fused(const GemmPlan& p, const uint16_t* xb, i
     const size_t red = (size_t)p.kw * p.rt * p.mt * 64 * 16;
     const size_t lds = act > red ? act : red;
     return int4 ? launch_pdec_fused<kWI4>(p, a, lds, stream) : launch_pdec_fused<kWMx>(p, a, lds, stream);
+}
+
+// int5: the split-K decode kernel on rows [0, M), M <= 32
+hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* w5,
+                                     const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream) {
+    if (M < 1 || M > kPreparedDecodeMaxM) return hipErrorInvalidValue;
+    const GemmPlan p = plan_prepared(M, N, K, 0, 0, false, true);
+    if (p.ks > 1 && !ws) return hipErrorInvalidValue;
+    PDecArgs a = pdec_args(p, wt, st, out, M, N, K, ws);
+    a.x8 = x8; a.xs = xs;
+    a.w5 = reinterpret_cast<const uint32_t*>(w5);
+    const size_t lds = prepared_lds_bytes(p, M, false);
+    const hipError_t e = launch_pdec_plan<kWI5>(p, a, lds, stream);
+    if (e != hipSuccess || p.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 
 // W4A4 decode: the split-K decode kernel on MXFP4 activations (no token

@@ -182,6 +182,14 @@ void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 void prepared_i4z_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 hipError_t launch_prepare_i4z(const int32_t* qkn, const int32_t* qz, const uint16_t* sc, int64_t N, int64_t K,
                               uint8_t* wt, uint8_t* st, hipStream_t stream);
+// int5: codes' low bits as launch_prepare_i4, a fifth-bit plane, records as int4 with zero points
+void prepared_i5_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* w5_bytes, size_t* s_bytes);
+hipError_t launch_prepare_i5(const int32_t* qkn, const int32_t* qhi, const uint8_t* qz, const uint16_t* sc,
+                             int64_t N, int64_t K, uint8_t* wt, uint8_t* w5, uint8_t* st, hipStream_t stream);
+// the split-K decode kernel on int5 weights, M <= 32
+hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* w5,
+                                     const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                     hipStream_t stream);
 hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
                              uint8_t* st, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
