@@ -466,33 +466,51 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
     res["down_proj_prepared"] = pdp
     log("down_proj prepared", pdp)
     del pdc, dw, de
-    # int4 g128, fragment order (the load-time check of qzeros, then the repack), eight copies
-    q = synth.int4()
-    qkn = torch.from_numpy(q["qweight_kn"]).to(dev)
-    qz = torch.from_numpy(q["qzeros"]).to(dev)
-    sc = torch.from_numpy(q["scales"].view(np.int16)).view(torch.float16).to(dev)
-    qcopies = [w4.int4g128_prepare_fragments(qkn, qz, sc) for _ in range(8)]
-    del qkn, qz, sc
-    iws = w4.Workspace(64, q["N"], q["K"], "int4_prepared", dev)
-    i4 = {}
-    for M in (1, 16, 64, 2048):
-        xb = torch.from_numpy(synth.acts(M, q["K"], seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)
-        a8, asc = w4.quant_act_fp8_per_token(xb)
-        oo = torch.empty((M, q["N"]), dtype=torch.bfloat16, device=dev)
-        reps = 8 if M <= 64 else 2
-        dt = _timed_graph(torch, timer, graph_of,
-                          [lambda r=r: w4.int4g128_gemm_prepared(a8, asc, qcopies[r], out=oo, workspace=iws)
-                           for r in range(reps)], 10 if M <= 64 else 3)
-        b = q["N"] * q["K"] // 2 + q["N"] * q["K"] // 64 + M * q["K"] + M * 4 + M * q["N"] * 2
-        ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
-               "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
-        if M > 64:
-            fl = 2.0 * M * q["N"] * q["K"]
-            ent["tflops"] = round(fl / dt / 1e12, 1)
-            ent["frac_of_fp8_peak"] = round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4)
-        i4[str(M)] = ent
+    # int4 g128 (symmetric, then with zero points) and int5 g128, fragment order, eight copies
+    def to_dev(a, half=False):
+        t = torch.from_numpy(a.view(np.int16) if half else a)
+        return (t.view(torch.float16) if half else t).to(dev)
+
+    def int_family(q, prep, gemm, kind, extra_bits):
+        copies = [prep(q) for _ in range(8)]
+        ws = w4.Workspace(64, q["N"], q["K"], kind, dev)
+        out = {}
+        for M in (1, 16, 64, 2048):
+            xb = torch.from_numpy(synth.acts(M, q["K"], seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)
+            a8, asc = w4.quant_act_fp8_per_token(xb)
+            oo = torch.empty((M, q["N"]), dtype=torch.bfloat16, device=dev)
+            reps = 8 if M <= 64 else 2
+            dt = _timed_graph(torch, timer, graph_of,
+                              [lambda r=r: gemm(a8, asc, copies[r], out=oo, workspace=ws)
+                               for r in range(reps)], 10 if M <= 64 else 3)
+            # codes (4 or 5 bits), fp16 scale + zero nibble per group, activations, output
+            b = (q["N"] * q["K"] * extra_bits // 8 + q["N"] * q["K"] // 64 + M * q["K"] + M * 4
+                 + M * q["N"] * 2)
+            ent = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+                   "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
+            if M > 64:
+                fl = 2.0 * M * q["N"] * q["K"]
+                ent["tflops"] = round(fl / dt / 1e12, 1)
+                ent["frac_of_fp8_peak"] = round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4)
+            out[str(M)] = ent
+        del copies
+        return out
+
+    i4 = int_family(synth.int4(), lambda q: w4.int4g128_prepare_fragments(
+        to_dev(q["qweight_kn"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
+        w4.int4g128_gemm_prepared, "int4_prepared", 4)
     res["int4_g128"] = i4
     log("int4", i4)
+    i4z = int_family(synth.int4_zp(), lambda q: w4.int4g128_zp_prepare_fragments(
+        to_dev(q["qweight_kn"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
+        w4.int4g128_zp_gemm_prepared, "int4_zp_prepared", 4)
+    res["int4_g128_zp"] = i4z
+    log("int4 zp", i4z)
+    i5 = int_family(synth.int5(), lambda q: w4.int5g128_prepare_fragments(
+        to_dev(q["qweight_kn"]), to_dev(q["qweight_hi"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
+        w4.int5g128_gemm_prepared, "int5_prepared", 5)
+    res["int5_g128"] = i5
+    log("int5", i5)
     return res
 
 

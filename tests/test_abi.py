@@ -273,6 +273,9 @@ def test_int5_validation(L):
     assert pf(_p(), _p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 4), _p(), None) == INVALID
     assert g(_p(), _p(), _p(), None, _p(), _p(), 4, 64, 256, None, 0, None) == INVALID
     assert g(_p(), _p(), _p(), _p(), _p(), _p(), 4, 64, 200, None, 0, None) == SHAPE
-    # M past 32 runs 32-row slices: the workspace is the slices'
-    assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 6) == L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 6)
+    # M past 32 runs the tile kernel: the activation sums [K/512 chunks][M][4]
+    # fp32 plus 4 KiB, rounded to 256 bytes (no K split at 9 steps), the most
+    # at M_max; with a K split the partials come on top
+    assert L.w4a8_gemm_workspace_bytes(300, 520, 1152, 6) == (3 * 300 * 16 + 4096 + 255) // 256 * 256
     assert L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 6) > 0
+    assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 6) >= 34 * 64 * 16 + 4096 + 2 * 64 * 5120 * 4

@@ -1,6 +1,6 @@
-"""GPU parity: int5 g128 (W5A8) on the split-K decode kernel (M > 32 in
-32-row slices) against the oracle; with the fifth bits clear and every zero
-point 8 equal to int4 in value."""
+"""GPU parity: int5 g128 (W5A8) against the oracle, on the split-K decode
+kernel (M <= 32) and the tile kernel (M > 32: 64-, 128- and 256-row tiles,
+K split across workgroups when the tiles are few)."""
 import numpy as np
 import pytest
 import torch
@@ -44,10 +44,13 @@ def _case(name, q, M, seed, sample=None, spread=10.0):
     return got
 
 
-# one and two activation tiles, K split across workgroups, ragged N (not a
-# multiple of 16 or 4), K ending inside a 4-step chunk, M past 32 in slices
+# decode: one and two activation tiles, K split across workgroups, ragged N
+# (not a multiple of 16 or 4), K ending inside a 4-step chunk; tiles: 64 rows
+# (M 33..64), 128 rows (65..128) and 256 rows, each with and without a K
+# split, ragged M, N and chunks
 INT5 = [(1, 64, 128), (3, 130, 640), (16, 200, 1152), (17, 1000, 4096), (32, 522, 17408), (5, 20000, 512),
-        (33, 96, 384), (70, 300, 1024)]
+        (33, 96, 384), (40, 300, 4096), (64, 20000, 512), (70, 300, 1024), (100, 1000, 17408),
+        (129, 1000, 2176), (300, 520, 1152), (513, 4100, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", INT5)
@@ -55,14 +58,24 @@ def test_int5_ragged(M, N, K):
     _case(f"{M}x{N}x{K}", synth.int5(N, K, seed=(M, N, K, 61)), M, (M, K, 61))
 
 
-@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("M", [1, 16, 64, 2048])
 def test_int5_full_size(M):
     _case(f"int5 M={M}", synth.int5(), M, (62, M), sample=4096)
 
 
-def test_int5_symmetric():
+@pytest.mark.parametrize("M", [8, 200])
+def test_int5_symmetric(M):
     q = synth.int5(520, 2048, seed=63, symmetric=True)
-    _case("symmetric", q, 8, 64)
+    _case(f"symmetric M={M}", q, M, 64)
+
+
+def _transposed(h):
+    # bit pair (8 i + 2 q, +1) of a checkpoint word -> bits (8 q + 2 i, +1)
+    o = np.zeros_like(h)
+    for i in range(4):
+        for q in range(4):
+            o |= ((h >> np.uint32(8 * i + 2 * q)) & np.uint32(3)) << np.uint32(8 * q + 2 * i)
+    return o
 
 
 def test_int5_prepared_planes():
@@ -71,7 +84,7 @@ def test_int5_prepared_planes():
     pw = _prep(q)
     s_pad = 4 * ((K // 128 + 3) // 4)
     w5 = pw.w5.cpu().numpy().view(np.uint32).reshape(2, s_pad, 64)
-    hi = q["qweight_hi"].view(np.uint32)
+    hi = _transposed(q["qweight_hi"].view(np.uint32))
     for t in range(2):
         for s_ in range(s_pad):
             for L in range(64):

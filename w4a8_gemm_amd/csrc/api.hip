@@ -139,11 +139,22 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         return 0;
     size_t need = 0;
     if (kind == W4A8_WEIGHT_INT5G128_PREPARED) {
-        // the decode kernel on slices of at most 32 rows, one after another
+        // the decode kernel up to 32 rows; above, the tile kernel, whose shape
+        // is constant on (32, 64], (64, 128] and each (256 j - 256, 256 j], its
+        // workspace growing with M there: the interval ends and M_max cover it
         for (int64_t m = 1; m <= M_max && m <= kPreparedDecodeMaxM; ++m) {
             const size_t b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
             if (b > need) need = b;
         }
+        auto keep = [&](int64_t m) {
+            if (m <= kPreparedDecodeMaxM || m > M_max || !i5_tiled_fits(m, K)) return;
+            const size_t b = i5_tiled_workspace_bytes(m, N, K);
+            if (b > need) need = b;
+        };
+        keep(64);
+        keep(128);
+        for (int64_t m = 256; m < M_max && m <= 32768; m += 256) keep(m);
+        keep(M_max);
         return need;
     }
     if (kind == W4A8_W4A4_PREPARED) {
@@ -424,25 +435,20 @@ w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x
     if (!d_w5_prepared || !d_s_prepared || !aligned(d_w5_prepared, 16) || !aligned(d_s_prepared, 16))
         return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-    // the split-K decode kernel on row slices of at most 32 (one slice at
-    // decode sizes); each slice's split workspace is reused by the next
-    const int64_t first = M < kPreparedDecodeMaxM ? M : kPreparedDecodeMaxM;
-    size_t need = 0;
-    for (int64_t m : {first, M % kPreparedDecodeMaxM}) {
-        if (m < 1) continue;
-        const size_t b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
-        if (b > need) need = b;
-    }
-    st = check_workspace(need, d_ws, ws_bytes);
-    if (st != W4A8_OK) return st;
     hipStream_t s = as_stream(stream);
-    for (int64_t m0 = 0; m0 < M; m0 += kPreparedDecodeMaxM) {
-        const int64_t m = M - m0 < kPreparedDecodeMaxM ? M - m0 : kPreparedDecodeMaxM;
-        st = hip_status(launch_prepared_decode_i5(d_x_fp8 + m0 * K, d_x_scale + m0, d_w_prepared, d_w5_prepared,
-                                                  d_s_prepared, d_out + m0 * N, m, N, K, d_ws, s));
+    if (M <= kPreparedDecodeMaxM) {
+        // the split-K decode kernel
+        st = check_workspace(plan_workspace_bytes(plan_prepared(M, N, K, 0, 0, false, true), M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_decode_i5(d_x_fp8, d_x_scale, d_w_prepared, d_w5_prepared, d_s_prepared,
+                                                    d_out, M, N, K, d_ws, s));
     }
-    return W4A8_OK;
+    // the tile kernel (its activation-sum pre-pass writes the workspace)
+    if (!i5_tiled_fits(M, K)) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    st = check_workspace(i5_tiled_workspace_bytes(M, N, K), d_ws, ws_bytes);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_prepared_tiled_i5(d_x_fp8, d_x_scale, d_w_prepared, d_w5_prepared, d_s_prepared, d_out,
+                                               M, N, K, d_ws, s));
 }
 
 w4a8_status w4a8_int4g128_prepare(const int32_t* d_qweight_kn, const int32_t* d_qzeros, int64_t N,

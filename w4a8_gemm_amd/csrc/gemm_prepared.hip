@@ -83,14 +83,24 @@ __device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, 
 //         block.  Scales and zeros share one 256-byte record per 16-row tile
 //         and 4-step chunk: fp16 scales [step][row], then bytes 16 - z
 //         [step][row], then padding.
-//   kWI5  int5 g128 (split-K decode kernel only): the low four bits of each
-//         code as kWI4's nibbles, the fifth bits in a plane of one word per
-//         lane and step (bit j = k 32g + j); c - 16 = 2 v(c & 3) + 8 v((c >> 2)
-//         & 3) + 16 b4 - 16 as four fp4 x fp8 products (the fifth bits
-//         spread to e2m1 1.0 nibbles, scale 16), and the zero point folded as
-//         (16 - z) x sum(x).  Records as kWI4Z with the bytes 16 - z (signed).
+//   kWI5  int5 g128: the low four bits of each code as kWI4's nibbles, the
+//         fifth bits in a plane of one word per lane and step whose bit
+//         8 q + 2 i + p is the fifth bit of the lane's code 8 i + 2 q + p
+//         (the checkpoint word with its 2-bit units transposed as a 4 x 4
+//         array, so that each byte's bits for even and odd codes sit in
+//         one column).  The split-K decode kernel takes c - 16 = 2 v(c & 3) +
+//         8 v((c >> 2) & 3) + 16 b4 - 16 as four fp4 x fp8 products (the
+//         fifth bits spread to e2m1 1.0 nibbles, scale 16) and folds
+//         (16 - z) x sum(x) per step.  The tiled kernel widens c - 16 to e4m3
+//         (exact: -16..15) through four 8-byte tables, and adds the
+//         zero-point term sum over a chunk's four steps of
+//         s (16 - z) x sum(x) with one fp32 16x16x4 product per output
+//         tile, the token-and-group activation sums from a pre-pass.
+//         Records as kWI4Z with the bytes 16 - z (signed).
 constexpr int kWMx = 0, kWI4 = 1, kWMxA4 = 2, kWI4Z = 3, kWI5 = 4;
 template <int WF> constexpr bool kIsI4 = WF == kWI4 || WF == kWI4Z;
+// formats the tiled kernel widens to e4m3 in registers (one wave row)
+template <int WF> constexpr bool kWiden = kIsI4<WF> || WF == kWI5;
 
 template <int WF> struct WStep;                               // per-step scale data of a lane
 template <> struct WStep<kWMx> { using T = uint32_t; };      // e8m0 dword (byte = step % 4)
@@ -188,14 +198,13 @@ __device__ __forceinline__ v4f i4z_split_mma(const I4Split& w, v8i bx, v4f acc, 
 // int5: the fifth bits of a lane's 32 codes (bit j = k 32g + j) as an e2m1
 // fragment, nibble j = 2 (value 1.0) where the bit is set
 __device__ __forceinline__ v8i i5_bit_frag(uint32_t b) {
+    // plane bit 8 q + 2 i + p is the fifth bit of code 8 i + 2 q + p: word i's
+    // byte q takes bits p = 0, 1 of (b >> 2 i) into the low and high nibble
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t x = (b >> (8 * i)) & 0xFFu;
-        x = (x | (x << 12)) & 0x000F000Fu;
-        x = (x | (x << 6)) & 0x03030303u;
-        x = (x | (x << 3)) & 0x11111111u;   // bit j -> bit 4j
-        w[i] = x << 1;
+        const uint32_t x = b >> (2 * i);
+        w[i] = ((x << 1) & 0x02020202u) | ((x << 4) & 0x20202020u);
     }
     return v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
 }
@@ -328,7 +337,12 @@ __global__ __launch_bounds__(256) void prep_i5b_kernel(const uint32_t* __restric
     const int64_t blk = i >> 6;
     const int s = (int)(blk % s_pad), t = (int)(blk / s_pad);
     const int row = 16 * t + (L & 15), g = L >> 4;
-    w5[i] = (row < N && s < K / 128) ? qhi[(int64_t)(4 * s + g) * N + row] : 0u;
+    const uint32_t h = (row < N && s < K / 128) ? qhi[(int64_t)(4 * s + g) * N + row] : 0u;
+    // bit pair (8 i + 2 q, +1) of the checkpoint word -> bits 8 q + 2 i, +1
+    uint32_t o = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) o |= ((h >> (8 * (u >> 2) + 2 * (u & 3))) & 3u) << (8 * (u & 3) + 2 * (u >> 2));
+    w5[i] = o;
 }
 
 // int5 records as the int4 zero-point ones, the zero byte holding 16 - z as
@@ -847,6 +861,8 @@ struct PfArgs {
     int ks, s_per;              // K splits (steps s_per each, a multiple of 4; ks = 1: none)
     float* partials;            // ks > 1: fp32 [ks][M][N], token scale not applied
     const uint8_t* xe;          // W4A4: activation e8m0 [M, K/32] (x8 then holds e2m1 [M, K/2])
+    const uint32_t* w5;         // int5: fifth-bit plane [tile][step][lane]
+    const float* rs;            // int5: activation sums [chunk][M][4 steps] (fp32)
 };
 
 constexpr int kPfThreads = 512;
@@ -896,7 +912,7 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t voff, uint32_
 // the MXFP4 format does inside the matrix instruction).
 template <int BM, int BN, int WF = 0>
 struct PfShape {
-    static constexpr int NWM = kIsI4<WF> ? 1 : (BM >= 256 ? 4 : (BM >= 128 ? 2 : 1));
+    static constexpr int NWM = kWiden<WF> ? 1 : (BM >= 256 ? 4 : (BM >= 128 ? 2 : 1));
     static constexpr int NWN = 8 / NWM;
     static constexpr int FN = BN / (16 * NWN);
     static constexpr int FM = BM / (16 * NWM);
@@ -912,11 +928,19 @@ struct PfShape {
 // of tiles (BN/128) w and (BN/128) w + 1 -- for BN = 128 the second half holds
 // the next tile's record and is not read), or the int4 records with zero
 // points (256 B per tile, copied as the MXFP4 ones).
-template <int WF> constexpr bool kRec256 = WF == kWMx || WF == kWI4Z;
-template <int BN, int WF>
+template <int WF> constexpr bool kRec256 = WF == kWMx || WF == kWI4Z || WF == kWI5;
+// int5 adds, per chunk, the fifth-bit planes of the panel's tiles (1 KiB per
+// tile: [step][lane] words) and the activation sums of the tile's rows (16 B
+// per row: [row][step], at least 128 rows so that every wave copies alike)
+template <int BM> constexpr int kI5SumRows = BM > 128 ? BM : 128;
+template <int BN, int WF, int BM = 0>
 struct PfScales {
-    static constexpr int BYTES = kRec256<WF> ? BN / 16 * 256 : 8 * 256;
-    static constexpr int DMA = kRec256<WF> ? (BN / 16) / 8 : 1;           // per wave, per chunk
+    static constexpr int REC = kRec256<WF> ? BN / 16 * 256 : 8 * 256;
+    static constexpr int PLANES = WF == kWI5 ? BN / 16 * 1024 : 0;
+    static constexpr int SUMS = WF == kWI5 ? kI5SumRows<BM> * 16 : 0;
+    static constexpr int BYTES = REC + PLANES + SUMS;
+    static constexpr int DMA = (kRec256<WF> ? (BN / 16) / 8 : 1) +
+                               (WF == kWI5 ? (BN / 16) / 8 + kI5SumRows<BM> / 128 : 0);   // per wave, per chunk
     static constexpr int TILE_BYTES = kRec256<WF> ? 256 : 128;           // per tile and chunk in HBM
 };
 
@@ -953,6 +977,8 @@ template <int BM, int BN>
 struct PfSrc {
     i32x4 w, x, sc;
     uint32_t w_off[BN / 128], x_off[BM / 64], s_off[BN / 128];
+    i32x4 w5, rs;                       // int5: fifth-bit planes, activation sums
+    uint32_t p_off[BN / 128], r_off[2], r_chunk;
 };
 
 template <int BM, int BN, int WF>
@@ -968,6 +994,23 @@ __device__ __forceinline__ void pf_sources(const PfArgs& a, int tm, int tn, int 
         const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
         src.w_off[i] = (uint32_t)(t * wblk) + 16u * lane;
         src.s_off[i] = (uint32_t)(t * sblk) + 4u * lane;
+    }
+    if constexpr (WF == kWI5) {
+        // planes: 4 steps x 256 B per tile and chunk, tile wave + 8 i as the
+        // weight blocks; sums: rows tm BM .. of each chunk's [M][4] block, 256
+        // bytes per copy (rows past M read the next rows or, past the end, zero)
+        src.w5 = make_rsrc(a.w5 + (int64_t)t0 * a.s_pad * 64, (uint64_t)(a.tiles16 - t0) * a.s_pad * 256);
+        // (the workspace holds 4 KiB past the last chunk: every copy stays in it)
+        const int64_t rs_bytes = (int64_t)a.c_pad * a.M * 16 + 4096;
+        src.rs = make_rsrc(a.rs + (int64_t)tm * BM * 4, (uint64_t)(rs_bytes - (int64_t)tm * BM * 16));
+        src.r_chunk = (uint32_t)a.M * 16u;
+#pragma unroll
+        for (int i = 0; i < BN / 128; ++i) {
+            const int t = min(t0 + wave + 8 * i, a.tiles16 - 1) - t0;
+            src.p_off[i] = (uint32_t)(t * (int64_t)a.s_pad * 256) + 16u * lane;
+        }
+#pragma unroll
+        for (int i = 0; i < kI5SumRows<BM> / 128; ++i) src.r_off[i] = 256u * (wave + 8 * i) + 4u * lane;
     }
     if constexpr (WF == kWI4) {
         // int4 row-scale records: tile (BN/128) wave + lane / 32, 4 bytes per lane
@@ -998,12 +1041,22 @@ __device__ __forceinline__ void pf_issue_one(const PfSrc<BM, BN>& src, uint8_t* 
 }
 
 // e8m0 dwords of 4-step chunk c (two 256-byte blocks per wave) into `sbuf`
+// (int5: then the planes and the activation sums)
 template <int BM, int BN, int WF>
 __device__ __forceinline__ void pf_issue_scales(const PfSrc<BM, BN>& src, uint8_t* sbuf, int c, int wave) {
     if constexpr (kRec256<WF>) {
 #pragma unroll
-        for (int i = 0; i < PfScales<BN, WF>::DMA; ++i)
+        for (int i = 0; i < (BN / 16) / 8; ++i)
             lds_dma4(src.sc, src.s_off[i], 256u * c, lds_addr(sbuf + 256 * (wave + 8 * i)));
+        if constexpr (WF == kWI5) {
+            using SC = PfScales<BN, WF, BM>;
+#pragma unroll
+            for (int i = 0; i < (BN / 16) / 8; ++i)
+                lds_dma16(src.w5, src.p_off[i], 1024u * c, lds_addr(sbuf + SC::REC + 1024 * (wave + 8 * i)));
+#pragma unroll
+            for (int i = 0; i < kI5SumRows<BM> / 128; ++i)
+                lds_dma4(src.rs, src.r_off[i], src.r_chunk * c, lds_addr(sbuf + SC::REC + SC::PLANES + 256 * (wave + 8 * i)));
+        }
     } else {
         lds_dma4(src.sc, src.s_off[0], 128u * c, lds_addr(sbuf + 256 * wave));
     }
@@ -1189,6 +1242,63 @@ __device__ __forceinline__ void pfi_fill_zero_tables(uint8_t* zt) {
     }
 }
 
+template <int N>
+__device__ __forceinline__ uint32_t shl_signed(uint32_t x) {
+    if constexpr (N >= 0) return x << N;
+    else return x >> (-N);
+}
+// Word I of a lane's int5 codes: eight low nibbles (nibble j = code 8 I + j)
+// and the plane word P (bit 8 q + 2 I + p = fifth bit of code 8 I + 2 q + p)
+// -> eight e4m3 bytes of c - 16 in code order.  By (fifth bit, bit 3) the
+// values are -16..-9, -8..-1, 0..7, 8..15: four 8-byte tables over c & 7,
+// then two byte selects.
+template <int I>
+__device__ __forceinline__ uint2 int5x8_to_e4m3(uint32_t w, uint32_t P) {
+    constexpr uint32_t kA0 = 0xD5D6D7D8u, kA1 = 0xD1D2D3D4u;   // -16 -15 -14 -13 | -12 -11 -10 -9
+    constexpr uint32_t kB0 = 0xCACCCED0u, kB1 = 0xB8C0C4C8u;   //  -8  -7  -6  -5 |  -4  -3  -2 -1
+    constexpr uint32_t kC0 = 0x44403800u, kC1 = 0x4E4C4A48u;   //   0   1   2   3 |   4   5   6  7
+    constexpr uint32_t kD0 = 0x53525150u, kD1 = 0x57565554u;   //   8   9  10  11 |  12  13  14 15
+    const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t se = ev & 0x07070707u, so = od & 0x07070707u;
+    const uint32_t me = ((ev >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t mo = ((od >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t fe = (shl_signed<2 - 2 * I>(P) & 0x04040404u) | 0x03020100u;
+    const uint32_t fo = (shl_signed<1 - 2 * I>(P) & 0x04040404u) | 0x03020100u;
+    const uint32_t e0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(kB1, kB0, se), __builtin_amdgcn_perm(kA1, kA0, se), me);
+    const uint32_t e1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(kD1, kD0, se), __builtin_amdgcn_perm(kC1, kC0, se), me);
+    const uint32_t o0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(kB1, kB0, so), __builtin_amdgcn_perm(kA1, kA0, so), mo);
+    const uint32_t o1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(kD1, kD0, so), __builtin_amdgcn_perm(kC1, kC0, so), mo);
+    const uint32_t e = __builtin_amdgcn_perm(e1, e0, fe);
+    const uint32_t o = __builtin_amdgcn_perm(o1, o0, fo);
+    return make_uint2(__builtin_amdgcn_perm(o, e, 0x05010400u), __builtin_amdgcn_perm(o, e, 0x07030602u));
+}
+
+// int5, first step of a chunk: acc += s (16 - z) x sum(x) over the chunk's
+// four steps, one fp32 16x16x4 product per output tile: A = the lane's
+// (row lane % 16, step lane / 16) factor from the tile's record, B = the
+// activation sum of (token lane % 16, step lane / 16)
+template <int BM, int BN>
+__device__ __forceinline__ void pfi_zero_fold(const uint8_t* sbuf, int wn, int lane,
+                                              v4f (&acc)[PfShape<BM, BN, kWI5>::FN][PfShape<BM, BN, kWI5>::FM]) {
+    using W = PfShape<BM, BN, kWI5>;
+    using SC = PfScales<BN, kWI5, BM>;
+    const int r = lane & 15, u = lane >> 4;
+    float zs[W::FN];
+#pragma unroll
+    for (int f = 0; f < W::FN; ++f) {
+        const uint8_t* rec = sbuf + 256 * (wn * W::FN + f);
+        const uint32_t h = *reinterpret_cast<const uint16_t*>(rec + 2 * (16 * u + r));
+        zs[f] = f16_to_f32(h) * (float)(int)(int8_t)rec[128 + 16 * u + r];
+    }
+    const float* sums = reinterpret_cast<const float*>(sbuf + SC::REC + SC::PLANES);
+#pragma unroll
+    for (int h = 0; h < W::FM; ++h) {
+        const float x = sums[4 * (16 * h + r) + u];
+#pragma unroll
+        for (int f = 0; f < W::FN; ++f) acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[f], x, acc[f][h], 0, 0, 0);
+    }
+}
+
 // (zt: kWI4Z's 16 tables of 16 bytes, table z - 1 = e4m3(c - z) for c = 0..15)
 template <int BM, int BN, int WF>
 __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, int lane,
@@ -1202,10 +1312,16 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
     uint4 q[W::FN];
     uint2 sc[W::FN];
     [[maybe_unused]] uint4 tz[W::FN];
+    [[maybe_unused]] uint32_t pl[W::FN];
 #pragma unroll
     for (int f = 0; f < W::FN; ++f) {
         q[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
-        if constexpr (WF == kWI4Z) {
+        if constexpr (WF == kWI5) {
+            // record of tile b (scales as kWI4Z's); the lane's plane word of step s
+            sc[f] = *reinterpret_cast<const uint2*>(sbuf + 256 * (wn * W::FN + f) + 32 * (s & 3) + 8 * g);
+            pl[f] = *reinterpret_cast<const uint32_t*>(sbuf + PfScales<BN, kWI5, BM>::REC + 1024 * (wn * W::FN + f) +
+                                                       256 * (s & 3) + 4 * lane);
+        } else if constexpr (WF == kWI4Z) {
             // record of tile b: scales of the lane's output rows; the zero
             // byte 16 - z of its weight-operand row (row lane % 16) picks the
             // table z - 1
@@ -1223,7 +1339,11 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
     float sf[W::FN][4];
 #pragma unroll
     for (int f = 0; f < W::FN; ++f) {
-        if constexpr (WF == kWI4Z) {
+        if constexpr (WF == kWI5) {
+            const uint2 a0 = int5x8_to_e4m3<0>(q[f].x, pl[f]), a1 = int5x8_to_e4m3<1>(q[f].y, pl[f]);
+            const uint2 a2 = int5x8_to_e4m3<2>(q[f].z, pl[f]), a3 = int5x8_to_e4m3<3>(q[f].w, pl[f]);
+            af[f] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, (int)a3.x, (int)a3.y};
+        } else if constexpr (WF == kWI4Z) {
             const uint4 qq = q[f], t = tz[f];
             const uint2 a0 = int4x8_to_e4m3_tab(qq.x, t.x, t.y, t.z, t.w);
             const uint2 a1 = int4x8_to_e4m3_tab(qq.y, t.x, t.y, t.z, t.w);
@@ -1237,6 +1357,9 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
         sf[f][1] = f16_to_f32(sc[f].x >> 16);
         sf[f][2] = f16_to_f32(sc[f].y & 0xFFFFu);
         sf[f][3] = f16_to_f32(sc[f].y >> 16);
+    }
+    if constexpr (WF == kWI5) {
+        if ((s & 3) == 0) pfi_zero_fold<BM, BN>(sbuf, wn, lane, acc);
     }
     pfi_groups<BM, BN, WF, 0>(as, g, lane, af, sf, bx, acc, src, nxt, s_nxt, wave);
 }
@@ -1308,7 +1431,7 @@ template <int BM, int BN, int NS, int WF>
 __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
     using S = PfShape<BM, BN>;
     using W = PfShape<BM, BN, WF>;
-    using SC = PfScales<BN, WF>;
+    using SC = PfScales<BN, WF, BM>;
     static_assert(NS >= 3 && NS <= 5, "ring depth");
     constexpr int D = S::DMA_PER_STAGE, DS = SC::DMA;
     constexpr int LDS = kPfBase + NS * S::STAGE + 2 * SC::BYTES;
@@ -1366,7 +1489,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_kernel(PfArgs a) {
         // copies for step u; in the last NS - 1 steps they repeat the last step
         // into the free stage, which is never read again (no branch in the
         // product sequence)
-        if constexpr (kIsI4<WF>)
+        if constexpr (kWiden<WF>)
             pfi_compute<BM, BN, WF>(base + cur, s, wn, lane, acc, sbase + ((s >> 2) & 1) * SC::BYTES, src, base + nxt,
                                     min(u, s1 - 1), wave, lds);
         else
@@ -1770,6 +1893,38 @@ hipError_t launch_pfa(const PfArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// int5 tiles' pre-pass: each token's activation sum over each 128-wide K
+// step, rs[chunk][m][step % 4] (fp32; steps past K give 0), the B operand
+// of the zero-point fold.  One thread per (token, step), 128 codes summed
+// in fp32 (the sum needs at most 25 significant bits, so it is exact or
+// off by one rounding).
+__global__ __launch_bounds__(256) void i5_act_sums_kernel(const uint8_t* __restrict__ x8, int M, int K, int c_pad,
+                                                          float* __restrict__ rs) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int s_pad = 4 * c_pad;
+    if (i >= (int64_t)M * s_pad) return;
+    const int s = (int)(i % s_pad);
+    const int64_t m = i / s_pad;
+    float acc = 0.f;
+    if (s < K / 128) {
+        const uint4* p = reinterpret_cast<const uint4*>(x8 + m * K + 128 * (int64_t)s);
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[e], 1.0f, false);
+                const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[e], 1.0f, true);
+                acc += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+            }
+        }
+    }
+    rs[((int64_t)(s >> 2) * M + m) * 4 + (s & 3)] = acc;
+}
+
 template <int BM, int BN, int NS, int WF>
 hipError_t launch_pf(const PfArgs& a, hipStream_t stream) {
     const int total = a.tiles_m * a.tiles_n * a.ks;
@@ -2021,6 +2176,85 @@ static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
         }
     }
     return t;
+}
+
+// int5 tiles: 64 rows (M <= 64), 128 (M <= 128), else 256; always 128 wide
+// (the chunk's fifth-bit planes and activation sums need LDS beside the
+// 256-row stages); K split as tiled_shape does when the tiles are few
+static TiledShape i5_tiled_shape(int64_t M, int64_t N, int64_t K) {
+    TiledShape t{};
+    t.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+    t.bn = 128;
+    t.tiles_m = (int)((M + t.bm - 1) / t.bm);
+    t.tiles_n = (int)((N + 127) / 128);
+    const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n, steps = K / 128;
+    t.ks = 1;
+    t.s_per = (int)steps;
+    if (tiles < 128 && steps >= 16) {
+        int64_t k = 256 / tiles;
+        int64_t per = (steps + k - 1) / k;
+        per = (per + 3) / 4 * 4;
+        if (per < 8) per = 8;
+        k = (steps + per - 1) / per;
+        if (k > 1) {
+            t.ks = (int)k;
+            t.s_per = (int)per;
+        }
+    }
+    return t;
+}
+// workspace: the activation sums [c_pad][M][4] fp32 and 4 KiB that the last
+// tiles' copies may read past them, then (K split) the counter region and
+// the fp32 partials
+static size_t i5_sums_bytes(int64_t M, int64_t K) {
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    return (size_t)((c_pad * M * 16 + 4096 + 255) / 256 * 256);
+}
+size_t i5_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const TiledShape t = i5_tiled_shape(M, N, K);
+    size_t b = i5_sums_bytes(M, K);
+    if (t.ks > 1) b += ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
+    return b;
+}
+bool i5_tiled_fits(int64_t M, int64_t K) {
+    // 32-bit buffer offsets: the activation block of a 256-row tile and the
+    // per-chunk offset into the sums
+    return K <= kPreparedTiledMaxK && (K / 128 + 3) / 4 * M * 16 + 4096 <= (int64_t)UINT32_MAX;
+}
+
+hipError_t launch_prepared_tiled_i5(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* w5,
+                                    const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                    hipStream_t stream) {
+    if (!ws || !i5_tiled_fits(M, K)) return hipErrorInvalidValue;
+    PfArgs a{};
+    a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
+    a.w5 = reinterpret_cast<const uint32_t*>(w5);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.tiles16 = (int)((N + 15) / 16);
+    a.group_m = 8;
+    const TiledShape t = i5_tiled_shape(M, N, K);
+    a.tiles_m = t.tiles_m;
+    a.tiles_n = t.tiles_n;
+    a.ks = t.ks;
+    a.s_per = t.s_per;
+    if ((int64_t)a.tiles_m * a.tiles_n * a.ks > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    float* rs = reinterpret_cast<float*>(wsb);
+    a.rs = rs;
+    if (a.ks > 1) a.partials = reinterpret_cast<float*>(wsb + i5_sums_bytes(M, K) + ws_counter_bytes(a.tiles16));
+    const int64_t n_sums = M * a.s_pad;
+    hipLaunchKernelGGL(i5_act_sums_kernel, dim3((unsigned)((n_sums + 255) / 256)), dim3(256), 0, stream, x8,
+                       (int)M, (int)K, a.c_pad, rs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (t.bm == 64) e = launch_pf<64, 128, 5, kWI5>(a, stream);
+    else if (t.bm == 128) e = launch_pf<128, 128, 4, kWI5>(a, stream);
+    else if (t.bm == 256) e = launch_pf<256, 128, 3, kWI5>(a, stream);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess || a.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4) {

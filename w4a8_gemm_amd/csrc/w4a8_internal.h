@@ -187,6 +187,11 @@ void prepared_i5_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* w5_bytes, 
 hipError_t launch_prepare_i5(const int32_t* qkn, const int32_t* qhi, const uint8_t* qz, const uint16_t* sc,
                              int64_t N, int64_t K, uint8_t* wt, uint8_t* w5, uint8_t* st, hipStream_t stream);
 // the split-K decode kernel on int5 weights, M <= 32
+size_t i5_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bool i5_tiled_fits(int64_t M, int64_t K);
+hipError_t launch_prepared_tiled_i5(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* w5,
+                                    const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
+                                    hipStream_t stream);
 hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* w5,
                                      const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws,
                                      hipStream_t stream);
