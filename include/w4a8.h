@@ -376,16 +376,22 @@ w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t *d_x_fp8, const float *
  * (fp32 accumulation; summation order may differ).  The split-K decode
  * kernel takes x . (c - 16) as four block-scaled fp4 x fp8 products per step
  * (two 2-bit halves of the low nibble, the fifth bit, a constant -16 term)
- * and adds (16 - z) times the group's activation sum before its scale.
+ * and adds (16 - z) times the group's activation sum before its scale.  The
+ * tile kernel widens c - 16 to e4m3 and adds the zero-point term per 4-step
+ * chunk from per-token, per-step activation sums that a pre-pass writes into
+ * the workspace.
  *   w4a8_int5g128_prepared_bytes: sizes of the three buffers (host): codes as
  *     the int4 fragment order, the fifth-bit plane (256 B per 16-row tile and
- *     step), 256-byte scale and zero records per tile and 4-step chunk.
+ *     step: one word per lane, the lane's 32 checkpoint bits with their 2-bit
+ *     units transposed as a 4 x 4 array), 256-byte scale and zero records per
+ *     tile and 4-step chunk.
  *   w4a8_int5g128_prepare_fragments: the checkpoint tensors -> the three
  *     buffers (16-byte aligned).  Asynchronous.
- *   w4a8_int5g128_gemm_prepared: any M >= 1; M <= 32 one pass of the split-K
- *     decode kernel, larger M that kernel on consecutive 32-row slices (the
- *     weights read once per slice: there is no tiled int5 kernel).
- *     Workspace sized with W4A8_WEIGHT_INT5G128_PREPARED.
+ *   w4a8_int5g128_gemm_prepared: any M >= 1; M <= 32 the split-K decode
+ *     kernel, larger M the tile kernel (64-, 128- or 256-row tiles, 128 wide;
+ *     K split across workgroups when the tiles are few).  The workspace
+ *     (sized with W4A8_WEIGHT_INT5G128_PREPARED) is required above M = 32:
+ *     it holds the activation sums; calls that overlap on one workspace race.
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_int5g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_w5_bytes,
