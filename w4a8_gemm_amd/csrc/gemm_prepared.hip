@@ -429,10 +429,10 @@ template <int WF>
 __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, const uint32_t* bp, int j,
                                           PChunk<WF>& c) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) c.w[u] = wp[(4 * j + u) * 64];
+    for (int u = 0; u < 4; ++u) c.w[u] = load_stream16(wp + (4 * j + u) * 64);
     if constexpr (WF == kWI5) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) c.b[u] = bp[(4 * j + u) * 64];
+        for (int u = 0; u < 4; ++u) c.b[u] = __builtin_nontemporal_load(bp + (4 * j + u) * 64);
     }
     if constexpr (WF == kWI4) {
 #pragma unroll
@@ -447,7 +447,7 @@ __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, const
             c.z[u] = *reinterpret_cast<const uint32_t*>(rec + 128 + 16 * u + 4 * g);
         }
     } else {
-        c.s = reinterpret_cast<const uint32_t*>(sp)[j * 64];
+        c.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp) + j * 64);
     }
 }
 
