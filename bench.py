@@ -216,7 +216,7 @@ def main():
     b1 = gemm_bytes(1, N, K)
     achieved = b1 / per_m[1] / 1e9
     roofline = {"bound": "hbm",
-                "kernel": "pdec_kernel<1,3,0,4> (fragment-order split-K decode), gate_up M=1; "
+                "kernel": "pdec_kernel<1,2,0,4> (fragment-order split-K decode), gate_up M=1; "
                           "average over graph replays of 64 launches rotating 8 weight copies",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic_record(),

@@ -115,7 +115,7 @@ __device__ __forceinline__ void i4_load(const I4DecArgs& a, int lane, const int*
         const int n0 = min(row0 + rt * 16 + 4 * g, a.N - 4);   // N % 8 == 0, so n0..n0+3 in range
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            c.w[rt][u] = load_stream16(reinterpret_cast<const uint4*>(wr + 16 * u));
+            c.w[rt][u] = *reinterpret_cast<const uint4*>(wr + 16 * u);
             c.s[rt][u] = *reinterpret_cast<const uint2*>(a.sc + (int64_t)(grp + u) * a.N + n0);
         }
     }

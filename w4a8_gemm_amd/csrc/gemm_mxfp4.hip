@@ -110,7 +110,7 @@ __device__ __forceinline__ void dec_load(const DecArgs& a, int lane, const int* 
         const uint8_t* er = a.we + (int64_t)rows[rt] * (a.K >> 5) + 4 * (int64_t)s;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            c.w[rt][u] = load_stream16(reinterpret_cast<const uint4*>(wr + 64 * u));
+            c.w[rt][u] = *reinterpret_cast<const uint4*>(wr + 64 * u);
             c.s[rt][u] = *reinterpret_cast<const uint32_t*>(er + 4 * u);
         }
     }

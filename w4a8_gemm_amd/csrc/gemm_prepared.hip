@@ -2077,9 +2077,11 @@ static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, bool int4, 
     *c_per = (int)cp;
 }
 
-// Decode plan: the shape above; ring depth 3 on MXFP4 weights at M <= 4 (and
-// M <= 8 on wide layers), else 2 (int4's split products hold more
-// registers); 4 activation loads per thread and batch when one batch covers
+// Decode plan: the shape above; ring depth 2 (with the weight stream loaded
+// non-temporally, depth 3 measured 2-4 % slower on every shape it had won
+// before: gate_up M = 1 / 4 / 8: 17.6 / 17.6 / 18.4 us at depth 2 against
+// 17.9 / 18.1 / 19.1, down_proj M = 1: 11.6 against 12.1, W4A4 alike);
+// 4 activation loads per thread and batch when one batch covers
 // the workgroup's slice or LDS bounds the workgroups per CU (fewer
 // registers, more resident waves), else 8.
 // Fitted to a sweep of ring depth x batch x tiles x K parts on gfx950 (graph
@@ -2102,10 +2104,9 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, 
         if (kw * tw > 16) kw = 16 / tw;
         if (kw > cp) kw = cp;
     }
-    const bool narrow = (N + 255) / 256 < 64;
     p.rt = tw;
     p.kw = kw;
-    p.u = depth > 0 ? depth : (!int4 && (M <= 4 || (!narrow && M <= 8)) ? 3 : 2);
+    p.u = depth > 0 ? depth : 2;
     const int64_t per_row = (int64_t)cp * 512 / (a4 ? 32 : 16);   // 16-byte activation loads per row
     p.ab = lds_bound || M * per_row <= 4 * 64 * (int64_t)tw * kw ? 4 : 8;
     p.ks = ks;

@@ -48,12 +48,13 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// A 16-byte load with the non-temporal hint: the decode kernels read each
-// weight (and scale) byte once per launch, and keeping it out of the caches'
-// reuse (gfx950 `nt`) measured 3-8 % faster on the decode weight stream
-// (gate_up M = 1: 18.8 -> 18.0 us; with the scale loads too, 17.8).  The
-// tile kernels' copies keep the default policy: there the hint slowed the
-// K-split down_proj tiles (M = 64: 24 -> 27 us).
+// A 16-byte load with the non-temporal hint: the fragment-order decode
+// kernel reads each weight (and scale) byte once per launch, and keeping it
+// out of the caches' reuse (gfx950 `nt`) measured 3-8 % faster on its weight
+// stream (gate_up M = 1: 18.8 -> 18.0 us; with the scale loads too, 17.8).
+// The tile kernels' copies keep the default policy (the hint slowed the
+// K-split down_proj tiles, M = 64: 24 -> 27 us), and so do the row-major
+// decode kernels (gate_up M = 1: 25 -> 29 us with it).
 __device__ __forceinline__ uint4 load_stream16(const uint4* p) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
