@@ -8,11 +8,14 @@ repacked once into matrix-core fragment order), for each batch M in
 block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights, one call
 of the linear entry point per M (at M = 1 one launch: the quantization runs in
 the split-K decode kernel's prologue; M = 8 the quant kernel and the decode
-kernel; M = 16 and 64 the quant kernel and the tiled kernel).  Steps rotate
-over eight copies of the weight (95 MB each, 758 MB in all, three times the
-256 MB Infinity Cache), so every weight byte of a step comes from HBM.  Each
-step is one HIP graph replay (captured once per weight copy), so host launch
-latency is not in the timed region.
+kernel; M = 16 and 64 the quant kernel and the tiled kernel).  The step's four
+linears read four different copies of the weight out of eight (95 MB each,
+758 MB in all, three times the 256 MB Infinity Cache; step s uses copies
+4s .. 4s + 3 mod 8), so between two reads of a copy seven others stream
+through and every weight byte of a step comes from HBM (with one copy per step
+the later linears found much of the weight still in the cache).  Each step is
+one HIP graph replay (one graph per pair of copy sets), so host launch latency
+is not in the timed region.
 
 value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
 weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
@@ -184,9 +187,10 @@ def main():
     def step(c):
         # the linear on bf16 activations: the per-token quantization runs in
         # the decode kernel's prologue where it fits (M = 1), else its own
-        # kernel before the GEMM
-        for M in DECODE_MS:
-            w4.mxfp4_linear_prepared(xs_bf16[M], pcopies[c], out=out[M], workspace=pws, x8=x8[M], xs=xsc[M])
+        # kernel before the GEMM; each M on its own weight copy
+        for i, M in enumerate(DECODE_MS):
+            w = pcopies[(len(DECODE_MS) * c + i) % COPIES]
+            w4.mxfp4_linear_prepared(xs_bf16[M], w, out=out[M], workspace=pws, x8=x8[M], xs=xsc[M])
 
     graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(COPIES)]
     step_bytes = sum(decode_bytes(M, N, K) for M in DECODE_MS)
