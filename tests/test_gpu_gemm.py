@@ -256,7 +256,7 @@ def test_mxfp4_prepared_gate_up(gate_up_mx, M):
     assert rel_frobenius(o1[mi, ni], ref) <= GEMM_REL_F
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 48, 64])
 def test_mxfp4_prepared_down_proj(M):
     d = synth.down_proj()
     x8, s = _acts(M, synth.INTERMEDIATE, (2, M))
@@ -342,8 +342,8 @@ def test_mxfp4_prepared_tiled_wide(M, N, K):
     assert (np.abs(got[mi, ni] - ref) <= slack).all()
 
 
-# narrow layers at 33 <= M <= 64: 64-row tiles, K split across workgroups
-# (fp32 partials + reduction) when long
+# narrow layers at 33 <= M <= 64: 64-row tiles 128 wide, K split across
+# workgroups (fp32 partials + reduction) when long
 @pytest.mark.parametrize("M,N,K", [(33, 16, 1152), (64, 200, 1024), (40, 2000, 2048), (48, 1000, 4096),
                                    (57, 301, 3200)])
 def test_mxfp4_prepared_narrow_mid(M, N, K):

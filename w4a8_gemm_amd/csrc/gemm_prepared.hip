@@ -2139,13 +2139,16 @@ size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4) {
 struct TiledShape {
     int bm, bn, tiles_m, tiles_n, ks, s_per;
 };
-static void tiled_grid(int64_t M, int64_t N, int bm, TiledShape& t) {
+static void tiled_grid(int64_t M, int64_t N, int bm, TiledShape& t, bool int4) {
     t.bm = bm;
     t.tiles_m = (int)((M + bm - 1) / bm);
     const int64_t wide = (int64_t)t.tiles_m * ((N + 255) / 256);
-    // 64-row tiles come only 256 wide (the router sends narrow layers at
-    // M <= 64 to other kernels; few of them are split in K instead)
-    t.bn = bm == 64 || wide >= 64 ? 256 : 128;
+    // 128 wide when 256-wide tiles would be few; int4's 64-row tiles stay 256
+    // wide.  MXFP4 on the down_proj shape at M = 48 / 64 (64-row tiles, K
+    // split): 22.7 / 24.2 us with 256-wide tiles, 20.0 / 20.7 with 128-wide
+    // ones (twice the workgroups, each splitting K as often); on gate_up the
+    // 128-wide tiles were slower (M = 64: 34.5 against 29.8 us).
+    t.bn = (bm == 64 && int4) || wide >= 64 ? 256 : 128;
     t.tiles_n = (int)((N + t.bn - 1) / t.bn);
 }
 static int64_t tiled_rounds(const TiledShape& t) {
@@ -2154,10 +2157,10 @@ static int64_t tiled_rounds(const TiledShape& t) {
 }
 static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
     TiledShape t{};
-    tiled_grid(M, N, M <= 64 ? 64 : 128, t);
+    tiled_grid(M, N, M <= 64 ? 64 : 128, t, int4);
     if (M > 128) {
         TiledShape t256{};
-        tiled_grid(M, N, 256, t256);
+        tiled_grid(M, N, 256, t256, int4);
         const bool take = int4 ? (int64_t)t256.tiles_m * t256.tiles_n >= 128
                                : 9 * tiled_rounds(t256) <= 5 * tiled_rounds(t);
         if (take) t = t256;
@@ -2302,6 +2305,7 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
         else return hipErrorInvalidValue;
     } else {
         if (bm == 64 && bn == 256) e = launch_pfp<64, 256, 5, kWMx>(a, stream);
+        else if (bm == 64 && bn == 128) e = launch_pfp<64, 128, 4, kWMx>(a, stream);
         else if (bm == 128 && bn == 128) e = launch_pfp<128, 128, 4, kWMx>(a, stream);
         else if (bm == 128 && bn == 256) e = launch_pfp<128, 256, 4, kWMx>(a, stream);
         else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWMx>(a, stream);
