@@ -2143,12 +2143,14 @@ static void tiled_grid(int64_t M, int64_t N, int bm, TiledShape& t, bool int4) {
     t.bm = bm;
     t.tiles_m = (int)((M + bm - 1) / bm);
     const int64_t wide = (int64_t)t.tiles_m * ((N + 255) / 256);
-    // 128 wide when 256-wide tiles would be few; int4's 64-row tiles stay 256
-    // wide.  MXFP4 on the down_proj shape at M = 48 / 64 (64-row tiles, K
-    // split): 22.7 / 24.2 us with 256-wide tiles, 20.0 / 20.7 with 128-wide
-    // ones (twice the workgroups, each splitting K as often); on gate_up the
-    // 128-wide tiles were slower (M = 64: 34.5 against 29.8 us).
-    t.bn = (bm == 64 && int4) || wide >= 64 ? 256 : 128;
+    // 128 wide when 256-wide tiles would be few.  On the down_proj shape at
+    // M = 48 / 64 (64-row tiles, K split): MXFP4 22.7 / 24.2 us with 256-wide
+    // tiles, 20.0 / 20.7 with 128-wide ones (twice the workgroups, each
+    // splitting K as often); int4 at M = 64 30.3 -> 28.7 us, with zero points
+    // 32.0 -> 29.8.  On gate_up the 128-wide tiles were slower (MXFP4 M = 64:
+    // 34.5 against 29.8 us).
+    (void)int4;
+    t.bn = wide >= 64 ? 256 : 128;
     t.tiles_n = (int)((N + t.bn - 1) / t.bn);
 }
 static int64_t tiled_rounds(const TiledShape& t) {
@@ -2293,12 +2295,14 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     hipError_t e;
     if (int4 && zp) {
         if (bm == 64 && bn == 256) e = launch_pf<64, 256, 5, kWI4Z>(a, stream);
+        else if (bm == 64 && bn == 128) e = launch_pf<64, 128, 5, kWI4Z>(a, stream);
         else if (bm == 128 && bn == 128) e = launch_pf<128, 128, 4, kWI4Z>(a, stream);
         else if (bm == 128 && bn == 256) e = launch_pf<128, 256, 4, kWI4Z>(a, stream);
         else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWI4Z>(a, stream);
         else return hipErrorInvalidValue;
     } else if (int4) {
         if (bm == 64 && bn == 256) e = launch_pf<64, 256, 5, kWI4>(a, stream);
+        else if (bm == 64 && bn == 128) e = launch_pf<64, 128, 5, kWI4>(a, stream);
         else if (bm == 128 && bn == 128) e = launch_pf<128, 128, 4, kWI4>(a, stream);
         else if (bm == 128 && bn == 256) e = launch_pf<128, 256, 4, kWI4>(a, stream);
         else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWI4>(a, stream);
