@@ -307,14 +307,15 @@ w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t *d_x_fp4, const uint8_t *d_x_e
  * 128-wide K step s, tiles major; lane L = n + 16g holds 16 bytes of codes of
  * row 16t+n: words 16s+4g .. 16s+4g+3 of the checkpoint layout (k = 128s+32g
  * .. +31, nibble j of a word is k = 8i + j).  Row scales: fp16 [tile][4-step
- * chunk][step][16 rows].  Rows are padded to 16 and steps to a multiple of
+ * chunk][row / 4][step][row % 4] (128 B per tile and chunk; the 16 lanes
+ * that share four output rows read 32 contiguous bytes).  Rows are padded to 16 and steps to a multiple of
  * 4 (code 8, scale 0).  The result equals
  * w4a8_int4g128_gemm's in value (fp32 accumulation; summation order may
  * differ).
  *   w4a8_int4g128_prepared_bytes: sizes of the two buffers (host).
  *   w4a8_int4g128_prepare_fragments: checkpoint qweight [K/8, N], qzeros
  *     [K/128, N/8] (all 0x77777777, else ASYMMETRIC), scales [K/128, N] fp16
- *     -> d_w_prepared (16-byte aligned), d_s_prepared (8-byte aligned).
+ *     -> d_w_prepared (16-byte aligned), d_s_prepared (16-byte aligned).
  *     Synchronizes `stream` (the check result is read back).
  *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
  *     kernels of w4a8_mxfp4_gemm_prepared (the split-K decode kernel for
@@ -344,8 +345,8 @@ w4a8_status w4a8_int4g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
  * group's activation sum is added per group before its scale.
  *   w4a8_int4g128_zp_prepared_bytes: sizes of the two buffers (host): the
  *     codes as w4a8_int4g128_prepare_fragments; per 16-row tile and 4-step
- *     chunk one 256-byte record of fp16 scales [step][row], bytes 16 - z
- *     [step][row] and padding.
+ *     chunk one 256-byte record of fp16 scales, bytes 16 - z (both in
+ *     lane-group order [row / 4][step][row % 4]) and padding.
  *   w4a8_int4g128_zp_prepare_fragments: qweight [K/8, N], qzeros [K/128, N/8],
  *     scales [K/128, N] fp16 -> d_w_prepared (16-byte aligned), d_s_prepared
  *     (16-byte aligned).  Any zero points; asynchronous.

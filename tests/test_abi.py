@@ -141,7 +141,7 @@ def test_gemm_validation(L):
     assert pf(_p(), _p(), _p(), 60, 256, _p(), _p(), None) == SHAPE
     assert pf(_p(), _p(), _p(), 64, 200, _p(), _p(), None) == SHAPE
     assert pf(_p(), _p(), _p(), 64, 256, _p(FAKE + 8), _p(), None) == INVALID   # 16-byte aligned
-    assert pf(_p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 4), None) == INVALID   # 8-byte aligned
+    assert pf(_p(), _p(), _p(), 64, 256, _p(), _p(FAKE + 8), None) == INVALID   # 16-byte aligned
     ip = L.w4a8_int4g128_gemm_prepared
     assert ip(_p(), _p(), _p(), _p(), _p(), 4, 60, 256, None, 0, None) == SHAPE  # N % 8
     assert ip(_p(), _p(), _p(), _p(), _p(), 4, 64, 192, None, 0, None) == SHAPE  # K % 128

@@ -436,8 +436,8 @@ def _unprepare_int4(wt, st, N, K):
     s4 = 4 * ((steps + 3) // 4)
     w = wt.view(np.uint32).reshape(tiles, s4, 4, 16, 4)           # t, s, g, n, word
     w = w.transpose(0, 3, 1, 2, 4).reshape(tiles * 16, s4 * 16)     # word 16s + 4g + i
-    sc = st.view(np.uint16).reshape(tiles, s4 // 4, 4, 16)        # t, chunk, step, n
-    sc = sc.transpose(0, 3, 1, 2).reshape(tiles * 16, s4)
+    sc = st.view(np.uint16).reshape(tiles, s4 // 4, 4, 4, 4)     # t, chunk, n / 4, step, n % 4
+    sc = sc.transpose(0, 2, 4, 1, 3).reshape(tiles * 16, s4)
     return w, sc
 
 

@@ -75,8 +75,8 @@ def test_int4_zp_symmetric_zeros_equal_symmetric_kernels(M, N, K):
 
 
 def test_int4_zp_prepared_records():
-    # the record of tile 0, chunk 0: scales of steps 0..3 x rows 0..15, then
-    # the bytes 16 - z, then zero padding; rows past N: scale 0, z = 8
+    # the records: scales of steps 0..3 x rows 0..15, then the bytes 16 - z,
+    # both in lane-group order, then zero padding; rows past N: scale 0, z = 8
     N, K = 24, 640
     q = synth.int4_zp(N, K, seed=44)
     pw = w4.int4g128_zp_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]), dev_f16(q["scales"]))
@@ -88,8 +88,9 @@ def test_int4_zp_prepared_records():
     for t in range(2):
         for c in range(c_pad):
             rec = st[(t * c_pad + c) * 256:(t * c_pad + c + 1) * 256]
-            sc = rec[:128].view(np.uint16).reshape(4, 16)
-            zb = rec[128:192].reshape(4, 16)
+            # lane-group order [row / 4][step][row % 4] -> [step][row]
+            sc = rec[:128].view(np.uint16).reshape(4, 4, 4).transpose(1, 0, 2).reshape(4, 16)
+            zb = rec[128:192].reshape(4, 4, 4).transpose(1, 0, 2).reshape(4, 16)
             assert (rec[192:] == 0).all()
             for u in range(4):
                 s_ = 4 * c + u

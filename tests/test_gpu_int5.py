@@ -96,7 +96,7 @@ def test_int5_prepared_planes():
     for t in range(2):
         for c in range(c_pad):
             rec = st[(t * c_pad + c) * 256:(t * c_pad + c + 1) * 256]
-            zb = rec[128:192].view(np.int8).reshape(4, 16)
+            zb = rec[128:192].view(np.int8).reshape(4, 4, 4).transpose(1, 0, 2).reshape(4, 16)   # [step][row]
             for u in range(4):
                 for r in range(16):
                     n, s_ = 16 * t + r, 4 * c + u

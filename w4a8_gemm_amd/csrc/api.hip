@@ -250,7 +250,7 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
                                  void* d_ws, size_t ws_bytes, void* stream, bool int4, bool zp = false) {
     w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
-    if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
+    if (!d_s || !aligned(d_s, int4 ? 16 : 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     // the tiled kernel addresses activations with 32-bit offsets
     const PreparedRoute route = prepared_route(M, N, K, int4);
@@ -280,7 +280,7 @@ static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const 
     if (ldx < K || ldx > kMaxDim) return ldx < K ? W4A8_ERR_UNSUPPORTED_SHAPE : W4A8_ERR_INVALID_ARG;
     w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
-    if (!d_s || !aligned(d_s, int4 ? 8 : 4)) return W4A8_ERR_INVALID_ARG;
+    if (!d_s || !aligned(d_s, int4 ? 16 : 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     GemmPlan p{};
     const bool vec = aligned(d_x_bf16, 16) && ldx % 8 == 0;
@@ -346,7 +346,7 @@ w4a8_status w4a8_int4g128_prepare_fragments(const int32_t* d_qweight_kn, const i
     if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
     if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
     if (!aligned(d_qweight_kn, 4) || !aligned(d_qzeros, 4) || !aligned(d_scales_f16, 2) ||
-        !aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 8))
+        !aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 16))
         return W4A8_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     // the first prepared word serves as the mismatch counter before the repack

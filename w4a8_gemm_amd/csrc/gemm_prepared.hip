@@ -81,8 +81,10 @@ __device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, 
 //         kernels widen c - z directly (exact in e4m3: -16..14), each lane
 //         through the 16-byte table of its row's z, read from a 16-table LDS
 //         block.  Scales and zeros share one 256-byte record per 16-row tile
-//         and 4-step chunk: fp16 scales [step][row], then bytes 16 - z
-//         [step][row], then padding.
+//         and 4-step chunk: fp16 scales, then bytes 16 - z, then padding,
+//         scales and bytes in lane-group order [row / 4][step][row % 4]
+//         (a decode lane reads its chunk's scales as 32 contiguous bytes
+//         and its zero bytes as 16).
 //   kWI5  int5 g128: the low four bits of each code as kWI4's nibbles, the
 //         fifth bits in a plane of one word per lane and step whose bit
 //         8 q + 2 i + p is the fifth bit of the lane's code 8 i + 2 q + p
@@ -300,12 +302,16 @@ __global__ __launch_bounds__(256) void prep_i4s_kernel(const uint16_t* __restric
     const int64_t tc = i >> 6;
     const int c = (int)(tc % c_pad), t = (int)(tc / c_pad);
     const int s = 4 * c + u, n = 16 * t + r;
-    st[i] = (n < N && s < K / 128) ? sc[(int64_t)s * N + n] : (uint16_t)0;
+    // lane-group order: rows 4q .. 4q + 3 of all four steps in 32 bytes
+    st[tc * 64 + 16 * (r >> 2) + 4 * u + (r & 3)] = (n < N && s < K / 128) ? sc[(int64_t)s * N + n] : (uint16_t)0;
 }
 
 // int4 with zero points: one 256-byte record per (16-row tile, 4-step chunk):
-// fp16 scales [step][row] (bytes 0..127), bytes 16 - z [step][row] (128..191;
-// z - 1 is nibble n % 8 of qzeros[s, n / 8]), zero padding (192..255).  Rows
+// fp16 scales (bytes 0..127), bytes 16 - z (128..191; z - 1 is nibble n % 8
+// of qzeros[s, n / 8]), zero padding (192..255); scales and bytes in
+// lane-group order [row / 4][step][row % 4], so that the 16 lanes that share
+// four output rows read their chunk's scales as 32 contiguous bytes and
+// their zero bytes as 16.  Rows
 // past N and steps past K get scale 0 and z = 8.  One thread per (record, step,
 // row), the first 64 also clearing the padding.
 __global__ __launch_bounds__(256) void prep_i4zs_kernel(const uint16_t* __restrict__ sc,
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(256) void prep_i4zs_kernel(const uint16_t* __restri
     const int s = 4 * c + u, n = 16 * t + r;
     const bool in = n < N && s < K / 128;
     uint8_t* rec = st + 256 * tc;
-    const int e = 16 * u + r;
+    const int e = 16 * (r >> 2) + 4 * u + (r & 3);
     reinterpret_cast<uint16_t*>(rec)[e] = in ? sc[(int64_t)s * N + n] : (uint16_t)0;
     rec[128 + e] = in ? (uint8_t)(15u - ((qz[(int64_t)s * (N / 8) + n / 8] >> (4 * (n % 8))) & 15u)) : (uint8_t)8;
     rec[192 + e] = 0;
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256) void prep_i5s_kernel(const uint16_t* __restric
     const int s = 4 * c + u, n = 16 * t + r;
     const bool in = n < N && s < K / 128;
     uint8_t* rec = st + 256 * tc;
-    const int e = 16 * u + r;
+    const int e = 16 * (r >> 2) + 4 * u + (r & 3);
     reinterpret_cast<uint16_t*>(rec)[e] = in ? sc[(int64_t)s * N + n] : (uint16_t)0;
     rec[128 + e] = in ? (uint8_t)(int8_t)(15 - (int)qz[(int64_t)s * N + n]) : (uint8_t)0;
     rec[192 + e] = 0;
@@ -434,17 +440,24 @@ __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, const
 #pragma unroll
         for (int u = 0; u < 4; ++u) c.b[u] = __builtin_nontemporal_load(bp + (4 * j + u) * 64);
     }
-    if constexpr (WF == kWI4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) c.s[u] = reinterpret_cast<const uint2*>(sp)[j * 16 + u * 4];
-    } else if constexpr (WF == kWI4Z || WF == kWI5) {
-        // sp: the tile's record of the wave's first chunk (256 bytes per chunk)
-        const int g = (threadIdx.x & 63) >> 4;
-        const uint8_t* rec = reinterpret_cast<const uint8_t*>(sp) + 256 * j;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            c.s[u] = *reinterpret_cast<const uint2*>(rec + 32 * u + 8 * g);
-            c.z[u] = *reinterpret_cast<const uint32_t*>(rec + 128 + 16 * u + 4 * g);
+    if constexpr (WF == kWI4 || WF == kWI4Z || WF == kWI5) {
+        // sp: the lane group's 32 scale bytes in the wave's first chunk
+        // record (128 bytes per chunk, or 256 with the zero bytes 128 on)
+        constexpr int kRec = WF == kWI4 ? 128 : 256;
+        const uint8_t* rec = reinterpret_cast<const uint8_t*>(sp) + kRec * j;
+        const uint4 s01 = *reinterpret_cast<const uint4*>(rec);
+        const uint4 s23 = *reinterpret_cast<const uint4*>(rec + 16);
+        c.s[0] = make_uint2(s01.x, s01.y);
+        c.s[1] = make_uint2(s01.z, s01.w);
+        c.s[2] = make_uint2(s23.x, s23.y);
+        c.s[3] = make_uint2(s23.z, s23.w);
+        if constexpr (WF != kWI4) {
+            // the zero bytes: 16 per lane group, 128 + 16 q from the record
+            const uint4 z = *reinterpret_cast<const uint4*>(rec + 128 - 16 * ((threadIdx.x & 63) >> 4));
+            c.z[0] = z.x;
+            c.z[1] = z.y;
+            c.z[2] = z.z;
+            c.z[3] = z.w;
         }
     } else {
         c.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp) + j * 64);
@@ -658,9 +671,9 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const uint32_t* bp = WF == kWI5 ? a.w5 + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane : nullptr;
     const void* sp;
     if constexpr (WF == kWI4)
-        sp = reinterpret_cast<const uint2*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 16 + (lane >> 4);
+        sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 128 + 32 * (lane >> 4);
     else if constexpr (WF == kWI4Z || WF == kWI5)
-        sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 256;
+        sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 256 + 32 * (lane >> 4);
     else
         sp = reinterpret_cast<const uint32_t*>(a.st) + ((int64_t)tc * a.c_pad + c0 + jb) * 64 + lane;
     const int last = nch > 0 ? nch - 1 : 0;
@@ -924,7 +937,8 @@ struct PfShape {
 
 // Scale buffer of one 4-step chunk: MXFP4 e8m0 dwords (256 B per tile, lane
 // order, BN/128 copies per wave), or int4 row scales (128 B per tile = 4 steps
-// x 16 fp16, one 256-byte copy per wave: wave w's 256 bytes hold the records
+// x 16 fp16 in lane-group order [row / 4][step][row % 4], one 256-byte copy
+// per wave: wave w's 256 bytes hold the records
 // of tiles (BN/128) w and (BN/128) w + 1 -- for BN = 128 the second half holds
 // the next tile's record and is not read), or the int4 records with zero
 // points (256 B per tile, copied as the MXFP4 ones).
@@ -951,8 +965,8 @@ __device__ __forceinline__ typename WStep<WF>::T pf_scale(const uint8_t* sbuf, i
         return reinterpret_cast<const uint32_t*>(sbuf)[64 * b + lane] >> (8 * (s & 3));
     } else {
         constexpr int TPW = BN / 128;   // tiles per wave record
-        return *reinterpret_cast<const uint2*>(sbuf + 256 * (b / TPW) + 128 * (b % TPW) + 32 * (s & 3) +
-                                               8 * (lane >> 4));
+        return *reinterpret_cast<const uint2*>(sbuf + 256 * (b / TPW) + 128 * (b % TPW) + 32 * (lane >> 4) +
+                                               8 * (s & 3));
     }
 }
 
@@ -1287,8 +1301,9 @@ __device__ __forceinline__ void pfi_zero_fold(const uint8_t* sbuf, int wn, int l
 #pragma unroll
     for (int f = 0; f < W::FN; ++f) {
         const uint8_t* rec = sbuf + 256 * (wn * W::FN + f);
-        const uint32_t h = *reinterpret_cast<const uint16_t*>(rec + 2 * (16 * u + r));
-        zs[f] = f16_to_f32(h) * (float)(int)(int8_t)rec[128 + 16 * u + r];
+        const int e = 16 * (r >> 2) + 4 * u + (r & 3);      // lane-group order
+        const uint32_t h = *reinterpret_cast<const uint16_t*>(rec + 2 * e);
+        zs[f] = f16_to_f32(h) * (float)(int)(int8_t)rec[128 + e];
     }
     const float* sums = reinterpret_cast<const float*>(sbuf + SC::REC + SC::PLANES);
 #pragma unroll
@@ -1318,7 +1333,7 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
         q[f] = *reinterpret_cast<const uint4*>(wp + 1024 * f);
         if constexpr (WF == kWI5) {
             // record of tile b (scales as kWI4Z's); the lane's plane word of step s
-            sc[f] = *reinterpret_cast<const uint2*>(sbuf + 256 * (wn * W::FN + f) + 32 * (s & 3) + 8 * g);
+            sc[f] = *reinterpret_cast<const uint2*>(sbuf + 256 * (wn * W::FN + f) + 32 * g + 8 * (s & 3));
             pl[f] = *reinterpret_cast<const uint32_t*>(sbuf + PfScales<BN, kWI5, BM>::REC + 1024 * (wn * W::FN + f) +
                                                        256 * (s & 3) + 4 * lane);
         } else if constexpr (WF == kWI4Z) {
@@ -1326,8 +1341,9 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
             // byte 16 - z of its weight-operand row (row lane % 16) picks the
             // table z - 1
             const uint8_t* rec = sbuf + 256 * (wn * W::FN + f);
-            sc[f] = *reinterpret_cast<const uint2*>(rec + 32 * (s & 3) + 8 * g);
-            const uint32_t zb = rec[128 + 16 * (s & 3) + (lane & 15)];
+            sc[f] = *reinterpret_cast<const uint2*>(rec + 32 * g + 8 * (s & 3));
+            const int r = lane & 15;
+            const uint32_t zb = rec[128 + 16 * (r >> 2) + 4 * (s & 3) + (r & 3)];
             tz[f] = *reinterpret_cast<const uint4*>(zt + 16 * ((15u - zb) & 15u));
         } else {
             sc[f] = pf_scale<BN, kWI4>(sbuf, wn * W::FN + f, s, lane);
