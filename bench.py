@@ -477,7 +477,7 @@ def extra_measurements(torch, w4, synth, timer, graph_of, log, nv_p, nv_s, g, wp
 
     def int_family(q, prep, gemm, kind, extra_bits):
         copies = [prep(q) for _ in range(8)]
-        ws = w4.Workspace(64, q["N"], q["K"], kind, dev)
+        ws = w4.Workspace(2048, q["N"], q["K"], kind, dev)
         out = {}
         for M in (1, 16, 64, 2048):
             xb = torch.from_numpy(synth.acts(M, q["K"], seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -2196,6 +2196,22 @@ static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
             t.ks = (int)k;
             t.s_per = (int)per;
         }
+    } else if (int4 && tiles < 256 && steps >= 48) {
+        // int4 tiles (vector-ALU bound, long per workgroup) that leave CUs
+        // idle in their one round: split K so that the workgroups fill two
+        // rounds with less work each (down_proj-shaped M = 2048, 160 tiles:
+        // three splits, 306 -> 289 us; MXFP4 tiles, bound by their copy
+        // feed, lost 10 % the same way and are not split)
+        int64_t k = 512 / tiles;
+        if ((tiles * k + 255) / 256 < k) {
+            int64_t per = (steps + k - 1) / k;
+            per = (per + 3) / 4 * 4;
+            k = (steps + per - 1) / per;
+            if (k > 1) {
+                t.ks = (int)k;
+                t.s_per = (int)per;
+            }
+        }
     }
     return t;
 }
