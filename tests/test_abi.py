@@ -177,10 +177,12 @@ def test_prepared_tiled_split_workspace(L):
         assert L.w4a8_gemm_workspace_bytes(M, N, K, kind) == want
         assert L.w4a8_gemm_workspace_bytes(M + 64, N, K, kind) >= want
     # many tiles: no split, the decode band's need is all that remains (MXFP4);
-    # int4 also splits K in three where 160 256-row tiles (M = 2048) would
-    # leave CUs idle, the largest need up to M = 4096
+    # int4 also splits K where fewer tiles than CUs leave some idle: 160
+    # 256-row tiles at M = 2048 in three, 180 at M = 2304 in four (the largest
+    # need up to M = 4096)
     assert L.w4a8_gemm_workspace_bytes(4096, N, K, 2) == L.w4a8_gemm_workspace_bytes(1024, N, K, 2)
-    assert L.w4a8_gemm_workspace_bytes(4096, N, K, 3) == header + 3 * 2048 * N * 4
+    assert L.w4a8_gemm_workspace_bytes(2048, N, K, 3) == header + 3 * 2048 * N * 4
+    assert L.w4a8_gemm_workspace_bytes(4096, N, K, 3) == header + 4 * 2304 * N * 4
     g = L.w4a8_mxfp4_gemm_prepared
     assert g(_p(), _p(), _p(), _p(), _p(), M, N, K, None, 0, None) == WORKSPACE
     assert g(_p(), _p(), _p(), _p(), _p(), M, N, K, _p(), want - 256, None) == WORKSPACE

@@ -2173,6 +2173,35 @@ static int64_t tiled_rounds(const TiledShape& t) {
     const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n;
     return tiles < 128 ? 1 : (tiles + 255) / 256;      // few tiles: K split fills one round
 }
+// K splits (2-4) for at least 128 tiles of the widening kernels (int4, int5:
+// vector-ALU bound, long per workgroup): the count that minimises the rounds
+// of workgroups per split over 256 CUs, taken when it cuts them by a fifth
+// or more, else 1.  160 tiles: 3 (two rounds of a third each); 320: 4 (five
+// rounds of a quarter, against two whole ones).
+static int64_t rounds_split(int64_t tiles) {
+    const double whole = (double)((tiles + 255) / 256);
+    int64_t best = 1;
+    double best_cost = whole;
+    for (int64_t k = 2; k <= 4; ++k) {
+        const double c = (double)((tiles * k + 255) / 256) / (double)k;
+        if (c < whole * 0.8 && c < best_cost) {
+            best = k;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+static void apply_split(TiledShape& t, int64_t steps, int64_t k) {
+    if (k <= 1) return;
+    int64_t per = (steps + k - 1) / k;
+    per = (per + 3) / 4 * 4;
+    k = (steps + per - 1) / per;
+    if (k > 1) {
+        t.ks = (int)k;
+        t.s_per = (int)per;
+    }
+}
+
 static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
     TiledShape t{};
     tiled_grid(M, N, M <= 64 ? 64 : 128, t, int4);
@@ -2197,21 +2226,12 @@ static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
             t.s_per = (int)per;
         }
     } else if (int4 && tiles < 256 && steps >= 48) {
-        // int4 tiles (vector-ALU bound, long per workgroup) that leave CUs
-        // idle in their one round: split K so that the workgroups fill two
-        // rounds with less work each (down_proj-shaped M = 2048, 160 tiles:
-        // three splits, 306 -> 289 us; MXFP4 tiles, bound by their copy
-        // feed, lost 10 % the same way and are not split)
-        int64_t k = 512 / tiles;
-        if ((tiles * k + 255) / 256 < k) {
-            int64_t per = (steps + k - 1) / k;
-            per = (per + 3) / 4 * 4;
-            k = (steps + per - 1) / per;
-            if (k > 1) {
-                t.ks = (int)k;
-                t.s_per = (int)per;
-            }
-        }
+        // int4 tiles that leave CUs idle in their one round (down_proj-shaped
+        // M = 2048, 160 tiles: three splits, 306 -> 289 us).  From 256 tiles
+        // on the partials outweigh it (M = 4096, 320 tiles, four splits: 3-5 %
+        // for a 335 MB workspace), and MXFP4 tiles, bound by their copy
+        // feed, lost 10 % at 160 tiles: neither is split.
+        apply_split(t, steps, rounds_split(tiles));
     }
     return t;
 }
@@ -2238,6 +2258,10 @@ static TiledShape i5_tiled_shape(int64_t M, int64_t N, int64_t K) {
             t.ks = (int)k;
             t.s_per = (int)per;
         }
+    } else if (steps >= 48) {
+        // a short last round (down_proj-shaped M = 1024 / 2048: 160 / 320
+        // tiles, three / four splits: 249 -> 222 us and 473 -> 404 us)
+        apply_split(t, steps, rounds_split(tiles));
     }
     return t;
 }
