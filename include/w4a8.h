@@ -382,9 +382,9 @@ w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t *d_x_fp8, const float *
  * chunk from per-token, per-step activation sums that a pre-pass writes into
  * the workspace.
  *   w4a8_int5g128_prepared_bytes: sizes of the three buffers (host): codes as
- *     the int4 fragment order, the fifth-bit plane (256 B per 16-row tile and
- *     step: one word per lane, the lane's 32 checkpoint bits with their 2-bit
- *     units transposed as a 4 x 4 array), 256-byte scale and zero records per
+ *     the int4 fragment order, the fifth-bit plane (one word per 16-row tile,
+ *     step and lane, [tile][4-step chunk][lane][step]: the lane's 32
+ *     checkpoint bits with their 2-bit units transposed as a 4 x 4 array), 256-byte scale and zero records per
  *     tile and 4-step chunk.
  *   w4a8_int5g128_prepare_fragments: the checkpoint tensors -> the three
  *     buffers (16-byte aligned).  Asynchronous.

@@ -83,14 +83,14 @@ def test_int5_prepared_planes():
     q = synth.int5(N, K, seed=65)
     pw = _prep(q)
     s_pad = 4 * ((K // 128 + 3) // 4)
-    w5 = pw.w5.cpu().numpy().view(np.uint32).reshape(2, s_pad, 64)
+    w5 = pw.w5.cpu().numpy().view(np.uint32).reshape(2, s_pad // 4, 64, 4)     # tile, chunk, lane, step
     hi = _transposed(q["qweight_hi"].view(np.uint32))
     for t in range(2):
         for s_ in range(s_pad):
             for L in range(64):
                 row, g = 16 * t + (L & 15), L >> 4
                 want = hi[4 * s_ + g, row] if row < N and s_ < K // 128 else 0
-                assert w5[t, s_, L] == want
+                assert w5[t, s_ // 4, L, s_ % 4] == want
     st = pw.s.cpu().numpy()
     c_pad = s_pad // 4
     for t in range(2):

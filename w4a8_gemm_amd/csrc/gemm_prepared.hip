@@ -90,7 +90,8 @@ __device__ __forceinline__ v4f mfma44(v8i a_fp4, v8i b_fp4, v4f c, int scale_a, 
 //         8 q + 2 i + p is the fifth bit of the lane's code 8 i + 2 q + p
 //         (the checkpoint word with its 2-bit units transposed as a 4 x 4
 //         array, so that each byte's bits for even and odd codes sit in
-//         one column).  The split-K decode kernel takes c - 16 = 2 v(c & 3) +
+//         one column), stored [tile][chunk][lane][step] so that a lane
+//         reads a chunk's four words with one load.  The split-K decode kernel takes c - 16 = 2 v(c & 3) +
 //         8 v((c >> 2) & 3) + 16 b4 - 16 as four fp4 x fp8 products (the
 //         fifth bits spread to e2m1 1.0 nibbles, scale 16) and folds
 //         (16 - z) x sum(x) per step.  The tiled kernel widens c - 16 to e4m3
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(256) void prep_i4zs_kernel(const uint16_t* __restri
     rec[192 + e] = 0;
 }
 
-// int5: the fifth-bit plane, one word per (tile, step, lane): lane L's 32
+// int5: the fifth-bit plane, one word per (tile, chunk, lane, step): lane L's 32
 // codes (row 16t + L % 16, k = 128s + 32(L / 16) + j) are bits j of the
 // checkpoint word qweight_hi[4s + L / 16, row]; zero past N or K
 __global__ __launch_bounds__(256) void prep_i5b_kernel(const uint32_t* __restrict__ qhi, int N, int K, int tiles,
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(256) void prep_i5b_kernel(const uint32_t* __restric
     uint32_t o = 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) o |= ((h >> (8 * (u >> 2) + 2 * (u & 3))) & 3u) << (8 * (u & 3) + 2 * (u >> 2));
-    w5[i] = o;
+    // [tile][chunk][lane][step]: a lane's four words of a chunk are one 16-byte load
+    w5[(((int64_t)t * (s_pad >> 2) + (s >> 2)) * 64 + L) * 4 + (s & 3)] = o;
 }
 
 // int5 records as the int4 zero-point ones, the zero byte holding 16 - z as
@@ -393,7 +395,7 @@ struct PDecArgs {
     const uint8_t* x8;      // fp8 [M, K] (W4A4: e2m1 codes [M, K/2])
     const float* xs;        // token scales (W4A4: none)
     const uint8_t* xe;      // W4A4: activation e8m0 [M, K/32]
-    const uint32_t* w5;     // int5: fifth-bit plane, one word per lane and step
+    const uint32_t* w5;     // int5: fifth-bit plane [tile][chunk][lane][step] words
     const uint16_t* xb;     // fused quant: bf16 activations, row stride ldx elements
     int64_t ldx;
     uint8_t* x8_out;        // fused quant: e4m3 codes [M, K] and token scales [M] written
@@ -437,8 +439,12 @@ __device__ __forceinline__ void pdec_load(const uint4* wp, const void* sp, const
 #pragma unroll
     for (int u = 0; u < 4; ++u) c.w[u] = load_stream16(wp + (4 * j + u) * 64);
     if constexpr (WF == kWI5) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) c.b[u] = __builtin_nontemporal_load(bp + (4 * j + u) * 64);
+        // the lane's four plane words of chunk j
+        const uint4 b = load_stream16(reinterpret_cast<const uint4*>(bp) + 64 * j);
+        c.b[0] = b.x;
+        c.b[1] = b.y;
+        c.b[2] = b.z;
+        c.b[3] = b.w;
     }
     if constexpr (WF == kWI4 || WF == kWI4Z || WF == kWI5) {
         // sp: the lane group's 32 scale bytes in the wave's first chunk
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     const int jb = nch > 0 ? j0 : 0;
     const uint4* wp = a.wt + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane;
     // int5: the same lane's fifth-bit words (one per step)
-    const uint32_t* bp = WF == kWI5 ? a.w5 + ((int64_t)tc * a.s_pad + 4 * (int64_t)(c0 + jb)) * 64 + lane : nullptr;
+    const uint32_t* bp = WF == kWI5 ? a.w5 + (((int64_t)tc * (a.s_pad >> 2) + c0 + jb) * 64 + lane) * 4 : nullptr;
     const void* sp;
     if constexpr (WF == kWI4)
         sp = a.st + ((int64_t)tc * a.c_pad + c0 + jb) * 128 + 32 * (lane >> 4);
@@ -874,7 +880,7 @@ struct PfArgs {
     int ks, s_per;              // K splits (steps s_per each, a multiple of 4; ks = 1: none)
     float* partials;            // ks > 1: fp32 [ks][M][N], token scale not applied
     const uint8_t* xe;          // W4A4: activation e8m0 [M, K/32] (x8 then holds e2m1 [M, K/2])
-    const uint32_t* w5;         // int5: fifth-bit plane [tile][step][lane]
+    const uint32_t* w5;         // int5: fifth-bit plane [tile][chunk][lane][step]
     const float* rs;            // int5: activation sums [chunk][M][4 steps] (fp32)
 };
 
@@ -944,7 +950,7 @@ struct PfShape {
 // points (256 B per tile, copied as the MXFP4 ones).
 template <int WF> constexpr bool kRec256 = WF == kWMx || WF == kWI4Z || WF == kWI5;
 // int5 adds, per chunk, the fifth-bit planes of the panel's tiles (1 KiB per
-// tile: [step][lane] words) and the activation sums of the tile's rows (16 B
+// tile: [lane][step] words) and the activation sums of the tile's rows (16 B
 // per row: [row][step], at least 128 rows so that every wave copies alike)
 template <int BM> constexpr int kI5SumRows = BM > 128 ? BM : 128;
 template <int BN, int WF, int BM = 0>
@@ -1335,7 +1341,7 @@ __device__ __forceinline__ void pfi_compute(const uint8_t* st, int s, int wn, in
             // record of tile b (scales as kWI4Z's); the lane's plane word of step s
             sc[f] = *reinterpret_cast<const uint2*>(sbuf + 256 * (wn * W::FN + f) + 32 * g + 8 * (s & 3));
             pl[f] = *reinterpret_cast<const uint32_t*>(sbuf + PfScales<BN, kWI5, BM>::REC + 1024 * (wn * W::FN + f) +
-                                                       256 * (s & 3) + 4 * lane);
+                                                       16 * lane + 4 * (s & 3));
         } else if constexpr (WF == kWI4Z) {
             // record of tile b: scales of the lane's output rows; the zero
             // byte 16 - z of its weight-operand row (row lane % 16) picks the
