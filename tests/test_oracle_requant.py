@@ -37,6 +37,35 @@ def test_dequant_nvfp4_golden(orc):
         assert (w == np.float32(expect)).all(), (sb, gd, code, w[0, :4])
 
 
+def _e4m3_exact(b):
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def test_dequant_golden_rows_fix_the_rounding_order():
+    """The golden rows separate the page's order (divide the scale by the
+    divisor, then multiply by the code) from the two other fp32 orders: an
+    oracle that multiplied first, or multiplied by the divisor's reciprocal,
+    would fail at least one row of test_dequant_nvfp4_golden."""
+    f = np.float32
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    orders = {
+        "divide_first": lambda c, s, g: f(f(c) * f(f(s) / f(g))),
+        "multiply_first": lambda c, s, g: f(f(f(c) * f(s)) / f(g)),
+        "reciprocal": lambda c, s, g: f(f(c) * f(f(s) * f(f(1.0) / f(g)))),
+    }
+    fails = {k: 0 for k in orders}
+    for sb, gd, code, expect in _rows("nvfp4_layout.txt"):
+        c = int(code)
+        cv = -grid[c & 7] if c & 8 else grid[c & 7]
+        for name, fn in orders.items():
+            if fn(cv, _e4m3_exact(int(sb, 16)), float(gd)) != np.float32(expect):
+                fails[name] += 1
+    assert fails["divide_first"] == 0
+    assert fails["multiply_first"] >= 1 and fails["reciprocal"] >= 1, fails
+
+
 def test_dequant_nvfp4_nibble_order_and_scale_index(orc):
     packed = np.zeros((1, 16), np.uint8)
     packed[0, 0] = 0x07 | (0x02 << 4)          # k=0: code 7 (6.0), k=1: code 2 (1.0)
