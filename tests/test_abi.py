@@ -284,3 +284,22 @@ def test_int5_validation(L):
     assert L.w4a8_gemm_workspace_bytes(300, 520, 1152, 6) == (3 * 300 * 16 + 4096 + 255) // 256 * 256
     assert L.w4a8_gemm_workspace_bytes(32, 5120, 17408, 6) > 0
     assert L.w4a8_gemm_workspace_bytes(64, 5120, 17408, 6) >= 34 * 64 * 16 + 4096 + 2 * 64 * 5120 * 4
+
+
+def test_workspace_bytes_cover_every_smaller_call(L):
+    """The size for M_max covers every call of m <= M_max rows: the function is
+    non-decreasing in M_max for every prepared kind, also where the tile
+    kernels split K beyond 32768 rows (int4 and int4 with zero points at 128-255
+    tiles on a 256-wide layer, int5 at any M on a narrow one)."""
+    wb = L.w4a8_gemm_workspace_bytes
+    for kind in (2, 3, 4, 5, 6):
+        for N, K in ((256, 8192), (5120, 17408), (34816, 5120)):
+            prev = 0
+            for m in sorted(set(range(1, 200)) | set(range(200, 70000, 977)) | {65536, 131072, 300000}):
+                cur = wb(m, N, K, kind)
+                assert cur >= prev, (kind, N, K, m, cur, prev)
+                prev = cur
+    # the cases a 32768-row cap missed: the need at M = 49138 (int4, N = 256)
+    # and M = 40903 (int5) is inside the size for 65536 rows
+    assert wb(65536, 256, 8192, 3) >= wb(49138, 256, 8192, 3) > 0
+    assert wb(65536, 256, 8192, 6) >= wb(40903, 256, 8192, 6) > 0

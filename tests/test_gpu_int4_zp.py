@@ -60,7 +60,7 @@ def test_int4_zp_ragged(M, N, K):
 
 @pytest.mark.parametrize("M", [1, 16, 64, 2048])
 def test_int4_zp_full_size(M):
-    _case(f"zp M={M}", synth.int4_zp(), M, (42, M), sample=4096)
+    _case(f"zp M={M}", synth.int4_zp(), M, (42, M), sample=4096 if M > 64 else None)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 136, 1152), (16, 1000, 4096), (64, 5120, 2048), (300, 600, 768)])

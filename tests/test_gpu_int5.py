@@ -60,7 +60,7 @@ def test_int5_ragged(M, N, K):
 
 @pytest.mark.parametrize("M", [1, 16, 64, 2048])
 def test_int5_full_size(M):
-    _case(f"int5 M={M}", synth.int5(), M, (62, M), sample=4096)
+    _case(f"int5 M={M}", synth.int5(), M, (62, M), sample=4096 if M > 64 else None)
 
 
 @pytest.mark.parametrize("M", [8, 200])

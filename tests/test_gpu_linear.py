@@ -36,7 +36,6 @@ def _run(name, bits, pw, unfused, x_view=None, sample=None, ref_fn=None):
     r8, rs = oracle.quant_act_fp8(bits)
     assert np.array_equal(host(x8), r8), name
     assert np.array_equal(host(xs), rs), name
-    # the unfused GPU path on the same codes and scales
     # the unfused GPU path on the same codes and scales: the same kernel plan,
     # so the same bits
     ref_gpu = host_bf16_as_f64(unfused["gemm"](dev_u8(r8), torch.from_numpy(rs).cuda(), pw))
@@ -106,22 +105,28 @@ def test_mxfp4_linear_strided_and_unaligned_rows():
     _run("unaligned", bits, pw, MX, x_view=xo, ref_fn=ref)
 
 
-@pytest.mark.parametrize("M", [1, 2, 8, 16])
-def test_mxfp4_linear_gate_up(gate_up_mx, M):
+@pytest.fixture(scope="module")
+def gate_up_pw(gate_up_mx):
+    return w4.mxfp4_prepare(dev_u8(gate_up_mx[0]), dev_u8(gate_up_mx[1]))
+
+
+# the headline decode step's four calls (M = 1, 8, 16, 64) and M = 2: every
+# output against the oracle
+@pytest.mark.parametrize("M", [1, 2, 8, 16, 64])
+def test_mxfp4_linear_gate_up(gate_up_mx, gate_up_pw, M):
     wp, we = gate_up_mx[:2]
-    pw = w4.mxfp4_prepare(dev_u8(wp), dev_u8(we))
     bits = synth.acts(M, synth.HIDDEN, seed=(25, M), spread=10.0)
-    _run(f"gate_up M={M}", bits, pw, MX, sample=4096,
-         ref_fn=lambda b, mi, ni: oracle.linear_bf16(b, wp, we, mi=mi, ni=ni))
+    _run(f"gate_up M={M}", bits, gate_up_pw, MX,
+         ref_fn=lambda b, mi=None, ni=None: oracle.linear_bf16(b, wp, we, mi=mi, ni=ni))
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 64])
 def test_mxfp4_linear_down_proj(M):
     d = synth.down_proj()
     pw = w4.mxfp4_prepare(dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"]))
     bits = synth.acts(M, synth.INTERMEDIATE, seed=(26, M), spread=10.0)
-    _run(f"down_proj M={M}", bits, pw, MX, sample=4096,
-         ref_fn=lambda b, mi, ni: oracle.linear_bf16(b, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni))
+    _run(f"down_proj M={M}", bits, pw, MX,
+         ref_fn=lambda b, mi=None, ni=None: oracle.linear_bf16(b, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (4, 136, 1152), (9, 520, 2048), (24, 200, 640)])

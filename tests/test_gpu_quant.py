@@ -161,13 +161,9 @@ def test_requant_gate_up_full_mse(gate_up_mx):
 
 @pytest.mark.parametrize("mode", ["ocp", "noclip"])
 def test_requant_gate_up_other_modes(mode):
-    g = synth.gate_up()
-    # both partitions, 2048 rows each (one from each divisor)
-    rows = 2048
-    sel = np.r_[0:rows, 17408:17408 + rows]
-    d = dict(nv_packed=g["nv_packed"][sel], nv_scale=g["nv_scale"][sel],
-             part_rows=np.array([rows, rows], np.int64), part_divisor=g["part_divisor"])
-    _requant_case(d, mode, name="gate_up subset")
+    # the whole merged layer (both partitions, each with its divisor) in passes
+    # of 4096 rows, as the full-layer requant config runs it
+    _requant_case(synth.gate_up(), mode, row_chunk=4096, name="gate_up ROW_CHUNK=4096")
 
 
 def test_requant_rejects_bad_arguments():
@@ -223,6 +219,38 @@ def test_quant_fp8ch_random_codes(mode):
         c[(c & 0x7F) == 0x7F] = 0x7E                              # no NaN codes
         s = np.exp2(g.uniform(-30, 20, rows)).astype(np.float32) * g.uniform(1, 2, rows).astype(np.float32)
         _load_case("fp8", c, mode, f"random {rows}x{K}", s)
+
+
+def _decision_point_sweep():
+    """fp8 per-channel rows built so that the encoder's fp32 -> e2m1 step sees
+    every fp32 mantissa near each of its decision points.  Row r has scale
+    s_r in [1, 2); block j (j = 0..4) holds e4m3 2^j at element 0, which fixes
+    the ocp exponent at j - 2, and +-2^-i (i = k mod 5) at element k, so
+    w = +-2^-i s_r exactly and the scaled magnitude is 4 s_r / 2^(i + j): s_r's
+    mantissa lands on [4, 8), [2, 4), [1, 2), [0.5, 1) and [0.25, 0.5), where the
+    nearest-even decisions sit at 5 (and the clip at 6), 2.5 and 3.5, 1.25 and
+    1.75, 0.75, and 0.25.  The scales sweep 4096 fp32 steps on each side of
+    mantissa 1, 1.25, 1.5, 1.75 and 2, plus random mantissas."""
+    one = int(np.float32(1.0).view(np.uint32))
+    centres = [one + (c << 21) for c in (0, 2, 4, 6, 8)]        # mantissas 1, 1.25, 1.5, 1.75, 2
+    bits = np.concatenate([np.arange(c - 4096, c + 4097) for c in centres]
+                          + [one + np.random.default_rng(31).integers(0, 1 << 23, 16384)])
+    bits = bits[(bits >= one) & (bits < one + (1 << 23))]
+    scale = bits.astype(np.uint32).view(np.float32)
+    K = 160
+    k = np.arange(K) % 32
+    j = np.arange(K) // 32
+    i = k % 5
+    code = ((7 - i) << 3).astype(np.uint8)                     # e4m3 2^-i
+    code[k % 2 == 1] |= 0x80                                  # every other element negative
+    code[k == 0] = ((7 + j[k == 0]) << 3).astype(np.uint8)    # e4m3 2^j: the block's amax
+    return np.tile(code, (scale.size, 1)), np.ascontiguousarray(scale)
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_quant_fp8ch_e2m1_decision_points(mode):
+    codes, scale = _decision_point_sweep()
+    _load_case("fp8", codes, mode, f"decision points {codes.shape}", scale)
 
 
 def test_quant_bf16_gate_up_shape():

@@ -70,13 +70,13 @@ def test_w4a4_decode(M, N, K):
 
 @pytest.mark.parametrize("M", [1, 8, 12, 13, 64, 4096])
 def test_w4a4_gate_up(gate_up_mx, M):
-    _case(f"gate_up M={M}", gate_up_mx[0], gate_up_mx[1], M, (8, M), sample=4096)
+    _case(f"gate_up M={M}", gate_up_mx[0], gate_up_mx[1], M, (8, M), sample=4096 if M > 64 else None)
 
 
 @pytest.mark.parametrize("M", [1, 16, 32, 4096])
 def test_w4a4_down_proj(M):
     d = synth.down_proj()
-    _case(f"down_proj M={M}", d["w_packed"], d["w_e8m0"], M, (9, M), sample=4096)
+    _case(f"down_proj M={M}", d["w_packed"], d["w_e8m0"], M, (9, M), sample=4096 if M > 64 else None)
 
 
 def test_w4a4_rejects_bad_shapes():

@@ -138,58 +138,36 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         kind != W4A8_WEIGHT_INT4G128_ZP_PREPARED && kind != W4A8_WEIGHT_INT5G128_PREPARED)
         return 0;
     size_t need = 0;
-    if (kind == W4A8_WEIGHT_INT5G128_PREPARED) {
-        // the decode kernel up to 32 rows; above, the tile kernel, whose shape
-        // is constant on (32, 64], (64, 128] and each (256 j - 256, 256 j], its
-        // workspace growing with M there: the interval ends and M_max cover it
-        for (int64_t m = 1; m <= M_max && m <= kPreparedDecodeMaxM; ++m) {
-            const size_t b = plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
-            if (b > need) need = b;
-        }
-        auto keep = [&](int64_t m) {
-            if (m <= kPreparedDecodeMaxM || m > M_max || !i5_tiled_fits(m, K)) return;
-            const size_t b = i5_tiled_workspace_bytes(m, N, K);
-            if (b > need) need = b;
-        };
-        keep(64);
-        keep(128);
-        for (int64_t m = 256; m < M_max && m <= 32768; m += 256) keep(m);
-        keep(M_max);
-        return need;
-    }
-    if (kind == W4A8_W4A4_PREPARED) {
-        // the decode kernel's split for every M it serves; above, one tile
-        // kernel, its shape constant on each interval (128j, 128j + 128] and
-        // its split workspace growing with M there
-        if (K > kPreparedTiledMaxK) return 0;
-        for (int64_t m = 1; m <= M_max && m <= kPreparedDecodeMaxM; ++m) {
-            const size_t b = w4a4_workspace_bytes(m, N, K);
-            if (b > need) need = b;
-        }
-        for (int64_t m = 128; m < M_max && m <= 32768; m += 128) {
-            const size_t b = w4a4_workspace_bytes(m, N, K);
-            if (b > need) need = b;
-        }
-        const size_t b = w4a4_workspace_bytes(M_max, N, K);
-        return b > need ? b : need;
-    }
-    if (kind == W4A8_WEIGHT_MXFP4_PREPARED || kind == W4A8_WEIGHT_INT4G128_PREPARED ||
-        kind == W4A8_WEIGHT_INT4G128_ZP_PREPARED) {
-        // the zero-point form takes the int4 kernels' routes and shapes
-        const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
+    auto keep = [&](size_t b) { if (b > need) need = b; };
+    if (kind != W4A8_WEIGHT_MXFP4 && kind != W4A8_WEIGHT_INT4G128) {
+        // fragment-order weights: the workspace a call of m rows takes, by the
+        // route and shape that call gets
         auto at = [&](int64_t m) -> size_t {
-            const PreparedRoute r = prepared_route(m, N, K, int4);
-            if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
+            if (kind == W4A8_WEIGHT_INT5G128_PREPARED) {
+                if (m <= kPreparedDecodeMaxM) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
+                return i5_tiled_fits(m, K) ? i5_tiled_workspace_bytes(m, N, K) : 0;
+            }
+            if (kind == W4A8_W4A4_PREPARED) return K <= kPreparedTiledMaxK ? w4a4_workspace_bytes(m, N, K) : 0;
+            // the zero-point form takes the int4 kernels' routes and shapes
+            const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
+            if (prepared_route(m, N, K, int4) == PreparedRoute::Decode)
+                return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
             return K <= kPreparedTiledMaxK ? tiled_workspace_bytes(m, N, K, int4) : 0;
         };
-        auto keep = [&](size_t b) { if (b > need) need = b; };
-        // every M up to 64; above, the tiled kernel's shape is constant on each
-        // interval (64j, 64j + 64] and its split workspace grows with M there,
-        // so the interval ends and M_max cover it; from 32768 rows on there
-        // are at least 128 tiles and K is not split
+        // Every M up to 64 (the decode band, whose plans change at any M).
+        // Above, every tile kernel's shape (64-, 128- or 256-row tiles, the K
+        // split) is constant between consecutive multiples of 64 and its split
+        // workspace grows with M there, so the multiples of 64 and M_max itself
+        // cover every call.  No rule splits K once even 256 x 256 tiles number
+        // 1024 or more (the fewest a call of m rows can have), so the scan stops
+        // there.
         for (int64_t m = 1; m <= M_max && m <= kDecodeMaxM; ++m) keep(at(m));
-        for (int64_t m = 2 * kDecodeMaxM; m < M_max && m <= 32768; m += kDecodeMaxM) keep(at(m));
-        if (M_max > kDecodeMaxM) keep(at(M_max));
+        const int64_t tiles_n = (N + 255) / 256;
+        for (int64_t m = 2 * kDecodeMaxM; m < M_max; m += kDecodeMaxM) {
+            keep(at(m));
+            if ((m / 256) * tiles_n >= 1024) break;
+        }
+        keep(at(M_max));
         return need;
     }
     const int64_t top = M_max < kDecodeMaxM ? M_max : kDecodeMaxM;
