@@ -102,9 +102,11 @@ typedef enum {
  *   n_parts       >= 1
  *   K             elements per row, K % 32 == 0, K >= 32
  *   mode          w4a8_exp_mode
- *   row_chunk     rows per pass (one kernel launch per pass and partition);
- *                 0 = one pass per partition.  4096 reproduces the page's
- *                 ROW_CHUNK.  Results do not depend on it.
+ *   row_chunk     rows per pass of the page's requant_rows (its ROW_CHUNK is
+ *                 4096; 0 = one pass per partition).  Each block is encoded on
+ *                 its own, so results do not depend on it, and every pass of
+ *                 every partition runs in one kernel launch (one per group of
+ *                 16 partitions).
  *   d_mx_packed   device uint8 [rows, K/2]   out: e2m1 codes, even k low nibble
  *   d_mx_e8m0     device uint8 [rows, K/32]  out: block exponents + 127
  *   d_err_stats   device double [2*n_parts] or NULL: out, per partition

@@ -62,20 +62,26 @@ w4a8_status w4a8_requant_nvfp4_to_mxfp4(const uint8_t* d_nv_packed, const uint8_
         const hipError_t e = launch_fill_zero_f64(d_err_stats, 2 * (int64_t)n_parts, s);
         if (e != hipSuccess) return W4A8_ERR_HIP;
     }
+    // Every partition and every row chunk in one launch (groups of up to
+    // requant_max_parts() partitions): the passes of row_chunk rows change no
+    // output, each block being encoded on its own, so they are not separate
+    // launches.
+    const int group = requant_max_parts();
     int64_t r0 = 0;
-    for (int p = 0; p < n_parts; ++p) {
-        const int64_t width = h_part_rows[p];
-        const int64_t chunk = row_chunk > 0 ? row_chunk : (width > 0 ? width : 1);
-        for (int64_t a = 0; a < width; a += chunk) {
-            const int64_t n = (width - a) < chunk ? (width - a) : chunk;
-            const int64_t r = r0 + a;
-            const hipError_t e = launch_requant(
-                d_nv_packed + r * (K / 2), d_nv_scale + r * (K / 16), h_part_divisor[p],
-                n * (K / 32), (int)mode, d_mx_packed + r * (K / 2), d_mx_e8m0 + r * (K / 32),
-                d_err_stats ? d_err_stats + 2 * p : nullptr, s);
-            if (e != hipSuccess) return W4A8_ERR_HIP;
+    for (int p0 = 0; p0 < n_parts; p0 += group) {
+        const int n = n_parts - p0 < group ? n_parts - p0 : group;
+        int64_t blocks[64];
+        int64_t rows = 0;
+        for (int i = 0; i < n; ++i) {
+            blocks[i] = h_part_rows[p0 + i] * (K / 32);
+            rows += h_part_rows[p0 + i];
         }
-        r0 += width;
+        const hipError_t e = launch_requant(d_nv_packed + r0 * (K / 2), d_nv_scale + r0 * (K / 16), blocks,
+                                            h_part_divisor + p0, n, (int)mode, d_mx_packed + r0 * (K / 2),
+                                            d_mx_e8m0 + r0 * (K / 32), d_err_stats ? d_err_stats + 2 * p0 : nullptr,
+                                            s);
+        if (e != hipSuccess) return W4A8_ERR_HIP;
+        r0 += rows;
     }
     return W4A8_OK;
 }

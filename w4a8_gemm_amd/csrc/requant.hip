@@ -14,11 +14,15 @@
 // Mapping: one lane per 32-element block.  A block is 16 bytes of NVFP4 codes and
 // 2 e4m3 scale bytes in, 16 bytes of MXFP4 codes and 1 e8m0 byte out, and the
 // blocks of a row-major [rows, K] weight are consecutive in all four arrays, so a
-// wavefront reads and writes contiguous 1 KiB / 128 B / 1 KiB / 64 B runs.  The
-// pass is bandwidth/ALU bound; no LDS is needed.  Squared errors are summed in
-// fp32 in element order 0..31, each square rounded first, with no fused
-// multiply-add (the file is compiled with -ffp-contract=off), so the mse
-// decision is a fixed function of the inputs.
+// wavefront reads and writes contiguous 1 KiB / 128 B / 1 KiB / 64 B runs.  Each
+// workgroup takes a contiguous range of blocks inside one partition (so its
+// divisor is uniform) in iterations of one block per lane, the next
+// iteration's input loaded before the current one is encoded, so that loads
+// stay in flight while the vector ALU works.  One launch covers every
+// partition and row chunk of a call.  Squared errors are summed in fp32 in
+// element order 0..31, each square rounded first, with no fused multiply-add
+// (the file is compiled with -ffp-contract=off), so the mse decision is a fixed
+// function of the inputs.
 #include "w4a8_internal.h"
 
 #pragma clang fp contract(off)
@@ -46,49 +50,62 @@ __device__ __forceinline__ int block_exponent(float amax, int mode) {
     return max(-127, min(127, e));
 }
 
-// Encode one block at exponent e.  Returns the fp32 squared error summed in
-// element order; writes 4-bit magnitude indices (no sign) into idx.  The index
-// of |w| / 2^e comes from the matrix-format conversion instructions, whose
-// rounding is the page's e2m1_index on magnitudes (nearest grid point, ties
-// to the even index -- the index's low bit is the mantissa bit -- and values
-// above 6 saturating at 6; checked against the rule for every magnitude class
-// on gfx950); the grid value comes back through the reverse conversion.
+// Encode one block at exponent e: the e2m1 codes of w / 2^e and, if ERR, the
+// fp32 squared error of the block summed in element order.  The codes come
+// from the matrix-format conversion instruction, whose rounding is the page's
+// e2m1_index on magnitudes (nearest grid point, ties to the even index -- the
+// index's low bit is the mantissa bit -- and values above 6 saturating at 6;
+// checked against the rule for every magnitude class on gfx950), with the
+// input's sign in bit 3.  A negative value that rounds to zero therefore comes
+// out as code 8 (-0), which is folded to code 0: the page sets the sign only on
+// nonzero codes.
 template <int T>
 __device__ __forceinline__ uint32_t to_e2m1(uint32_t old, float a0, float a1) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a0, a1, 1.0f, T);   // byte T <- indices of a0, a1
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a0, a1, 1.0f, T);   // byte T <- codes of a0, a1
 }
-// squared errors of the two elements of byte T (grid values scaled by 2^e,
-// signed like w), added to err in element order
+// the sign bit of every nibble whose magnitude bits are zero cleared (8 -> 0)
+__device__ __forceinline__ uint32_t fold_neg_zero(uint32_t x) {
+    const uint32_t m = x & 0x77777777u;
+    const uint32_t nz = (m | (m >> 1) | (m >> 2)) & 0x11111111u;   // nibble bit 0: magnitude != 0
+    return m | (x & (nz << 3));
+}
+// squared errors of the two elements of byte T, added to err in element order.
+// The grid value q has the sign of w (or is zero), so q - w = +-(|q| - |w|) and
+// its square is that of |q| - |w|: the difference is exact (the magnitudes are
+// within a factor of two of each other unless q is 0) and the square rounded
+// once, as for q - w.
 template <int T>
-__device__ __forceinline__ float byte_err(uint32_t packed, const float* w2, float scale, float err) {
-    const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, T);
+__device__ __forceinline__ float byte_err(uint32_t codes, const float* w2, float scale, float err) {
+    const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, T);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const float qv = copysignf(g[u] * scale, w2[u]);   // exact
-        const float d = qv - w2[u];
+        const float d = fabsf(g[u]) * scale - fabsf(w2[u]);
         const float sq = d * d;
         err = err + sq;
     }
     return err;
 }
 
-__device__ __forceinline__ float encode_block(const float* w, int e, uint32_t* idx) {
+template <bool ERR>
+__device__ __forceinline__ float encode_block(const float* w, int e, uint32_t* code) {
     const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, normal for e in [-127, 126]
     const float scale = ldexpf(1.0f, e);                            // 2^e, exact (subnormal at -127)
     float err = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float* b = w + 8 * q;
-        // |w / 2^e|, each product correctly rounded
-        uint32_t packed = to_e2m1<0>(0u, fabsf(b[0] * inv), fabsf(b[1] * inv));
-        packed = to_e2m1<1>(packed, fabsf(b[2] * inv), fabsf(b[3] * inv));
-        packed = to_e2m1<2>(packed, fabsf(b[4] * inv), fabsf(b[5] * inv));
-        packed = to_e2m1<3>(packed, fabsf(b[6] * inv), fabsf(b[7] * inv));
-        idx[q] = packed;
-        err = byte_err<0>(packed, b, scale, err);
-        err = byte_err<1>(packed, b + 2, scale, err);
-        err = byte_err<2>(packed, b + 4, scale, err);
-        err = byte_err<3>(packed, b + 6, scale, err);
+        // w / 2^e, each product correctly rounded
+        uint32_t packed = to_e2m1<0>(0u, b[0] * inv, b[1] * inv);
+        packed = to_e2m1<1>(packed, b[2] * inv, b[3] * inv);
+        packed = to_e2m1<2>(packed, b[4] * inv, b[5] * inv);
+        packed = to_e2m1<3>(packed, b[6] * inv, b[7] * inv);
+        code[q] = fold_neg_zero(packed);
+        if (ERR) {
+            err = byte_err<0>(code[q], b, scale, err);
+            err = byte_err<1>(code[q], b + 2, scale, err);
+            err = byte_err<2>(code[q], b + 4, scale, err);
+            err = byte_err<3>(code[q], b + 6, scale, err);
+        }
     }
     return err;
 }
@@ -101,11 +118,19 @@ __device__ __forceinline__ float encode_block(const float* w, int e, uint32_t* i
 //   kInFp8Ch  32 bytes of e4m3 and the row's fp32 scale: w = e4m3 * scale
 constexpr int kInNvfp4 = 0, kInBf16 = 1, kInFp8Ch = 2;
 
+// Partitions of one launch: consecutive block ranges, each with its divisor
+// (NVFP4) and its first workgroup; the other inputs take one partition.
+constexpr int kMaxParts = 16;
+constexpr int kIters = 8;                                  // blocks per lane and workgroup
+constexpr int64_t kWgBlocks = (int64_t)kThreads * kIters;
 struct QuantIn {
     const uint8_t* data;        // codes or values of the rows
     const void* aux;            // nvfp4: e4m3 scale pairs; fp8: fp32 row scales
-    float divisor;              // nvfp4 global divisor
     int64_t blocks_per_row;     // fp8: the row of a block
+    int n_parts;
+    int64_t part_begin[kMaxParts + 1];   // first block of each partition; [n_parts] = the end
+    int64_t wg_begin[kMaxParts + 1];     // first workgroup of each partition; [n_parts] = the grid
+    float divisor[kMaxParts];            // nvfp4 global divisor
 };
 
 // Exact decodes through the matrix-format conversion instructions (unit
@@ -132,100 +157,139 @@ __device__ __forceinline__ void e4m3_x4(uint32_t dw, float* out) {
     out[3] = hi[1];
 }
 
+// Raw input of one block, loaded an iteration ahead of its encode
+template <int IN> struct Raw;
+template <> struct Raw<kInNvfp4> { uint4 c; uint32_t s; };
+template <> struct Raw<kInBf16> { uint4 v[4]; };
+template <> struct Raw<kInFp8Ch> { uint4 v[2]; float s; };
+
 template <int IN>
-__device__ __forceinline__ void load_block(const QuantIn& in, int64_t b, float (&w)[32]) {
+__device__ __forceinline__ void load_raw(const QuantIn& in, int64_t b, Raw<IN>& r) {
     if constexpr (IN == kInNvfp4) {
-        const uint4 p = reinterpret_cast<const uint4*>(in.data)[b];
-        const uint32_t sc = reinterpret_cast<const uint16_t*>(in.aux)[b];
+        r.c = reinterpret_cast<const uint4*>(in.data)[b];
+        r.s = reinterpret_cast<const uint16_t*>(in.aux)[b];
+    } else if constexpr (IN == kInBf16) {
+        const uint4* p = reinterpret_cast<const uint4*>(in.data) + 4 * b;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.v[q] = p[q];
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(in.data) + 2 * b;
+        r.v[0] = p[0];
+        r.v[1] = p[1];
+        // the row of block b (32-bit division: the entry point keeps the block
+        // count below 2^32)
+        r.s = reinterpret_cast<const float*>(in.aux)[(uint32_t)b / (uint32_t)in.blocks_per_row];
+    }
+}
+
+template <int IN>
+__device__ __forceinline__ void decode_block(const Raw<IN>& r, float divisor, float (&w)[32]) {
+    if constexpr (IN == kInNvfp4) {
         float sv[4];
-        e4m3_x4(sc, sv);
-        const float s0 = sv[0] / in.divisor;  // IEEE division
-        const float s1 = sv[1] / in.divisor;
-        const uint32_t dw[4] = {p.x, p.y, p.z, p.w};
+        e4m3_x4(r.s, sv);
+        const float s0 = sv[0] / divisor;  // IEEE division
+        const float s1 = sv[1] / divisor;
+        const uint32_t dw[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) e2m1_x8(dw[q], w + 8 * q);
 #pragma unroll
         for (int j = 0; j < 32; ++j) w[j] = w[j] * (j < 16 ? s0 : s1);
     } else if constexpr (IN == kInBf16) {
-        const uint4* p = reinterpret_cast<const uint4*>(in.data) + 4 * b;
         uint32_t dw[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint4 v = p[q];
-            dw[4 * q] = v.x; dw[4 * q + 1] = v.y; dw[4 * q + 2] = v.z; dw[4 * q + 3] = v.w;
+            dw[4 * q] = r.v[q].x; dw[4 * q + 1] = r.v[q].y; dw[4 * q + 2] = r.v[q].z; dw[4 * q + 3] = r.v[q].w;
         }
 #pragma unroll
         for (int j = 0; j < 32; ++j) w[j] = bf16_to_f32((dw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
     } else {
-        const uint4* p = reinterpret_cast<const uint4*>(in.data) + 2 * b;
-        // the row of block b (32-bit division: the entry point keeps the block
-        // count below 2^32)
-        const float s = reinterpret_cast<const float*>(in.aux)[(uint32_t)b / (uint32_t)in.blocks_per_row];
-        const uint4 v0 = p[0], v1 = p[1];
-        const uint32_t dw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const uint32_t dw[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
 #pragma unroll
         for (int q = 0; q < 8; ++q) e4m3_x4(dw[q], w + 4 * q);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) w[j] = w[j] * s;
+        for (int j = 0; j < 32; ++j) w[j] = w[j] * r.s;
+    }
+}
+
+// One block: the exponent by the rule, the codes, the e8m0 byte; the chosen
+// error and the sum of squares go into the lane's statistics.
+template <int IN, int MODE, bool STATS>
+__device__ __forceinline__ void requant_block(const Raw<IN>& r, float divisor, int64_t b,
+                                              uint4* __restrict__ out_packed, uint8_t* __restrict__ out_e8m0,
+                                              double& err_sum, double& ssq_sum) {
+    float w[32];
+    decode_block<IN>(r, divisor, w);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    uint32_t code[4];
+    int e;
+    float err;
+    if (MODE == W4A8_EXP_MSE) {
+        const int e0 = block_exponent(amax, W4A8_EXP_NOCLIP);
+        err = encode_block<true>(w, e0, code);
+        e = e0;
+        if (e0 - 1 >= -127) {
+            uint32_t code1[4];
+            const float r1 = encode_block<true>(w, e0 - 1, code1);
+            if (r1 < err) {
+                err = r1;
+                e = e0 - 1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) code[q] = code1[q];
+            }
+        }
+    } else {
+        e = block_exponent(amax, MODE);
+        err = encode_block<STATS>(w, e, code);
+    }
+    out_packed[b] = make_uint4(code[0], code[1], code[2], code[3]);
+    out_e8m0[b] = (uint8_t)(e + 127);
+    if (STATS) {
+        err_sum += (double)err;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) ssq_sum += (double)w[j] * (double)w[j];
     }
 }
 
 template <int IN, int MODE, bool STATS>
-__global__ __launch_bounds__(kThreads) void requant_kernel(
-    QuantIn in, int64_t nblocks, uint4* __restrict__ out_packed, uint8_t* __restrict__ out_e8m0,
-    double* __restrict__ stats) {
+__global__ __launch_bounds__(kThreads) void requant_kernel(QuantIn in, uint4* __restrict__ out_packed,
+                                                           uint8_t* __restrict__ out_e8m0,
+                                                           double* __restrict__ stats) {
+    // this workgroup's partition and block range (uniform: a scan over the
+    // launch's table with constant indices)
+    const int64_t wg = blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxParts; ++i)
+        if (i < in.n_parts && wg >= in.wg_begin[i]) p = i;
+    int64_t lo = 0, hi = 0;
+    float divisor = 1.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i)
+        if (i == p) {
+            lo = in.part_begin[i] + (wg - in.wg_begin[i]) * kWgBlocks;
+            hi = min(lo + kWgBlocks, in.part_begin[i + 1]);
+            divisor = in.divisor[i];
+        }
     double err_sum = 0.0, ssq_sum = 0.0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-        float w[32];
-        load_block<IN>(in, b, w);
-        float amax = 0.0f;
+    // iteration it encodes block lo + it * kThreads + tid; a lane past the
+    // range's end loads its last block and stores nothing
+    auto blk = [&](int it) { return lo + (int64_t)it * kThreads + threadIdx.x; };
+    Raw<IN> r0, r1;
+    load_raw<IN>(in, min(blk(0), hi - 1), r0);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(w[j]));
-        uint32_t idx[4];
-        int e;
-        float err;
-        if (MODE == W4A8_EXP_MSE) {
-            const int e0 = block_exponent(amax, W4A8_EXP_NOCLIP);
-            err = encode_block(w, e0, idx);
-            e = e0;
-            if (e0 - 1 >= -127) {
-                uint32_t idx1[4];
-                const float r1 = encode_block(w, e0 - 1, idx1);
-                if (r1 < err) {
-                    err = r1;
-                    e = e0 - 1;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) idx[q] = idx1[q];
-                }
-            }
-        } else {
-            e = block_exponent(amax, MODE);
-            err = encode_block(w, e, idx);
-        }
-        // sign bit only where the index is nonzero (a negative zero keeps code 0)
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t sgn = 0u;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int j = 8 * q + t;
-                const uint32_t nz = (idx[q] >> (4 * t)) & 7u;
-                if (nz && (__float_as_uint(w[j]) >> 31)) sgn |= 8u << (4 * t);
-            }
-            o[q] = idx[q] | sgn;
-        }
-        out_packed[b] = make_uint4(o[0], o[1], o[2], o[3]);
-        out_e8m0[b] = (uint8_t)(e + 127);
-        if (STATS) {
-            err_sum += (double)err;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) ssq_sum += (double)w[j] * (double)w[j];
-        }
+    for (int it = 0; it < kIters; it += 2) {
+        load_raw<IN>(in, min(blk(it + 1), hi - 1), r1);
+        if (blk(it) < hi)
+            requant_block<IN, MODE, STATS>(r0, divisor, blk(it), out_packed, out_e8m0, err_sum, ssq_sum);
+        if (it + 2 < kIters) load_raw<IN>(in, min(blk(it + 2), hi - 1), r0);
+        if (blk(it + 1) < hi)
+            requant_block<IN, MODE, STATS>(r1, divisor, blk(it + 1), out_packed, out_e8m0, err_sum, ssq_sum);
     }
     if (STATS) {
         // wavefront then workgroup reduction, one pair of atomics per workgroup
+        // into its partition's slots
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             err_sum += __shfl_xor(err_sum, off);
@@ -244,11 +308,12 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(
                 a += red[0][i];
                 s += red[1][i];
             }
-            atomicAdd(&stats[0], a);
-            atomicAdd(&stats[1], s);
+            atomicAdd(&stats[2 * p], a);
+            atomicAdd(&stats[2 * p + 1], s);
         }
     }
 }
+static_assert(kIters % 2 == 0, "the loop above takes iterations in pairs");
 
 __global__ void fill_zero_f64(double* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -260,53 +325,80 @@ __global__ void fill_zero_u32(uint32_t* p, int64_t n) {
 }
 
 template <int IN, int MODE>
-hipError_t launch_mode(const QuantIn& in, int64_t nblocks, uint8_t* mx_packed, uint8_t* mx_e8m0,
-                       double* stats, hipStream_t stream) {
-    // enough workgroups to fill 256 CUs several times over; lanes loop beyond that
-    const int64_t want = (nblocks + kThreads - 1) / kThreads;
-    const int grid = (int)(want < 4096 ? want : 4096);
+hipError_t launch_mode(const QuantIn& in, uint8_t* mx_packed, uint8_t* mx_e8m0, double* stats,
+                       hipStream_t stream) {
+    const int64_t grid = in.wg_begin[in.n_parts];
+    if (grid <= 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
     if (stats)
-        hipLaunchKernelGGL((requant_kernel<IN, MODE, true>), dim3(grid), dim3(kThreads), 0, stream, in, nblocks,
+        hipLaunchKernelGGL((requant_kernel<IN, MODE, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, in,
                            (uint4*)mx_packed, mx_e8m0, stats);
     else
-        hipLaunchKernelGGL((requant_kernel<IN, MODE, false>), dim3(grid), dim3(kThreads), 0, stream, in,
-                           nblocks, (uint4*)mx_packed, mx_e8m0, stats);
+        hipLaunchKernelGGL((requant_kernel<IN, MODE, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           in, (uint4*)mx_packed, mx_e8m0, stats);
     return hipGetLastError();
 }
 
 template <int IN>
-hipError_t launch_in(const QuantIn& in, int64_t nblocks, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0,
-                     double* stats, hipStream_t stream) {
-    if (nblocks <= 0) return hipSuccess;
+hipError_t launch_in(const QuantIn& in, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0, double* stats,
+                     hipStream_t stream) {
     switch (mode) {
         case W4A8_EXP_OCP:
-            return launch_mode<IN, W4A8_EXP_OCP>(in, nblocks, mx_packed, mx_e8m0, stats, stream);
+            return launch_mode<IN, W4A8_EXP_OCP>(in, mx_packed, mx_e8m0, stats, stream);
         case W4A8_EXP_NOCLIP:
-            return launch_mode<IN, W4A8_EXP_NOCLIP>(in, nblocks, mx_packed, mx_e8m0, stats, stream);
+            return launch_mode<IN, W4A8_EXP_NOCLIP>(in, mx_packed, mx_e8m0, stats, stream);
         default:
-            return launch_mode<IN, W4A8_EXP_MSE>(in, nblocks, mx_packed, mx_e8m0, stats, stream);
+            return launch_mode<IN, W4A8_EXP_MSE>(in, mx_packed, mx_e8m0, stats, stream);
+    }
+}
+
+// the launch table of partitions 0..n-1 with cnt[i] blocks each
+void plan_parts(QuantIn& in, const int64_t* cnt, const float* divisor, int n) {
+    in.n_parts = n;
+    in.part_begin[0] = 0;
+    in.wg_begin[0] = 0;
+    for (int i = 0; i < n; ++i) {
+        in.part_begin[i + 1] = in.part_begin[i] + cnt[i];
+        in.wg_begin[i + 1] = in.wg_begin[i] + (cnt[i] + kWgBlocks - 1) / kWgBlocks;
+        in.divisor[i] = divisor ? divisor[i] : 1.0f;
     }
 }
 
 }  // namespace
 
-hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, float divisor,
-                          int64_t nblocks, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0,
-                          double* stats, hipStream_t stream) {
-    const QuantIn in{nv_packed, nv_scale, divisor, 1};
-    return launch_in<kInNvfp4>(in, nblocks, mode, mx_packed, mx_e8m0, stats, stream);
+int requant_max_parts() { return kMaxParts; }
+
+hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, const int64_t* part_blocks,
+                          const float* part_divisor, int n_parts, int mode, uint8_t* mx_packed,
+                          uint8_t* mx_e8m0, double* stats, hipStream_t stream) {
+    if (n_parts < 1 || n_parts > kMaxParts) return hipErrorInvalidValue;
+    QuantIn in{};
+    in.data = nv_packed;
+    in.aux = nv_scale;
+    in.blocks_per_row = 1;
+    plan_parts(in, part_blocks, part_divisor, n_parts);
+    return launch_in<kInNvfp4>(in, mode, mx_packed, mx_e8m0, stats, stream);
 }
 
 hipError_t launch_quant_bf16(const uint16_t* w, int64_t rows, int64_t K, int mode, uint8_t* mx_packed,
                              uint8_t* mx_e8m0, double* stats, hipStream_t stream) {
-    const QuantIn in{reinterpret_cast<const uint8_t*>(w), nullptr, 1.0f, K / 32};
-    return launch_in<kInBf16>(in, rows * (K / 32), mode, mx_packed, mx_e8m0, stats, stream);
+    QuantIn in{};
+    in.data = reinterpret_cast<const uint8_t*>(w);
+    in.blocks_per_row = K / 32;
+    const int64_t n = rows * (K / 32);
+    plan_parts(in, &n, nullptr, 1);
+    return launch_in<kInBf16>(in, mode, mx_packed, mx_e8m0, stats, stream);
 }
 
 hipError_t launch_quant_fp8ch(const uint8_t* w, const float* row_scale, int64_t rows, int64_t K, int mode,
                               uint8_t* mx_packed, uint8_t* mx_e8m0, double* stats, hipStream_t stream) {
-    const QuantIn in{w, row_scale, 1.0f, K / 32};
-    return launch_in<kInFp8Ch>(in, rows * (K / 32), mode, mx_packed, mx_e8m0, stats, stream);
+    QuantIn in{};
+    in.data = w;
+    in.aux = row_scale;
+    in.blocks_per_row = K / 32;
+    const int64_t n = rows * (K / 32);
+    plan_parts(in, &n, nullptr, 1);
+    return launch_in<kInFp8Ch>(in, mode, mx_packed, mx_e8m0, stats, stream);
 }
 
 hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream) {

@@ -117,9 +117,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
 // launchers (host side; each returns a hipError_t from the launch)
 // ---------------------------------------------------------------------------
 
-hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, float divisor,
-                          int64_t nblocks, int mode, uint8_t* mx_packed, uint8_t* mx_e8m0,
-                          double* stats, hipStream_t stream);
+// NVFP4 -> MXFP4 over n_parts consecutive partitions (part_blocks[i] 32-element
+// blocks each, divisor part_divisor[i]; host arrays), one launch; stats: per
+// partition {sum err, sum w^2} accumulated into stats[2i], stats[2i + 1]
+hipError_t launch_requant(const uint8_t* nv_packed, const uint8_t* nv_scale, const int64_t* part_blocks,
+                          const float* part_divisor, int n_parts, int mode, uint8_t* mx_packed,
+                          uint8_t* mx_e8m0, double* stats, hipStream_t stream);
+int requant_max_parts();   // partitions one launch_requant call takes
 // bf16 / fp8-per-channel weights -> MXFP4 (the requant encoder, other input stages)
 hipError_t launch_quant_bf16(const uint16_t* w, int64_t rows, int64_t K, int mode, uint8_t* mx_packed,
                              uint8_t* mx_e8m0, double* stats, hipStream_t stream);
