@@ -448,14 +448,22 @@ w4a8_status w4a8_int4g128_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx,
  *   rt  16-row weight tiles per wavefront (1, 2 or 4; 4 waves per workgroup),
  *   u   128-wide K steps per prefetched chunk (1, 2 or 4; 1 if K % 128 != 0),
  *   ks  requested K splits (>= 1; rounded so each split holds whole chunks).
- * Kind MXFP4_PREPARED (prepared weights, M <= 32): rt must be 0, u is the
- * register ring depth in 512-wide chunks (2, 3 or 4), ks the K parts each
- * weight tile is divided into inside a workgroup (clamped to 16 waves per
- * workgroup and to the chunks of a split); the K splits across workgroups and
- * the tiles per workgroup are the entry point's own.
+ * Kind MXFP4_PREPARED (prepared weights) selects one of the kernels that
+ * w4a8_mxfp4_gemm_prepared chooses among, with the plan given here:
+ *   rt = 0        split-K decode kernel (M <= 32), the entry point's tiles per
+ *                 workgroup and K splits; u = register ring depth in 512-wide
+ *                 chunks (2, 3 or 4), ks = K parts per tile inside a workgroup
+ *                 (clamped to 16 waves per workgroup and to the split's chunks);
+ *   rt = 100 + t  the same kernel with t tiles per workgroup (t * ks <= 16), K
+ *                 split across workgroups only as far as the activation slice
+ *                 needs to fit 160 KB of LDS;
+ *   rt = -r       register-streamed tiles (M <= 64): r = 1, 2 or 4 tiles per
+ *                 wave, u = 4, 8 or 16 waves per workgroup, ks = K splits
+ *                 across workgroups;
+ *   rt = -100     the LDS-tiled kernel with K split in ks parts (any M).
  * w4a8_decode_plan_workspace_bytes: workspace for that plan (0 = none needed, or
- * invalid arguments; rt = 0 selects the prepared-weight plan).  Errors as the
- * GEMMs, INVALID_ARG for a bad plan. */
+ * invalid arguments; rt = 0, rt > 100 and rt < 0 select the prepared-weight
+ * plans above).  Errors as the GEMMs, INVALID_ARG for a bad plan. */
 size_t      w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt, int u, int ks);
 w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t *d_x_fp8,
                                   const float *d_x_scale, const void *d_w, const void *d_w_scale,

@@ -357,7 +357,43 @@ def test_mxfp4_prepared_tiled_wide(M, N, K):
     assert_gemm_close(got[mi, ni], ref, (M, N, K))
 
 
-# narrow layers at 33 <= M <= 64: 64-row tiles 128 wide, K split across
+# narrow layers at 9 <= M <= 40: the register-streamed tiles (one to three
+# 16-row activation tiles, eight waves per workgroup, K split across
+# workgroups with fp32 partials and the reduction kernel): ragged N (a
+# partial last tile, N not a multiple of 4), K of one step, K not a multiple
+# of 512 (a padded last step), one split and several
+DTILE = [(9, 64, 128), (16, 1000, 4096), (17, 130, 512), (24, 600, 1152), (32, 512, 2048),
+         (33, 301, 3200), (40, 2000, 2048), (40, 1026, 640), (16, 5120, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", DTILE)
+def test_mxfp4_prepared_register_tiles(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 8))
+    x8, s = _acts(M, K, (M, K, 8), spread=10.0)
+    say("prepared register tiles", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    again = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    assert np.array_equal(got, again)
+    assert_gemm_close(got, oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"]), (M, N, K))
+
+
+# wide layers at 9 <= M <= 32 whose activation slice fits one workgroup's LDS:
+# the split-K decode kernel with 16 tiles per workgroup (ragged N, a partial
+# last group, K not a multiple of 512)
+@pytest.mark.parametrize("M,N,K", [(9, 33000, 640), (24, 32768, 1152), (31, 40000, 4736), (32, 33000, 256)])
+def test_mxfp4_prepared_wide_sixteen(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 9))
+    x8, s = _acts(M, K, (M, K, 9), spread=10.0)
+    say("prepared wide sixteen", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dev_u8(x8), dev_f32(s), pw))
+    mi, ni = _sample_idx(M, N, 8192, M + N)
+    assert_gemm_close(got[mi, ni], oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni), (M, N, K))
+
+
+# narrow layers at 41 <= M <= 64: 64-row tiles 128 wide, K split across
 # workgroups (fp32 partials + reduction) when long
 @pytest.mark.parametrize("M,N,K", [(33, 16, 1152), (64, 200, 1024), (40, 2000, 2048), (48, 1000, 4096),
                                    (57, 301, 3200)])

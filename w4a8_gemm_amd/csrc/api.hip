@@ -156,9 +156,11 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
             if (kind == W4A8_W4A4_PREPARED) return K <= kPreparedTiledMaxK ? w4a4_workspace_bytes(m, N, K) : 0;
             // the zero-point form takes the int4 kernels' routes and shapes
             const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
-            if (prepared_route(m, N, K, int4) == PreparedRoute::Decode)
-                return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
-            return K <= kPreparedTiledMaxK ? tiled_workspace_bytes(m, N, K, int4) : 0;
+            const PreparedRoute r = prepared_route(m, N, K, int4);
+            if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
+            if (K > kPreparedTiledMaxK) return 0;
+            if (r == PreparedRoute::DTile) return dtile_workspace_bytes(plan_dtile_route(m, N, K), m, N);
+            return tiled_workspace_bytes(m, N, K, int4);
         };
         // Every M up to 64 (the decode band, whose plans change at any M).
         // Above, every tile kernel's shape (64-, 128- or 256-row tiles, the K
@@ -240,6 +242,12 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     const PreparedRoute route = prepared_route(M, N, K, int4);
     if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
+    case PreparedRoute::DTile: {
+        const DtPlan p = plan_dtile_route(M, N, K);
+        st = check_workspace(dtile_workspace_bytes(p, M, N), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_dtile(p, d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws, as_stream(stream)));
+    }
     case PreparedRoute::Tiled:
         st = check_workspace(tiled_workspace_bytes(M, N, K, int4), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
@@ -479,6 +487,19 @@ size_t w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt,
         if (M > kPreparedDecodeMaxM || K % 128 != 0 || u < 2 || u > 4 || ks < 1) return 0;
         return plan_workspace_bytes(plan_prepared(M, N, K, ks, u, false, false), M, N);
     }
+    if (rt > 100) {   // prepared weights, split-K decode kernel: rt - 100 tiles x ks K parts per workgroup
+        if (u < 2 || u > 4 || ks < 1 || (rt - 100) * ks > 16 || M > kPreparedDecodeMaxM || K % 128 != 0) return 0;
+        return plan_workspace_bytes(plan_prepared_explicit(M, N, K, rt - 100, ks, u), M, N);
+    }
+    if (rt == -100) {   // prepared weights, the tiled kernel with K split in ks
+        if (K % 128 != 0 || ks < 1) return 0;
+        return tiled_workspace_bytes(M, N, K, false, ks);
+    }
+    if (rt < 0) {    // prepared weights, register-streamed tiles: -rt tiles per wave
+        if (K % 128 != 0 || (rt != -1 && rt != -2 && rt != -4) || (u != 4 && u != 8 && u != 16) || ks < 1)
+            return 0;
+        return dtile_workspace_bytes(plan_dtile(M, N, K, -rt, u, ks), M, N);
+    }
     if ((rt != 1 && rt != 2 && rt != 4) || (u != 1 && u != 2 && u != 4) || ks < 1) return 0;
     return plan_workspace_bytes(make_decode_plan(M, N, K, rt, u, ks), M, N);
 }
@@ -489,11 +510,32 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
                                   int ks, void* d_ws, size_t ws_bytes, void* stream) {
     w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w, d_out, M, N, K);
     if (st != W4A8_OK) return st;
-    if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
-        if (!d_w_scale || !aligned(d_w_scale, 4) || M > kPreparedDecodeMaxM || u < 2 || u > 4 || ks < 1)
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED && rt == -100) {
+        if (!d_w_scale || !aligned(d_w_scale, 4) || ks < 1) return W4A8_ERR_INVALID_ARG;
+        if (K % 128 != 0 || K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
+        st = check_workspace(tiled_workspace_bytes(M, N, K, false, ks), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, (const uint8_t*)d_w, (const uint8_t*)d_w_scale,
+                                                d_out, M, N, K, d_ws, as_stream(stream), false, false, ks));
+    }
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED && rt < 0) {
+        if (!d_w_scale || !aligned(d_w_scale, 4) || (rt != -1 && rt != -2 && rt != -4) ||
+            (u != 4 && u != 8 && u != 16) || ks < 1)
             return W4A8_ERR_INVALID_ARG;
         if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
-        const GemmPlan p = plan_prepared(M, N, K, ks, u, false, false);
+        const DtPlan p = plan_dtile(M, N, K, -rt, u, ks);
+        st = check_workspace(dtile_workspace_bytes(p, M, N), d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_dtile(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w, (const uint8_t*)d_w_scale,
+                                       d_out, M, N, K, d_ws, as_stream(stream)));
+    }
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED) {
+        if (!d_w_scale || !aligned(d_w_scale, 4) || M > kPreparedDecodeMaxM || u < 2 || u > 4 || ks < 1 ||
+            (rt != 0 && (rt <= 100 || (rt - 100) * ks > 16)))
+            return W4A8_ERR_INVALID_ARG;
+        if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+        const GemmPlan p = rt > 100 ? plan_prepared_explicit(M, N, K, rt - 100, ks, u)
+                                    : plan_prepared(M, N, K, ks, u, false, false);
         st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_decode(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w,

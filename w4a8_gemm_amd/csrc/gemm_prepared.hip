@@ -18,6 +18,8 @@
 //
 // A wavefront then reads every weight and scale byte in whole contiguous
 // 1 KiB / 256 B runs, exactly once, and nothing needs rearranging in registers.
+#include <type_traits>
+
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -836,6 +838,249 @@ hipError_t launch_pdec_plan(const GemmPlan& p, const PDecArgs& a, size_t lds, hi
     W4A8_PDEC(2, 4, 4) W4A8_PDEC(2, 4, 8)
 #undef W4A8_PDEC
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Register-streamed tiles (decode band beyond one 16-row activation tile).
+//
+// A workgroup of four waves covers 4 R 16-row weight tiles against every
+// activation row (16 MT of them); each wave owns R tiles, so each weight
+// fragment has exactly one consumer and goes from HBM straight into that
+// wave's registers -- a ring of D two-step units, loaded D - 1 units ahead --
+// never through LDS, whose capacity then holds no weight bytes in flight.  The
+// activations, which all four waves read, go through a 3-stage LDS ring of two
+// K steps (256 bytes per row, rows padded by 16 bytes so that the 16 column
+// lanes of a fragment hit distinct banks): a unit's activation loads are
+// issued three units ahead, before that unit's weight loads, stored to LDS two
+// units ahead of their use, and published by one barrier per unit.  Vector
+// memory loads complete in issue order, so the wait that an activation store
+// needs never holds back the weight loads issued after it.  With few tiles
+// the grid also splits K; fp32 partials then go to the reduction kernel.
+// ---------------------------------------------------------------------------
+
+struct DtArgs {
+    const uint8_t* x8;
+    const float* xs;
+    const uint4* wt;
+    const uint32_t* st;
+    uint16_t* out;
+    float* partials;
+    int M, N, K;
+    int s_pad, c_pad, tiles;
+    int groups;      // workgroups per K split
+    int ks, h_per;   // K splits across workgroups; two-step units per split (even)
+};
+constexpr int kDtRow = 256 + 16;     // LDS bytes per activation row and stage
+template <int MT> constexpr int kDtStage = 16 * MT * kDtRow;
+
+__device__ __forceinline__ void dt_barrier() {
+    // the stage's LDS stores done, then the workgroup barrier; the empty asm
+    // keeps the compiler from moving LDS accesses across it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// unit h's activations (absolute two-step unit h): 16 MT rows x 16 items of
+// 16 bytes, MT per thread (item i of a thread: threadIdx.x + 256 i); rows past
+// M repeat row M - 1, columns past K (a padded last step, whose weight codes
+// are zero) read the row's last 16 bytes.  Items are named members of a
+// native vector type (a struct copy of uint4 would go through private memory),
+// so that they stay in registers across the unit loop.
+typedef uint32_t dt_u32x4 __attribute__((ext_vector_type(4)));
+template <int MT>
+struct DtAct {
+    dt_u32x4 v0, v1, v2, v3;
+};
+template <int MT, int I>
+__device__ __forceinline__ dt_u32x4& dt_item(DtAct<MT>& x) {
+    if constexpr (I == 0) return x.v0;
+    else if constexpr (I == 1) return x.v1;
+    else if constexpr (I == 2) return x.v2;
+    else return x.v3;
+}
+// items of a thread: it = threadIdx.x + 64 W I < 256 MT (MT x 16 rows x 16)
+template <int MT, int W> constexpr int kDtItems = (4 * MT + W - 1) / W;
+template <int MT, int W, int I>
+__device__ __forceinline__ void dt_act_load_item(const DtArgs& a, int h, DtAct<MT>& x) {
+    if constexpr (I < kDtItems<MT, W>) {
+        const int it = threadIdx.x + 64 * W * I, r = min(it >> 4, 16 * MT - 1), q = it & 15;
+        const int m = min(r, a.M - 1);
+        const int k = min(256 * h + 16 * q, a.K - 16);
+        dt_item<MT, I>(x) = *reinterpret_cast<const dt_u32x4*>(a.x8 + (int64_t)m * a.K + k);
+    }
+}
+template <int MT, int W, int I>
+__device__ __forceinline__ void dt_act_store_item(uint8_t* sb, DtAct<MT>& x) {
+    if constexpr (I < kDtItems<MT, W>) {
+        const int it = threadIdx.x + 64 * W * I, r = it >> 4, q = it & 15;
+        // fewer items than threads (16 waves, one activation tile): the rest store nothing
+        if (64 * W * kDtItems<MT, W> == 256 * MT || it < 256 * MT)
+            *reinterpret_cast<dt_u32x4*>(sb + r * kDtRow + 16 * q) = dt_item<MT, I>(x);
+    }
+}
+template <int MT, int W>
+__device__ __forceinline__ void dt_act_load(const DtArgs& a, int h, DtAct<MT>& x) {
+    dt_act_load_item<MT, W, 0>(a, h, x);
+    dt_act_load_item<MT, W, 1>(a, h, x);
+    dt_act_load_item<MT, W, 2>(a, h, x);
+    dt_act_load_item<MT, W, 3>(a, h, x);
+}
+template <int MT, int W>
+__device__ __forceinline__ void dt_act_store(uint8_t* sb, DtAct<MT>& x) {
+    dt_act_store_item<MT, W, 0>(sb, x);
+    dt_act_store_item<MT, W, 1>(sb, x);
+    dt_act_store_item<MT, W, 2>(sb, x);
+    dt_act_store_item<MT, W, 3>(sb, x);
+}
+
+template <int MT, int R, int U0>
+__device__ __forceinline__ void dt_products(const uint8_t* sb, int lane, const uint4 (&w)[R][2], const uint32_t (&s)[R],
+                                            v4f (&acc)[R][MT]) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+        v8i bx[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint8_t* p = sb + (16 * mt + (lane & 15)) * kDtRow + 128 * uu + 16 * g;
+            bx[mt] = frag_fp8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const v8i af = frag_fp4(w[r][uu]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (uu == 0) acc[r][mt] = mfma16<U0>(af, bx[mt], acc[r][mt], (int)s[r]);
+                else acc[r][mt] = mfma16<U0 + 1>(af, bx[mt], acc[r][mt], (int)s[r]);
+            }
+        }
+    }
+}
+
+// a wave's weights of one two-step unit: steps 2 h, 2 h + 1 of its R tiles
+// (h relative to the split) and their chunk's e8m0 dwords
+template <int R>
+struct DtW {
+    uint4 w[R][2];
+    uint32_t s[R];
+};
+template <int R>
+__device__ __forceinline__ void dt_wload(const uint4* const (&wp)[R], const uint32_t* const (&sp)[R], int h, DtW<R>& u) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        u.w[r][0] = load_stream16(wp[r] + (2 * h) * 64);
+        u.w[r][1] = load_stream16(wp[r] + (2 * h + 1) * 64);
+        u.s[r] = __builtin_nontemporal_load(sp[r] + (h >> 1) * 64);
+    }
+}
+
+// Unit y (ring slot d = y % 4): the loads of unit y + 3 (activations first,
+// into the set of y + 1's parity), the store of unit y + 2's activations
+// (loaded in unit y - 1, in the set of y's parity), the products of unit y, the
+// barrier.  nh is uniform over the workgroup, so every wave takes the same
+// branches and barriers.
+template <int MT, int R, int W, int d>
+__device__ __forceinline__ void dt_unit(const DtArgs& a, uint8_t* lds, int lane, int h0, int nh, int y,
+                                        const uint4* const (&wp)[R], const uint32_t* const (&sp)[R],
+                                        DtW<R> (&ring)[4], DtAct<MT>& av_even, DtAct<MT>& av_odd,
+                                        v4f (&acc)[R][MT]) {
+    if (y >= nh) return;
+    const int last = nh - 1;
+    const int yl = min(y + 3, last);
+    if constexpr ((d & 1) == 0) dt_act_load<MT, W>(a, h0 + yl, av_odd);
+    else dt_act_load<MT, W>(a, h0 + yl, av_even);
+    dt_wload<R>(wp, sp, yl, ring[(d + 3) & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* sb2 = lds + ((y + 2) % 3) * kDtStage<MT>;
+    if constexpr ((d & 1) == 0) dt_act_store<MT, W>(sb2, av_even);
+    else dt_act_store<MT, W>(sb2, av_odd);
+    dt_products<MT, R, 2 * (d & 1)>(lds + (y % 3) * kDtStage<MT>, lane, ring[d].w, ring[d].s, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    dt_barrier();
+}
+
+template <int MT, int R, int W, int D>
+__global__ __launch_bounds__(64 * W) void dtile_kernel(DtArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    static_assert(D == 4, "the unit bookkeeping assumes a 4-deep weight ring");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4;
+    const int tg = blockIdx.x % a.groups, split = blockIdx.x / a.groups;
+    const int t0 = (tg * W + wave) * R;
+    const int h0 = split * a.h_per;                     // even
+    const int nh = min(a.s_pad / 2 - h0, a.h_per);      // >= 1 (host)
+    const int last = nh - 1;
+    const uint4* wp[R];
+    const uint32_t* sp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int tt = min(t0 + r, a.tiles - 1);         // waves past the last tile stream a valid one
+        wp[r] = a.wt + ((int64_t)tt * a.s_pad + 2 * h0) * 64 + lane;
+        sp[r] = a.st + ((int64_t)tt * a.c_pad + h0 / 2) * 64 + lane;
+    }
+    v4f acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    DtW<R> ring[D];
+    DtAct<MT> av_even, av_odd;
+    // prologue: units 0 and 1 staged, unit 2's activations and units 0..2's
+    // weights in flight
+    dt_act_load<MT, W>(a, h0, av_even);
+    dt_act_load<MT, W>(a, h0 + min(1, last), av_odd);
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) dt_wload<R>(wp, sp, min(d, last), ring[d]);
+    dt_act_store<MT, W>(lds, av_even);
+    dt_act_store<MT, W>(lds + kDtStage<MT>, av_odd);
+    dt_act_load<MT, W>(a, h0 + min(2, last), av_even);
+    dt_barrier();
+    for (int h = 0; h < nh; h += 4) {
+        dt_unit<MT, R, W, 0>(a, lds, lane, h0, nh, h, wp, sp, ring, av_even, av_odd, acc);
+        dt_unit<MT, R, W, 1>(a, lds, lane, h0, nh, h + 1, wp, sp, ring, av_even, av_odd, acc);
+        dt_unit<MT, R, W, 2>(a, lds, lane, h0, nh, h + 2, wp, sp, ring, av_even, av_odd, acc);
+        dt_unit<MT, R, W, 3>(a, lds, lane, h0, nh, h + 3, wp, sp, ring, av_even, av_odd, acc);
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int t = t0 + r;
+        const int n0 = 16 * t + 4 * g;
+        if (t >= a.tiles || n0 >= a.N) continue;
+        const bool vec = (a.N & 3) == 0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m >= a.M) continue;
+            if (a.ks == 1) {
+                const float sm = a.xs[m];
+                uint16_t* o = a.out + (int64_t)m * a.N + n0;
+                if (vec) {
+                    const uint32_t h0w = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
+                    const uint32_t h1w = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
+                    *reinterpret_cast<uint2*>(o) = make_uint2(h0w, h1w);
+                } else {
+                    for (int q = 0; q < 4; ++q)
+                        if (n0 + q < a.N) o[q] = (uint16_t)f32_to_bf16_rne(sm * acc[r][mt][q]);
+                }
+            } else {
+                float* pp = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
+                if (vec) {
+                    *reinterpret_cast<float4*>(pp) = make_float4(acc[r][mt][0], acc[r][mt][1], acc[r][mt][2], acc[r][mt][3]);
+                } else {
+                    for (int q = 0; q < 4; ++q)
+                        if (n0 + q < a.N) pp[q] = acc[r][mt][q];
+                }
+            }
+        }
+    }
+}
+
+template <int MT, int R, int W>
+hipError_t launch_dtile_inst(const DtArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((dtile_kernel<MT, R, W, 4>), dim3(a.groups * a.ks), dim3(64 * W), 3 * kDtStage<MT>,
+                       stream, a);
+    return hipGetLastError();
 }
 
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
@@ -2061,10 +2306,29 @@ hipError_t launch_prepare_i5(const int32_t* qkn, const int32_t* qhi, const uint8
 static int64_t lds_row_chunk(bool a4) { return a4 ? 272 : 512; }
 static int64_t lds_row_pad(bool a4) { return a4 ? 32 : 16; }
 
+// Wide MXFP4 layers above 8 rows whose whole activation slice fits LDS: one
+// workgroup of 16 waves per 16 tiles, one wave per tile over all of K (gate_up
+// M = 12 / 16 / 24: 22.0 / 25.4 / 25.5 us with the shape below or the tiled
+// kernel, 20.2 / 20.6 / 21.7 us with it: the slice is staged once per 16 tiles
+// instead of once per 3).  Needs 128 or more such workgroups.
+static bool wide_sixteen(int64_t M, int64_t N, int64_t K, bool a4, bool int4) {
+    const int64_t tiles = (N + 15) / 16, c_pad = (K / 128 + 3) / 4;
+    if (a4 || int4 || M <= 8 || M > kPreparedDecodeMaxM || tiles < 16 * 128) return false;
+    return M * (c_pad * lds_row_chunk(false) + lds_row_pad(false)) <= 160 * 1024;
+}
+
 static void prepared_shape(int64_t M, int64_t N, int64_t K, bool a4, bool int4, int* tw, int* kw, int* ks,
                            int* c_per, bool* lds_bound) {
     const int64_t tiles = (N + 15) / 16;
     const int64_t c_pad = (K / 128 + 3) / 4;
+    if (wide_sixteen(M, N, K, a4, int4)) {
+        *tw = 16;
+        *kw = 1;
+        *ks = 1;
+        *c_per = (int)c_pad;
+        *lds_bound = false;
+        return;
+    }
     const int64_t act_budget = 80 * 1024;          // activations resident in LDS per workgroup
     // K splits across workgroups only when the activations do not fit
     int64_t c_max = (act_budget / M - lds_row_pad(a4)) / lds_row_chunk(a4);
@@ -2133,6 +2397,30 @@ GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, 
     p.ab = lds_bound || M * per_row <= 4 * 64 * (int64_t)tw * kw ? 4 : 8;
     p.ks = ks;
     p.s_per = cp;
+    p.tiles = (N + 15) / 16;
+    return p;
+}
+
+// An explicit split-K decode plan (tuning sweeps): tw tiles and kw K parts
+// per workgroup, ring depth `depth`; K split across workgroups only as far as
+// the activation slice needs to fit 160 KB of LDS.
+GemmPlan plan_prepared_explicit(int64_t M, int64_t N, int64_t K, int tw, int kw, int depth) {
+    GemmPlan p{};
+    p.band = 2;
+    p.mt = (int)((M + 15) / 16);
+    const int64_t c_pad = (K / 128 + 3) / 4;
+    int64_t c_max = (160 * 1024 / M - lds_row_pad(false)) / lds_row_chunk(false);
+    if (c_max < 1) c_max = 1;
+    int64_t s = (c_pad + c_max - 1) / c_max;
+    int64_t cp = (c_pad + s - 1) / s;
+    s = (c_pad + cp - 1) / cp;
+    p.rt = tw;
+    p.kw = kw > cp ? (int)cp : kw;
+    p.u = depth;
+    const int64_t per_row = cp * 512 / 16;
+    p.ab = M * per_row <= 4 * 64 * (int64_t)tw * p.kw ? 4 : 8;
+    p.ks = (int)s;
+    p.s_per = (int)cp;
     p.tiles = (N + 15) / 16;
     return p;
 }
@@ -2208,7 +2496,7 @@ static void apply_split(TiledShape& t, int64_t steps, int64_t k) {
     }
 }
 
-static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
+static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4, int force_ks = 0) {
     TiledShape t{};
     tiled_grid(M, N, M <= 64 ? 64 : 128, t, int4);
     if (M > 128) {
@@ -2231,6 +2519,8 @@ static TiledShape tiled_shape(int64_t M, int64_t N, int64_t K, bool int4) {
             t.ks = (int)k;
             t.s_per = (int)per;
         }
+    } else if (force_ks > 1) {
+        apply_split(t, steps, force_ks);
     } else if (int4 && tiles < 256 && steps >= 48) {
         // int4 tiles that leave CUs idle in their one round (down_proj-shaped
         // M = 2048, 160 tiles: three splits, 306 -> 289 us).  From 256 tiles
@@ -2325,15 +2615,15 @@ hipError_t launch_prepared_tiled_i5(const uint8_t* x8, const float* xs, const ui
     return launch_splitk_reduce(a.partials, xs, M, N, a.ks, out, stream);
 }
 
-size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4) {
-    const TiledShape t = tiled_shape(M, N, K, int4);
+size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4, int force_ks) {
+    const TiledShape t = tiled_shape(M, N, K, int4, force_ks);
     if (t.ks <= 1) return 0;
     return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
 }
 
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 void* ws, hipStream_t stream, bool int4, bool zp) {
+                                 void* ws, hipStream_t stream, bool int4, bool zp, int force_ks) {
     PfArgs a{};
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -2341,7 +2631,7 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
     a.group_m = 8;
-    const TiledShape t = tiled_shape(M, N, K, int4);
+    const TiledShape t = tiled_shape(M, N, K, int4, force_ks);
     const int bm = t.bm, bn = t.bn;
     a.tiles_m = t.tiles_m;
     a.tiles_n = t.tiles_n;
@@ -2468,6 +2758,11 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
     // workgroups (three quarters of the CUs idle in the tiled kernel)
     const bool narrow = (N + 255) / 256 < 64;
+    // narrow MXFP4 layers from 9 to 40 rows: the register-streamed tiles, K
+    // split (down_proj M = 16 / 32: 15.5 / 21.0 us with the split-K decode
+    // kernel or the tiled kernel, 14.3 / 16.3 us with them)
+    if (narrow && !int4 && M > 8 && M <= 40) return PreparedRoute::DTile;
+    if (wide_sixteen(M, N, K, false, int4)) return PreparedRoute::Decode;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
     // M = 16 / 32: 15.9 / 20.2 us vs 18.4 / 21.1 us (tiled split in K); int4
@@ -2525,7 +2820,9 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 // beyond what stays resident (gate_up M = 4 fused in three rounds: 37 us
 // against 23 us for the quant kernel and the GEMM).
 bool plan_prepared_fused(int64_t M, int64_t N, int64_t K, bool int4, GemmPlan* out) {
-    if (M > 16) return false;
+    // (the 16-tile workgroups above 8 rows would each quantize a slice of
+    // 9+ rows: thousands of vector instructions per thread before the stream)
+    if (M > 8) return false;
     GemmPlan p = plan_prepared(M, N, K, 0, 0, false, int4);
     if (p.ks != 1) return false;
     const int64_t items = M * ((int64_t)p.s_per * 512 / 8), threads = 64 * (int64_t)p.rt * p.kw;
@@ -2587,6 +2884,71 @@ static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const
     const hipError_t e = launch_pdec_plan<kWMxA4>(p, a, lds, stream);
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, nullptr, M, N, p.ks, out, stream);
+}
+
+// The register-streamed tiles of the DTile route: one tile per wave, eight
+// waves, K split so that about one round of workgroups covers the CUs.
+DtPlan plan_dtile_route(int64_t M, int64_t N, int64_t K) {
+    const int64_t groups = ((N + 15) / 16 + 7) / 8;
+    int64_t ks = 256 / groups;
+    ks = ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+    return plan_dtile(M, N, K, 1, 8, (int)ks);
+}
+
+// Register-streamed tiles: R tiles per wave (1, 2 or 4), K split across ks
+// workgroups (units of two steps per split rounded up to an even count).
+DtPlan plan_dtile(int64_t M, int64_t N, int64_t K, int R, int W, int ks) {
+    DtPlan p{};
+    p.mt = (int)((M + 15) / 16);
+    p.r = R;
+    p.w = W;
+    const int64_t units = 2 * ((K / 128 + 3) / 4);            // two-step units of the padded steps
+    if (ks < 1) ks = 1;
+    int64_t per = (units + ks - 1) / ks;
+    per = (per + 1) / 2 * 2;
+    p.h_per = (int)per;
+    p.ks = (int)((units + per - 1) / per);
+    p.tiles = (N + 15) / 16;
+    p.groups = (p.tiles + W * R - 1) / (W * R);
+    return p;
+}
+
+size_t dtile_workspace_bytes(const DtPlan& p, int64_t M, int64_t N) {
+    if (p.ks <= 1) return 0;
+    return ws_counter_bytes(p.tiles) + (size_t)p.ks * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                        uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream) {
+    if (M < 1 || M > 64 || p.mt != (int)((M + 15) / 16) || K % 128 != 0) return hipErrorInvalidValue;
+    if (p.ks > 1 && !ws) return hipErrorInvalidValue;
+    if ((int64_t)p.groups * p.ks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+    DtArgs a{};
+    a.x8 = x8; a.xs = xs; a.out = out;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.tiles = (int)p.tiles;
+    a.groups = (int)p.groups;
+    a.ks = p.ks;
+    a.h_per = p.h_per;
+    if (p.ks > 1) a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+    hipError_t e;
+#define W4A8_DT(MT, R, W) else if (p.mt == MT && p.r == R && p.w == W) e = launch_dtile_inst<MT, R, W>(a, stream);
+    if (false) e = hipErrorInvalidValue;
+    // four tiles per wave only with one or two activation tiles (beyond, the
+    // ring and accumulators exceed the registers); 16 waves (128 registers
+    // each) with one tile per wave
+    W4A8_DT(1, 1, 4) W4A8_DT(1, 2, 4) W4A8_DT(1, 4, 4) W4A8_DT(2, 1, 4) W4A8_DT(2, 2, 4) W4A8_DT(2, 4, 4)
+    W4A8_DT(3, 1, 4) W4A8_DT(3, 2, 4) W4A8_DT(4, 1, 4) W4A8_DT(4, 2, 4)
+    W4A8_DT(1, 1, 8) W4A8_DT(1, 2, 8) W4A8_DT(2, 1, 8) W4A8_DT(2, 2, 8) W4A8_DT(3, 1, 8) W4A8_DT(4, 1, 8)
+    W4A8_DT(4, 2, 8) W4A8_DT(1, 1, 16) W4A8_DT(2, 1, 16) W4A8_DT(3, 1, 16) W4A8_DT(4, 1, 16)
+    else return hipErrorInvalidValue;
+#undef W4A8_DT
+    if (e != hipSuccess || p.ks == 1) return e;
+    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 
 }  // namespace w4a8

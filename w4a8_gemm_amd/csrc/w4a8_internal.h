@@ -163,6 +163,7 @@ hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64
 // split-K decode plan on prepared weights; depth 0 = the plan's own ring depth
 GemmPlan plan_prepared(int64_t M, int64_t N, int64_t K, int ks_hint, int depth, bool a4, bool int4);
 size_t prepared_lds_bytes(const GemmPlan& p, int64_t M, bool a4 = false);
+GemmPlan plan_prepared_explicit(int64_t M, int64_t N, int64_t K, int tw, int kw, int depth);
 // zp: int4 weights with zero points (prepared by launch_prepare_i4z)
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
                                   const uint8_t* wt, const uint8_t* st, uint16_t* out, int64_t M,
@@ -171,9 +172,11 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 // (M <= 32 on narrow layers and for int4 weights; on wide MXFP4 layers up to
 // M = 16 while the activation slice of all of K fits one workgroup's LDS) or
 // the tiled kernel (K split across workgroups when its tiles are few).
-enum class PreparedRoute { Decode, Tiled };
+// DTile: the register-streamed tiles (narrow MXFP4 layers, 9 to 40 rows).
+enum class PreparedRoute { Decode, Tiled, DTile };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
-size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4);
+// force_ks > 1: K split in that many parts where the shape rules would not (tuning)
+size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4, int force_ks = 0);
 // The linear on bf16 activations with the per-token fp8 quantization fused
 // into the split-K decode kernel's prologue (one launch), where the plan
 // allows it (plan_prepared_fused); codes and scales also written to x8_out /
@@ -191,7 +194,7 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
-                                 void* ws, hipStream_t stream, bool int4, bool zp);
+                                 void* ws, hipStream_t stream, bool int4, bool zp, int force_ks = 0);
 // int4 g128 in fragment order (same weight geometry as MXFP4; row scales
 // [tile][chunk][step][16] fp16)
 void prepared_i4_sizes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
@@ -214,6 +217,18 @@ hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const u
                                      hipStream_t stream);
 hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
                              uint8_t* st, hipStream_t stream);
+// Register-streamed tiles on prepared MXFP4 weights (decode band, M <= 64):
+// R 16-row tiles per wave, W waves per workgroup, K split across ks
+// workgroups (h_per two-step units each).
+struct DtPlan {
+    int mt, r, w, ks, h_per;
+    int64_t tiles, groups;
+};
+DtPlan plan_dtile(int64_t M, int64_t N, int64_t K, int R, int W, int ks);
+DtPlan plan_dtile_route(int64_t M, int64_t N, int64_t K);
+size_t dtile_workspace_bytes(const DtPlan& p, int64_t M, int64_t N);
+hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                        uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
