@@ -35,6 +35,10 @@ def lib():
         if not os.path.exists(_build.LIB):
             _build.build()
         L = ctypes.CDLL(_build.LIB)
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_set_threads.restype = None
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = ctypes.c_int
         L.orc_e2m1_value.argtypes = [ctypes.c_int]
         L.orc_e2m1_value.restype = ctypes.c_float
         L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -190,6 +194,15 @@ def dequant_mxfp4(packed, e8m0):
     w = np.zeros((rows, half * 2), np.float32)
     lib().orc_dequant_mxfp4(packed, e8m0, rows, half * 2, w)
     return w
+
+
+def set_threads(n):
+    """Threads of the oracle's OpenMP loops (timing only; results do not change)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads():
+    return int(lib().orc_max_threads())
 
 
 def dequant_nvfp4(packed, scale, divisor):

@@ -32,8 +32,14 @@
 
 #include <float.h>
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the parallel loops below (timing only: every loop writes disjoint
+ * outputs, so no result depends on it). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* [P1] module constants: the eight e2m1 magnitudes, index = low three bits. */
 static const float E2M1_GRID[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};

@@ -98,4 +98,8 @@ void    orc_e4m3_encode_array(const float *y, int64_t n, uint8_t *out);
 #ifdef __cplusplus
 }
 #endif
+/* threads of the parallel loops (timing only) */
+void orc_set_threads(int n);
+int orc_max_threads(void);
+
 #endif

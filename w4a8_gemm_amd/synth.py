@@ -112,33 +112,46 @@ def _nvfp4_encode(w: torch.Tensor, gd: float, rows_per_step: int = 2048):
     return packed, scale
 
 
-@functools.lru_cache(maxsize=4)
-def gate_up(seed: int = 1, rows: int = INTERMEDIATE, K: int = HIDDEN, ratio: float = 1.7) -> dict:
-    """Merged gate_up projection, two partitions of `rows` rows each.  Each is
-    N(0, 0.02^2) with 0.1% of entries (Bernoulli) multiplied by 20; the up
-    partition is rescaled so amax_gate / amax_up = ratio; each partition is
-    NVFP4-encoded with its own divisor 6*448/amax."""
+def _gate_up_partitions(seed, rows, K, ratio):
+    """The two fp32 partitions of the gate_up weight, in order, each with its
+    NVFP4 global divisor 6*448/amax."""
     g = _gen(seed)
-    parts, divs = [], []
     amax_gate = None
     for p in range(2):
         w = torch.randn((rows, K), generator=g, dtype=torch.float32) * 0.02
         out = torch.rand((rows, K), generator=g) < 0.001
         w = torch.where(out, w * 20.0, w)
+        del out
         amax = float(w.abs().max())
         if p == 0:
             amax_gate = amax
         else:
             w = w * np.float32(amax_gate / ratio / amax)
             amax = float(w.abs().max())
-        gd = float(np.float32(NVFP4_GLOBAL_NUM / amax))
+        yield w, float(np.float32(NVFP4_GLOBAL_NUM / amax))
+
+
+@functools.lru_cache(maxsize=4)
+def gate_up(seed: int = 1, rows: int = INTERMEDIATE, K: int = HIDDEN, ratio: float = 1.7) -> dict:
+    """Merged gate_up projection, two partitions of `rows` rows each.  Each is
+    N(0, 0.02^2) with 0.1% of entries (Bernoulli) multiplied by 20; the up
+    partition is rescaled so amax_gate / amax_up = ratio; each partition is
+    NVFP4-encoded with its own divisor 6*448/amax."""
+    parts, divs = [], []
+    for w, gd in _gate_up_partitions(seed, rows, K, ratio):
         parts.append(_nvfp4_encode(w, gd))
         divs.append(gd)
-        del w, out
+        del w
     return dict(nv_packed=np.concatenate([parts[0][0], parts[1][0]]),
                 nv_scale=np.concatenate([parts[0][1], parts[1][1]]),
                 part_rows=np.array([rows, rows], np.int64),
                 part_divisor=np.array(divs, np.float32), N=2 * rows, K=K)
+
+
+def gate_up_original(seed: int = 1, rows: int = INTERMEDIATE, K: int = HIDDEN, ratio: float = 1.7) -> torch.Tensor:
+    """The unquantized fp32 weight [2 rows, K] that gate_up() encodes to NVFP4
+    (same draws), for accuracy reports against the original."""
+    return torch.cat([w for w, _ in _gate_up_partitions(seed, rows, K, ratio)])
 
 
 # Magnitude-index frequencies for synthetic MXFP4 codes (shaped like a
