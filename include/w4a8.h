@@ -440,6 +440,25 @@ w4a8_status w4a8_int4g128_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx,
                                           size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * w4a8_mxfp4_gemm_prepared without a workspace argument.  Its split-K partials
+ * go to a static device array of the library (one per GPU, of
+ * w4a8_mxfp4_gemm_prepared_noalloc_max_scratch() bytes = 16 MiB, held until
+ * the process ends); the call allocates and frees nothing.  The caller passes
+ * inputs and outputs as for w4a8_mxfp4_gemm_prepared, on the device current at
+ * the call (the first call on a device looks the array's address up on it).
+ * Every call on one GPU uses that GPU's array, so calls that overlap on one
+ * GPU (concurrent streams) race; calls ordered on a stream do not.  Results
+ * are identical to w4a8_mxfp4_gemm_prepared's.  Errors as that call, and
+ * WORKSPACE when the call's split-K partials need more than the array
+ * (sizes: w4a8_gemm_workspace_bytes with kind MXFP4_PREPARED). */
+w4a8_status w4a8_mxfp4_gemm_prepared_noalloc(const uint8_t *d_x_fp8, const float *d_x_scale,
+                                             const uint8_t *d_w_prepared, const uint8_t *d_s_prepared,
+                                             uint16_t *d_out, int64_t M, int64_t N, int64_t K, void *stream);
+size_t      w4a8_mxfp4_gemm_prepared_noalloc_max_scratch(void);
+
+/* ---------------------------------------------------------------------------
  * Decode band with an explicit plan, for tile-size sweeps (the two GEMM entry
  * points above pick these parameters themselves).  Computes exactly what
  * w4a8_mxfp4_gemm (kind MXFP4: d_w = packed codes, d_w_scale = e8m0) or

@@ -23,6 +23,7 @@ __all__ = [
     "mxfp4_linear_prepared", "int4g128_linear_prepared",
     "PreparedInt4ZP", "int4g128_zp_prepare_fragments", "int4g128_zp_gemm_prepared",
     "PreparedInt5", "int5g128_prepare_fragments", "int5g128_gemm_prepared",
+    "mxfp4_gemm_prepared_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.w4a8_mxfp4_prepare.restype = _int
         L.w4a8_mxfp4_gemm_prepared.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _size, _vp]
         L.w4a8_mxfp4_gemm_prepared.restype = _int
+        L.w4a8_mxfp4_gemm_prepared_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+        L.w4a8_mxfp4_gemm_prepared_noalloc.restype = _int
+        L.w4a8_mxfp4_gemm_prepared_noalloc_max_scratch.argtypes = []
+        L.w4a8_mxfp4_gemm_prepared_noalloc_max_scratch.restype = _size
         for f in ("w4a8_mxfp4_linear_prepared", "w4a8_int4g128_linear_prepared"):
             getattr(L, f).argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _size, _vp]
             getattr(L, f).restype = _int
@@ -461,6 +466,26 @@ def mxfp4_gemm_prepared(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedM
     status = lib().w4a8_mxfp4_gemm_prepared(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
                                             _ptr(out), M, w.N, K, wp, wn, _stream(x_fp8))
     _check(status, "w4a8_mxfp4_gemm_prepared")
+    return out
+
+
+def mxfp4_gemm_prepared_noalloc(x_fp8: torch.Tensor, x_scale: torch.Tensor, w: PreparedMXFP4,
+                                out: torch.Tensor) -> torch.Tensor:
+    """As mxfp4_gemm_prepared with the library's static split-K scratch (no
+    workspace, nothing allocated by the call: `out` is required)."""
+    _need(x_fp8, "x_fp8", torch.uint8)
+    dev = x_fp8.device
+    _need(x_scale, "x_scale", torch.float32, dev)
+    M, K = x_fp8.shape
+    if K != w.K:
+        raise ValueError(f"activation K {K} != weight K {w.K}")
+    _check_weight_sizes("prepared", w.w, w.s, w.N, w.K)
+    _need(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (M, w.N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{M}, {w.N}] tensor")
+    status = lib().w4a8_mxfp4_gemm_prepared_noalloc(_ptr(x_fp8), _ptr(x_scale), _ptr(w.w), _ptr(w.s),
+                                                    _ptr(out), M, w.N, K, _stream(x_fp8))
+    _check(status, "w4a8_mxfp4_gemm_prepared_noalloc")
     return out
 
 

@@ -5,6 +5,8 @@
 // is allocated or freed here; nothing is printed; no environment is read.
 #include <math.h>
 
+#include <mutex>
+
 #include "w4a8_internal.h"
 
 using namespace w4a8;
@@ -263,6 +265,42 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     }
 }
 
+// ---- GEMM on prepared MXFP4 weights with no caller workspace ----
+//
+// The split-K partials of w4a8_mxfp4_gemm_prepared_noalloc live in this
+// file-scope device array: one copy on every GPU the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: host code only ever uses the device address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).  No
+// kernel reads the workspace before a split has written it, so the array
+// needs no clearing between calls.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call per device (with that device current) and kept.
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 // the linear on bf16 activations: fused per-token quant in the decode kernel
 // where the plan allows it, else the quant kernel then gemm_prepared
 static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const uint8_t* d_w, const uint8_t* d_s,
@@ -283,6 +321,21 @@ static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const 
     if (st != W4A8_OK) return st;
     return gemm_prepared(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws, ws_bytes, stream, int4);
 }
+
+w4a8_status w4a8_mxfp4_gemm_prepared_noalloc(const uint8_t* d_x_fp8, const float* d_x_scale,
+                                             const uint8_t* d_w_prepared, const uint8_t* d_s_prepared,
+                                             uint16_t* d_out, int64_t M, int64_t N, int64_t K, void* stream) {
+    w4a8_status st = check_gemm_common(d_x_fp8, d_x_scale, d_w_prepared, d_out, M, N, K);
+    if (st != W4A8_OK) return st;
+    void* ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return W4A8_ERR_HIP;
+    // a call whose split-K partials exceed the array fails in gemm_prepared's
+    // workspace check (W4A8_ERR_WORKSPACE) before anything is enqueued
+    return gemm_prepared(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, ws,
+                         kNoAllocScratchBytes, stream, false);
+}
+
+size_t w4a8_mxfp4_gemm_prepared_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
 
 w4a8_status w4a8_mxfp4_linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const uint8_t* d_w_prepared,
                                        const uint8_t* d_s_prepared, uint16_t* d_out, int64_t M, int64_t N,
