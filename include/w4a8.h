@@ -225,9 +225,11 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
- *     M >= 1.  Small M runs the split-K decode kernel (M <= 32 on narrow
- *     layers: fewer than 64 column tiles of 256; on wider ones up to M = 16
- *     while M x K fp8 activations fit about 80 KB of LDS); larger M the tiled
+ *     M >= 1.  Small M runs the split-K decode kernel (M = 1 and M <= 8 on
+ *     narrow layers: fewer than 64 column tiles of 256), narrow layers at
+ *     9 <= M <= 40 the register-streamed tiles, wide layers (at least 1536
+ *     16-row tiles on 256 CUs, at most 16 per CU) at 2 <= M <= 64 the spread
+ *     tiles (one workgroup per CU, all of K, no workspace); larger M the tiled
  *     kernel (64/128/256 x 128/256 output tiles), which splits K across
  *     workgroups when it has fewer than 128 tiles (fp32 partials in the
  *     workspace, then a reduction kernel).  A workspace sized
@@ -479,7 +481,11 @@ size_t      w4a8_mxfp4_gemm_prepared_noalloc_max_scratch(void);
  *   rt = -r       register-streamed tiles (M <= 64): r = 1, 2 or 4 tiles per
  *                 wave, u = 4, 8 or 16 waves per workgroup, ks = K splits
  *                 across workgroups;
- *   rt = -100     the LDS-tiled kernel with K split in ks parts (any M).
+ *   rt = -100     the LDS-tiled kernel with K split in ks parts (any M);
+ *   rt = -200     spread tiles (M <= 64): one workgroup per CU, each over all
+ *                 of K, ks = weight ring depth in 128-wide steps (4 or 8, 0 =
+ *                 the entry point's choice; UNSUPPORTED_SHAPE unless it
+ *                 divides the padded step count), u ignored; no workspace.
  * w4a8_decode_plan_workspace_bytes: workspace for that plan (0 = none needed, or
  * invalid arguments; rt = 0, rt > 100 and rt < 0 select the prepared-weight
  * plans above).  Errors as the GEMMs, INVALID_ARG for a bad plan. */

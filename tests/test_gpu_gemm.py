@@ -379,10 +379,45 @@ def test_mxfp4_prepared_register_tiles(M, N, K):
     assert_gemm_close(got, oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"]), (M, N, K))
 
 
-# wide layers at 9 <= M <= 32 whose activation slice fits one workgroup's LDS:
+# spread tiles (wide MXFP4 layers, 2 <= M <= 64): every activation-tile
+# count, ragged N (a partial last tile; N % 4 != 0 takes the scalar stores),
+# padded K steps (K / 128 not a multiple of 4), workgroups of 8 and 9 tiles
+# (1 and 2 per wave), through the default route and with each ring depth
+SPREAD = [(2, 24576, 256), (9, 25001, 640), (16, 24600, 1152), (17, 30000, 512), (33, 24584, 384),
+          (48, 26002, 256), (64, 24576, 512), (64, 34816, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", SPREAD)
+def test_mxfp4_prepared_spread(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 10))
+    x8, s = _acts(M, K, (M, K, 10), spread=10.0)
+    say("prepared spread tiles", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    s_pad = 4 * ((K // 128 + 3) // 4)
+    for depth in (4, 8):
+        if depth == 8 and s_pad % 8:
+            with pytest.raises(ValueError):
+                w4.decode_with_plan(dx, ds, pw.w, pw.s, -200, 0, depth, kind="prepared", N=N)
+            continue
+        forced = host_bf16_as_f64(w4.decode_with_plan(dx, ds, pw.w, pw.s, -200, 0, depth, kind="prepared", N=N))
+        # the same products in the same order: bit-identical at either depth
+        assert np.array_equal(forced, got), depth
+    if M * N <= 64 * 26002:
+        ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"])
+        assert_gemm_close(got, ref, (M, N, K))
+    else:
+        mi, ni = _sample_idx(M, N, 8192, M + N)
+        ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni)
+        assert_gemm_close(got[mi, ni], ref, (M, N, K))
+
+
+# layers wider than the spread tiles take (more than 2 x 8 tiles per
+# workgroup) at 9 <= M <= 32 whose activation slice fits one workgroup's LDS:
 # the split-K decode kernel with 16 tiles per workgroup (ragged N, a partial
 # last group, K not a multiple of 512)
-@pytest.mark.parametrize("M,N,K", [(9, 33000, 640), (24, 32768, 1152), (31, 40000, 4736), (32, 33000, 256)])
+@pytest.mark.parametrize("M,N,K", [(9, 66000, 640), (24, 65600, 1152), (31, 70000, 4736), (32, 66008, 256)])
 def test_mxfp4_prepared_wide_sixteen(M, N, K):
     w = synth.mxfp4_random(N, K, seed=(M, N, K, 9))
     x8, s = _acts(M, K, (M, K, 9), spread=10.0)

@@ -160,6 +160,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
             const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
             const PreparedRoute r = prepared_route(m, N, K, int4);
             if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
+            if (r == PreparedRoute::Spread) return 0;
             if (K > kPreparedTiledMaxK) return 0;
             if (r == PreparedRoute::DTile) return dtile_workspace_bytes(plan_dtile_route(m, N, K), m, N);
             return tiled_workspace_bytes(m, N, K, int4);
@@ -242,8 +243,12 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     // the tiled kernel addresses activations with 32-bit offsets
     const PreparedRoute route = prepared_route(M, N, K, int4);
-    if (route != PreparedRoute::Decode && K > kPreparedTiledMaxK) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (route != PreparedRoute::Decode && route != PreparedRoute::Spread && K > kPreparedTiledMaxK)
+        return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
+    case PreparedRoute::Spread:
+        return hip_status(launch_spread(plan_spread(M, N, K, 0), d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
+                                        as_stream(stream)));
     case PreparedRoute::DTile: {
         const DtPlan p = plan_dtile_route(M, N, K);
         st = check_workspace(dtile_workspace_bytes(p, M, N), d_ws, ws_bytes);
@@ -544,6 +549,7 @@ size_t w4a8_decode_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, int rt,
         if (u < 2 || u > 4 || ks < 1 || (rt - 100) * ks > 16 || M > kPreparedDecodeMaxM || K % 128 != 0) return 0;
         return plan_workspace_bytes(plan_prepared_explicit(M, N, K, rt - 100, ks, u), M, N);
     }
+    if (rt == -200) return 0;   // prepared weights, spread tiles (ring depth ks, 0: default): no workspace
     if (rt == -100) {   // prepared weights, the tiled kernel with K split in ks
         if (K % 128 != 0 || ks < 1) return 0;
         return tiled_workspace_bytes(M, N, K, false, ks);
@@ -570,6 +576,15 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
         if (st != W4A8_OK) return st;
         return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, (const uint8_t*)d_w, (const uint8_t*)d_w_scale,
                                                 d_out, M, N, K, d_ws, as_stream(stream), false, false, ks));
+    }
+    if (kind == W4A8_WEIGHT_MXFP4_PREPARED && rt == -200) {
+        if (!d_w_scale || !aligned(d_w_scale, 4) || (ks != 0 && ks != 4 && ks != 8)) return W4A8_ERR_INVALID_ARG;
+        // the ring turns in whole trips over the padded steps
+        if (K % 128 != 0 || M > 64 || (ks != 0 && (4 * ((K / 128 + 3) / 4)) % ks != 0))
+            return W4A8_ERR_UNSUPPORTED_SHAPE;
+        const SpPlan p = plan_spread(M, N, K, ks);
+        return hip_status(launch_spread(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w, (const uint8_t*)d_w_scale, d_out,
+                                        M, N, K, as_stream(stream)));
     }
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED && rt < 0) {
         if (!d_w_scale || !aligned(d_w_scale, 4) || (rt != -1 && rt != -2 && rt != -4) ||

@@ -1083,6 +1083,225 @@ hipError_t launch_dtile_inst(const DtArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Spread tiles (wide layers, decode band up to 64 rows): one workgroup of
+// eight waves per CU and the layer's 16-row weight tiles dealt out evenly --
+// a workgroup takes the floor or the ceiling of tiles / workgroups, a wave
+// the floor or the ceiling of an eighth of that (gate_up, 2176 tiles on 256
+// CUs: 8 or 9 per workgroup, 1 or 2 per wave) -- each over all of K, so
+// there are no partial sums and no second pass.  (The tiled kernel's 256-row
+// panels give the same layer 136 workgroups: 120 CUs idle.)
+//
+// Weights stream straight into a register ring D steps ahead: per tile and
+// step one 16-byte load per lane (the 1 KiB fragment block, lane order =
+// operand order) and the chunk's e8m0 dword.  The activation slice of a step
+// (64 rows x 128 bytes; rows past M repeat row M - 1) goes global ->
+// registers (one 16-byte item per thread, D + 1 steps ahead) -> a 4-stage
+// LDS ring shared by the eight waves, rows 128 bytes with 16-byte chunk c of
+// row r at c ^ ((r >> 1) & 7), so that a fragment read (16 rows x 4 chunk
+// groups) hits every bank once.  One barrier per step.  Iteration s:
+//   barrier (stores of step s + 1 visible; step s - 2's stage free)
+//   LDS reads of step s + 1's fragments (into the other register set)
+//   load of step s + D + 1's activation item; store of step s + 2's
+//   products of step s (fragments read in iteration s - 1)
+//   loads of step s + D's weights (into the ring slot step s just used)
+// so the LDS latency hides under the matrix pipe, and two waves per SIMD
+// overlap one's reads with the other's products.  Every load is an ordinary
+// compiler-visible load; the activation item is issued ahead of the weights
+// of the same iteration, so the wait before its store (two steps ahead of
+// use) never drains weights newer than the next step's.
+//
+// The loop runs over the padded steps (the padding blocks hold zero codes,
+// whose products are zero) in branch-free trips of D steps (the padded step
+// count is a multiple of 4; D = 8 only where it is a multiple of 8);
+// activation loads past K repeat the last real step.  A wave with fewer
+// tiles than the most (R) runs its own copy of the loop with R - 1, chosen
+// once per wave.
+// ---------------------------------------------------------------------------
+struct SpArgs {
+    const uint8_t* x8;
+    const float* xs;
+    const uint4* wt;
+    const uint32_t* st;
+    uint16_t* out;
+    int M, N, K;
+    int s_pad, c_pad, tiles, steps;   // steps = K / 128 (real), s_pad = padded
+    int groups;
+};
+constexpr int kSpThreads = 512;
+constexpr int kSpWaves = kSpThreads / 64;
+constexpr int kSpStage = 64 * 128;
+constexpr int kSpStages = 4;
+
+template <int R, int D>
+struct SpRing {
+    dt_u32x4 w[D][R];
+    uint32_t s[D][R];
+};
+
+template <int MT>
+__device__ __forceinline__ void sp_read(const uint8_t* stage, int lane, v8i (&F)[MT]) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * mt + (lane & 15), sw = (r >> 1) & 7;
+        const uint8_t* row = stage + 128 * r;
+        F[mt] = frag_fp8(*reinterpret_cast<const uint4*>(row + 16 * (g ^ sw)),
+                         *reinterpret_cast<const uint4*>(row + 16 * ((g + 4) ^ sw)));
+    }
+}
+
+// this wave's per-lane sources and this thread's activation item
+template <int R>
+struct SpSrc {
+    const uint4* wp[R];
+    const uint32_t* sp[R];
+    const uint8_t* xrow;     // activation row of this thread's item, at its chunk
+    uint32_t xdst;           // the item's offset in a stage
+    int x_last, w_last;      // last real step (activations), last padded step (weights)
+};
+
+template <int R>
+__device__ __forceinline__ dt_u32x4 sp_act(const SpSrc<R>& q, int j) {
+    return *reinterpret_cast<const dt_u32x4*>(q.xrow + 128 * (int64_t)min(j, q.x_last));
+}
+
+template <int R, int D>
+__device__ __forceinline__ void sp_wload(const SpSrc<R>& q, int j, SpRing<R, D>& ring, int slot) {
+    j = min(j, q.w_last);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint4 v = load_stream16(q.wp[r] + (int64_t)j * 64);
+        ring.w[slot][r] = dt_u32x4{v.x, v.y, v.z, v.w};
+        ring.s[slot][r] = q.sp[r][(j >> 2) * 64];
+    }
+}
+
+// one step of the main loop; J = s mod D (ring and activation slots, stage
+// and fragment set are compile-time)
+template <int MT, int R, int D, int J>
+__device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
+                                        dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+    dt_barrier();
+    if constexpr ((J & 1) == 0) sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F1);
+    else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
+    av[(J + 1) % D] = sp_act(q, s + D + 1);
+    *reinterpret_cast<dt_u32x4*>(lds + ((J + 2) % kSpStages) * kSpStage + q.xdst) = av[(J + 2) % D];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const dt_u32x4 w = ring.w[J % D][r];
+        const v8i af = frag_fp4(make_uint4(w[0], w[1], w[2], w[3]));
+        const int sc = (int)(ring.s[J % D][r] >> (8 * (J & 3)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr ((J & 1) == 0) acc[r][mt] = mfma16<0>(af, F0[mt], acc[r][mt], sc);
+            else acc[r][mt] = mfma16<0>(af, F1[mt], acc[r][mt], sc);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sp_wload<R, D>(q, s + D, ring, J % D);
+}
+
+template <int MT, int R, int D, int J>
+__device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
+                                        dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+    if constexpr (J < D) {
+        sp_step<MT, R, D, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
+        sp_trip<MT, R, D, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
+    }
+}
+
+// a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x sum
+template <int MT, int R, int D>
+__device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane) {
+    const int tid = threadIdx.x, g = lane >> 4;
+    SpSrc<R> q;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
+        q.sp[r] = a.st + (int64_t)(w0 + r) * a.c_pad * 64 + lane;
+    }
+    // this thread's activation item: row tid / 8 (clamped to M - 1), chunk tid % 8
+    const int xr = tid >> 3, c = tid & 7;
+    q.xrow = a.x8 + (int64_t)min(xr, a.M - 1) * a.K + 16 * c;
+    q.xdst = 128u * xr + 16u * (c ^ ((xr >> 1) & 7));
+    q.x_last = a.steps - 1;
+    q.w_last = a.s_pad - 1;
+
+    v4f acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    SpRing<R, D> ring;
+    dt_u32x4 av[D];
+    v8i F0[MT], F1[MT];
+
+    // prologue = iterations -D-1 .. -1 without products: activation items of
+    // steps 0 .. D, weights of steps 0 .. D - 1, steps 0 and 1 stored, step
+    // 0's fragments read
+    av[0] = sp_act(q, 0);
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        av[(k + 1) % D] = sp_act(q, k + 1);
+        if (k == D - 2) *reinterpret_cast<dt_u32x4*>(lds + q.xdst) = av[0];
+        sp_wload<R, D>(q, k, ring, k);
+    }
+    dt_barrier();
+    sp_read<MT>(lds, lane, F0);
+    *reinterpret_cast<dt_u32x4*>(lds + kSpStage + q.xdst) = av[1];
+
+    for (int s = 0; s < a.s_pad; s += D) sp_trip<MT, R, D, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
+
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int n0 = 16 * (w0 + r) + 4 * g;
+        if (n0 >= a.N) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m >= a.M) continue;
+            const float sm = a.xs[m];
+            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            if (vec) {
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
+                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
+            } else {
+                for (int qq = 0; qq < 4; ++qq)
+                    if (n0 + qq < a.N) o[qq] = (uint16_t)f32_to_bf16_rne(sm * acc[r][mt][qq]);
+            }
+        }
+    }
+}
+
+template <int MT, int R, int D>
+__global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
+    static_assert(D == 4 || D == 8, "a trip is one turn of the ring and whole 4-step chunks");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform: scalar branches
+    // this workgroup's tiles, then this wave's (the host gives every wave 1 .. R)
+    const int64_t T = a.tiles, G = a.groups;
+    const int t_lo = (int)(T * blockIdx.x / G), n = (int)(T * (blockIdx.x + 1) / G) - t_lo;
+    const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
+    if constexpr (R > 1) {
+        if (nr < R) {
+            sp_run<MT, R - 1, D>(a, lds, w0, lane);
+            return;
+        }
+    }
+    sp_run<MT, R, D>(a, lds, w0, lane);
+}
+
+template <int MT, int R, int D>
+hipError_t launch_spread_inst(const SpArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((spread_kernel<MT, R, D>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
 // batch of 4 loads per thread (ring depth 2 or 3) or 8 (depth 2)
 template <int WF>
@@ -2762,6 +2981,11 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // split (down_proj M = 16 / 32: 15.5 / 21.0 us with the split-K decode
     // kernel or the tiled kernel, 14.3 / 16.3 us with them)
     if (narrow && !int4 && M > 8 && M <= 40) return PreparedRoute::DTile;
+    // wide MXFP4 layers from 2 to 64 rows: the spread tiles, one workgroup per
+    // CU over all of K (gate_up M = 8 / 16 / 32 / 64: 17.7 / 18.1 / 19.5 /
+    // 24 us against 18.1 / 20.7 / 26 / 28.9 us with the split-K decode or the
+    // tiled kernel)
+    if (!int4 && M >= 2 && spread_fits(M, N, K)) return PreparedRoute::Spread;
     if (wide_sixteen(M, N, K, false, int4)) return PreparedRoute::Decode;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
@@ -2949,6 +3173,72 @@ hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, con
 #undef W4A8_DT
     if (e != hipSuccess || p.ks == 1) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+}
+
+
+// CUs of the current device (cached per device)
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Spread tiles: one workgroup per CU (at most tiles / 8, so that every wave
+// has a tile); R = the most tiles a wave gets; ring depth 8 steps for one
+// activation tile where the padded steps allow (measured on gate_up M = 1 ..
+// 16: 17.4 - 18.1 us against 18.1 - 19.5 us at depth 4), else 4 (two to four
+// activation tiles: depth 8 was no faster).
+SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D) {
+    SpPlan p{};
+    p.mt = (int)((M + 15) / 16);
+    const int64_t s_pad = 4 * ((K / 128 + 3) / 4);
+    p.d = D > 0 ? D : (p.mt == 1 && s_pad % 8 == 0 ? 8 : 4);
+    p.tiles = (N + 15) / 16;
+    int64_t g = device_cus();
+    if (g > p.tiles / kSpWaves) g = p.tiles / kSpWaves;
+    p.groups = g;
+    p.r = g >= 1 ? (int)(((p.tiles + g - 1) / g + kSpWaves - 1) / kSpWaves) : 0;
+    return p;
+}
+
+bool spread_fits(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > 64 || K % 128 != 0) return false;
+    const SpPlan p = plan_spread(M, N, K, 0);
+    // most CUs busy, and an instantiated tile count
+    return p.groups * 4 >= (int64_t)device_cus() * 3 && p.r >= 1 && p.r <= 2;
+}
+
+hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (M < 1 || M > 64 || p.mt != (int)((M + 15) / 16) || K % 128 != 0 || p.groups < 1) return hipErrorInvalidValue;
+    if (p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16) return hipErrorInvalidValue;
+    // every wave has a tile, and none more than R
+    if (p.tiles < (int64_t)kSpWaves * p.groups || (p.tiles + p.groups - 1) / p.groups > (int64_t)kSpWaves * p.r)
+        return hipErrorInvalidValue;
+    SpArgs a{};
+    a.x8 = x8; a.xs = xs; a.out = out;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.steps = (int)(K / 128);
+    a.tiles = (int)p.tiles;
+    a.groups = (int)p.groups;
+    if (a.s_pad % p.d != 0) return hipErrorInvalidValue;
+#define W4A8_SP(MT, R, D) else if (p.mt == MT && p.r == R && p.d == D) return launch_spread_inst<MT, R, D>(a, stream);
+    if (false) {}
+    W4A8_SP(1, 1, 4) W4A8_SP(2, 1, 4) W4A8_SP(3, 1, 4) W4A8_SP(4, 1, 4)
+    W4A8_SP(1, 2, 4) W4A8_SP(2, 2, 4) W4A8_SP(3, 2, 4) W4A8_SP(4, 2, 4)
+    W4A8_SP(1, 1, 8) W4A8_SP(1, 2, 8) W4A8_SP(2, 2, 8) W4A8_SP(3, 2, 8) W4A8_SP(4, 2, 8)
+#undef W4A8_SP
+    return hipErrorInvalidValue;
 }
 
 }  // namespace w4a8

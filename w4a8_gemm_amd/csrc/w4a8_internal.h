@@ -173,7 +173,7 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 // M = 16 while the activation slice of all of K fits one workgroup's LDS) or
 // the tiled kernel (K split across workgroups when its tiles are few).
 // DTile: the register-streamed tiles (narrow MXFP4 layers, 9 to 40 rows).
-enum class PreparedRoute { Decode, Tiled, DTile };
+enum class PreparedRoute { Decode, Tiled, DTile, Spread };
 PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 // force_ks > 1: K split in that many parts where the shape rules would not (tuning)
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4, int force_ks = 0);
@@ -229,6 +229,18 @@ DtPlan plan_dtile_route(int64_t M, int64_t N, int64_t K);
 size_t dtile_workspace_bytes(const DtPlan& p, int64_t M, int64_t N);
 hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                         uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream);
+// Spread tiles on prepared MXFP4 weights (wide layers, M <= 64): one
+// workgroup of eight waves per CU, the 16-row tiles dealt out evenly (at most
+// R per wave), all of K per workgroup; D = weight ring depth in steps (0:
+// the default for the shape).
+struct SpPlan {
+    int mt, r, d;
+    int64_t tiles, groups;
+};
+SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D);
+bool spread_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
