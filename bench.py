@@ -8,9 +8,8 @@ repacked once into matrix-core fragment order), for each batch M in
 block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights, one call
 of the linear entry point per M.  The calls' kernels (STEP_KERNELS): M = 1 one
 launch (the quantization fused into the split-K decode kernel's prologue);
-M = 8 the quant kernel and the split-K decode kernel; M = 16 the quant kernel
-and the split-K decode kernel with 16 tiles per workgroup; M = 64 the quant
-kernel and the LDS-tiled kernel.  The step's four linears read four different
+M = 8, 16 and 64 the quant kernel and the spread-tile kernel (one workgroup
+per CU, the weight tiles dealt out evenly, each over all of K).  The step's four linears read four different
 copies of the weight out of eight (95 MB each, 758 MB in all, three times the
 256 MB Infinity Cache; step s uses copies 4s .. 4s + 3 mod 8), so every weight
 byte of a step comes from HBM.  Each step is one HIP graph replay (one graph
@@ -62,11 +61,11 @@ N_GU, K_GU = 34816, 5120
 STEP_KERNELS = {
     1: [("pdec_kernel<1, 3, 0, 4, true>", "split-K decode, per-token quant fused in its prologue")],
     8: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-        ("pdec_kernel<1, 2, 0, 8, false>", "split-K decode, 3 tiles per workgroup")],
+        ("spread_kernel<1, 2, 8>", "spread tiles: one workgroup per CU over all of K, ring depth 8")],
     16: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("pdec_kernel<1, 2, 0, 8, false>", "split-K decode, 16 tiles per workgroup")],
+         ("spread_kernel<1, 2, 8>", "spread tiles: one workgroup per CU over all of K, ring depth 8")],
     64: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("pfp_kernel<64, 256, 5, 0>", "LDS-tiled, 64 x 256 tiles")],
+         ("spread_kernel<4, 2, 4>", "spread tiles: one workgroup per CU over all of K, ring depth 4")],
 }
 SOURCES = {"gemm": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip"),
            "act_quant": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "act_quant.hip"),
