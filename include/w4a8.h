@@ -168,11 +168,16 @@ w4a8_status w4a8_quant_act_fp8_per_token(
 
 /* ---------------------------------------------------------------------------
  * GEMM workspace.  The decode band may split K across workgroups; the fp32
- * partial sums live in a caller-owned workspace, reduced in split order by a
- * second kernel on the same stream ("radiance_autoround.py": the split-K
- * scratch is registered once, before any launch, because allocating inside a
- * captured graph is illegal).  The library keeps no state in it between calls;
- * w4a8_workspace_init (zero fill) is optional.
+ * partial sums live in a caller-owned workspace ("radiance_autoround.py": the
+ * split-K scratch is registered once, before any launch, because allocating
+ * inside a captured graph is illegal).  In the decode kernels the last split
+ * of an output block to arrive adds them in split order ("vllm-radiance
+ * (MXFP4)", The W4A8 fp8-WMMA kernel), counting arrivals in one word per
+ * block at the start of the workspace; the tile kernels' splits are added by
+ * a second kernel on the same stream.  Zero the workspace once before its
+ * first use (w4a8_workspace_init, or any zero fill): every call leaves the
+ * counters at zero again, so it needs no clearing between calls.  Calls that
+ * overlap on one workspace race.
  *
  * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
  * N, K and kind and any M <= M_max (0 if no split is used).  Pure host

@@ -150,6 +150,39 @@ def test_mxfp4_split_k_deterministic_and_workspace_reuse():
                 assert np.array_equal(o, first[M]), M
 
 
+def test_split_k_in_place_counters_return_to_zero(down_proj_prepared):
+    """Split-K reduced in place by the last split ("vllm-radiance (MXFP4)", The
+    W4A8 fp8-WMMA kernel): calls with different split counts on one workspace
+    (register tiles at M = 16 / 32, split-K decode at M = 3 / 8, the
+    plain-layout decode kernel) each match the reference, repeat bit for bit,
+    and leave every arrival counter at zero."""
+    d, pw = down_proj_prepared
+    ws = w4.Workspace(64, d["N"], d["K"], "prepared")
+    ws_rm = w4.Workspace(64, d["N"], d["K"], "mxfp4")
+    dw, de = dev_u8(d["w_packed"]), dev_u8(d["w_e8m0"])
+    first = {}
+    for rep in range(3):
+        for M in (16, 3, 32, 8, 1):
+            x8, s = _acts(M, d["K"], (11, M))
+            say("split-K in place", rep, M)
+            dx, ds = dev_u8(x8), dev_f32(s)
+            o = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw, workspace=ws))
+            o_rm = host_bf16_as_f64(w4.mxfp4_gemm(dx, ds, dw, de, workspace=ws_rm))
+            if rep == 0:
+                mi, ni = _sample_idx(M, d["N"], 4096, M)
+                ref = oracle.mxfp4_gemm(x8, s, d["w_packed"], d["w_e8m0"], mi=mi, ni=ni)
+                assert_gemm_close(o[mi, ni], ref, ("prepared", M))
+                assert_gemm_close(o_rm[mi, ni], ref, ("row-major", M))
+                first[M] = (o, o_rm)
+            else:
+                assert np.array_equal(o, first[M][0]), M
+                assert np.array_equal(o_rm, first[M][1]), M
+    torch.cuda.synchronize()
+    for w in (ws, ws_rm):
+        head = w.buf[:256].cpu().numpy()
+        assert not head.any(), "arrival counters left nonzero"
+
+
 def test_mxfp4_rejects_small_workspace():
     d = synth.down_proj()
     x8, s = _acts(16, d["K"], 1)

@@ -402,7 +402,8 @@ def decode_with_plan(x_fp8, x_scale, w, w_scale, rt: int, u: int, ks: int, kind:
     """Decode-band GEMM (M <= 64) with an explicit plan (for tile sweeps): rt 16-row
     weight tiles per wave, u 128-wide K steps per chunk, ks requested K splits
     (kind "prepared": rt 0, u the prefetch depth, N required).  `workspace` is a
-    uint8 cuda tensor of at least the plan's workspace bytes."""
+    uint8 cuda tensor of at least the plan's workspace bytes, zeroed before its
+    first use (its split-K arrival counters)."""
     M, K = x_fp8.shape
     if N is None:
         if kind == "prepared":
@@ -414,7 +415,8 @@ def decode_with_plan(x_fp8, x_scale, w, w_scale, rt: int, u: int, ks: int, kind:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     need = int(lib().w4a8_decode_plan_workspace_bytes(M, N, K, rt, u, ks))
     if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty((need + 255) // 256 * 256, dtype=torch.uint8, device=dev)
+        # zeroed: the split-K arrival counters start at zero (and stay there between calls)
+        workspace = torch.zeros((need + 255) // 256 * 256, dtype=torch.uint8, device=dev)
     status = lib().w4a8_decode_with_plan(_KINDS[kind], _ptr(x_fp8), _ptr(x_scale), _ptr(w), _ptr(w_scale),
                                          _ptr(out), M, N, K, rt, u, ks, _ptr(workspace),
                                          0 if workspace is None else workspace.numel(),

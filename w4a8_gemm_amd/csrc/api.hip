@@ -276,9 +276,11 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
 // file-scope device array: one copy on every GPU the library runs on, held
 // until the process ends.  In host code `scratch` names a host-side stand-in,
 // not device memory: host code only ever uses the device address that
-// hipGetSymbolAddress returns for the current device (noalloc_scratch).  No
-// kernel reads the workspace before a split has written it, so the array
-// needs no clearing between calls.
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).  The
+// array starts zeroed (static device storage), as the split-K arrival
+// counters at its start must be; every call leaves them at zero again, and no
+// kernel reads a partial before its split has written it, so the array needs
+// no clearing between calls.
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 

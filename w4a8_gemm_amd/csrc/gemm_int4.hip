@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
 // (m, g) holds the same 32 activation bytes (the fp8 operand's byte j < 16 sits
 // at MFMA slot 16g + j and byte 16 + j at slot 64 + 16g + j, identically for
 // both operands).  The lane's four output rows n0..n0+3 take their group scales
-// from one 8-byte load.  Split K goes through fp32 partials and the shared
-// reduction kernel.
+// from one 8-byte load.  Split K goes through fp32 partials that the row
+// block's last split to arrive adds in place (sk_arrive / sk_reduce).
 // ---------------------------------------------------------------------------
 
 constexpr int kDecThreads = 256;
@@ -94,6 +94,8 @@ struct I4DecArgs {
     const uint16_t* sc;
     uint16_t* out;
     float* partials;
+    uint32_t* counters;   // ks > 1: one arrival counter per row block
+    int sk_inplace;       // ks > 1: the last split reduces (else the reduction kernel does)
     int M, N, K;
     int ks, s_per, tiles;
 };
@@ -221,10 +223,17 @@ __global__ __launch_bounds__(kDecThreads) void i4_decode_kernel(I4DecArgs a) {
                 const uint32_t h1 = f32_to_bf16_rne(sm * acc[rt][mt][2]) | (f32_to_bf16_rne(sm * acc[rt][mt][3]) << 16);
                 *reinterpret_cast<uint2*>(a.out + (int64_t)m * a.N + n0) = make_uint2(h0, h1);
             } else {
-                *reinterpret_cast<float4*>(a.partials + ((int64_t)split * a.M + m) * a.N + n0) =
-                    make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
+                sk_put4(sk_rsrc(a.partials), 4u * (uint32_t)(((int64_t)split * a.M + m) * a.N + n0),
+                        acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
             }
         }
+    }
+    if (a.ks > 1 && a.sk_inplace) {
+        // K split: the row block's last split to arrive adds the partials
+        __shared__ uint32_t last_flag;
+        if (sk_arrive(a.counters + tile, a.ks, &last_flag))
+            sk_reduce(a.partials, a.xs, a.M, a.N, a.ks, tile * (4 * RT * 16), min(a.N, (tile + 1) * (4 * RT * 16)),
+                      a.out, threadIdx.x, kDecThreads);
     }
 }
 
@@ -482,8 +491,11 @@ hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* x
     a.x8 = x8; a.xs = xs; a.qw = qw_nk; a.sc = scales; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.ks = p.ks; a.s_per = p.s_per; a.tiles = (int)p.tiles;
-    if (p.ks > 1)
+    if (p.ks > 1) {
+        a.counters = reinterpret_cast<uint32_t*>(ws);
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+        a.sk_inplace = sk_inplace_fits(p.ks, M, N) ? 1 : 0;
+    }
     hipError_t e;
     switch (p.mt) {
         case 1: e = launch_i4dec_rt<1>(a, p.rt, p.u, stream); break;
@@ -491,7 +503,7 @@ hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* x
         case 3: e = launch_i4dec_rt<3>(a, p.rt, p.u, stream); break;
         default: e = launch_i4dec_rt<4>(a, p.rt, p.u, stream); break;
     }
-    if (e != hipSuccess || p.ks == 1) return e;
+    if (e != hipSuccess || p.ks == 1 || a.sk_inplace) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 

@@ -71,10 +71,9 @@ __device__ __forceinline__ v16f mfma32(v8i a_fp4, v8i b_fp8, v16f c, int scale_a
 // 128t + 16g and 128t + 64 + 16g of row m (L2 resident, shared by all waves).
 // The whole next chunk (weights, scales, activations) is issued before the
 // current chunk's MFMAs, so one chunk of loads is always in flight per wave.
-// With more than one K split each split writes fp32 partial sums; a separate
-// reduction kernel adds them in split order (bitwise deterministic) -- a kernel
-// boundary is the only coherence point shared by all eight per-XCD L2 caches
-// that costs nothing inside the streaming kernel.
+// With more than one K split each split writes fp32 partial sums through to the
+// device's coherence point, and the row block's last split to arrive adds
+// them in split order (bitwise deterministic; sk_arrive / sk_reduce).
 // K % 128 != 0 runs one masked step at a time (U = 1).
 // ===========================================================================
 
@@ -87,6 +86,8 @@ struct DecArgs {
     const uint8_t* we;
     uint16_t* out;
     float* partials;
+    uint32_t* counters;   // ks > 1: one arrival counter per row block
+    int sk_inplace;       // ks > 1: the last split reduces (else the reduction kernel does)
     int M, N, K;
     int ks;        // K splits
     int s_per;     // 128-wide steps per split
@@ -265,16 +266,22 @@ __global__ __launch_bounds__(kDecThreads) void mx_decode_kernel(DecArgs a) {
                     for (int r = 0; r < 4; ++r)
                         if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[rt][mt][r]);
                 }
+            } else if (vec) {
+                sk_put4(sk_rsrc(a.partials), 4u * (uint32_t)(((int64_t)split * a.M + m) * a.N + n0),
+                        acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
             } else {
                 float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-                if (vec) {
-                    *reinterpret_cast<float4*>(p) = make_float4(acc[rt][mt][0], acc[rt][mt][1], acc[rt][mt][2], acc[rt][mt][3]);
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (n0 + r < a.N) p[r] = acc[rt][mt][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < a.N) sk_put(p + r, acc[rt][mt][r]);
             }
         }
+    }
+    if (a.ks > 1 && a.sk_inplace) {
+        // K split: the row block's last split to arrive adds the partials
+        __shared__ uint32_t last_flag;
+        if (sk_arrive(a.counters + tile, a.ks, &last_flag))
+            sk_reduce(a.partials, a.xs, a.M, a.N, a.ks, tile * (4 * RT * 16), min(a.N, (tile + 1) * (4 * RT * 16)),
+                      a.out, threadIdx.x, kDecThreads);
     }
 }
 
@@ -594,8 +601,11 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
     a.x8 = x8; a.xs = xs; a.wq = wq; a.we = we; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     a.ks = p.ks; a.s_per = p.s_per; a.tiles = (int)p.tiles;
-    if (p.ks > 1)
+    if (p.ks > 1) {
+        a.counters = reinterpret_cast<uint32_t*>(ws);
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+        a.sk_inplace = sk_inplace_fits(p.ks, M, N) ? 1 : 0;
+    }
     const bool k128 = (K % 128) == 0;
     hipError_t e;
     switch (p.mt) {
@@ -604,7 +614,7 @@ hipError_t launch_mxfp4_gemm(const GemmPlan& p, const uint8_t* x8, const float* 
         case 3: e = launch_dec_rt<3>(a, p.rt, p.u, k128, stream); break;
         default: e = launch_dec_rt<4>(a, p.rt, p.u, k128, stream); break;
     }
-    if (e != hipSuccess || p.ks == 1) return e;
+    if (e != hipSuccess || p.ks == 1 || a.sk_inplace) return e;
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 

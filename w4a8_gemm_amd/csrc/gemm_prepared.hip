@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void prep_i5s_kernel(const uint16_t* __restric
 // partial accumulators of a tile are added through LDS in part order 0..KW-1
 // (deterministic) by the part-0 wave, which writes the bf16 output -- or, when
 // the grid also splits K across workgroups (ks > 1, for activations too large
-// for LDS), fp32 partials for the reduction kernel.
+// for LDS), fp32 partials that the group's last split to arrive adds in place.
 // ---------------------------------------------------------------------------
 
 struct PDecArgs {
@@ -406,6 +406,8 @@ struct PDecArgs {
     const uint8_t* st;      // e8m0 dwords (MXFP4) or fp16 row scales (int4), fragment order
     uint16_t* out;
     float* partials;
+    uint32_t* counters;     // ks > 1: one arrival counter per group
+    int sk_inplace;         // ks > 1: the last split reduces (else the reduction kernel does)
     int M, N, K;
     int s_pad, c_pad;   // padded 128-steps and 4-step chunks per row tile
     int tiles;          // 16-row tiles (ceil(N / 16))
@@ -643,6 +645,41 @@ __device__ __forceinline__ void pdec_act_store(uint8_t* xl, int stride, int per_
     }
 }
 
+// a tile's outputs (ks = 1: bf16 of s_m x acc; K split: fp32 partials, written
+// through to the device's coherence point)
+template <int MT, bool A4, bool FQ>
+__device__ __forceinline__ void pdec_store(const PDecArgs& a, int split, int n0, int lane, const v4f (&acc)[MT],
+                                           const float (&sm_fq)[MT]) {
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + (lane & 15);
+        if (m >= a.M) continue;
+        if (a.ks == 1) {
+            float sm;
+            if constexpr (A4) sm = 1.f;
+            else if constexpr (FQ) sm = sm_fq[mt];
+            else sm = a.xs[m];
+            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            if (vec) {
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[mt][2]) | (f32_to_bf16_rne(sm * acc[mt][3]) << 16);
+                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[mt][r]);
+            }
+        } else if (vec) {
+            sk_put4(sk_rsrc(a.partials), 4u * (uint32_t)(((int64_t)split * a.M + m) * a.N + n0), acc[mt][0],
+                    acc[mt][1], acc[mt][2], acc[mt][3]);
+        } else {
+            float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
+            for (int r = 0; r < 4; ++r)
+                if (n0 + r < a.N) sk_put(p + r, acc[mt][r]);
+        }
+    }
+}
+
 template <int MT, int D, int WF, int AB, bool FQ>
 __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
@@ -754,7 +791,9 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
         }
     }
 
-    // add the K parts of each tile through LDS, in part order
+    // add the K parts of each tile through LDS, in part order (the part-0
+    // wave of a tile writes it)
+    bool writer = true;
     if (a.kw > 1) {
         __syncthreads();   // all waves are done reading activations
         float4* red = reinterpret_cast<float4*>(xl);   // [kw][tw][MT][64 lanes]
@@ -763,53 +802,33 @@ __global__ __launch_bounds__(1024) void pdec_kernel(PDecArgs a) {
             red[((part * a.tw + wave % a.tw) * MT + mt) * 64 + lane] =
                 make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
         __syncthreads();
-        if (part != 0) return;
+        writer = part == 0;
+        if (writer) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float4 tsum = red[((0 * a.tw + wave) * MT + mt) * 64 + lane];
-            for (int q = 1; q < a.kw; ++q) {
-                const float4 v = red[((q * a.tw + wave) * MT + mt) * 64 + lane];
-                tsum.x = tsum.x + v.x;
-                tsum.y = tsum.y + v.y;
-                tsum.z = tsum.z + v.z;
-                tsum.w = tsum.w + v.w;
+            for (int mt = 0; mt < MT; ++mt) {
+                float4 tsum = red[((0 * a.tw + wave) * MT + mt) * 64 + lane];
+                for (int q = 1; q < a.kw; ++q) {
+                    const float4 v = red[((q * a.tw + wave) * MT + mt) * 64 + lane];
+                    tsum.x = tsum.x + v.x;
+                    tsum.y = tsum.y + v.y;
+                    tsum.z = tsum.z + v.z;
+                    tsum.w = tsum.w + v.w;
+                }
+                acc[mt] = v4f{tsum.x, tsum.y, tsum.z, tsum.w};
             }
-            acc[mt] = v4f{tsum.x, tsum.y, tsum.z, tsum.w};
         }
     }
-    if (t >= a.tiles) return;
-
     const int g = lane >> 4;
     const int n0 = 16 * t + 4 * g;
-    if (n0 >= a.N) return;
-    const bool vec = (a.N & 3) == 0;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        if (m >= a.M) continue;
-        if (a.ks == 1) {
-            float sm;
-            if constexpr (A4) sm = 1.f;
-            else if constexpr (FQ) sm = sm_fq[mt];
-            else sm = a.xs[m];
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
-            if (vec) {
-                const uint32_t h0 = f32_to_bf16_rne(sm * acc[mt][0]) | (f32_to_bf16_rne(sm * acc[mt][1]) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * acc[mt][2]) | (f32_to_bf16_rne(sm * acc[mt][3]) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-            } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) o[r] = (uint16_t)f32_to_bf16_rne(sm * acc[mt][r]);
-            }
-        } else {
-            float* p = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-            if (vec) {
-                *reinterpret_cast<float4*>(p) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-            } else {
-                for (int r = 0; r < 4; ++r)
-                    if (n0 + r < a.N) p[r] = acc[mt][r];
-            }
-        }
+    if (writer && t < a.tiles && n0 < a.N) pdec_store<MT, A4, FQ>(a, split, n0, lane, acc, sm_fq);
+    if (a.ks > 1 && a.sk_inplace) {
+        // K split across workgroups: the group's last split to arrive adds the
+        // partials of its columns (the flag word in the activation LDS, which
+        // every wave is done with once the arrival's first barrier passes; a
+        // static LDS word would not fit beside the full 160 KB dynamic range)
+        if (sk_arrive(a.counters + tg, a.ks, reinterpret_cast<uint32_t*>(xl)))
+            sk_reduce(a.partials, A4 ? nullptr : a.xs, a.M, a.N, a.ks, 16 * tg * a.tw,
+                      min(a.N, 16 * (tg + 1) * a.tw), a.out, threadIdx.x, nthreads);
     }
 }
 
@@ -855,7 +874,8 @@ hipError_t launch_pdec_plan(const GemmPlan& p, const PDecArgs& a, size_t lds, hi
 // units ahead of their use, and published by one barrier per unit.  Vector
 // memory loads complete in issue order, so the wait that an activation store
 // needs never holds back the weight loads issued after it.  With few tiles
-// the grid also splits K; fp32 partials then go to the reduction kernel.
+// the grid also splits K; the group's last split to arrive adds the fp32
+// partials in place.
 // ---------------------------------------------------------------------------
 
 struct DtArgs {
@@ -865,6 +885,8 @@ struct DtArgs {
     const uint32_t* st;
     uint16_t* out;
     float* partials;
+    uint32_t* counters;   // ks > 1: one arrival counter per group
+    int sk_inplace;       // ks > 1: the last split reduces (else the reduction kernel does)
     int M, N, K;
     int s_pad, c_pad, tiles;
     int groups;      // workgroups per K split
@@ -1063,15 +1085,22 @@ __global__ __launch_bounds__(64 * W) void dtile_kernel(DtArgs a) {
                     for (int q = 0; q < 4; ++q)
                         if (n0 + q < a.N) o[q] = (uint16_t)f32_to_bf16_rne(sm * acc[r][mt][q]);
                 }
+            } else if (vec) {
+                sk_put4(sk_rsrc(a.partials), 4u * (uint32_t)(((int64_t)split * a.M + m) * a.N + n0), acc[r][mt][0],
+                        acc[r][mt][1], acc[r][mt][2], acc[r][mt][3]);
             } else {
                 float* pp = a.partials + ((int64_t)split * a.M + m) * a.N + n0;
-                if (vec) {
-                    *reinterpret_cast<float4*>(pp) = make_float4(acc[r][mt][0], acc[r][mt][1], acc[r][mt][2], acc[r][mt][3]);
-                } else {
-                    for (int q = 0; q < 4; ++q)
-                        if (n0 + q < a.N) pp[q] = acc[r][mt][q];
-                }
+                for (int q = 0; q < 4; ++q)
+                    if (n0 + q < a.N) sk_put(pp + q, acc[r][mt][q]);
             }
+        }
+    }
+    if (a.ks > 1 && a.sk_inplace) {
+        // K split: the group's last split to arrive adds the partials of its columns
+        __shared__ uint32_t last_flag;
+        if (sk_arrive(a.counters + tg, a.ks, &last_flag)) {
+            const int n_lo = 16 * tg * W * R, n_hi = min(a.N, 16 * (tg + 1) * W * R);
+            sk_reduce(a.partials, a.xs, a.M, a.N, a.ks, n_lo, n_hi, a.out, threadIdx.x, 64 * W);
         }
     }
 }
@@ -3019,9 +3048,19 @@ static PDecArgs pdec_args(const GemmPlan& p, const uint8_t* wt, const uint8_t* s
     a.groups = (int)((p.tiles + p.rt - 1) / p.rt);
     a.ks = p.ks;
     a.c_per = p.s_per;
-    if (p.ks > 1)
+    if (p.ks > 1) {
+        a.counters = reinterpret_cast<uint32_t*>(ws);
         a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+        a.sk_inplace = sk_inplace_fits(p.ks, M, N) ? 1 : 0;
+    }
     return a;
+}
+
+// the K split's partials reduced by a separate kernel where the last split
+// cannot (more splits than it takes in one batch, or offsets past 32 bits)
+static hipError_t pdec_finish(const PDecArgs& a, hipError_t e, const float* xs, hipStream_t stream) {
+    if (e != hipSuccess || a.ks == 1 || a.sk_inplace) return e;
+    return launch_splitk_reduce(a.partials, xs, a.M, a.N, a.ks, a.out, stream);
 }
 
 hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const float* xs,
@@ -3033,8 +3072,7 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
     const size_t lds = prepared_lds_bytes(p, M, false);
     const hipError_t e = int4 ? (zp ? launch_pdec_plan<kWI4Z>(p, a, lds, stream) : launch_pdec_plan<kWI4>(p, a, lds, stream))
                               : launch_pdec_plan<kWMx>(p, a, lds, stream);
-    if (e != hipSuccess || p.ks == 1) return e;
-    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+    return pdec_finish(a, e, xs, stream);
 }
 
 // The fused-quant plan: the decode plan, when K is not split across
@@ -3090,8 +3128,7 @@ hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const u
     a.w5 = reinterpret_cast<const uint32_t*>(w5);
     const size_t lds = prepared_lds_bytes(p, M, false);
     const hipError_t e = launch_pdec_plan<kWI5>(p, a, lds, stream);
-    if (e != hipSuccess || p.ks == 1) return e;
-    return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
+    return pdec_finish(a, e, xs, stream);
 }
 
 // W4A4 decode: the split-K decode kernel on MXFP4 activations (no token
@@ -3106,8 +3143,7 @@ static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const
     a.x8 = x4; a.xe = xe; a.xs = nullptr;
     const size_t lds = prepared_lds_bytes(p, M, true);
     const hipError_t e = launch_pdec_plan<kWMxA4>(p, a, lds, stream);
-    if (e != hipSuccess || p.ks == 1) return e;
-    return launch_splitk_reduce(a.partials, nullptr, M, N, p.ks, out, stream);
+    return pdec_finish(a, e, nullptr, stream);
 }
 
 // The register-streamed tiles of the DTile route: one tile per wave, eight
@@ -3158,7 +3194,11 @@ hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, con
     a.groups = (int)p.groups;
     a.ks = p.ks;
     a.h_per = p.h_per;
-    if (p.ks > 1) a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+    if (p.ks > 1) {
+        a.counters = reinterpret_cast<uint32_t*>(ws);
+        a.partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + ws_counter_bytes(p.tiles));
+        a.sk_inplace = sk_inplace_fits(p.ks, M, N) ? 1 : 0;
+    }
     hipError_t e;
 #define W4A8_DT(MT, R, W) else if (p.mt == MT && p.r == R && p.w == W) e = launch_dtile_inst<MT, R, W>(a, stream);
     if (false) e = hipErrorInvalidValue;
@@ -3171,7 +3211,7 @@ hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, con
     W4A8_DT(4, 2, 8) W4A8_DT(1, 1, 16) W4A8_DT(2, 1, 16) W4A8_DT(3, 1, 16) W4A8_DT(4, 1, 16)
     else return hipErrorInvalidValue;
 #undef W4A8_DT
-    if (e != hipSuccess || p.ks == 1) return e;
+    if (e != hipSuccess || p.ks == 1 || a.sk_inplace) return e;   // else reduced by a second kernel
     return launch_splitk_reduce(a.partials, xs, M, N, p.ks, out, stream);
 }
 

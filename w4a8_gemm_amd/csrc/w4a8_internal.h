@@ -257,10 +257,131 @@ hipError_t launch_int4_gemm(const GemmPlan& p, const uint8_t* x8, const float* x
 hipError_t launch_splitk_reduce(const float* partials, const float* xs, int64_t M, int64_t N,
                                 int ks, uint16_t* out, hipStream_t stream);
 
-// Split-K workspace layout: a 256-byte-aligned header region (one word per row
-// block, reserved), then fp32 partials [ks][M][N].
+// Split-K workspace layout: a 256-byte-aligned header region (one arrival
+// counter per 16-row tile or group of tiles, zero between calls), then fp32
+// partials [ks][M][N].
 inline size_t ws_counter_bytes(int64_t tiles) {
     return (size_t)((tiles * 4 + 255) / 256 * 256);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduced in place by the last split to arrive ("vllm-radiance
+// (MXFP4)", How the MXFP4 path works, The W4A8 fp8-WMMA kernel: the K splits
+// of an output block race on a counter, and the one that arrives last adds
+// the partials, with no second launch).
+//
+// The eight XCDs of an MI355X have L2 caches of their own, and the splits of
+// one block run on any of them.  Partials are therefore written and read with
+// device-scope relaxed atomic accesses: on gfx950 ordinary loads and stores
+// carrying the sc1 bit, which go to the device's coherence point instead of
+// staying in (or being served from) the XCD's L2.  A split waits for its
+// stores to complete (vmcnt(0)) before its workgroup barrier, and one thread
+// then increments the block's counter (a device-scope atomic); the split that
+// reads ks - 1 is the last, resets the counter to zero for the next call and
+// sums the ks partials in split order, so the output is bit-identical to the
+// separate reduction kernel's.  No release or acquire fence is needed (at
+// device scope those write back or invalidate the whole L2), and no split
+// waits for another: the splits that are not last simply end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void sk_put(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float sk_get(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte forms for four consecutive columns: buffer accesses with the same
+// sc1 bit (cache-policy operand 16), addressed by a 32-bit byte offset from
+// the partials' base (the host keeps ks x M x N x 4 below 2^31)
+typedef int32_t sk_i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const float* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void sk_put4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+    const sk_i32x4 v = {__float_as_int(a), __float_as_int(b), __float_as_int(c), __float_as_int(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+}
+__device__ __forceinline__ sk_i32x4 sk_get4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16);
+}
+// Every thread of the workgroup calls it (after its partial stores); true in
+// the last split of the block.  flag: one word of LDS.
+__device__ __forceinline__ bool sk_arrive(uint32_t* counter, int ks, uint32_t* flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)(ks - 1);
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    return *flag != 0u;
+}
+// Host: whether a K split of ks parts over an M x N output reduces in place
+// (partials addressed with 32-bit byte offsets).
+inline bool sk_inplace_fits(int64_t ks, int64_t M, int64_t N) {
+    return ks >= 2 && ks * M * N * 4 < ((int64_t)1 << 31);
+}
+
+// The last split's sum over rows m < M and columns [n_lo, n_hi): out = bf16(s_m
+// x (p_0 + p_1 + ... + p_{ks-1})) in split order (xs null: no token scale).
+// Atomic loads keep their program order, so each thread issues a batch of
+// loads (up to kSkBatch splits of its outputs) before the batch's adds: one
+// memory latency per batch instead of one per partial, in 32 registers.  With
+// N, n_lo and n_hi multiples of 4 the loads are 16 bytes (four columns) each.
+constexpr int kSkBatch = 8;
+__device__ __forceinline__ void sk_reduce(const float* partials, const float* xs, int M, int N, int ks, int n_lo,
+                                          int n_hi, uint16_t* out, int tid, int nthreads) {
+    const int64_t plane = (int64_t)M * N;
+    const int w = n_hi - n_lo;
+    if ((N & 3) == 0 && (n_lo & 3) == 0 && (w & 3) == 0) {
+        const __amdgpu_buffer_rsrc_t r = sk_rsrc(partials);
+        const int w4 = w >> 2, total = M * w4;
+        for (int i = tid; i < total; i += nthreads) {
+            const int m = i / w4;
+            const uint32_t o = (uint32_t)((int64_t)m * N + n_lo + 4 * (i - m * w4));
+            float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
+            for (int j0 = 0; j0 < ks; j0 += kSkBatch) {
+                sk_i32x4 v[kSkBatch];
+#pragma unroll
+                for (int j = 0; j < kSkBatch; ++j)
+                    if (j0 + j < ks) v[j] = sk_get4(r, 4u * (uint32_t)((j0 + j) * plane + o));
+#pragma unroll
+                for (int j = 0; j < kSkBatch; ++j)
+                    if (j0 + j < ks) {
+                        if (j0 + j == 0) {
+                            t0 = __int_as_float(v[j][0]); t1 = __int_as_float(v[j][1]);
+                            t2 = __int_as_float(v[j][2]); t3 = __int_as_float(v[j][3]);
+                        } else {
+                            t0 = t0 + __int_as_float(v[j][0]); t1 = t1 + __int_as_float(v[j][1]);
+                            t2 = t2 + __int_as_float(v[j][2]); t3 = t3 + __int_as_float(v[j][3]);
+                        }
+                    }
+            }
+            const float sm = xs ? xs[m] : 1.0f;
+            const uint32_t h0 = f32_to_bf16_rne(sm * t0) | (f32_to_bf16_rne(sm * t1) << 16);
+            const uint32_t h1 = f32_to_bf16_rne(sm * t2) | (f32_to_bf16_rne(sm * t3) << 16);
+            *reinterpret_cast<uint2*>(out + o) = make_uint2(h0, h1);
+        }
+        return;
+    }
+    const int total = M * w;
+    for (int i = tid; i < total; i += nthreads) {
+        const int m = i / w;
+        const int64_t o = (int64_t)m * N + n_lo + (i - m * w);
+        float t = 0.f;
+        for (int j0 = 0; j0 < ks; j0 += kSkBatch) {
+            float v[kSkBatch];
+#pragma unroll
+            for (int j = 0; j < kSkBatch; ++j)
+                if (j0 + j < ks) v[j] = sk_get(partials + (j0 + j) * plane + o);
+#pragma unroll
+            for (int j = 0; j < kSkBatch; ++j)
+                if (j0 + j < ks) t = j0 + j == 0 ? v[j] : t + v[j];
+        }
+        const float sm = xs ? xs[m] : 1.0f;
+        out[o] = (uint16_t)f32_to_bf16_rne(sm * t);
+    }
 }
 
 }  // namespace w4a8
