@@ -61,11 +61,11 @@ N_GU, K_GU = 34816, 5120
 STEP_KERNELS = {
     1: [("pdec_kernel<1, 3, 0, 4, true>", "split-K decode, per-token quant fused in its prologue")],
     8: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-        ("spread_kernel<1, 2, 8>", "spread tiles: one workgroup per CU over all of K, ring depth 8")],
+        ("spread_kernel<1, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
     16: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("spread_kernel<1, 2, 8>", "spread tiles: one workgroup per CU over all of K, ring depth 8")],
+         ("spread_kernel<1, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
     64: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("spread_kernel<4, 2, 4>", "spread tiles: one workgroup per CU over all of K, ring depth 4")],
+         ("spread_kernel<4, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
 }
 SOURCES = {"gemm": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip"),
            "act_quant": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "act_quant.hip"),

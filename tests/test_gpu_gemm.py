@@ -415,7 +415,8 @@ def test_mxfp4_prepared_register_tiles(M, N, K):
 # spread tiles (wide MXFP4 layers, 2 <= M <= 64): every activation-tile
 # count, ragged N (a partial last tile; N % 4 != 0 takes the scalar stores),
 # padded K steps (K / 128 not a multiple of 4), workgroups of 8 and 9 tiles
-# (1 and 2 per wave), through the default route and with each ring depth
+# (1 and 2 per wave), through the default route and with each ring depth and
+# e8m0 loading
 SPREAD = [(2, 24576, 256), (9, 25001, 640), (16, 24600, 1152), (17, 30000, 512), (33, 24584, 384),
           (48, 26002, 256), (64, 24576, 512), (64, 34816, 5120)]
 
@@ -429,8 +430,9 @@ def test_mxfp4_prepared_spread(M, N, K):
     dx, ds = dev_u8(x8), dev_f32(s)
     got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
     s_pad = 4 * ((K // 128 + 3) // 4)
-    for depth in (4, 8):
-        if depth == 8 and s_pad % 8:
+    # ring depth 4 and 8 with the e8m0 dwords per step, 4 with them per chunk (+100)
+    for depth in (4, 8, 104):
+        if depth in (8, 104) and s_pad % 8:
             with pytest.raises(ValueError):
                 w4.decode_with_plan(dx, ds, pw.w, pw.s, -200, 0, depth, kind="prepared", N=N)
             continue

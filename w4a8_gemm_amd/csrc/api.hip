@@ -247,7 +247,7 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
         return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
     case PreparedRoute::Spread:
-        return hip_status(launch_spread(plan_spread(M, N, K, 0), d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
+        return hip_status(launch_spread(plan_spread(M, N, K, 0, -1), d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
                                         as_stream(stream)));
     case PreparedRoute::DTile: {
         const DtPlan p = plan_dtile_route(M, N, K);
@@ -580,11 +580,16 @@ w4a8_status w4a8_decode_with_plan(w4a8_weight_kind kind, const uint8_t* d_x_fp8,
                                                 d_out, M, N, K, d_ws, as_stream(stream), false, false, ks));
     }
     if (kind == W4A8_WEIGHT_MXFP4_PREPARED && rt == -200) {
-        if (!d_w_scale || !aligned(d_w_scale, 4) || (ks != 0 && ks != 4 && ks != 8)) return W4A8_ERR_INVALID_ARG;
+        // ks = ring depth (0: the entry point's), plus 100 for the e8m0 dwords once per chunk
+        const int depth = ks % 100, cs = ks / 100;
+        if (!d_w_scale || !aligned(d_w_scale, 4) || (depth != 0 && depth != 4 && depth != 8) || cs > 1 ||
+            (cs && depth != 4))
+            return W4A8_ERR_INVALID_ARG;
         // the ring turns in whole trips over the padded steps
-        if (K % 128 != 0 || M > 64 || (ks != 0 && (4 * ((K / 128 + 3) / 4)) % ks != 0))
+        const int64_t s_pad = 4 * ((K / 128 + 3) / 4);
+        if (K % 128 != 0 || M > 64 || (depth != 0 && s_pad % depth != 0) || (cs && s_pad % 8 != 0))
             return W4A8_ERR_UNSUPPORTED_SHAPE;
-        const SpPlan p = plan_spread(M, N, K, ks);
+        const SpPlan p = plan_spread(M, N, K, depth, cs);
         return hip_status(launch_spread(p, d_x_fp8, d_x_scale, (const uint8_t*)d_w, (const uint8_t*)d_w_scale, d_out,
                                         M, N, K, as_stream(stream)));
     }

@@ -1162,10 +1162,14 @@ constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpStage = 64 * 128;
 constexpr int kSpStages = 4;
 
+// CS: the e8m0 dwords loaded once per 4-step chunk into two chunk slots (the
+// next chunk's issued at the chunk start, before that step's weights),
+// instead of with every step's weights
 template <int R, int D>
 struct SpRing {
     dt_u32x4 w[D][R];
     uint32_t s[D][R];
+    uint32_t cs[2][R];
 };
 
 template <int MT>
@@ -1195,20 +1199,27 @@ __device__ __forceinline__ dt_u32x4 sp_act(const SpSrc<R>& q, int j) {
     return *reinterpret_cast<const dt_u32x4*>(q.xrow + 128 * (int64_t)min(j, q.x_last));
 }
 
-template <int R, int D>
+template <int R, int D, bool CS>
 __device__ __forceinline__ void sp_wload(const SpSrc<R>& q, int j, SpRing<R, D>& ring, int slot) {
     j = min(j, q.w_last);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint4 v = load_stream16(q.wp[r] + (int64_t)j * 64);
         ring.w[slot][r] = dt_u32x4{v.x, v.y, v.z, v.w};
-        ring.s[slot][r] = q.sp[r][(j >> 2) * 64];
+        if constexpr (!CS) ring.s[slot][r] = q.sp[r][(j >> 2) * 64];
     }
 }
+// chunk c's e8m0 dwords (clamped to the last chunk) into chunk slot `slot`
+template <int R, int D>
+__device__ __forceinline__ void sp_csload(const SpSrc<R>& q, int c, SpRing<R, D>& ring, int slot) {
+    c = min(c, q.w_last >> 2);
+#pragma unroll
+    for (int r = 0; r < R; ++r) ring.cs[slot][r] = q.sp[r][c * 64];
+}
 
-// one step of the main loop; J = s mod D (ring and activation slots, stage
-// and fragment set are compile-time)
-template <int MT, int R, int D, int J>
+// one step of the main loop; J = s mod the trip length (ring and activation
+// slots, stage, fragment set and chunk slot are compile-time)
+template <int MT, int R, int D, bool CS, int J>
 __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     dt_barrier();
@@ -1221,7 +1232,7 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
     for (int r = 0; r < R; ++r) {
         const dt_u32x4 w = ring.w[J % D][r];
         const v8i af = frag_fp4(make_uint4(w[0], w[1], w[2], w[3]));
-        const int sc = (int)(ring.s[J % D][r] >> (8 * (J & 3)));
+        const int sc = (int)((CS ? ring.cs[(J / 4) % 2][r] : ring.s[J % D][r]) >> (8 * (J & 3)));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if constexpr ((J & 1) == 0) acc[r][mt] = mfma16<0>(af, F0[mt], acc[r][mt], sc);
@@ -1229,20 +1240,23 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    sp_wload<R, D>(q, s + D, ring, J % D);
+    if constexpr (CS && J % 4 == 0) sp_csload<R, D>(q, s / 4 + 1, ring, (J / 4 + 1) % 2);
+    sp_wload<R, D, CS>(q, s + D, ring, J % D);
 }
 
-template <int MT, int R, int D, int J>
+// the trip: D steps (per-step e8m0), or 8 with chunk slots (two chunks)
+template <int D, bool CS> constexpr int kSpTrip = CS ? 8 : D;
+template <int MT, int R, int D, bool CS, int J>
 __device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
-    if constexpr (J < D) {
-        sp_step<MT, R, D, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
-        sp_trip<MT, R, D, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
+    if constexpr (J < kSpTrip<D, CS>) {
+        sp_step<MT, R, D, CS, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
+        sp_trip<MT, R, D, CS, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
     }
 }
 
 // a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x sum
-template <int MT, int R, int D>
+template <int MT, int R, int D, bool CS>
 __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;
@@ -1270,18 +1284,19 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     // prologue = iterations -D-1 .. -1 without products: activation items of
     // steps 0 .. D, weights of steps 0 .. D - 1, steps 0 and 1 stored, step
     // 0's fragments read
+    if constexpr (CS) sp_csload<R, D>(q, 0, ring, 0);
     av[0] = sp_act(q, 0);
 #pragma unroll
     for (int k = 0; k < D; ++k) {
         av[(k + 1) % D] = sp_act(q, k + 1);
         if (k == D - 2) *reinterpret_cast<dt_u32x4*>(lds + q.xdst) = av[0];
-        sp_wload<R, D>(q, k, ring, k);
+        sp_wload<R, D, CS>(q, k, ring, k);
     }
     dt_barrier();
     sp_read<MT>(lds, lane, F0);
     *reinterpret_cast<dt_u32x4*>(lds + kSpStage + q.xdst) = av[1];
 
-    for (int s = 0; s < a.s_pad; s += D) sp_trip<MT, R, D, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>) sp_trip<MT, R, D, CS, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
 
     const bool vec = (a.N & 3) == 0;
 #pragma unroll
@@ -1306,9 +1321,11 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     }
 }
 
-template <int MT, int R, int D>
+template <int MT, int R, int D, bool CS>
 __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     static_assert(D == 4 || D == 8, "a trip is one turn of the ring and whole 4-step chunks");
+    static_assert(!CS || D == 4, "chunk slots one chunk ahead: the ring may be at most 4 steps deep (deeper, the "
+                                 "wait for a chunk's dwords would drain weights of later steps)");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform: scalar branches
@@ -1318,16 +1335,16 @@ __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            sp_run<MT, R - 1, D>(a, lds, w0, lane);
+            sp_run<MT, R - 1, D, CS>(a, lds, w0, lane);
             return;
         }
     }
-    sp_run<MT, R, D>(a, lds, w0, lane);
+    sp_run<MT, R, D, CS>(a, lds, w0, lane);
 }
 
-template <int MT, int R, int D>
+template <int MT, int R, int D, bool CS>
 hipError_t launch_spread_inst(const SpArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((spread_kernel<MT, R, D>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
+    hipLaunchKernelGGL((spread_kernel<MT, R, D, CS>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -3230,15 +3247,18 @@ static int device_cus() {
 }
 
 // Spread tiles: one workgroup per CU (at most tiles / 8, so that every wave
-// has a tile); R = the most tiles a wave gets; ring depth 8 steps for one
-// activation tile where the padded steps allow (measured on gate_up M = 1 ..
-// 16: 17.4 - 18.1 us against 18.1 - 19.5 us at depth 4), else 4 (two to four
-// activation tiles: depth 8 was no faster).
-SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D) {
+// has a tile); R = the most tiles a wave gets; ring depth D and the e8m0
+// dwords per step or per chunk (CS) as below.
+SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS) {
     SpPlan p{};
     p.mt = (int)((M + 15) / 16);
     const int64_t s_pad = 4 * ((K / 128 + 3) / 4);
-    p.d = D > 0 ? D : (p.mt == 1 && s_pad % 8 == 0 ? 8 : 4);
+    // default: ring depth 4 with the e8m0 dwords once per chunk where the
+    // padded steps are a multiple of 8 (gate_up M = 1 / 8 / 16 / 64: 17.2 /
+    // 17.5 / 17.8 / 24.1 us, against 17.4 / 17.7 / 18.2 / 24.3 us with the
+    // dwords loaded every step at depth 8 / 8 / 8 / 4)
+    p.d = D > 0 ? D : 4;
+    p.cs = CS >= 0 ? CS : (p.d == 4 && s_pad % 8 == 0 ? 1 : 0);
     p.tiles = (N + 15) / 16;
     int64_t g = device_cus();
     if (g > p.tiles / kSpWaves) g = p.tiles / kSpWaves;
@@ -3249,7 +3269,7 @@ SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D) {
 
 bool spread_fits(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > 64 || K % 128 != 0) return false;
-    const SpPlan p = plan_spread(M, N, K, 0);
+    const SpPlan p = plan_spread(M, N, K, 0, -1);
     // most CUs busy, and an instantiated tile count
     return p.groups * 4 >= (int64_t)device_cus() * 3 && p.r >= 1 && p.r <= 2;
 }
@@ -3271,12 +3291,15 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     a.steps = (int)(K / 128);
     a.tiles = (int)p.tiles;
     a.groups = (int)p.groups;
-    if (a.s_pad % p.d != 0) return hipErrorInvalidValue;
-#define W4A8_SP(MT, R, D) else if (p.mt == MT && p.r == R && p.d == D) return launch_spread_inst<MT, R, D>(a, stream);
+    if (a.s_pad % p.d != 0 || (p.cs && (p.d != 4 || a.s_pad % 8 != 0))) return hipErrorInvalidValue;
+#define W4A8_SP(MT, R, D, CS) \
+    else if (p.mt == MT && p.r == R && p.d == D && p.cs == CS) return launch_spread_inst<MT, R, D, CS>(a, stream);
     if (false) {}
-    W4A8_SP(1, 1, 4) W4A8_SP(2, 1, 4) W4A8_SP(3, 1, 4) W4A8_SP(4, 1, 4)
-    W4A8_SP(1, 2, 4) W4A8_SP(2, 2, 4) W4A8_SP(3, 2, 4) W4A8_SP(4, 2, 4)
-    W4A8_SP(1, 1, 8) W4A8_SP(1, 2, 8) W4A8_SP(2, 2, 8) W4A8_SP(3, 2, 8) W4A8_SP(4, 2, 8)
+    W4A8_SP(1, 1, 4, 0) W4A8_SP(2, 1, 4, 0) W4A8_SP(3, 1, 4, 0) W4A8_SP(4, 1, 4, 0)
+    W4A8_SP(1, 2, 4, 0) W4A8_SP(2, 2, 4, 0) W4A8_SP(3, 2, 4, 0) W4A8_SP(4, 2, 4, 0)
+    W4A8_SP(1, 1, 4, 1) W4A8_SP(2, 1, 4, 1) W4A8_SP(3, 1, 4, 1) W4A8_SP(4, 1, 4, 1)
+    W4A8_SP(1, 2, 4, 1) W4A8_SP(2, 2, 4, 1) W4A8_SP(3, 2, 4, 1) W4A8_SP(4, 2, 4, 1)
+    W4A8_SP(1, 1, 8, 0) W4A8_SP(1, 2, 8, 0) W4A8_SP(2, 2, 8, 0) W4A8_SP(3, 2, 8, 0) W4A8_SP(4, 2, 8, 0)
 #undef W4A8_SP
     return hipErrorInvalidValue;
 }

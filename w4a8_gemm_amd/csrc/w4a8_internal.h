@@ -234,10 +234,10 @@ hipError_t launch_dtile(const DtPlan& p, const uint8_t* x8, const float* xs, con
 // R per wave), all of K per workgroup; D = weight ring depth in steps (0:
 // the default for the shape).
 struct SpPlan {
-    int mt, r, d;
+    int mt, r, d, cs;     // cs: e8m0 dwords once per 4-step chunk (ring depth 4, padded steps a multiple of 8)
     int64_t tiles, groups;
 };
-SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D);
+SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS);
 bool spread_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
