@@ -230,11 +230,11 @@ w4a8_status w4a8_mxfp4_gemm(
  *   w4a8_mxfp4_prepare: d_w_packed [N, K/2], d_w_e8m0 [N, K/32] -> d_w_prepared,
  *     d_s_prepared (caller-allocated, sizes above; 16- and 4-byte aligned).
  *   w4a8_mxfp4_gemm_prepared: as w4a8_mxfp4_gemm on prepared weights, any
- *     M >= 1.  Small M runs the split-K decode kernel (M = 1 and M <= 8 on
- *     narrow layers: fewer than 64 column tiles of 256), narrow layers at
- *     9 <= M <= 40 the register-streamed tiles, wide layers (at least 1536
- *     16-row tiles on 256 CUs, at most 16 per CU) at 2 <= M <= 64 the spread
- *     tiles (one workgroup per CU, all of K, no workspace); larger M the tiled
+ *     M >= 1.  Small M on narrow layers (fewer than 64 column tiles of 256)
+ *     runs the split-K decode kernel to M = 8 and the register-streamed tiles
+ *     for 9 <= M <= 40; wide layers (at least 1536 16-row tiles on 256 CUs, at
+ *     most 16 per CU) at M <= 64 the spread tiles (one workgroup per CU, all
+ *     of K, no workspace); larger M the tiled
  *     kernel (64/128/256 x 128/256 output tiles), which splits K across
  *     workgroups when it has fewer than 128 tiles (fp32 partials in the
  *     workspace, then a reduction kernel).  A workspace sized

@@ -321,7 +321,12 @@ static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const 
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     GemmPlan p{};
     const bool vec = aligned(d_x_bf16, 16) && ldx % 8 == 0;
-    if (vec && prepared_route(M, N, K, int4) == PreparedRoute::Decode && plan_prepared_fused(M, N, K, int4, &p))
+    // the quantization fused into the split-K decode kernel where its plan
+    // allows, also for one row on wide layers whose GEMM alone takes the spread
+    // tiles (gate_up M = 1: 19.1 us fused against 20.4 us for quant kernel + spread)
+    const PreparedRoute route = prepared_route(M, N, K, int4);
+    if (vec && (route == PreparedRoute::Decode || (route == PreparedRoute::Spread && M == 1)) &&
+        plan_prepared_fused(M, N, K, int4, &p))
         return hip_status(launch_prepared_linear_fused(p, d_x_bf16, ldx, d_w, d_s, d_out, M, N, K, d_x_fp8,
                                                        d_x_scale, as_stream(stream), int4));
     st = hip_status(launch_act_quant(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, as_stream(stream)));

@@ -1240,8 +1240,8 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (CS && J % 4 == 0) sp_csload<R, D>(q, s / 4 + 1, ring, (J / 4 + 1) % 2);
     sp_wload<R, D, CS>(q, s + D, ring, J % D);
+    if constexpr (CS && J % 4 == 0) sp_csload<R, D>(q, s / 4 + 1, ring, (J / 4 + 1) % 2);
 }
 
 // the trip: D steps (per-step e8m0), or 8 with chunk slots (two chunks)
@@ -1284,7 +1284,13 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     // prologue = iterations -D-1 .. -1 without products: activation items of
     // steps 0 .. D, weights of steps 0 .. D - 1, steps 0 and 1 stored, step
     // 0's fragments read
-    if constexpr (CS) sp_csload<R, D>(q, 0, ring, 0);
+    if constexpr (CS) {
+        // first, and pinned there: the loop's wait for a chunk slot also covers
+        // the entry from here, and a load the scheduler sank to the end of the
+        // prologue would make that wait drain every load in flight on every trip
+        sp_csload<R, D>(q, 0, ring, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     av[0] = sp_act(q, 0);
 #pragma unroll
     for (int k = 0; k < D; ++k) {
@@ -3027,11 +3033,11 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // split (down_proj M = 16 / 32: 15.5 / 21.0 us with the split-K decode
     // kernel or the tiled kernel, 14.3 / 16.3 us with them)
     if (narrow && !int4 && M > 8 && M <= 40) return PreparedRoute::DTile;
-    // wide MXFP4 layers from 2 to 64 rows: the spread tiles, one workgroup per
-    // CU over all of K (gate_up M = 8 / 16 / 32 / 64: 17.7 / 18.1 / 19.5 /
-    // 24 us against 18.1 / 20.7 / 26 / 28.9 us with the split-K decode or the
-    // tiled kernel)
-    if (!int4 && M >= 2 && spread_fits(M, N, K)) return PreparedRoute::Spread;
+    // wide MXFP4 layers up to 64 rows: the spread tiles, one workgroup per CU
+    // over all of K (gate_up M = 1 / 8 / 16 / 32 / 64: 16.7 / 17.1 / 17.4 /
+    // 19.5 / 22.8 us against 17.0 / 18.1 / 20.7 / 26 / 28.9 us with the
+    // split-K decode or the tiled kernel)
+    if (!int4 && spread_fits(M, N, K)) return PreparedRoute::Spread;
     if (wide_sixteen(M, N, K, false, int4)) return PreparedRoute::Decode;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
@@ -3254,8 +3260,8 @@ SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS) {
     p.mt = (int)((M + 15) / 16);
     const int64_t s_pad = 4 * ((K / 128 + 3) / 4);
     // default: ring depth 4 with the e8m0 dwords once per chunk where the
-    // padded steps are a multiple of 8 (gate_up M = 1 / 8 / 16 / 64: 17.2 /
-    // 17.5 / 17.8 / 24.1 us, against 17.4 / 17.7 / 18.2 / 24.3 us with the
+    // padded steps are a multiple of 8 (gate_up M = 1 / 8 / 16 / 64: 16.7 /
+    // 17.1 / 17.4 / 22.8 us, against 17.4 / 17.7 / 18.2 / 24.4 us with the
     // dwords loaded every step at depth 8 / 8 / 8 / 4)
     p.d = D > 0 ? D : 4;
     p.cs = CS >= 0 ? CS : (p.d == 4 && s_pad % 8 == 0 ? 1 : 0);
