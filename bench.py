@@ -14,6 +14,9 @@ copies of the weight out of eight (95 MB each, 758 MB in all, three times the
 256 MB Infinity Cache; step s uses copies 4s .. 4s + 3 mod 8), so every weight
 byte of a step comes from HBM.  Each step is one HIP graph replay (one graph
 per pair of copy sets), so host launch latency is not in the timed region.
+Every timed region starts at the sustained shader clock: untimed replays for
+0.3 s before the W warm-up steps, and for 50 ms before each per-launch timing
+below (the clock ramps up over tens of milliseconds of load).
 
 value = algorithmic HBM bytes of the step / step time (GB/s): per M the MXFP4
 weight (codes + e8m0) plus bf16 activations read, e4m3 activations written and
@@ -72,6 +75,8 @@ SOURCES = {"gemm": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hi
            "requant": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "requant.hip")}
 PROFILES = os.path.join(HERE, "profiles")
 CALIB_BYTES = 1 << 30           # plain device-to-device copy used to scale the HBM counters
+PREWARM_S = 0.3                 # untimed step replays before the warm-up steps (sustained clock)
+STEADY_S = 0.05                 # untimed replays before each per-launch timing
 SIMDS = 256 * 4                 # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8
 
@@ -168,11 +173,25 @@ def graph_of(torch, fn):
     return g
 
 
+def steady(torch, fn, seconds):
+    """Untimed: call `fn` (at least once) until `seconds` of wall time have
+    passed.  The shader clock ramps up over tens of milliseconds of sustained
+    load (the gate_up prefill graph: 670 us per launch after one replay, 560 us
+    after 50 ms), so every timed region starts from the sustained clock."""
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def _timed_graph(torch, timer, calls, reps):
     """Average duration of one call: `calls` is a list of closures replayed as
-    one graph; the graph is replayed `reps` times after one untimed replay."""
+    one graph; the graph is replayed `reps` times after untimed replays for
+    STEADY_S of wall time."""
     gg = graph_of(torch, lambda: [c() for c in calls])
-    gg.replay()
+    steady(torch, gg.replay, STEADY_S)
     return timer(lambda i: gg.replay(), reps) / len(calls)
 
 
@@ -261,6 +280,13 @@ def main():
     step_bytes = sum(decode_bytes(M, N, K) for M in DECODE_MS)
 
     # ---------------- headline: K steps ----------------
+    # sustained clock first (untimed replays for PREWARM_S), then W warm-up steps
+    ctr = [0]
+
+    def one_step():
+        graphs[ctr[0] % COPIES].replay()
+        ctr[0] += 1
+    steady(torch, one_step, PREWARM_S)
     for i in range(args.warmup):
         graphs[i % COPIES].replay()
     torch.cuda.synchronize()
@@ -603,16 +629,20 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
     flops = 2.0 * M * N * K
     dt = _timed_graph(torch, timer, [lambda r=r: w4.mxfp4_gemm_prepared(x8, xs, pcopies[r], out=o) for r in range(4)], 5)
     mf = read_record(os.path.join(PROFILES, "pf_kernel_prefill_M4096_mfma.md"), ["mfma_busy_frac"], SOURCES["gemm"])
-    res["prefill_gemm"] = {"M": M, "N": N, "K": K, "kernel": "pf_kernel<256, 256, 3, 0>", "us": round(dt * 1e6, 2),
+    res["prefill_gemm"] = {"M": M, "N": N, "K": K, "us": round(dt * 1e6, 2),
+                           "kernel": "pf_kernel<256, 256, 3, 0> on the first 32768 columns (8 whole rounds), then "
+                                     "pf_kernel<256, 128, 3, 0> on the last 2048 (one round)",
                            "tflops": round(flops / dt / 1e12, 1),
                            "frac_of_fp8_peak": round(flops / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
                            "mfma_busy_frac": mf["mfma_busy_frac"] if mf else None}
     log("prefill", res["prefill_gemm"])
+    steady(torch, lambda: w4.quant_act_fp8_per_token(xb, out=x8, scale=xs), STEADY_S)
     aq = timer(lambda i: w4.quant_act_fp8_per_token(xb, out=x8, scale=xs), 5)
     res["act_quant_prefill"] = {"M": M, "K": K, "us": round(aq * 1e6, 2),
                                 "gbps": round(act_quant_bytes(M, K) / aq / 1e9, 1)}
     # W4A4 (MXFP4 activations, OCP rule) on the same prepared weights
     xa4, xe4 = w4.quant_act_mxfp4(xb)
+    steady(torch, lambda: w4.quant_act_mxfp4(xb), STEADY_S)
     aq4 = timer(lambda i: w4.quant_act_mxfp4(xb), 5)
     dt4 = _timed_graph(torch, timer, [lambda r=r: w4.w4a4_gemm_prepared(xa4, xe4, pcopies[r], out=o) for r in range(4)], 5)
     res["w4a4"] = {"prefill_M4096": {"us": round(dt4 * 1e6, 2), "tflops": round(flops / dt4 / 1e12, 1),
@@ -663,6 +693,7 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
                 w4.requant_nvfp4_to_mxfp4(p, s, g["part_rows"], g["part_divisor"], mode=mode,
                                           row_chunk=chunk, out_packed=op, out_e8m0=oe)
             rg = [graph_of(torch, lambda i=i: run(i)) for i in range(2)]
+            steady(torch, lambda: [r.replay() for r in rg], STEADY_S)
             dt = timer(lambda i: rg[i % 2].replay(), 6)
             ent = {"us": round(dt * 1e6, 1), "gbps": round(requant_bytes(N, K) / dt / 1e9, 1),
                    "frac_of_hbm": round(requant_bytes(N, K) / dt / 1e9 / HBM_PEAK_GBS, 4)}
@@ -696,6 +727,7 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
         for name, run, nbytes in (("bf16", run_b, N * K * 2 + N * K // 2 + N * K // 32),
                                   ("fp8ch", run_f, N * K + 4 * N + N * K // 2 + N * K // 32)):
             rg = [graph_of(torch, lambda i=i, run=run: run(i)) for i in range(2)]
+            steady(torch, lambda: [r.replay() for r in rg], STEADY_S)
             dt = timer(lambda i: rg[i % 2].replay(), 6)
             lq[f"{name}_{mode}"] = {"us": round(dt * 1e6, 1), "gbps": round(nbytes / dt / 1e9, 1)}
     res["load_quant_full_layer"] = lq

@@ -237,7 +237,10 @@ w4a8_status w4a8_mxfp4_gemm(
  *     of K, no workspace); larger M the tiled
  *     kernel (64/128/256 x 128/256 output tiles), which splits K across
  *     workgroups when it has fewer than 128 tiles (fp32 partials in the
- *     workspace, then a reduction kernel).  A workspace sized
+ *     workspace, then a reduction kernel); 256 x 256 tiles that fill four or
+ *     more whole rounds of workgroups but leave a part round run in two
+ *     launches, the leading columns in whole rounds and the rest on
+ *     narrower tiles (the same value per output).  A workspace sized
  *     with W4A8_WEIGHT_MXFP4_PREPARED for the largest M covers every case
  *     (many tiles need none).  Above the split-K decode kernel's range K must
  *     be < 2^24 (UNSUPPORTED_SHAPE): those kernels address a 256-row

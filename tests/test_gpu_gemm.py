@@ -463,6 +463,31 @@ def test_mxfp4_prepared_wide_sixteen(M, N, K):
     assert_gemm_close(got[mi, ni], oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni), (M, N, K))
 
 
+# 256 x 256 tiles whose count leaves the last round part-empty: the leading
+# columns on whole rounds, the tail columns on narrower tiles in a second
+# launch (128 x 128 at M = 2048; 256 x 128 at M = 4096, here with ragged M and
+# a ragged N that takes the scalar stores).  Every output is still one tile's
+# full-K sum in step order: bit-identical to the single launch (the explicit
+# tiled plan, which never splits the columns), and checked on a sample
+# against the oracle.
+@pytest.mark.parametrize("M,N,K", [(2048, 34816, 256), (4000, 34810, 384)])
+def test_mxfp4_prepared_tail_columns(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 12))
+    x8, s = _acts(M, K, (M, K, 12), spread=10.0)
+    say("prepared tiled tail columns", (M, N, K))
+    pw = w4.mxfp4_prepare(dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"]))
+    dx, ds = dev_u8(x8), dev_f32(s)
+    got = host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw))
+    whole = host_bf16_as_f64(w4.decode_with_plan(dx, ds, pw.w, pw.s, -100, 0, 1, kind="prepared", N=N))
+    assert np.array_equal(got, whole)
+    mi, ni = _sample_idx(M, N, 8192, M + N)
+    # the tail columns in every sample
+    mi = np.concatenate([mi, np.arange(M)[:: max(1, M // 512)]])
+    ni = np.concatenate([ni, N - 1 - np.arange(len(mi) - len(ni)) % 2048])
+    ref = oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni)
+    assert_gemm_close(got[mi, ni], ref, (M, N, K))
+
+
 # narrow layers at 41 <= M <= 64: 64-row tiles 128 wide, K split across
 # workgroups (fp32 partials + reduction) when long
 @pytest.mark.parametrize("M,N,K", [(33, 16, 1152), (64, 200, 1024), (40, 2000, 2048), (48, 1000, 4096),

@@ -1390,6 +1390,7 @@ struct PfArgs {
     const uint8_t* st;
     uint16_t* out;
     int M, N, K;
+    int ldo;                    // output row stride (N, or the whole layer's width for a column range)
     int s_pad, c_pad, tiles16;
     int tiles_m, tiles_n;
     int group_m;                // M tiles per group of the tile order
@@ -1940,7 +1941,7 @@ __device__ __forceinline__ void pf_epilogue(const PfArgs& a, int tm, int tn, int
         for (int f = 0; f < S::FN; ++f) {
             const int n0 = tn * BN + (wn * S::FN + f) * 16 + 4 * g;
             if (n0 >= a.N) continue;
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            uint16_t* o = a.out + (int64_t)m * a.ldo + n0;
             if (vec) {
                 const uint32_t h0 = f32_to_bf16_rne(sm * acc[f][h][0]) | (f32_to_bf16_rne(sm * acc[f][h][1]) << 16);
                 const uint32_t h1 = f32_to_bf16_rne(sm * acc[f][h][2]) | (f32_to_bf16_rne(sm * acc[f][h][3]) << 16);
@@ -2859,6 +2860,7 @@ hipError_t launch_prepared_tiled_i5(const uint8_t* x8, const float* xs, const ui
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.w5 = reinterpret_cast<const uint32_t*>(w5);
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.ldo = (int)N;
     a.c_pad = (int)((K / 128 + 3) / 4);
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
@@ -2892,12 +2894,56 @@ size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4, int for
     return ws_counter_bytes((N + 15) / 16) + (size_t)t.ks * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// Tail columns of the 256 x 256 MXFP4 tiles: when their count leaves the
+// last round of workgroups part-empty, the leading columns that make whole
+// rounds (four or more) keep the 256 x 256 tiles and the rest take narrower
+// tiles in one round of their own (every output is still one tile's full-K
+// sum, in the same step order).  gate_up M = 4096: 2176 tiles = 8.5 rounds
+// on 256 CUs -> 32768 columns in 8 rounds, then 2048 columns as 256 tiles of
+// 256 x 128 (567.5 -> 554.8 us, weights streamed from HBM); M = 2048: 1088
+// tiles -> 4 rounds, then 256 tiles of 128 x 128 (313.0 -> 289.7 us).  With
+// a single whole round (down_proj M = 4096, 320 tiles -> 256 + 256 tiles of
+// 128 x 128) it lost 9 %: the short last round of the single launch runs on
+// a quarter of the CUs at a higher clock, and the narrow tiles' copy feed per
+// product is twice that of the wide ones.
+static int device_cus();
+struct PfTail {
+    int64_t n_main;   // leading columns on 256 x 256 tiles (a multiple of 256)
+    int bm, bn;       // the tail's tile
+};
+static bool pf_tail(const TiledShape& t, int64_t M, int64_t N, PfTail* r) {
+    const int64_t cus = device_cus();
+    const int64_t tiles = (int64_t)t.tiles_m * t.tiles_n;
+    if (t.bm != 256 || t.bn != 256 || t.ks != 1 || tiles < cus || tiles % cus == 0) return false;
+    int64_t g = t.tiles_m, h = cus;   // gcd: the 256-wide column tiles per whole-round block
+    while (h) {
+        const int64_t q = g % h;
+        g = h;
+        h = q;
+    }
+    const int64_t per = cus / g, n_tiles = (N / 256) / per * per;
+    if (n_tiles == 0 || n_tiles * 256 >= N || t.tiles_m * n_tiles < 4 * cus) return false;
+    const int64_t tail = N - n_tiles * 256;
+    r->n_main = n_tiles * 256;
+    if (((M + 127) / 128) * ((tail + 127) / 128) <= cus) {
+        r->bm = 128;
+        r->bn = 128;
+    } else if (((M + 255) / 256) * ((tail + 127) / 128) <= cus) {
+        r->bm = 256;
+        r->bn = 128;
+    } else {
+        return false;
+    }
+    return true;
+}
+
 hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8_t* wt,
                                  const uint8_t* st, uint16_t* out, int64_t M, int64_t N, int64_t K,
                                  void* ws, hipStream_t stream, bool int4, bool zp, int force_ks) {
     PfArgs a{};
     a.x8 = x8; a.xs = xs; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.ldo = (int)N;
     a.c_pad = (int)((K / 128 + 3) / 4);
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
@@ -2931,6 +2977,28 @@ hipError_t launch_prepared_tiled(const uint8_t* x8, const float* xs, const uint8
         else if (bm == 256 && bn == 256) e = launch_pf<256, 256, 3, kWI4>(a, stream);
         else return hipErrorInvalidValue;
     } else {
+        PfTail tl{};
+        if (force_ks == 0 && pf_tail(t, M, N, &tl)) {
+            // the leading columns on whole rounds of 256 x 256 tiles
+            PfArgs m = a;
+            m.N = (int)tl.n_main;
+            m.tiles16 = (int)(tl.n_main / 16);
+            m.tiles_n = (int)(tl.n_main / 256);
+            e = launch_pf<256, 256, 3, kWMx>(m, stream);
+            if (e != hipSuccess) return e;
+            // the tail columns: weights, scales and outputs from column n_main on
+            PfArgs r = a;
+            const int64_t t0 = tl.n_main / 16;
+            r.wt = wt + t0 * (int64_t)a.s_pad * 1024;
+            r.st = st + t0 * (int64_t)a.c_pad * 256;
+            r.out = out + tl.n_main;
+            r.N = (int)(N - tl.n_main);
+            r.tiles16 = (int)((r.N + 15) / 16);
+            r.tiles_m = (int)((M + tl.bm - 1) / tl.bm);
+            r.tiles_n = (int)((r.N + tl.bn - 1) / tl.bn);
+            if (tl.bm == 128) return launch_pfp<128, 128, 4, kWMx>(r, stream);
+            return launch_pf<256, 128, 3, kWMx>(r, stream);
+        }
         if (bm == 64 && bn == 256) e = launch_pfp<64, 256, 5, kWMx>(a, stream);
         else if (bm == 64 && bn == 128) e = launch_pfp<64, 128, 4, kWMx>(a, stream);
         else if (bm == 128 && bn == 128) e = launch_pfp<128, 128, 4, kWMx>(a, stream);
@@ -3003,6 +3071,7 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
     PfArgs a{};
     a.x8 = x4; a.xe = xe; a.xs = nullptr; a.wt = wt; a.st = st; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.ldo = (int)N;
     a.c_pad = (int)((K / 128 + 3) / 4);
     a.s_pad = 4 * a.c_pad;
     a.tiles16 = (int)((N + 15) / 16);
