@@ -206,9 +206,12 @@ w4a8_status w4a8_workspace_init(void *d_ws, size_t bytes, void *stream);
  *   d_ws, ws_bytes   workspace of at least w4a8_gemm_workspace_bytes(M, N, K,
  *                    W4A8_WEIGHT_MXFP4) bytes, initialized once; may be NULL/0
  *                    when that is 0.
- * Band: M <= 64 runs the decode kernels (weights streamed from HBM, split K),
- * larger M the LDS-tiled prefill kernel.  Errors: INVALID_ARG,
- * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+ * Band: M <= 64 on wide layers (at least 1536 16-row tiles, at most 16 per
+ * CU) with K a multiple of 1024 and d_w_e8m0 16-byte aligned runs the spread
+ * tiles of w4a8_mxfp4_gemm_prepared on this layout directly (no workspace;
+ * value identical to the prepared path); other M <= 64 the decode kernels
+ * (weights streamed from HBM, split K), larger M the LDS-tiled prefill kernel.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const uint8_t *d_w_packed, const uint8_t *d_w_e8m0, uint16_t *d_out,

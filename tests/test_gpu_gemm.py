@@ -128,6 +128,25 @@ def test_mxfp4_down_proj_decode(M):
     _mx_full_size(f"down_proj M={M}", ("down_proj", M), x8, s, d["w_packed"], d["w_e8m0"])
 
 
+# the plain layout on wide layers at decode M: the spread tiles read [N, K/2]
+# codes and [N, K/32] e8m0 in place (K steps a multiple of 8): the same
+# products in the same order as on fragment-order weights, so bit-identical
+# to the prepared entry point; every activation-tile count, a ragged N (a
+# partial last tile, scalar stores), workgroups of 8 and 9 tiles
+@pytest.mark.parametrize("M,N,K", [(1, 34816, 5120), (8, 25001, 1024), (17, 30000, 2048), (33, 24584, 1024),
+                                   (64, 24576, 1024)])
+def test_mxfp4_plain_layout_spread(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 13))
+    x8, s = _acts(M, K, (M, K, 13), spread=10.0)
+    say("plain-layout spread tiles", (M, N, K))
+    dx, ds, dw, de = dev_u8(x8), dev_f32(s), dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"])
+    got = host_bf16_as_f64(w4.mxfp4_gemm(dx, ds, dw, de))
+    pw = w4.mxfp4_prepare(dw, de)
+    assert np.array_equal(got, host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw)))
+    mi, ni = _sample_idx(M, N, 8192, M + N)
+    assert_gemm_close(got[mi, ni], oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni), (M, N, K))
+
+
 def test_mxfp4_prefill_full_size(gate_up_mx):
     x8, s = _acts(4096, synth.HIDDEN, 3)
     _mx_sampled("prefill 4096", x8, s, *gate_up_mx[:2], n_samples=16384, reps=1)

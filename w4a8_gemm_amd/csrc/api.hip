@@ -205,6 +205,10 @@ w4a8_status w4a8_mxfp4_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (st != W4A8_OK) return st;
     if (!d_w_e8m0 || !aligned(d_w_e8m0, 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 32 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    // wide layers at decode M: the spread tiles read this layout directly (no workspace)
+    if (spread_plain_fits(M, N, K) && aligned(d_w_e8m0, 16))
+        return hip_status(launch_spread(plan_spread(M, N, K, 0, -1), d_x_fp8, d_x_scale, d_w_packed, d_w_e8m0, d_out,
+                                        M, N, K, as_stream(stream), true));
     const GemmPlan p = plan_mxfp4(M, N, K);
     st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
     if (st != W4A8_OK) return st;

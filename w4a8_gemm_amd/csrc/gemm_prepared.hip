@@ -1170,6 +1170,9 @@ struct SpRing {
     dt_u32x4 w[D][R];
     uint32_t s[D][R];
     uint32_t cs[2][R];
+    dt_u32x4 cr[2][R];      // plain layout: the row's e8m0 dwords of the chunk's 4 steps
+    dt_u32x4 w8[8][R];      // plain layout: weights as loaded, steps s .. s + 7
+    dt_u32x4 wp[2][R];      // plain layout: weights of steps s, s + 1 in operand lane order
 };
 
 template <int MT>
@@ -1191,6 +1194,8 @@ struct SpSrc {
     const uint32_t* sp[R];
     const uint8_t* xrow;     // activation row of this thread's item, at its chunk
     uint32_t xdst;           // the item's offset in a stage
+    uint32_t sh;             // plain layout: bit offset of the lane's K block in an e8m0 dword (8 g)
+    int perm;                // plain layout: byte address of the loading lane whose item this lane takes
     int x_last, w_last;      // last real step (activations), last padded step (weights)
 };
 
@@ -1199,7 +1204,9 @@ __device__ __forceinline__ dt_u32x4 sp_act(const SpSrc<R>& q, int j) {
     return *reinterpret_cast<const dt_u32x4*>(q.xrow + 128 * (int64_t)min(j, q.x_last));
 }
 
-template <int R, int D, bool CS>
+// PL: the plain layout ([N, K/2] codes, [N, K/32] e8m0), whose 16-byte lane
+// items of a step lie 64 bytes apart along the row instead of in one 1 KiB block
+template <int R, int D, bool CS, bool PL>
 __device__ __forceinline__ void sp_wload(const SpSrc<R>& q, int j, SpRing<R, D>& ring, int slot) {
     j = min(j, q.w_last);
 #pragma unroll
@@ -1209,17 +1216,47 @@ __device__ __forceinline__ void sp_wload(const SpSrc<R>& q, int j, SpRing<R, D>&
         if constexpr (!CS) ring.s[slot][r] = q.sp[r][(j >> 2) * 64];
     }
 }
-// chunk c's e8m0 dwords (clamped to the last chunk) into chunk slot `slot`
-template <int R, int D>
+// chunk c's e8m0 dwords (clamped to the last chunk) into chunk slot `slot`;
+// plain layout: the row's 16 bytes of steps 4c .. 4c + 3 (the lane's K block
+// is byte g of each dword), taken apart where the products use them so that
+// no wait follows the loads
+template <int R, int D, bool PL>
 __device__ __forceinline__ void sp_csload(const SpSrc<R>& q, int c, SpRing<R, D>& ring, int slot) {
     c = min(c, q.w_last >> 2);
 #pragma unroll
-    for (int r = 0; r < R; ++r) ring.cs[slot][r] = q.sp[r][c * 64];
+    for (int r = 0; r < R; ++r) {
+        if constexpr (PL) ring.cr[slot][r] = *reinterpret_cast<const dt_u32x4*>(q.sp[r] + 4 * c);
+        else ring.cs[slot][r] = q.sp[r][c * 64];
+    }
+}
+
+// plain layout: steps j0 .. j0 + 3 of every tile, issued together so that each
+// row's 256 contiguous bytes are requested at once (one step's 64 bytes per
+// row, sixteen rows 2.5 KB apart per load, read one at a time, made poor use
+// of the DRAM pages); default cache policy, as a 128-byte line holds two steps
+template <int R, int D>
+__device__ __forceinline__ void sp_wload_pl(const SpSrc<R>& q, int j0, SpRing<R, D>& ring, int slot0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            ring.w8[(slot0 + u) % 8][r] =
+                *reinterpret_cast<const dt_u32x4*>(q.wp[r] + (int64_t)min(j0 + u, q.w_last) * 4);
+}
+// plain layout: the loading lane 4n + g holds row n's K block g (four lanes
+// per 64 contiguous bytes); the operand wants it in lane n + 16g
+template <int R, int D>
+__device__ __forceinline__ void sp_permute(const SpSrc<R>& q, SpRing<R, D>& ring, int from, int to) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ring.wp[to][r][i] = (uint32_t)__builtin_amdgcn_ds_bpermute(q.perm, (int)ring.w8[from][r][i]);
 }
 
 // one step of the main loop; J = s mod the trip length (ring and activation
 // slots, stage, fragment set and chunk slot are compile-time)
-template <int MT, int R, int D, bool CS, int J>
+template <int MT, int R, int D, bool CS, bool PL, int J>
 __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     dt_barrier();
@@ -1227,12 +1264,16 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
     else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
     av[(J + 1) % D] = sp_act(q, s + D + 1);
     *reinterpret_cast<dt_u32x4*>(lds + ((J + 2) % kSpStages) * kSpStage + q.xdst) = av[(J + 2) % D];
+    // plain layout: step s + 1's weights into operand order, a step ahead of their products
+    if constexpr (PL) sp_permute<R, D>(q, ring, (J + 1) % 8, (J + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const dt_u32x4 w = ring.w[J % D][r];
+        const dt_u32x4 w = PL ? ring.wp[J & 1][r] : ring.w[J % D][r];
         const v8i af = frag_fp4(make_uint4(w[0], w[1], w[2], w[3]));
-        const int sc = (int)((CS ? ring.cs[(J / 4) % 2][r] : ring.s[J % D][r]) >> (8 * (J & 3)));
+        // the scale operand's low byte (opsel 0) is this step's e8m0
+        const int sc = PL ? (int)(ring.cr[(J / 4) % 2][r][J & 3] >> q.sh)
+                          : (int)((CS ? ring.cs[(J / 4) % 2][r] : ring.s[J % D][r]) >> (8 * (J & 3)));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if constexpr ((J & 1) == 0) acc[r][mt] = mfma16<0>(af, F0[mt], acc[r][mt], sc);
@@ -1240,31 +1281,47 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    sp_wload<R, D, CS>(q, s + D, ring, J % D);
-    if constexpr (CS && J % 4 == 0) sp_csload<R, D>(q, s / 4 + 1, ring, (J / 4 + 1) % 2);
+    if constexpr (PL) {
+        // steps s + 4 .. s + 7 into the slots of steps s - 4 .. s - 1
+        if constexpr (J % 4 == 0) sp_wload_pl<R, D>(q, s + 4, ring, (J + 4) % 8);
+    } else {
+        sp_wload<R, D, CS, PL>(q, s + D, ring, J % D);
+    }
+    if constexpr (CS && J % 4 == 0) sp_csload<R, D, PL>(q, s / 4 + 1, ring, (J / 4 + 1) % 2);
 }
 
 // the trip: D steps (per-step e8m0), or 8 with chunk slots (two chunks)
 template <int D, bool CS> constexpr int kSpTrip = CS ? 8 : D;
-template <int MT, int R, int D, bool CS, int J>
+template <int MT, int R, int D, bool CS, bool PL, int J>
 __device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     if constexpr (J < kSpTrip<D, CS>) {
-        sp_step<MT, R, D, CS, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
-        sp_trip<MT, R, D, CS, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
+        sp_step<MT, R, D, CS, PL, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
+        sp_trip<MT, R, D, CS, PL, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
     }
 }
 
 // a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x sum
-template <int MT, int R, int D, bool CS>
+template <int MT, int R, int D, bool CS, bool PL>
 __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
-        q.sp[r] = a.st + (int64_t)(w0 + r) * a.c_pad * 64 + lane;
+        if constexpr (PL) {
+            // plain layout (rows past N clamped: they are not stored): lane 4n + g loads row 16 t + n's
+            // K block g of a step; lane n + 16 g loads row 16 t + n's e8m0
+            const int row = min(16 * (w0 + r) + (lane >> 2), a.N - 1);
+            const int srow = min(16 * (w0 + r) + (lane & 15), a.N - 1);
+            q.wp[r] = a.wt + (int64_t)row * (a.K / 32) + (lane & 3);
+            q.sp[r] = a.st + (int64_t)srow * (a.K / 128);
+        } else {
+            q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
+            q.sp[r] = a.st + (int64_t)(w0 + r) * a.c_pad * 64 + lane;
+        }
     }
+    q.sh = 8u * g;
+    q.perm = 4 * (4 * (lane & 15) + g);
     // this thread's activation item: row tid / 8 (clamped to M - 1), chunk tid % 8
     const int xr = tid >> 3, c = tid & 7;
     q.xrow = a.x8 + (int64_t)min(xr, a.M - 1) * a.K + 16 * c;
@@ -1288,7 +1345,7 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
         // first, and pinned there: the loop's wait for a chunk slot also covers
         // the entry from here, and a load the scheduler sank to the end of the
         // prologue would make that wait drain every load in flight on every trip
-        sp_csload<R, D>(q, 0, ring, 0);
+        sp_csload<R, D, PL>(q, 0, ring, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     av[0] = sp_act(q, 0);
@@ -1296,13 +1353,18 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     for (int k = 0; k < D; ++k) {
         av[(k + 1) % D] = sp_act(q, k + 1);
         if (k == D - 2) *reinterpret_cast<dt_u32x4*>(lds + q.xdst) = av[0];
-        sp_wload<R, D, CS>(q, k, ring, k);
+        if constexpr (PL) {
+            if (k == 0) sp_wload_pl<R, D>(q, 0, ring, 0);
+        } else {
+            sp_wload<R, D, CS, PL>(q, k, ring, k);
+        }
     }
     dt_barrier();
     sp_read<MT>(lds, lane, F0);
     *reinterpret_cast<dt_u32x4*>(lds + kSpStage + q.xdst) = av[1];
+    if constexpr (PL) sp_permute<R, D>(q, ring, 0, 0);
 
-    for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>) sp_trip<MT, R, D, CS, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>) sp_trip<MT, R, D, CS, PL, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
 
     const bool vec = (a.N & 3) == 0;
 #pragma unroll
@@ -1327,9 +1389,10 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     }
 }
 
-template <int MT, int R, int D, bool CS>
+template <int MT, int R, int D, bool CS, bool PL>
 __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     static_assert(D == 4 || D == 8, "a trip is one turn of the ring and whole 4-step chunks");
+    static_assert(!PL || CS, "plain layout: the e8m0 bytes are gathered once per chunk");
     static_assert(!CS || D == 4, "chunk slots one chunk ahead: the ring may be at most 4 steps deep (deeper, the "
                                  "wait for a chunk's dwords would drain weights of later steps)");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
@@ -1341,16 +1404,16 @@ __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            sp_run<MT, R - 1, D, CS>(a, lds, w0, lane);
+            sp_run<MT, R - 1, D, CS, PL>(a, lds, w0, lane);
             return;
         }
     }
-    sp_run<MT, R, D, CS>(a, lds, w0, lane);
+    sp_run<MT, R, D, CS, PL>(a, lds, w0, lane);
 }
 
-template <int MT, int R, int D, bool CS>
+template <int MT, int R, int D, bool CS, bool PL = false>
 hipError_t launch_spread_inst(const SpArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((spread_kernel<MT, R, D, CS>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
+    hipLaunchKernelGGL((spread_kernel<MT, R, D, CS, PL>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -3349,8 +3412,14 @@ bool spread_fits(int64_t M, int64_t N, int64_t K) {
     return p.groups * 4 >= (int64_t)device_cus() * 3 && p.r >= 1 && p.r <= 2;
 }
 
+// the spread tiles on the plain layout: K steps a multiple of 8 (no padding
+// steps; the e8m0 bytes gathered once per chunk, in trips of two chunks)
+bool spread_plain_fits(int64_t M, int64_t N, int64_t K) {
+    return spread_fits(M, N, K) && (K / 128) % 8 == 0;
+}
+
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain) {
     if (M < 1 || M > 64 || p.mt != (int)((M + 15) / 16) || K % 128 != 0 || p.groups < 1) return hipErrorInvalidValue;
     if (p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16) return hipErrorInvalidValue;
     // every wave has a tile, and none more than R
@@ -3367,6 +3436,17 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     a.tiles = (int)p.tiles;
     a.groups = (int)p.groups;
     if (a.s_pad % p.d != 0 || (p.cs && (p.d != 4 || a.s_pad % 8 != 0))) return hipErrorInvalidValue;
+    if (plain) {
+        // [N, K/2] codes and [N, K/32] e8m0 in place of the fragment-order blocks
+        if (a.steps % 8 != 0 || p.d != 4 || !p.cs) return hipErrorInvalidValue;
+#define W4A8_SPL(MT, R) \
+    else if (p.mt == MT && p.r == R) return launch_spread_inst<MT, R, 4, true, true>(a, stream);
+        if (false) {}
+        W4A8_SPL(1, 1) W4A8_SPL(2, 1) W4A8_SPL(3, 1) W4A8_SPL(4, 1)
+        W4A8_SPL(1, 2) W4A8_SPL(2, 2) W4A8_SPL(3, 2) W4A8_SPL(4, 2)
+#undef W4A8_SPL
+        return hipErrorInvalidValue;
+    }
 #define W4A8_SP(MT, R, D, CS) \
     else if (p.mt == MT && p.r == R && p.d == D && p.cs == CS) return launch_spread_inst<MT, R, D, CS>(a, stream);
     if (false) {}

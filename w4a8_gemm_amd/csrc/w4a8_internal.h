@@ -239,8 +239,11 @@ struct SpPlan {
 };
 SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS);
 bool spread_fits(int64_t M, int64_t N, int64_t K);
+bool spread_plain_fits(int64_t M, int64_t N, int64_t K);
+// plain: wt / st are the plain layout ([N, K/2] codes, [N, K/32] e8m0, both
+// 16-byte aligned, K / 128 a multiple of 8) instead of fragment order
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
