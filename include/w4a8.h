@@ -180,8 +180,9 @@ w4a8_status w4a8_quant_act_fp8_per_token(
  * overlap on one workspace race.
  *
  * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
- * N, K and kind and any M <= M_max (0 if no split is used).  Pure host
- * function, never fails (returns 0 for invalid sizes).
+ * N, K and kind and any M <= M_max (K splits; for W4A8_WEIGHT_MXFP4 with
+ * M_max > 64 also the weight repacked into fragment order; 0 if no call
+ * needs any).  Pure host function, never fails (returns 0 for invalid sizes).
  * w4a8_workspace_init: zero a workspace of `bytes` bytes (device, 256-byte
  * aligned) on `stream`.  Errors: INVALID_ARG, WORKSPACE, HIP. */
 size_t      w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weight_kind kind);
@@ -210,8 +211,13 @@ w4a8_status w4a8_workspace_init(void *d_ws, size_t bytes, void *stream);
  * CU) with K a multiple of 1024 and d_w_e8m0 16-byte aligned runs the spread
  * tiles of w4a8_mxfp4_gemm_prepared on this layout directly (no workspace;
  * value identical to the prepared path); other M <= 64 the decode kernels
- * (weights streamed from HBM, split K), larger M the LDS-tiled prefill kernel.
- * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+ * (weights streamed from HBM, split K).  M > 64 with K % 128 == 0 and
+ * K < 2^24: each call repacks the weight into fragment order inside the
+ * workspace (w4a8_mxfp4_prepare's layout, after the decode band's split-K
+ * counters, which it leaves untouched), then runs the tile kernel of
+ * w4a8_mxfp4_gemm_prepared (value identical to it); other M > 64 the
+ * LDS-tiled kernel on this layout.  Errors: INVALID_ARG, UNSUPPORTED_SHAPE,
+ * WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const uint8_t *d_w_packed, const uint8_t *d_w_e8m0, uint16_t *d_out,

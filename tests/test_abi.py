@@ -155,13 +155,28 @@ def test_workspace_bytes_contract(L):
     assert wb(4, 64, 100, 0) == 0                                # K % 32
     assert wb(4, 60, 256, 1) == 0                                # int4 N % 8
     assert wb(4, 64, 128, 7) == 0                                # unknown kind
-    # covers every smaller M, and prefill-only sizes need none
+    # covers every smaller M
     prev = 0
     for m in (1, 2, 8, 16, 17, 32, 64, 65, 4096):
         cur = wb(m, 5120, 17408, 0)
         assert cur >= prev
         prev = cur
-    assert wb(4096, 5120, 17408, 0) == wb(64, 5120, 17408, 0)
+    # above 64 rows the plain-layout MXFP4 GEMM repacks its weight into the
+    # workspace after the decode band's split-K counters (one per 16 rows,
+    # 256-byte rounded): that and the two fragment-order buffers at least, and
+    # exactly those plus the tile kernel's own split where none is needed
+    N, K = 5120, 17408
+    wbytes, sbytes = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wbytes), ctypes.byref(sbytes)) == 0
+    up = lambda b: (b + 255) // 256 * 256
+    repack = up(((N + 15) // 16) * 4) + up(wbytes.value) + up(sbytes.value)
+    assert wb(4096, N, K, 0) >= repack and wb(4096, N, K, 0) > wb(64, N, K, 0)
+    N2, K2 = 34816, 5120          # 256 x 256 tiles from 4096 rows on: no split at M_max; 128 rows: 136 tiles
+    wb2, sb2 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.w4a8_mxfp4_prepared_bytes(N2, K2, ctypes.byref(wb2), ctypes.byref(sb2)) == 0
+    assert wb(128, N2, K2, 0) == up(((N2 + 15) // 16) * 4) + up(wb2.value) + up(sb2.value)
+    # K % 128 != 0 keeps the row-major tile kernel: no repack
+    assert wb(4096, 5120, 17440, 0) == wb(64, 5120, 17440, 0)
 
 
 def test_prepared_tiled_split_workspace(L):

@@ -147,6 +147,31 @@ def test_mxfp4_plain_layout_spread(M, N, K):
     assert_gemm_close(got[mi, ni], oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni), (M, N, K))
 
 
+# the plain layout above the decode band: each call repacks the weight into
+# fragment order inside the workspace and runs the prepared tile kernel, so
+# the value is the prepared entry point's, bit for bit; K % 128 != 0 keeps
+# the row-major tile kernel (checked against the oracle).  A decode call on
+# the same workspace afterwards still finds its split-K counters at zero.
+@pytest.mark.parametrize("M,N,K", [(65, 5000, 1152), (300, 1000, 4096), (1024, 20000, 640), (200, 520, 1056)])
+def test_mxfp4_plain_layout_prefill(M, N, K):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 14))
+    x8, s = _acts(M, K, (M, K, 14), spread=10.0)
+    say("plain-layout prefill", (M, N, K))
+    dx, ds, dw, de = dev_u8(x8), dev_f32(s), dev_u8(w["w_packed"]), dev_u8(w["w_e8m0"])
+    ws = w4.Workspace(M, N, K, "mxfp4")
+    got = host_bf16_as_f64(w4.mxfp4_gemm(dx, ds, dw, de, workspace=ws))
+    if K % 128 == 0:
+        pw = w4.mxfp4_prepare(dw, de)
+        assert np.array_equal(got, host_bf16_as_f64(w4.mxfp4_gemm_prepared(dx, ds, pw)))
+    mi, ni = _sample_idx(M, N, 8192, M + N)
+    assert_gemm_close(got[mi, ni], oracle.mxfp4_gemm(x8, s, w["w_packed"], w["w_e8m0"], mi=mi, ni=ni), (M, N, K))
+    # a split-K decode call on the same workspace
+    xd, sd = _acts(16, K, (16, K, 14))
+    a = host_bf16_as_f64(w4.mxfp4_gemm(dev_u8(xd), dev_f32(sd), dw, de, workspace=ws))
+    b = host_bf16_as_f64(w4.mxfp4_gemm(dev_u8(xd), dev_f32(sd), dw, de))
+    assert np.array_equal(a, b)
+
+
 def test_mxfp4_prefill_full_size(gate_up_mx):
     x8, s = _acts(4096, synth.HIDDEN, 3)
     _mx_sampled("prefill 4096", x8, s, *gate_up_mx[:2], n_samples=16384, reps=1)
