@@ -767,7 +767,8 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
         return (t.view(torch.float16) if half else t).to(dev)
 
     # the int4 g128 entry point on the transposed checkpoint layout
-    # (w4a8_int4g128_prepare + w4a8_int4g128_gemm), config I
+    # (w4a8_int4g128_prepare + w4a8_int4g128_gemm), config I; above 64 rows each
+    # call repacks into fragment order in the workspace, then the tile kernel
     q = synth.int4()
     nk = w4.int4g128_prepare(to_dev(q["qweight_kn"]), to_dev(q["qzeros"]))
     nkc = [nk] + [nk.clone() for _ in range(7)]

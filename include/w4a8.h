@@ -180,9 +180,10 @@ w4a8_status w4a8_quant_act_fp8_per_token(
  * overlap on one workspace race.
  *
  * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
- * N, K and kind and any M <= M_max (K splits; for W4A8_WEIGHT_MXFP4 with
- * M_max > 64 also the weight repacked into fragment order; 0 if no call
- * needs any).  Pure host function, never fails (returns 0 for invalid sizes).
+ * N, K and kind and any M <= M_max (K splits; for W4A8_WEIGHT_MXFP4 and
+ * W4A8_WEIGHT_INT4G128 with M_max > 64 also the weight repacked into fragment
+ * order; 0 if no call needs any).  Pure host function, never fails (returns
+ * 0 for invalid sizes).
  * w4a8_workspace_init: zero a workspace of `bytes` bytes (device, 256-byte
  * aligned) on `stream`.  Errors: INVALID_ARG, WORKSPACE, HIP. */
 size_t      w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weight_kind kind);
@@ -289,7 +290,12 @@ w4a8_status w4a8_int4g128_prepare(
  *   d_qweight_nk  device int32 [N, K/8]  (from w4a8_int4g128_prepare)
  *   d_scales_f16  device uint16 [K/128, N]  fp16 bits
  *   others as w4a8_mxfp4_gemm; N % 8 == 0, K % 128 == 0; workspace sized with
- *   W4A8_WEIGHT_INT4G128.  Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
+ *   W4A8_WEIGHT_INT4G128.  M <= 64: the decode kernel on this layout; M > 64
+ *   (K < 2^24): each call repacks the weight into fragment order inside the
+ *   workspace (w4a8_int4g128_prepare_fragments' layout, after the decode
+ *   band's split-K counters, which it leaves untouched), then runs the tile
+ *   kernel of w4a8_int4g128_gemm_prepared (value identical to it).
+ *   Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_int4g128_gemm(
     const uint8_t *d_x_fp8, const float *d_x_scale,
     const int32_t *d_qweight_nk, const uint16_t *d_scales_f16, uint16_t *d_out,

@@ -260,6 +260,11 @@ def _int4_case(name, q, M, seed, full=False, n_samples=4096):
     x8, s = _acts(M, K, seed)
     say("int4 gemm", name, (M, N, K))
     out = host_bf16_as_f64(w4.int4g128_gemm(dev_u8(x8), dev_f32(s), nk, dev_f16(q["scales"])))
+    if M > 64:
+        # above the decode band each call repacks into fragment order and runs
+        # the prepared tile kernel: the prepared entry point's value, bit for bit
+        pw = w4.int4g128_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]), dev_f16(q["scales"]))
+        assert np.array_equal(out, host_bf16_as_f64(w4.int4g128_gemm_prepared(dev_u8(x8), dev_f32(s), pw))), name
     if full:
         ref = oracle.int4_gemm(x8, s, ref_nk, q["scales"])
         assert_gemm_close(out, ref, name)

@@ -132,21 +132,23 @@ w4a8_status w4a8_quant_act_fp8_per_token(const uint16_t* d_x_bf16, int64_t M, in
     return hip_status(launch_act_quant(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, as_stream(stream)));
 }
 
-// The plain-layout MXFP4 GEMM above the decode band (K a multiple of 128, in
-// the tile kernel's range) repacks the weight into fragment order inside the
-// workspace, then runs the tile kernel of the prepared weights.  Workspace:
-// [split-K counters of the decode band, left untouched | repacked codes |
-// repacked e8m0 | the tile kernel's own workspace].
+// The plain-layout GEMMs above the decode band (MXFP4 [N, K/2] and the
+// transposed int4 [N, K/8]; K a multiple of 128, in the tile kernel's range)
+// repack the weight into fragment order inside the workspace, then run the
+// tile kernel of the prepared weights.  Workspace: [split-K counters of the
+// decode band, left untouched | repacked codes | repacked scales | the tile
+// kernel's own workspace].
 struct PlainRepack {
     size_t w_off, s_off, t_off, bytes;
 };
 static bool plain_repack_route(int64_t M, int64_t K) {
     return M > kDecodeMaxM && K % 128 == 0 && K <= kPreparedTiledMaxK;
 }
-static PlainRepack plain_repack_layout(int64_t N, int64_t K, size_t tiled_bytes) {
+static PlainRepack plain_repack_layout(int64_t N, int64_t K, size_t tiled_bytes, bool int4) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     size_t wb = 0, sb = 0;
-    prepared_sizes(N, K, &wb, &sb);
+    if (int4) prepared_i4_sizes(N, K, &wb, &sb);
+    else prepared_sizes(N, K, &wb, &sb);
     PlainRepack r{};
     r.w_off = up(ws_counter_bytes((N + 15) / 16));
     r.s_off = r.w_off + up(wb);
@@ -210,19 +212,20 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         const size_t b = plan_workspace_bytes(p, m, N);
         if (b > need) need = b;
     }
-    if (kind == W4A8_WEIGHT_MXFP4 && plain_repack_route(M_max, K)) {
+    if (plain_repack_route(M_max, K)) {
         // the repack and the largest tile-kernel workspace of the calls above
         // the decode band (scanned as for the prepared weights)
+        const bool int4 = kind == W4A8_WEIGHT_INT4G128;
         size_t tiled = 0;
         const int64_t tiles_n = (N + 255) / 256;
         for (int64_t m = 2 * kDecodeMaxM; m < M_max; m += kDecodeMaxM) {
-            const size_t b = tiled_workspace_bytes(m, N, K, false);
+            const size_t b = tiled_workspace_bytes(m, N, K, int4);
             if (b > tiled) tiled = b;
             if ((m / 256) * tiles_n >= 1024) break;
         }
-        const size_t b = tiled_workspace_bytes(M_max, N, K, false);
+        const size_t b = tiled_workspace_bytes(M_max, N, K, int4);
         if (b > tiled) tiled = b;
-        keep(plain_repack_layout(N, K, tiled).bytes);
+        keep(plain_repack_layout(N, K, tiled, int4).bytes);
     }
     return need;
 }
@@ -248,7 +251,7 @@ w4a8_status w4a8_mxfp4_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
                                         M, N, K, as_stream(stream), true));
     // above the decode band: repack into fragment order in the workspace, then the tile kernel
     if (plain_repack_route(M, K)) {
-        const PlainRepack r = plain_repack_layout(N, K, tiled_workspace_bytes(M, N, K, false));
+        const PlainRepack r = plain_repack_layout(N, K, tiled_workspace_bytes(M, N, K, false), false);
         st = check_workspace(r.bytes, d_ws, ws_bytes);
         if (st != W4A8_OK) return st;
         uint8_t* ws = reinterpret_cast<uint8_t*>(d_ws);
@@ -589,6 +592,18 @@ w4a8_status w4a8_int4g128_gemm(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (st != W4A8_OK) return st;
     if (!d_scales_f16 || !aligned(d_scales_f16, 8)) return W4A8_ERR_INVALID_ARG;
     if (N % 8 != 0 || K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    // above the decode band: repack into fragment order in the workspace, then the tile kernel
+    if (plain_repack_route(M, K)) {
+        const PlainRepack r = plain_repack_layout(N, K, tiled_workspace_bytes(M, N, K, true), true);
+        st = check_workspace(r.bytes, d_ws, ws_bytes);
+        if (st != W4A8_OK) return st;
+        uint8_t* ws = reinterpret_cast<uint8_t*>(d_ws);
+        hipError_t e = launch_prepare_i4_nk(d_qweight_nk, d_scales_f16, N, K, ws + r.w_off, ws + r.s_off,
+                                            as_stream(stream));
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(launch_prepared_tiled(d_x_fp8, d_x_scale, ws + r.w_off, ws + r.s_off, d_out, M, N, K,
+                                                ws + r.t_off, as_stream(stream), true, false, 0));
+    }
     const GemmPlan p = plan_int4(M, N, K);
     st = check_workspace(plan_workspace_bytes(p, M, N), d_ws, ws_bytes);
     if (st != W4A8_OK) return st;

@@ -239,15 +239,18 @@ __device__ __forceinline__ v4f i5_split_mma(const I4Split& w, v8i b4, v8i bx, v4
 // prepare: plain [N, K/2] codes + [N, K/32] e8m0 -> fragment order
 // ---------------------------------------------------------------------------
 
+// (also the int4 [N, K/8] layout, whose row n holds the same 16-byte lane
+// items at the same offsets: padding then the int4 zero code 8 in every nibble)
 __global__ __launch_bounds__(256) void prep_w_kernel(const uint8_t* __restrict__ wq, int N, int K,
-                                                     int tiles, int s_pad, uint4* __restrict__ wt) {
+                                                     int tiles, int s_pad, uint4* __restrict__ wt,
+                                                     uint32_t pad) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)tiles * s_pad * 64) return;
     const int L = (int)(i & 63);
     const int64_t blk = i >> 6;
     const int s = (int)(blk % s_pad), t = (int)(blk / s_pad);
     const int row = 16 * t + (L & 15), g = L >> 4;
-    uint4 v = make_uint4(0, 0, 0, 0);
+    uint4 v = make_uint4(pad, pad, pad, pad);
     if (row < N && s < K / 128)
         v = *reinterpret_cast<const uint4*>(wq + (int64_t)row * (K / 2) + 64 * (int64_t)s + 16 * g);
     wt[i] = v;
@@ -2554,7 +2557,7 @@ hipError_t launch_prepare(const uint8_t* wq, const uint8_t* we, int64_t N, int64
     const int c_pad = (int)((K / 128 + 3) / 4);
     const int64_t nw = (int64_t)tiles * c_pad * 4 * 64, ns = (int64_t)tiles * c_pad * 64;
     hipLaunchKernelGGL(prep_w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream, wq,
-                       (int)N, (int)K, tiles, 4 * c_pad, reinterpret_cast<uint4*>(wt));
+                       (int)N, (int)K, tiles, 4 * c_pad, reinterpret_cast<uint4*>(wt), 0u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prep_s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, we,
@@ -2577,6 +2580,22 @@ hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, 
     hipLaunchKernelGGL(prep_i4w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
                        reinterpret_cast<const uint32_t*>(qkn), (int)N, (int)K, tiles, 4 * c_pad,
                        reinterpret_cast<uint4*>(wt));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_i4s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, sc,
+                       (int)N, (int)K, tiles, c_pad, reinterpret_cast<uint16_t*>(st));
+    return hipGetLastError();
+}
+
+// the same from the transposed [N, K/8] codes (int4g128 GEMM's layout)
+hipError_t launch_prepare_i4_nk(const int32_t* qnk, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
+                                uint8_t* st, hipStream_t stream) {
+    const int tiles = (int)((N + 15) / 16);
+    const int c_pad = (int)((K / 128 + 3) / 4);
+    const int64_t nw = (int64_t)tiles * c_pad * 4 * 64, ns = (int64_t)tiles * c_pad * 64;
+    hipLaunchKernelGGL(prep_w_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint8_t*>(qnk), (int)N, (int)K, tiles, 4 * c_pad,
+                       reinterpret_cast<uint4*>(wt), 0x88888888u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prep_i4s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, sc,

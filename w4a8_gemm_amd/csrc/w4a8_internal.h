@@ -217,6 +217,9 @@ hipError_t launch_prepared_decode_i5(const uint8_t* x8, const float* xs, const u
                                      hipStream_t stream);
 hipError_t launch_prepare_i4(const int32_t* qkn, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
                              uint8_t* st, hipStream_t stream);
+// the same from the transposed [N, K/8] codes (w4a8_int4g128_gemm's layout)
+hipError_t launch_prepare_i4_nk(const int32_t* qnk, const uint16_t* sc, int64_t N, int64_t K, uint8_t* wt,
+                                uint8_t* st, hipStream_t stream);
 // Register-streamed tiles on prepared MXFP4 weights (decode band, M <= 64):
 // R 16-row tiles per wave, W waves per workgroup, K split across ks
 // workgroups (h_per two-step units each).
