@@ -7,9 +7,9 @@ repacked once into matrix-core fragment order), for each batch M in
 {1, 8, 16, 64}: per-token fp8 quantization of a bf16 [M, K] activation, then the
 block-scaled W4A8 GEMM -> bf16 [M, N] on the fragment-order weights, one call
 of the linear entry point per M.  The calls' kernels (STEP_KERNELS): M = 1 one
-launch (the quantization fused into the split-K decode kernel's prologue);
-M = 8, 16 and 64 the quant kernel and the spread-tile kernel (one workgroup
-per CU, the weight tiles dealt out evenly, each over all of K).  The step's four linears read four different
+launch of the spread-tile kernel (one workgroup per CU, the weight tiles dealt
+out evenly, each over all of K) with the quantization fused into its prologue;
+M = 8, 16 and 64 the quant kernel, then the spread-tile kernel.  The step's four linears read four different
 copies of the weight out of eight (95 MB each, 758 MB in all, three times the
 256 MB Infinity Cache; step s uses copies 4s .. 4s + 3 mod 8), so every weight
 byte of a step comes from HBM.  Each step is one HIP graph replay (one graph
@@ -62,13 +62,14 @@ N_GU, K_GU = 34816, 5120
 # (the library's routes, M -> [quant kernel,] GEMM kernel); the names are the
 # template instances rocprofv3 lists.
 STEP_KERNELS = {
-    1: [("pdec_kernel<1, 3, 0, 4, true>", "split-K decode, per-token quant fused in its prologue")],
+    1: [("spread_kernel<1, 2, 4, true, false, true>",
+         "spread tiles, per-token quant fused in the prologue (the quantized row resident in LDS)")],
     8: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-        ("spread_kernel<1, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
+        ("spread_kernel<1, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
     16: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("spread_kernel<1, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
+         ("spread_kernel<1, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
     64: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
-         ("spread_kernel<4, 2, 4, true>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
+         ("spread_kernel<4, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
 }
 SOURCES = {"gemm": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip"),
            "act_quant": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "act_quant.hip"),
@@ -544,8 +545,8 @@ def pmc_summarize(kind, dirs, probe_m):
         ]
     elif kind == "prefill":
         c = _per_dispatch(dirs[0], ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES"])
-        busy = _pick(c["SQ_VALU_MFMA_BUSY_CYCLES"], "pf_kernel")
-        gui = _pick(c["GRBM_GUI_ACTIVE"], "pf_kernel")
+        busy = _pick(c["SQ_VALU_MFMA_BUSY_CYCLES"], "pf_kernel<256, 256")
+        gui = _pick(c["GRBM_GUI_ACTIVE"], "pf_kernel<256, 256")
         mfmas = 2.0 * 4096 * N_GU * K_GU / (2 * 16 * 16 * 128)
         b, gu = sum(busy) / len(busy), sum(gui) / len(gui)
         util = b / (gu / XCDS * SIMDS)

@@ -448,12 +448,15 @@ w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
  *   others as w4a8_mxfp4_gemm_prepared / w4a8_int4g128_gemm_prepared, the
  *   workspace sized with the same kind.
  * out equals that GEMM on d_x_fp8 / d_x_scale bit for bit (the same kernel
- * plan, the same products in the same order).  When the split-K decode
- * kernel serves the GEMM with K unsplit, x is 16-byte aligned with
- * ldx % 8 == 0, M <= 16 and the bf16 slice fits one batch of the kernel's
- * registers (M x K/8 <= 8 x its threads), the quantization runs in that
- * kernel's prologue: one launch (codes and scales written out by one
- * workgroup).  Otherwise the quant kernel runs first, then the GEMM.
+ * plan, the same products in the same order).  With x 16-byte aligned and
+ * ldx % 8 == 0 the quantization joins the GEMM kernel in one launch (codes
+ * and scales written out by one workgroup): for one token on a wide MXFP4
+ * layer (the spread tiles; K a multiple of 1024, at most 8192) in the spread
+ * kernel's prologue, the quantized row staying in LDS; otherwise where the
+ * split-K decode kernel serves the GEMM with K unsplit, M <= 16 and the bf16
+ * slice fits one batch of its registers (M x K/8 <= 8 x its threads), in
+ * that kernel's prologue.  Otherwise the quant kernel runs first, then the
+ * GEMM.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx, const uint8_t *d_w_prepared,
                                        const uint8_t *d_s_prepared, uint16_t *d_out, int64_t M, int64_t N,

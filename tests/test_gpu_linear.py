@@ -62,9 +62,12 @@ def _mx(N, K, seed):
 
 
 # fused (one launch) for small M with K unsplit; the quant kernel + GEMM
-# otherwise (M = 17, long K, M = 40 tiled); ragged N, K of one step to many
+# otherwise (M = 17, long K, M = 40 tiled); ragged N, K of one step to many;
+# one token on a wide layer (K a multiple of 1024 up to 8192): fused into the
+# spread tiles, ragged N and the longest K
 LINEAR = [(1, 64, 128), (1, 300, 640), (2, 1000, 4736), (5, 257, 1024), (8, 520, 2048), (16, 130, 512),
-          (17, 600, 1152), (3, 1001, 17408), (40, 700, 384), (1, 20000, 5120), (12, 20000, 640)]
+          (17, 600, 1152), (3, 1001, 17408), (40, 700, 384), (1, 20000, 5120), (12, 20000, 640),
+          (1, 25001, 1024), (1, 30000, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR)
@@ -86,6 +89,18 @@ def test_mxfp4_linear_special_rows():
     x[3, ::3] = 1.0e-30
     bits = (x.view(np.uint32) >> 16).astype(np.uint16)
     _run("special rows", bits, pw, MX, ref_fn=ref)
+
+
+def test_mxfp4_linear_special_token_wide():
+    # one token on a wide layer (the spread tiles with the quantization fused):
+    # a zero token (scale 1, codes 0), then one huge value among small ones
+    N, K = 24576, 2048
+    pw, ref = _mx(N, K, 26)
+    for i, x in enumerate((np.zeros((1, K), np.float32), np.full((1, K), 1.0e-3, np.float32))):
+        if i == 1:
+            x[0, 5] = -1.0e30
+        bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+        _run(f"special token {i}", bits, pw, MX, ref_fn=ref, sample=4096)
 
 
 def test_mxfp4_linear_strided_and_unaligned_rows():

@@ -380,6 +380,9 @@ static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const 
     // allows, also for one row on wide layers whose GEMM alone takes the spread
     // tiles (gate_up M = 1: 19.1 us fused against 20.4 us for quant kernel + spread)
     const PreparedRoute route = prepared_route(M, N, K, int4);
+    // one token on a wide layer: the quantization fused into the spread tiles
+    if (!int4 && vec && route == PreparedRoute::Spread && spread_fq_fits(M, N, K))
+        return hip_status(launch_spread_fq(d_x_bf16, d_w, d_s, d_out, d_x_fp8, d_x_scale, N, K, as_stream(stream)));
     if (vec && (route == PreparedRoute::Decode || (route == PreparedRoute::Spread && M == 1)) &&
         plan_prepared_fused(M, N, K, int4, &p))
         return hip_status(launch_prepared_linear_fused(p, d_x_bf16, ldx, d_w, d_s, d_out, M, N, K, d_x_fp8,

@@ -1159,6 +1159,9 @@ struct SpArgs {
     int M, N, K;
     int s_pad, c_pad, tiles, steps;   // steps = K / 128 (real), s_pad = padded
     int groups;
+    const uint16_t* xb;     // fused quant (one token): bf16 activations
+    uint8_t* x8_out;        // fused quant: e4m3 codes [K] and token scale written
+    float* xs_out;          // by workgroup 0
 };
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
@@ -1259,14 +1262,28 @@ __device__ __forceinline__ void sp_permute(const SpSrc<R>& q, SpRing<R, D>& ring
 
 // one step of the main loop; J = s mod the trip length (ring and activation
 // slots, stage, fragment set and chunk slot are compile-time)
-template <int MT, int R, int D, bool CS, bool PL, int J>
+// fused quant (one token): step s's fragment from the resident quantized row
+// (every column of the operand the same row: a broadcast read)
+__device__ __forceinline__ void sp_read_row(const uint8_t* row, int lane, v8i (&F)[1]) {
+    const int g = lane >> 4;
+    F[0] = frag_fp8(*reinterpret_cast<const uint4*>(row + 16 * g), *reinterpret_cast<const uint4*>(row + 16 * (g + 4)));
+}
+
+template <int MT, int R, int D, bool CS, bool PL, bool FQ, int J>
 __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
-    dt_barrier();
-    if constexpr ((J & 1) == 0) sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F1);
-    else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
-    av[(J + 1) % D] = sp_act(q, s + D + 1);
-    *reinterpret_cast<dt_u32x4*>(lds + ((J + 2) % kSpStages) * kSpStage + q.xdst) = av[(J + 2) % D];
+    if constexpr (FQ) {
+        // the row stays in LDS: no staging, no barrier
+        const uint8_t* row = lds + 128 * min(s + 1, q.x_last);
+        if constexpr ((J & 1) == 0) sp_read_row(row, lane, F1);
+        else sp_read_row(row, lane, F0);
+    } else {
+        dt_barrier();
+        if constexpr ((J & 1) == 0) sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F1);
+        else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
+        av[(J + 1) % D] = sp_act(q, s + D + 1);
+        *reinterpret_cast<dt_u32x4*>(lds + ((J + 2) % kSpStages) * kSpStage + q.xdst) = av[(J + 2) % D];
+    }
     // plain layout: step s + 1's weights into operand order, a step ahead of their products
     if constexpr (PL) sp_permute<R, D>(q, ring, (J + 1) % 8, (J + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -1295,17 +1312,17 @@ __device__ __forceinline__ void sp_step(uint8_t* lds, int s, int lane, const SpS
 
 // the trip: D steps (per-step e8m0), or 8 with chunk slots (two chunks)
 template <int D, bool CS> constexpr int kSpTrip = CS ? 8 : D;
-template <int MT, int R, int D, bool CS, bool PL, int J>
+template <int MT, int R, int D, bool CS, bool PL, bool FQ, int J>
 __device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpSrc<R>& q, SpRing<R, D>& ring,
                                         dt_u32x4 (&av)[D], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     if constexpr (J < kSpTrip<D, CS>) {
-        sp_step<MT, R, D, CS, PL, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
-        sp_trip<MT, R, D, CS, PL, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
+        sp_step<MT, R, D, CS, PL, FQ, J>(lds, s + J, lane, q, ring, av, F0, F1, acc);
+        sp_trip<MT, R, D, CS, PL, FQ, J + 1>(lds, s, lane, q, ring, av, F0, F1, acc);
     }
 }
 
 // a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x sum
-template <int MT, int R, int D, bool CS, bool PL>
+template <int MT, int R, int D, bool CS, bool PL, bool FQ>
 __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;
@@ -1351,23 +1368,87 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
         sp_csload<R, D, PL>(q, 0, ring, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-    av[0] = sp_act(q, 0);
+    [[maybe_unused]] float sm_fq = 1.0f;
+    if constexpr (FQ) {
+        // fused quant, one token: its bf16 row (16-byte items tid and tid + 512
+        // of K / 8 <= 1024) before the weight ring prologue, so that the
+        // quantization waits only for these L2-resident loads
+        const int items = a.K / 8;
+        uint4 xv[2];
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-        av[(k + 1) % D] = sp_act(q, k + 1);
-        if (k == D - 2) *reinterpret_cast<dt_u32x4*>(lds + q.xdst) = av[0];
-        if constexpr (PL) {
-            if (k == 0) sp_wload_pl<R, D>(q, 0, ring, 0);
-        } else {
-            sp_wload<R, D, CS, PL>(q, k, ring, k);
+        for (int u = 0; u < 2; ++u) {
+            const int qi = tid + kSpThreads * u;
+            const uint4 t = *reinterpret_cast<const uint4*>(a.xb + 8 * (int64_t)min(qi, items - 1));
+            xv[u] = qi < items ? t : make_uint4(0u, 0u, 0u, 0u);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < D; ++k) sp_wload<R, D, CS, PL>(q, k, ring, k);
+        __builtin_amdgcn_sched_barrier(0);
+        // the standalone quant kernel's rule: s = amax / 448 (1 for a zero row),
+        // code = e4m3 of x / s, nearest even, saturating; the amax as the
+        // largest bit pattern of the non-negative maxima (fmaxf drops NaN)
+        uint32_t* amax_u = reinterpret_cast<uint32_t*>(lds + a.K);
+        if (tid == 0) *amax_u = 0u;
+        __syncthreads();
+        float mx = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t d[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mx = fmaxf(mx, fabsf(bf16_to_f32(d[i] & 0xFFFFu)));
+                mx = fmaxf(mx, fabsf(bf16_to_f32(d[i] >> 16)));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lane == 0) atomicMax(amax_u, __float_as_uint(mx));
+        __syncthreads();
+        const float amax = __uint_as_float(*amax_u);
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int qi = tid + kSpThreads * u;
+            if (qi >= items) continue;
+            const uint32_t d[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+            uint32_t o[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = f32_to_e4m3_rne_sat(bf16_to_f32(d[i] & 0xFFFFu) / sc);
+                const uint32_t hi = f32_to_e4m3_rne_sat(bf16_to_f32(d[i] >> 16) / sc);
+                o[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+            }
+            *reinterpret_cast<uint2*>(lds + 8 * qi) = make_uint2(o[0], o[1]);
+            // the codes and the scale written out once, by workgroup 0
+            if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.x8_out + 8 * (int64_t)qi) = make_uint2(o[0], o[1]);
+        }
+        if (blockIdx.x == 0 && tid == 0) a.xs_out[0] = sc;
+        sm_fq = sc;
+        __syncthreads();
+        v8i f[1];
+        sp_read_row(lds, lane, f);
+        F0[0] = f[0];
+    } else {
+        av[0] = sp_act(q, 0);
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            av[(k + 1) % D] = sp_act(q, k + 1);
+            if (k == D - 2) *reinterpret_cast<dt_u32x4*>(lds + q.xdst) = av[0];
+            if constexpr (PL) {
+                if (k == 0) sp_wload_pl<R, D>(q, 0, ring, 0);
+            } else {
+                sp_wload<R, D, CS, PL>(q, k, ring, k);
+            }
+        }
+        dt_barrier();
+        sp_read<MT>(lds, lane, F0);
+        *reinterpret_cast<dt_u32x4*>(lds + kSpStage + q.xdst) = av[1];
+        if constexpr (PL) sp_permute<R, D>(q, ring, 0, 0);
     }
-    dt_barrier();
-    sp_read<MT>(lds, lane, F0);
-    *reinterpret_cast<dt_u32x4*>(lds + kSpStage + q.xdst) = av[1];
-    if constexpr (PL) sp_permute<R, D>(q, ring, 0, 0);
 
-    for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>) sp_trip<MT, R, D, CS, PL, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>)
+        sp_trip<MT, R, D, CS, PL, FQ, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
 
     const bool vec = (a.N & 3) == 0;
 #pragma unroll
@@ -1378,7 +1459,7 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
         for (int mt = 0; mt < MT; ++mt) {
             const int m = mt * 16 + (lane & 15);
             if (m >= a.M) continue;
-            const float sm = a.xs[m];
+            const float sm = FQ ? sm_fq : a.xs[m];
             uint16_t* o = a.out + (int64_t)m * a.N + n0;
             if (vec) {
                 const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
@@ -1392,10 +1473,11 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     }
 }
 
-template <int MT, int R, int D, bool CS, bool PL>
+template <int MT, int R, int D, bool CS, bool PL, bool FQ>
 __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     static_assert(D == 4 || D == 8, "a trip is one turn of the ring and whole 4-step chunks");
     static_assert(!PL || CS, "plain layout: the e8m0 bytes are gathered once per chunk");
+    static_assert(!FQ || (MT == 1 && !PL), "fused quant: one token, fragment order");
     static_assert(!CS || D == 4, "chunk slots one chunk ahead: the ring may be at most 4 steps deep (deeper, the "
                                  "wait for a chunk's dwords would drain weights of later steps)");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
@@ -1407,16 +1489,16 @@ __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            sp_run<MT, R - 1, D, CS, PL>(a, lds, w0, lane);
+            sp_run<MT, R - 1, D, CS, PL, FQ>(a, lds, w0, lane);
             return;
         }
     }
-    sp_run<MT, R, D, CS, PL>(a, lds, w0, lane);
+    sp_run<MT, R, D, CS, PL, FQ>(a, lds, w0, lane);
 }
 
-template <int MT, int R, int D, bool CS, bool PL = false>
+template <int MT, int R, int D, bool CS, bool PL = false, bool FQ = false>
 hipError_t launch_spread_inst(const SpArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((spread_kernel<MT, R, D, CS, PL>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
+    hipLaunchKernelGGL((spread_kernel<MT, R, D, CS, PL, FQ>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -3429,6 +3511,35 @@ bool spread_fits(int64_t M, int64_t N, int64_t K) {
     const SpPlan p = plan_spread(M, N, K, 0, -1);
     // most CUs busy, and an instantiated tile count
     return p.groups * 4 >= (int64_t)device_cus() * 3 && p.r >= 1 && p.r <= 2;
+}
+
+// the linear on one bf16 token with its quantization fused into the spread
+// tiles: the quantized row resident in LDS (K + 4 bytes of the 32 KiB), K
+// steps a multiple of 8 (the trips of two chunks, no padding steps), the row
+// read as 16-byte items
+bool spread_fq_fits(int64_t M, int64_t N, int64_t K) {
+    return M == 1 && spread_fits(M, N, K) && (K / 128) % 8 == 0 && K <= 8192;
+}
+
+hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t* st, uint16_t* out,
+                            uint8_t* x8_out, float* xs_out, int64_t N, int64_t K, hipStream_t stream) {
+    if (!spread_fq_fits(1, N, K)) return hipErrorInvalidValue;
+    const SpPlan p = plan_spread(1, N, K, 0, -1);
+    if (p.d != 4 || !p.cs || p.groups < 1 || p.r < 1 || p.r > 2) return hipErrorInvalidValue;
+    if (p.tiles < (int64_t)kSpWaves * p.groups || (p.tiles + p.groups - 1) / p.groups > (int64_t)kSpWaves * p.r)
+        return hipErrorInvalidValue;
+    SpArgs a{};
+    a.xb = xb; a.x8_out = x8_out; a.xs_out = xs_out; a.out = out;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.M = 1; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.steps = (int)(K / 128);
+    a.tiles = (int)p.tiles;
+    a.groups = (int)p.groups;
+    if (p.r == 1) return launch_spread_inst<1, 1, 4, true, false, true>(a, stream);
+    return launch_spread_inst<1, 2, 4, true, false, true>(a, stream);
 }
 
 // the spread tiles on the plain layout: K steps a multiple of 8 (no padding

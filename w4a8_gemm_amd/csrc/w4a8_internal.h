@@ -243,6 +243,11 @@ struct SpPlan {
 SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS);
 bool spread_fits(int64_t M, int64_t N, int64_t K);
 bool spread_plain_fits(int64_t M, int64_t N, int64_t K);
+// the linear on one bf16 token (16-byte aligned row) with the quantization
+// fused into the spread tiles; x8_out / xs_out receive the codes and the scale
+bool spread_fq_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t* st, uint16_t* out,
+                            uint8_t* x8_out, float* xs_out, int64_t N, int64_t K, hipStream_t stream);
 // plain: wt / st are the plain layout ([N, K/2] codes, [N, K/32] e8m0, both
 // 16-byte aligned, K / 128 a multiple of 8) instead of fragment order
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
