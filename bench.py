@@ -485,10 +485,10 @@ def trace_summarize(d):
         raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {d}")
     rows = list(csv.DictReader(open(stats[0])))
     lines = ["# Kernel trace of the default bench.py run", "",
-             "rocprofv3 command (run from the repository root on one MI355X):", "",
+             "rocprofv3 command (run from the repository root on one MI355X; $OUT is an output directory):", "",
              "    cd /tmp && export TMPDIR=/tmp && cd - && rocprofv3 --kernel-trace --stats -f csv "
-             "-d gpurun_out/prof_bench -o run -- python3 -u bench.py",
-             "    python3 bench.py --trace-summarize gpurun_out/prof_bench", "",
+             "-d $OUT/prof_bench -o run -- python3 -u bench.py",
+             "    python3 bench.py --trace-summarize $OUT/prof_bench", "",
              "Per kernel (`run_kernel_stats.csv`):", "",
              "| kernel | calls | avg us | min us | % time |", "|---|---|---|---|---|"]
     for r in rows[:30]:
@@ -525,13 +525,13 @@ def pmc_summarize(kind, dirs, probe_m):
         lines = [
             f"# HBM traffic of {name}, gate_up decode GEMM M = {probe_m}",
             "",
-            "Commands (repository root, one MI355X):",
+            "Commands (repository root, one MI355X; $OUT is an output directory):",
             "",
-            f"    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python3 -u bench.py "
+            f"    rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pmc_fetch -o run -- python3 -u bench.py "
             f"--pmc-probe decode --probe-m {probe_m}",
-            f"    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python3 -u bench.py "
+            f"    rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/pmc_write -o run -- python3 -u bench.py "
             f"--pmc-probe decode --probe-m {probe_m}",
-            f"    python3 bench.py --probe-m {probe_m} --pmc-summarize decode gpurun_out/pmc_fetch gpurun_out/pmc_write",
+            f"    python3 bench.py --probe-m {probe_m} --pmc-summarize decode $OUT/pmc_fetch $OUT/pmc_write",
             "",
             f"Calibration: a {CALIB_BYTES} B device-to-device copy reads FETCH_SIZE at scale {fs:.4f} and "
             f"WRITE_SIZE at scale {ws:.4f} (counter bytes per byte moved).",
@@ -554,11 +554,11 @@ def pmc_summarize(kind, dirs, probe_m):
         lines = [
             "# MFMA utilisation of pf_kernel<256, 256, 3, 0>, gate_up prefill M = 4096",
             "",
-            "Commands (repository root, one MI355X):",
+            "Commands (repository root, one MI355X; $OUT is an output directory):",
             "",
             "    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CYCLES -f csv "
-            "-d gpurun_out/pmc_mfma -o run -- python3 -u bench.py --pmc-probe prefill",
-            "    python3 bench.py --pmc-summarize prefill gpurun_out/pmc_mfma",
+            "-d $OUT/pmc_mfma -o run -- python3 -u bench.py --pmc-probe prefill",
+            "    python3 bench.py --pmc-summarize prefill $OUT/pmc_mfma",
             "",
             f"{len(busy)} dispatches: mean SQ_VALU_MFMA_BUSY_CYCLES {b:.4g} (summed over SIMDs), mean "
             f"GRBM_GUI_ACTIVE {gu:.4g} (summed over {XCDS} XCDs).",
@@ -578,16 +578,16 @@ def pmc_summarize(kind, dirs, probe_m):
         lines = [
             "# Full-layer requant (gate_up 34816 x 5120): HBM bytes and VALU activity of requant_kernel",
             "",
-            "Commands (repository root, one MI355X):",
+            "Commands (repository root, one MI355X; $OUT is an output directory):",
             "",
-            "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_rq_fetch -o run -- python3 -u bench.py "
+            "    rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pmc_rq_fetch -o run -- python3 -u bench.py "
             "--pmc-probe requant",
-            "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_rq_write -o run -- python3 -u bench.py "
+            "    rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/pmc_rq_write -o run -- python3 -u bench.py "
             "--pmc-probe requant",
-            "    rocprofv3 --pmc SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_rq_valu "
+            "    rocprofv3 --pmc SQ_ACTIVE_INST_VALU SQ_INSTS_VALU GRBM_GUI_ACTIVE -f csv -d $OUT/pmc_rq_valu "
             "-o run -- python3 -u bench.py --pmc-probe requant",
-            "    python3 bench.py --pmc-summarize requant gpurun_out/pmc_rq_fetch gpurun_out/pmc_rq_write "
-            "gpurun_out/pmc_rq_valu",
+            "    python3 bench.py --pmc-summarize requant $OUT/pmc_rq_fetch $OUT/pmc_rq_write "
+            "$OUT/pmc_rq_valu",
             "",
             f"Calibration scales: FETCH_SIZE {fs:.4f}, WRITE_SIZE {ws:.4f}.  Algorithmic bytes {algo}.",
             "VALU busy = SQ_ACTIVE_INST_VALU x 4 / SIMDs / (GRBM_GUI_ACTIVE / XCDs) (the rocprof VALUBusy "

@@ -5,7 +5,7 @@
  * cpu_baseline leg of bench.py; never by the library.  Shares no code with
  * the HIP path.  Page citations as in oracle.h ([P1], [P2], [P3]).
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *  R1  Block exponents are the exact-arithmetic values of the page's closed
  *      forms (floor(log2 amax)-2 and ceil(log2(amax/6))), i.e. the integers
  *      that satisfy the page's stated ranges [4,8) and (3,6]; not a float
