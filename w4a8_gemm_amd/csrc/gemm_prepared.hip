@@ -1162,6 +1162,8 @@ struct SpArgs {
     const uint16_t* xb;     // fused quant (one token): bf16 activations
     uint8_t* x8_out;        // fused quant: e4m3 codes [K] and token scale written
     float* xs_out;          // by workgroup 0
+    int out16;              // output rows stored in 16-byte pieces through LDS (N % 8 == 0, out 16-byte aligned,
+                            // the block M x 32 nt bytes within the stage ring)
 };
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
@@ -1321,9 +1323,10 @@ __device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpS
     }
 }
 
-// a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x sum
+// a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x
+// sum (the workgroup's tiles: t_lo .. t_lo + nt - 1)
 template <int MT, int R, int D, bool CS, bool PL, bool FQ>
-__device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane) {
+__device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, int lane, int t_lo, int nt) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;
 #pragma unroll
@@ -1450,6 +1453,38 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>)
         sp_trip<MT, R, D, CS, PL, FQ, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
 
+    if (a.out16) {
+        // the workgroup's output block (M rows x 16 nt columns of bf16) assembled
+        // in LDS, then stored row by row in 16-byte pieces, consecutive lanes
+        // along a row: whole 128-byte lines per store instead of sixteen 32-byte
+        // pieces (the products' lane layout), which took the write-back of a
+        // 64-row block 2-3 us longer at the end of the launch
+        const int pitch = 32 * nt;
+        __syncthreads();   // every wave past its last fragment read
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = mt * 16 + (lane & 15);
+                if (m >= a.M) continue;
+                const float sm = FQ ? sm_fq : a.xs[m];
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
+                *reinterpret_cast<uint2*>(lds + m * pitch + 32 * (w0 - t_lo + r) + 8 * g) = make_uint2(h0, h1);
+            }
+        }
+        __syncthreads();
+        // columns past N (the last tile's) are not stored; N is a multiple of 8
+        const int cpr = (min(16 * nt, a.N - 16 * t_lo)) / 8;
+        uint8_t* ob = reinterpret_cast<uint8_t*>(a.out + 16 * (int64_t)t_lo);
+        for (int i = (int)threadIdx.x; i < a.M * cpr; i += kSpThreads) {
+            const int row = i / cpr, ch = i - row * cpr;
+            *reinterpret_cast<uint4*>(ob + 2 * (int64_t)row * a.N + 16 * ch) =
+                *reinterpret_cast<const uint4*>(lds + row * pitch + 16 * ch);
+        }
+        return;
+    }
+
     const bool vec = (a.N & 3) == 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1489,11 +1524,11 @@ __global__ __launch_bounds__(kSpThreads) void spread_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            sp_run<MT, R - 1, D, CS, PL, FQ>(a, lds, w0, lane);
+            sp_run<MT, R - 1, D, CS, PL, FQ>(a, lds, w0, lane, t_lo, n);
             return;
         }
     }
-    sp_run<MT, R, D, CS, PL, FQ>(a, lds, w0, lane);
+    sp_run<MT, R, D, CS, PL, FQ>(a, lds, w0, lane, t_lo, n);
 }
 
 template <int MT, int R, int D, bool CS, bool PL = false, bool FQ = false>
@@ -3506,6 +3541,14 @@ SpPlan plan_spread(int64_t M, int64_t N, int64_t K, int D, int CS) {
     return p;
 }
 
+// the output block of a workgroup (M rows, at most ceil(tiles / groups) tiles of
+// 32 bytes) assembled in the stage ring for 16-byte row stores
+static int spread_out16(const uint16_t* out, int64_t M, int64_t N, const SpPlan& p) {
+    const int64_t nt_max = (p.tiles + p.groups - 1) / p.groups;
+    return (N % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
+            M * 32 * nt_max <= (int64_t)kSpStages * kSpStage) ? 1 : 0;
+}
+
 bool spread_fits(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > 64 || K % 128 != 0) return false;
     const SpPlan p = plan_spread(M, N, K, 0, -1);
@@ -3538,6 +3581,7 @@ hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t
     a.steps = (int)(K / 128);
     a.tiles = (int)p.tiles;
     a.groups = (int)p.groups;
+    a.out16 = spread_out16(out, 1, N, p);
     if (p.r == 1) return launch_spread_inst<1, 1, 4, true, false, true>(a, stream);
     return launch_spread_inst<1, 2, 4, true, false, true>(a, stream);
 }
@@ -3565,6 +3609,7 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     a.steps = (int)(K / 128);
     a.tiles = (int)p.tiles;
     a.groups = (int)p.groups;
+    a.out16 = spread_out16(out, M, N, p);
     if (a.s_pad % p.d != 0 || (p.cs && (p.d != 4 || a.s_pad % 8 != 0))) return hipErrorInvalidValue;
     if (plain) {
         // [N, K/2] codes and [N, K/32] e8m0 in place of the fragment-order blocks
