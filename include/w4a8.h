@@ -182,8 +182,9 @@ w4a8_status w4a8_quant_act_fp8_per_token(
  * w4a8_gemm_workspace_bytes: bytes needed by every GEMM call with the given
  * N, K and kind and any M <= M_max (K splits; for W4A8_WEIGHT_MXFP4 and
  * W4A8_WEIGHT_INT4G128 with M_max > 64 also the weight repacked into fragment
- * order; 0 if no call needs any).  Pure host function, never fails (returns
- * 0 for invalid sizes).
+ * order; for W4A8_WEIGHT_MXFP4_PREPARED on a wide layer with M_max > 16 the
+ * linear's step-major copy of the codes; 0 if no call needs any).  Pure
+ * host function, never fails (returns 0 for invalid sizes).
  * w4a8_workspace_init: zero a workspace of `bytes` bytes (device, 256-byte
  * aligned) on `stream`.  Errors: INVALID_ARG, WORKSPACE, HIP. */
 size_t      w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weight_kind kind);
@@ -456,7 +457,10 @@ w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t *d_x_fp8, const float *d_x
  * split-K decode kernel serves the GEMM with K unsplit, M <= 16 and the bf16
  * slice fits one batch of its registers (M x K/8 <= 8 x its threads), in
  * that kernel's prologue.  Otherwise the quant kernel runs first, then the
- * GEMM.
+ * GEMM; for 17 <= M <= 64 on a wide MXFP4 layer (the spread tiles) the quant
+ * kernel also writes the codes step-major ([K/128][M][128], a step's rows
+ * contiguous) into the workspace after its split-K counters, and the tiles
+ * read that copy (a workspace without room for it: the codes as written).
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_mxfp4_linear_prepared(const uint16_t *d_x_bf16, int64_t ldx, const uint8_t *d_w_prepared,
                                        const uint8_t *d_s_prepared, uint16_t *d_out, int64_t M, int64_t N,

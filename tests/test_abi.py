@@ -151,6 +151,14 @@ def test_gemm_validation(L):
 
 def test_workspace_bytes_contract(L):
     wb = L.w4a8_gemm_workspace_bytes
+    # prepared MXFP4 on a wide layer (the spread tiles): no workspace up to 16
+    # rows; above, the linear's step-major copy of the codes, after the split-K
+    # counters (one word per 16 rows, 256-byte rounded)
+    up = lambda b: (b + 255) // 256 * 256
+    Nw, Kw = 34816, 5120
+    assert wb(1, Nw, Kw, 2) == 0 and wb(16, Nw, Kw, 2) == 0
+    assert wb(17, Nw, Kw, 2) == up(((Nw + 15) // 16) * 4) + up(17 * Kw)
+    assert wb(64, Nw, Kw, 2) == up(((Nw + 15) // 16) * 4) + up(64 * Kw)
     assert wb(0, 64, 128, 0) == 0
     assert wb(4, 64, 100, 0) == 0                                # K % 32
     assert wb(4, 60, 256, 1) == 0                                # int4 N % 8

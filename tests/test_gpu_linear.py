@@ -120,6 +120,27 @@ def test_mxfp4_linear_strided_and_unaligned_rows():
     _run("unaligned", bits, pw, MX, x_view=xo, ref_fn=ref)
 
 
+class _NoWorkspace:
+    """A workspace argument of no bytes: the linear's codes stay row-major."""
+
+    def args(self):
+        return None, 0
+
+
+# more than 16 rows on a wide layer: the quant kernel also writes the codes
+# step-major into the workspace and the spread tiles stage from that copy;
+# without room in the workspace the same call reads the row-major codes.
+# Ragged N, K of 5 steps (no e8m0 chunk slots), 9 and 16; both outputs the
+# GEMM's on the written codes bit for bit (M = 3: the row-major path both times)
+@pytest.mark.parametrize("M,N,K", [(3, 25001, 640), (17, 25001, 640), (33, 24600, 2048), (64, 30000, 1152)])
+def test_mxfp4_linear_wide_step_major(M, N, K):
+    pw, ref = _mx(N, K, (M, N, K, 28))
+    bits = synth.acts(M, K, seed=(M, K, 28), spread=10.0)
+    got, ref_gpu = _run(f"wide {M}x{N}x{K}", bits, pw, MX, ref_fn=ref, sample=4096)
+    out, _, _ = w4.mxfp4_linear_prepared(dev_bf16(bits), pw, workspace=_NoWorkspace())
+    assert np.array_equal(host_bf16_as_f64(out), ref_gpu), "row-major codes"
+
+
 @pytest.fixture(scope="module")
 def gate_up_pw(gate_up_mx):
     return w4.mxfp4_prepare(dev_u8(gate_up_mx[0]), dev_u8(gate_up_mx[1]))

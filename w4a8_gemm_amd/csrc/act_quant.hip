@@ -81,11 +81,14 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
     }
 }
 
-// single pass: the row in registers, R uint4 (8 bf16 each) per thread
+// single pass: the row in registers, R uint4 (8 bf16 each) per thread; with
+// x8s the codes also go step-major ([K/128][M][128]: the 128-wide steps of all
+// rows one after the other, the layout the wide-layer decode tiles stage from)
 template <int R>
 __global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint16_t* __restrict__ x, int64_t K,
                                                                  int64_t ldx, uint8_t* __restrict__ x8,
-                                                                 float* __restrict__ xs) {
+                                                                 float* __restrict__ xs,
+                                                                 uint8_t* __restrict__ x8s) {
     const int64_t m = blockIdx.x;
     const uint4* r4 = reinterpret_cast<const uint4*>(x + m * ldx);
     uint2* o2 = reinterpret_cast<uint2*>(x8 + m * K);
@@ -122,6 +125,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint16_t*
             o[q >> 1] |= (lo | (hi << 8)) << (16 * (q & 1));
         }
         o2[c] = make_uint2(o[0], o[1]);
+        if (x8s)
+            *reinterpret_cast<uint2*>(x8s + (int64_t)(c >> 4) * 128 * gridDim.x + 128 * m + 8 * (c & 15)) =
+                make_uint2(o[0], o[1]);
     }
 }
 
@@ -134,17 +140,35 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
     const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;   // uint4 per thread
     if (vec && per_thread <= 16) {
         const dim3 g((unsigned)M), b(kThreads);
-        if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs);
-        else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs);
-        else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs);
-        else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs);
-        else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs);
+        if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
+        else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
+        else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
+        else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
+        else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
     } else if (vec)
         hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(kThreads), 0, stream, x,
                            K, ldx, x8, xs);
     else
         hipLaunchKernelGGL(act_quant_kernel<false>, dim3((unsigned)M), dim3(kThreads), 0, stream,
                            x, K, ldx, x8, xs);
+    return hipGetLastError();
+}
+
+bool act_quant_sm_fits(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* x8) {
+    return M >= 1 && K % 128 == 0 && ldx % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)x8 % 8 == 0 &&
+           (K / 8 + kThreads - 1) / kThreads <= 16;
+}
+
+hipError_t launch_act_quant_sm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8, float* xs,
+                               uint8_t* x8s, hipStream_t stream) {
+    if (!act_quant_sm_fits(x, M, K, ldx, x8) || !x8s || (uintptr_t)x8s % 16 != 0) return hipErrorInvalidValue;
+    const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;
+    const dim3 g((unsigned)M), b(kThreads);
+    if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
+    else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
+    else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
+    else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
+    else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
     return hipGetLastError();
 }
 

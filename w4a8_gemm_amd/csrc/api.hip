@@ -144,6 +144,13 @@ struct PlainRepack {
 static bool plain_repack_route(int64_t M, int64_t K) {
     return M > kDecodeMaxM && K % 128 == 0 && K <= kPreparedTiledMaxK;
 }
+// the linear at 17 <= M <= 64 on a wide MXFP4 layer: the codes also step-major
+// ([K/128][M][128]) in the workspace, after the decode band's split-K counters
+static size_t linear_sm_offset(int64_t N) { return (ws_counter_bytes((N + 15) / 16) + 255) / 256 * 256; }
+static size_t linear_sm_bytes(int64_t M, int64_t N, int64_t K) {
+    return linear_sm_offset(N) + (size_t)((M * K + 255) / 256 * 256);
+}
+
 static PlainRepack plain_repack_layout(int64_t N, int64_t K, size_t tiled_bytes, bool int4) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     size_t wb = 0, sb = 0;
@@ -185,7 +192,8 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
             const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
             const PreparedRoute r = prepared_route(m, N, K, int4);
             if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
-            if (r == PreparedRoute::Spread) return 0;
+            // the linear's step-major copy of the codes (more than one activation tile)
+            if (r == PreparedRoute::Spread) return m > 16 && !int4 ? linear_sm_bytes(m, N, K) : 0;
             if (K > kPreparedTiledMaxK) return 0;
             if (r == PreparedRoute::DTile) return dtile_workspace_bytes(plan_dtile_route(m, N, K), m, N);
             return tiled_workspace_bytes(m, N, K, int4);
@@ -387,6 +395,19 @@ static w4a8_status linear_prepared(const uint16_t* d_x_bf16, int64_t ldx, const 
         plan_prepared_fused(M, N, K, int4, &p))
         return hip_status(launch_prepared_linear_fused(p, d_x_bf16, ldx, d_w, d_s, d_out, M, N, K, d_x_fp8,
                                                        d_x_scale, as_stream(stream), int4));
+    // more than one activation tile on a wide layer: the quant kernel also
+    // writes the codes step-major into the workspace (a step's rows contiguous),
+    // which the spread tiles stage from (gate_up M = 32 / 64: 18.4 / 21.3 us on
+    // the row-major codes, 17.8 / 20.4 step-major; no gain at M <= 16, where
+    // the staged rows are 16 lines a step); without room, the codes as written
+    if (!int4 && route == PreparedRoute::Spread && M > 16 && act_quant_sm_fits(d_x_bf16, M, K, ldx, d_x_fp8) &&
+        d_ws && aligned(d_ws, 256) && ws_bytes >= linear_sm_bytes(M, N, K)) {
+        uint8_t* x8s = static_cast<uint8_t*>(d_ws) + linear_sm_offset(N);
+        st = hip_status(launch_act_quant_sm(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, x8s, as_stream(stream)));
+        if (st != W4A8_OK) return st;
+        return hip_status(launch_spread(plan_spread(M, N, K, 0, -1), x8s, d_x_scale, d_w, d_s, d_out, M, N, K,
+                                        as_stream(stream), false, true));
+    }
     st = hip_status(launch_act_quant(d_x_bf16, M, K, ldx, d_x_fp8, d_x_scale, as_stream(stream)));
     if (st != W4A8_OK) return st;
     return gemm_prepared(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, d_ws, ws_bytes, stream, int4);

@@ -1164,6 +1164,8 @@ struct SpArgs {
     float* xs_out;          // by workgroup 0
     int out16;              // output rows stored in 16-byte pieces through LDS (N % 8 == 0, out 16-byte aligned,
                             // the block M x 32 nt bytes within the stage ring)
+    int64_t xrs, xss;       // activation codes: bytes between rows and between 128-wide steps
+                            // (row-major K and 128; step-major 128 and 128 M)
 };
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
@@ -1205,11 +1207,12 @@ struct SpSrc {
     uint32_t sh;             // plain layout: bit offset of the lane's K block in an e8m0 dword (8 g)
     int perm;                // plain layout: byte address of the loading lane whose item this lane takes
     int x_last, w_last;      // last real step (activations), last padded step (weights)
+    int64_t xss;             // bytes between the steps of an activation row
 };
 
 template <int R>
 __device__ __forceinline__ dt_u32x4 sp_act(const SpSrc<R>& q, int j) {
-    return *reinterpret_cast<const dt_u32x4*>(q.xrow + 128 * (int64_t)min(j, q.x_last));
+    return *reinterpret_cast<const dt_u32x4*>(q.xrow + q.xss * min(j, q.x_last));
 }
 
 // PL: the plain layout ([N, K/2] codes, [N, K/32] e8m0), whose 16-byte lane
@@ -1347,7 +1350,8 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     q.perm = 4 * (4 * (lane & 15) + g);
     // this thread's activation item: row tid / 8 (clamped to M - 1), chunk tid % 8
     const int xr = tid >> 3, c = tid & 7;
-    q.xrow = a.x8 + (int64_t)min(xr, a.M - 1) * a.K + 16 * c;
+    q.xrow = a.x8 + (int64_t)min(xr, a.M - 1) * a.xrs + 16 * c;
+    q.xss = a.xss;
     q.xdst = 128u * xr + 16u * (c ^ ((xr >> 1) & 7));
     q.x_last = a.steps - 1;
     q.w_last = a.s_pad - 1;
@@ -3593,7 +3597,8 @@ bool spread_plain_fits(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain) {
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain,
+                         bool x_step_major) {
     if (M < 1 || M > 64 || p.mt != (int)((M + 15) / 16) || K % 128 != 0 || p.groups < 1) return hipErrorInvalidValue;
     if (p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16) return hipErrorInvalidValue;
     // every wave has a tile, and none more than R
@@ -3610,6 +3615,8 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     a.tiles = (int)p.tiles;
     a.groups = (int)p.groups;
     a.out16 = spread_out16(out, M, N, p);
+    a.xrs = x_step_major ? 128 : K;
+    a.xss = x_step_major ? 128 * M : 128;
     if (a.s_pad % p.d != 0 || (p.cs && (p.d != 4 || a.s_pad % 8 != 0))) return hipErrorInvalidValue;
     if (plain) {
         // [N, K/2] codes and [N, K/32] e8m0 in place of the fragment-order blocks

@@ -134,6 +134,11 @@ hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8,
                             float* xs, hipStream_t stream);
+// the same codes also written step-major to x8s ([K/128][M][128], 16-byte
+// aligned), where the single-pass kernel serves the shape (act_quant_sm_fits)
+bool act_quant_sm_fits(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* x8);
+hipError_t launch_act_quant_sm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8, float* xs,
+                               uint8_t* x8s, hipStream_t stream);
 
 // GEMM plans: the host picks the band, the tile and the K split.
 struct GemmPlan {
@@ -249,9 +254,12 @@ bool spread_fq_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t* st, uint16_t* out,
                             uint8_t* x8_out, float* xs_out, int64_t N, int64_t K, hipStream_t stream);
 // plain: wt / st are the plain layout ([N, K/2] codes, [N, K/32] e8m0, both
-// 16-byte aligned, K / 128 a multiple of 8) instead of fragment order
+// 16-byte aligned, K / 128 a multiple of 8) instead of fragment order;
+// x_step_major: the codes x8 in step-major order [K/128][M][128] (a step's
+// rows contiguous) instead of [M, K]
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
-                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false);
+                         uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false,
+                         bool x_step_major = false);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
