@@ -31,7 +31,8 @@ changed since).
 
 extra: the prefill GEMM (M = 4096) in TFLOP/s with its MFMA-busy counter
 record; the full-layer requant in GB/s (three rules, ROW_CHUNK and one pass)
-with its HBM and VALU counter record; requant accuracy (relRMS) against the
+with its HBM and VALU counter record, and written straight into fragment order
+beside the repack pass it saves; requant accuracy (relRMS) against the
 synthetic original; the two plain-layout GEMM entry points (MXFP4 row-major,
 int4 transposed); W4A4; the bf16 / fp8-per-channel encoders; down_proj; int4,
 int4 with zero points and int5.
@@ -705,6 +706,23 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
                 ent["valu_busy"] = rqc[f"valu_busy_{mode}"]
                 ent["traffic"] = int(rqc[f"traffic_bytes_{mode}"])
             rq[f"{mode}_chunk{chunk}"] = ent
+    # the requant written straight into fragment order, against the row-major
+    # requant followed by the load-time repack
+    pq = [w4.mxfp4_prepare(wp, we) for _ in range(2)]
+    for mode in ("ocp", "mse"):
+        def run_p(i, mode=mode):
+            p, s = src[i % 2]
+            w4.requant_nvfp4_to_mxfp4_prepared(p, s, g["part_rows"], g["part_divisor"], mode=mode, out=pq[i % 2])
+        rg = [graph_of(torch, lambda i=i: run_p(i)) for i in range(2)]
+        steady(torch, lambda: [r.replay() for r in rg], STEADY_S)
+        dt = timer(lambda i: rg[i % 2].replay(), 6)
+        rq[f"{mode}_to_fragment_order"] = {"us": round(dt * 1e6, 1), "gbps": round(requant_bytes(N, K) / dt / 1e9, 1),
+                                           "frac_of_hbm": round(requant_bytes(N, K) / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    rg = [graph_of(torch, lambda i=i: w4.mxfp4_prepare(outs[i % 2][0], outs[i % 2][1], out=pq[i % 2]))
+          for i in range(2)]
+    steady(torch, lambda: [r.replay() for r in rg], STEADY_S)
+    rq["repack_pass_us"] = round(timer(lambda i: rg[i % 2].replay(), 6) * 1e6, 1)
+    del pq
     res["requant_full_layer"] = rq
     log("requant", rq)
     # requant accuracy against the synthetic original (reported, not gated)

@@ -150,6 +150,35 @@ w4a8_status w4a8_quant_fp8ch_to_mxfp4(const uint8_t *d_w_e4m3, const float *d_ro
                                       uint8_t *d_mx_e8m0, double *d_err_stats, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The three load-time encoders above writing the GEMM's prepared layout
+ * directly (the matrix-core fragment order of w4a8_mxfp4_prepare), so that a
+ * checkpoint goes to the fast layout in one pass, with no row-major MXFP4 in
+ * between.  Source: "radiance_nvfp4.py", module docstring (the weight is
+ * requantized once at load, then handed to the fp8-WMMA GEMM, which reads
+ * fragment-order weights) and the three schemes'
+ * process_weights_after_loading.  Codes and e8m0 bytes are bit for bit those
+ * of w4a8_mxfp4_prepare applied to the row-major encoder's output (the same
+ * per-block rule), padding included (rows to 16, steps to a multiple of 4:
+ * code 0, e8m0 127).
+ *   arguments as the row-major encoders, K % 128 == 0 (else
+ *   UNSUPPORTED_SHAPE), n_parts <= 16; rows = the partitions' rows summed
+ *   d_w_prepared, d_s_prepared  out, sized by w4a8_mxfp4_prepared_bytes(rows,
+ *                 K), 16- and 4-byte aligned
+ * No statistics (the row-major entry points report them); no row chunking
+ * (it changes no output).  Inputs and outputs must not overlap.  Errors:
+ * INVALID_ARG, UNSUPPORTED_SHAPE, HIP. */
+w4a8_status w4a8_requant_nvfp4_to_mxfp4_prepared(const uint8_t *d_nv_packed, const uint8_t *d_nv_scale,
+                                                 const int64_t *h_part_rows, const float *h_part_divisor,
+                                                 int n_parts, int64_t K, w4a8_exp_mode mode,
+                                                 uint8_t *d_w_prepared, uint8_t *d_s_prepared, void *stream);
+w4a8_status w4a8_quant_bf16_to_mxfp4_prepared(const uint16_t *d_w_bf16, int64_t rows, int64_t K,
+                                              w4a8_exp_mode mode, uint8_t *d_w_prepared, uint8_t *d_s_prepared,
+                                              void *stream);
+w4a8_status w4a8_quant_fp8ch_to_mxfp4_prepared(const uint8_t *d_w_e4m3, const float *d_row_scale, int64_t rows,
+                                               int64_t K, w4a8_exp_mode mode, uint8_t *d_w_prepared,
+                                               uint8_t *d_s_prepared, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Dynamic per-token fp8 activation quantization.
  * Source: "radiance_autoround.py", autoround_linear (per-token dynamic e4m3
  * with one fp32 scale per row, consumed by the W4A8 GEMM).  The pages leave the

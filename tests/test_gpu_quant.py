@@ -272,3 +272,71 @@ def test_load_quant_rejects_bad_arguments():
         w4.quant_fp8ch_to_mxfp4(c, torch.ones(3, dtype=torch.float32, device="cuda"))
     with pytest.raises(ValueError):
         w4.quant_bf16_to_mxfp4(torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"), mode="nearest")
+
+
+# ---------------------------------------------------------------------------
+# the same encoders writing the GEMM's fragment order directly: bit for bit the
+# repack (w4a8_mxfp4_prepare) of the oracle's row-major codes and e8m0, padding
+# rows and steps included
+# ---------------------------------------------------------------------------
+
+def _repacked(codes, e8m0):
+    return w4.mxfp4_prepare(dev_u8(codes), dev_u8(e8m0))
+
+
+def _same_prepared(got, want, name):
+    gw, ww = host(got.w), host(want.w)
+    bad = np.argwhere(gw != ww)
+    assert bad.size == 0, (name, "codes", bad[:5])
+    gs, ws = host(got.s), host(want.s)
+    bad = np.argwhere(gs != ws)
+    assert bad.size == 0, (name, "e8m0", bad[:5])
+    assert (got.N, got.K) == (want.N, want.K)
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_requant_prepared_random_bytes(mode):
+    # 157 rows (a partial last tile), K of 5 steps (three padding steps), three
+    # partitions whose boundaries fall inside 16-row tiles, divisors from 1e-30
+    # to 3e38
+    d = _random_nvfp4(157, 640, 41, [2688.0, 3e38, 1e-30])
+    say("requant prepared", mode, d["part_rows"])
+    got = w4.requant_nvfp4_to_mxfp4_prepared(dev_u8(d["nv_packed"]), dev_u8(d["nv_scale"]), d["part_rows"],
+                                             d["part_divisor"], mode=mode)
+    rp, re_, _ = oracle.requant_nvfp4_to_mxfp4(d["nv_packed"], d["nv_scale"], d["part_rows"], d["part_divisor"],
+                                               mode=mode)
+    _same_prepared(got, _repacked(rp, re_), f"random {mode}")
+
+
+def test_requant_prepared_gate_up(gate_up_mx):
+    g = synth.gate_up()
+    say("requant prepared", "gate_up", g["nv_packed"].shape)
+    got = w4.requant_nvfp4_to_mxfp4_prepared(dev_u8(g["nv_packed"]), dev_u8(g["nv_scale"]), g["part_rows"],
+                                             g["part_divisor"], mode="mse")
+    _same_prepared(got, _repacked(gate_up_mx[0], gate_up_mx[1]), "gate_up")
+
+
+@pytest.mark.parametrize("mode", ["ocp", "noclip", "mse"])
+def test_load_quant_prepared_random(mode):
+    g = np.random.default_rng(42)
+    a = g.integers(0, 1 << 16, (257, 384)).astype(np.uint16)
+    a[(a & 0x7F80) == 0x7F80] &= 0xFF7F                           # no inf / NaN
+    say("bf16 prepared", mode, a.shape)
+    rp, re_, _ = oracle.quant_bf16_to_mxfp4(a, mode)
+    _same_prepared(w4.quant_bf16_to_mxfp4_prepared(dev_bf16(a), mode=mode), _repacked(rp, re_), f"bf16 {mode}")
+    c = g.integers(0, 256, (300, 640)).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E                                  # no NaN codes
+    s = np.exp2(g.uniform(-30, 20, 300)).astype(np.float32)
+    say("fp8ch prepared", mode, c.shape)
+    rp, re_, _ = oracle.quant_fp8ch_to_mxfp4(c, s, mode)
+    got = w4.quant_fp8ch_to_mxfp4_prepared(dev_u8(c), torch.from_numpy(s).cuda(), mode=mode)
+    _same_prepared(got, _repacked(rp, re_), f"fp8ch {mode}")
+
+
+def test_load_quant_prepared_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        w4.quant_bf16_to_mxfp4_prepared(torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda"))   # K % 128
+    p = torch.zeros((32, 64), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((32, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        w4.requant_nvfp4_to_mxfp4_prepared(p, s, [2] * 16 + [0], [1.0] * 17)                    # 17 partitions

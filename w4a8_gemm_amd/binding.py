@@ -23,7 +23,8 @@ __all__ = [
     "mxfp4_linear_prepared", "int4g128_linear_prepared",
     "PreparedInt4ZP", "int4g128_zp_prepare_fragments", "int4g128_zp_gemm_prepared",
     "PreparedInt5", "int5g128_prepare_fragments", "int5g128_gemm_prepared",
-    "mxfp4_gemm_prepared_noalloc",
+    "mxfp4_gemm_prepared_noalloc", "requant_nvfp4_to_mxfp4_prepared", "quant_bf16_to_mxfp4_prepared",
+    "quant_fp8ch_to_mxfp4_prepared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
@@ -64,6 +65,12 @@ def lib() -> ctypes.CDLL:
         L.w4a8_quant_bf16_to_mxfp4.restype = _int
         L.w4a8_quant_fp8ch_to_mxfp4.argtypes = [_vp, _vp, _i64, _i64, _int, _vp, _vp, _vp, _vp]
         L.w4a8_quant_fp8ch_to_mxfp4.restype = _int
+        L.w4a8_requant_nvfp4_to_mxfp4_prepared.argtypes = [_vp, _vp, _vp, _vp, _int, _i64, _int, _vp, _vp, _vp]
+        L.w4a8_requant_nvfp4_to_mxfp4_prepared.restype = _int
+        L.w4a8_quant_bf16_to_mxfp4_prepared.argtypes = [_vp, _i64, _i64, _int, _vp, _vp, _vp]
+        L.w4a8_quant_bf16_to_mxfp4_prepared.restype = _int
+        L.w4a8_quant_fp8ch_to_mxfp4_prepared.argtypes = [_vp, _vp, _i64, _i64, _int, _vp, _vp, _vp]
+        L.w4a8_quant_fp8ch_to_mxfp4_prepared.restype = _int
         L.w4a8_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
         L.w4a8_gemm_workspace_bytes.restype = _size
         L.w4a8_workspace_init.argtypes = [_vp, _size, _vp]
@@ -256,6 +263,77 @@ def quant_fp8ch_to_mxfp4(w8: torch.Tensor, row_scale: torch.Tensor, mode: str = 
     return (out_packed, out_e8m0, st) if stats else (out_packed, out_e8m0)
 
 
+def _prepared_outputs(rows, K, dev, mode, out=None):
+    if mode not in EXP_MODES:
+        raise ValueError(f"mode must be one of {sorted(EXP_MODES)}")
+    if K % 128:
+        raise ValueError("the prepared layout needs K % 128 == 0")
+    if out is not None:
+        if (out.N, out.K) != (rows, K):
+            raise ValueError(f"out holds a {out.N} x {out.K} weight, not {rows} x {K}")
+        _check_weight_sizes("prepared", out.w, out.s, rows, K)
+        return out.w, out.s
+    wb, sb = _size(), _size()
+    _check(lib().w4a8_mxfp4_prepared_bytes(rows, K, ctypes.byref(wb), ctypes.byref(sb)),
+           "w4a8_mxfp4_prepared_bytes")
+    return (torch.empty(wb.value, dtype=torch.uint8, device=dev),
+            torch.empty(sb.value, dtype=torch.uint8, device=dev))
+
+
+def requant_nvfp4_to_mxfp4_prepared(nv_packed: torch.Tensor, nv_scale: torch.Tensor, part_rows,
+                                    part_divisor, mode: str = "mse", out=None) -> "PreparedMXFP4":
+    """As requant_nvfp4_to_mxfp4, written straight into the GEMM's fragment
+    order (the bytes mxfp4_prepare makes of the row-major result); `out`: a
+    PreparedMXFP4 of the same shape to write into."""
+    _need(nv_packed, "nv_packed", torch.uint8)
+    _need(nv_scale, "nv_scale", torch.uint8, nv_packed.device)
+    if nv_packed.dim() != 2 or nv_scale.dim() != 2:
+        raise ValueError("nv_packed and nv_scale must be 2-D")
+    rows, half = nv_packed.shape
+    K = 2 * half
+    if tuple(nv_scale.shape) != (rows, K // 16) or not (nv_packed.is_contiguous() and nv_scale.is_contiguous()):
+        raise ValueError("nv_scale must be [rows, K/16], both contiguous")
+    if len(part_rows) != len(part_divisor) or sum(int(r) for r in part_rows) != rows:
+        raise ValueError("partition rows must add up to the rows, one divisor each")
+    pr = (ctypes.c_int64 * len(part_rows))(*[int(r) for r in part_rows])
+    pd = (ctypes.c_float * len(part_divisor))(*[float(d) for d in part_divisor])
+    wt, st = _prepared_outputs(rows, K, nv_packed.device, mode, out)
+    _check(lib().w4a8_requant_nvfp4_to_mxfp4_prepared(_ptr(nv_packed), _ptr(nv_scale), pr, pd, len(part_rows), K,
+                                                       EXP_MODES[mode], _ptr(wt), _ptr(st), _stream(nv_packed)),
+           "w4a8_requant_nvfp4_to_mxfp4_prepared")
+    return PreparedMXFP4(wt, st, rows, K)
+
+
+def quant_bf16_to_mxfp4_prepared(w: torch.Tensor, mode: str = "mse", out=None) -> "PreparedMXFP4":
+    """As quant_bf16_to_mxfp4, written straight into fragment order."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    rows, K = w.shape
+    wt, st = _prepared_outputs(rows, K, w.device, mode, out)
+    _check(lib().w4a8_quant_bf16_to_mxfp4_prepared(_ptr(w), rows, K, EXP_MODES[mode], _ptr(wt), _ptr(st),
+                                                    _stream(w)), "w4a8_quant_bf16_to_mxfp4_prepared")
+    return PreparedMXFP4(wt, st, rows, K)
+
+
+def quant_fp8ch_to_mxfp4_prepared(w8: torch.Tensor, row_scale: torch.Tensor, mode: str = "mse",
+                                  out=None) -> "PreparedMXFP4":
+    """As quant_fp8ch_to_mxfp4, written straight into fragment order."""
+    if isinstance(w8, torch.Tensor) and w8.dtype == torch.float8_e4m3fn:
+        w8 = w8.view(torch.uint8)
+    _need(w8, "w8", torch.uint8)
+    if w8.dim() != 2 or not w8.is_contiguous():
+        raise ValueError("w8 must be a contiguous 2-D tensor")
+    rows, K = w8.shape
+    _need(row_scale, "row_scale", torch.float32, w8.device)
+    if row_scale.numel() != rows or not row_scale.is_contiguous():
+        raise ValueError("row_scale must hold one contiguous fp32 scale per row")
+    wt, st = _prepared_outputs(rows, K, w8.device, mode, out)
+    _check(lib().w4a8_quant_fp8ch_to_mxfp4_prepared(_ptr(w8), _ptr(row_scale), rows, K, EXP_MODES[mode], _ptr(wt),
+                                                     _ptr(st), _stream(w8)), "w4a8_quant_fp8ch_to_mxfp4_prepared")
+    return PreparedMXFP4(wt, st, rows, K)
+
+
 # ---------------------------------------------------------------------------
 # run time
 # ---------------------------------------------------------------------------
@@ -432,19 +510,26 @@ class PreparedMXFP4:
         self.w, self.s, self.N, self.K = w, s, int(N), int(K)
 
 
-def mxfp4_prepare(w_packed: torch.Tensor, w_e8m0: torch.Tensor) -> PreparedMXFP4:
-    """[N, K/2] codes + [N, K/32] e8m0 -> PreparedMXFP4 (K % 128 == 0)."""
+def mxfp4_prepare(w_packed: torch.Tensor, w_e8m0: torch.Tensor, out: "PreparedMXFP4 | None" = None) -> PreparedMXFP4:
+    """[N, K/2] codes + [N, K/32] e8m0 -> PreparedMXFP4 (K % 128 == 0); `out`:
+    a PreparedMXFP4 of the same shape to write into."""
     _need(w_packed, "w_packed", torch.uint8)
     dev = w_packed.device
     _need(w_e8m0, "w_e8m0", torch.uint8, dev)
     N, K = w_packed.shape[0], 2 * w_packed.shape[1]
     if tuple(w_e8m0.shape) != (N, K // 32):
         raise ValueError("w_e8m0 must be [N, K/32]")
-    wb, sb = _size(), _size()
-    _check(lib().w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)),
-           "w4a8_mxfp4_prepared_bytes")
-    wt = torch.empty(wb.value, dtype=torch.uint8, device=dev)
-    st = torch.empty(sb.value, dtype=torch.uint8, device=dev)
+    if out is not None:
+        if (out.N, out.K) != (N, K):
+            raise ValueError(f"out holds a {out.N} x {out.K} weight, not {N} x {K}")
+        _check_weight_sizes("prepared", out.w, out.s, N, K)
+        wt, st = out.w, out.s
+    else:
+        wb, sb = _size(), _size()
+        _check(lib().w4a8_mxfp4_prepared_bytes(N, K, ctypes.byref(wb), ctypes.byref(sb)),
+               "w4a8_mxfp4_prepared_bytes")
+        wt = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+        st = torch.empty(sb.value, dtype=torch.uint8, device=dev)
     _check(lib().w4a8_mxfp4_prepare(_ptr(w_packed), _ptr(w_e8m0), N, K, _ptr(wt), _ptr(st),
                                     _stream(w_packed)), "w4a8_mxfp4_prepare")
     return PreparedMXFP4(wt, st, N, K)

@@ -122,6 +122,60 @@ w4a8_status w4a8_quant_fp8ch_to_mxfp4(const uint8_t* d_w_e4m3, const float* d_ro
                       stream);
 }
 
+// ---- the load-time encoders writing fragment order directly ----
+static w4a8_status check_prepared_out(int64_t rows, int64_t K, w4a8_exp_mode mode, uint8_t* d_w_prepared,
+                                      uint8_t* d_s_prepared) {
+    if (!d_w_prepared || !d_s_prepared) return W4A8_ERR_INVALID_ARG;
+    if (rows < 0 || rows > kMaxDim || K < 1 || K > kMaxDim) return W4A8_ERR_INVALID_ARG;
+    if (mode != W4A8_EXP_OCP && mode != W4A8_EXP_NOCLIP && mode != W4A8_EXP_MSE) return W4A8_ERR_INVALID_ARG;
+    if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(d_w_prepared, 16) || !aligned(d_s_prepared, 4)) return W4A8_ERR_INVALID_ARG;
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_requant_nvfp4_to_mxfp4_prepared(const uint8_t* d_nv_packed, const uint8_t* d_nv_scale,
+                                                 const int64_t* h_part_rows, const float* h_part_divisor,
+                                                 int n_parts, int64_t K, w4a8_exp_mode mode,
+                                                 uint8_t* d_w_prepared, uint8_t* d_s_prepared, void* stream) {
+    if (!d_nv_packed || !d_nv_scale || !h_part_rows || !h_part_divisor) return W4A8_ERR_INVALID_ARG;
+    if (n_parts < 1 || n_parts > requant_max_parts()) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(d_nv_packed, 16) || !aligned(d_nv_scale, 2)) return W4A8_ERR_INVALID_ARG;
+    int64_t rows = 0, blocks[64];
+    for (int p = 0; p < n_parts; ++p) {
+        const float gd = h_part_divisor[p];
+        if (h_part_rows[p] < 0 || h_part_rows[p] > kMaxDim) return W4A8_ERR_INVALID_ARG;
+        if (!(gd > 0.0f) || !isfinite(gd)) return W4A8_ERR_INVALID_ARG;
+        rows += h_part_rows[p];
+        blocks[p] = h_part_rows[p] * (K / 32);
+    }
+    const w4a8_status st = check_prepared_out(rows, K, mode, d_w_prepared, d_s_prepared);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_requant_prepared(d_nv_packed, d_nv_scale, blocks, h_part_divisor, n_parts, rows, K,
+                                              (int)mode, d_w_prepared, d_s_prepared, as_stream(stream)));
+}
+
+w4a8_status w4a8_quant_bf16_to_mxfp4_prepared(const uint16_t* d_w_bf16, int64_t rows, int64_t K,
+                                              w4a8_exp_mode mode, uint8_t* d_w_prepared, uint8_t* d_s_prepared,
+                                              void* stream) {
+    if (!d_w_bf16 || !aligned(d_w_bf16, 16)) return W4A8_ERR_INVALID_ARG;
+    const w4a8_status st = check_prepared_out(rows, K, mode, d_w_prepared, d_s_prepared);
+    if (st != W4A8_OK) return st;
+    return hip_status(launch_quant_bf16_prepared(d_w_bf16, rows, K, (int)mode, d_w_prepared, d_s_prepared,
+                                                 as_stream(stream)));
+}
+
+w4a8_status w4a8_quant_fp8ch_to_mxfp4_prepared(const uint8_t* d_w_e4m3, const float* d_row_scale, int64_t rows,
+                                               int64_t K, w4a8_exp_mode mode, uint8_t* d_w_prepared,
+                                               uint8_t* d_s_prepared, void* stream) {
+    if (!d_w_e4m3 || !d_row_scale || !aligned(d_w_e4m3, 16) || !aligned(d_row_scale, 4))
+        return W4A8_ERR_INVALID_ARG;
+    const w4a8_status st = check_prepared_out(rows, K, mode, d_w_prepared, d_s_prepared);
+    if (st != W4A8_OK) return st;
+    if (rows * (K / 32) >= ((int64_t)1 << 32)) return W4A8_ERR_UNSUPPORTED_SHAPE;   // 32-bit block index
+    return hip_status(launch_quant_fp8ch_prepared(d_w_e4m3, d_row_scale, rows, K, (int)mode, d_w_prepared,
+                                                  d_s_prepared, as_stream(stream)));
+}
+
 w4a8_status w4a8_quant_act_fp8_per_token(const uint16_t* d_x_bf16, int64_t M, int64_t K,
                                          int64_t ldx, uint8_t* d_x_fp8, float* d_x_scale,
                                          void* stream) {

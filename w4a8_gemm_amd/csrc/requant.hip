@@ -211,18 +211,16 @@ __device__ __forceinline__ void decode_block(const Raw<IN>& r, float divisor, fl
     }
 }
 
-// One block: the exponent by the rule, the codes, the e8m0 byte; the chosen
+// One block: the exponent by the rule (returned) and the codes; the chosen
 // error and the sum of squares go into the lane's statistics.
 template <int IN, int MODE, bool STATS>
-__device__ __forceinline__ void requant_block(const Raw<IN>& r, float divisor, int64_t b,
-                                              uint4* __restrict__ out_packed, uint8_t* __restrict__ out_e8m0,
+__device__ __forceinline__ int requant_encode(const Raw<IN>& r, float divisor, uint32_t (&code)[4],
                                               double& err_sum, double& ssq_sum) {
     float w[32];
     decode_block<IN>(r, divisor, w);
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(w[j]));
-    uint32_t code[4];
     int e;
     float err;
     if (MODE == W4A8_EXP_MSE) {
@@ -243,13 +241,23 @@ __device__ __forceinline__ void requant_block(const Raw<IN>& r, float divisor, i
         e = block_exponent(amax, MODE);
         err = encode_block<STATS>(w, e, code);
     }
-    out_packed[b] = make_uint4(code[0], code[1], code[2], code[3]);
-    out_e8m0[b] = (uint8_t)(e + 127);
     if (STATS) {
         err_sum += (double)err;
 #pragma unroll
         for (int j = 0; j < 32; ++j) ssq_sum += (double)w[j] * (double)w[j];
     }
+    return e;
+}
+
+// ... stored at block b of the row-major outputs
+template <int IN, int MODE, bool STATS>
+__device__ __forceinline__ void requant_block(const Raw<IN>& r, float divisor, int64_t b,
+                                              uint4* __restrict__ out_packed, uint8_t* __restrict__ out_e8m0,
+                                              double& err_sum, double& ssq_sum) {
+    uint32_t code[4];
+    const int e = requant_encode<IN, MODE, STATS>(r, divisor, code, err_sum, ssq_sum);
+    out_packed[b] = make_uint4(code[0], code[1], code[2], code[3]);
+    out_e8m0[b] = (uint8_t)(e + 127);
 }
 
 template <int IN, int MODE, bool STATS>
@@ -315,6 +323,53 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(QuantIn in, uint4* __
 }
 static_assert(kIters % 2 == 0, "the loop above takes iterations in pairs");
 
+// The same encoder writing the matrix-core fragment order of the GEMM's
+// prepared weights directly (the layout the load-time repack writes from the
+// row-major arrays): one wave per 16-row tile t and 4-step chunk c, lane
+// L = n + 16 g on row 16 t + n and K-blocks 4 s + g of the chunk's steps s.
+// Each step's 16 code bytes go to lane L's slot of the tile's 1 KiB block for
+// that step, the four e8m0 bytes to lane L's dword of the chunk's 256-byte
+// record (byte u: step 4 c + u), so a wave stores whole 1 KiB and 256-byte
+// runs.  Rows past the weight and steps past K are padding: code 0 and e8m0
+// 127 (the repack's).  The partition (divisor) is the row's; no statistics.
+template <int IN, int MODE>
+__global__ __launch_bounds__(kThreads) void requant_frag_kernel(QuantIn in, int64_t rows, int64_t K, int64_t tiles,
+                                                                int c_pad, uint4* __restrict__ wt,
+                                                                uint32_t* __restrict__ st) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (unit >= tiles * c_pad) return;
+    const int64_t t = unit / c_pad;
+    const int c = (int)(unit - t * c_pad);
+    const int64_t row = 16 * t + (lane & 15);
+    const int g = lane >> 4, steps = (int)(K / 128);
+    const int64_t bpr = K / 32;
+    float divisor = 1.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i)
+        if (i < in.n_parts && row * bpr >= in.part_begin[i]) divisor = in.divisor[i];
+    // the chunk's four blocks loaded before any is encoded (block 0 for padding)
+    Raw<IN> r[4];
+    bool real[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int s = 4 * c + j;
+        real[j] = row < rows && s < steps;
+        load_raw<IN>(in, real[j] ? row * bpr + 4 * s + g : 0, r[j]);
+    }
+    double none = 0.0;
+    uint32_t e8 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t code[4] = {0u, 0u, 0u, 0u};
+        uint32_t byte = 127u;
+        if (real[j]) byte = (uint32_t)(requant_encode<IN, MODE, false>(r[j], divisor, code, none, none) + 127);
+        wt[(t * 4 * c_pad + 4 * c + j) * 64 + lane] = make_uint4(code[0], code[1], code[2], code[3]);
+        e8 |= byte << (8 * j);
+    }
+    st[(t * c_pad + c) * 64 + lane] = e8;
+}
+
 __global__ void fill_zero_f64(double* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0.0;
@@ -350,6 +405,26 @@ hipError_t launch_in(const QuantIn& in, int mode, uint8_t* mx_packed, uint8_t* m
         default:
             return launch_mode<IN, W4A8_EXP_MSE>(in, mx_packed, mx_e8m0, stats, stream);
     }
+}
+
+template <int IN>
+hipError_t launch_frag(const QuantIn& in, int mode, int64_t rows, int64_t K, uint8_t* wt, uint8_t* st,
+                       hipStream_t stream) {
+    const int64_t tiles = (rows + 15) / 16, c_pad = (K / 128 + 3) / 4;
+    const int64_t grid = (tiles * c_pad + kThreads / 64 - 1) / (kThreads / 64);
+    if (grid <= 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    uint4* w = reinterpret_cast<uint4*>(wt);
+    uint32_t* s = reinterpret_cast<uint32_t*>(st);
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (mode == W4A8_EXP_OCP)
+        hipLaunchKernelGGL((requant_frag_kernel<IN, W4A8_EXP_OCP>), g, b, 0, stream, in, rows, K, tiles, (int)c_pad, w, s);
+    else if (mode == W4A8_EXP_NOCLIP)
+        hipLaunchKernelGGL((requant_frag_kernel<IN, W4A8_EXP_NOCLIP>), g, b, 0, stream, in, rows, K, tiles, (int)c_pad, w,
+                           s);
+    else
+        hipLaunchKernelGGL((requant_frag_kernel<IN, W4A8_EXP_MSE>), g, b, 0, stream, in, rows, K, tiles, (int)c_pad, w, s);
+    return hipGetLastError();
 }
 
 // the launch table of partitions 0..n-1 with cnt[i] blocks each
@@ -399,6 +474,43 @@ hipError_t launch_quant_fp8ch(const uint8_t* w, const float* row_scale, int64_t 
     const int64_t n = rows * (K / 32);
     plan_parts(in, &n, nullptr, 1);
     return launch_in<kInFp8Ch>(in, mode, mx_packed, mx_e8m0, stats, stream);
+}
+
+// the three load-time encoders writing fragment order (K % 128 == 0; at most
+// requant_max_parts() partitions in one launch)
+hipError_t launch_requant_prepared(const uint8_t* nv_packed, const uint8_t* nv_scale, const int64_t* part_blocks,
+                                   const float* part_divisor, int n_parts, int64_t rows, int64_t K, int mode,
+                                   uint8_t* wt, uint8_t* st, hipStream_t stream) {
+    if (n_parts < 1 || n_parts > kMaxParts || K % 128 != 0) return hipErrorInvalidValue;
+    QuantIn in{};
+    in.data = nv_packed;
+    in.aux = nv_scale;
+    in.blocks_per_row = 1;
+    plan_parts(in, part_blocks, part_divisor, n_parts);
+    return launch_frag<kInNvfp4>(in, mode, rows, K, wt, st, stream);
+}
+
+hipError_t launch_quant_bf16_prepared(const uint16_t* w, int64_t rows, int64_t K, int mode, uint8_t* wt,
+                                      uint8_t* st, hipStream_t stream) {
+    if (K % 128 != 0) return hipErrorInvalidValue;
+    QuantIn in{};
+    in.data = reinterpret_cast<const uint8_t*>(w);
+    in.blocks_per_row = K / 32;
+    const int64_t n = rows * (K / 32);
+    plan_parts(in, &n, nullptr, 1);
+    return launch_frag<kInBf16>(in, mode, rows, K, wt, st, stream);
+}
+
+hipError_t launch_quant_fp8ch_prepared(const uint8_t* w, const float* row_scale, int64_t rows, int64_t K, int mode,
+                                       uint8_t* wt, uint8_t* st, hipStream_t stream) {
+    if (K % 128 != 0) return hipErrorInvalidValue;
+    QuantIn in{};
+    in.data = w;
+    in.aux = row_scale;
+    in.blocks_per_row = K / 32;
+    const int64_t n = rows * (K / 32);
+    plan_parts(in, &n, nullptr, 1);
+    return launch_frag<kInFp8Ch>(in, mode, rows, K, wt, st, stream);
 }
 
 hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream) {

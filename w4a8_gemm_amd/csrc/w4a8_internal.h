@@ -129,6 +129,15 @@ hipError_t launch_quant_bf16(const uint16_t* w, int64_t rows, int64_t K, int mod
                              uint8_t* mx_e8m0, double* stats, hipStream_t stream);
 hipError_t launch_quant_fp8ch(const uint8_t* w, const float* row_scale, int64_t rows, int64_t K, int mode,
                               uint8_t* mx_packed, uint8_t* mx_e8m0, double* stats, hipStream_t stream);
+// the same encoders writing the fragment order of w4a8_mxfp4_prepare directly
+// (K % 128 == 0; wt / st sized by prepared_sizes(rows, K); no statistics)
+hipError_t launch_requant_prepared(const uint8_t* nv_packed, const uint8_t* nv_scale, const int64_t* part_blocks,
+                                   const float* part_divisor, int n_parts, int64_t rows, int64_t K, int mode,
+                                   uint8_t* wt, uint8_t* st, hipStream_t stream);
+hipError_t launch_quant_bf16_prepared(const uint16_t* w, int64_t rows, int64_t K, int mode, uint8_t* wt,
+                                      uint8_t* st, hipStream_t stream);
+hipError_t launch_quant_fp8ch_prepared(const uint8_t* w, const float* row_scale, int64_t rows, int64_t K, int mode,
+                                       uint8_t* wt, uint8_t* st, hipStream_t stream);
 hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream);
 hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 
