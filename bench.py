@@ -65,11 +65,11 @@ N_GU, K_GU = 34816, 5120
 STEP_KERNELS = {
     1: [("spread_kernel<1, 2, 4, true, false, true>",
          "spread tiles, per-token quant fused in the prologue (the quantized row resident in LDS)")],
-    8: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
+    8: [("act_quant_split_kernel<4>", "per-token fp8 quant (each row split over 3 workgroups)"),
         ("spread_kernel<1, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
-    16: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
+    16: [("act_quant_split_kernel<4>", "per-token fp8 quant (each row split over 3 workgroups)"),
          ("spread_kernel<1, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
-    64: [("act_quant_reg_kernel<4>", "per-token fp8 quant"),
+    64: [("act_quant_split_kernel<4>", "per-token fp8 quant (each row split over 3 workgroups)"),
          ("spread_kernel<4, 2, 4, true, false, false>", "spread tiles: one workgroup per CU over all of K, e8m0 per chunk")],
 }
 SOURCES = {"gemm": os.path.join(HERE, "w4a8_gemm_amd", "csrc", "gemm_prepared.hip"),

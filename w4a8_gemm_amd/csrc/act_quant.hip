@@ -5,12 +5,14 @@
 // arithmetic to a library op; the plain reading used here:
 //   s = amax_k |x[m,k]| / 448   (1 for an all-zero row)
 //   code = e4m3 round-to-nearest-even of x / s, saturating at 448, sign kept.
-// One workgroup per row.  Rows of up to 256 * 8 * 16 elements (and 16-byte
-// aligned) are read once into registers -- every load issued before the first
-// use, so the row costs one memory latency -- then the block max (wavefront
-// butterfly, then LDS across the four waves) and the divide-and-encode from
-// registers.  Longer or unaligned rows take a two-pass form that re-reads the
-// row from L2.
+// Rows of up to 256 * 8 * 16 elements (and 16-byte aligned) are split over
+// ceil(K / 8 / 256) workgroups when the rows are fewer than the CUs (else one
+// workgroup per row): each reads the whole row once into registers
+// -- every load issued before the first use, so the row costs one memory
+// latency -- takes the block max (wavefront butterfly, then LDS across the
+// four waves) and divides and encodes its share of the row from registers.
+// Longer or unaligned rows take a two-pass form, one workgroup per row, that
+// re-reads the row from L2.
 #include "w4a8_internal.h"
 
 #pragma clang fp contract(off)
@@ -81,23 +83,26 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
     }
 }
 
-// single pass: the row in registers, R uint4 (8 bf16 each) per thread; with
-// x8s the codes also go step-major ([K/128][M][128]: the 128-wide steps of all
-// rows one after the other, the layout the wide-layer decode tiles stage from)
+// Rows split over S workgroups (S = ceil(items / threads), so that a thread
+// encodes at most one 8-value item): every workgroup of a row reads the whole
+// row for its amax (all loads issued before the first use), then encodes only
+// its share of the items, [n8 c / S, n8 (c + 1) / S); the row's first
+// workgroup writes the scale.  The divide-and-encode of a row, about 25
+// vector instructions per value, is then spread over S CUs instead of one.
 template <int R>
-__global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint16_t* __restrict__ x, int64_t K,
-                                                                 int64_t ldx, uint8_t* __restrict__ x8,
-                                                                 float* __restrict__ xs,
-                                                                 uint8_t* __restrict__ x8s) {
-    const int64_t m = blockIdx.x;
+__global__ __launch_bounds__(kThreads) void act_quant_split_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                                   int64_t ldx, uint8_t* __restrict__ x8,
+                                                                   float* __restrict__ xs,
+                                                                   uint8_t* __restrict__ x8s, int S, int M) {
+    const int64_t m = blockIdx.x / S;
+    const int c = (int)(blockIdx.x - m * S);
     const uint4* r4 = reinterpret_cast<const uint4*>(x + m * ldx);
-    uint2* o2 = reinterpret_cast<uint2*>(x8 + m * K);
     const int n8 = (int)(K / 8);
     uint4 v[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int c = threadIdx.x + kThreads * i;
-        v[i] = c < n8 ? r4[c] : make_uint4(0, 0, 0, 0);
+        const int it = threadIdx.x + kThreads * i;
+        v[i] = it < n8 ? r4[it] : make_uint4(0, 0, 0, 0);
     }
     float amax = 0.0f;
 #pragma unroll
@@ -111,24 +116,50 @@ __global__ __launch_bounds__(kThreads) void act_quant_reg_kernel(const uint16_t*
     }
     amax = block_max(amax);
     const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division
-    if (threadIdx.x == 0) xs[m] = s;
+    if (c == 0 && threadIdx.x == 0) xs[m] = s;
+    const int lo = (int)((int64_t)n8 * c / S), hi = (int)((int64_t)n8 * (c + 1) / S);
+    uint2* o2 = reinterpret_cast<uint2*>(x8 + m * K);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int c = threadIdx.x + kThreads * i;
-        if (c >= n8) continue;
+        const int it = threadIdx.x + kThreads * i;
+        if (it < lo || it >= hi) continue;
         const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
         uint32_t o[2] = {0u, 0u};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] & 0xFFFFu) / s);
-            const uint32_t hi = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] >> 16) / s);
-            o[q >> 1] |= (lo | (hi << 8)) << (16 * (q & 1));
+            const uint32_t l = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] & 0xFFFFu) / s);
+            const uint32_t h = f32_to_e4m3_rne_sat(bf16_to_f32(d[q] >> 16) / s);
+            o[q >> 1] |= (l | (h << 8)) << (16 * (q & 1));
         }
-        o2[c] = make_uint2(o[0], o[1]);
+        o2[it] = make_uint2(o[0], o[1]);
         if (x8s)
-            *reinterpret_cast<uint2*>(x8s + (int64_t)(c >> 4) * 128 * gridDim.x + 128 * m + 8 * (c & 15)) =
+            *reinterpret_cast<uint2*>(x8s + (int64_t)(it >> 4) * 128 * M + 128 * m + 8 * (it & 15)) =
                 make_uint2(o[0], o[1]);
     }
+}
+
+// fewer rows than CUs: each split over S workgroups; more: one workgroup per
+// row (each workgroup re-reads its whole row, so a split would multiply the
+// HBM reads of a prefill-sized launch)
+template <int R>
+hipError_t launch_split(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8, float* xs, uint8_t* x8s,
+                        hipStream_t stream) {
+    const int S = M < 256 ? (int)((K / 8 + kThreads - 1) / kThreads) : 1;
+    if (M * S > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(act_quant_split_kernel<R>, dim3((unsigned)(M * S)), dim3(kThreads), 0, stream, x, K, ldx, x8,
+                       xs, x8s, S, (int)M);
+    return hipGetLastError();
+}
+
+// the single-pass rows
+hipError_t launch_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8, float* xs, uint8_t* x8s,
+                       hipStream_t stream) {
+    const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;   // uint4 per thread
+    if (per_thread <= 1) return launch_split<1>(x, M, K, ldx, x8, xs, x8s, stream);
+    if (per_thread <= 2) return launch_split<2>(x, M, K, ldx, x8, xs, x8s, stream);
+    if (per_thread <= 4) return launch_split<4>(x, M, K, ldx, x8, xs, x8s, stream);
+    if (per_thread <= 8) return launch_split<8>(x, M, K, ldx, x8, xs, x8s, stream);
+    return launch_split<16>(x, M, K, ldx, x8, xs, x8s, stream);
 }
 
 }  // namespace
@@ -139,12 +170,7 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
                      ((uintptr_t)x8 % 8 == 0);
     const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;   // uint4 per thread
     if (vec && per_thread <= 16) {
-        const dim3 g((unsigned)M), b(kThreads);
-        if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
-        else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
-        else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
-        else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
-        else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs, nullptr);
+        return launch_rows(x, M, K, ldx, x8, xs, nullptr, stream);
     } else if (vec)
         hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(kThreads), 0, stream, x,
                            K, ldx, x8, xs);
@@ -162,14 +188,7 @@ bool act_quant_sm_fits(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
 hipError_t launch_act_quant_sm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* x8, float* xs,
                                uint8_t* x8s, hipStream_t stream) {
     if (!act_quant_sm_fits(x, M, K, ldx, x8) || !x8s || (uintptr_t)x8s % 16 != 0) return hipErrorInvalidValue;
-    const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;
-    const dim3 g((unsigned)M), b(kThreads);
-    if (per_thread <= 1) hipLaunchKernelGGL(act_quant_reg_kernel<1>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
-    else if (per_thread <= 2) hipLaunchKernelGGL(act_quant_reg_kernel<2>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
-    else if (per_thread <= 4) hipLaunchKernelGGL(act_quant_reg_kernel<4>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
-    else if (per_thread <= 8) hipLaunchKernelGGL(act_quant_reg_kernel<8>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
-    else hipLaunchKernelGGL(act_quant_reg_kernel<16>, g, b, 0, stream, x, K, ldx, x8, xs, x8s);
-    return hipGetLastError();
+    return launch_rows(x, M, K, ldx, x8, xs, x8s, stream);
 }
 
 }  // namespace w4a8
