@@ -209,7 +209,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill/requant/variant loops")
     ap.add_argument("--cpu-rows", type=int, default=34816, help="weight rows in the all-threads oracle sample")
-    ap.add_argument("--pmc-probe", choices=["decode", "prefill", "requant"],
+    ap.add_argument("--pmc-probe", choices=["decode", "prefill", "requant", "tiles"],
                     help="only the launches a counter record is read on (run under rocprofv3 --pmc): a 1 GiB "
                          "device copy (calibration), then the kernel of interest")
     ap.add_argument("--probe-m", type=int, default=64, help="decode probe: the step's M whose GEMM is probed")
@@ -219,7 +219,7 @@ def main():
     ap.add_argument("--pmc-summarize", nargs="+", metavar="ARG",
                     help="KIND DIR [DIR ...]: turn rocprofv3 --pmc output directories into a record under "
                          "profiles/ (decode: FETCH_SIZE dir, WRITE_SIZE dir; prefill: the SQ/GRBM dir; "
-                         "requant: FETCH_SIZE dir, WRITE_SIZE dir, SQ/GRBM dir)")
+                         "requant and tiles: FETCH_SIZE dir, WRITE_SIZE dir, SQ/GRBM dir)")
     args = ap.parse_args()
     if args.trace_summarize:
         trace_summarize(args.trace_summarize)
@@ -242,7 +242,7 @@ def main():
     timer = Timer(torch)
     log = lambda *m: print("[bench]", *m, file=sys.stderr, flush=True)
 
-    if args.pmc_probe in ("prefill", "requant"):
+    if args.pmc_probe in ("prefill", "requant", "tiles"):
         pmc_probe_other(args.pmc_probe, torch, w4, synth, dev, log)
         return
 
@@ -396,6 +396,44 @@ def pmc_probe_other(kind, torch, w4, synth, dev, log):
         o = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
         for _ in range(4):
             w4.mxfp4_gemm_prepared(x8, xs, pw, out=o)
+    elif kind == "tiles":
+        # the W4A4 tiles (gate_up M = 4096), then the int4 and int5 tiles
+        # (down_proj shape, M = 2048), four launches each
+        g = synth.gate_up()
+        N, K = g["N"], g["K"]
+        wp, we = w4.requant_nvfp4_to_mxfp4(torch.from_numpy(g["nv_packed"]).to(dev),
+                                           torch.from_numpy(g["nv_scale"]).to(dev), g["part_rows"],
+                                           g["part_divisor"], mode="mse")
+        pw = w4.mxfp4_prepare(wp, we)
+        del wp, we
+        xb = torch.from_numpy(synth.acts(4096, K, seed=3).view(np.int16)).view(torch.bfloat16).to(dev)
+        xa4, xe4 = w4.quant_act_mxfp4(xb)
+        o = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(4):
+            w4.w4a4_gemm_prepared(xa4, xe4, pw, out=o)
+        torch.cuda.synchronize()
+        del pw, xb, xa4, xe4, o
+
+        def dv(a, half=False):
+            t = torch.from_numpy(a.view(np.int16) if half else a)
+            return (t.view(torch.float16) if half else t).to(dev)
+
+        for q, prep, gemm, kind_ws in (
+                (synth.int4(), lambda q: w4.int4g128_prepare_fragments(dv(q["qweight_kn"]), dv(q["qzeros"]),
+                                                                       dv(q["scales"], True)),
+                 w4.int4g128_gemm_prepared, "int4_prepared"),
+                (synth.int5(), lambda q: w4.int5g128_prepare_fragments(dv(q["qweight_kn"]), dv(q["qweight_hi"]),
+                                                                       dv(q["qzeros"]), dv(q["scales"], True)),
+                 w4.int5g128_gemm_prepared, "int5_prepared")):
+            pq = prep(q)
+            ws = w4.Workspace(2048, q["N"], q["K"], kind_ws, dev)
+            xb = torch.from_numpy(synth.acts(2048, q["K"], seed=(4, 2048)).view(np.int16)).view(torch.bfloat16).to(dev)
+            a8, asc = w4.quant_act_fp8_per_token(xb)
+            oo = torch.empty((2048, q["N"]), dtype=torch.bfloat16, device=dev)
+            for _ in range(4):
+                gemm(a8, asc, pq, out=oo, workspace=ws)
+            torch.cuda.synchronize()
+            del pq, ws, xb, a8, asc, oo
     else:
         g = synth.gate_up()
         src = [(torch.from_numpy(g["nv_packed"]).to(dev), torch.from_numpy(g["nv_scale"]).to(dev))]
@@ -569,6 +607,8 @@ def pmc_summarize(kind, dirs, probe_m):
             f"mfma_busy_frac: {util:.4f}",
             f"kernel_source_sha256: {_source_hash(SOURCES['gemm'])}",
         ]
+    elif kind == "tiles":
+        lines, path = _tiles_record(dirs)
     else:
         f = _per_dispatch(dirs[0], ["FETCH_SIZE"])["FETCH_SIZE"]
         w = _per_dispatch(dirs[1], ["WRITE_SIZE"])["WRITE_SIZE"]
@@ -616,6 +656,81 @@ def pmc_summarize(kind, dirs, probe_m):
     print("\n".join(lines))
 
 
+TILE_SQ = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_LDS",
+           "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+# (key, kernel name pattern, what, M, N, K, code bits, MFMA busy cycles at the instruction's dense rate)
+TILE_KERNELS = [
+    ("w4a4", r"^pfa_kernel<256, 256, \d+>$", "W4A4 tiles, gate_up M = 4096", 4096, 34816, 5120, 4, 16),
+    ("int4", r"^pf_kernel<256, \d+, \d+, 1>$", "int4 g128 tiles, down_proj shape M = 2048", 2048, 5120, 17408, 4, 32),
+    ("int5", r"^pf_kernel<256, \d+, \d+, 4>$", "int5 g128 tiles, down_proj shape M = 2048", 2048, 5120, 17408, 5, 32),
+]
+
+
+def _tiles_record(dirs):
+    """Counter record of the three tile kernels of the tiles probe: MFMA
+    busy, vector-ALU busy and HBM bytes per launch."""
+    import re
+    f = _per_dispatch(dirs[0], ["FETCH_SIZE"])["FETCH_SIZE"]
+    w = _per_dispatch(dirs[1], ["WRITE_SIZE"])["WRITE_SIZE"]
+    c = _per_dispatch(dirs[2], TILE_SQ)
+    fs, ws = _calib_scale(f), _calib_scale(w)
+
+    def mean(recs, rx):
+        v = [x for n, g, x in recs if re.match(rx, _short(n))]
+        if not v:
+            raise SystemExit(f"no dispatch matching {rx}")
+        return sum(v) / len(v), len(v), next(_short(n) for n, g, x in recs if re.match(rx, _short(n)))
+
+    cmd = "-f csv -o run -- python3 -u bench.py --pmc-probe tiles"
+    lines = [
+        "# Counter record of the prefill tile kernels: W4A4 (gate_up M = 4096), int4 and int5 g128 "
+        "(down_proj shape M = 2048)",
+        "",
+        "Commands (repository root, one MI355X; $OUT is an output directory):",
+        "",
+        f"    rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_tl_fetch {cmd}",
+        f"    rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_tl_write {cmd}",
+        f"    rocprofv3 --pmc {' '.join(TILE_SQ)} -d $OUT/pmc_tl_sq {cmd}",
+        "    python3 bench.py --pmc-summarize tiles $OUT/pmc_tl_fetch $OUT/pmc_tl_write $OUT/pmc_tl_sq",
+        "",
+        f"Calibration scales: FETCH_SIZE {fs:.4f}, WRITE_SIZE {ws:.4f} (counter bytes per byte of a plain copy).",
+        "Busy fractions are per SIMD over the dispatch: MFMA = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs "
+        "x SIMDs); VALU = SQ_ACTIVE_INST_VALU x 4 / SIMDs / (GRBM_GUI_ACTIVE / XCDs). Ideal MFMA cycles = the "
+        "GEMM's 16x16x128 products x their dense issue cycles (16 fp4 x fp4, 32 fp8 x fp8), over the same "
+        "denominator: the fraction of the matrix peak the launch reaches. Algorithmic bytes = weight codes and "
+        "scales, activations and their scales in, bf16 out (split-K partials are not counted). "
+        "SQ_ACTIVE_INST_LDS and SQ_LDS_BANK_CONFLICT are collected but not reported: on the W4A4 tiles both "
+        "read the same value, on the int4 / int5 tiles the conflict count exceeds the LDS-active count, so "
+        "their ratio is no conflict share.",
+        "",
+        "| kernel | dispatches | MFMA busy | of matrix peak | VALU busy | VALU instr. per MFMA "
+        "| HBM bytes per launch | ratio to algorithmic |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    keys = []
+    for key, rx, what, M, N, K, bits, cyc in TILE_KERNELS:
+        gui, nd, name = mean(c["GRBM_GUI_ACTIVE"], rx)
+        mb = mean(c["SQ_VALU_MFMA_BUSY_CYCLES"], rx)[0]
+        va = mean(c["SQ_ACTIVE_INST_VALU"], rx)[0]
+        vi = mean(c["SQ_INSTS_VALU"], rx)[0]
+        traffic = mean(f, rx)[0] * 1024 / fs + mean(w, rx)[0] * 1024 / ws
+        if key == "w4a4":
+            algo = N * K // 2 + N * K // 32 + M * K // 2 + M * K // 32 + 2 * M * N
+        else:
+            algo = N * K * bits // 8 + N * K // 64 + M * K + 4 * M + 2 * M * N
+        mfmas = M * N * K / (16 * 16 * 128)
+        denom = gui / XCDS * SIMDS
+        busy, peak = mb / denom, mfmas * cyc / denom
+        valu = va * 4 / SIMDS / (gui / XCDS)
+        vpm = vi / mfmas
+        lines.append(f"| {name} ({what}) | {nd} | {busy:.3f} | {peak:.3f} | {valu:.3f} | {vpm:.1f} | "
+                     f"{traffic:.4g} | {traffic / algo:.2f} |")
+        keys += [f"mfma_busy_{key}: {busy:.4f}", f"peak_frac_{key}: {peak:.4f}", f"valu_busy_{key}: {valu:.4f}",
+                 f"traffic_bytes_{key}: {int(round(traffic))}"]
+    lines += [""] + keys + [f"kernel_source_sha256: {_source_hash(SOURCES['gemm'])}"]
+    return lines, os.path.join(PROFILES, "tile_kernels_prefill_counters.md")
+
+
 # ---------------------------------------------------------------------------
 # extra measurements
 # ---------------------------------------------------------------------------
@@ -647,8 +762,20 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
     steady(torch, lambda: w4.quant_act_mxfp4(xb), STEADY_S)
     aq4 = timer(lambda i: w4.quant_act_mxfp4(xb), 5)
     dt4 = _timed_graph(torch, timer, [lambda r=r: w4.w4a4_gemm_prepared(xa4, xe4, pcopies[r], out=o) for r in range(4)], 5)
+    tiles_rec = read_record(os.path.join(PROFILES, "tile_kernels_prefill_counters.md"),
+                            [f"{f}_{k}" for f in ("mfma_busy", "valu_busy", "traffic_bytes") for k in
+                             ("w4a4", "int4", "int5")], SOURCES["gemm"]) or {}
+
+    def counters(key):
+        # the committed counter record of the family's prefill tile kernel (None once the source has changed)
+        if f"mfma_busy_{key}" not in tiles_rec:
+            return None
+        return {"kernel_mfma_busy": tiles_rec[f"mfma_busy_{key}"], "kernel_valu_busy": tiles_rec[f"valu_busy_{key}"],
+                "kernel_hbm_bytes": int(tiles_rec[f"traffic_bytes_{key}"])}
+
     res["w4a4"] = {"prefill_M4096": {"us": round(dt4 * 1e6, 2), "tflops": round(flops / dt4 / 1e12, 1),
-                                     "frac_of_fp4_peak": round(flops / dt4 / 1e12 / FP4_PEAK_TFLOPS, 4)},
+                                     "frac_of_fp4_peak": round(flops / dt4 / 1e12 / FP4_PEAK_TFLOPS, 4),
+                                     "counters": counters("w4a4")},
                    "act_quant_mxfp4_M4096_us": round(aq4 * 1e6, 2)}
     ws4 = w4.Workspace(32, N, K, "w4a4", dev)
     for Md in (1, 32):
@@ -814,7 +941,7 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
     del nkc, nk
 
     # int4 g128 (symmetric, then with zero points) and int5 g128, fragment order, eight copies
-    def int_family(q, prep, gemm, kind, extra_bits):
+    def int_family(q, prep, gemm, kind, extra_bits, key):
         copies = [prep(q) for _ in range(8)]
         ws = w4.Workspace(2048, q["N"], q["K"], kind, dev)
         out = {}
@@ -834,23 +961,25 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
                 fl = 2.0 * M * q["N"] * q["K"]
                 ent["tflops"] = round(fl / dt / 1e12, 1)
                 ent["frac_of_fp8_peak"] = round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4)
+                if key:
+                    ent["counters"] = counters(key)
             out[str(M)] = ent
         del copies
         return out
 
     i4 = int_family(q, lambda q: w4.int4g128_prepare_fragments(
         to_dev(q["qweight_kn"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
-        w4.int4g128_gemm_prepared, "int4_prepared", 4)
+        w4.int4g128_gemm_prepared, "int4_prepared", 4, "int4")
     res["int4_g128"] = i4
     log("int4", i4)
     i4z = int_family(synth.int4_zp(), lambda q: w4.int4g128_zp_prepare_fragments(
         to_dev(q["qweight_kn"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
-        w4.int4g128_zp_gemm_prepared, "int4_zp_prepared", 4)
+        w4.int4g128_zp_gemm_prepared, "int4_zp_prepared", 4, None)
     res["int4_g128_zp"] = i4z
     log("int4 zp", i4z)
     i5 = int_family(synth.int5(), lambda q: w4.int5g128_prepare_fragments(
         to_dev(q["qweight_kn"]), to_dev(q["qweight_hi"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
-        w4.int5g128_gemm_prepared, "int5_prepared", 5)
+        w4.int5g128_gemm_prepared, "int5_prepared", 5, "int5")
     res["int5_g128"] = i5
     log("int5", i5)
     return res
