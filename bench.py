@@ -777,8 +777,8 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
                                      "frac_of_fp4_peak": round(flops / dt4 / 1e12 / FP4_PEAK_TFLOPS, 4),
                                      "counters": counters("w4a4")},
                    "act_quant_mxfp4_M4096_us": round(aq4 * 1e6, 2)}
-    ws4 = w4.Workspace(32, N, K, "w4a4", dev)
-    for Md in (1, 32):
+    ws4 = w4.Workspace(64, N, K, "w4a4", dev)
+    for Md in (1, 32, 64):
         xad, xed = w4.quant_act_mxfp4(xb[:Md].contiguous())
         od = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
         dtd = _timed_graph(torch, timer, [lambda r=r: w4.w4a4_gemm_prepared(xad, xed, pcopies[r], out=od, workspace=ws4)

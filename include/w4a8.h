@@ -346,11 +346,14 @@ w4a8_status w4a8_int4g128_gemm(
  *   d_x_e8m0  device uint8 [M, K/32], 4-byte aligned
  *   d_w_prepared, d_s_prepared: from w4a8_mxfp4_prepare
  *   d_out     device bf16 [M, N], 8-byte aligned
- * Any M >= 1; K % 128 == 0 and K < 2^24 (else UNSUPPORTED_SHAPE).  M <= 32:
- * the split-K decode kernel (weights streamed once, activations resident in
- * LDS, K split across workgroups when they do not fit); above, a tiled kernel
- * (128- or 256-row tiles, 256 wide), K split across workgroups when its tiles
- * are fewer than 128.  A split writes fp32 partials to the workspace (size it
+ * Any M >= 1; K % 128 == 0 and K < 2^24 (else UNSUPPORTED_SHAPE).  Wide
+ * layers (at least 1536 16-row tiles on 256 CUs, at most 16 per CU) at
+ * M <= 64 with ceil(K/512) even: the spread tiles (one workgroup per CU over
+ * all of K, no workspace).  Otherwise M <= 32: the split-K decode kernel
+ * (weights streamed once, activations resident in LDS, K split across
+ * workgroups when they do not fit); above, a tiled kernel (128- or 256-row
+ * tiles, 256 wide), K split across workgroups when its tiles are fewer than
+ * 128.  A split writes fp32 partials to the workspace (size it
  * with W4A8_W4A4_PREPARED for the largest M), then a reduction.  Errors:
  * INVALID_ARG, UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t *d_x_fp4, const uint8_t *d_x_e8m0,

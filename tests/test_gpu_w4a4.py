@@ -68,7 +68,22 @@ def test_w4a4_decode(M, N, K):
     _case(f"decode {M}x{N}x{K}", w["w_packed"], w["w_e8m0"], M, (M, K, 11), spread=10.0)
 
 
-@pytest.mark.parametrize("M", [1, 8, 12, 13, 64, 4096])
+# the spread tiles (wide layers, M <= 64, padded K steps a multiple of 8): one
+# to four 16-row activation tiles with ragged M, one or two weight tiles per
+# wave, N not a multiple of 8 (row stores by the products' lanes) or of 4
+# (scalar stores), K ending inside a 4-step chunk, and a K whose padded steps
+# are not a multiple of 8 (the split-K decode kernel / the tile kernel instead)
+W4A4_SPREAD = [(3, 25001, 640, None), (17, 24602, 896, None), (33, 30000, 2048, None), (64, 65536, 512, None),
+               (47, 40000, 5120, 2048), (2, 24576, 1152, None), (40, 24576, 1152, None)]
+
+
+@pytest.mark.parametrize("M,N,K,sample", W4A4_SPREAD)
+def test_w4a4_spread(M, N, K, sample):
+    w = synth.mxfp4_random(N, K, seed=(M, N, K, 13))
+    _case(f"spread {M}x{N}x{K}", w["w_packed"], w["w_e8m0"], M, (M, K, 13), spread=10.0, sample=sample)
+
+
+@pytest.mark.parametrize("M", [1, 8, 12, 13, 16, 32, 48, 64, 4096])
 def test_w4a4_gate_up(gate_up_mx, M):
     _case(f"gate_up M={M}", gate_up_mx[0], gate_up_mx[1], M, (8, M), sample=4096 if M > 64 else None)
 

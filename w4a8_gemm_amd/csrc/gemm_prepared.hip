@@ -1166,6 +1166,7 @@ struct SpArgs {
                             // the block M x 32 nt bytes within the stage ring)
     int64_t xrs, xss;       // activation codes: bytes between rows and between 128-wide steps
                             // (row-major K and 128; step-major 128 and 128 M)
+    const uint8_t* xe;      // MXFP4 activations: e8m0 [M, K/32] (x8 then holds e2m1 codes [M, K/2])
 };
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
@@ -1326,6 +1327,66 @@ __device__ __forceinline__ void sp_trip(uint8_t* lds, int s, int lane, const SpS
     }
 }
 
+// bf16 out = scale x sum for the wave's tiles w0 .. w0 + R - 1 (the
+// workgroup's: t_lo .. t_lo + nt - 1); SM 0: the token's scale xs[m], 1: s
+template <int MT, int R, int SM>
+__device__ __forceinline__ void sp_epilogue(const SpArgs& a, uint8_t* lds, const v4f (&acc)[R][MT], int w0, int lane,
+                                            int t_lo, int nt, float s) {
+    const int g = lane >> 4;
+    if (a.out16) {
+        // the workgroup's output block (M rows x 16 nt columns of bf16) assembled
+        // in LDS, then stored row by row in 16-byte pieces, consecutive lanes
+        // along a row: whole 128-byte lines per store instead of sixteen 32-byte
+        // pieces (the products' lane layout), which took the write-back of a
+        // 64-row block 2-3 us longer at the end of the launch
+        const int pitch = 32 * nt;
+        __syncthreads();   // every wave past its last fragment read
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = mt * 16 + (lane & 15);
+                if (m >= a.M) continue;
+                const float sm = SM ? s : a.xs[m];
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
+                *reinterpret_cast<uint2*>(lds + m * pitch + 32 * (w0 - t_lo + r) + 8 * g) = make_uint2(h0, h1);
+            }
+        }
+        __syncthreads();
+        // columns past N (the last tile's) are not stored; N is a multiple of 8
+        const int cpr = (min(16 * nt, a.N - 16 * t_lo)) / 8;
+        uint8_t* ob = reinterpret_cast<uint8_t*>(a.out + 16 * (int64_t)t_lo);
+        for (int i = (int)threadIdx.x; i < a.M * cpr; i += kSpThreads) {
+            const int row = i / cpr, ch = i - row * cpr;
+            *reinterpret_cast<uint4*>(ob + 2 * (int64_t)row * a.N + 16 * ch) =
+                *reinterpret_cast<const uint4*>(lds + row * pitch + 16 * ch);
+        }
+        return;
+    }
+    const bool vec = (a.N & 3) == 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int n0 = 16 * (w0 + r) + 4 * g;
+        if (n0 >= a.N) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m >= a.M) continue;
+            const float sm = SM ? s : a.xs[m];
+            uint16_t* o = a.out + (int64_t)m * a.N + n0;
+            if (vec) {
+                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
+                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
+                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
+            } else {
+                for (int qq = 0; qq < 4; ++qq)
+                    if (n0 + qq < a.N) o[qq] = (uint16_t)f32_to_bf16_rne(sm * acc[r][mt][qq]);
+            }
+        }
+    }
+}
+
 // a wave's loop over its tiles w0 .. w0 + R - 1, then bf16 out = token scale x
 // sum (the workgroup's tiles: t_lo .. t_lo + nt - 1)
 template <int MT, int R, int D, bool CS, bool PL, bool FQ>
@@ -1457,59 +1518,7 @@ __device__ __forceinline__ void sp_run(const SpArgs& a, uint8_t* lds, int w0, in
     for (int s = 0; s < a.s_pad; s += kSpTrip<D, CS>)
         sp_trip<MT, R, D, CS, PL, FQ, 0>(lds, s, lane, q, ring, av, F0, F1, acc);
 
-    if (a.out16) {
-        // the workgroup's output block (M rows x 16 nt columns of bf16) assembled
-        // in LDS, then stored row by row in 16-byte pieces, consecutive lanes
-        // along a row: whole 128-byte lines per store instead of sixteen 32-byte
-        // pieces (the products' lane layout), which took the write-back of a
-        // 64-row block 2-3 us longer at the end of the launch
-        const int pitch = 32 * nt;
-        __syncthreads();   // every wave past its last fragment read
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int m = mt * 16 + (lane & 15);
-                if (m >= a.M) continue;
-                const float sm = FQ ? sm_fq : a.xs[m];
-                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
-                *reinterpret_cast<uint2*>(lds + m * pitch + 32 * (w0 - t_lo + r) + 8 * g) = make_uint2(h0, h1);
-            }
-        }
-        __syncthreads();
-        // columns past N (the last tile's) are not stored; N is a multiple of 8
-        const int cpr = (min(16 * nt, a.N - 16 * t_lo)) / 8;
-        uint8_t* ob = reinterpret_cast<uint8_t*>(a.out + 16 * (int64_t)t_lo);
-        for (int i = (int)threadIdx.x; i < a.M * cpr; i += kSpThreads) {
-            const int row = i / cpr, ch = i - row * cpr;
-            *reinterpret_cast<uint4*>(ob + 2 * (int64_t)row * a.N + 16 * ch) =
-                *reinterpret_cast<const uint4*>(lds + row * pitch + 16 * ch);
-        }
-        return;
-    }
-
-    const bool vec = (a.N & 3) == 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int n0 = 16 * (w0 + r) + 4 * g;
-        if (n0 >= a.N) continue;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + (lane & 15);
-            if (m >= a.M) continue;
-            const float sm = FQ ? sm_fq : a.xs[m];
-            uint16_t* o = a.out + (int64_t)m * a.N + n0;
-            if (vec) {
-                const uint32_t h0 = f32_to_bf16_rne(sm * acc[r][mt][0]) | (f32_to_bf16_rne(sm * acc[r][mt][1]) << 16);
-                const uint32_t h1 = f32_to_bf16_rne(sm * acc[r][mt][2]) | (f32_to_bf16_rne(sm * acc[r][mt][3]) << 16);
-                *reinterpret_cast<uint2*>(o) = make_uint2(h0, h1);
-            } else {
-                for (int qq = 0; qq < 4; ++qq)
-                    if (n0 + qq < a.N) o[qq] = (uint16_t)f32_to_bf16_rne(sm * acc[r][mt][qq]);
-            }
-        }
-    }
+    sp_epilogue<MT, R, FQ ? 1 : 0>(a, lds, acc, w0, lane, t_lo, nt, sm_fq);
 }
 
 template <int MT, int R, int D, bool CS, bool PL, bool FQ>
@@ -1539,6 +1548,193 @@ template <int MT, int R, int D, bool CS, bool PL = false, bool FQ = false>
 hipError_t launch_spread_inst(const SpArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((spread_kernel<MT, R, D, CS, PL, FQ>), dim3(a.groups), dim3(kSpThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The spread tiles with MXFP4 activations (W4A4 on wide layers, M <= 64).
+// The weight stream is the fp8 form's (register ring 4 steps deep, the tiles'
+// e8m0 dwords once per 4-step chunk, trips of 8 steps), and so is the 4-stage
+// LDS ring of activation steps with one barrier per step.  A stage holds a
+// step's e2m1 codes, 64 B per row with the four 16-byte K blocks XOR-swizzled
+// by (row >> 2) & 3 as in the fp4 tile kernel.  The rows' e8m0 sit in two
+// chunk areas (even and odd 4-step chunks), [step % 4][row] dwords, so that a
+// fragment's 16 rows read 16 consecutive dwords.
+//
+// Staging is coarser than the fp8 form's, because what limits these tiles at
+// 64 rows is the number of distinct activation lines a CU requests per step:
+// each of the 512 threads (row tid / 8, piece tid % 8) loads 16 code bytes
+// every second step (the row's two steps are one 128-byte line: piece p is
+// step p / 4's K block p % 4) and one e8m0 dword every fourth (the row's
+// chunk is 16 bytes: piece p takes step p % 4's dword, pieces p and p + 4
+// store copies), which is 48 lines per step instead of 128 with a step's 64
+// code bytes and e8m0 dword loaded every step.  A pair of steps is loaded
+// four steps ahead of its store (two pair slots), a chunk's dwords four steps
+// ahead (two chunk slots); the products are fp4 x fp4 (16 cycles, half the
+// fp8 one) with both scale operands: the weight's byte of the chunk dword and
+// byte g (the lane's K block) of the row's activation dword.  No token scale:
+// out = bf16(sum).
+// ---------------------------------------------------------------------------
+constexpr int kSa4Stage = 64 * 64;                 // a step's codes (64 rows)
+constexpr int kSa4Area = 2 * 1024;                 // a chunk's e8m0: two copies of [4 steps][64 rows] dwords
+constexpr int kSa4E = kSpStages * kSa4Stage;       // the two chunk areas follow the four stages
+
+template <int R>
+struct Sa4Src {
+    SpSrc<R> w;              // the weight sources (wp, sp, w_last)
+    const uint8_t* xrow;     // this thread's code bytes (its row, K block) of step 0
+    const uint8_t* erow;     // its row's e8m0 (step 0's dword)
+    uint32_t xdst, edst;     // its offsets from the first stage of a pair / in a chunk area
+    int h, d;                // its step within a pair, within a chunk
+    int x_last;              // last real step
+};
+
+// the thread's 16 code bytes of pair u (steps 2u, 2u + 1); its dword of chunk c
+template <int R>
+__device__ __forceinline__ uint4 sa4_pair(const Sa4Src<R>& q, int u) {
+    return *reinterpret_cast<const uint4*>(q.xrow + 64 * (int64_t)min(2 * u + q.h, q.x_last));
+}
+template <int R>
+__device__ __forceinline__ uint32_t sa4_chunk(const Sa4Src<R>& q, int c) {
+    return *reinterpret_cast<const uint32_t*>(q.erow + 4 * (int64_t)min(4 * c + q.d, q.x_last));
+}
+// step t's fragments (stage t % 4) and activation scale operands (byte g of
+// the row's dword in the low byte; chunk area (t / 4) % 2)
+template <int MT>
+__device__ __forceinline__ void sa4_read(const uint8_t* stage, const uint8_t* area, int t4, int lane, v8i (&F)[MT],
+                                         int (&E)[MT]) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * mt + (lane & 15);
+        F[mt] = frag_fp4(*reinterpret_cast<const uint4*>(stage + 64 * r + 16 * (g ^ ((r >> 2) & 3))));
+        E[mt] = (int)(*reinterpret_cast<const uint32_t*>(area + 256 * t4 + 4 * r) >> (8 * g));
+    }
+}
+
+template <int MT, int R, int J>
+__device__ __forceinline__ void sa4_step(uint8_t* lds, int s, int lane, const Sa4Src<R>& q, SpRing<R, 4>& ring,
+                                         uint4 (&pv)[2], uint32_t (&ev)[2], v8i (&F0)[MT], v8i (&F1)[MT],
+                                         int (&E0)[MT], int (&E1)[MT], v4f (&acc)[R][MT]) {
+    dt_barrier();
+    // step s + 1's operands
+    {
+        const uint8_t* stage = lds + ((J + 1) % kSpStages) * kSa4Stage;
+        const uint8_t* area = lds + kSa4E + (((J + 1) / 4) % 2) * kSa4Area;
+        if constexpr ((J & 1) == 0) sa4_read<MT>(stage, area, (J + 1) % 4, lane, F1, E1);
+        else sa4_read<MT>(stage, area, (J + 1) % 4, lane, F0, E0);
+    }
+    if constexpr ((J & 1) == 0) {
+        // steps s + 2, s + 3 into their stages (both last read before this
+        // step's barrier), then the pair of steps s + 6, s + 7 into the slot
+        constexpr int slot = (J / 2 + 1) % 2;
+        *reinterpret_cast<uint4*>(lds + ((J + 2) % kSpStages) * kSa4Stage + q.xdst) = pv[slot];
+        pv[slot] = sa4_pair(q, s / 2 + 3);
+    }
+    if constexpr (J % 4 == 2) {
+        // the chunk of steps s + 2 .. s + 5 into its area (the chunk two
+        // before it was last read at step s - 4), then the next chunk's dword
+        // into the other slot (its previous chunk stored at step s - 4)
+        constexpr int c = ((J + 2) / 4) % 2;
+        *reinterpret_cast<uint32_t*>(lds + kSa4E + c * kSa4Area + q.edst) = ev[c];
+        ev[1 - c] = sa4_chunk(q, (s + 2) / 4 + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const dt_u32x4 w = ring.w[J % 4][r];
+        const v8i af = frag_fp4(make_uint4(w[0], w[1], w[2], w[3]));
+        const int sc = (int)(ring.cs[(J / 4) % 2][r] >> (8 * (J & 3)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr ((J & 1) == 0) acc[r][mt] = mfma44<0>(af, F0[mt], acc[r][mt], sc, E0[mt]);
+            else acc[r][mt] = mfma44<0>(af, F1[mt], acc[r][mt], sc, E1[mt]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sp_wload<R, 4, true, false>(q.w, s + 4, ring, J % 4);
+    if constexpr (J % 4 == 0) sp_csload<R, 4, false>(q.w, s / 4 + 1, ring, (J / 4 + 1) % 2);
+}
+template <int MT, int R, int J>
+__device__ __forceinline__ void sa4_trip(uint8_t* lds, int s, int lane, const Sa4Src<R>& q, SpRing<R, 4>& ring,
+                                         uint4 (&pv)[2], uint32_t (&ev)[2], v8i (&F0)[MT], v8i (&F1)[MT],
+                                         int (&E0)[MT], int (&E1)[MT], v4f (&acc)[R][MT]) {
+    if constexpr (J < 8) {
+        sa4_step<MT, R, J>(lds, s + J, lane, q, ring, pv, ev, F0, F1, E0, E1, acc);
+        sa4_trip<MT, R, J + 1>(lds, s, lane, q, ring, pv, ev, F0, F1, E0, E1, acc);
+    }
+}
+
+template <int MT, int R>
+__device__ __forceinline__ void sa4_run(const SpArgs& a, uint8_t* lds, int w0, int lane, int t_lo, int nt) {
+    const int tid = threadIdx.x;
+    Sa4Src<R> q;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        q.w.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
+        q.w.sp[r] = a.st + (int64_t)(w0 + r) * a.c_pad * 64 + lane;
+    }
+    q.w.w_last = a.s_pad - 1;
+    // this thread's staging items: row tid / 8 (clamped to M - 1), piece tid % 8
+    const int xr = tid >> 3, pc = tid & 7;
+    const int64_t row = min(xr, a.M - 1);
+    q.h = pc >> 2;
+    q.d = pc & 3;
+    q.xrow = a.x8 + row * (a.K / 2) + 16 * (pc & 3);
+    q.erow = a.xe + row * (a.K / 32);
+    q.xdst = (uint32_t)(q.h * kSa4Stage + 64 * xr + 16 * ((pc & 3) ^ ((xr >> 2) & 3)));
+    q.edst = (uint32_t)(q.h * 1024 + 256 * q.d + 4 * xr);
+    q.x_last = a.steps - 1;
+
+    v4f acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    SpRing<R, 4> ring;
+    uint4 pv[2];
+    uint32_t ev[2];
+    v8i F0[MT], F1[MT];
+    int E0[MT], E1[MT];
+
+    // prologue: chunk 0's weight dwords first (as in the fp8 form), the
+    // activations of steps 0 .. 5 and chunks 0 and 1, the weights of steps
+    // 0 .. 3; steps 0, 1 and chunk 0 stored, step 0's operands read.  Then
+    // the loop's invariant holds at s = 0: slots hold pairs (2, 3), (4, 5) and
+    // chunk 1
+    sp_csload<R, 4, false>(q.w, 0, ring, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 p01 = sa4_pair(q, 0);
+    const uint32_t e0 = sa4_chunk(q, 0);
+    pv[1] = sa4_pair(q, 1);
+    ev[1] = sa4_chunk(q, 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sp_wload<R, 4, true, false>(q.w, k, ring, k);
+    *reinterpret_cast<uint4*>(lds + q.xdst) = p01;
+    *reinterpret_cast<uint32_t*>(lds + kSa4E + q.edst) = e0;
+    pv[0] = sa4_pair(q, 2);
+    dt_barrier();
+    sa4_read<MT>(lds, lds + kSa4E, 0, lane, F0, E0);
+
+    for (int s = 0; s < a.s_pad; s += 8) sa4_trip<MT, R, 0>(lds, s, lane, q, ring, pv, ev, F0, F1, E0, E1, acc);
+    sp_epilogue<MT, R, 1>(a, lds, acc, w0, lane, t_lo, nt, 1.0f);
+}
+
+template <int MT, int R>
+__global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
+    static_assert(kSa4E + 2 * kSa4Area <= kSpStages * kSpStage, "the stages and chunk areas fit the ring's LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int64_t T = a.tiles, G = a.groups;
+    const int t_lo = (int)(T * blockIdx.x / G), n = (int)(T * (blockIdx.x + 1) / G) - t_lo;
+    const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
+    if constexpr (R > 1) {
+        if (nr < R) {
+            sa4_run<MT, R - 1>(a, lds, w0, lane, t_lo, n);
+            return;
+        }
+    }
+    sa4_run<MT, R>(a, lds, w0, lane, t_lo, n);
 }
 
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
@@ -3248,16 +3444,18 @@ static TiledShape w4a4_shape(int64_t M, int64_t N, int64_t K) {
 }
 
 bool w4a4_decode_route(int64_t M, int64_t N) {
-    // the split-K decode kernel for every M it takes (two 16-row activation
-    // tiles), on wide layers too: with fp4 activations its LDS reads and
-    // products cost half of W4A8's (measured on gfx950, gate_up 34816 x 5120:
-    // M = 1 / 12 / 13 / 32: 19.8 / 21.4 / 24.2 / 30.0 us, against 32.5 / 35.2 /
-    // 35.2 / 34.3 us in the 128-row tile kernel)
+    // where the spread tiles do not apply: the split-K decode kernel for every
+    // M it takes (two 16-row activation tiles): with fp4 activations its LDS
+    // reads and products cost half of W4A8's (measured on gfx950, gate_up
+    // 34816 x 5120: M = 1 / 12 / 13 / 32: 19.8 / 21.4 / 24.2 / 30.0 us, against
+    // 32.5 / 35.2 / 35.2 / 34.3 us in the 128-row tile kernel; the spread tiles
+    // 16.5-17.9 us for M = 1-32, 19.2 / 20.0 us at M = 48 / 64)
     (void)N;
     return M <= kPreparedDecodeMaxM;
 }
 
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (spread_a4_fits(M, N, K)) return 0;
     if (w4a4_decode_route(M, N)) return plan_workspace_bytes(plan_prepared(M, N, K, 0, 0, true, false), M, N);
     const TiledShape t = w4a4_shape(M, N, K);
     if (t.ks <= 1) return 0;
@@ -3270,6 +3468,7 @@ static hipError_t launch_w4a4_decode(const uint8_t* x4, const uint8_t* xe, const
 
 hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
                                 uint16_t* out, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t stream) {
+    if (spread_a4_fits(M, N, K)) return launch_spread_a4(x4, xe, wt, st, out, M, N, K, stream);
     if (w4a4_decode_route(M, N)) return launch_w4a4_decode(x4, xe, wt, st, out, M, N, K, ws, stream);
     PfArgs a{};
     a.x8 = x4; a.xe = xe; a.xs = nullptr; a.wt = wt; a.st = st; a.out = out;
@@ -3638,6 +3837,44 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     W4A8_SP(1, 2, 4, 1) W4A8_SP(2, 2, 4, 1) W4A8_SP(3, 2, 4, 1) W4A8_SP(4, 2, 4, 1)
     W4A8_SP(1, 1, 8, 0) W4A8_SP(1, 2, 8, 0) W4A8_SP(2, 2, 8, 0) W4A8_SP(3, 2, 8, 0) W4A8_SP(4, 2, 8, 0)
 #undef W4A8_SP
+    return hipErrorInvalidValue;
+}
+
+// W4A4 on the spread tiles: the wide layers of the fp8 form, with the padded
+// steps a multiple of 8 (the trips of two chunks)
+bool spread_a4_fits(int64_t M, int64_t N, int64_t K) {
+    return spread_fits(M, N, K) && ((K / 128 + 3) / 4) % 2 == 0;
+}
+
+hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                            uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (!spread_a4_fits(M, N, K)) return hipErrorInvalidValue;
+    const SpPlan p = plan_spread(M, N, K, 4, 1);
+    if (p.groups < 1 || p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16 ||
+        p.mt != (int)((M + 15) / 16))
+        return hipErrorInvalidValue;
+    // every wave has a tile, and none more than R
+    if (p.tiles < (int64_t)kSpWaves * p.groups || (p.tiles + p.groups - 1) / p.groups > (int64_t)kSpWaves * p.r)
+        return hipErrorInvalidValue;
+    SpArgs a{};
+    a.x8 = x4; a.xe = xe; a.xs = nullptr; a.out = out;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.steps = (int)(K / 128);
+    a.tiles = (int)p.tiles;
+    a.groups = (int)p.groups;
+    a.out16 = spread_out16(out, M, N, p);
+#define W4A8_SA4(MT, R)                                                                                 \
+    if (p.mt == MT && p.r == R) {                                                                     \
+        hipLaunchKernelGGL((spread_a4_kernel<MT, R>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
+        return hipGetLastError();                                                                     \
+    }
+    W4A8_SA4(1, 1) W4A8_SA4(2, 1) W4A8_SA4(3, 1) W4A8_SA4(4, 1)
+    W4A8_SA4(1, 2) W4A8_SA4(2, 2) W4A8_SA4(3, 2) W4A8_SA4(4, 2)
+#undef W4A8_SA4
     return hipErrorInvalidValue;
 }
 

@@ -269,6 +269,10 @@ hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false,
                          bool x_step_major = false);
+// W4A4 (e2m1 codes x4 [M, K/2], e8m0 xe [M, K/32]) on the spread tiles
+bool spread_a4_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
+                            uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 constexpr int64_t kPreparedDecodeMaxM = 32;
 // largest K of the tiled kernel on prepared weights (32-bit buffer offsets
 // into a 256-row activation block: 256 * K < 2^32)
