@@ -348,8 +348,8 @@ w4a8_status w4a8_int4g128_gemm(
  *   d_out     device bf16 [M, N], 8-byte aligned
  * Any M >= 1; K % 128 == 0 and K < 2^24 (else UNSUPPORTED_SHAPE).  Wide
  * layers (at least 1536 16-row tiles on 256 CUs, at most 16 per CU) at
- * M <= 64 with ceil(K/512) even: the spread tiles (one workgroup per CU over
- * all of K, no workspace).  Otherwise M <= 32: the split-K decode kernel
+ * M <= 64: the spread tiles (one workgroup per CU over all of K, no
+ * workspace).  Otherwise M <= 32: the split-K decode kernel
  * (weights streamed once, activations resident in LDS, K split across
  * workgroups when they do not fit); above, a tiled kernel (128- or 256-row
  * tiles, 256 wide), K split across workgroups when its tiles are fewer than

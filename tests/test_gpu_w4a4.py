@@ -68,13 +68,16 @@ def test_w4a4_decode(M, N, K):
     _case(f"decode {M}x{N}x{K}", w["w_packed"], w["w_e8m0"], M, (M, K, 11), spread=10.0)
 
 
-# the spread tiles (wide layers, M <= 64, padded K steps a multiple of 8): one
-# to four 16-row activation tiles with ragged M, one or two weight tiles per
-# wave, N not a multiple of 8 (row stores by the products' lanes) or of 4
-# (scalar stores), K ending inside a 4-step chunk, and a K whose padded steps
-# are not a multiple of 8 (the split-K decode kernel / the tile kernel instead)
+# the spread tiles (wide layers, M <= 64): one to four 16-row activation tiles
+# with ragged M, one or two weight tiles per wave, N not a multiple of 8 (row
+# stores by the products' lanes) or of 4 (scalar stores), K ending inside a
+# 4-step chunk, and an odd number of 4-step chunks, where the last trip of 8
+# steps runs past the padded steps (weights of the last padded step repeated,
+# activation codes zero): after padding steps (K = 1152) and after a real step
+# (K = 512, 1536)
 W4A4_SPREAD = [(3, 25001, 640, None), (17, 24602, 896, None), (33, 30000, 2048, None), (64, 65536, 512, None),
-               (47, 40000, 5120, 2048), (2, 24576, 1152, None), (40, 24576, 1152, None)]
+               (47, 40000, 5120, 2048), (2, 24576, 1152, None), (40, 24576, 1152, None), (24, 24576, 1536, None),
+               (1, 30000, 512, None), (64, 24600, 4608, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K,sample", W4A4_SPREAD)

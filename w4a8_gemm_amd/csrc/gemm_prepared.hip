@@ -1588,10 +1588,20 @@ struct Sa4Src {
     int x_last;              // last real step
 };
 
-// the thread's 16 code bytes of pair u (steps 2u, 2u + 1); its dword of chunk c
+// the thread's 16 code bytes of pair u (steps 2u, 2u + 1; clamped to the last
+// real step); its dword of chunk c
 template <int R>
 __device__ __forceinline__ uint4 sa4_pair(const Sa4Src<R>& q, int u) {
     return *reinterpret_cast<const uint4*>(q.xrow + 64 * (int64_t)min(2 * u + q.h, q.x_last));
+}
+// the codes of the thread's step t as staged: zero past the last real step.
+// The loop runs whole trips of 8 steps, which may pass the padded steps;
+// there the weight loads repeat the last padded step, and the zero codes make
+// those products zero.  (Selected at the store, where the loaded value is
+// needed anyway: a select right after the load would wait for it there.)
+template <int R>
+__device__ __forceinline__ uint4 sa4_staged(const Sa4Src<R>& q, int t, uint4 v) {
+    return t <= q.x_last ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 template <int R>
 __device__ __forceinline__ uint32_t sa4_chunk(const Sa4Src<R>& q, int c) {
@@ -1627,7 +1637,8 @@ __device__ __forceinline__ void sa4_step(uint8_t* lds, int s, int lane, const Sa
         // steps s + 2, s + 3 into their stages (both last read before this
         // step's barrier), then the pair of steps s + 6, s + 7 into the slot
         constexpr int slot = (J / 2 + 1) % 2;
-        *reinterpret_cast<uint4*>(lds + ((J + 2) % kSpStages) * kSa4Stage + q.xdst) = pv[slot];
+        *reinterpret_cast<uint4*>(lds + ((J + 2) % kSpStages) * kSa4Stage + q.xdst) =
+            sa4_staged(q, s + 2 + q.h, pv[slot]);
         pv[slot] = sa4_pair(q, s / 2 + 3);
     }
     if constexpr (J % 4 == 2) {
@@ -1709,7 +1720,7 @@ __device__ __forceinline__ void sa4_run(const SpArgs& a, uint8_t* lds, int w0, i
     ev[1] = sa4_chunk(q, 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) sp_wload<R, 4, true, false>(q.w, k, ring, k);
-    *reinterpret_cast<uint4*>(lds + q.xdst) = p01;
+    *reinterpret_cast<uint4*>(lds + q.xdst) = sa4_staged(q, q.h, p01);
     *reinterpret_cast<uint32_t*>(lds + kSa4E + q.edst) = e0;
     pv[0] = sa4_pair(q, 2);
     dt_barrier();
@@ -3840,10 +3851,9 @@ hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, co
     return hipErrorInvalidValue;
 }
 
-// W4A4 on the spread tiles: the wide layers of the fp8 form, with the padded
-// steps a multiple of 8 (the trips of two chunks)
+// W4A4 on the spread tiles: the wide layers of the fp8 form
 bool spread_a4_fits(int64_t M, int64_t N, int64_t K) {
-    return spread_fits(M, N, K) && ((K / 128 + 3) / 4) % 2 == 0;
+    return spread_fits(M, N, K);
 }
 
 hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
