@@ -972,6 +972,24 @@ def extra_measurements(torch, w4, synth, timer, log, nv_p, nv_s, g, wp, we, pcop
         w4.int4g128_gemm_prepared, "int4_prepared", 4, "int4")
     res["int4_g128"] = i4
     log("int4", i4)
+    # int4 g128 on a wide (gate_up-shaped) layer: the spread tiles from 9 rows
+    qw = synth.int4_random(N, K, seed=(N, K, 1))
+    wcopies = [w4.int4g128_prepare_fragments(to_dev(qw["qweight_kn"]), to_dev(qw["qzeros"]), to_dev(qw["scales"], True))
+               for _ in range(8)]
+    iw = {}
+    wws = w4.Workspace(64, N, K, "int4_prepared", dev)
+    for M in (1, 16, 64):
+        xb = torch.from_numpy(synth.acts(M, K, seed=(4, M)).view(np.int16)).view(torch.bfloat16).to(dev)
+        a8, asc = w4.quant_act_fp8_per_token(xb)
+        oo = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        dt = _timed_graph(torch, timer, [lambda r=r: w4.int4g128_gemm_prepared(a8, asc, wcopies[r], out=oo, workspace=wws)
+                                         for r in range(8)], 10)
+        b = N * K // 2 + N * K // 64 + M * K + M * 4 + M * N * 2
+        iw[str(M)] = {"us": round(dt * 1e6, 2), "gbps": round(b / dt / 1e9, 1),
+                      "frac_of_hbm": round(b / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    del wcopies
+    res["int4_g128_wide"] = {"N": N, "K": K, **iw}
+    log("int4 wide", res["int4_g128_wide"])
     i4z = int_family(synth.int4_zp(), lambda q: w4.int4g128_zp_prepare_fragments(
         to_dev(q["qweight_kn"]), to_dev(q["qzeros"]), to_dev(q["scales"], True)),
         w4.int4g128_zp_gemm_prepared, "int4_zp_prepared", 4, None)

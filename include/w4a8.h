@@ -378,9 +378,11 @@ w4a8_status w4a8_w4a4_gemm_prepared(const uint8_t *d_x_fp4, const uint8_t *d_x_e
  *     -> d_w_prepared (16-byte aligned), d_s_prepared (16-byte aligned).
  *     Synchronizes `stream` (the check result is read back).
  *   w4a8_int4g128_gemm_prepared: as w4a8_int4g128_gemm, any M >= 1, with the
- *     kernels of w4a8_mxfp4_gemm_prepared (the split-K decode kernel for
- *     M <= 32 on every layer, and 256-row tiles from 128 of them on) and its
- *     workspace rules (size it with W4A8_WEIGHT_INT4G128_PREPARED).
+ *     kernels of w4a8_mxfp4_gemm_prepared (on wide layers for 9 <= M <= 64
+ *     the spread tiles, each code taken as two e2m1 halves; else the split-K
+ *     decode kernel for M <= 32 on every layer, and 256-row tiles from 128 of
+ *     them on) and its workspace rules (size it with
+ *     W4A8_WEIGHT_INT4G128_PREPARED).
  * N % 8 == 0, K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, ASYMMETRIC (prepare), HIP. */
 w4a8_status w4a8_int4g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_s_bytes);

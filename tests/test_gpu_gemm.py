@@ -666,14 +666,45 @@ def test_int4_prepared_ragged(M, N, K):
                         full=True, spread=10.0)
 
 
-# wide layers: split-K decode (M <= 32; one and two 16-row activation tiles),
-# tiled (64/128/256-row tiles)
+# wide layers: the spread tiles (9 <= M <= 64 where at most two 16-row tiles
+# fall to a wave: N = 34816), else split-K decode (M <= 32; one and two 16-row
+# activation tiles) and tiled (64/128/256-row tiles; N = 65600)
 @pytest.mark.parametrize("M,N,K", [(5, 65600, 256), (13, 34816, 5120), (20, 65600, 384), (32, 34816, 5120),
                                    (33, 34816, 640), (40, 65600, 256),
                                    (300, 33000, 384), (600, 45064, 256)])
 def test_int4_prepared_wide(M, N, K):
     _int4_prepared_case(f"wide {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 9)), M,
                         (M, K, 9), n_samples=8192)
+
+
+# the spread tiles for symmetric int4 (above 8 rows): one to four 16-row activation tiles with
+# ragged M, one or two weight tiles per wave, output rows stored by the
+# products' lanes (N not a multiple of 16) or assembled, K ending inside a
+# 4-step chunk, and an odd number of chunks, where the last trip of 8 steps
+# runs past the padded steps with zero activation codes: after padding steps
+# (K = 1152) and after a real step (K = 512, 1536)
+INT4_SPREAD = [(9, 24576, 640), (17, 24600, 896), (33, 30000, 2048), (64, 65536, 512), (47, 40000, 5120),
+               (40, 24576, 1152), (24, 24576, 1536), (12, 30000, 512), (64, 24600, 4608)]
+
+
+@pytest.mark.parametrize("M,N,K", INT4_SPREAD)
+def test_int4_prepared_spread(M, N, K):
+    _int4_prepared_case(f"spread {M}x{N}x{K}", synth.int4_random(N, K, seed=(M, N, K, 12)), M,
+                        (M, K, 12), full=M * N * K <= 2 ** 31, n_samples=8192, spread=10.0)
+
+
+def test_int4_linear_spread():
+    # the linear on bf16 rows through the spread tiles (quant kernel, then the
+    # int4 spread tiles) against the quant and GEMM entry points called apart
+    N, K, M = 34816, 1024, 24
+    q = synth.int4_random(N, K, seed=(N, K, 14))
+    pw = w4.int4g128_prepare_fragments(dev_i32(q["qweight_kn"]), dev_i32(q["qzeros"]), dev_f16(q["scales"]))
+    xb = torch.from_numpy(synth.acts(M, K, seed=(14, M)).view(np.int16)).view(torch.bfloat16).cuda()
+    say("int4 linear spread", (M, N, K))
+    x8, xs = w4.quant_act_fp8_per_token(xb)
+    ref = host_bf16_as_f64(w4.int4g128_gemm_prepared(x8, xs, pw))
+    got = host_bf16_as_f64(w4.int4g128_linear_prepared(xb, pw)[0])
+    assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("M", [1, 16, 64, 128, 512, 2048])

@@ -1748,6 +1748,158 @@ __global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
     sa4_run<MT, R>(a, lds, w0, lane, t_lo, n);
 }
 
+// ---------------------------------------------------------------------------
+// The spread tiles with symmetric int4 g128 weights (wide layers, M <= 64).
+// Weight blocks, activation staging and trips are the fp8 form's (register
+// ring 4 steps deep, 4-stage LDS ring of e4m3 steps, trips of 8 steps).  The
+// products are the split-K decode kernel's: each code taken as two e2m1
+// fragments (c & 3 and (c >> 2) & 3, scaled by 2 and 8 through the e8m0
+// operand) on top of the -8 sum(x) term from a constant fragment, which is
+// taken once per activation tile and step for all of the wave's tiles; the
+// step's fp16 row scales multiply the sum in fp32.  The row scales of a
+// 4-step chunk (the lane's four output rows x four steps: 32 bytes of the
+// tile's 128-byte record) are loaded once per chunk into two chunk slots, as
+// the fp8 form's e8m0 dwords.  Where the chunk count is odd the last trip
+// passes the padded steps by four; the staged activation codes are zero there
+// (selected at the LDS store), so those products add nothing.
+// ---------------------------------------------------------------------------
+template <int R>
+struct Si4Scales {
+    const uint4* p[R];       // the lane's 32 bytes of chunk 0's record, per tile
+    int c_last;              // last padded chunk
+};
+template <int R>
+__device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (&cs)[R][2]) {
+    c = min(c, q.c_last);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        cs[r][0] = q.p[r][8 * c];
+        cs[r][1] = q.p[r][8 * c + 1];
+    }
+}
+__device__ __forceinline__ void si4_stage(uint8_t* stage, const SpSrc<1>& q, int t, dt_u32x4 v) {
+    *reinterpret_cast<dt_u32x4*>(stage + q.xdst) = t <= q.x_last ? v : dt_u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int MT, int R, int J>
+__device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][2],
+                                         dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+    constexpr int kX2 = 128, kX8 = 130;   // e8m0 2^1, 2^3
+    dt_barrier();
+    if constexpr ((J & 1) == 0) sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F1);
+    else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
+    av[(J + 1) % 4] = sp_act(xq, s + 5);
+    si4_stage(lds + ((J + 2) % kSpStages) * kSpStage, xq, s + 2, av[(J + 2) % 4]);
+    __builtin_amdgcn_sched_barrier(0);
+    const v8i neg1 = {(int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, (int)0xAAAAAAAA, 0, 0, 0, 0};
+    v4f t0[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        t0[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(neg1, (J & 1) == 0 ? F0[mt] : F1[mt],
+                                                                  v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4, kFmtFp8, 0, kX8,
+                                                                  0, kUnitScale);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const dt_u32x4 wv = ring.w[J % 4][r];
+        const I4Split w = i4_split(make_uint4(wv[0], wv[1], wv[2], wv[3]));
+        const uint4 sv = cs[(J / 4) % 2][r][(J & 3) / 2];
+        const uint32_t s01 = (J & 1) == 0 ? sv.x : sv.z, s23 = (J & 1) == 0 ? sv.y : sv.w;
+        const float s4[4] = {f16_to_f32(s01 & 0xFFFFu), f16_to_f32(s01 >> 16), f16_to_f32(s23 & 0xFFFFu),
+                             f16_to_f32(s23 >> 16)};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const v8i bx = (J & 1) == 0 ? F0[mt] : F1[mt];
+            v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.lo, bx, t0[mt], kFmtFp4, kFmtFp8, 0, kX2, 0,
+                                                                     kUnitScale);
+            t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0,
+                                                                 kUnitScale);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[r][mt][i] = __builtin_fmaf(s4[i], t[i], acc[r][mt][i]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sp_wload<R, 4, true, false>(q, s + 4, ring, J % 4);
+    if constexpr (J % 4 == 0) si4_csload<R>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
+}
+template <int MT, int R, int J>
+__device__ __forceinline__ void si4_trip(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][2],
+                                         dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+    if constexpr (J < 8) {
+        si4_step<MT, R, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_trip<MT, R, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+    }
+}
+
+template <int MT, int R>
+__device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, int lane, int t_lo, int nt) {
+    const int tid = threadIdx.x, g = lane >> 4;
+    SpSrc<R> q;          // weights: blocks of tiles w0 .. w0 + R - 1
+    Si4Scales<R> sq;     // their row-scale records
+    const uint8_t* st = reinterpret_cast<const uint8_t*>(a.st);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
+        sq.p[r] = reinterpret_cast<const uint4*>(st + (int64_t)(w0 + r) * a.c_pad * 128 + 32 * g);
+    }
+    q.w_last = a.s_pad - 1;
+    sq.c_last = a.c_pad - 1;
+    // this thread's activation item: row tid / 8 (clamped to M - 1), chunk tid % 8
+    SpSrc<1> xq;
+    const int xr = tid >> 3, c = tid & 7;
+    xq.xrow = a.x8 + (int64_t)min(xr, a.M - 1) * a.xrs + 16 * c;
+    xq.xss = a.xss;
+    xq.xdst = 128u * xr + 16u * (c ^ ((xr >> 1) & 7));
+    xq.x_last = a.steps - 1;
+
+    v4f acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    SpRing<R, 4> ring;
+    uint4 cs[2][R][2];
+    dt_u32x4 av[4];
+    v8i F0[MT], F1[MT];
+
+    // prologue as the fp8 form's: chunk 0's scales first, then the items of
+    // steps 0 .. 4 and the weights of steps 0 .. 3; steps 0 and 1 staged, step
+    // 0's fragments read
+    si4_csload<R>(sq, 0, cs[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    av[0] = sp_act(xq, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        av[(k + 1) % 4] = sp_act(xq, k + 1);
+        if (k == 2) si4_stage(lds, xq, 0, av[0]);
+        sp_wload<R, 4, true, false>(q, k, ring, k);
+    }
+    dt_barrier();
+    sp_read<MT>(lds, lane, F0);
+    si4_stage(lds + kSpStage, xq, 1, av[1]);
+
+    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+    sp_epilogue<MT, R, 0>(a, lds, acc, w0, lane, t_lo, nt, 1.0f);
+}
+
+template <int MT, int R>
+__global__ __launch_bounds__(kSpThreads) void spread_i4_kernel(SpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int64_t T = a.tiles, G = a.groups;
+    const int t_lo = (int)(T * blockIdx.x / G), n = (int)(T * (blockIdx.x + 1) / G) - t_lo;
+    const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
+    if constexpr (R > 1) {
+        if (nr < R) {
+            si4_run<MT, R - 1>(a, lds, w0, lane, t_lo, n);
+            return;
+        }
+    }
+    si4_run<MT, R>(a, lds, w0, lane, t_lo, n);
+}
+
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
 // batch of 4 loads per thread (ring depth 2 or 3) or 8 (depth 2)
 template <int WF>
@@ -3507,7 +3659,7 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
     return launch_splitk_reduce(a.partials, nullptr, M, N, a.ks, out, stream);
 }
 
-PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4, bool zp) {
     // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
     // workgroups (three quarters of the CUs idle in the tiled kernel)
     const bool narrow = (N + 255) / 256 < 64;
@@ -3520,6 +3672,12 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // 19.5 / 22.8 us against 17.0 / 18.1 / 20.7 / 26 / 28.9 us with the
     // split-K decode or the tiled kernel)
     if (!int4 && spread_fits(M, N, K)) return PreparedRoute::Spread;
+    // symmetric int4 on the same wide layers above 8 rows: the spread tiles
+    // with the decode kernel's split-code products (gate_up-shaped M = 16 /
+    // 32 / 64: 18.3 / 22.6 / 33.8 us against 24.5 / 34.1 / 49.4 us with the
+    // split-K decode or the tiled kernel; M = 1 / 8: 17.7 / 18.0 us against
+    // 17.0 / 18.0 us, which keep the decode kernel)
+    if (int4 && !zp && M > 8 && spread_fits(M, N, K)) return PreparedRoute::Spread;
     if (wide_sixteen(M, N, K, false, int4)) return PreparedRoute::Decode;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
@@ -3885,6 +4043,40 @@ hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t*
     W4A8_SA4(1, 1) W4A8_SA4(2, 1) W4A8_SA4(3, 1) W4A8_SA4(4, 1)
     W4A8_SA4(1, 2) W4A8_SA4(2, 2) W4A8_SA4(3, 2) W4A8_SA4(4, 2)
 #undef W4A8_SA4
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st, uint16_t* out,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (!spread_fits(M, N, K)) return hipErrorInvalidValue;
+    const SpPlan p = plan_spread(M, N, K, 4, 1);
+    if (p.groups < 1 || p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16 ||
+        p.mt != (int)((M + 15) / 16))
+        return hipErrorInvalidValue;
+    // every wave has a tile, and none more than R
+    if (p.tiles < (int64_t)kSpWaves * p.groups || (p.tiles + p.groups - 1) / p.groups > (int64_t)kSpWaves * p.r)
+        return hipErrorInvalidValue;
+    SpArgs a{};
+    a.x8 = x8; a.xs = xs; a.out = out;
+    a.wt = reinterpret_cast<const uint4*>(wt);
+    a.st = reinterpret_cast<const uint32_t*>(st);
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.c_pad = (int)((K / 128 + 3) / 4);
+    a.s_pad = 4 * a.c_pad;
+    a.steps = (int)(K / 128);
+    a.tiles = (int)p.tiles;
+    a.groups = (int)p.groups;
+    a.out16 = spread_out16(out, M, N, p);
+    a.xrs = K;
+    a.xss = 128;
+#define W4A8_SI4(MT, R)                                                                                 \
+    if (p.mt == MT && p.r == R) {                                                                     \
+        hipLaunchKernelGGL((spread_i4_kernel<MT, R>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
+        return hipGetLastError();                                                                     \
+    }
+    W4A8_SI4(1, 1) W4A8_SI4(2, 1) W4A8_SI4(3, 1) W4A8_SI4(4, 1)
+    W4A8_SI4(1, 2) W4A8_SI4(2, 2) W4A8_SI4(3, 2) W4A8_SI4(4, 2)
+#undef W4A8_SI4
     return hipErrorInvalidValue;
 }
 
