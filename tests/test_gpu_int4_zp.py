@@ -58,12 +58,25 @@ def test_int4_zp_ragged(M, N, K):
     _case(f"{M}x{N}x{K}", synth.int4_zp(N, K, seed=(M, N, K, 41)), M, (M, K, 41))
 
 
+# the spread tiles (wide layers, 9 <= M <= 64): one to four activation tiles,
+# one or two weight tiles per wave, odd chunk counts (the last trip past the
+# padded steps: after padding steps, K = 1152, and after a real step, K = 1536)
+ZP_SPREAD = [(9, 24576, 640, None), (33, 30000, 2048, None), (64, 65536, 512, None), (40, 24576, 1152, None),
+             (24, 24576, 1536, None), (64, 24600, 4608, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K,sample", ZP_SPREAD)
+def test_int4_zp_spread(M, N, K, sample):
+    _case(f"spread {M}x{N}x{K}", synth.int4_zp(N, K, seed=(M, N, K, 45)), M, (M, K, 45), sample=sample)
+
+
 @pytest.mark.parametrize("M", [1, 16, 64, 2048])
 def test_int4_zp_full_size(M):
     _case(f"zp M={M}", synth.int4_zp(), M, (42, M), sample=4096 if M > 64 else None)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 136, 1152), (16, 1000, 4096), (64, 5120, 2048), (300, 600, 768)])
+@pytest.mark.parametrize("M,N,K", [(1, 136, 1152), (16, 1000, 4096), (64, 5120, 2048), (300, 600, 768),
+                                   (24, 34816, 1024)])
 def test_int4_zp_symmetric_zeros_equal_symmetric_kernels(M, N, K):
     # every zero point 8: the zero term adds exactly zero, so the outputs are
     # those of the symmetric kernels, bit for bit

@@ -244,7 +244,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
             if (kind == W4A8_W4A4_PREPARED) return K <= kPreparedTiledMaxK ? w4a4_workspace_bytes(m, N, K) : 0;
             // the zero-point form takes the int4 kernels' routes and shapes
             const bool int4 = kind != W4A8_WEIGHT_MXFP4_PREPARED;
-            const PreparedRoute r = prepared_route(m, N, K, int4, kind == W4A8_WEIGHT_INT4G128_ZP_PREPARED);
+            const PreparedRoute r = prepared_route(m, N, K, int4);
             if (r == PreparedRoute::Decode) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, int4), m, N);
             // the linear's step-major copy of the codes (more than one activation tile)
             if (r == PreparedRoute::Spread) return m > 16 && !int4 ? linear_sm_bytes(m, N, K) : 0;
@@ -359,13 +359,13 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     if (!d_s || !aligned(d_s, int4 ? 16 : 4)) return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0 || (int4 && N % 8 != 0)) return W4A8_ERR_UNSUPPORTED_SHAPE;
     // the tiled kernel addresses activations with 32-bit offsets
-    const PreparedRoute route = prepared_route(M, N, K, int4, zp);
+    const PreparedRoute route = prepared_route(M, N, K, int4);
     if (route != PreparedRoute::Decode && route != PreparedRoute::Spread && K > kPreparedTiledMaxK)
         return W4A8_ERR_UNSUPPORTED_SHAPE;
     switch (route) {
     case PreparedRoute::Spread:
         if (int4)
-            return hip_status(launch_spread_i4(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, as_stream(stream)));
+            return hip_status(launch_spread_i4(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, as_stream(stream), zp));
         return hip_status(launch_spread(plan_spread(M, N, K, 0, -1), d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
                                         as_stream(stream)));
     case PreparedRoute::DTile: {

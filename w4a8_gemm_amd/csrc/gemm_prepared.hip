@@ -1749,7 +1749,8 @@ __global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The spread tiles with symmetric int4 g128 weights (wide layers, M <= 64).
+// The spread tiles with int4 g128 weights (wide layers, M <= 64; ZP: with a
+// zero point per group and row).
 // Weight blocks, activation staging and trips are the fp8 form's (register
 // ring 4 steps deep, 4-stage LDS ring of e4m3 steps, trips of 8 steps).  The
 // products are the split-K decode kernel's: each code taken as two e2m1
@@ -1761,29 +1762,36 @@ __global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
 // tile's 128-byte record) are loaded once per chunk into two chunk slots, as
 // the fp8 form's e8m0 dwords.  Where the chunk count is odd the last trip
 // passes the padded steps by four; the staged activation codes are zero there
-// (selected at the LDS store), so those products add nothing.
+// (selected at the LDS store), so those products add nothing.  ZP: the
+// records are 256 bytes (the scales, then bytes 16 - z in the same order) and
+// the products add (8 - z) sum(x) per row before its scale, sum(x) being
+// -1/8 of the constant product.
 // ---------------------------------------------------------------------------
 template <int R>
 struct Si4Scales {
-    const uint4* p[R];       // the lane's 32 bytes of chunk 0's record, per tile
+    const uint4* p[R];       // the lane's 32 bytes of scales in chunk 0's record, per tile
+    const uint4* z[R];       // ZP: the lane's 16 zero bytes in chunk 0's record
     int c_last;              // last padded chunk
 };
-template <int R>
-__device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (&cs)[R][2]) {
+// chunk c's slot: the lane's scales (2 x 16 bytes), ZP also its 16 zero bytes
+template <int R, bool ZP>
+__device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (&cs)[R][3]) {
     c = min(c, q.c_last);
+    constexpr int rec = ZP ? 16 : 8;   // record size in 16-byte units
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        cs[r][0] = q.p[r][8 * c];
-        cs[r][1] = q.p[r][8 * c + 1];
+        cs[r][0] = q.p[r][rec * c];
+        cs[r][1] = q.p[r][rec * c + 1];
+        if constexpr (ZP) cs[r][2] = q.z[r][rec * c];
     }
 }
 __device__ __forceinline__ void si4_stage(uint8_t* stage, const SpSrc<1>& q, int t, dt_u32x4 v) {
     *reinterpret_cast<dt_u32x4*>(stage + q.xdst) = t <= q.x_last ? v : dt_u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int MT, int R, int J>
+template <int MT, int R, bool ZP, int J>
 __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
-                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][2],
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][3],
                                          dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     constexpr int kX2 = 128, kX8 = 130;   // e8m0 2^1, 2^3
     dt_barrier();
@@ -1807,6 +1815,14 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
         const uint32_t s01 = (J & 1) == 0 ? sv.x : sv.z, s23 = (J & 1) == 0 ? sv.y : sv.w;
         const float s4[4] = {f16_to_f32(s01 & 0xFFFFu), f16_to_f32(s01 >> 16), f16_to_f32(s23 & 0xFFFFu),
                              f16_to_f32(s23 >> 16)};
+        // ZP: (8 - z) / -8 per row, the factor of the constant product (-8 sum(x))
+        float zf[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ZP) {
+            const uint4 zv = cs[(J / 4) % 2][r][2];
+            const uint32_t zb = (J & 3) == 0 ? zv.x : (J & 3) == 1 ? zv.y : (J & 3) == 2 ? zv.z : zv.w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zf[i] = (float)((int)((zb >> (8 * i)) & 0xFFu) - 8) * -0.125f;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const v8i bx = (J & 1) == 0 ? F0[mt] : F1[mt];
@@ -1815,24 +1831,27 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
             t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0,
                                                                  kUnitScale);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[r][mt][i] = __builtin_fmaf(s4[i], t[i], acc[r][mt][i]);
+            for (int i = 0; i < 4; ++i) {
+                const float u = ZP ? __builtin_fmaf(zf[i], t0[mt][i], t[i]) : t[i];
+                acc[r][mt][i] = __builtin_fmaf(s4[i], u, acc[r][mt][i]);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     sp_wload<R, 4, true, false>(q, s + 4, ring, J % 4);
-    if constexpr (J % 4 == 0) si4_csload<R>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
+    if constexpr (J % 4 == 0) si4_csload<R, ZP>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
 }
-template <int MT, int R, int J>
+template <int MT, int R, bool ZP, int J>
 __device__ __forceinline__ void si4_trip(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
-                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][2],
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][3],
                                          dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     if constexpr (J < 8) {
-        si4_step<MT, R, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
-        si4_trip<MT, R, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_step<MT, R, ZP, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_trip<MT, R, ZP, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
     }
 }
 
-template <int MT, int R>
+template <int MT, int R, bool ZP>
 __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, int lane, int t_lo, int nt) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;          // weights: blocks of tiles w0 .. w0 + R - 1
@@ -1841,7 +1860,9 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
-        sq.p[r] = reinterpret_cast<const uint4*>(st + (int64_t)(w0 + r) * a.c_pad * 128 + 32 * g);
+        const uint8_t* rec = st + (int64_t)(w0 + r) * a.c_pad * (ZP ? 256 : 128);
+        sq.p[r] = reinterpret_cast<const uint4*>(rec + 32 * g);
+        sq.z[r] = reinterpret_cast<const uint4*>(rec + 128 + 16 * g);
     }
     q.w_last = a.s_pad - 1;
     sq.c_last = a.c_pad - 1;
@@ -1859,14 +1880,14 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
     SpRing<R, 4> ring;
-    uint4 cs[2][R][2];
+    uint4 cs[2][R][3];
     dt_u32x4 av[4];
     v8i F0[MT], F1[MT];
 
     // prologue as the fp8 form's: chunk 0's scales first, then the items of
     // steps 0 .. 4 and the weights of steps 0 .. 3; steps 0 and 1 staged, step
     // 0's fragments read
-    si4_csload<R>(sq, 0, cs[0]);
+    si4_csload<R, ZP>(sq, 0, cs[0]);
     __builtin_amdgcn_sched_barrier(0);
     av[0] = sp_act(xq, 0);
 #pragma unroll
@@ -1879,11 +1900,11 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
     sp_read<MT>(lds, lane, F0);
     si4_stage(lds + kSpStage, xq, 1, av[1]);
 
-    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, ZP, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
     sp_epilogue<MT, R, 0>(a, lds, acc, w0, lane, t_lo, nt, 1.0f);
 }
 
-template <int MT, int R>
+template <int MT, int R, bool ZP>
 __global__ __launch_bounds__(kSpThreads) void spread_i4_kernel(SpArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
     const int lane = threadIdx.x & 63;
@@ -1893,11 +1914,11 @@ __global__ __launch_bounds__(kSpThreads) void spread_i4_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            si4_run<MT, R - 1>(a, lds, w0, lane, t_lo, n);
+            si4_run<MT, R - 1, ZP>(a, lds, w0, lane, t_lo, n);
             return;
         }
     }
-    si4_run<MT, R>(a, lds, w0, lane, t_lo, n);
+    si4_run<MT, R, ZP>(a, lds, w0, lane, t_lo, n);
 }
 
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
@@ -3659,7 +3680,7 @@ hipError_t launch_prepared_w4a4(const uint8_t* x4, const uint8_t* xe, const uint
     return launch_splitk_reduce(a.partials, nullptr, M, N, a.ks, out, stream);
 }
 
-PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4, bool zp) {
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4) {
     // a layer is narrow when 256-wide tiles of 64 rows give fewer than 64
     // workgroups (three quarters of the CUs idle in the tiled kernel)
     const bool narrow = (N + 255) / 256 < 64;
@@ -3672,12 +3693,13 @@ PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4, bool zp
     // 19.5 / 22.8 us against 17.0 / 18.1 / 20.7 / 26 / 28.9 us with the
     // split-K decode or the tiled kernel)
     if (!int4 && spread_fits(M, N, K)) return PreparedRoute::Spread;
-    // symmetric int4 on the same wide layers above 8 rows: the spread tiles
-    // with the decode kernel's split-code products (gate_up-shaped M = 16 /
-    // 32 / 64: 18.3 / 22.6 / 33.8 us against 24.5 / 34.1 / 49.4 us with the
-    // split-K decode or the tiled kernel; M = 1 / 8: 17.7 / 18.0 us against
+    // int4 (and its zero-point form) on the same wide layers above 8 rows: the
+    // spread tiles with the decode kernel's split-code products (gate_up-shaped
+    // M = 16 / 32 / 64: 18.3 / 22.6 / 33.8 us against 24.5 / 34.1 / 49.4 us
+    // with the split-K decode or the tiled kernel, zero points M = 16 / 64:
+    // 20.6 / 37.9 against 25.7 / 54.0 us; M = 1 / 8: 17.7 / 18.0 us against
     // 17.0 / 18.0 us, which keep the decode kernel)
-    if (int4 && !zp && M > 8 && spread_fits(M, N, K)) return PreparedRoute::Spread;
+    if (int4 && M > 8 && spread_fits(M, N, K)) return PreparedRoute::Spread;
     if (wide_sixteen(M, N, K, false, int4)) return PreparedRoute::Decode;
     // measured on gfx950 (gate_up 34816 x 5120 wide, down_proj 5120 x 17408
     // narrow), split-K decode kernel against the tiled kernel: narrow layers
@@ -4047,7 +4069,7 @@ hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t*
 }
 
 hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st, uint16_t* out,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream, bool zp) {
     if (!spread_fits(M, N, K)) return hipErrorInvalidValue;
     const SpPlan p = plan_spread(M, N, K, 4, 1);
     if (p.groups < 1 || p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16 ||
@@ -4069,13 +4091,15 @@ hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* w
     a.out16 = spread_out16(out, M, N, p);
     a.xrs = K;
     a.xss = 128;
-#define W4A8_SI4(MT, R)                                                                                 \
-    if (p.mt == MT && p.r == R) {                                                                     \
-        hipLaunchKernelGGL((spread_i4_kernel<MT, R>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
-        return hipGetLastError();                                                                     \
+#define W4A8_SI4(MT, R, ZP)                                                                                 \
+    if (p.mt == MT && p.r == R && zp == ZP) {                                                             \
+        hipLaunchKernelGGL((spread_i4_kernel<MT, R, ZP>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
+        return hipGetLastError();                                                                         \
     }
-    W4A8_SI4(1, 1) W4A8_SI4(2, 1) W4A8_SI4(3, 1) W4A8_SI4(4, 1)
-    W4A8_SI4(1, 2) W4A8_SI4(2, 2) W4A8_SI4(3, 2) W4A8_SI4(4, 2)
+    W4A8_SI4(1, 1, false) W4A8_SI4(2, 1, false) W4A8_SI4(3, 1, false) W4A8_SI4(4, 1, false)
+    W4A8_SI4(1, 2, false) W4A8_SI4(2, 2, false) W4A8_SI4(3, 2, false) W4A8_SI4(4, 2, false)
+    W4A8_SI4(1, 1, true) W4A8_SI4(2, 1, true) W4A8_SI4(3, 1, true) W4A8_SI4(4, 1, true)
+    W4A8_SI4(1, 2, true) W4A8_SI4(2, 2, true) W4A8_SI4(3, 2, true) W4A8_SI4(4, 2, true)
 #undef W4A8_SI4
     return hipErrorInvalidValue;
 }

@@ -187,10 +187,10 @@ hipError_t launch_prepared_decode(const GemmPlan& p, const uint8_t* x8, const fl
 // M = 16 while the activation slice of all of K fits one workgroup's LDS) or
 // the tiled kernel (K split across workgroups when its tiles are few).
 // DTile: the register-streamed tiles (narrow MXFP4 layers, 9 to 40 rows).
-// Spread: the spread tiles (wide layers, M <= 64; MXFP4, and symmetric int4,
-// zp false: the zero-point form keeps the other routes).
+// Spread: the spread tiles (wide layers, M <= 64; int4 and its zero-point
+// form from 9 rows).
 enum class PreparedRoute { Decode, Tiled, DTile, Spread };
-PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4, bool zp = false);
+PreparedRoute prepared_route(int64_t M, int64_t N, int64_t K, bool int4);
 // force_ks > 1: K split in that many parts where the shape rules would not (tuning)
 size_t tiled_workspace_bytes(int64_t M, int64_t N, int64_t K, bool int4, int force_ks = 0);
 // The linear on bf16 activations with the per-token fp8 quantization fused
@@ -271,10 +271,11 @@ hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false,
                          bool x_step_major = false);
-// symmetric int4 g128 fragment-order weights (wt codes, st the 128-byte
-// row-scale records per tile and chunk) on the spread tiles; x8 row-major
+// int4 g128 fragment-order weights (wt codes, st the row-scale records per
+// tile and chunk: 128 bytes, or 256 with the zero bytes when zp) on the
+// spread tiles; x8 row-major
 hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st, uint16_t* out,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream, bool zp);
 // W4A4 (e2m1 codes x4 [M, K/2], e8m0 xe [M, K/32]) on the spread tiles
 bool spread_a4_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
