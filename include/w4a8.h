@@ -450,11 +450,13 @@ w4a8_status w4a8_int4g128_zp_gemm_prepared(const uint8_t *d_x_fp8, const float *
  *     tile and 4-step chunk.
  *   w4a8_int5g128_prepare_fragments: the checkpoint tensors -> the three
  *     buffers (16-byte aligned).  Asynchronous.
- *   w4a8_int5g128_gemm_prepared: any M >= 1; M <= 32 the split-K decode
- *     kernel, larger M the tile kernel (64-, 128- or 256-row tiles, 128 wide;
- *     K split across workgroups when the tiles are few).  The workspace
- *     (sized with W4A8_WEIGHT_INT5G128_PREPARED) is required above M = 32:
- *     it holds the activation sums; calls that overlap on one workspace race.
+ *   w4a8_int5g128_gemm_prepared: any M >= 1; on wide layers (at least 1536
+ *     16-row tiles on 256 CUs, at most 16 per CU) for 9 <= M <= 64 the spread
+ *     tiles (no workspace); else M <= 32 the split-K decode kernel, larger M
+ *     the tile kernel (64-, 128- or 256-row tiles, 128 wide; K split across
+ *     workgroups when the tiles are few).  The workspace (sized with
+ *     W4A8_WEIGHT_INT5G128_PREPARED) is required for the tile kernel: it
+ *     holds the activation sums; calls that overlap on one workspace race.
  * K % 128 == 0 (else UNSUPPORTED_SHAPE).  Errors: INVALID_ARG,
  * UNSUPPORTED_SHAPE, WORKSPACE, HIP. */
 w4a8_status w4a8_int5g128_prepared_bytes(int64_t N, int64_t K, size_t *h_w_bytes, size_t *h_w5_bytes,

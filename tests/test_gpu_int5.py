@@ -58,6 +58,18 @@ def test_int5_ragged(M, N, K):
     _case(f"{M}x{N}x{K}", synth.int5(N, K, seed=(M, N, K, 61)), M, (M, K, 61))
 
 
+# the spread tiles (wide layers, 9 <= M <= 64): one to four activation tiles,
+# one or two weight tiles per wave, odd chunk counts (the last trip past the
+# padded steps: after padding steps, K = 1152, and after a real step, K = 1536)
+INT5_SPREAD = [(9, 24576, 640, None), (33, 30000, 2048, None), (64, 65536, 512, None), (40, 24576, 1152, None),
+               (24, 24576, 1536, None), (64, 24600, 4608, 4096), (17, 24602, 896, None)]
+
+
+@pytest.mark.parametrize("M,N,K,sample", INT5_SPREAD)
+def test_int5_spread(M, N, K, sample):
+    _case(f"spread {M}x{N}x{K}", synth.int5(N, K, seed=(M, N, K, 65)), M, (M, K, 65), sample=sample)
+
+
 @pytest.mark.parametrize("M", [1, 16, 64, 2048])
 def test_int5_full_size(M):
     _case(f"int5 M={M}", synth.int5(), M, (62, M), sample=4096 if M > 64 else None)

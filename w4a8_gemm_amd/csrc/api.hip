@@ -238,6 +238,7 @@ size_t w4a8_gemm_workspace_bytes(int64_t M_max, int64_t N, int64_t K, w4a8_weigh
         // route and shape that call gets
         auto at = [&](int64_t m) -> size_t {
             if (kind == W4A8_WEIGHT_INT5G128_PREPARED) {
+                if (m > 8 && spread_fits(m, N, K)) return 0;
                 if (m <= kPreparedDecodeMaxM) return plan_workspace_bytes(plan_prepared(m, N, K, 0, 0, false, true), m, N);
                 return i5_tiled_fits(m, K) ? i5_tiled_workspace_bytes(m, N, K) : 0;
             }
@@ -365,7 +366,8 @@ static w4a8_status gemm_prepared(const uint8_t* d_x_fp8, const float* d_x_scale,
     switch (route) {
     case PreparedRoute::Spread:
         if (int4)
-            return hip_status(launch_spread_i4(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, as_stream(stream), zp));
+            return hip_status(launch_spread_i4(d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K, as_stream(stream),
+                                               zp ? 3 : 1, nullptr));
         return hip_status(launch_spread(plan_spread(M, N, K, 0, -1), d_x_fp8, d_x_scale, d_w, d_s, d_out, M, N, K,
                                         as_stream(stream)));
     case PreparedRoute::DTile: {
@@ -628,6 +630,10 @@ w4a8_status w4a8_int5g128_gemm_prepared(const uint8_t* d_x_fp8, const float* d_x
         return W4A8_ERR_INVALID_ARG;
     if (K % 128 != 0) return W4A8_ERR_UNSUPPORTED_SHAPE;
     hipStream_t s = as_stream(stream);
+    // wide layers from 9 to 64 rows: the spread tiles (no workspace)
+    if (M > 8 && spread_fits(M, N, K))
+        return hip_status(launch_spread_i4(d_x_fp8, d_x_scale, d_w_prepared, d_s_prepared, d_out, M, N, K, s, 4,
+                                           d_w5_prepared));
     if (M <= kPreparedDecodeMaxM) {
         // the split-K decode kernel
         st = check_workspace(plan_workspace_bytes(plan_prepared(M, N, K, 0, 0, false, true), M, N), d_ws, ws_bytes);

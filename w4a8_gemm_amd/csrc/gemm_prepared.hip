@@ -1167,6 +1167,7 @@ struct SpArgs {
     int64_t xrs, xss;       // activation codes: bytes between rows and between 128-wide steps
                             // (row-major K and 128; step-major 128 and 128 M)
     const uint8_t* xe;      // MXFP4 activations: e8m0 [M, K/32] (x8 then holds e2m1 codes [M, K/2])
+    const uint32_t* w5;     // int5: the fifth-bit planes of the fragment-order weights
 };
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
@@ -1749,8 +1750,8 @@ __global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The spread tiles with int4 g128 weights (wide layers, M <= 64; ZP: with a
-// zero point per group and row).
+// The spread tiles with int4 g128 weights (wide layers, M <= 64; WF: kWI4,
+// kWI4Z with a zero point per group and row, or kWI5, int5 codes).
 // Weight blocks, activation staging and trips are the fp8 form's (register
 // ring 4 steps deep, 4-stage LDS ring of e4m3 steps, trips of 8 steps).  The
 // products are the split-K decode kernel's: each code taken as two e2m1
@@ -1762,38 +1763,46 @@ __global__ __launch_bounds__(kSpThreads) void spread_a4_kernel(SpArgs a) {
 // tile's 128-byte record) are loaded once per chunk into two chunk slots, as
 // the fp8 form's e8m0 dwords.  Where the chunk count is odd the last trip
 // passes the padded steps by four; the staged activation codes are zero there
-// (selected at the LDS store), so those products add nothing.  ZP: the
+// (selected at the LDS store), so those products add nothing.  kWI4Z: the
 // records are 256 bytes (the scales, then bytes 16 - z in the same order) and
 // the products add (8 - z) sum(x) per row before its scale, sum(x) being
-// -1/8 of the constant product.
+// -1/8 of the constant product.  kWI5: records as kWI4Z with signed bytes
+// 16 - z; c - 16 = 2 (c & 3)/2 + 8 ((c >> 2) & 3)/2 + 16 b4 - 16 takes a
+// third product on the fifth bits (the lane's four plane words of a chunk
+// loaded with its scales), the constant product is -16 sum(x), and each row
+// adds (16 - z) sum(x).
 // ---------------------------------------------------------------------------
 template <int R>
 struct Si4Scales {
     const uint4* p[R];       // the lane's 32 bytes of scales in chunk 0's record, per tile
-    const uint4* z[R];       // ZP: the lane's 16 zero bytes in chunk 0's record
+    const uint4* z[R];       // kWI4Z / kWI5: the lane's 16 zero bytes in chunk 0's record
+    const uint4* b[R];       // kWI5: the lane's four fifth-bit plane words of chunk 0
     int c_last;              // last padded chunk
 };
-// chunk c's slot: the lane's scales (2 x 16 bytes), ZP also its 16 zero bytes
-template <int R, bool ZP>
-__device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (&cs)[R][3]) {
+// chunk c's slot: the lane's scales (2 x 16 bytes), with zero points also its
+// 16 zero bytes, int5 also its plane words
+template <int R, int WF>
+__device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (&cs)[R][4]) {
     c = min(c, q.c_last);
-    constexpr int rec = ZP ? 16 : 8;   // record size in 16-byte units
+    constexpr int rec = WF == kWI4 ? 8 : 16;   // record size in 16-byte units
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         cs[r][0] = q.p[r][rec * c];
         cs[r][1] = q.p[r][rec * c + 1];
-        if constexpr (ZP) cs[r][2] = q.z[r][rec * c];
+        if constexpr (WF != kWI4) cs[r][2] = q.z[r][rec * c];
+        if constexpr (WF == kWI5) cs[r][3] = q.b[r][64 * c];
     }
 }
 __device__ __forceinline__ void si4_stage(uint8_t* stage, const SpSrc<1>& q, int t, dt_u32x4 v) {
     *reinterpret_cast<dt_u32x4*>(stage + q.xdst) = t <= q.x_last ? v : dt_u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int MT, int R, bool ZP, int J>
+template <int MT, int R, int WF, int J>
 __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
-                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][3],
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][4],
                                          dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
-    constexpr int kX2 = 128, kX8 = 130;   // e8m0 2^1, 2^3
+    constexpr int kX2 = 128, kX8 = 130, kX16 = 131;   // e8m0 2^1, 2^3, 2^4
+    constexpr int kXc = WF == kWI5 ? kX16 : kX8;      // the constant product: -16 or -8 sum(x)
     dt_barrier();
     if constexpr ((J & 1) == 0) sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F1);
     else sp_read<MT>(lds + ((J + 1) % kSpStages) * kSpStage, lane, F0);
@@ -1805,7 +1814,7 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         t0[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(neg1, (J & 1) == 0 ? F0[mt] : F1[mt],
-                                                                  v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4, kFmtFp8, 0, kX8,
+                                                                  v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp4, kFmtFp8, 0, kXc,
                                                                   0, kUnitScale);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1815,13 +1824,22 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
         const uint32_t s01 = (J & 1) == 0 ? sv.x : sv.z, s23 = (J & 1) == 0 ? sv.y : sv.w;
         const float s4[4] = {f16_to_f32(s01 & 0xFFFFu), f16_to_f32(s01 >> 16), f16_to_f32(s23 & 0xFFFFu),
                              f16_to_f32(s23 >> 16)};
-        // ZP: (8 - z) / -8 per row, the factor of the constant product (-8 sum(x))
+        // zero points: the row's zero term over the constant product, (8 - z) / -8
+        // (int4, bytes 16 - z) or (16 - z) / -16 (int5, signed bytes 16 - z)
         float zf[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (ZP) {
+        v8i b4 = {0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (WF != kWI4) {
             const uint4 zv = cs[(J / 4) % 2][r][2];
             const uint32_t zb = (J & 3) == 0 ? zv.x : (J & 3) == 1 ? zv.y : (J & 3) == 2 ? zv.z : zv.w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) zf[i] = (float)((int)((zb >> (8 * i)) & 0xFFu) - 8) * -0.125f;
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (WF == kWI5) zf[i] = (float)(int)(int8_t)((zb >> (8 * i)) & 0xFFu) * -0.0625f;
+                else zf[i] = (float)((int)((zb >> (8 * i)) & 0xFFu) - 8) * -0.125f;
+            }
+        }
+        if constexpr (WF == kWI5) {
+            const uint4 bv = cs[(J / 4) % 2][r][3];
+            b4 = i5_bit_frag((J & 3) == 0 ? bv.x : (J & 3) == 1 ? bv.y : (J & 3) == 2 ? bv.z : bv.w);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -1830,28 +1848,31 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
                                                                      kUnitScale);
             t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.hi, bx, t, kFmtFp4, kFmtFp8, 0, kX8, 0,
                                                                  kUnitScale);
+            if constexpr (WF == kWI5)
+                t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b4, bx, t, kFmtFp4, kFmtFp8, 0, kX16, 0,
+                                                                     kUnitScale);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float u = ZP ? __builtin_fmaf(zf[i], t0[mt][i], t[i]) : t[i];
+                const float u = WF != kWI4 ? __builtin_fmaf(zf[i], t0[mt][i], t[i]) : t[i];
                 acc[r][mt][i] = __builtin_fmaf(s4[i], u, acc[r][mt][i]);
             }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     sp_wload<R, 4, true, false>(q, s + 4, ring, J % 4);
-    if constexpr (J % 4 == 0) si4_csload<R, ZP>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
+    if constexpr (J % 4 == 0) si4_csload<R, WF>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
 }
-template <int MT, int R, bool ZP, int J>
+template <int MT, int R, int WF, int J>
 __device__ __forceinline__ void si4_trip(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
-                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][3],
+                                         const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][4],
                                          dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
     if constexpr (J < 8) {
-        si4_step<MT, R, ZP, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
-        si4_trip<MT, R, ZP, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_step<MT, R, WF, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_trip<MT, R, WF, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
     }
 }
 
-template <int MT, int R, bool ZP>
+template <int MT, int R, int WF>
 __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, int lane, int t_lo, int nt) {
     const int tid = threadIdx.x, g = lane >> 4;
     SpSrc<R> q;          // weights: blocks of tiles w0 .. w0 + R - 1
@@ -1860,9 +1881,12 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         q.wp[r] = a.wt + (int64_t)(w0 + r) * a.s_pad * 64 + lane;
-        const uint8_t* rec = st + (int64_t)(w0 + r) * a.c_pad * (ZP ? 256 : 128);
+        const uint8_t* rec = st + (int64_t)(w0 + r) * a.c_pad * (WF == kWI4 ? 128 : 256);
         sq.p[r] = reinterpret_cast<const uint4*>(rec + 32 * g);
         sq.z[r] = reinterpret_cast<const uint4*>(rec + 128 + 16 * g);
+        // int5 planes [tile][chunk][lane][step]: 16 bytes per lane and chunk
+        sq.b[r] = WF == kWI5 ? reinterpret_cast<const uint4*>(a.w5) + (int64_t)(w0 + r) * a.c_pad * 64 + lane
+                             : nullptr;
     }
     q.w_last = a.s_pad - 1;
     sq.c_last = a.c_pad - 1;
@@ -1880,14 +1904,14 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
     SpRing<R, 4> ring;
-    uint4 cs[2][R][3];
+    uint4 cs[2][R][4];
     dt_u32x4 av[4];
     v8i F0[MT], F1[MT];
 
     // prologue as the fp8 form's: chunk 0's scales first, then the items of
     // steps 0 .. 4 and the weights of steps 0 .. 3; steps 0 and 1 staged, step
     // 0's fragments read
-    si4_csload<R, ZP>(sq, 0, cs[0]);
+    si4_csload<R, WF>(sq, 0, cs[0]);
     __builtin_amdgcn_sched_barrier(0);
     av[0] = sp_act(xq, 0);
 #pragma unroll
@@ -1900,11 +1924,11 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
     sp_read<MT>(lds, lane, F0);
     si4_stage(lds + kSpStage, xq, 1, av[1]);
 
-    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, ZP, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, WF, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
     sp_epilogue<MT, R, 0>(a, lds, acc, w0, lane, t_lo, nt, 1.0f);
 }
 
-template <int MT, int R, bool ZP>
+template <int MT, int R, int WF>
 __global__ __launch_bounds__(kSpThreads) void spread_i4_kernel(SpArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
     const int lane = threadIdx.x & 63;
@@ -1914,11 +1938,11 @@ __global__ __launch_bounds__(kSpThreads) void spread_i4_kernel(SpArgs a) {
     const int w0 = t_lo + wave * n / kSpWaves, nr = t_lo + (wave + 1) * n / kSpWaves - w0;
     if constexpr (R > 1) {
         if (nr < R) {
-            si4_run<MT, R - 1, ZP>(a, lds, w0, lane, t_lo, n);
+            si4_run<MT, R - 1, WF>(a, lds, w0, lane, t_lo, n);
             return;
         }
     }
-    si4_run<MT, R, ZP>(a, lds, w0, lane, t_lo, n);
+    si4_run<MT, R, WF>(a, lds, w0, lane, t_lo, n);
 }
 
 // fused-quant instances: one 16-row activation tile, the bf16 slice in one
@@ -4069,7 +4093,9 @@ hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t*
 }
 
 hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st, uint16_t* out,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream, bool zp) {
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream, int wf, const uint8_t* w5) {
+    if (wf != kWI4 && wf != kWI4Z && wf != kWI5) return hipErrorInvalidValue;
+    if ((wf == kWI5) != (w5 != nullptr)) return hipErrorInvalidValue;
     if (!spread_fits(M, N, K)) return hipErrorInvalidValue;
     const SpPlan p = plan_spread(M, N, K, 4, 1);
     if (p.groups < 1 || p.groups > (int64_t)INT32_MAX || p.tiles > (int64_t)INT32_MAX / 16 ||
@@ -4091,15 +4117,18 @@ hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* w
     a.out16 = spread_out16(out, M, N, p);
     a.xrs = K;
     a.xss = 128;
-#define W4A8_SI4(MT, R, ZP)                                                                                 \
-    if (p.mt == MT && p.r == R && zp == ZP) {                                                             \
-        hipLaunchKernelGGL((spread_i4_kernel<MT, R, ZP>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
+    a.w5 = reinterpret_cast<const uint32_t*>(w5);
+#define W4A8_SI4(MT, R, WF)                                                                                 \
+    if (p.mt == MT && p.r == R && wf == WF) {                                                             \
+        hipLaunchKernelGGL((spread_i4_kernel<MT, R, WF>), dim3(a.groups), dim3(kSpThreads), 0, stream, a); \
         return hipGetLastError();                                                                         \
     }
-    W4A8_SI4(1, 1, false) W4A8_SI4(2, 1, false) W4A8_SI4(3, 1, false) W4A8_SI4(4, 1, false)
-    W4A8_SI4(1, 2, false) W4A8_SI4(2, 2, false) W4A8_SI4(3, 2, false) W4A8_SI4(4, 2, false)
-    W4A8_SI4(1, 1, true) W4A8_SI4(2, 1, true) W4A8_SI4(3, 1, true) W4A8_SI4(4, 1, true)
-    W4A8_SI4(1, 2, true) W4A8_SI4(2, 2, true) W4A8_SI4(3, 2, true) W4A8_SI4(4, 2, true)
+    W4A8_SI4(1, 1, kWI4) W4A8_SI4(2, 1, kWI4) W4A8_SI4(3, 1, kWI4) W4A8_SI4(4, 1, kWI4)
+    W4A8_SI4(1, 2, kWI4) W4A8_SI4(2, 2, kWI4) W4A8_SI4(3, 2, kWI4) W4A8_SI4(4, 2, kWI4)
+    W4A8_SI4(1, 1, kWI4Z) W4A8_SI4(2, 1, kWI4Z) W4A8_SI4(3, 1, kWI4Z) W4A8_SI4(4, 1, kWI4Z)
+    W4A8_SI4(1, 2, kWI4Z) W4A8_SI4(2, 2, kWI4Z) W4A8_SI4(3, 2, kWI4Z) W4A8_SI4(4, 2, kWI4Z)
+    W4A8_SI4(1, 1, kWI5) W4A8_SI4(2, 1, kWI5) W4A8_SI4(3, 1, kWI5) W4A8_SI4(4, 1, kWI5)
+    W4A8_SI4(1, 2, kWI5) W4A8_SI4(2, 2, kWI5) W4A8_SI4(3, 2, kWI5) W4A8_SI4(4, 2, kWI5)
 #undef W4A8_SI4
     return hipErrorInvalidValue;
 }

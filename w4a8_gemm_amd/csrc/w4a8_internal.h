@@ -271,11 +271,12 @@ hipError_t launch_spread_fq(const uint16_t* xb, const uint8_t* wt, const uint8_t
 hipError_t launch_spread(const SpPlan& p, const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st,
                          uint16_t* out, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool plain = false,
                          bool x_step_major = false);
-// int4 g128 fragment-order weights (wt codes, st the row-scale records per
-// tile and chunk: 128 bytes, or 256 with the zero bytes when zp) on the
-// spread tiles; x8 row-major
+// int4 / int5 g128 fragment-order weights on the spread tiles (wt codes, st
+// the row-scale records per tile and chunk: 128 bytes, or 256 with the zero
+// bytes; w5 the int5 fifth-bit planes, else null); x8 row-major.  wf: 1 int4,
+// 3 int4 with zero points, 4 int5
 hipError_t launch_spread_i4(const uint8_t* x8, const float* xs, const uint8_t* wt, const uint8_t* st, uint16_t* out,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream, bool zp);
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream, int wf, const uint8_t* w5);
 // W4A4 (e2m1 codes x4 [M, K/2], e8m0 xe [M, K/32]) on the spread tiles
 bool spread_a4_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_spread_a4(const uint8_t* x4, const uint8_t* xe, const uint8_t* wt, const uint8_t* st,
