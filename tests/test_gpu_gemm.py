@@ -684,7 +684,8 @@ def test_int4_prepared_wide(M, N, K):
 # runs past the padded steps with zero activation codes: after padding steps
 # (K = 1152) and after a real step (K = 512, 1536)
 INT4_SPREAD = [(9, 24576, 640), (17, 24600, 896), (33, 30000, 2048), (64, 65536, 512), (47, 40000, 5120),
-               (40, 24576, 1152), (24, 24576, 1536), (12, 30000, 512), (64, 24600, 4608)]
+               (40, 24576, 1152), (24, 24576, 1536), (12, 30000, 512), (64, 24600, 4608), (10, 24576, 128),
+               (50, 24576, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", INT4_SPREAD)

@@ -62,7 +62,7 @@ def test_int4_zp_ragged(M, N, K):
 # one or two weight tiles per wave, odd chunk counts (the last trip past the
 # padded steps: after padding steps, K = 1152, and after a real step, K = 1536)
 ZP_SPREAD = [(9, 24576, 640, None), (33, 30000, 2048, None), (64, 65536, 512, None), (40, 24576, 1152, None),
-             (24, 24576, 1536, None), (64, 24600, 4608, 4096)]
+             (24, 24576, 1536, None), (64, 24600, 4608, 4096), (16, 24576, 128, None)]
 
 
 @pytest.mark.parametrize("M,N,K,sample", ZP_SPREAD)

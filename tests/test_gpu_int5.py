@@ -62,7 +62,7 @@ def test_int5_ragged(M, N, K):
 # one or two weight tiles per wave, odd chunk counts (the last trip past the
 # padded steps: after padding steps, K = 1152, and after a real step, K = 1536)
 INT5_SPREAD = [(9, 24576, 640, None), (33, 30000, 2048, None), (64, 65536, 512, None), (40, 24576, 1152, None),
-               (24, 24576, 1536, None), (64, 24600, 4608, 4096), (17, 24602, 896, None)]
+               (24, 24576, 1536, None), (64, 24600, 4608, 4096), (17, 24602, 896, None), (12, 24576, 128, None)]
 
 
 @pytest.mark.parametrize("M,N,K,sample", INT5_SPREAD)

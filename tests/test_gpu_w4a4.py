@@ -77,7 +77,7 @@ def test_w4a4_decode(M, N, K):
 # (K = 512, 1536)
 W4A4_SPREAD = [(3, 25001, 640, None), (17, 24602, 896, None), (33, 30000, 2048, None), (64, 65536, 512, None),
                (47, 40000, 5120, 2048), (2, 24576, 1152, None), (40, 24576, 1152, None), (24, 24576, 1536, None),
-               (1, 30000, 512, None), (64, 24600, 4608, 2048)]
+               (1, 30000, 512, None), (64, 24600, 4608, 2048), (5, 24576, 128, None), (50, 24576, 256, None)]
 
 
 @pytest.mark.parametrize("M,N,K,sample", W4A4_SPREAD)
