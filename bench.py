@@ -34,8 +34,10 @@ record; the full-layer requant in GB/s (three rules, ROW_CHUNK and one pass)
 with its HBM and VALU counter record, and written straight into fragment order
 beside the repack pass it saves; requant accuracy (relRMS) against the
 synthetic original; the two plain-layout GEMM entry points (MXFP4 row-major,
-int4 transposed); W4A4; the bf16 / fp8-per-channel encoders; down_proj; int4,
-int4 with zero points and int5.
+int4 transposed); W4A4 (prefill with its counter record, decode M = 1, 32,
+64); the bf16 / fp8-per-channel encoders; down_proj; int4 on a wide layer
+(M = 1, 16, 64); int4, int4 with zero points and int5 on the down_proj shape,
+the M = 2048 tiles with their counter record.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same step, on
 all host threads and on one.
 """
