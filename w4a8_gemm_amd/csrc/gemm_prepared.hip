@@ -1793,6 +1793,23 @@ __device__ __forceinline__ void si4_csload(const Si4Scales<R>& q, int c, uint4 (
         if constexpr (WF == kWI5) cs[r][3] = q.b[r][64 * c];
     }
 }
+// The int5 tiles with four activation tiles and two weight tiles per wave hold
+// too much for 256 registers with the chunk slots (64 of them); they take each
+// step's side data with its weights instead, one ring slot per step: the two
+// fp16 scale pairs, the zero-byte dword and the plane word (32 registers)
+template <int MT, int R, int WF> constexpr bool kSi4Step = WF == kWI5 && MT == 4 && R == 2;
+template <int R>
+__device__ __forceinline__ void si4_sdload(const Si4Scales<R>& q, int j, int w_last, uint4 (&sd)[R]) {
+    j = min(j, w_last);
+    const int c = j >> 2, u = j & 3;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint2 sc = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(q.p[r]) + 256 * c + 8 * u);
+        const uint32_t zb = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(q.z[r]) + 256 * c + 4 * u);
+        const uint32_t pw = reinterpret_cast<const uint32_t*>(q.b[r] + 64 * (int64_t)c)[u];
+        sd[r] = make_uint4(sc.x, sc.y, zb, pw);
+    }
+}
 __device__ __forceinline__ void si4_stage(uint8_t* stage, const SpSrc<1>& q, int t, dt_u32x4 v) {
     *reinterpret_cast<dt_u32x4*>(stage + q.xdst) = t <= q.x_last ? v : dt_u32x4{0u, 0u, 0u, 0u};
 }
@@ -1800,7 +1817,9 @@ __device__ __forceinline__ void si4_stage(uint8_t* stage, const SpSrc<1>& q, int
 template <int MT, int R, int WF, int J>
 __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
                                          const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][4],
-                                         dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+                                         uint4 (&sd)[4][R], dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT],
+                                         v4f (&acc)[R][MT]) {
+    constexpr bool PS = kSi4Step<MT, R, WF>;
     constexpr int kX2 = 128, kX8 = 130, kX16 = 131;   // e8m0 2^1, 2^3, 2^4
     constexpr int kXc = WF == kWI5 ? kX16 : kX8;      // the constant product: -16 or -8 sum(x)
     dt_barrier();
@@ -1820,8 +1839,8 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
     for (int r = 0; r < R; ++r) {
         const dt_u32x4 wv = ring.w[J % 4][r];
         const I4Split w = i4_split(make_uint4(wv[0], wv[1], wv[2], wv[3]));
-        const uint4 sv = cs[(J / 4) % 2][r][(J & 3) / 2];
-        const uint32_t s01 = (J & 1) == 0 ? sv.x : sv.z, s23 = (J & 1) == 0 ? sv.y : sv.w;
+        const uint4 sv = PS ? sd[J % 4][r] : cs[(J / 4) % 2][r][(J & 3) / 2];
+        const uint32_t s01 = PS || (J & 1) == 0 ? sv.x : sv.z, s23 = PS || (J & 1) == 0 ? sv.y : sv.w;
         const float s4[4] = {f16_to_f32(s01 & 0xFFFFu), f16_to_f32(s01 >> 16), f16_to_f32(s23 & 0xFFFFu),
                              f16_to_f32(s23 >> 16)};
         // zero points: the row's zero term over the constant product, (8 - z) / -8
@@ -1830,7 +1849,8 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
         v8i b4 = {0, 0, 0, 0, 0, 0, 0, 0};
         if constexpr (WF != kWI4) {
             const uint4 zv = cs[(J / 4) % 2][r][2];
-            const uint32_t zb = (J & 3) == 0 ? zv.x : (J & 3) == 1 ? zv.y : (J & 3) == 2 ? zv.z : zv.w;
+            const uint32_t zb = PS ? sd[J % 4][r].z
+                                   : (J & 3) == 0 ? zv.x : (J & 3) == 1 ? zv.y : (J & 3) == 2 ? zv.z : zv.w;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (WF == kWI5) zf[i] = (float)(int)(int8_t)((zb >> (8 * i)) & 0xFFu) * -0.0625f;
@@ -1839,7 +1859,8 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
         }
         if constexpr (WF == kWI5) {
             const uint4 bv = cs[(J / 4) % 2][r][3];
-            b4 = i5_bit_frag((J & 3) == 0 ? bv.x : (J & 3) == 1 ? bv.y : (J & 3) == 2 ? bv.z : bv.w);
+            b4 = i5_bit_frag(PS ? sd[J % 4][r].w
+                                : (J & 3) == 0 ? bv.x : (J & 3) == 1 ? bv.y : (J & 3) == 2 ? bv.z : bv.w);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -1860,15 +1881,17 @@ __device__ __forceinline__ void si4_step(uint8_t* lds, int s, int lane, const Sp
     }
     __builtin_amdgcn_sched_barrier(0);
     sp_wload<R, 4, true, false>(q, s + 4, ring, J % 4);
-    if constexpr (J % 4 == 0) si4_csload<R, WF>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
+    if constexpr (PS) si4_sdload<R>(sq, s + 4, q.w_last, sd[J % 4]);
+    else if constexpr (J % 4 == 0) si4_csload<R, WF>(sq, s / 4 + 1, cs[(J / 4 + 1) % 2]);
 }
 template <int MT, int R, int WF, int J>
 __device__ __forceinline__ void si4_trip(uint8_t* lds, int s, int lane, const SpSrc<1>& xq, const SpSrc<R>& q,
                                          const Si4Scales<R>& sq, SpRing<R, 4>& ring, uint4 (&cs)[2][R][4],
-                                         dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT], v4f (&acc)[R][MT]) {
+                                         uint4 (&sd)[4][R], dt_u32x4 (&av)[4], v8i (&F0)[MT], v8i (&F1)[MT],
+                                         v4f (&acc)[R][MT]) {
     if constexpr (J < 8) {
-        si4_step<MT, R, WF, J>(lds, s + J, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
-        si4_trip<MT, R, WF, J + 1>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+        si4_step<MT, R, WF, J>(lds, s + J, lane, xq, q, sq, ring, cs, sd, av, F0, F1, acc);
+        si4_trip<MT, R, WF, J + 1>(lds, s, lane, xq, q, sq, ring, cs, sd, av, F0, F1, acc);
     }
 }
 
@@ -1904,14 +1927,16 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
     SpRing<R, 4> ring;
-    uint4 cs[2][R][4];
+    uint4 cs[2][R][4];   // chunk slots (unused with per-step side data)
+    uint4 sd[4][R];      // per-step side data (kSi4Step only)
     dt_u32x4 av[4];
     v8i F0[MT], F1[MT];
+    constexpr bool PS = kSi4Step<MT, R, WF>;
 
     // prologue as the fp8 form's: chunk 0's scales first, then the items of
     // steps 0 .. 4 and the weights of steps 0 .. 3; steps 0 and 1 staged, step
     // 0's fragments read
-    si4_csload<R, WF>(sq, 0, cs[0]);
+    if constexpr (!PS) si4_csload<R, WF>(sq, 0, cs[0]);
     __builtin_amdgcn_sched_barrier(0);
     av[0] = sp_act(xq, 0);
 #pragma unroll
@@ -1919,12 +1944,14 @@ __device__ __forceinline__ void si4_run(const SpArgs& a, uint8_t* lds, int w0, i
         av[(k + 1) % 4] = sp_act(xq, k + 1);
         if (k == 2) si4_stage(lds, xq, 0, av[0]);
         sp_wload<R, 4, true, false>(q, k, ring, k);
+        if constexpr (PS) si4_sdload<R>(sq, k, q.w_last, sd[k]);
     }
     dt_barrier();
     sp_read<MT>(lds, lane, F0);
     si4_stage(lds + kSpStage, xq, 1, av[1]);
 
-    for (int s = 0; s < a.s_pad; s += 8) si4_trip<MT, R, WF, 0>(lds, s, lane, xq, q, sq, ring, cs, av, F0, F1, acc);
+    for (int s = 0; s < a.s_pad; s += 8)
+        si4_trip<MT, R, WF, 0>(lds, s, lane, xq, q, sq, ring, cs, sd, av, F0, F1, acc);
     sp_epilogue<MT, R, 0>(a, lds, acc, w0, lane, t_lo, nt, 1.0f);
 }
 
